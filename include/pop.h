@@ -1,0 +1,168 @@
+/*
+ * libpop: POP (Partition-guided Online Pruning) channel-pruned gated-MLP path
+ * for AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes.
+ *
+ * The method (cited by page title and section):
+ *   "POP: Online Structural Pruning Enables Efficient Inference of Large
+ *   Foundation Models" (paper notes), "Key design 1": during prefill, every
+ *   intermediate channel i of the FFN gets an importance from the whole prompt,
+ *   I_i = || W_up[i,:] * s ||_2 with s_k = || X[:,:,k] ||_2, and the channels are
+ *   split by the quantile thresholds q_{r-delta} and q_{r+delta} into Retained
+ *   (R), Candidate (C) and Pruned (P) regions.  "Key design 2": in every decode
+ *   step the input goes through W_gate / W_up restricted to R u C, the
+ *   candidates are scored and the best k of them top R up to the live count that
+ *   r requires, and W_down is applied to R plus the selected candidates.
+ *   The gated MLP itself is equation (1) of "Batch-wise adaptive pruning ... for
+ *   language reasoning models", section 3.1: z = SiLU(W_g x) * (W_1 x),
+ *   y = W_2 z.
+ *
+ * Readings taken where the pages leave a step open:
+ *   - delta = gamma; cut ranks c = round(p * d_ff) with p clamped to [0, 1]
+ *     and round half away from zero; live = round((1 - r) * d_ff);
+ *     k = clamp(live - |R|, 0, |C|).
+ *   - one total order for every selection: a larger value is more important;
+ *     on equal values the lower index is more important.
+ *   - decode candidate score = max over the batch rows of |SiLU(g_i) * u_i|
+ *     (a batch shares one mask).
+ *   - no biases.
+ *
+ * Conventions shared by every entry point:
+ *   - Every call returns pop_status.  Arguments are validated before anything is
+ *     enqueued; on an error nothing is enqueued, outputs are untouched and
+ *     pop_last_error() holds a message for this thread.
+ *   - POP_OK means the work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream).  The host never waits for the device and never reads device
+ *     memory, so every call may be captured in a HIP graph.
+ *   - The caller allocates and owns every buffer: inputs, outputs and the
+ *     workspace.  The library keeps no pointer after it returns and holds no
+ *     mutable global state; calls on different streams need distinct
+ *     workspaces.
+ *   - Device buffers are contiguous, row-major and 16-byte aligned.
+ *     dtype POP_BF16 needs d % 8 == 0, POP_F32 needs d % 4 == 0.
+ *   - Index lists (R, C) are int32, strictly ascending, in [0, d_ff) and
+ *     mutually disjoint (unchecked in release builds).
+ *   - Outputs are fp32 whatever the input dtype; accumulation is fp32.
+ */
+#ifndef POP_H_
+#define POP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  POP_OK = 0,
+  POP_ERR_INVALID_ARGUMENT = 1,   /* r, gamma out of range; null pointer; count mismatch */
+  POP_ERR_UNSUPPORTED_DTYPE = 2,
+  POP_ERR_BAD_SHAPE = 3,          /* sizes negative, too large, or d not a vector multiple */
+  POP_ERR_MISALIGNED = 4,         /* a device pointer not 16-byte aligned */
+  POP_ERR_WORKSPACE_TOO_SMALL = 5,
+  POP_ERR_HIP = 6                 /* a HIP launch failed; see pop_last_error() */
+} pop_status;
+
+typedef enum { POP_F32 = 0, POP_BF16 = 1 } pop_dtype;
+
+/* Region sizes of one partition and the per-step top-k count. */
+typedef struct {
+  int32_t d_ff;
+  int32_t c_low;   /* cut rank at r - delta: |P| */
+  int32_t c_high;  /* cut rank at r + delta: |P| + |C| */
+  int32_t n_P, n_C, n_R;
+  int32_t n_live;  /* round((1 - r) * d_ff) */
+  int32_t k;       /* candidates selected per decode step; n_R + k == n_live when feasible */
+} pop_counts;
+
+/* Largest d_ff a single partition or a single decode call accepts. */
+#define POP_MAX_D_FF 32768
+/* Largest d (model width) accepted. */
+#define POP_MAX_D 16384
+/* Largest decode batch that shares one mask. */
+#define POP_MAX_BATCH 256
+
+/* Human-readable name of a status code (static storage). */
+const char* pop_status_string(pop_status s);
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* pop_last_error(void);
+
+/*
+ * pop_partition_counts — pure host function, no device work.
+ * The sizes of P, C, R and the top-k count for d_ff channels at pruning rate
+ * r and partition width gamma (POP notes, "Key design 1" thresholds
+ * q_{r-delta}, q_{r+delta}; "Key design 2" exact live count).
+ * Requires 1 <= d_ff <= POP_MAX_D_FF, 0 <= r < 1, 0 <= gamma < 1.
+ */
+pop_status pop_partition_counts(int32_t d_ff, double r, double gamma, pop_counts* out);
+
+/* Workspace bytes pop_prefill_partition needs for these sizes. */
+size_t pop_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff);
+
+/*
+ * pop_prefill_partition — POP notes, "Key design 1".
+ *   X          device, [n_tokens, d] in dt: the FFN inputs of every prompt token
+ *              of every sequence (B*L rows; n_tokens may be 0).
+ *   W_up       device, [d_ff, d] in dt (nn.Linear layout: row i = channel i).
+ *   r, gamma   pruning rate and partition width (delta = gamma).
+ *   R, C, P    device int32 outputs of n_R, n_C, n_P entries (sizes from
+ *              pop_partition_counts), each written in ascending order.
+ *   importance optional device fp32 [d_ff]: I_i (NULL to skip).
+ *   ws         device workspace of at least pop_prefill_workspace_bytes().
+ * Kernels: column sum of squares of X (two-stage, fixed order), weighted row
+ * norm of W_up, one-workgroup radix select of the two cut keys and an
+ * order-preserving compaction.  Deterministic: identical inputs give
+ * bit-identical outputs.
+ */
+pop_status pop_prefill_partition(const void* X, int64_t n_tokens, int32_t d, const void* W_up,
+                                  int32_t d_ff, pop_dtype dt, double r, double gamma, int32_t* R,
+                                  int32_t* C, int32_t* P, float* importance, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/* Workspace bytes pop_decode_ffn / pop_dense_ffn_decode need. */
+size_t pop_decode_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff);
+
+/*
+ * pop_decode_ffn — POP notes, "Key design 2" and "Overall framework".
+ *   x          device, [batch, d] in dt: this step's FFN inputs; the batch
+ *              rows share one mask (0 <= batch <= POP_MAX_BATCH).
+ *   W_gate     device, [d_ff, d] in dt.
+ *   W_up       device, [d_ff, d] in dt.
+ *   W_downT    device, [d_ff, d] in dt: the TRANSPOSE of the nn.Linear down
+ *              weight [d, d_ff], so channel i's down column is a contiguous row.
+ *   R, n_R     device int32 retained channels (ascending).
+ *   C, n_C     device int32 candidate channels (ascending).
+ *   r          pruning rate; k = clamp(round((1 - r) d_ff) - n_R, 0, n_C).
+ *   y          device fp32 [batch, d] output.
+ *   selected   optional device int32 [k]: the selected candidates, ascending.
+ *   ws         device workspace >= pop_decode_workspace_bytes(batch, d, d_ff).
+ *              After the call completes it starts with the intermediate
+ *              z (fp32 [batch, n_R + n_C], R columns first, then C); the
+ *              candidate scores (fp32 [n_C]) start at byte offset
+ *              align_up(4 * batch * d_ff + 16, 256).
+ * Kernels: row-gathered gate/up GEMV with fused SiLU*up and fused candidate
+ * score; one-workgroup radix top-k over the candidates; gathered
+ * down-projection over R and the selected rows of W_downT with a fixed-order
+ * two-stage reduction.
+ */
+pop_status pop_decode_ffn(const void* x, int32_t batch, int32_t d, const void* W_gate,
+                          const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
+                          const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C,
+                          double r, float* y, int32_t* selected, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * pop_dense_ffn_decode — the unpruned gated MLP (equation (1) of the
+ * batch-wise pruning page, section 3.1) for one decode step over all d_ff
+ * channels: the dense baseline the pruned step is compared with.  Same
+ * layouts as pop_decode_ffn; after the call the workspace starts with z
+ * (fp32 [batch, d_ff]).
+ */
+pop_status pop_dense_ffn_decode(const void* x, int32_t batch, int32_t d, const void* W_gate,
+                                const void* W_up, const void* W_downT, int32_t d_ff,
+                                pop_dtype dt, float* y, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* POP_H_ */

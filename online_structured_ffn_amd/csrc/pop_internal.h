@@ -1,0 +1,28 @@
+// Host-side helpers shared by the libpop translation units (no device code).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pop.h"
+
+namespace pop {
+
+// Records a message for pop_last_error() and returns s.
+pop_status fail(pop_status s, const char* fmt, ...);
+// Clears the thread's last error.
+void clear_error();
+// pop_partition_counts without argument validation of `out`.
+pop_counts counts(int32_t d_ff, double r, double gamma);
+// Live count and per-step k for an existing partition.
+int32_t live_count(int32_t d_ff, double r);
+int32_t topk_count(int32_t d_ff, double r, int32_t n_R, int32_t n_C);
+
+bool aligned16(const void* p);
+int elem_bytes(pop_dtype dt);
+// Checks dtype and that d suits the 16-byte vector width of dt.
+pop_status check_dtype_width(pop_dtype dt, int64_t d);
+pop_status check_rate(double r, double gamma);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace pop

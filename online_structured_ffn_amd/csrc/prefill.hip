@@ -1,0 +1,235 @@
+// Prefill three-region partition (POP notes, "Key design 1").
+//
+//   K1  column sum of squares  s2[k] = sum_n X[n,k]^2         (HBM-bound on X)
+//   K1r fixed-order reduction of the K1 partial sums
+//   K2  importance  I[i] = sqrt(sum_k W_up[i,k]^2 * s2[k])    (HBM-bound on W_up)
+//   K3  one-workgroup radix select of the keys at ranks c_low and c_high and an
+//       order-preserving compaction into P, C, R            (latency-bound)
+#include <hip/hip_runtime.h>
+
+#include "pop_device.h"
+#include "pop_internal.h"
+
+namespace pop {
+
+// ---------------------------------------------------------------- K1
+// Block: 64 threads (one wave); thread t owns the Vec<T>::N columns starting at
+// (blockIdx.x*64 + t)*N; blockIdx.y is a chunk of rows.  Each wave reads whole
+// 16-byte vectors of consecutive columns of one row per instruction (1 KB of
+// bf16 per row per wave, coalesced).
+template <typename T>
+__global__ __launch_bounds__(64) void k_colsq_partial(const T* __restrict__ X, int64_t n_tokens, int d,
+                                                      int64_t rows_per_chunk, float* __restrict__ partial) {
+  constexpr int V = Vec<T>::N;
+  const int col = (blockIdx.x * 64 + threadIdx.x) * V;
+  if (col >= d) return;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
+  int64_t r1 = r0 + rows_per_chunk;
+  if (r1 > n_tokens) r1 = n_tokens;
+  float acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  const T* p = X + col;
+  int64_t r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    u32x4 q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = ld16_stream(p + (r + j) * d);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float f[V];
+      unpack(q[j], f, T{});
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] = fmaf(f[v], f[v], acc[v]);
+    }
+  }
+  for (; r < r1; ++r) {
+    float f[V];
+    unpack(ld16_stream(p + r * d), f, T{});
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = fmaf(f[v], f[v], acc[v]);
+  }
+  float* out = partial + (int64_t)blockIdx.y * d + col;
+#pragma unroll
+  for (int v = 0; v < V; ++v) out[v] = acc[v];
+}
+
+// ---------------------------------------------------------------- K2
+// Block: 256 threads = 4 waves, one W_up row per wave at a time.  s2 sits in
+// LDS; each lane reads 16-byte vectors of its row, 4 in flight.
+template <typename T>
+__global__ __launch_bounds__(256) void k_importance(const T* __restrict__ W, int d_ff, int d,
+                                                    const float* __restrict__ s2, float* __restrict__ I) {
+  constexpr int V = Vec<T>::N;
+  extern __shared__ float s2_lds[];
+  for (int k = threadIdx.x; k < d; k += 256) s2_lds[k] = s2[k];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  constexpr int STEP = 64 * V;
+  for (int row = blockIdx.x * 4 + wave; row < d_ff; row += gridDim.x * 4) {
+    const T* w = W + (int64_t)row * d;
+    float acc = 0.f;
+    int k0 = 0;
+    for (; k0 + 4 * STEP <= d; k0 += 4 * STEP) {
+      u32x4 q[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q[j] = ld16_stream(w + k0 + j * STEP + lane * V);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float f[V];
+        unpack(q[j], f, T{});
+        const float* sp = s2_lds + k0 + j * STEP + lane * V;
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc = fmaf(f[v] * f[v], sp[v], acc);
+      }
+    }
+    for (; k0 < d; k0 += STEP) {
+      const int k = k0 + lane * V;
+      if (k < d) {
+        float f[V];
+        unpack(ld16_stream(w + k), f, T{});
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc = fmaf(f[v] * f[v], s2_lds[k + v], acc);
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) I[row] = sqrtf(acc);
+  }
+}
+
+// ---------------------------------------------------------------- K3
+__global__ __launch_bounds__(kSelThreads) void k_partition(const float* __restrict__ I, int n, int c_low, int c_high,
+                                                           int32_t* __restrict__ R, int32_t* __restrict__ C,
+                                                           int32_t* __restrict__ P) {
+  __shared__ SelShared sh;
+  sel_load(I, n, sh);
+  const int ranks[2] = {c_low, c_high};
+  select_thresholds<2>(n, ranks, sh);
+  const SelTarget lo = sh.tgt[0];
+  const SelTarget hi = sh.tgt[1];
+  const int E = (n + kSelThreads - 1) / kSelThreads;
+  const int base = threadIdx.x * E;
+  const int end = min(n, base + E);
+  int pos[3] = {0, 0, 0};  // P, C, R
+  for (int i = base; i < end; ++i) {
+    const unsigned long long key = sel_key(sh.vals[i], i);
+    if (sel_less(lo, key)) ++pos[0];
+    else if (sel_less(hi, key)) ++pos[1];
+    else ++pos[2];
+  }
+  int tot[3];
+  block_exclusive_scan3(pos, tot, sh);
+  // Positions are capped at the list sizes the host derived from the counts;
+  // an exact select never reaches the caps.
+  const int n_P = c_low, n_C = c_high - c_low, n_R = n - c_high;
+  for (int i = base; i < end; ++i) {
+    const unsigned long long key = sel_key(sh.vals[i], i);
+    if (sel_less(lo, key)) {
+      if (pos[0] < n_P) P[pos[0]] = i;
+      ++pos[0];
+    } else if (sel_less(hi, key)) {
+      if (pos[1] < n_C) C[pos[1]] = i;
+      ++pos[1];
+    } else {
+      if (pos[2] < n_R) R[pos[2]] = i;
+      ++pos[2];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- host
+struct PrefillPlan {
+  int64_t rows_per_chunk;
+  int n_chunks;
+  int col_blocks;
+};
+
+static PrefillPlan plan_prefill(int64_t n_tokens, int32_t d, int vec) {
+  PrefillPlan p;
+  p.col_blocks = (d + 64 * vec - 1) / (64 * vec);
+  // About 2048 single-wave blocks, at least 16 rows per chunk, at most 512 chunks.
+  int64_t want_chunks = (2048 + p.col_blocks - 1) / p.col_blocks;
+  int64_t max_chunks = (n_tokens + 15) / 16;
+  if (want_chunks > max_chunks) want_chunks = max_chunks;
+  if (want_chunks > 512) want_chunks = 512;
+  if (want_chunks < 1) want_chunks = 1;
+  p.rows_per_chunk = (n_tokens + want_chunks - 1) / want_chunks;
+  if (p.rows_per_chunk < 1) p.rows_per_chunk = 1;
+  p.n_chunks = (int)((n_tokens + p.rows_per_chunk - 1) / p.rows_per_chunk);
+  if (p.n_chunks < 1) p.n_chunks = 1;
+  return p;
+}
+
+}  // namespace pop
+
+using namespace pop;
+
+extern "C" size_t pop_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff) {
+  if (n_tokens < 0 || d <= 0 || d_ff <= 0) return 0;
+  // Widest plan over both dtypes (bf16 has fewer column blocks, hence more chunks).
+  const PrefillPlan p = plan_prefill(n_tokens, d, 8);
+  const PrefillPlan q = plan_prefill(n_tokens, d, 4);
+  const int chunks = p.n_chunks > q.n_chunks ? p.n_chunks : q.n_chunks;
+  size_t b = align_up((size_t)chunks * d * sizeof(float), 256);  // partial sums
+  b += align_up((size_t)d * sizeof(float), 256);                 // s2
+  b += align_up((size_t)d_ff * sizeof(float), 256);              // importance scratch
+  return b;
+}
+
+extern "C" pop_status pop_prefill_partition(const void* X, int64_t n_tokens, int32_t d, const void* W_up,
+                                            int32_t d_ff, pop_dtype dt, double r, double gamma, int32_t* R,
+                                            int32_t* C, int32_t* P, float* importance, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  clear_error();
+  pop_status s = check_dtype_width(dt, d);
+  if (s != POP_OK) return s;
+  if ((s = check_rate(r, gamma)) != POP_OK) return s;
+  if (d_ff < 1 || d_ff > POP_MAX_D_FF) return fail(POP_ERR_BAD_SHAPE, "d_ff=%d outside [1, %d]", d_ff, POP_MAX_D_FF);
+  if (n_tokens < 0 || n_tokens > ((int64_t)1 << 40) / d)
+    return fail(POP_ERR_BAD_SHAPE, "n_tokens=%lld out of range", (long long)n_tokens);
+  if ((n_tokens > 0 && X == nullptr) || W_up == nullptr || ws == nullptr)
+    return fail(POP_ERR_INVALID_ARGUMENT, "X, W_up and ws must be non-NULL");
+  const pop_counts c = counts(d_ff, r, gamma);
+  if ((c.n_R > 0 && R == nullptr) || (c.n_C > 0 && C == nullptr) || (c.n_P > 0 && P == nullptr))
+    return fail(POP_ERR_INVALID_ARGUMENT, "an output list with a nonzero size is NULL");
+  if (!aligned16(X) || !aligned16(W_up) || !aligned16(ws) || !aligned16(importance))
+    return fail(POP_ERR_MISALIGNED, "X, W_up, importance and ws must be 16-byte aligned");
+  const size_t need = pop_prefill_workspace_bytes(n_tokens, d, d_ff);
+  if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+
+  const int vec = dt == POP_BF16 ? 8 : 4;
+  const PrefillPlan p = plan_prefill(n_tokens, d, vec);
+  char* w = (char*)ws;
+  float* partial = (float*)w;
+  const PrefillPlan pb = plan_prefill(n_tokens, d, 8), pf = plan_prefill(n_tokens, d, 4);
+  const int max_chunks = pb.n_chunks > pf.n_chunks ? pb.n_chunks : pf.n_chunks;
+  w += align_up((size_t)max_chunks * d * sizeof(float), 256);
+  float* s2 = (float*)w;
+  w += align_up((size_t)d * sizeof(float), 256);
+  float* I = importance ? importance : (float*)w;
+
+  hipStream_t st = (hipStream_t)stream;
+  if (n_tokens > 0) {
+    dim3 g1(p.col_blocks, p.n_chunks);
+    if (dt == POP_BF16)
+      hipLaunchKernelGGL(k_colsq_partial<bf16s>, g1, dim3(64), 0, st, (const bf16s*)X, n_tokens, d, p.rows_per_chunk, partial);
+    else
+      hipLaunchKernelGGL(k_colsq_partial<float>, g1, dim3(64), 0, st, (const float*)X, n_tokens, d, p.rows_per_chunk, partial);
+    hipLaunchKernelGGL(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(256), 0, st, (const float*)partial, p.n_chunks,
+                       (int64_t)d, s2);
+  } else {
+    // No prompt token: s = 0, hence I = 0 (n_chunks = 0 sums nothing).
+    hipLaunchKernelGGL(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(256), 0, st, (const float*)partial, 0, (int64_t)d, s2);
+  }
+  const int g2 = (d_ff + 3) / 4;
+  const size_t lds2 = (size_t)d * sizeof(float);
+  if (dt == POP_BF16)
+    hipLaunchKernelGGL(k_importance<bf16s>, dim3(g2), dim3(256), lds2, st, (const bf16s*)W_up, d_ff, d, (const float*)s2, I);
+  else
+    hipLaunchKernelGGL(k_importance<float>, dim3(g2), dim3(256), lds2, st, (const float*)W_up, d_ff, d, (const float*)s2, I);
+  hipLaunchKernelGGL(k_partition, dim3(1), dim3(kSelThreads), 0, st, (const float*)I, d_ff, c.c_low, c.c_high, R, C, P);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(POP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return POP_OK;
+}

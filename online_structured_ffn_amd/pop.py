@@ -1,0 +1,183 @@
+"""Thin ctypes binding of libpop (declared in include/pop.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libpop.so.  Importing this module loads the library and raises ImportError
+when it has not been built (run ``python -m online_structured_ffn_amd.build``);
+there is no fallback.  Tensors are torch tensors on the current HIP device;
+work is enqueued on ``stream`` (default: torch's current stream).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpop.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "pop.h")
+
+POP_F32, POP_BF16 = 0, 1
+_c_i32, _c_i64, _c_dbl, _c_size, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_size_t, ctypes.c_void_p
+
+
+class PopCounts(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("d_ff", "c_low", "c_high", "n_P", "n_C", "n_R", "n_live", "k")]
+
+
+class PopError(RuntimeError):
+    def __init__(self, func, status, detail):
+        self.status = status
+        super().__init__(f"{func}: {status_string(status)}: {detail}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m online_structured_ffn_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "pop_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "pop_last_error": (ctypes.c_char_p, []),
+        "pop_partition_counts": (ctypes.c_int, [_c_i32, _c_dbl, _c_dbl, ctypes.POINTER(PopCounts)]),
+        "pop_prefill_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32]),
+        "pop_prefill_partition": (ctypes.c_int, [_c_vp, _c_i64, _c_i32, _c_vp, _c_i32, ctypes.c_int, _c_dbl, _c_dbl,
+                                                 _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
+        "pop_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32]),
+        "pop_decode_ffn": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
+                                          _c_vp, _c_i32, _c_vp, _c_i32, _c_dbl, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
+        "pop_dense_ffn_decode": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
+                                                _c_vp, _c_vp, _c_size, _c_vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def declared_functions() -> list[str]:
+    """Every function include/pop.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(pop_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def status_string(status: int) -> str:
+    return lib.pop_status_string(int(status)).decode()
+
+
+def _check(func: str, status: int):
+    if status != 0:
+        raise PopError(func, status, lib.pop_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype(t) -> int:
+    if t.dtype == torch.float32:
+        return POP_F32
+    if t.dtype == torch.bfloat16:
+        return POP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+# ---------------------------------------------------------------- host-only
+def pop_partition_counts(d_ff: int, r: float, gamma: float) -> dict:
+    c = PopCounts()
+    _check("pop_partition_counts", lib.pop_partition_counts(int(d_ff), float(r), float(gamma), ctypes.byref(c)))
+    return {n: getattr(c, n) for n, _ in PopCounts._fields_}
+
+
+def pop_prefill_workspace_bytes(n_tokens: int, d: int, d_ff: int) -> int:
+    return int(lib.pop_prefill_workspace_bytes(int(n_tokens), int(d), int(d_ff)))
+
+
+def pop_decode_workspace_bytes(batch: int, d: int, d_ff: int) -> int:
+    return int(lib.pop_decode_workspace_bytes(int(batch), int(d), int(d_ff)))
+
+
+def workspace(nbytes: int, device=None) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device or "cuda")
+
+
+# ---------------------------------------------------------------- device calls
+def pop_prefill_partition(X, W_up, r: float, gamma: float, *, importance: bool = False, out=None,
+                          ws=None, stream=None):
+    """(R, C, P[, I]) for prompt activations X [n_tokens, d] and W_up [d_ff, d]."""
+    _dev(X, W_up)
+    n_tokens, d = X.shape
+    d_ff = W_up.shape[0]
+    if W_up.shape[1] != d or X.dtype != W_up.dtype:
+        raise ValueError("X and W_up disagree in width or dtype")
+    c = pop_partition_counts(d_ff, r, gamma)
+    dev = W_up.device
+    if out is None:
+        R = torch.empty(c["n_R"], dtype=torch.int32, device=dev)
+        C = torch.empty(c["n_C"], dtype=torch.int32, device=dev)
+        P = torch.empty(c["n_P"], dtype=torch.int32, device=dev)
+        I = torch.empty(d_ff, dtype=torch.float32, device=dev) if importance else None
+    else:
+        R, C, P, I = out
+    if ws is None:
+        ws = workspace(pop_prefill_workspace_bytes(n_tokens, d, d_ff), dev)
+    _check("pop_prefill_partition", lib.pop_prefill_partition(
+        _ptr(X), n_tokens, d, _ptr(W_up), d_ff, _dtype(W_up), float(r), float(gamma),
+        _ptr(R), _ptr(C), _ptr(P), _ptr(I), _ptr(ws), ws.numel(), _stream(stream)))
+    return (R, C, P, I) if importance else (R, C, P)
+
+
+def pop_decode_ffn(x, W_gate, W_up, W_downT, R, C, r: float, *, y=None, selected: bool = False,
+                   ws=None, stream=None):
+    """y [batch, d] (fp32) for one decode step; optionally also the selected candidates."""
+    _dev(x, W_gate, W_up, W_downT, R, C)
+    batch, d = x.shape
+    d_ff = W_gate.shape[0]
+    dev = W_gate.device
+    if y is None:
+        y = torch.empty((batch, d), dtype=torch.float32, device=dev)
+    S = None
+    if selected:
+        S = torch.empty(_k(d_ff, r, R.numel(), C.numel()), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(pop_decode_workspace_bytes(batch, d, d_ff), dev)
+    _check("pop_decode_ffn", lib.pop_decode_ffn(
+        _ptr(x), batch, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
+        _ptr(R), R.numel(), _ptr(C), C.numel(), float(r), _ptr(y), _ptr(S), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return (y, S) if selected else y
+
+
+def _k(d_ff, r, n_R, n_C):
+    live = pop_partition_counts(d_ff, r, 0.0)["n_live"]
+    return max(0, min(live - n_R, n_C))
+
+
+def pop_dense_ffn_decode(x, W_gate, W_up, W_downT, *, y=None, ws=None, stream=None):
+    _dev(x, W_gate, W_up, W_downT)
+    batch, d = x.shape
+    d_ff = W_gate.shape[0]
+    dev = W_gate.device
+    if y is None:
+        y = torch.empty((batch, d), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(pop_decode_workspace_bytes(batch, d, d_ff), dev)
+    _check("pop_dense_ffn_decode", lib.pop_dense_ffn_decode(
+        _ptr(x), batch, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
+        _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    return y

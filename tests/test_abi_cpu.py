@@ -1,0 +1,103 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/pop.h declares, and its host-only logic (counts, argument
+validation, workspace sizing) behaves as documented.  No call here reaches the
+device: every device entry point is called with arguments that fail
+validation, which happens before anything is enqueued."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from online_structured_ffn_amd import pop
+
+OK, INVALID, DTYPE, SHAPE, MISALIGNED, WS = 0, 1, 2, 3, 4, 5
+
+
+def test_exports_every_declared_symbol():
+    names = pop.declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(pop.lib, n), n
+
+
+def test_counts_match_oracle_everywhere():
+    g = np.random.default_rng(0)
+    for _ in range(3000):
+        n = int(g.integers(1, 32769))
+        r = float(g.uniform(0, 0.999))
+        gam = float(g.uniform(0, 0.999))
+        if g.integers(4) == 0:  # exact binary fractions hit the rounding halves
+            r = float(g.integers(0, 64)) / 64
+            gam = float(g.integers(0, 64)) / 64
+            if r >= 1.0:
+                continue
+        got = pop.pop_partition_counts(n, r, gam)
+        exp = oracle.partition_counts(n, r, gam)
+        for k in ("c_low", "c_high", "n_P", "n_C", "n_R", "n_live", "k"):
+            assert got[k] == exp[k], (n, r, gam, k, got, exp)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 0.3, 0.1), SHAPE), ((32769, 0.3, 0.1), SHAPE), ((10, -0.1, 0.1), INVALID),
+    ((10, 1.0, 0.1), INVALID), ((10, 0.3, -0.01), INVALID), ((10, 0.3, 1.0), INVALID),
+    ((10, float("nan"), 0.1), INVALID),
+])
+def test_counts_errors(args, status):
+    c = pop.PopCounts()
+    assert pop.lib.pop_partition_counts(*args, ctypes.byref(c)) == status
+    assert pop.lib.pop_last_error().decode() != ""
+
+
+def test_counts_null_out():
+    assert pop.lib.pop_partition_counts(10, 0.3, 0.1, None) == INVALID
+    assert pop.status_string(INVALID) == "POP_ERR_INVALID_ARGUMENT"
+    assert pop.status_string(99) == "POP_ERR_UNKNOWN"
+
+
+def test_workspace_sizes():
+    assert pop.pop_prefill_workspace_bytes(512, 4096, 11008) >= 4 * (4096 + 11008)
+    assert pop.pop_prefill_workspace_bytes(0, 256, 688) > 0
+    assert pop.pop_prefill_workspace_bytes(-1, 256, 688) == 0
+    a = pop.pop_decode_workspace_bytes(1, 4096, 11008)
+    b = pop.pop_decode_workspace_bytes(16, 4096, 11008)
+    assert 0 < a < b
+    assert pop.pop_decode_workspace_bytes(0, 4096, 11008) > 0
+
+
+A = 1 << 20   # a fake, 16-byte-aligned "device address": never dereferenced (validation fails first)
+
+
+def _prefill(X=A, n=16, d=256, W=A, d_ff=688, dt=0, r=0.3, g=0.1, R=A, C=A, P=A, I=None, ws=A, wsb=1 << 30):
+    return pop.lib.pop_prefill_partition(X, n, d, W, d_ff, dt, r, g, R, C, P, I, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), DTYPE), (dict(d=0), SHAPE), (dict(d=250), SHAPE), (dict(d=12, dt=1), SHAPE),
+    (dict(d_ff=0), SHAPE), (dict(d_ff=40000), SHAPE), (dict(n=-1), SHAPE), (dict(r=1.5), INVALID),
+    (dict(X=None), INVALID), (dict(W=None), INVALID), (dict(R=None), INVALID), (dict(ws=None), INVALID),
+    (dict(X=A + 4), MISALIGNED), (dict(I=A + 8), MISALIGNED), (dict(wsb=16), WS),
+])
+def test_prefill_validation(kw, status):
+    assert _prefill(**kw) == status
+    assert pop.lib.pop_last_error().decode()
+
+
+def _decode(x=A, b=1, d=256, Wg=A, Wu=A, Wd=A, d_ff=688, dt=0, R=A, nR=413, C=A, nC=137, r=0.3, y=A, S=None,
+            ws=A, wsb=1 << 30):
+    return pop.lib.pop_decode_ffn(x, b, d, Wg, Wu, Wd, d_ff, dt, R, nR, C, nC, r, y, S, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=3), DTYPE), (dict(d=4, dt=1), SHAPE), (dict(b=-1), SHAPE), (dict(b=100000), SHAPE),
+    (dict(nR=600), INVALID), (dict(nR=-1), INVALID), (dict(R=None), INVALID), (dict(x=None), INVALID),
+    (dict(Wd=A + 2), MISALIGNED), (dict(y=A + 4), MISALIGNED), (dict(wsb=100), WS), (dict(r=1.0), INVALID),
+])
+def test_decode_validation(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_dense_decode_validation():
+    f = pop.lib.pop_dense_ffn_decode
+    assert f(A, 1, 256, A, A, A, 688, 0, A, A, 10, None) == WS
+    assert f(A, 1, 256, None, A, A, 688, 0, A, A, 1 << 30, None) == INVALID

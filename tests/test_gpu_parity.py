@@ -1,0 +1,237 @@
+"""HIP path against the CPU oracle (through the C ABI), on seeded inputs.
+
+Small cases span several tiles with ragged tails and the degenerate cases of
+the method; full-size cases use the workloads' real shapes.  The comparison
+protocol is in tests/parity.py."""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from online_structured_ffn_amd import configs, pop, synth
+from tests.parity import check_decode, check_partition, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    yield
+    torch.cuda.synchronize()
+
+
+def _partition_case(X, W_up, dtype, r, gamma):
+    Xd, Wd = dev(X, dtype), dev(W_up, dtype)
+    R, C, P, I = pop.pop_prefill_partition(Xd, Wd, r, gamma, importance=True)
+    torch.cuda.synchronize()
+    I_ref = oracle.importance(W_up, oracle.column_norm(X))
+    n_ex = check_partition(R, C, P, I, I_ref, r, gamma)
+    return (host(R), host(C), host(P)), n_ex
+
+
+PART_CASES = [
+    # name, n_tokens, d, d_ff, dtype, r, gamma
+    ("f32_several_tiles", 300, 1028, 2053, "f32", 0.45, 0.15),
+    ("bf16_ragged", 37, 264, 1000, "bf16", 0.3, 0.1),
+    ("bf16_r0_dense", 20, 128, 333, "bf16", 0.0, 0.1),
+    ("bf16_gamma0_no_candidates", 20, 128, 333, "bf16", 0.4, 0.0),
+    ("f32_window_clamped", 20, 64, 97, "f32", 0.5, 0.6),
+    ("bf16_d_ff_1", 5, 8, 1, "bf16", 0.3, 0.1),
+    ("f32_d_ff_3", 5, 8, 3, "f32", 0.5, 0.2),
+    ("bf16_empty_prompt", 0, 128, 500, "bf16", 0.3, 0.1),
+    ("bf16_max_d_ff", 4, 64, 32768, "bf16", 0.3, 0.1),
+    ("bf16_max_d", 3, 16384, 40, "bf16", 0.3, 0.1),
+    ("f32_long_prompt", 5000, 256, 700, "f32", 0.25, 0.1),
+]
+
+
+@pytest.mark.parametrize("name,n,d,d_ff,dtype,r,gamma", PART_CASES, ids=[c[0] for c in PART_CASES])
+def test_partition_small(name, n, d, d_ff, dtype, r, gamma):
+    say(f"[partition] {name} n={n} d={d} d_ff={d_ff} {dtype} r={r} gamma={gamma}")
+    c = synth.random_case(zlib.crc32(name.encode()) % 1000, n, d, d_ff, 1, dtype)
+    _, n_ex = _partition_case(c["X"], c["W_up"], dtype, r, gamma)
+    say(f"  near-tie exclusions: {n_ex}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_partition_exact_ties(dtype):
+    """Small-integer inputs: every I^2 is an exact small integer on both sides,
+    so the device partition must equal the fp64 oracle exactly, ties included."""
+    g = np.random.default_rng(7)
+    X = g.integers(-1, 2, (9, 64)).astype(np.float32)
+    W = g.integers(-2, 3, (777, 64)).astype(np.float32)
+    say(f"[partition ties] {dtype}")
+    (R, C, P), n_ex = _partition_case(X, W, dtype, 0.3, 0.1)
+    assert n_ex == 0
+    I = oracle.importance(W, oracle.column_norm(X))
+    assert len(np.unique(I)) < len(I) // 2   # the case really has many ties
+    eR, eC, eP = oracle.partition(I, 0.3, 0.1)
+    assert np.array_equal(R, eR) and np.array_equal(C, eC) and np.array_equal(P, eP)
+
+
+def test_partition_zero_prompt_is_index_order():
+    say("[partition] all-zero prompt")
+    X = np.zeros((8, 32), np.float32)
+    W = np.ones((101, 32), np.float32)
+    (R, C, P), _ = _partition_case(X, W, "f32", 0.3, 0.1)
+    cnt = oracle.partition_counts(101, 0.3, 0.1)
+    assert list(R) == list(range(cnt["n_R"]))
+    assert list(P) == list(range(101 - cnt["n_P"], 101))
+
+
+def test_partition_deterministic():
+    c = synth.random_case(11, 700, 1024, 3001, 1, "bf16")
+    Xd, Wd = dev(c["X"], "bf16"), dev(c["W_up"], "bf16")
+    outs = [pop.pop_prefill_partition(Xd, Wd, 0.3, 0.1, importance=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ decode
+def _decode_case(X, x_steps, w, dtype, r, gamma, label):
+    Xd = dev(X, dtype)
+    Wg, Wu, WdT = dev(w["W_gate"], dtype), dev(w["W_up"], dtype), dev(w["W_downT"], dtype)
+    R, C, P, I = pop.pop_prefill_partition(Xd, Wu, r, gamma, importance=True)
+    torch.cuda.synchronize()
+    I_ref = oracle.importance(w["W_up"], oracle.column_norm(X))
+    check_partition(R, C, P, I, I_ref, r, gamma)
+    Rh, Ch = host(R), host(C)
+    errs = []
+    for t, x in enumerate(x_steps):
+        xd = dev(x, dtype)
+        ws = pop.workspace(pop.pop_decode_workspace_bytes(x.shape[0], x.shape[1], w["W_gate"].shape[0]))
+        y, S = pop.pop_decode_ffn(xd, Wg, Wu, WdT, R, C, r, selected=True, ws=ws)
+        torch.cuda.synchronize()
+        err, n_ex = check_decode(y, S, ws, x, w, Rh, Ch, r, dtype)
+        errs.append(err)
+        say(f"  {label} step {t}: rel err {err:.2e}, near-tie exclusions {n_ex}")
+    return errs
+
+
+DEC_CASES = [
+    # name, n_tokens, d, d_ff, batch, dtype, r, gamma
+    ("f32_b1", 16, 256, 688, 1, "f32", 0.3, 0.1),
+    ("bf16_ragged_b1", 37, 264, 1000, 1, "bf16", 0.3, 0.1),
+    ("bf16_b3", 50, 520, 1501, 3, "bf16", 0.3, 0.1),
+    ("f32_b5_tiles", 40, 1028, 999, 5, "f32", 0.5, 0.1),
+    ("bf16_b9", 30, 1032, 2000, 9, "bf16", 0.299, 0.1),
+    ("bf16_b0", 12, 256, 500, 0, "bf16", 0.3, 0.1),
+    ("bf16_r0", 12, 256, 500, 2, "bf16", 0.0, 0.1),
+    ("bf16_gamma0", 12, 256, 500, 2, "bf16", 0.4, 0.0),
+    ("f32_high_r", 12, 128, 300, 1, "f32", 0.95, 0.1),
+]
+
+
+@pytest.mark.parametrize("name,n,d,d_ff,b,dtype,r,gamma", DEC_CASES, ids=[c[0] for c in DEC_CASES])
+def test_decode_small(name, n, d, d_ff, b, dtype, r, gamma):
+    say(f"[decode] {name} d={d} d_ff={d_ff} B={b} {dtype} r={r} gamma={gamma}")
+    c = synth.random_case(zlib.crc32(name.encode()) % 1000, n, d, d_ff, b, dtype)
+    xs = [c["x"], synth.random_case(zlib.crc32(name.encode()) % 1000 + 1, 1, d, 1, b, dtype)["x"]]
+    _decode_case(c["X"], xs, c, dtype, r, gamma, name)
+
+
+def test_decode_zero_input_selects_lowest_candidates():
+    say("[decode] x = 0")
+    c = synth.random_case(5, 20, 256, 640, 2, "bf16")
+    x = np.zeros((2, 256), np.float32)
+    Xd = dev(c["X"], "bf16")
+    Wg, Wu, WdT = dev(c["W_gate"], "bf16"), dev(c["W_up"], "bf16"), dev(c["W_downT"], "bf16")
+    R, C, P = pop.pop_prefill_partition(Xd, Wu, 0.3, 0.1)
+    y, S = pop.pop_decode_ffn(dev(x, "bf16"), Wg, Wu, WdT, R, C, 0.3, selected=True)
+    torch.cuda.synchronize()
+    k = len(host(S))
+    assert np.array_equal(host(S), host(C)[:k])
+    assert float(y.abs().max()) == 0.0
+
+
+def test_dense_decode_matches_oracle():
+    for dtype, b in (("f32", 1), ("bf16", 4), ("bf16", 6)):
+        say(f"[dense decode] {dtype} B={b}")
+        c = synth.random_case(21 + b, 1, 520, 1300, b, dtype)
+        y = pop.pop_dense_ffn_decode(dev(c["x"], dtype), dev(c["W_gate"], dtype), dev(c["W_up"], dtype),
+                                     dev(c["W_downT"], dtype))
+        torch.cuda.synchronize()
+        ref = oracle.dense_ffn(c["x"], c["W_gate"], c["W_up"], c["W_down"])
+        err = np.abs(host(y) - ref).max() / np.abs(ref).max()
+        say(f"  rel err {err:.2e}")
+        assert err <= (1e-5 if dtype == "f32" else 2e-2)
+
+
+def test_r0_pruned_equals_dense():
+    say("[decode] r = 0 equals the dense FFN")
+    c = synth.random_case(31, 40, 512, 1111, 3, "bf16")
+    Xd, xd = dev(c["X"], "bf16"), dev(c["x"], "bf16")
+    Wg, Wu, WdT = dev(c["W_gate"], "bf16"), dev(c["W_up"], "bf16"), dev(c["W_downT"], "bf16")
+    R, C, P = pop.pop_prefill_partition(Xd, Wu, 0.0, 0.1)
+    assert P.numel() == 0
+    y = pop.pop_decode_ffn(xd, Wg, Wu, WdT, R, C, 0.0)
+    yd = pop.pop_dense_ffn_decode(xd, Wg, Wu, WdT)
+    torch.cuda.synchronize()
+    assert float((y - yd).abs().max()) <= 1e-5 * float(yd.abs().max())
+
+
+def test_decode_deterministic_and_graph_replay():
+    say("[decode] determinism and HIP-graph replay")
+    c = synth.random_case(41, 64, 1024, 2816, 2, "bf16")
+    Xd, xd = dev(c["X"], "bf16"), dev(c["x"], "bf16")
+    Wg, Wu, WdT = dev(c["W_gate"], "bf16"), dev(c["W_up"], "bf16"), dev(c["W_downT"], "bf16")
+    R, C, P = pop.pop_prefill_partition(Xd, Wu, 0.3, 0.1)
+    ws = pop.workspace(pop.pop_decode_workspace_bytes(2, 1024, 2816))
+    y0, S0 = pop.pop_decode_ffn(xd, Wg, Wu, WdT, R, C, 0.3, selected=True, ws=ws)
+    y1, S1 = pop.pop_decode_ffn(xd, Wg, Wu, WdT, R, C, 0.3, selected=True, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(S0, S1)
+    yg = torch.empty_like(y0)
+    Sg = torch.empty_like(S0)
+    x_in = xd.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pop.pop_decode_ffn(x_in, Wg, Wu, WdT, R, C, 0.3, y=yg, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pop.pop_decode_ffn(x_in, Wg, Wu, WdT, R, C, 0.3, y=yg, ws=ws)
+    x2 = dev(synth.random_case(42, 1, 1024, 1, 2, "bf16")["x"], "bf16")
+    y2 = pop.pop_decode_ffn(x2, Wg, Wu, WdT, R, C, 0.3)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        x_in.copy_(xd if rep % 2 == 0 else x2)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y0 if rep % 2 == 0 else y2), f"replay {rep} differs from eager"
+
+
+# ------------------------------------------------------------------ full-size workloads
+def test_tiny_workload_end_to_end():
+    w = configs.TINY
+    say(f"[workload] {w.name}")
+    wts = synth.layer_weights(w, 0)
+    X = synth.prompt(w, 0)
+    xs = [synth.decode_input(w, 0, t) for t in range(w.decode_steps)]
+    _decode_case(X, xs, wts, w.dtype, w.r, w.gamma, w.name)
+
+
+@pytest.mark.parametrize("wname,layer,steps", [
+    ("llama2_7b_ffn_b1", 0, 2), ("llama2_7b_ffn_b1", 31, 1), ("qwen2_7b_ffn_b4", 5, 2), ("llama2_7b_ffn_b16", 0, 1),
+])
+def test_full_size_layer(wname, layer, steps):
+    w = configs.BY_NAME[wname]
+    say(f"[workload] {w.name} layer {layer}: generating inputs")
+    wts = synth.layer_weights(w, layer)
+    X = synth.prompt(w, layer)
+    sets = synth.drifting_outliers(w, layer, steps) if w.outlier_kind == "drift_scale" else None
+    xs = [synth.decode_input(w, layer, t, drift_sets=sets) for t in range(steps)]
+    say(f"  X {X.shape}, weights {wts['W_up'].shape}")
+    _decode_case(X, xs, wts, w.dtype, w.r, w.gamma, w.name)
