@@ -119,6 +119,36 @@ pop_status pop_prefill_partition(const void* X, int64_t n_tokens, int32_t d, con
                                   int32_t* C, int32_t* P, float* importance, void* ws,
                                   size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Stages of pop_prefill_partition, callable on their own.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes pop_prefill_importance needs. */
+size_t pop_prefill_importance_workspace_bytes(int64_t n_tokens, int32_t d);
+
+/*
+ * pop_prefill_importance — POP notes, "Key design 1", importance equation
+ * (read with row i of W_up; the Wanda-style |W| * ||X||_2 metric named in
+ * "Loss / training strategy").
+ *   importance  device fp32 [d_ff] output: I_i = sqrt(sum_k W_up[i,k]^2 s_k^2),
+ *               s_k^2 = sum over the n_tokens rows of X[:,k]^2.
+ * Other arguments as for pop_prefill_partition.
+ */
+pop_status pop_prefill_importance(const void* X, int64_t n_tokens, int32_t d, const void* W_up,
+                                  int32_t d_ff, pop_dtype dt, float* importance, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/*
+ * pop_partition_select — POP notes, "Key design 1", three-region split.
+ * Splits d_ff channels by their importance (device fp32 [d_ff], values >= 0)
+ * at the cut ranks of pop_partition_counts: P = the c_low least important,
+ * C = the next n_C, R = the rest (larger value more important; on equal values
+ * the lower index more important).  R, C, P: device int32, ascending.
+ * One workgroup; needs no workspace.
+ */
+pop_status pop_partition_select(const float* importance, int32_t d_ff, double r, double gamma,
+                                int32_t* R, int32_t* C, int32_t* P, void* stream);
+
 /* Workspace bytes pop_decode_ffn / pop_dense_ffn_decode need. */
 size_t pop_decode_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff);
 
@@ -150,6 +180,58 @@ pop_status pop_decode_ffn(const void* x, int32_t batch, int32_t d, const void* W
                           const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C,
                           double r, float* y, int32_t* selected, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Stages of pop_decode_ffn, callable on their own (also the building blocks of
+ * the static-mask and full re-evaluation variants of the POP notes' ablation
+ * table).
+ * ------------------------------------------------------------------------- */
+
+/*
+ * pop_decode_gateup — POP notes, "Key design 2": H_t = f(X_t; R u C), with f the
+ * gated MLP's first half (equation (1) of the batch-wise pruning page):
+ * z[b, p] = SiLU(W_gate[ch_p] . x_b) * (W_up[ch_p] . x_b) for the positions
+ * p < n_R + n_C, where ch_p = R[p] for p < n_R and C[p - n_R] after.
+ *   R == NULL means R = 0, 1, ..., n_R - 1 (then n_C must be 0): the dense
+ *   first half over all channels when n_R == d_ff.
+ *   z      device fp32 [batch, n_R + n_C] output.
+ *   score  optional device fp32 [n_C] output: max over b of |z[b, n_R + j]|.
+ */
+pop_status pop_decode_gateup(const void* x, int32_t batch, int32_t d, const void* W_gate,
+                             const void* W_up, int32_t d_ff, pop_dtype dt, const int32_t* R,
+                             int32_t n_R, const int32_t* C, int32_t n_C, float* z, float* score,
+                             void* stream);
+
+/*
+ * pop_decode_select — POP notes, "Key design 2": the candidates sorted by their
+ * step score, highest first (equal scores: lower position first), and the first
+ * k kept.
+ *   score      device fp32 [n_C], values >= 0.
+ *   C          device int32 [n_C]: the candidate channels.
+ *   positions  device int32 [k] output: the kept positions into C, ascending.
+ *   selected   device int32 [k] output: C[positions[j]].
+ * One workgroup; 0 <= k <= n_C <= POP_MAX_D_FF.
+ */
+pop_status pop_decode_select(const float* score, int32_t n_C, const int32_t* C, int32_t k,
+                             int32_t* positions, int32_t* selected, void* stream);
+
+/* Workspace bytes pop_decode_down needs for n_live = n_R + k rows. */
+size_t pop_decode_down_workspace_bytes(int32_t batch, int32_t d, int32_t n_live);
+
+/*
+ * pop_decode_down — POP notes, "Overall framework": the FFN finished on R plus
+ * the selected candidates: y[b, :] = sum over live rows of z[b, col] * W_downT[ch, :]
+ * with (ch, col) = (R[q], q) for q < n_R and (selected[j], n_R + positions[j])
+ * for j < k (the pop_decode_select outputs).  R == NULL means R = 0, ...,
+ * n_R - 1 (valid with k == 0).
+ *   z   device fp32 [batch, n_A] (the pop_decode_gateup output, n_A columns).
+ *   y   device fp32 [batch, d] output.
+ * The partial sums of row chunks are reduced in a fixed order: deterministic.
+ */
+pop_status pop_decode_down(const float* z, int32_t batch, int32_t n_A, const void* W_downT,
+                           int32_t d, int32_t d_ff, pop_dtype dt, const int32_t* R, int32_t n_R,
+                           const int32_t* selected, const int32_t* positions, int32_t k, float* y,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /*
  * pop_dense_ffn_decode — the unpruned gated MLP (equation (1) of the

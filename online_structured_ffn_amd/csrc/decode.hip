@@ -21,7 +21,6 @@ namespace pop {
 __device__ __forceinline__ int clamp_channel(int ch, int d_ff) { return min(max(ch, 0), d_ff - 1); }
 
 __device__ __forceinline__ int gateup_channel(const int32_t* R, int n_R, const int32_t* C, int p, int d_ff) {
-  if (R == nullptr) return p;
   return clamp_channel(p < n_R ? R[p] : C[p - n_R], d_ff);
 }
 
@@ -30,7 +29,9 @@ __device__ __forceinline__ int gateup_channel(const int32_t* R, int n_R, const i
 // Each lane reads 16-byte vectors of the gate and up rows (two rows, U
 // vectors each in flight) and the matching vectors of x (cache-resident).
 // BT batch rows are accumulated per pass over the weights.
-template <typename T, int BT>
+// kIdentity: rows 0..n_R-1 in order (the dense baseline); a separate
+// instantiation so profiles tell the dense and pruned kernels apart.
+template <typename T, int BT, bool kIdentity>
 __global__ __launch_bounds__(256) void k_gateup(const T* __restrict__ x, int B, int d, const T* __restrict__ Wg,
                                                 const T* __restrict__ Wu, int d_ff, const int32_t* __restrict__ R,
                                                 int n_R, const int32_t* __restrict__ C, int n_C, float* __restrict__ z,
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void k_gateup(const T* __restrict__ x, int B, 
   const int wave = threadIdx.x >> 6;
   const int n_A = n_R + n_C;
   for (int p = blockIdx.x * 4 + wave; p < n_A; p += gridDim.x * 4) {
-    const int ch = gateup_channel(R, n_R, C, p, d_ff);
+    const int ch = kIdentity ? p : gateup_channel(R, n_R, C, p, d_ff);
     const T* wg = Wg + (int64_t)ch * d;
     const T* wu = Wu + (int64_t)ch * d;
     float smax = 0.f;
@@ -115,27 +116,29 @@ __global__ __launch_bounds__(256) void k_gateup(const T* __restrict__ x, int B, 
 
 // ---------------------------------------------------------------- K5
 // S = the k most important candidates (score descending, position ascending on
-// ties); written as ascending positions Q into C and, optionally, as channels.
-__global__ __launch_bounds__(kSelThreads) void k_topk(const float* __restrict__ score, int n, int k,
-                                                      const int32_t* __restrict__ C, int32_t* __restrict__ Q,
-                                                      int32_t* __restrict__ selected) {
-  __shared__ SelShared sh;
-  sel_load(score, n, sh);
+// ties), written in ascending order as positions into C and as channels.
+constexpr int kTopkThreads = 256;
+
+__global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ score, int n, int k,
+                                                       const int32_t* __restrict__ C, int32_t* __restrict__ positions,
+                                                       int32_t* __restrict__ selected) {
+  __shared__ SelShared<kTopkThreads> sh;
+  sel_load<kTopkThreads>(score, n, sh);
   const int ranks[1] = {n - k};
-  select_thresholds<1>(n, ranks, sh);
+  select_thresholds<kTopkThreads, 1>(n, ranks, sh);
   const SelTarget t = sh.tgt[0];
-  const int E = (n + kSelThreads - 1) / kSelThreads;
+  const int E = (n + kTopkThreads - 1) / kTopkThreads;
   const int base = threadIdx.x * E;
   const int end = min(n, base + E);
   int pos[3] = {0, 0, 0};
   for (int i = base; i < end; ++i)
     if (!sel_less(t, sel_key(sh.vals[i], i))) ++pos[0];
   int tot[3];
-  block_exclusive_scan3(pos, tot, sh);
+  block_exclusive_scan3<kTopkThreads>(pos, tot, sh);
   for (int i = base; i < end; ++i) {
     if (!sel_less(t, sel_key(sh.vals[i], i))) {
       if (pos[0] < k) {  // an exact select never reaches the cap
-        Q[pos[0]] = i;
+        positions[pos[0]] = i;
         if (selected != nullptr) selected[pos[0]] = C[i];
       }
       ++pos[0];
@@ -144,20 +147,24 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------- K6
-// Block: 256 threads = 4 waves sharing one column slice of 64*V columns; the
-// block's chunk of live rows is dealt round-robin to the waves, each lane
-// reading one 16-byte vector per row (a wave reads 1 KB of a bf16 row).  The
-// four wave accumulators are combined in wave order through LDS and written as
-// this chunk's partial sum.
-template <typename T, int BT>
+// Block: 256 threads = 4 waves sharing one column slice of 64*V columns.  The
+// block owns a chunk of live rows; wave w takes rows q0 + w, q0 + w + 4, ...
+// Each wave first loads the channel and z column of up to 64 of its rows in one
+// coalesced load (lane l holds row l), then streams the rows U at a time, each
+// lane reading one 16-byte vector of every row (a wave reads 1 KB of a bf16
+// row).  Live row q is (ch, zcol) = (R[q], q) for q < n_R and
+// (sel[q - n_R], n_R + pos[q - n_R]) after; with kIdentity it is (q, q).
+// The four wave accumulators are combined in wave order through LDS and written
+// as this chunk's partial sum.
+template <typename T, int BT, bool kIdentity>
 __global__ __launch_bounds__(256) void k_down_partial(const float* __restrict__ z, int n_A, int B,
                                                       const T* __restrict__ WdT, int d, int d_ff,
-                                                      const int32_t* __restrict__ R,
-                                                      int n_R, const int32_t* __restrict__ C,
-                                                      const int32_t* __restrict__ Q, int n_live, int rows_per_chunk,
-                                                      float* __restrict__ partial) {
+                                                      const int32_t* __restrict__ R, int n_R,
+                                                      const int32_t* __restrict__ sel,
+                                                      const int32_t* __restrict__ pos, int n_live,
+                                                      int rows_per_chunk, float* __restrict__ partial) {
   constexpr int V = Vec<T>::N;
-  constexpr int U = 4;
+  constexpr int U = BT == 1 ? 16 : 8;
   __shared__ float red[3][BT * V][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -165,70 +172,53 @@ __global__ __launch_bounds__(256) void k_down_partial(const float* __restrict__ 
   const bool on = col < d;
   const int q0 = blockIdx.y * rows_per_chunk;
   const int q1 = min(n_live, q0 + rows_per_chunk);
+  const int my_rows = q1 - q0 - wave > 0 ? (q1 - q0 - wave + 3) / 4 : 0;
   for (int b0 = 0; b0 < B; b0 += BT) {
     float acc[BT][V];
 #pragma unroll
     for (int b = 0; b < BT; ++b)
 #pragma unroll
       for (int v = 0; v < V; ++v) acc[b][v] = 0.f;
-    int q = q0 + wave;
-    for (; q + 4 * (U - 1) < q1; q += 4 * U) {
-      int ch[U], zp[U];
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const int qq = q + 4 * j;
-        if (R == nullptr) {
-          ch[j] = qq;
-          zp[j] = qq;
-        } else if (qq < n_R) {
-          ch[j] = clamp_channel(R[qq], d_ff);
-          zp[j] = qq;
+    for (int r0 = 0; r0 < my_rows; r0 += 64) {
+      // lane l: index of this wave's row r0 + l
+      const int ql = q0 + wave + 4 * (r0 + lane);
+      int ch_l = 0, zc_l = 0;
+      if (r0 + lane < my_rows) {
+        if (kIdentity) {
+          ch_l = ql;
+          zc_l = ql;
+        } else if (ql < n_R) {
+          ch_l = clamp_channel(R[ql], d_ff);
+          zc_l = ql;
         } else {
-          const int pj = Q[qq - n_R];
-          ch[j] = clamp_channel(C[pj], d_ff);
-          zp[j] = n_R + pj;
+          ch_l = clamp_channel(sel[ql - n_R], d_ff);
+          zc_l = n_R + min(max(pos[ql - n_R], 0), n_A - n_R - 1);
         }
       }
-      u32x4 w[U];
+      const int cnt = min(64, my_rows - r0);
+      for (int j = 0; j < cnt; j += U) {
+        u32x4 w[U];
+        int zc[U];
 #pragma unroll
-      for (int j = 0; j < U; ++j)
-        if (on) w[j] = ld16_stream(WdT + (int64_t)ch[j] * d + col);
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        float f[V];
-        if (on) unpack(w[j], f, T{});
-#pragma unroll
-        for (int b = 0; b < BT; ++b) {
-          if (b0 + b < B && on) {
-            const float zb = z[(int64_t)(b0 + b) * n_A + zp[j]];
-#pragma unroll
-            for (int v = 0; v < V; ++v) acc[b][v] = fmaf(zb, f[v], acc[b][v]);
-          }
+        for (int u = 0; u < U; ++u) {
+          const int src = j + u < 64 ? j + u : 63;  // lanes past cnt are never used
+          const int ch = __builtin_amdgcn_readlane(ch_l, src);
+          zc[u] = __builtin_amdgcn_readlane(zc_l, src);
+          if (on && j + u < cnt) w[u] = ld16_stream(WdT + (int64_t)ch * d + col);
         }
-      }
-    }
-    for (; q < q1; q += 4) {
-      int ch, zpp;
-      if (R == nullptr) {
-        ch = q;
-        zpp = q;
-      } else if (q < n_R) {
-        ch = clamp_channel(R[q], d_ff);
-        zpp = q;
-      } else {
-        const int pj = Q[q - n_R];
-        ch = clamp_channel(C[pj], d_ff);
-        zpp = n_R + pj;
-      }
-      if (on) {
-        float f[V];
-        unpack(ld16_stream(WdT + (int64_t)ch * d + col), f, T{});
 #pragma unroll
-        for (int b = 0; b < BT; ++b) {
-          if (b0 + b < B) {
-            const float zb = z[(int64_t)(b0 + b) * n_A + zpp];
+        for (int u = 0; u < U; ++u) {
+          if (on && j + u < cnt) {
+            float f[V];
+            unpack(w[u], f, T{});
 #pragma unroll
-            for (int v = 0; v < V; ++v) acc[b][v] = fmaf(zb, f[v], acc[b][v]);
+            for (int b = 0; b < BT; ++b) {
+              if (b0 + b < B) {
+                const float zb = z[(int64_t)(b0 + b) * n_A + zc[u]];
+#pragma unroll
+                for (int v = 0; v < V; ++v) acc[b][v] = fmaf(zb, f[v], acc[b][v]);
+              }
+            }
           }
         }
       }
@@ -267,26 +257,46 @@ struct DownPlan {
   int rows_per_chunk;
 };
 
-static DownPlan plan_down(int n_live, int B, int d, int vec) {
-  DownPlan p;
-  p.col_blocks = (d + 64 * vec - 1) / (64 * vec);
-  int want = (1024 + p.col_blocks - 1) / p.col_blocks;     // ~1024 blocks of 4 waves
-  const int by_rows = (n_live + 15) / 16;                  // >= 16 rows per chunk
-  const int by_bytes = B > 0 ? (n_live + 8 * B - 1) / (8 * B) : want;  // partials <= ~1/4 of the row bytes
+// Chunks of live rows for the down-projection: about 1024 blocks of 4 waves,
+// at least 16 rows per chunk, and partial sums kept under ~1/4 of the bytes
+// of the rows themselves.
+static int down_chunks_wanted(int n_live, int B, int d, int vec) {
+  const int col_blocks = (d + 64 * vec - 1) / (64 * vec);
+  int want = (1024 + col_blocks - 1) / col_blocks;
+  const int by_rows = (n_live + 15) / 16;
+  const int by_bytes = B > 0 ? (n_live + 8 * B - 1) / (8 * B) : want;
   if (want > by_rows) want = by_rows;
   if (want > by_bytes) want = by_bytes;
   if (want > 256) want = 256;
   if (want < 1) want = 1;
+  return want;
+}
+
+static DownPlan plan_down(int n_live, int B, int d, int vec) {
+  DownPlan p;
+  p.col_blocks = (d + 64 * vec - 1) / (64 * vec);
+  const int want = down_chunks_wanted(n_live, B, d, vec);
   p.rows_per_chunk = n_live > 0 ? (n_live + want - 1) / want : 1;
   p.n_chunks = n_live > 0 ? (n_live + p.rows_per_chunk - 1) / p.rows_per_chunk : 1;
   return p;
 }
 
+static size_t down_ws_bytes(int32_t batch, int32_t d, int32_t n_live) {
+  // The chunk count only grows with n_live; bf16 (fewer column blocks) wants at least as many as fp32.
+  const int c8 = down_chunks_wanted(n_live, batch, d, 8);
+  const int c4 = down_chunks_wanted(n_live, batch, d, 4);
+  const int chunks = c8 > c4 ? c8 : c4;
+  const int b = batch > 0 ? batch : 1;
+  return align_up((size_t)chunks * b * d * sizeof(float), 256);
+}
+
 struct DecodeWs {
   float* z;
   float* score;
-  int32_t* Q;
-  float* partial;
+  int32_t* Q;    // selected positions into C
+  int32_t* sel;  // selected channels
+  char* down;
+  size_t down_bytes;
 };
 
 static size_t decode_ws_layout(int32_t batch, int32_t d, int32_t d_ff, char* base, DecodeWs* out) {
@@ -294,77 +304,97 @@ static size_t decode_ws_layout(int32_t batch, int32_t d, int32_t d_ff, char* bas
   const size_t zb = align_up((size_t)batch * d_ff * sizeof(float) + 16, 256);
   const size_t sb = align_up((size_t)d_ff * sizeof(float), 256);
   const size_t qb = align_up((size_t)d_ff * sizeof(int32_t), 256);
-  if (out) out->z = (float*)(base + off);
-  off += zb;
-  if (out) out->score = (float*)(base + off);
-  off += sb;
-  if (out) out->Q = (int32_t*)(base + off);
-  off += qb;
-  if (out) out->partial = (float*)(base + off);
-  const int b = batch > 0 ? batch : 1;
-  off += align_up((size_t)256 * b * d * sizeof(float), 256);  // at most 256 chunks
-  return off;
+  const size_t db = down_ws_bytes(batch, d, d_ff);
+  if (out) {
+    out->z = (float*)(base + off);
+    out->score = (float*)(base + off + zb);
+    out->Q = (int32_t*)(base + off + zb + sb);
+    out->sel = (int32_t*)(base + off + zb + sb + qb);
+    out->down = base + off + zb + sb + 2 * qb;
+    out->down_bytes = db;
+  }
+  return zb + sb + 2 * qb + db;
 }
 
-template <typename T, int BT>
-static void launch_gateup(hipStream_t st, int grid, const void* x, int B, int d, const void* Wg, const void* Wu,
-                          int d_ff, const int32_t* R, int n_R, const int32_t* C, int n_C, float* z, float* score) {
-  hipLaunchKernelGGL((k_gateup<T, BT>), dim3(grid), dim3(256), 0, st, (const T*)x, B, d, (const T*)Wg,
-                     (const T*)Wu, d_ff, R, n_R, C, n_C, z, score);
+// ---- stage launchers (arguments already validated)
+template <typename T>
+static void launch_gateup(hipStream_t st, const void* x, int B, int d, const void* Wg, const void* Wu, int d_ff,
+                          const int32_t* R, int n_R, const int32_t* C, int n_C, float* z, float* score) {
+  const int n_A = n_R + n_C;
+  int grid = (n_A + 3) / 4;
+  if (grid < 1) grid = 1;
+#define POP_GATEUP(BT)                                                                                        \
+  if (R == nullptr)                                                                                           \
+    hipLaunchKernelGGL((k_gateup<T, BT, true>), dim3(grid), dim3(256), 0, st, (const T*)x, B, d, (const T*)Wg, \
+                       (const T*)Wu, d_ff, R, n_R, C, n_C, z, score);                                         \
+  else                                                                                                        \
+    hipLaunchKernelGGL((k_gateup<T, BT, false>), dim3(grid), dim3(256), 0, st, (const T*)x, B, d, (const T*)Wg, \
+                       (const T*)Wu, d_ff, R, n_R, C, n_C, z, score)
+  if (B <= 1) {
+    POP_GATEUP(1);
+  } else if (B <= 2) {
+    POP_GATEUP(2);
+  } else {
+    POP_GATEUP(4);
+  }
+#undef POP_GATEUP
 }
 
-template <typename T, int BT>
-static void launch_down(hipStream_t st, const DownPlan& p, const float* z, int n_A, int B, const void* WdT, int d,
-                        int d_ff, const int32_t* R, int n_R, const int32_t* C, const int32_t* Q, int n_live,
-                        float* partial) {
-  hipLaunchKernelGGL((k_down_partial<T, BT>), dim3(p.col_blocks, p.n_chunks), dim3(256), 0, st, z, n_A, B,
-                     (const T*)WdT, d, d_ff, R, n_R, C, Q, n_live, p.rows_per_chunk, partial);
+static void launch_select(hipStream_t st, const float* score, int n_C, const int32_t* C, int k, int32_t* Q,
+                          int32_t* selected) {
+  if (n_C > 0) hipLaunchKernelGGL(k_topk, dim3(1), dim3(kTopkThreads), 0, st, score, n_C, k, C, Q, selected);
 }
 
 template <typename T>
-static void run_decode(hipStream_t st, const void* x, int B, int d, int d_ff, const void* Wg, const void* Wu,
-                       const void* WdT, const int32_t* R, int n_R, const int32_t* C, int n_C, int k, float* y, int32_t* selected,
-                       const DecodeWs& w) {
-  const int n_A = n_R + n_C;
-  const int vec = Vec<T>::N;
-  int grid = (n_A + 3) / 4;
-  if (grid < 1) grid = 1;
-  if (B <= 1)
-    launch_gateup<T, 1>(st, grid, x, B, d, Wg, Wu, d_ff, R, n_R, C, n_C, w.z, w.score);
-  else if (B <= 2)
-    launch_gateup<T, 2>(st, grid, x, B, d, Wg, Wu, d_ff, R, n_R, C, n_C, w.z, w.score);
-  else
-    launch_gateup<T, 4>(st, grid, x, B, d, Wg, Wu, d_ff, R, n_R, C, n_C, w.z, w.score);
-  if (R != nullptr && n_C > 0)
-    hipLaunchKernelGGL(k_topk, dim3(1), dim3(kSelThreads), 0, st, (const float*)w.score, n_C, k, C, w.Q, selected);
-  const int n_live = n_R + k;
+static void launch_down(hipStream_t st, const float* z, int B, int n_A, const void* WdT, int d, int d_ff,
+                        const int32_t* R, int n_R, const int32_t* sel, const int32_t* Q, int k, float* y,
+                        float* partial) {
   if (B == 0) return;
-  const DownPlan p = plan_down(n_live, B, d, vec);
-  if (B <= 1)
-    launch_down<T, 1>(st, p, w.z, n_A, B, WdT, d, d_ff, R, n_R, C, w.Q, n_live, w.partial);
-  else if (B <= 2)
-    launch_down<T, 2>(st, p, w.z, n_A, B, WdT, d, d_ff, R, n_R, C, w.Q, n_live, w.partial);
-  else
-    launch_down<T, 4>(st, p, w.z, n_A, B, WdT, d, d_ff, R, n_R, C, w.Q, n_live, w.partial);
+  const int n_live = n_R + k;
+  const DownPlan p = plan_down(n_live, B, d, Vec<T>::N);
+#define POP_DOWN(BT)                                                                                          \
+  if (R == nullptr)                                                                                           \
+    hipLaunchKernelGGL((k_down_partial<T, BT, true>), dim3(p.col_blocks, p.n_chunks), dim3(256), 0, st, z, n_A, \
+                       B, (const T*)WdT, d, d_ff, R, n_R, sel, Q, n_live, p.rows_per_chunk, partial);        \
+  else                                                                                                        \
+    hipLaunchKernelGGL((k_down_partial<T, BT, false>), dim3(p.col_blocks, p.n_chunks), dim3(256), 0, st, z,    \
+                       n_A, B, (const T*)WdT, d, d_ff, R, n_R, sel, Q, n_live, p.rows_per_chunk, partial)
+  if (B <= 1) {
+    POP_DOWN(1);
+  } else if (B <= 2) {
+    POP_DOWN(2);
+  } else {
+    POP_DOWN(4);
+  }
+#undef POP_DOWN
   const int64_t n_out = (int64_t)B * d;
-  hipLaunchKernelGGL(k_sum_chunks<0>, dim3((unsigned)((n_out + 31) / 32)), dim3(256), 0, st, (const float*)w.partial,
+  hipLaunchKernelGGL(k_sum_chunks<0>, dim3((unsigned)((n_out + 31) / 32)), dim3(256), 0, st, (const float*)partial,
                      n_live > 0 ? p.n_chunks : 0, n_out, y);
 }
 
-static pop_status check_decode_common(const void* x, int32_t batch, int32_t d, const void* Wg, const void* Wu,
-                                      const void* WdT, int32_t d_ff, pop_dtype dt, float* y, void* ws,
-                                      size_t ws_bytes) {
+static pop_status launched() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(POP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return POP_OK;
+}
+
+// ---- validation
+static pop_status check_shape(int32_t batch, int32_t d, int32_t d_ff, pop_dtype dt) {
   pop_status s = check_dtype_width(dt, d);
   if (s != POP_OK) return s;
   if (d_ff < 1 || d_ff > POP_MAX_D_FF) return fail(POP_ERR_BAD_SHAPE, "d_ff=%d outside [1, %d]", d_ff, POP_MAX_D_FF);
   if (batch < 0 || batch > POP_MAX_BATCH) return fail(POP_ERR_BAD_SHAPE, "batch=%d outside [0, %d]", batch, POP_MAX_BATCH);
-  if ((batch > 0 && (x == nullptr || y == nullptr)) || Wg == nullptr || Wu == nullptr || WdT == nullptr ||
-      ws == nullptr)
-    return fail(POP_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
-  if (!aligned16(x) || !aligned16(Wg) || !aligned16(Wu) || !aligned16(WdT) || !aligned16(y) || !aligned16(ws))
-    return fail(POP_ERR_MISALIGNED, "x, weights, y and ws must be 16-byte aligned");
-  const size_t need = pop_decode_workspace_bytes(batch, d, d_ff);
-  if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  return POP_OK;
+}
+
+static pop_status check_lists(int32_t d_ff, const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C,
+                              bool r_may_be_identity) {
+  if (n_R < 0 || n_C < 0 || (int64_t)n_R + n_C > d_ff)
+    return fail(POP_ERR_INVALID_ARGUMENT, "n_R=%d, n_C=%d inconsistent with d_ff=%d", n_R, n_C, d_ff);
+  if ((n_R > 0 && R == nullptr && !r_may_be_identity) || (n_C > 0 && C == nullptr))
+    return fail(POP_ERR_INVALID_ARGUMENT, "R or C is NULL with a nonzero size");
+  if (R == nullptr && r_may_be_identity && n_C > 0 && n_R > 0)
+    return fail(POP_ERR_INVALID_ARGUMENT, "R == NULL (identity) is only valid with n_C == 0");
   return POP_OK;
 }
 
@@ -372,9 +402,66 @@ static pop_status check_decode_common(const void* x, int32_t batch, int32_t d, c
 
 using namespace pop;
 
+#define POP_DISPATCH(dt, FN, ...) \
+  ((dt) == POP_BF16 ? FN<bf16s>(__VA_ARGS__) : FN<float>(__VA_ARGS__))
+
 extern "C" size_t pop_decode_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff) {
   if (batch < 0 || d <= 0 || d_ff <= 0) return 0;
   return decode_ws_layout(batch, d, d_ff, nullptr, nullptr);
+}
+
+extern "C" size_t pop_decode_down_workspace_bytes(int32_t batch, int32_t d, int32_t n_live) {
+  if (batch < 0 || d <= 0 || n_live < 0) return 0;
+  return down_ws_bytes(batch, d, n_live > 0 ? n_live : 1);
+}
+
+extern "C" pop_status pop_decode_gateup(const void* x, int32_t batch, int32_t d, const void* W_gate,
+                                        const void* W_up, int32_t d_ff, pop_dtype dt, const int32_t* R,
+                                        int32_t n_R, const int32_t* C, int32_t n_C, float* z, float* score,
+                                        void* stream) {
+  clear_error();
+  pop_status s = check_shape(batch, d, d_ff, dt);
+  if (s != POP_OK) return s;
+  if ((s = check_lists(d_ff, R, n_R, C, n_C, true)) != POP_OK) return s;
+  if ((batch > 0 && (x == nullptr || z == nullptr)) || W_gate == nullptr || W_up == nullptr)
+    return fail(POP_ERR_INVALID_ARGUMENT, "x, z, W_gate and W_up must be non-NULL");
+  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up))
+    return fail(POP_ERR_MISALIGNED, "x and the weights must be 16-byte aligned");
+  POP_DISPATCH(dt, launch_gateup, (hipStream_t)stream, x, batch, d, W_gate, W_up, d_ff, R, n_R, C, n_C, z, score);
+  return launched();
+}
+
+extern "C" pop_status pop_decode_select(const float* score, int32_t n_C, const int32_t* C, int32_t k,
+                                        int32_t* positions, int32_t* selected, void* stream) {
+  clear_error();
+  if (n_C < 0 || n_C > POP_MAX_D_FF) return fail(POP_ERR_BAD_SHAPE, "n_C=%d outside [0, %d]", n_C, POP_MAX_D_FF);
+  if (k < 0 || k > n_C) return fail(POP_ERR_INVALID_ARGUMENT, "k=%d outside [0, n_C=%d]", k, n_C);
+  if (n_C > 0 && (score == nullptr || C == nullptr || (k > 0 && (positions == nullptr || selected == nullptr))))
+    return fail(POP_ERR_INVALID_ARGUMENT, "score, C, positions and selected must be non-NULL");
+  launch_select((hipStream_t)stream, score, n_C, C, k, positions, selected);
+  return launched();
+}
+
+extern "C" pop_status pop_decode_down(const float* z, int32_t batch, int32_t n_A, const void* W_downT, int32_t d,
+                                      int32_t d_ff, pop_dtype dt, const int32_t* R, int32_t n_R,
+                                      const int32_t* selected, const int32_t* positions, int32_t k, float* y,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  pop_status s = check_shape(batch, d, d_ff, dt);
+  if (s != POP_OK) return s;
+  if (n_R < 0 || k < 0 || n_A < n_R + k || n_A > d_ff)
+    return fail(POP_ERR_INVALID_ARGUMENT, "n_R=%d, k=%d, n_A=%d inconsistent (d_ff=%d)", n_R, k, n_A, d_ff);
+  if ((n_R > 0 && R == nullptr && k > 0) || (k > 0 && (selected == nullptr || positions == nullptr)))
+    return fail(POP_ERR_INVALID_ARGUMENT, "R, selected or positions is NULL with a nonzero size");
+  if ((batch > 0 && (z == nullptr || y == nullptr)) || W_downT == nullptr || ws == nullptr)
+    return fail(POP_ERR_INVALID_ARGUMENT, "z, y, W_downT and ws must be non-NULL");
+  if (!aligned16(W_downT) || !aligned16(y) || !aligned16(ws))
+    return fail(POP_ERR_MISALIGNED, "W_downT, y and ws must be 16-byte aligned");
+  const size_t need = pop_decode_down_workspace_bytes(batch, d, n_R + k);
+  if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  POP_DISPATCH(dt, launch_down, (hipStream_t)stream, z, batch, n_A, W_downT, d, d_ff, R, n_R, selected, positions, k,
+               y, (float*)ws);
+  return launched();
 }
 
 extern "C" pop_status pop_decode_ffn(const void* x, int32_t batch, int32_t d, const void* W_gate, const void* W_up,
@@ -382,44 +469,52 @@ extern "C" pop_status pop_decode_ffn(const void* x, int32_t batch, int32_t d, co
                                      const int32_t* C, int32_t n_C, double r, float* y, int32_t* selected, void* ws,
                                      size_t ws_bytes, void* stream) {
   clear_error();
-  pop_status s = check_decode_common(x, batch, d, W_gate, W_up, W_downT, d_ff, dt, y, ws, ws_bytes);
+  pop_status s = check_shape(batch, d, d_ff, dt);
   if (s != POP_OK) return s;
   if (!(r >= 0.0 && r < 1.0)) return fail(POP_ERR_INVALID_ARGUMENT, "r=%g outside [0, 1)", r);
-  if (n_R < 0 || n_C < 0 || (int64_t)n_R + n_C > d_ff)
-    return fail(POP_ERR_INVALID_ARGUMENT, "n_R=%d, n_C=%d inconsistent with d_ff=%d", n_R, n_C, d_ff);
-  if ((n_R > 0 && R == nullptr) || (n_C > 0 && C == nullptr))
-    return fail(POP_ERR_INVALID_ARGUMENT, "R or C is NULL with a nonzero size");
+  if ((s = check_lists(d_ff, R, n_R, C, n_C, false)) != POP_OK) return s;
+  if ((batch > 0 && (x == nullptr || y == nullptr)) || W_gate == nullptr || W_up == nullptr || W_downT == nullptr ||
+      ws == nullptr)
+    return fail(POP_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_downT) || !aligned16(y) ||
+      !aligned16(ws))
+    return fail(POP_ERR_MISALIGNED, "x, weights, y and ws must be 16-byte aligned");
+  const size_t need = pop_decode_workspace_bytes(batch, d, d_ff);
+  if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
   const int32_t k = topk_count(d_ff, r, n_R, n_C);
   DecodeWs w;
   decode_ws_layout(batch, d, d_ff, (char*)ws, &w);
-  // R == NULL selects the identity channel map inside the kernels; give the
-  // kernels a non-NULL R even when it is empty.
+  // An empty R is passed to the kernels as a non-NULL list (NULL means identity there).
   const int32_t* Rk = R != nullptr ? R : w.Q;
   const int32_t* Ck = C != nullptr ? C : w.Q;
   hipStream_t st = (hipStream_t)stream;
-  if (dt == POP_BF16)
-    run_decode<bf16s>(st, x, batch, d, d_ff, W_gate, W_up, W_downT, Rk, n_R, Ck, n_C, k, y, selected, w);
-  else
-    run_decode<float>(st, x, batch, d, d_ff, W_gate, W_up, W_downT, Rk, n_R, Ck, n_C, k, y, selected, w);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(POP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-  return POP_OK;
+  POP_DISPATCH(dt, launch_gateup, st, x, batch, d, W_gate, W_up, d_ff, Rk, n_R, Ck, n_C, w.z, w.score);
+  int32_t* sel = selected != nullptr ? selected : w.sel;  // the down stage reads the selected channels here
+  launch_select(st, w.score, n_C, Ck, k, w.Q, sel);
+  POP_DISPATCH(dt, launch_down, st, w.z, batch, n_R + n_C, W_downT, d, d_ff, Rk, n_R, sel, w.Q, k, y,
+               (float*)w.down);
+  return launched();
 }
 
 extern "C" pop_status pop_dense_ffn_decode(const void* x, int32_t batch, int32_t d, const void* W_gate,
                                            const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
                                            float* y, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  pop_status s = check_decode_common(x, batch, d, W_gate, W_up, W_downT, d_ff, dt, y, ws, ws_bytes);
+  pop_status s = check_shape(batch, d, d_ff, dt);
   if (s != POP_OK) return s;
+  if ((batch > 0 && (x == nullptr || y == nullptr)) || W_gate == nullptr || W_up == nullptr || W_downT == nullptr ||
+      ws == nullptr)
+    return fail(POP_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_downT) || !aligned16(y) ||
+      !aligned16(ws))
+    return fail(POP_ERR_MISALIGNED, "x, weights, y and ws must be 16-byte aligned");
+  const size_t need = pop_decode_workspace_bytes(batch, d, d_ff);
+  if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
   DecodeWs w;
   decode_ws_layout(batch, d, d_ff, (char*)ws, &w);
   hipStream_t st = (hipStream_t)stream;
-  if (dt == POP_BF16)
-    run_decode<bf16s>(st, x, batch, d, d_ff, W_gate, W_up, W_downT, nullptr, d_ff, nullptr, 0, 0, y, nullptr, w);
-  else
-    run_decode<float>(st, x, batch, d, d_ff, W_gate, W_up, W_downT, nullptr, d_ff, nullptr, 0, 0, y, nullptr, w);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(POP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-  return POP_OK;
+  POP_DISPATCH(dt, launch_gateup, st, x, batch, d, W_gate, W_up, d_ff, nullptr, d_ff, nullptr, 0, w.z, nullptr);
+  POP_DISPATCH(dt, launch_down, st, w.z, batch, d_ff, W_downT, d, d_ff, nullptr, d_ff, nullptr, nullptr, 0, y,
+               (float*)w.down);
+  return launched();
 }

@@ -63,32 +63,46 @@ __device__ __forceinline__ uint32_t value_bits(float v) { return __float_as_uint
 // Element i (0 <= i < n) has the 64-bit key  (value_bits << 32) | (0xffffffff - i):
 // a larger value is more important and, on equal values, the lower index is
 // more important.  All keys are distinct, so "the key of ascending rank c" is
-// unique.  For each of NT targets (ascending ranks) the select finds a
-// threshold such that  less(key)  holds exactly for the c keys below rank c.
+// unique.  For each of NT targets (ascending ranks) the select finds the key T
+// of that rank; less(key) := key < T then holds for exactly c keys.
 //
 // The value bits sit in LDS (sh.vals).  Thread t owns the consecutive elements
-// [t*E, min(n, (t+1)*E)), E = ceil(n / kSelThreads).  The radix passes start at
-// the highest bit where the values differ (all common leading bits are
-// skipped, so the first pass spreads over the histogram), use 8-bit digits and
-// stop for a target as soon as its bucket holds a single key.
+// [t*E, min(n, (t+1)*E)), E = ceil(n / NTH).
+//   pass 1   an 11-bit digit taken just below the common leading bits of all n
+//            keys (so the digit always splits the set), one 2048-bin histogram
+//            and a block scan locate each target's bucket;
+//   compact  a bucket of at most kSelListCap keys is copied to a list, so later
+//            passes scan only the bucket;
+//   passes   8-bit digits below the known bits until a bucket holds at most
+//            kSelBrute keys;
+//   rank     the last bucket is ranked by direct comparison (one thread per key)
+//            and the key of the target rank becomes the threshold.
+// Every loop is bounded; every LDS write index is checked against its array.
 // ---------------------------------------------------------------------------
-constexpr int kSelThreads = 1024;
 constexpr int kSelMaxN = 32768;
+constexpr int kSelBins1 = 2048;
+constexpr int kSelListCap = 2048;
+constexpr int kSelBrute = 128;
 
 struct SelTarget {
-  unsigned long long prefix;  // key bits at positions >= known
-  int known;                  // lowest known bit position
+  unsigned long long prefix;  // key bits at positions >= known (the whole key once state == 1)
+  int known;                  // lowest known bit position (0 once state == 1)
   int rank;                   // remaining rank inside the current bucket
-  int state;                  // 0 active, 1 found, 2 rank >= n (every key is below)
+  int count;                  // keys in the current bucket
+  int state;                  // 0 searching, 1 found, 2 rank >= n (every key is below)
 };
 
+template <int NTH>
 struct SelShared {
   uint32_t vals[kSelMaxN];
-  unsigned int hist[2][256];
+  unsigned int hist[kSelBins1];
+  int list[2][kSelListCap];
+  int small[2][kSelBrute];
+  int list_n[2];   // -1: the bucket is scanned in the full array
+  int small_n[2];
   SelTarget tgt[2];
-  unsigned int red_or[16];
-  unsigned int red_and[16];
-  int scan[16][3];
+  uint32_t red[NTH / 64][4];
+  int scan[NTH / 64][3];
 };
 
 __device__ __forceinline__ unsigned long long sel_key(uint32_t vb, int i) {
@@ -100,130 +114,313 @@ __device__ __forceinline__ bool sel_less(const SelTarget& t, unsigned long long 
   return (key >> t.known) < (t.prefix >> t.known);
 }
 
-// Loads value_bits of src[0..n) into sh.vals (all threads), then a barrier.
-__device__ __forceinline__ void sel_load(const float* __restrict__ src, int n, SelShared& sh) {
-  for (int i = threadIdx.x; i < n; i += kSelThreads) sh.vals[i] = value_bits(src[i]);
+__device__ __forceinline__ bool sel_in_bucket(const SelTarget& t, unsigned long long key) {
+  return t.known >= 64 || ((key ^ t.prefix) >> t.known) == 0ull;
+}
+
+// Loads value_bits of src[0..n) into sh.vals, then a barrier.
+template <int NTH>
+__device__ __forceinline__ void sel_load(const float* __restrict__ src, int n, SelShared<NTH>& sh) {
+  // 8 loads in flight per thread before any LDS store.
+  for (int i0 = threadIdx.x; i0 < n; i0 += 8 * NTH) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (i0 + j * NTH < n) ? src[i0 + j * NTH] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (i0 + j * NTH < n) sh.vals[i0 + j * NTH] = value_bits(v[j]);
+  }
   __syncthreads();
 }
 
-template <int NT>
-__device__ void select_thresholds(int n, const int (&ranks)[NT], SelShared& sh) {
+// Block-wide exclusive scan of one int per thread; returns the exclusive
+// prefix and (through total) the block sum.  Contains two barriers.
+template <int NTH>
+__device__ __forceinline__ int block_excl_scan1(int v, int& total, SelShared<NTH>& sh) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) sh.scan[wave][0] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NTH / 64; ++w) {
+    const int x = sh.scan[w][0];
+    off += (w < wave) ? x : 0;
+    tot += x;
+  }
+  total = tot;
+  __syncthreads();
+  return off + incl - v;
+}
+
+template <int NTH, int NT>
+__device__ void select_thresholds(int n, const int (&ranks)[NT], SelShared<NTH>& sh) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int E = (n + kSelThreads - 1) / kSelThreads;
+  const int E = (n + NTH - 1) / NTH;
   const int base = tid * E;
   const int end = min(n, base + E);
 
-  // Common leading bits of every value.
-  uint32_t vor = 0u, vand = 0xffffffffu;
+  // ---- A. common leading bits of all keys
+  uint32_t hor = 0u, hand = 0xffffffffu, lor = 0u, land = 0xffffffffu;
   for (int i = base; i < end; ++i) {
-    vor |= sh.vals[i];
-    vand &= sh.vals[i];
+    const uint32_t v = sh.vals[i];
+    const uint32_t lo = 0xffffffffu - (uint32_t)i;
+    hor |= v;
+    hand &= v;
+    lor |= lo;
+    land &= lo;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    vor |= __shfl_xor(vor, o);
-    vand &= __shfl_xor(vand, o);
+    hor |= __shfl_xor(hor, o);
+    hand &= __shfl_xor(hand, o);
+    lor |= __shfl_xor(lor, o);
+    land &= __shfl_xor(land, o);
   }
   if (lane == 0) {
-    sh.red_or[wave] = vor;
-    sh.red_and[wave] = vand;
+    sh.red[wave][0] = hor;
+    sh.red[wave][1] = hand;
+    sh.red[wave][2] = lor;
+    sh.red[wave][3] = land;
   }
   __syncthreads();
   if (tid == 0) {
-    uint32_t a = 0u, b = 0xffffffffu;
-    for (int w = 0; w < kSelThreads / 64; ++w) {
-      a |= sh.red_or[w];
-      b &= sh.red_and[w];
+    uint32_t a0 = 0u, b0 = 0xffffffffu, a1 = 0u, b1 = 0xffffffffu;
+    for (int w = 0; w < NTH / 64; ++w) {
+      a0 |= sh.red[w][0];
+      b0 &= sh.red[w][1];
+      a1 |= sh.red[w][2];
+      b1 &= sh.red[w][3];
     }
-    const uint32_t diff = a ^ b;
-    int top;  // highest key bit that can differ
-    unsigned long long prefix;
-    if (n == 0) {
-      top = 31;
-      prefix = 0ull;
-    } else if (diff == 0u) {
-      top = 31;  // every value equal: only the index half differs
-      prefix = (unsigned long long)b << 32;
-    } else {
-      const int hb = 31 - __clz(diff);
-      top = 32 + hb;
-      const uint32_t keep = (hb == 31) ? 0u : ~((2u << hb) - 1u);
-      prefix = (unsigned long long)(b & keep) << 32;
-    }
+    const unsigned long long kor = ((unsigned long long)a0 << 32) | a1;
+    const unsigned long long kand = ((unsigned long long)b0 << 32) | b1;
+    const unsigned long long diff = kor ^ kand;
+    const int known = diff ? 64 - __clzll(diff) : 0;  // bits >= known are common to all keys
+    const unsigned long long prefix = known >= 64 ? 0ull : (kand >> known) << known;
     for (int t = 0; t < NT; ++t) {
-      sh.tgt[t].prefix = prefix;
-      sh.tgt[t].known = top + 1;
-      sh.tgt[t].rank = ranks[t];
-      sh.tgt[t].state = (ranks[t] >= n) ? 2 : 0;
+      SelTarget g;
+      g.prefix = prefix;
+      g.known = known;
+      g.rank = ranks[t];
+      g.count = n;
+      g.state = ranks[t] >= n ? 2 : (n == 1 ? 1 : 0);
+      if (g.state == 1) {  // a single key: it is the threshold
+        g.prefix = kand;
+        g.known = 0;
+      }
+      sh.tgt[t] = g;
+      sh.list_n[t] = -1;
     }
   }
   __syncthreads();
 
-  // At most 8 passes per target: 63 key bits in 8-bit digits.
-  for (int pass = 0; pass < 16; ++pass) {
-    bool active = false;
+  // ---- B. first pass: 11-bit digit just below the common bits
+  bool any = false;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) active |= (sh.tgt[t].state == 0);
-    if (!active) break;  // uniform: every thread reads the same shared state
-
-    for (int i = tid; i < NT * 256; i += kSelThreads) (&sh.hist[0][0])[i] = 0u;
+  for (int t = 0; t < NT; ++t) any |= sh.tgt[t].state == 0;
+  if (any) {
+    const int known0 = sh.tgt[0].known;  // every target starts from the same common bits
+    const int s1 = known0 > 11 ? known0 - 11 : 0;
+    const unsigned long long mask1 = (1ull << (known0 - s1)) - 1ull;
+    for (int i = tid; i < kSelBins1; i += NTH) sh.hist[i] = 0u;
     __syncthreads();
-
+    for (int i = base; i < end; ++i)
+      atomicAdd(&sh.hist[(int)((sel_key(sh.vals[i], i) >> s1) & mask1)], 1u);
+    __syncthreads();
+    constexpr int BPT = kSelBins1 / NTH;  // bins per thread
+    unsigned int c[BPT];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      c[j] = sh.hist[tid * BPT + j];
+      sum += (int)c[j];
+    }
+    // Snapshot the targets before the scan: its barriers order every read
+    // here before the single write per target below.
+    SelTarget snap[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) snap[t] = sh.tgt[t];
+    int total;
+    const int before0 = block_excl_scan1<NTH>(sum, total, sh);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const SelTarget tg = sh.tgt[t];
-      if (tg.state != 0) continue;
-      const int s = tg.known > 8 ? tg.known - 8 : 0;
-      const unsigned long long mask = (1ull << (tg.known - s)) - 1ull;
-      for (int i = base; i < end; ++i) {
-        const unsigned long long key = sel_key(sh.vals[i], i);
-        if (((key ^ tg.prefix) >> tg.known) == 0ull) atomicAdd(&sh.hist[t][(int)((key >> s) & mask)], 1u);
+      const SelTarget g = snap[t];
+      if (g.state != 0) continue;
+      int before = before0;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        if (c[j] > 0u && before <= g.rank && g.rank < before + (int)c[j]) {
+          SelTarget h = g;
+          h.prefix = g.prefix | ((unsigned long long)(tid * BPT + j) << s1);
+          h.known = s1;
+          h.rank = g.rank - before;
+          h.count = (int)c[j];
+          sh.tgt[t] = h;
+        }
+        before += (int)c[j];
       }
     }
     __syncthreads();
-
-    if (wave < NT) {
-      const int t = wave;
-      const SelTarget tg = sh.tgt[t];
-      if (tg.state == 0) {
-        const int s = tg.known > 8 ? tg.known - 8 : 0;
-        unsigned int c[4];
-        unsigned int sum = 0;
+    // compact small-enough buckets into lists
+    if (tid < NT) sh.list_n[tid] = (sh.tgt[tid].state == 0 && sh.tgt[tid].count <= kSelListCap) ? 0 : -1;
+    __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          c[j] = sh.hist[t][lane * 4 + j];
-          sum += c[j];
-        }
-        unsigned int incl = sum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const unsigned int v = __shfl_up(incl, o);
-          if (lane >= o) incl += v;
-        }
-        unsigned int before = incl - sum;
-        const unsigned int rk = (unsigned int)tg.rank;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (c[j] > 0u && before <= rk && rk < before + c[j]) {
-            SelTarget nt;
-            nt.prefix = tg.prefix | ((unsigned long long)(lane * 4 + j) << s);
-            nt.known = s;
-            nt.rank = (int)(rk - before);
-            nt.state = (c[j] == 1u || s == 0) ? 1 : 0;
-            sh.tgt[t] = nt;
-          }
-          before += c[j];
+    for (int t = 0; t < NT; ++t) {
+      const SelTarget g = sh.tgt[t];
+      if (g.state != 0 || sh.list_n[t] < 0) continue;
+      for (int i = base; i < end; ++i) {
+        if (sel_in_bucket(g, sel_key(sh.vals[i], i))) {
+          const int pos = atomicAdd(&sh.list_n[t], 1);
+          if (pos < kSelListCap) sh.list[t][pos] = i;
         }
       }
     }
     __syncthreads();
   }
+
+  // ---- C. 8-bit passes until every bucket is small, then rank directly
+  for (int pass = 0; pass < 16; ++pass) {
+    bool big = false, active = false;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      active |= sh.tgt[t].state == 0;
+      big |= sh.tgt[t].state == 0 && sh.tgt[t].count > kSelBrute;
+    }
+    if (!active) break;
+    if (big) {
+      for (int i = tid; i < NT * 256; i += NTH) sh.hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const SelTarget g = sh.tgt[t];
+        if (g.state != 0 || g.count <= kSelBrute) continue;
+        const int s = g.known > 8 ? g.known - 8 : 0;
+        const unsigned long long mask = (1ull << (g.known - s)) - 1ull;
+        const int ln = sh.list_n[t];
+        if (ln >= 0) {
+          for (int j = tid; j < ln && j < kSelListCap; j += NTH) {
+            const int i = sh.list[t][j];
+            const unsigned long long key = sel_key(sh.vals[i], i);
+            if (sel_in_bucket(g, key)) atomicAdd(&sh.hist[t * 256 + (int)((key >> s) & mask)], 1u);
+          }
+        } else {
+          for (int i = base; i < end; ++i) {
+            const unsigned long long key = sel_key(sh.vals[i], i);
+            if (sel_in_bucket(g, key)) atomicAdd(&sh.hist[t * 256 + (int)((key >> s) & mask)], 1u);
+          }
+        }
+      }
+      __syncthreads();
+      if (wave < NT) {
+        const int t = wave;
+        const SelTarget g = sh.tgt[t];
+        if (g.state == 0 && g.count > kSelBrute) {
+          const int s = g.known > 8 ? g.known - 8 : 0;
+          unsigned int cc[4];
+          unsigned int sum = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            cc[j] = sh.hist[t * 256 + lane * 4 + j];
+            sum += cc[j];
+          }
+          unsigned int incl = sum;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const unsigned int v = __shfl_up(incl, o);
+            if (lane >= o) incl += v;
+          }
+          unsigned int before = incl - sum;
+          const unsigned int rk = (unsigned int)g.rank;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (cc[j] > 0u && before <= rk && rk < before + cc[j]) {
+              SelTarget h = g;
+              h.prefix = g.prefix | ((unsigned long long)(lane * 4 + j) << s);
+              h.known = s;
+              h.rank = (int)(rk - before);
+              h.count = (int)cc[j];
+              sh.tgt[t] = h;
+            }
+            before += cc[j];
+          }
+        }
+      }
+      __syncthreads();
+      continue;
+    }
+    // every active bucket holds at most kSelBrute keys: gather and rank them
+    if (tid < NT) sh.small_n[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const SelTarget g = sh.tgt[t];
+      if (g.state != 0) continue;
+      const int ln = sh.list_n[t];
+      if (ln >= 0) {
+        for (int j = tid; j < ln && j < kSelListCap; j += NTH) {
+          const int i = sh.list[t][j];
+          if (sel_in_bucket(g, sel_key(sh.vals[i], i))) {
+            const int pos = atomicAdd(&sh.small_n[t], 1);
+            if (pos < kSelBrute) sh.small[t][pos] = i;
+          }
+        }
+      } else {
+        for (int i = base; i < end; ++i) {
+          if (sel_in_bucket(g, sel_key(sh.vals[i], i))) {
+            const int pos = atomicAdd(&sh.small_n[t], 1);
+            if (pos < kSelBrute) sh.small[t][pos] = i;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    SelTarget snap2[NT];
+    int msnap[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      snap2[t] = sh.tgt[t];
+      msnap[t] = min(sh.small_n[t], kSelBrute);
+    }
+    __syncthreads();  // every thread holds its snapshot before any target is rewritten
+    for (int slot = tid; slot < NT * kSelBrute; slot += NTH) {
+      const int t = slot / kSelBrute;
+      const int j = slot % kSelBrute;
+      const SelTarget g = (t == 0) ? snap2[0] : snap2[NT - 1];  // no runtime-indexed register array
+      const int m = (t == 0) ? msnap[0] : msnap[NT - 1];
+      if (g.state != 0 || j >= m) continue;
+      const int ij = sh.small[t][j];
+      const unsigned long long kj = sel_key(sh.vals[ij], ij);
+      int r = 0;
+      for (int q = 0; q < m; ++q) {
+        const int iq = sh.small[t][q];
+        r += sel_key(sh.vals[iq], iq) < kj ? 1 : 0;
+      }
+      if (r == g.rank) {
+        SelTarget h = g;
+        h.prefix = kj;
+        h.known = 0;
+        h.rank = 0;
+        h.count = 1;
+        h.state = 1;
+        sh.tgt[t] = h;
+      }
+    }
+    __syncthreads();
+    break;
+  }
 }
 
-// Block-wide exclusive scan of up to three per-thread counters (1024 threads).
-__device__ __forceinline__ void block_exclusive_scan3(int (&v)[3], int (&total)[3], SelShared& sh) {
+// Block-wide exclusive scan of three per-thread counters.
+template <int NTH>
+__device__ __forceinline__ void block_exclusive_scan3(int (&v)[3], int (&total)[3], SelShared<NTH>& sh) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -245,7 +442,7 @@ __device__ __forceinline__ void block_exclusive_scan3(int (&v)[3], int (&total)[
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     int off = 0, tot = 0;
-    for (int w = 0; w < kSelThreads / 64; ++w) {
+    for (int w = 0; w < NTH / 64; ++w) {
       const int x = sh.scan[w][j];
       if (w < wave) off += x;
       tot += x;

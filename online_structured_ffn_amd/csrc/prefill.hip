@@ -99,16 +99,18 @@ __global__ __launch_bounds__(256) void k_importance(const T* __restrict__ W, int
 }
 
 // ---------------------------------------------------------------- K3
-__global__ __launch_bounds__(kSelThreads) void k_partition(const float* __restrict__ I, int n, int c_low, int c_high,
+constexpr int kPartThreads = 1024;
+
+__global__ __launch_bounds__(kPartThreads) void k_partition(const float* __restrict__ I, int n, int c_low, int c_high,
                                                            int32_t* __restrict__ R, int32_t* __restrict__ C,
                                                            int32_t* __restrict__ P) {
-  __shared__ SelShared sh;
-  sel_load(I, n, sh);
+  __shared__ SelShared<kPartThreads> sh;
+  sel_load<kPartThreads>(I, n, sh);
   const int ranks[2] = {c_low, c_high};
-  select_thresholds<2>(n, ranks, sh);
+  select_thresholds<kPartThreads, 2>(n, ranks, sh);
   const SelTarget lo = sh.tgt[0];
   const SelTarget hi = sh.tgt[1];
-  const int E = (n + kSelThreads - 1) / kSelThreads;
+  const int E = (n + kPartThreads - 1) / kPartThreads;
   const int base = threadIdx.x * E;
   const int end = min(n, base + E);
   int pos[3] = {0, 0, 0};  // P, C, R
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kSelThreads) void k_partition(const float* __restri
     else ++pos[2];
   }
   int tot[3];
-  block_exclusive_scan3(pos, tot, sh);
+  block_exclusive_scan3<kPartThreads>(pos, tot, sh);
   // Positions are capped at the list sizes the host derived from the counts;
   // an exact select never reaches the caps.
   const int n_P = c_low, n_C = c_high - c_low, n_R = n - c_high;
@@ -161,20 +163,96 @@ static PrefillPlan plan_prefill(int64_t n_tokens, int32_t d, int vec) {
   return p;
 }
 
-}  // namespace pop
-
-using namespace pop;
-
-extern "C" size_t pop_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff) {
-  if (n_tokens < 0 || d <= 0 || d_ff <= 0) return 0;
+static size_t importance_ws_bytes(int64_t n_tokens, int32_t d) {
   // Widest plan over both dtypes (bf16 has fewer column blocks, hence more chunks).
   const PrefillPlan p = plan_prefill(n_tokens, d, 8);
   const PrefillPlan q = plan_prefill(n_tokens, d, 4);
   const int chunks = p.n_chunks > q.n_chunks ? p.n_chunks : q.n_chunks;
-  size_t b = align_up((size_t)chunks * d * sizeof(float), 256);  // partial sums
-  b += align_up((size_t)d * sizeof(float), 256);                 // s2
-  b += align_up((size_t)d_ff * sizeof(float), 256);              // importance scratch
-  return b;
+  return align_up((size_t)chunks * d * sizeof(float), 256)  // partial sums
+         + align_up((size_t)d * sizeof(float), 256);        // s2
+}
+
+template <typename T>
+static void launch_importance(hipStream_t st, const void* X, int64_t n_tokens, int32_t d, const void* W_up,
+                              int32_t d_ff, float* I, char* ws) {
+  const PrefillPlan p = plan_prefill(n_tokens, d, Vec<T>::N);
+  const PrefillPlan pb = plan_prefill(n_tokens, d, 8), pf = plan_prefill(n_tokens, d, 4);
+  const int max_chunks = pb.n_chunks > pf.n_chunks ? pb.n_chunks : pf.n_chunks;
+  float* partial = (float*)ws;
+  float* s2 = (float*)(ws + align_up((size_t)max_chunks * d * sizeof(float), 256));
+  if (n_tokens > 0)
+    hipLaunchKernelGGL(k_colsq_partial<T>, dim3(p.col_blocks, p.n_chunks), dim3(64), 0, st, (const T*)X, n_tokens,
+                       d, p.rows_per_chunk, partial);
+  // With no prompt token the sum runs over zero chunks: s = 0, hence I = 0.
+  hipLaunchKernelGGL(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(256), 0, st, (const float*)partial,
+                     n_tokens > 0 ? p.n_chunks : 0, (int64_t)d, s2);
+  hipLaunchKernelGGL(k_importance<T>, dim3((d_ff + 3) / 4), dim3(256), (size_t)d * sizeof(float), st, (const T*)W_up,
+                     d_ff, d, (const float*)s2, I);
+}
+
+static pop_status launched() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(POP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return POP_OK;
+}
+
+static pop_status check_importance_args(const void* X, int64_t n_tokens, int32_t d, const void* W_up, int32_t d_ff,
+                                        pop_dtype dt) {
+  pop_status s = check_dtype_width(dt, d);
+  if (s != POP_OK) return s;
+  if (d_ff < 1 || d_ff > POP_MAX_D_FF) return fail(POP_ERR_BAD_SHAPE, "d_ff=%d outside [1, %d]", d_ff, POP_MAX_D_FF);
+  if (n_tokens < 0 || n_tokens > ((int64_t)1 << 40) / d)
+    return fail(POP_ERR_BAD_SHAPE, "n_tokens=%lld out of range", (long long)n_tokens);
+  if ((n_tokens > 0 && X == nullptr) || W_up == nullptr)
+    return fail(POP_ERR_INVALID_ARGUMENT, "X and W_up must be non-NULL");
+  if (!aligned16(X) || !aligned16(W_up)) return fail(POP_ERR_MISALIGNED, "X and W_up must be 16-byte aligned");
+  return POP_OK;
+}
+
+}  // namespace pop
+
+using namespace pop;
+
+extern "C" size_t pop_prefill_importance_workspace_bytes(int64_t n_tokens, int32_t d) {
+  if (n_tokens < 0 || d <= 0) return 0;
+  return importance_ws_bytes(n_tokens, d);
+}
+
+extern "C" size_t pop_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff) {
+  if (n_tokens < 0 || d <= 0 || d_ff <= 0) return 0;
+  return importance_ws_bytes(n_tokens, d) + align_up((size_t)d_ff * sizeof(float), 256);
+}
+
+extern "C" pop_status pop_prefill_importance(const void* X, int64_t n_tokens, int32_t d, const void* W_up,
+                                             int32_t d_ff, pop_dtype dt, float* importance, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  clear_error();
+  pop_status s = check_importance_args(X, n_tokens, d, W_up, d_ff, dt);
+  if (s != POP_OK) return s;
+  if (importance == nullptr || ws == nullptr) return fail(POP_ERR_INVALID_ARGUMENT, "importance and ws must be non-NULL");
+  if (!aligned16(ws)) return fail(POP_ERR_MISALIGNED, "ws must be 16-byte aligned");
+  const size_t need = importance_ws_bytes(n_tokens, d);
+  if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (dt == POP_BF16)
+    launch_importance<bf16s>((hipStream_t)stream, X, n_tokens, d, W_up, d_ff, importance, (char*)ws);
+  else
+    launch_importance<float>((hipStream_t)stream, X, n_tokens, d, W_up, d_ff, importance, (char*)ws);
+  return launched();
+}
+
+extern "C" pop_status pop_partition_select(const float* importance, int32_t d_ff, double r, double gamma, int32_t* R,
+                                           int32_t* C, int32_t* P, void* stream) {
+  clear_error();
+  pop_status s = check_rate(r, gamma);
+  if (s != POP_OK) return s;
+  if (d_ff < 1 || d_ff > POP_MAX_D_FF) return fail(POP_ERR_BAD_SHAPE, "d_ff=%d outside [1, %d]", d_ff, POP_MAX_D_FF);
+  const pop_counts c = counts(d_ff, r, gamma);
+  if (importance == nullptr || (c.n_R > 0 && R == nullptr) || (c.n_C > 0 && C == nullptr) ||
+      (c.n_P > 0 && P == nullptr))
+    return fail(POP_ERR_INVALID_ARGUMENT, "importance or an output list with a nonzero size is NULL");
+  hipLaunchKernelGGL(k_partition, dim3(1), dim3(kPartThreads), 0, (hipStream_t)stream, importance, d_ff, c.c_low,
+                     c.c_high, R, C, P);
+  return launched();
 }
 
 extern "C" pop_status pop_prefill_partition(const void* X, int64_t n_tokens, int32_t d, const void* W_up,
@@ -182,54 +260,24 @@ extern "C" pop_status pop_prefill_partition(const void* X, int64_t n_tokens, int
                                             int32_t* C, int32_t* P, float* importance, void* ws, size_t ws_bytes,
                                             void* stream) {
   clear_error();
-  pop_status s = check_dtype_width(dt, d);
+  pop_status s = check_importance_args(X, n_tokens, d, W_up, d_ff, dt);
   if (s != POP_OK) return s;
   if ((s = check_rate(r, gamma)) != POP_OK) return s;
-  if (d_ff < 1 || d_ff > POP_MAX_D_FF) return fail(POP_ERR_BAD_SHAPE, "d_ff=%d outside [1, %d]", d_ff, POP_MAX_D_FF);
-  if (n_tokens < 0 || n_tokens > ((int64_t)1 << 40) / d)
-    return fail(POP_ERR_BAD_SHAPE, "n_tokens=%lld out of range", (long long)n_tokens);
-  if ((n_tokens > 0 && X == nullptr) || W_up == nullptr || ws == nullptr)
-    return fail(POP_ERR_INVALID_ARGUMENT, "X, W_up and ws must be non-NULL");
   const pop_counts c = counts(d_ff, r, gamma);
-  if ((c.n_R > 0 && R == nullptr) || (c.n_C > 0 && C == nullptr) || (c.n_P > 0 && P == nullptr))
-    return fail(POP_ERR_INVALID_ARGUMENT, "an output list with a nonzero size is NULL");
-  if (!aligned16(X) || !aligned16(W_up) || !aligned16(ws) || !aligned16(importance))
-    return fail(POP_ERR_MISALIGNED, "X, W_up, importance and ws must be 16-byte aligned");
+  if ((c.n_R > 0 && R == nullptr) || (c.n_C > 0 && C == nullptr) || (c.n_P > 0 && P == nullptr) || ws == nullptr)
+    return fail(POP_ERR_INVALID_ARGUMENT, "ws or an output list with a nonzero size is NULL");
+  if (!aligned16(ws) || !aligned16(importance))
+    return fail(POP_ERR_MISALIGNED, "importance and ws must be 16-byte aligned");
   const size_t need = pop_prefill_workspace_bytes(n_tokens, d, d_ff);
   if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
-
-  const int vec = dt == POP_BF16 ? 8 : 4;
-  const PrefillPlan p = plan_prefill(n_tokens, d, vec);
-  char* w = (char*)ws;
-  float* partial = (float*)w;
-  const PrefillPlan pb = plan_prefill(n_tokens, d, 8), pf = plan_prefill(n_tokens, d, 4);
-  const int max_chunks = pb.n_chunks > pf.n_chunks ? pb.n_chunks : pf.n_chunks;
-  w += align_up((size_t)max_chunks * d * sizeof(float), 256);
-  float* s2 = (float*)w;
-  w += align_up((size_t)d * sizeof(float), 256);
-  float* I = importance ? importance : (float*)w;
-
+  const size_t iw = importance_ws_bytes(n_tokens, d);
+  float* I = importance ? importance : (float*)((char*)ws + iw);
   hipStream_t st = (hipStream_t)stream;
-  if (n_tokens > 0) {
-    dim3 g1(p.col_blocks, p.n_chunks);
-    if (dt == POP_BF16)
-      hipLaunchKernelGGL(k_colsq_partial<bf16s>, g1, dim3(64), 0, st, (const bf16s*)X, n_tokens, d, p.rows_per_chunk, partial);
-    else
-      hipLaunchKernelGGL(k_colsq_partial<float>, g1, dim3(64), 0, st, (const float*)X, n_tokens, d, p.rows_per_chunk, partial);
-    hipLaunchKernelGGL(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(256), 0, st, (const float*)partial, p.n_chunks,
-                       (int64_t)d, s2);
-  } else {
-    // No prompt token: s = 0, hence I = 0 (n_chunks = 0 sums nothing).
-    hipLaunchKernelGGL(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(256), 0, st, (const float*)partial, 0, (int64_t)d, s2);
-  }
-  const int g2 = (d_ff + 3) / 4;
-  const size_t lds2 = (size_t)d * sizeof(float);
   if (dt == POP_BF16)
-    hipLaunchKernelGGL(k_importance<bf16s>, dim3(g2), dim3(256), lds2, st, (const bf16s*)W_up, d_ff, d, (const float*)s2, I);
+    launch_importance<bf16s>(st, X, n_tokens, d, W_up, d_ff, I, (char*)ws);
   else
-    hipLaunchKernelGGL(k_importance<float>, dim3(g2), dim3(256), lds2, st, (const float*)W_up, d_ff, d, (const float*)s2, I);
-  hipLaunchKernelGGL(k_partition, dim3(1), dim3(kSelThreads), 0, st, (const float*)I, d_ff, c.c_low, c.c_high, R, C, P);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(POP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-  return POP_OK;
+    launch_importance<float>(st, X, n_tokens, d, W_up, d_ff, I, (char*)ws);
+  hipLaunchKernelGGL(k_partition, dim3(1), dim3(kPartThreads), 0, st, (const float*)I, d_ff, c.c_low, c.c_high, R, C,
+                     P);
+  return launched();
 }

@@ -1,0 +1,54 @@
+"""Algorithmic HBM bytes and flops of each piece of the pruned gated-MLP path.
+
+"Algorithmic" means what the method itself must move: every weight row it uses
+read once, its inputs read once, its outputs written once.  Implementation
+overheads (partial sums of split reductions, re-reads) are not counted, so a
+kernel's achieved bandwidth on these bytes can only be lower than its raw
+traffic rate.  e = element bytes (2 for bf16, 4 for fp32).
+"""
+from __future__ import annotations
+
+
+def gateup_bytes(d: int, n_A: int, n_C: int, batch: int, e: int) -> int:
+    """Gate/up GEMV over the rows R u C: both weight rows, x, the index list,
+    z written, the candidate scores written."""
+    return 2 * n_A * d * e + batch * d * e + 4 * n_A + 4 * batch * n_A + 4 * n_C
+
+
+def select_bytes(n_C: int, k: int) -> int:
+    return 4 * n_C + 4 * k * 2 + 4 * k
+
+
+def down_bytes(d: int, n_live: int, batch: int, e: int, k: int = 0) -> int:
+    """Down-projection over the live rows of W_downT: the rows, z of those rows,
+    the index lists, y written."""
+    return n_live * d * e + 4 * batch * n_live + 4 * (n_live + k) + 4 * batch * d
+
+
+def decode_bytes(d: int, n_R: int, n_C: int, k: int, batch: int, e: int) -> int:
+    """One pruned decode layer-step (the three stages)."""
+    n_A = n_R + n_C
+    n_live = n_R + k
+    return gateup_bytes(d, n_A, n_C, batch, e) + select_bytes(n_C, k) + down_bytes(d, n_live, batch, e, k)
+
+
+def dense_decode_bytes(d: int, d_ff: int, batch: int, e: int) -> int:
+    return 3 * d_ff * d * e + batch * d * e + 4 * batch * d + 8 * batch * d_ff
+
+
+def decode_flops(d: int, n_A: int, n_live: int, batch: int) -> int:
+    return 2 * batch * d * (2 * n_A + n_live)
+
+
+def importance_bytes(n_tokens: int, d: int, d_ff: int, e: int) -> int:
+    """Prompt X once, W_up once, I written."""
+    return n_tokens * d * e + d_ff * d * e + 4 * d_ff
+
+
+def partition_bytes(n_tokens: int, d: int, d_ff: int, e: int) -> int:
+    """Importance plus the select (I read, the three lists written)."""
+    return importance_bytes(n_tokens, d, d_ff, e) + 4 * d_ff + 4 * d_ff
+
+
+def prefill_ffn_flops(n_tokens: int, d: int, d_ff: int) -> int:
+    return 6 * n_tokens * d * d_ff

@@ -48,6 +48,16 @@ def _load():
                                           _c_vp, _c_i32, _c_vp, _c_i32, _c_dbl, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
         "pop_dense_ffn_decode": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
                                                 _c_vp, _c_vp, _c_size, _c_vp]),
+        "pop_prefill_importance_workspace_bytes": (_c_size, [_c_i64, _c_i32]),
+        "pop_prefill_importance": (ctypes.c_int, [_c_vp, _c_i64, _c_i32, _c_vp, _c_i32, ctypes.c_int, _c_vp, _c_vp,
+                                                  _c_size, _c_vp]),
+        "pop_partition_select": (ctypes.c_int, [_c_vp, _c_i32, _c_dbl, _c_dbl, _c_vp, _c_vp, _c_vp, _c_vp]),
+        "pop_decode_gateup": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_i32, ctypes.c_int, _c_vp, _c_i32,
+                                             _c_vp, _c_i32, _c_vp, _c_vp, _c_vp]),
+        "pop_decode_select": (ctypes.c_int, [_c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp]),
+        "pop_decode_down_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32]),
+        "pop_decode_down": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, ctypes.c_int, _c_vp, _c_i32,
+                                           _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_size, _c_vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -179,5 +189,82 @@ def pop_dense_ffn_decode(x, W_gate, W_up, W_downT, *, y=None, ws=None, stream=No
         ws = workspace(pop_decode_workspace_bytes(batch, d, d_ff), dev)
     _check("pop_dense_ffn_decode", lib.pop_dense_ffn_decode(
         _ptr(x), batch, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
+        _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+# ---------------------------------------------------------------- stages
+def pop_prefill_importance(X, W_up, *, out=None, ws=None, stream=None):
+    """I [d_ff] (fp32): the importance of every channel from the prompt X."""
+    _dev(X, W_up)
+    n_tokens, d = X.shape
+    d_ff = W_up.shape[0]
+    I = torch.empty(d_ff, dtype=torch.float32, device=W_up.device) if out is None else out
+    if ws is None:
+        ws = workspace(lib.pop_prefill_importance_workspace_bytes(n_tokens, d), W_up.device)
+    _check("pop_prefill_importance", lib.pop_prefill_importance(
+        _ptr(X), n_tokens, d, _ptr(W_up), d_ff, _dtype(W_up), _ptr(I), _ptr(ws), ws.numel(), _stream(stream)))
+    return I
+
+
+def pop_partition_select(I, r: float, gamma: float, *, out=None, stream=None):
+    """(R, C, P) from an importance vector."""
+    _dev(I)
+    d_ff = I.numel()
+    c = pop_partition_counts(d_ff, r, gamma)
+    if out is None:
+        out = tuple(torch.empty(c[n], dtype=torch.int32, device=I.device) for n in ("n_R", "n_C", "n_P"))
+    R, C, P = out
+    _check("pop_partition_select", lib.pop_partition_select(
+        _ptr(I), d_ff, float(r), float(gamma), _ptr(R), _ptr(C), _ptr(P), _stream(stream)))
+    return R, C, P
+
+
+def pop_decode_gateup(x, W_gate, W_up, R, C, *, n_R=None, z=None, score=None, want_score=True, stream=None):
+    """(z [batch, n_R + n_C], score [n_C]).  R=None with n_R given: identity rows."""
+    _dev(x, W_gate, W_up, R, C)
+    batch, d = x.shape
+    d_ff = W_gate.shape[0]
+    nR = R.numel() if R is not None else int(n_R)
+    nC = C.numel() if C is not None else 0
+    dev = W_gate.device
+    if z is None:
+        z = torch.empty((batch, nR + nC), dtype=torch.float32, device=dev)
+    if score is None and want_score:
+        score = torch.empty(nC, dtype=torch.float32, device=dev)
+    _check("pop_decode_gateup", lib.pop_decode_gateup(
+        _ptr(x), batch, d, _ptr(W_gate), _ptr(W_up), d_ff, _dtype(W_gate), _ptr(R), nR, _ptr(C), nC,
+        _ptr(z), _ptr(score), _stream(stream)))
+    return z, score
+
+
+def pop_decode_select(score, C, k: int, *, positions=None, selected=None, stream=None):
+    """(positions [k], selected [k]) of the k best candidates."""
+    _dev(score, C)
+    n_C = score.numel()
+    dev = score.device
+    if positions is None:
+        positions = torch.empty(int(k), dtype=torch.int32, device=dev)
+    if selected is None:
+        selected = torch.empty(int(k), dtype=torch.int32, device=dev)
+    _check("pop_decode_select", lib.pop_decode_select(
+        _ptr(score), n_C, _ptr(C), int(k), _ptr(positions), _ptr(selected), _stream(stream)))
+    return positions, selected
+
+
+def pop_decode_down(z, W_downT, R, selected, positions, *, n_R=None, y=None, ws=None, stream=None):
+    """y [batch, d] from z over R and the selected candidates."""
+    _dev(z, W_downT, R, selected, positions)
+    batch, n_A = z.shape
+    d_ff, d = W_downT.shape
+    nR = R.numel() if R is not None else int(n_R)
+    k = positions.numel() if positions is not None else 0
+    dev = W_downT.device
+    if y is None:
+        y = torch.empty((batch, d), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(lib.pop_decode_down_workspace_bytes(batch, d, nR + k), dev)
+    _check("pop_decode_down", lib.pop_decode_down(
+        _ptr(z), batch, n_A, _ptr(W_downT), d, d_ff, _dtype(W_downT), _ptr(R), nR, _ptr(selected), _ptr(positions), k,
         _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
     return y

@@ -235,3 +235,28 @@ def test_full_size_layer(wname, layer, steps):
     xs = [synth.decode_input(w, layer, t, drift_sets=sets) for t in range(steps)]
     say(f"  X {X.shape}, weights {wts['W_up'].shape}")
     _decode_case(X, xs, wts, w.dtype, w.r, w.gamma, w.name)
+
+
+def test_stages_compose_bitwise():
+    """The stage entry points run the same kernels as the composite calls."""
+    say("[stages] importance + select == partition; gate/up + select + down == decode")
+    c = synth.random_case(51, 100, 1032, 2900, 3, "bf16")
+    Xd, xd = dev(c["X"], "bf16"), dev(c["x"], "bf16")
+    Wg, Wu, WdT = dev(c["W_gate"], "bf16"), dev(c["W_up"], "bf16"), dev(c["W_downT"], "bf16")
+    R, C, P, I = pop.pop_prefill_partition(Xd, Wu, 0.3, 0.1, importance=True)
+    I2 = pop.pop_prefill_importance(Xd, Wu)
+    R2, C2, P2 = pop.pop_partition_select(I2, 0.3, 0.1)
+    y, S = pop.pop_decode_ffn(xd, Wg, Wu, WdT, R, C, 0.3, selected=True)
+    z, score = pop.pop_decode_gateup(xd, Wg, Wu, R, C)
+    k = S.numel()
+    Q, S2 = pop.pop_decode_select(score, C, k)
+    y2 = pop.pop_decode_down(z, WdT, R, S2, Q)
+    torch.cuda.synchronize()
+    for a, b in ((I, I2), (R, R2), (C, C2), (P, P2), (S, S2), (y, y2)):
+        assert torch.equal(a, b)
+    # the dense first half through the identity row map
+    zd, _ = pop.pop_decode_gateup(xd, Wg, Wu, None, None, n_R=2900, want_score=False)
+    yd = pop.pop_decode_down(zd, WdT, None, None, None, n_R=2900)
+    yref = pop.pop_dense_ffn_decode(xd, Wg, Wu, WdT)
+    torch.cuda.synchronize()
+    assert torch.equal(yd, yref)
