@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing sample")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--two-streams", action="store_true",
+                    help="decode through pop_decode_ffn_2s (candidate chain on a second stream)")
     return ap.parse_args()
 
 
@@ -120,9 +122,17 @@ def main():
         for l in range(L):
             pop.pop_prefill_partition(X[l], Wu[l], w.r, w.gamma, out=(R[l], C[l], P[l], None), ws=ws_pre)
 
-    def decode_layers():
+    two = pop.TwoStream() if args.two_streams else None
+
+    def decode_layers_1s():
         for l in range(L):
             pop.pop_decode_ffn(x_buf[l], Wg[l], Wu[l], WdT[l], R[l], C[l], w.r, y=y[l], ws=ws_dec)
+
+    def decode_layers_2s():
+        for l in range(L):
+            pop.pop_decode_ffn_2s(x_buf[l], Wg[l], Wu[l], WdT[l], R[l], C[l], w.r, two, y=y[l], ws=ws_dec)
+
+    decode_layers = decode_layers_1s if two is None else decode_layers_2s
 
     def dense_layers():
         for l in range(L):
@@ -134,12 +144,14 @@ def main():
     with torch.cuda.stream(side):
         x_buf.copy_(Xdec[0])
         prefill()
+        decode_layers_1s()
         decode_layers()
         dense_layers()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graphs = {}
-    for name, fn in (("prefill", prefill), ("decode", decode_layers), ("dense", dense_layers)):
+    for name, fn in (("prefill", prefill), ("decode", decode_layers), ("decode_1s", decode_layers_1s),
+                     ("dense", dense_layers)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
@@ -183,55 +195,66 @@ def main():
             x_buf.copy_(Xdec[t])
             graphs["dense"].replay()
 
+    def decode_only_1s():
+        for t in range(T):
+            x_buf.copy_(Xdec[t])
+            graphs["decode_1s"].replay()
+
     ms_dec = timed(decode_only, 1)
+    ms_dec_1s = timed(decode_only_1s, 1)
     ms_dense = timed(dense_only, 1)
     t_ls = ms_dec / (T * L)          # ms per pruned layer-step
     t_ls_dense = ms_dense / (T * L)
     bytes_ls = metrics.decode_bytes(d, n_R, n_C, k, B, e)
     bytes_dense = metrics.dense_decode_bytes(d, d_ff, B, e)
-    log(f"[bench] decode {t_ls * 1e3:.1f} us/layer-step ({bytes_ls / (t_ls * 1e-3) / 1e9:.0f} GB/s), "
+    log(f"[bench] decode {t_ls * 1e3:.1f} us/layer-step ({bytes_ls / (t_ls * 1e-3) / 1e9:.0f} GB/s; "
+        f"pop_decode_ffn graph {ms_dec_1s / (T * L) * 1e3:.1f} us), "
         f"dense {t_ls_dense * 1e3:.1f} us ({bytes_dense / (t_ls_dense * 1e-3) / 1e9:.0f} GB/s), "
         f"prefill partition {ms_prefill / L * 1e3:.1f} us/layer")
 
     # ------------------------------------------------------------ per-kernel pass (eager, queued ahead)
+    # The same composite calls as the timed region, with libpop's trace hook
+    # recording a HIP event before and after every kernel.  A spin kernel
+    # queued first keeps the GPU busy while the host enqueues, so the traced
+    # kernels run back to back.
     S = min(args.kernel_steps, T)
-    zbuf = torch.empty((B, n_A), dtype=torch.float32, device=dev)
-    score = torch.empty(n_C, dtype=torch.float32, device=dev)
-    Q = torch.empty(k, dtype=torch.int32, device=dev)
-    Ssel = torch.empty(k, dtype=torch.int32, device=dev)
-    ws_down = pop.workspace(pop.lib.pop_decode_down_workspace_bytes(B, d, n_live), dev)
-    I = torch.empty(d_ff, dtype=torch.float32, device=dev)
-    ws_imp = pop.workspace(pop.lib.pop_prefill_importance_workspace_bytes(n_tok, d), dev)
+    # which kernels each call launches (the library's dispatch rules)
+    vec = 8 if e == 2 else 4
+    fused = B == 1 and d <= 8 * 64 * vec
+    labels_pre = ["k_colsq_partial", "k_sum_chunks(s2)", "k_importance", "k_partition"]
+    if fused:
+        labels_dec = ((["k_decode_fused(candidates)"] if n_C > 0 else []) + (["k_topk"] if n_C > 4096 else [])
+                      + ["k_decode_fused(top-k + retained)"] + (["k_down_selected"] if k > 0 else [])
+                      + ["k_sum_chunks(y)"])
+        labels_dense = ["k_decode_fused(dense)", "k_sum_chunks(y)"]
+    else:
+        labels_dec = ["k_gateup"] + (["k_topk"] if n_C > 0 else []) + ["k_down_partial", "k_sum_chunks(y)"]
+        labels_dense = ["k_gateup(dense)", "k_down_partial(dense)", "k_sum_chunks(y)"]
 
-    def kernel_pass(record):
-        """Eager stage calls of every layer (prefill) and S decode steps; with
-        record=True, events bracket every stage call."""
-        out = []
-        mk = (lambda: Ev(torch).record()) if record else (lambda: None)
+    def kernel_pass(marks):
         for l in range(L):
-            e0 = mk()
-            pop.pop_prefill_importance(X[l], Wu[l], out=I, ws=ws_imp)
-            e1 = mk()
-            pop.pop_partition_select(I, w.r, w.gamma, out=(R[l], C[l], P[l]))
-            e2 = mk()
-            out.append(("prefill", e0, e1, e2))
+            a = pop.lib.pop_trace_recorded()
+            pop.pop_prefill_partition(X[l], Wu[l], w.r, w.gamma, out=(R[l], C[l], P[l], None), ws=ws_pre)
+            marks.append((labels_pre, a, pop.lib.pop_trace_recorded()))
         for t in range(S):
             x_buf.copy_(Xdec[t])
             for l in range(L):
-                e0 = mk()
-                pop.pop_decode_gateup(x_buf[l], Wg[l], Wu[l], R[l], C[l], z=zbuf, score=score)
-                e1 = mk()
-                pop.pop_decode_select(score, C[l], k, positions=Q, selected=Ssel)
-                e2 = mk()
-                pop.pop_decode_down(zbuf, WdT[l], R[l], Ssel, Q, y=y[l], ws=ws_down)
-                e3 = mk()
-                out.append(("decode", e0, e1, e2, e3))
-        return out
+                a = pop.lib.pop_trace_recorded()
+                pop.pop_decode_ffn(x_buf[l], Wg[l], Wu[l], WdT[l], R[l], C[l], w.r, y=y[l], ws=ws_dec)
+                marks.append((labels_dec, a, pop.lib.pop_trace_recorded()))
+        for t in range(S):
+            x_buf.copy_(Xdec[t])
+            for l in range(L):
+                a = pop.lib.pop_trace_recorded()
+                pop.pop_dense_ffn_decode(x_buf[l], Wg[l], Wu[l], WdT[l], y=y[l], ws=ws_dec)
+                marks.append((labels_dense, a, pop.lib.pop_trace_recorded()))
 
-    # host enqueue time of the pass, and a warmed-up spin kernel calibrated on a long sleep
+    n_ev = L * (len(labels_pre) + 1) + S * L * (len(labels_dec) + len(labels_dense) + 2) + 8
+    tracer = pop.Tracer(n_ev)
     torch.cuda.synchronize()
     h0 = time.perf_counter()
-    kernel_pass(True)
+    with tracer:
+        kernel_pass([])
     host_s = time.perf_counter() - h0
     torch.cuda.synchronize()
     torch.cuda._sleep(1000)
@@ -243,26 +266,38 @@ def main():
     cyc_per_ms = 20_000_000 / max(a.ms(b), 1e-3)
     lead_ms = max(50.0, 3.0 * host_s * 1e3)
     torch.cuda._sleep(int(cyc_per_ms * lead_ms))
-    start_ev = Ev(torch).record()
-    evs = kernel_pass(True)
-    end_ev = Ev(torch).record()
+    marks = []
+    with tracer:
+        kernel_pass(marks)
     torch.cuda.synchronize()
-    span_ms = start_ev.ms(end_ev)
-    windows_ms = sum(x[1].ms(x[-1]) for x in evs)
+    per = {}
+    gaps = 0.0
+    span = tracer.elapsed_ms(marks[0][1], marks[-1][2] - 1)
+    busy = 0.0
+    for labels, i0, i1 in marks:
+        assert i1 - i0 == len(labels) + 1, (labels, i0, i1)
+        for j, name in enumerate(labels):
+            dt = tracer.elapsed_ms(i0 + j, i0 + j + 1)
+            per.setdefault(name, []).append(dt)
+            busy += dt
+    tracer.close()
+    kus = {name: float(np.mean(v)) * 1e3 for name, v in per.items()}
     log(f"[bench] kernel pass: host enqueue {host_s * 1e3:.1f} ms, lead {lead_ms:.0f} ms, "
-        f"event windows cover {windows_ms / span_ms:.3f} of the span")
-    imp_us = np.mean([x[1].ms(x[2]) for x in evs if x[0] == "prefill"]) * 1e3
-    psel_us = np.mean([x[2].ms(x[3]) for x in evs if x[0] == "prefill"]) * 1e3
-    gu_us = np.mean([x[1].ms(x[2]) for x in evs if x[0] == "decode"]) * 1e3
-    sel_us = np.mean([x[2].ms(x[3]) for x in evs if x[0] == "decode"]) * 1e3
-    dn_us = np.mean([x[3].ms(x[4]) for x in evs if x[0] == "decode"]) * 1e3
-    gu_bytes = metrics.gateup_bytes(d, n_A, n_C, B, e)
-    dn_bytes = metrics.down_bytes(d, n_live, B, e, k)
-    imp_bytes = metrics.importance_bytes(n_tok, d, d_ff, e)
-    gu_gbps = gu_bytes / (gu_us * 1e-6) / 1e9
-    log(f"[bench] kernels (us): importance {imp_us:.1f}, partition-select {psel_us:.1f}, gate/up {gu_us:.1f} "
-        f"({gu_gbps:.0f} GB/s), top-k {sel_us:.1f}, down {dn_us:.1f} ({dn_bytes / (dn_us * 1e-6) / 1e9:.0f} GB/s)")
+        f"traced kernels cover {busy / span:.3f} of the span")
+    log("[bench] kernels (us): " + ", ".join(f"{n} {v:.2f}" for n, v in kus.items()))
 
+    if fused:
+        dom = "k_decode_fused(top-k + retained)"
+        dom_desc = ("k_decode_fused, retained launch (batch-1 decode: gate, up and W_downT rows of every retained "
+                    "channel in one stream, with the one-workgroup candidate top-k beside it)")
+        dom_bytes = metrics.retained_stream_bytes(d, n_R, n_C, k, e)
+    else:
+        dom = "k_gateup"
+        dom_desc = "k_gateup (decode gate/up over R u C, fused SiLU*up and candidate score)"
+        dom_bytes = metrics.gateup_bytes(d, n_A, n_C, B, e)
+    dom_us = kus[dom]
+    dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
+    imp_bytes = metrics.importance_bytes(n_tok, d, d_ff, e)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -279,18 +314,19 @@ def main():
         "config": {
             "workload": w.name, "layers": L, "d": d, "d_ff": d_ff, "r_ffn": w.r, "gamma": w.gamma,
             "prompt_tokens": n_tok, "decode_steps": T, "decode_batch": B, "hip_graphs": True,
+            "streams": 1 if two is None else 2,
             "step": "prefill partition of every layer + every decode step over every layer",
         },
         "roofline": {
-            "kernel": "k_gateup (decode gate/up over R u C, fused SiLU*up and candidate score)",
+            "kernel": dom_desc,
             "bound": "hbm",
-            "achieved": round(gu_gbps, 1),
+            "achieved": round(dom_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
+            "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
             "traffic": None,
-            "bytes_per_launch": gu_bytes,
-            "avg_launch_us": round(gu_us, 3),
+            "bytes_per_launch": dom_bytes,
+            "avg_launch_us": round(dom_us, 3),
         },
         "decode": {
             "us_per_layer_step": round(t_ls * 1e3, 3),
@@ -305,24 +341,15 @@ def main():
             "algorithmic_bytes_per_layer_step": bytes_dense,
             "hbm_gbps": round(bytes_dense / (t_ls_dense * 1e-3) / 1e9, 1),
         },
+        "decode_pop_decode_ffn_us_per_layer_step": round(ms_dec_1s / (T * L) * 1e3, 3),
         "speedup_vs_dense": round(t_ls_dense / t_ls, 4),
         "ideal_speedup_bytes": round(bytes_dense / bytes_ls, 4),
         "prefill_partition_us_per_layer": round(ms_prefill / L * 1e3, 2),
         "prefill_partition_hbm_frac": round(metrics.partition_bytes(n_tok, d, d_ff, e) / (ms_prefill / L * 1e-3)
                                             / 1e9 / HBM_PEAK_GBPS, 4),
-        "kernel_pass_coverage": round(windows_ms / span_ms, 4),
-        "kernels_us": {
-            "importance (colsq + sum + k_importance)": round(imp_us, 2),
-            "partition select (k_partition)": round(psel_us, 2),
-            "decode gate/up (k_gateup)": round(gu_us, 2),
-            "decode top-k (k_topk)": round(sel_us, 2),
-            "decode down (k_down_partial + k_sum_chunks)": round(dn_us, 2),
-        },
-        "kernel_gbps": {
-            "importance": round(imp_bytes / (imp_us * 1e-6) / 1e9, 1),
-            "gate/up": round(gu_gbps, 1),
-            "down": round(dn_bytes / (dn_us * 1e-6) / 1e9, 1),
-        },
+        "kernel_pass_coverage": round(busy / span, 4),
+        "kernels_us": {n: round(v, 3) for n, v in kus.items()},
+        "importance_gbps": round(imp_bytes / (kus["k_importance"] * 1e-6) / 1e9, 1),
         "cpu_baseline": None,
     }
 

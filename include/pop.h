@@ -166,20 +166,42 @@ size_t pop_decode_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff);
  *   y          device fp32 [batch, d] output.
  *   selected   optional device int32 [k]: the selected candidates, ascending.
  *   ws         device workspace >= pop_decode_workspace_bytes(batch, d, d_ff).
- *              After the call completes it starts with the intermediate
- *              z (fp32 [batch, n_R + n_C], R columns first, then C); the
- *              candidate scores (fp32 [n_C]) start at byte offset
- *              align_up(4 * batch * d_ff + 16, 256).
- * Kernels: row-gathered gate/up GEMV with fused SiLU*up and fused candidate
- * score; one-workgroup radix top-k over the candidates; gathered
- * down-projection over R and the selected rows of W_downT with a fixed-order
- * two-stage reduction.
+ *              After the call completes, byte offset 256 holds the
+ *              intermediate z (fp32 [batch, n_R + n_C], R columns first, then
+ *              C) and byte offset 256 + align_up(4 * batch * d_ff + 16, 256)
+ *              the candidate scores (fp32 [n_C]).
+ * Kernels at batch 1: the candidates' gate/up rows and scores; then the
+ * one-workgroup top-k running beside a stream over every retained row's gate,
+ * up and W_downT rows (z and its down contribution in one pass); the selected
+ * rows' down contributions; a fixed-order reduction.
+ * At batch > 1: row-gathered gate/up GEMV with fused SiLU*up and candidate
+ * score; one-workgroup radix top-k; gathered down-projection over R and the
+ * selected rows of W_downT; fixed-order reduction.  Deterministic.
  */
 pop_status pop_decode_ffn(const void* x, int32_t batch, int32_t d, const void* W_gate,
                           const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
                           const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C,
                           double r, float* y, int32_t* selected, void* ws, size_t ws_bytes,
                           void* stream);
+
+/*
+ * pop_decode_ffn_2s — pop_decode_ffn with the candidate chain on a second
+ * stream.  At batch 1 the candidates' gate/up rows and scores, the top-k and
+ * the selected rows' down contributions depend on each other but not on the
+ * retained rows; they run on `aux_stream` beside the retained-row stream on
+ * `stream`, and the fixed-order sum on `stream` waits for both.  fork_event and
+ * join_event are caller-created HIP events (no timing needed) used to order
+ * the two streams; the call records them and makes the streams wait on them,
+ * so it may be captured in a HIP graph from `stream`.  Same result, bit for
+ * bit, as pop_decode_ffn.  Other batch sizes run pop_decode_ffn on `stream`.
+ * Errors: INVALID_ARGUMENT when aux_stream, fork_event or join_event is NULL
+ * or aux_stream == stream; otherwise as pop_decode_ffn.
+ */
+pop_status pop_decode_ffn_2s(const void* x, int32_t batch, int32_t d, const void* W_gate,
+                             const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
+                             const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C, double r,
+                             float* y, int32_t* selected, void* ws, size_t ws_bytes, void* stream,
+                             void* aux_stream, void* fork_event, void* join_event);
 
 /* ---------------------------------------------------------------------------
  * Stages of pop_decode_ffn, callable on their own (also the building blocks of
@@ -237,12 +259,28 @@ pop_status pop_decode_down(const float* z, int32_t batch, int32_t n_A, const voi
  * pop_dense_ffn_decode — the unpruned gated MLP (equation (1) of the
  * batch-wise pruning page, section 3.1) for one decode step over all d_ff
  * channels: the dense baseline the pruned step is compared with.  Same
- * layouts as pop_decode_ffn; after the call the workspace starts with z
- * (fp32 [batch, d_ff]).
+ * layouts and workspace as pop_decode_ffn; after the call, byte offset 256 of
+ * the workspace holds z (fp32 [batch, d_ff]).
  */
 pop_status pop_dense_ffn_decode(const void* x, int32_t batch, int32_t d, const void* W_gate,
                                 const void* W_up, const void* W_downT, int32_t d_ff,
                                 pop_dtype dt, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Kernel tracing (measurement hook).
+ * ------------------------------------------------------------------------- */
+
+/*
+ * pop_set_trace_events — arms kernel tracing on the calling thread: every
+ * later libpop call on this thread records the next unused event of `events`
+ * (hipEvent_t handles created by the caller) on its stream before its first
+ * kernel and right after each kernel it launches, until n_events are used.
+ * pop_set_trace_events(NULL, 0) disarms.  This thread-local list is the only
+ * state the library keeps between calls; it is never touched unless armed.
+ */
+pop_status pop_set_trace_events(void* const* events, int32_t n_events);
+/* Events recorded since the last pop_set_trace_events call on this thread. */
+int32_t pop_trace_recorded(void);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libpop.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["pop_host.cpp", "prefill.hip", "decode.hip"]
+SOURCES = ["pop_host.cpp", "trace.hip", "prefill.hip", "decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -28,9 +28,9 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, defines=(), tag: str = "") -> str:
+    obj = os.path.join(BUILD, tag + os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -40,19 +40,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, out: str = OUT, defines=()) -> str:
+    """Compile and link the library; `defines` (NAME=VALUE strings) override
+    the launch-shape tunables for a variant written to `out`."""
     os.makedirs(BUILD, exist_ok=True)
+    tag = "" if not defines else f"v{abs(hash(tuple(defines))) % 10**8}_"
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, defines, tag), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
-    return OUT
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

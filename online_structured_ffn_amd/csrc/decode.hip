@@ -119,22 +119,21 @@ __global__ __launch_bounds__(256) void k_gateup(const T* __restrict__ x, int B, 
 // ties), written in ascending order as positions into C and as channels.
 constexpr int kTopkThreads = 256;
 
-__global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ score, int n, int k,
-                                                       const int32_t* __restrict__ C, int32_t* __restrict__ positions,
-                                                       int32_t* __restrict__ selected) {
-  __shared__ SelShared<kTopkThreads> sh;
-  sel_load<kTopkThreads>(score, n, sh);
+template <int NTH, int MAXN>
+__device__ void topk_block(const float* __restrict__ score, int n, int k, const int32_t* __restrict__ C,
+                           int32_t* __restrict__ positions, int32_t* __restrict__ selected, SelShared<NTH, MAXN>& sh) {
+  sel_load(score, n, sh);
   const int ranks[1] = {n - k};
-  select_thresholds<kTopkThreads, 1>(n, ranks, sh);
+  select_thresholds(n, ranks, sh);
   const SelTarget t = sh.tgt[0];
-  const int E = (n + kTopkThreads - 1) / kTopkThreads;
+  const int E = (n + NTH - 1) / NTH;
   const int base = threadIdx.x * E;
   const int end = min(n, base + E);
   int pos[3] = {0, 0, 0};
   for (int i = base; i < end; ++i)
     if (!sel_less(t, sel_key(sh.vals[i], i))) ++pos[0];
   int tot[3];
-  block_exclusive_scan3<kTopkThreads>(pos, tot, sh);
+  block_exclusive_scan3(pos, tot, sh);
   for (int i = base; i < end; ++i) {
     if (!sel_less(t, sel_key(sh.vals[i], i))) {
       if (pos[0] < k) {  // an exact select never reaches the cap
@@ -146,6 +145,284 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
   }
 }
 
+__global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ score, int n, int k,
+                                                       const int32_t* __restrict__ C, int32_t* __restrict__ positions,
+                                                       int32_t* __restrict__ selected) {
+  __shared__ SelShared<kTopkThreads> sh;
+  topk_block(score, n, k, C, positions, selected, sh);
+}
+
+// ---------------------------------------------------------------- fused decode step (batch 1)
+// Row streaming at batch 1.  A block of 256 threads works on one row at a time
+// together: thread t owns the columns j*256*V + t*V + [0, V) (j < NV) of every
+// row, so a row's gate, up and W_downT vectors are 3*NV 16-byte loads per
+// thread.  Rows go in batches of two, double-buffered: the next batch's loads
+// are in flight while the current batch's dot products are reduced (DPP
+// within each wave, LDS across the four waves, fixed order).
+// k_decode_fused gives its blocks one of three roles by block index:
+//   [0, nbT)            top-k over candidate scores written by an earlier launch;
+//   [nbT, nbT + nbC)    candidate rows: z = SiLU(W_gate x) * (W_up x), score |z|;
+//   [nbT + nbC, grid)   retained rows (block rb_base + ...): z and
+//                       z * W_downT[ch, :] into the thread's accumulators; one
+//                       partial y per block.
+// A decode step launches it twice: the candidates with the first share of the
+// retained blocks, then the top-k block beside the rest of them, so the
+// one-CU top-k runs under the retained stream.  No block waits on another
+// inside a launch.
+// Launch-shape tunables (overridable with -D for sweeps).
+#ifndef POP_FUSED_RBLOCKS
+#define POP_FUSED_RBLOCKS 512  // most blocks for the retained rows
+#endif
+#ifndef POP_FUSED_CROWS
+#define POP_FUSED_CROWS 4  // candidate rows per block
+#endif
+#ifndef POP_FUSED_R1_PERCENT
+#define POP_FUSED_R1_PERCENT 0  // share of the retained blocks that run with the candidates
+#endif
+#ifndef POP_SEL_ROWS
+#define POP_SEL_ROWS 8  // selected rows per block of k_down_selected
+#endif
+constexpr int kFusedThreads = 256;
+constexpr int kFusedTopkMaxN = 4096;
+constexpr int kFusedMaxRows = 512;  // rows per block
+constexpr int kFusedP = 2;          // rows per batch
+
+template <typename T, int NV>
+struct FusedRowBuf {
+  u32x4 g[kFusedP][NV];
+  u32x4 u[kFusedP][NV];
+  u32x4 w[kFusedP][NV];
+};
+
+template <typename T, int NV, bool kDown>
+__device__ __forceinline__ void fused_issue(FusedRowBuf<T, NV>& b, const int* rows, int i0, int nrows,
+                                            const T* __restrict__ Wg, const T* __restrict__ Wu,
+                                            const T* __restrict__ WdT, int d) {
+  constexpr int V = Vec<T>::N;
+#pragma unroll
+  for (int p = 0; p < kFusedP; ++p) {
+    if (i0 + p < nrows) {
+      const int64_t base = (int64_t)rows[i0 + p] * d;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int col = j * kFusedThreads * V + (int)threadIdx.x * V;
+        if (col < d) {
+          b.g[p][j] = ld16_stream(Wg + base + col);
+          b.u[p][j] = ld16_stream(Wu + base + col);
+          if (kDown) b.w[p][j] = ld16_stream(WdT + base + col);
+        }
+      }
+    }
+  }
+}
+
+// Reduces the batch's dot products across the block and applies them.
+// Returns through zs the batch's z values (valid for i0 + p < nrows).
+template <typename T, int NV, bool kDown, int PB>
+__device__ __forceinline__ void fused_consume(const FusedRowBuf<T, NV>& b, const u32x4 (&xv)[NV], int i0, int nrows,
+                                              int d, float (&part)[2][4][2 * kFusedP], float (&acc)[NV][Vec<T>::N],
+                                              float (&zs)[kFusedP]) {
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  float pg[kFusedP], pu[kFusedP];
+#pragma unroll
+  for (int p = 0; p < kFusedP; ++p) {
+    pg[p] = 0.f;
+    pu[p] = 0.f;
+    if (i0 + p < nrows) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int col = j * kFusedThreads * V + (int)threadIdx.x * V;
+        if (col < d) {
+          float g[V], u[V], xx[V];
+          unpack(b.g[p][j], g, T{});
+          unpack(b.u[p][j], u, T{});
+          unpack(xv[j], xx, T{});
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            pg[p] = fmaf(g[v], xx[v], pg[p]);
+            pu[p] = fmaf(u[v], xx[v], pu[p]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kFusedP; ++p) {
+    pg[p] = wave_sum_last(pg[p]);
+    pu[p] = wave_sum_last(pu[p]);
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int p = 0; p < kFusedP; ++p) {
+      part[PB][wave][2 * p] = pg[p];
+      part[PB][wave][2 * p + 1] = pu[p];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < kFusedP; ++p) {
+    float g = part[PB][0][2 * p], u = part[PB][0][2 * p + 1];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      g += part[PB][w][2 * p];
+      u += part[PB][w][2 * p + 1];
+    }
+    zs[p] = silu(g) * u;
+  }
+  if (kDown) {
+#pragma unroll
+    for (int p = 0; p < kFusedP; ++p) {
+      if (i0 + p < nrows) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int col = j * kFusedThreads * V + (int)threadIdx.x * V;
+          if (col < d) {
+            float f[V];
+            unpack(b.w[p][j], f, T{});
+#pragma unroll
+            for (int v = 0; v < V; ++v) acc[j][v] = fmaf(zs[p], f[v], acc[j][v]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int NV, bool kDown>
+__device__ __forceinline__ void fused_rows(const int* rows, int nrows, const T* __restrict__ Wg, const T* __restrict__ Wu,
+                                           const T* __restrict__ WdT, int d, const u32x4 (&xv)[NV],
+                                           float (&part)[2][4][2 * kFusedP], float (&acc)[NV][Vec<T>::N],
+                                           float* __restrict__ zout, int zbase, float* __restrict__ score) {
+  FusedRowBuf<T, NV> A, Bf;
+  float zs[kFusedP];
+  fused_issue<T, NV, kDown>(A, rows, 0, nrows, Wg, Wu, WdT, d);
+  for (int i0 = 0; i0 < nrows; i0 += 2 * kFusedP) {
+    fused_issue<T, NV, kDown>(Bf, rows, i0 + kFusedP, nrows, Wg, Wu, WdT, d);
+    fused_consume<T, NV, kDown, 0>(A, xv, i0, nrows, d, part, acc, zs);
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int p = 0; p < kFusedP; ++p)
+        if (i0 + p < nrows) {
+          zout[zbase + i0 + p] = zs[p];
+          if (score != nullptr) score[i0 + p] = fabsf(zs[p]);
+        }
+    }
+    if (i0 + kFusedP >= nrows) break;
+    fused_issue<T, NV, kDown>(A, rows, i0 + 2 * kFusedP, nrows, Wg, Wu, WdT, d);
+    fused_consume<T, NV, kDown, 1>(Bf, xv, i0 + kFusedP, nrows, d, part, acc, zs);
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int p = 0; p < kFusedP; ++p)
+        if (i0 + kFusedP + p < nrows) {
+          zout[zbase + i0 + kFusedP + p] = zs[p];
+          if (score != nullptr) score[i0 + kFusedP + p] = fabsf(zs[p]);
+        }
+    }
+  }
+}
+
+// Down-projection of the selected candidates: block (c, cs) takes rows
+// [c * rows_per_schunk, (c + 1) * rows_per_schunk) of S and the column slice
+// cs * 256 * V + [0, 256 * V), every row's load in flight at once, and writes
+// its share of the chunk's partial partial_s[c].  Row j of S is
+// (ch, z) = (sel[j], z[zoff + pos[j]]).
+template <typename T, int ROWS>
+__global__ __launch_bounds__(kFusedThreads) void k_down_selected(const float* __restrict__ z, int zoff, int n_A,
+                                                                 const T* __restrict__ WdT, int d, int d_ff,
+                                                                 const int32_t* __restrict__ sel,
+                                                                 const int32_t* __restrict__ pos, int k,
+                                                                 float* __restrict__ partial_s) {
+  constexpr int V = Vec<T>::N;
+  const int c = blockIdx.x;
+  const int col = (blockIdx.y * kFusedThreads + threadIdx.x) * V;
+  const int j0 = c * ROWS;
+  const int nr = min(ROWS, k - j0);
+  u32x4 w[ROWS];
+  float zv[ROWS];
+#pragma unroll
+  for (int u = 0; u < ROWS; ++u) {
+    zv[u] = 0.f;
+    if (u < nr) {
+      const int ch = clamp_channel(sel[j0 + u], d_ff);
+      zv[u] = z[min(zoff + max(pos[j0 + u], 0), n_A - 1)];
+      if (col < d) w[u] = ld16_stream(WdT + (int64_t)ch * d + col);
+    }
+  }
+  if (col >= d) return;
+  float acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int u = 0; u < ROWS; ++u) {
+    if (u < nr) {
+      float f[V];
+      unpack(w[u], f, T{});
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] = fmaf(zv[u], f[v], acc[v]);
+    }
+  }
+  float* out = partial_s + (int64_t)c * d + col;
+#pragma unroll
+  for (int v = 0; v < V; ++v) out[v] = acc[v];
+}
+
+template <typename T, int NV, bool kIdentity>
+__global__ __launch_bounds__(kFusedThreads) void k_decode_fused(
+    const T* __restrict__ x, int d, const T* __restrict__ Wg, const T* __restrict__ Wu, const T* __restrict__ WdT,
+    int d_ff, const int32_t* __restrict__ R, int n_R, const int32_t* __restrict__ C, int n_C, int k,
+    float* __restrict__ z, float* __restrict__ score, int32_t* __restrict__ positions,
+    int32_t* __restrict__ selected, float* __restrict__ partial, int nbT, int nbC, int rows_per_cblock,
+    int rows_per_rblock, int rb_base) {
+  constexpr int V = Vec<T>::N;
+  __shared__ SelShared<kFusedThreads, kFusedTopkMaxN> sel;
+  __shared__ int rows[kFusedMaxRows];
+  __shared__ float part[2][4][2 * kFusedP];
+  const int tid = threadIdx.x;
+  const int bid = blockIdx.x;
+  if (bid < nbT) {  // the top-k over scores an earlier launch wrote
+    topk_block(score, n_C, k, C, positions, selected, sel);
+    return;
+  }
+  u32x4 xv[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int col = j * kFusedThreads * V + tid * V;
+    xv[j] = col < d ? ld16(x + col) : u32x4{0u, 0u, 0u, 0u};
+  }
+  float acc[NV][V];
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[j][v] = 0.f;
+
+  if (bid < nbT + nbC) {  // candidate rows: z and scores
+    const int r0 = (bid - nbT) * rows_per_cblock;
+    const int nrows = max(0, min(n_C, r0 + rows_per_cblock) - r0);
+    for (int i = tid; i < nrows; i += kFusedThreads) rows[i] = clamp_channel(C[r0 + i], d_ff);
+    __syncthreads();
+    fused_rows<T, NV, false>(rows, nrows, Wg, Wu, WdT, d, xv, part, acc, z, n_R + r0, score + r0);
+    return;
+  }
+
+  const int rb = rb_base + bid - nbT - nbC;  // retained rows: z and the down contribution
+  const int r0 = rb * rows_per_rblock;
+  const int nrows = max(0, min(n_R, r0 + rows_per_rblock) - r0);
+  for (int i = tid; i < nrows; i += kFusedThreads) rows[i] = kIdentity ? r0 + i : clamp_channel(R[r0 + i], d_ff);
+  __syncthreads();
+  fused_rows<T, NV, true>(rows, nrows, Wg, Wu, WdT, d, xv, part, acc, z, r0, nullptr);
+  float* out = partial + (int64_t)rb * d;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int col = j * kFusedThreads * V + tid * V;
+    if (col < d) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) out[col + v] = acc[j][v];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- K6
 // Block: 256 threads = 4 waves sharing one column slice of 64*V columns.  The
 // block owns a chunk of live rows; wave w takes rows q0 + w, q0 + w + 4, ...
@@ -153,7 +430,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 // coalesced load (lane l holds row l), then streams the rows U at a time, each
 // lane reading one 16-byte vector of every row (a wave reads 1 KB of a bf16
 // row).  Live row q is (ch, zcol) = (R[q], q) for q < n_R and
-// (sel[q - n_R], n_R + pos[q - n_R]) after; with kIdentity it is (q, q).
+// (sel[q - n_R], zoff + pos[q - n_R]) after; with kIdentity it is (q, q).
 // The four wave accumulators are combined in wave order through LDS and written
 // as this chunk's partial sum.
 template <typename T, int BT, bool kIdentity>
@@ -161,7 +438,7 @@ __global__ __launch_bounds__(256) void k_down_partial(const float* __restrict__ 
                                                       const T* __restrict__ WdT, int d, int d_ff,
                                                       const int32_t* __restrict__ R, int n_R,
                                                       const int32_t* __restrict__ sel,
-                                                      const int32_t* __restrict__ pos, int n_live,
+                                                      const int32_t* __restrict__ pos, int zoff, int n_live,
                                                       int rows_per_chunk, float* __restrict__ partial) {
   constexpr int V = Vec<T>::N;
   constexpr int U = BT == 1 ? 16 : 8;
@@ -192,7 +469,7 @@ __global__ __launch_bounds__(256) void k_down_partial(const float* __restrict__ 
           zc_l = ql;
         } else {
           ch_l = clamp_channel(sel[ql - n_R], d_ff);
-          zc_l = n_R + min(max(pos[ql - n_R], 0), n_A - n_R - 1);
+          zc_l = min(zoff + max(pos[ql - n_R], 0), n_A - 1);
         }
       }
       const int cnt = min(64, my_rows - r0);
@@ -291,6 +568,7 @@ static size_t down_ws_bytes(int32_t batch, int32_t d, int32_t n_live) {
 }
 
 struct DecodeWs {
+  unsigned int* ctl;  // reserved
   float* z;
   float* score;
   int32_t* Q;    // selected positions into C
@@ -299,21 +577,33 @@ struct DecodeWs {
   size_t down_bytes;
 };
 
+constexpr int kFusedRBlocks = POP_FUSED_RBLOCKS;
+
+static size_t fused_partial_bytes(int32_t d, int32_t d_ff) {
+  const int chunks = kFusedRBlocks + (d_ff + POP_SEL_ROWS - 1) / POP_SEL_ROWS;  // retained blocks + selected chunks
+  return align_up((size_t)chunks * d * sizeof(float), 256);
+}
+
 static size_t decode_ws_layout(int32_t batch, int32_t d, int32_t d_ff, char* base, DecodeWs* out) {
-  size_t off = 0;
+  const size_t tb = 256;
   const size_t zb = align_up((size_t)batch * d_ff * sizeof(float) + 16, 256);
   const size_t sb = align_up((size_t)d_ff * sizeof(float), 256);
   const size_t qb = align_up((size_t)d_ff * sizeof(int32_t), 256);
-  const size_t db = down_ws_bytes(batch, d, d_ff);
+  size_t db = down_ws_bytes(batch, d, d_ff);
+  if (batch == 1) {
+    const size_t fb = fused_partial_bytes(d, d_ff);
+    if (fb > db) db = fb;
+  }
   if (out) {
-    out->z = (float*)(base + off);
-    out->score = (float*)(base + off + zb);
-    out->Q = (int32_t*)(base + off + zb + sb);
-    out->sel = (int32_t*)(base + off + zb + sb + qb);
-    out->down = base + off + zb + sb + 2 * qb;
+    out->ctl = (unsigned int*)base;
+    out->z = (float*)(base + tb);
+    out->score = (float*)(base + tb + zb);
+    out->Q = (int32_t*)(base + tb + zb + sb);
+    out->sel = (int32_t*)(base + tb + zb + sb + qb);
+    out->down = base + tb + zb + sb + 2 * qb;
     out->down_bytes = db;
   }
-  return zb + sb + 2 * qb + db;
+  return tb + zb + sb + 2 * qb + db;
 }
 
 // ---- stage launchers (arguments already validated)
@@ -325,10 +615,10 @@ static void launch_gateup(hipStream_t st, const void* x, int B, int d, const voi
   if (grid < 1) grid = 1;
 #define POP_GATEUP(BT)                                                                                        \
   if (R == nullptr)                                                                                           \
-    hipLaunchKernelGGL((k_gateup<T, BT, true>), dim3(grid), dim3(256), 0, st, (const T*)x, B, d, (const T*)Wg, \
+    POP_LAUNCH((k_gateup<T, BT, true>), dim3(grid), dim3(256), 0, st, (const T*)x, B, d, (const T*)Wg, \
                        (const T*)Wu, d_ff, R, n_R, C, n_C, z, score);                                         \
   else                                                                                                        \
-    hipLaunchKernelGGL((k_gateup<T, BT, false>), dim3(grid), dim3(256), 0, st, (const T*)x, B, d, (const T*)Wg, \
+    POP_LAUNCH((k_gateup<T, BT, false>), dim3(grid), dim3(256), 0, st, (const T*)x, B, d, (const T*)Wg, \
                        (const T*)Wu, d_ff, R, n_R, C, n_C, z, score)
   if (B <= 1) {
     POP_GATEUP(1);
@@ -342,7 +632,7 @@ static void launch_gateup(hipStream_t st, const void* x, int B, int d, const voi
 
 static void launch_select(hipStream_t st, const float* score, int n_C, const int32_t* C, int k, int32_t* Q,
                           int32_t* selected) {
-  if (n_C > 0) hipLaunchKernelGGL(k_topk, dim3(1), dim3(kTopkThreads), 0, st, score, n_C, k, C, Q, selected);
+  if (n_C > 0) POP_LAUNCH(k_topk, dim3(1), dim3(kTopkThreads), 0, st, score, n_C, k, C, Q, selected);
 }
 
 template <typename T>
@@ -354,11 +644,11 @@ static void launch_down(hipStream_t st, const float* z, int B, int n_A, const vo
   const DownPlan p = plan_down(n_live, B, d, Vec<T>::N);
 #define POP_DOWN(BT)                                                                                          \
   if (R == nullptr)                                                                                           \
-    hipLaunchKernelGGL((k_down_partial<T, BT, true>), dim3(p.col_blocks, p.n_chunks), dim3(256), 0, st, z, n_A, \
-                       B, (const T*)WdT, d, d_ff, R, n_R, sel, Q, n_live, p.rows_per_chunk, partial);        \
+    POP_LAUNCH((k_down_partial<T, BT, true>), dim3(p.col_blocks, p.n_chunks), dim3(256), 0, st, z, n_A, \
+                       B, (const T*)WdT, d, d_ff, R, n_R, sel, Q, n_R, n_live, p.rows_per_chunk, partial);  \
   else                                                                                                        \
-    hipLaunchKernelGGL((k_down_partial<T, BT, false>), dim3(p.col_blocks, p.n_chunks), dim3(256), 0, st, z,    \
-                       n_A, B, (const T*)WdT, d, d_ff, R, n_R, sel, Q, n_live, p.rows_per_chunk, partial)
+    POP_LAUNCH((k_down_partial<T, BT, false>), dim3(p.col_blocks, p.n_chunks), dim3(256), 0, st, z,    \
+                       n_A, B, (const T*)WdT, d, d_ff, R, n_R, sel, Q, n_R, n_live, p.rows_per_chunk, partial)
   if (B <= 1) {
     POP_DOWN(1);
   } else if (B <= 2) {
@@ -368,8 +658,98 @@ static void launch_down(hipStream_t st, const float* z, int B, int n_A, const vo
   }
 #undef POP_DOWN
   const int64_t n_out = (int64_t)B * d;
-  hipLaunchKernelGGL(k_sum_chunks<0>, dim3((unsigned)((n_out + 31) / 32)), dim3(256), 0, st, (const float*)partial,
-                     n_live > 0 ? p.n_chunks : 0, n_out, y);
+  POP_LAUNCH(k_sum_chunks<0>, dim3((unsigned)((n_out + 31) / 32)), dim3(1024), 0, st, (const float*)partial,
+                     n_live > 0 ? p.n_chunks : 0, n_out, y, (unsigned int*)nullptr, 0);
+}
+
+// Batch-1 decode step through k_decode_fused: false when d is too wide for
+// the kernel's per-thread columns (the caller then runs the stage kernels).
+template <typename T>
+static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, const void* Wu, const void* WdT,
+                         int d_ff, const int32_t* R, int n_R, const int32_t* C, int n_C, int k, float* y,
+                         const DecodeWs& w, hipStream_t aux = nullptr, hipEvent_t fork = nullptr,
+                         hipEvent_t join = nullptr) {
+  constexpr int V = Vec<T>::N;
+  const int nv = (d + kFusedThreads * V - 1) / (kFusedThreads * V);
+  if (nv > 4) return false;
+  const bool identity = (R == nullptr);
+  int nbC = 0, rows_per_cblock = 1;
+  if (n_C > 0) {
+    nbC = (n_C + POP_FUSED_CROWS - 1) / POP_FUSED_CROWS;
+    rows_per_cblock = (n_C + nbC - 1) / nbC;
+    nbC = (n_C + rows_per_cblock - 1) / rows_per_cblock;
+  }
+  int nbR = 0, rows_per_rblock = 1;
+  if (n_R > 0) {
+    nbR = (n_R + 7) / 8;
+    if (nbR > kFusedRBlocks) nbR = kFusedRBlocks;
+    rows_per_rblock = (n_R + nbR - 1) / nbR;
+    nbR = (n_R + rows_per_rblock - 1) / rows_per_rblock;
+  }
+  if (rows_per_cblock > kFusedMaxRows || rows_per_rblock > kFusedMaxRows) return false;
+  const bool fuse_topk = n_C > 0 && n_C <= kFusedTopkMaxN;
+  // Retained blocks in launch 1 (with the candidates); the rest go beside the top-k.
+  const int nbR1 = (n_C > 0 && k > 0) ? nbR * POP_FUSED_R1_PERCENT / 100 : nbR;
+  const int nbR2 = nbR - nbR1;
+  const int n_schunks = k > 0 ? (k + POP_SEL_ROWS - 1) / POP_SEL_ROWS : 0;
+  float* partial = (float*)w.down;
+  float* partial_s = partial + (int64_t)nbR * d;
+#define POP_NV_DISPATCH(MACRO) \
+  if (nv <= 1) {               \
+    MACRO(1);                  \
+  } else if (nv <= 2) {        \
+    MACRO(2);                  \
+  } else {                     \
+    MACRO(4);                  \
+  }
+  auto fused = [&](hipStream_t sx, int nbT_, int nbC_, int nbR_, int rb_base) {
+    const dim3 grid(nbT_ + nbC_ + nbR_);
+    hipStream_t st = sx;
+#define POP_FUSED(NVT)                                                                                          \
+  if (identity)                                                                                                 \
+    POP_LAUNCH((k_decode_fused<T, NVT, true>), grid, dim3(kFusedThreads), 0, st, (const T*)x, d, (const T*)Wg,   \
+               (const T*)Wu, (const T*)WdT, d_ff, R, n_R, C, n_C, k, w.z, w.score, w.Q, w.sel, partial, nbT_,     \
+               nbC_, rows_per_cblock, rows_per_rblock, rb_base);                                                 \
+  else                                                                                                          \
+    POP_LAUNCH((k_decode_fused<T, NVT, false>), grid, dim3(kFusedThreads), 0, st, (const T*)x, d, (const T*)Wg,  \
+               (const T*)Wu, (const T*)WdT, d_ff, R, n_R, C, n_C, k, w.z, w.score, w.Q, w.sel, partial, nbT_,     \
+               nbC_, rows_per_cblock, rows_per_rblock, rb_base)
+    POP_NV_DISPATCH(POP_FUSED)
+#undef POP_FUSED
+  };
+#undef POP_NV_DISPATCH
+  auto selected_rows = [&](hipStream_t sx) {
+    if (n_schunks > 0) {
+      const dim3 g3(n_schunks, (d + kFusedThreads * V - 1) / (kFusedThreads * V));
+      POP_LAUNCH((k_down_selected<T, POP_SEL_ROWS>), g3, dim3(kFusedThreads), 0, sx, (const float*)w.z, n_R,
+                 n_R + n_C, (const T*)WdT, d, d_ff, (const int32_t*)w.sel, (const int32_t*)w.Q, k, partial_s);
+    }
+  };
+  if (aux != nullptr) {
+    // Two streams: the candidate chain (scores -> top-k -> selected rows) on
+    // `aux` beside the retained stream on `st`, joined before the sum.
+    (void)hipEventRecord(fork, st);
+    (void)hipStreamWaitEvent(aux, fork, 0);
+    if (nbC > 0) fused(aux, 0, nbC, 0, 0);
+    if (nbR > 0) fused(st, 0, 0, nbR, 0);
+    launch_select(aux, w.score, n_C, C, k, w.Q, w.sel);
+    selected_rows(aux);
+    (void)hipEventRecord(join, aux);
+    (void)hipStreamWaitEvent(st, join, 0);
+  } else {
+    // launch 1: candidate rows (scores) and the first retained blocks
+    if (nbC + nbR1 > 0) fused(st, 0, nbC, nbR1, 0);
+    if (n_C > 0 && !fuse_topk) launch_select(st, w.score, n_C, C, k, w.Q, w.sel);
+    // launch 2: the top-k block beside the remaining retained blocks
+    const int nbT = fuse_topk ? 1 : 0;
+    if (nbT + nbR2 > 0) fused(st, nbT, 0, nbR2, nbR1);
+    // launch 3: the selected candidates' down rows
+    selected_rows(st);
+  }
+  // launch 4: fixed-order sum of every partial
+  POP_LAUNCH(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(1024), 0, st, (const float*)partial, nbR + n_schunks,
+             (int64_t)d, y, (unsigned int*)nullptr, 0);
+  return true;
 }
 
 static pop_status launched() {
@@ -427,6 +807,7 @@ extern "C" pop_status pop_decode_gateup(const void* x, int32_t batch, int32_t d,
     return fail(POP_ERR_INVALID_ARGUMENT, "x, z, W_gate and W_up must be non-NULL");
   if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up))
     return fail(POP_ERR_MISALIGNED, "x and the weights must be 16-byte aligned");
+  trace_mark(stream);
   POP_DISPATCH(dt, launch_gateup, (hipStream_t)stream, x, batch, d, W_gate, W_up, d_ff, R, n_R, C, n_C, z, score);
   return launched();
 }
@@ -438,6 +819,7 @@ extern "C" pop_status pop_decode_select(const float* score, int32_t n_C, const i
   if (k < 0 || k > n_C) return fail(POP_ERR_INVALID_ARGUMENT, "k=%d outside [0, n_C=%d]", k, n_C);
   if (n_C > 0 && (score == nullptr || C == nullptr || (k > 0 && (positions == nullptr || selected == nullptr))))
     return fail(POP_ERR_INVALID_ARGUMENT, "score, C, positions and selected must be non-NULL");
+  trace_mark(stream);
   launch_select((hipStream_t)stream, score, n_C, C, k, positions, selected);
   return launched();
 }
@@ -459,6 +841,7 @@ extern "C" pop_status pop_decode_down(const float* z, int32_t batch, int32_t n_A
     return fail(POP_ERR_MISALIGNED, "W_downT, y and ws must be 16-byte aligned");
   const size_t need = pop_decode_down_workspace_bytes(batch, d, n_R + k);
   if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  trace_mark(stream);
   POP_DISPATCH(dt, launch_down, (hipStream_t)stream, z, batch, n_A, W_downT, d, d_ff, R, n_R, selected, positions, k,
                y, (float*)ws);
   return launched();
@@ -488,12 +871,57 @@ extern "C" pop_status pop_decode_ffn(const void* x, int32_t batch, int32_t d, co
   const int32_t* Rk = R != nullptr ? R : w.Q;
   const int32_t* Ck = C != nullptr ? C : w.Q;
   hipStream_t st = (hipStream_t)stream;
+  DecodeWs wf = w;
+  if (selected != nullptr) wf.sel = selected;  // the top-k writes the caller's list directly
+  trace_mark(st);
+  if (batch == 1 && n_R + n_C > 0 &&
+      POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, Rk, n_R, Ck, n_C, k, y, wf))
+    return launched();
   POP_DISPATCH(dt, launch_gateup, st, x, batch, d, W_gate, W_up, d_ff, Rk, n_R, Ck, n_C, w.z, w.score);
   int32_t* sel = selected != nullptr ? selected : w.sel;  // the down stage reads the selected channels here
   launch_select(st, w.score, n_C, Ck, k, w.Q, sel);
   POP_DISPATCH(dt, launch_down, st, w.z, batch, n_R + n_C, W_downT, d, d_ff, Rk, n_R, sel, w.Q, k, y,
                (float*)w.down);
   return launched();
+}
+
+extern "C" pop_status pop_decode_ffn_2s(const void* x, int32_t batch, int32_t d, const void* W_gate,
+                                        const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
+                                        const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C, double r,
+                                        float* y, int32_t* selected, void* ws, size_t ws_bytes, void* stream,
+                                        void* aux_stream, void* fork_event, void* join_event) {
+  clear_error();
+  if (aux_stream == nullptr || fork_event == nullptr || join_event == nullptr || aux_stream == stream)
+    return fail(POP_ERR_INVALID_ARGUMENT, "aux_stream, fork_event and join_event must be set and aux != stream");
+  pop_status s = check_shape(batch, d, d_ff, dt);
+  if (s != POP_OK) return s;
+  if (!(r >= 0.0 && r < 1.0)) return fail(POP_ERR_INVALID_ARGUMENT, "r=%g outside [0, 1)", r);
+  if ((s = check_lists(d_ff, R, n_R, C, n_C, false)) != POP_OK) return s;
+  if ((batch > 0 && (x == nullptr || y == nullptr)) || W_gate == nullptr || W_up == nullptr || W_downT == nullptr ||
+      ws == nullptr)
+    return fail(POP_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_downT) || !aligned16(y) ||
+      !aligned16(ws))
+    return fail(POP_ERR_MISALIGNED, "x, weights, y and ws must be 16-byte aligned");
+  const size_t need = pop_decode_workspace_bytes(batch, d, d_ff);
+  if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (batch != 1)  // only the batch-1 pipeline has a candidate chain to overlap
+    return pop_decode_ffn(x, batch, d, W_gate, W_up, W_downT, d_ff, dt, R, n_R, C, n_C, r, y, selected, ws,
+                          ws_bytes, stream);
+  const int32_t k = topk_count(d_ff, r, n_R, n_C);
+  DecodeWs w;
+  decode_ws_layout(batch, d, d_ff, (char*)ws, &w);
+  const int32_t* Rk = R != nullptr ? R : w.Q;
+  const int32_t* Ck = C != nullptr ? C : w.Q;
+  hipStream_t st = (hipStream_t)stream;
+  DecodeWs wf = w;
+  if (selected != nullptr) wf.sel = selected;
+  trace_mark(st);
+  if (n_R + n_C > 0 && POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, Rk, n_R, Ck, n_C, k, y,
+                                    wf, (hipStream_t)aux_stream, (hipEvent_t)fork_event, (hipEvent_t)join_event))
+    return launched();
+  return pop_decode_ffn(x, batch, d, W_gate, W_up, W_downT, d_ff, dt, R, n_R, C, n_C, r, y, selected, ws, ws_bytes,
+                        stream);
 }
 
 extern "C" pop_status pop_dense_ffn_decode(const void* x, int32_t batch, int32_t d, const void* W_gate,
@@ -513,6 +941,10 @@ extern "C" pop_status pop_dense_ffn_decode(const void* x, int32_t batch, int32_t
   DecodeWs w;
   decode_ws_layout(batch, d, d_ff, (char*)ws, &w);
   hipStream_t st = (hipStream_t)stream;
+  trace_mark(st);
+  if (batch == 1 &&
+      POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, nullptr, d_ff, nullptr, 0, 0, y, w))
+    return launched();
   POP_DISPATCH(dt, launch_gateup, st, x, batch, d, W_gate, W_up, d_ff, nullptr, d_ff, nullptr, 0, w.z, nullptr);
   POP_DISPATCH(dt, launch_down, st, w.z, batch, d_ff, W_downT, d, d_ff, nullptr, d_ff, nullptr, nullptr, 0, y,
                (float*)w.down);

@@ -48,6 +48,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Wave64 sum through DPP row/bank operations (no LDS round trips).  The
+// total is exact in lane 63; other lanes hold partial sums.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_last(float v) {
+  v += dpp_mov<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141, 0xf>(v);  // row_half_mirror: 8-lane sums
+  v += dpp_mov<0x140, 0xf>(v);  // row_mirror: 16-lane sums
+  v += dpp_mov<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_mov<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;                     // lane 63: sum of all 64 lanes
+}
+// The wave total broadcast to every lane.
+__device__ __forceinline__ float wave_sum_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_last(v)), 63));
+}
+
 __device__ __forceinline__ float silu(float a) {
   // a * sigmoid(a); expf(-a) overflows to +inf for a < -88 and the quotient is -0.
   return a / (1.0f + expf(-a));
@@ -92,9 +112,9 @@ struct SelTarget {
   int state;                  // 0 searching, 1 found, 2 rank >= n (every key is below)
 };
 
-template <int NTH>
+template <int NTH, int MAXN = kSelMaxN>
 struct SelShared {
-  uint32_t vals[kSelMaxN];
+  uint32_t vals[MAXN];
   unsigned int hist[kSelBins1];
   int list[2][kSelListCap];
   int small[2][kSelBrute];
@@ -119,8 +139,8 @@ __device__ __forceinline__ bool sel_in_bucket(const SelTarget& t, unsigned long 
 }
 
 // Loads value_bits of src[0..n) into sh.vals, then a barrier.
-template <int NTH>
-__device__ __forceinline__ void sel_load(const float* __restrict__ src, int n, SelShared<NTH>& sh) {
+template <int NTH, int MAXN>
+__device__ __forceinline__ void sel_load(const float* __restrict__ src, int n, SelShared<NTH, MAXN>& sh) {
   // 8 loads in flight per thread before any LDS store.
   for (int i0 = threadIdx.x; i0 < n; i0 += 8 * NTH) {
     float v[8];
@@ -135,8 +155,8 @@ __device__ __forceinline__ void sel_load(const float* __restrict__ src, int n, S
 
 // Block-wide exclusive scan of one int per thread; returns the exclusive
 // prefix and (through total) the block sum.  Contains two barriers.
-template <int NTH>
-__device__ __forceinline__ int block_excl_scan1(int v, int& total, SelShared<NTH>& sh) {
+template <int NTH, int MAXN>
+__device__ __forceinline__ int block_excl_scan1(int v, int& total, SelShared<NTH, MAXN>& sh) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   int incl = v;
@@ -159,8 +179,8 @@ __device__ __forceinline__ int block_excl_scan1(int v, int& total, SelShared<NTH
   return off + incl - v;
 }
 
-template <int NTH, int NT>
-__device__ void select_thresholds(int n, const int (&ranks)[NT], SelShared<NTH>& sh) {
+template <int NTH, int NT, int MAXN>
+__device__ void select_thresholds(int n, const int (&ranks)[NT], SelShared<NTH, MAXN>& sh) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -249,7 +269,7 @@ __device__ void select_thresholds(int n, const int (&ranks)[NT], SelShared<NTH>&
 #pragma unroll
     for (int t = 0; t < NT; ++t) snap[t] = sh.tgt[t];
     int total;
-    const int before0 = block_excl_scan1<NTH>(sum, total, sh);
+    const int before0 = block_excl_scan1(sum, total, sh);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const SelTarget g = snap[t];
@@ -419,8 +439,8 @@ __device__ void select_thresholds(int n, const int (&ranks)[NT], SelShared<NTH>&
 }
 
 // Block-wide exclusive scan of three per-thread counters.
-template <int NTH>
-__device__ __forceinline__ void block_exclusive_scan3(int (&v)[3], int (&total)[3], SelShared<NTH>& sh) {
+template <int NTH, int MAXN>
+__device__ __forceinline__ void block_exclusive_scan3(int (&v)[3], int (&total)[3], SelShared<NTH, MAXN>& sh) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -455,31 +475,32 @@ __device__ __forceinline__ void block_exclusive_scan3(int (&v)[3], int (&total)[
 }
 
 // ---------------------------------------------------------------- fixed-order chunk sum
-// out[i] = sum_{c < n_chunks} partial[c * n_out + i], summed as 8 contiguous
-// groups of chunks (each in chunk order) then the 8 group sums in group order:
-// the same bits on every run.
+// out[i] = sum_{c < n_chunks} partial[c * n_out + i].  A block of 1024 threads
+// covers 32 outputs; the chunks are dealt to 32 groups as contiguous ranges,
+// each group sums its range in chunk order (8 loads in flight), and the 32
+// group sums are added in group order: the same bits on every run.
 template <int kUnused = 0>
-__global__ __launch_bounds__(256) void k_sum_chunks(const float* __restrict__ partial, int n_chunks, int64_t n_out,
-                                                    float* __restrict__ out) {
-  __shared__ float part[8][33];
+__global__ __launch_bounds__(1024) void k_sum_chunks(const float* __restrict__ partial, int n_chunks, int64_t n_out,
+                                                     float* __restrict__ out, unsigned int* __restrict__ reset,
+                                                     int n_reset) {
+  // Control words of the call's earlier kernels, cleared for the next call.
+  if (reset != nullptr && blockIdx.x == 0 && (int)threadIdx.x < n_reset) reset[threadIdx.x] = 0u;
+  __shared__ float part[32][33];
   const int o = threadIdx.x & 31;
   const int g = threadIdx.x >> 5;
   const int64_t i = (int64_t)blockIdx.x * 32 + o;
-  const int per = (n_chunks + 7) / 8;
+  const int per = (n_chunks + 31) / 32;
   const int c0 = g * per;
   const int c1 = min(n_chunks, c0 + per);
   float s = 0.f;
   if (i < n_out) {
     int c = c0;
-    for (; c + 4 <= c1; c += 4) {
-      const float a0 = partial[(int64_t)c * n_out + i];
-      const float a1 = partial[(int64_t)(c + 1) * n_out + i];
-      const float a2 = partial[(int64_t)(c + 2) * n_out + i];
-      const float a3 = partial[(int64_t)(c + 3) * n_out + i];
-      s += a0;
-      s += a1;
-      s += a2;
-      s += a3;
+    for (; c + 8 <= c1; c += 8) {
+      float a[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] = partial[(int64_t)(c + j) * n_out + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += a[j];
     }
     for (; c < c1; ++c) s += partial[(int64_t)c * n_out + i];
   }
@@ -488,7 +509,7 @@ __global__ __launch_bounds__(256) void k_sum_chunks(const float* __restrict__ pa
   if (g == 0 && i < n_out) {
     float t = part[0][o];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) t += part[j][o];
+    for (int j = 1; j < 32; ++j) t += part[j][o];
     out[i] = t;
   }
 }

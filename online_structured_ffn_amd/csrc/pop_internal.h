@@ -25,4 +25,15 @@ pop_status check_rate(double r, double gamma);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Records the next caller-provided trace event on `stream` (no-op unless
+// pop_set_trace_events armed this thread).
+void trace_mark(void* stream);
+
+// hipLaunchKernelGGL followed by a trace mark on the same stream.
+#define POP_LAUNCH(kernel, grid, block, shmem, stream, ...)                  \
+  do {                                                                        \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);      \
+    ::pop::trace_mark((void*)(stream));                                       \
+  } while (0)
+
 }  // namespace pop

@@ -105,9 +105,9 @@ __global__ __launch_bounds__(kPartThreads) void k_partition(const float* __restr
                                                            int32_t* __restrict__ R, int32_t* __restrict__ C,
                                                            int32_t* __restrict__ P) {
   __shared__ SelShared<kPartThreads> sh;
-  sel_load<kPartThreads>(I, n, sh);
+  sel_load(I, n, sh);
   const int ranks[2] = {c_low, c_high};
-  select_thresholds<kPartThreads, 2>(n, ranks, sh);
+  select_thresholds(n, ranks, sh);
   const SelTarget lo = sh.tgt[0];
   const SelTarget hi = sh.tgt[1];
   const int E = (n + kPartThreads - 1) / kPartThreads;
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kPartThreads) void k_partition(const float* __restr
     else ++pos[2];
   }
   int tot[3];
-  block_exclusive_scan3<kPartThreads>(pos, tot, sh);
+  block_exclusive_scan3(pos, tot, sh);
   // Positions are capped at the list sizes the host derived from the counts;
   // an exact select never reaches the caps.
   const int n_P = c_low, n_C = c_high - c_low, n_R = n - c_high;
@@ -181,12 +181,12 @@ static void launch_importance(hipStream_t st, const void* X, int64_t n_tokens, i
   float* partial = (float*)ws;
   float* s2 = (float*)(ws + align_up((size_t)max_chunks * d * sizeof(float), 256));
   if (n_tokens > 0)
-    hipLaunchKernelGGL(k_colsq_partial<T>, dim3(p.col_blocks, p.n_chunks), dim3(64), 0, st, (const T*)X, n_tokens,
+    POP_LAUNCH(k_colsq_partial<T>, dim3(p.col_blocks, p.n_chunks), dim3(64), 0, st, (const T*)X, n_tokens,
                        d, p.rows_per_chunk, partial);
   // With no prompt token the sum runs over zero chunks: s = 0, hence I = 0.
-  hipLaunchKernelGGL(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(256), 0, st, (const float*)partial,
-                     n_tokens > 0 ? p.n_chunks : 0, (int64_t)d, s2);
-  hipLaunchKernelGGL(k_importance<T>, dim3((d_ff + 3) / 4), dim3(256), (size_t)d * sizeof(float), st, (const T*)W_up,
+  POP_LAUNCH(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(1024), 0, st, (const float*)partial,
+                     n_tokens > 0 ? p.n_chunks : 0, (int64_t)d, s2, (unsigned int*)nullptr, 0);
+  POP_LAUNCH(k_importance<T>, dim3((d_ff + 3) / 4), dim3(256), (size_t)d * sizeof(float), st, (const T*)W_up,
                      d_ff, d, (const float*)s2, I);
 }
 
@@ -233,6 +233,7 @@ extern "C" pop_status pop_prefill_importance(const void* X, int64_t n_tokens, in
   if (!aligned16(ws)) return fail(POP_ERR_MISALIGNED, "ws must be 16-byte aligned");
   const size_t need = importance_ws_bytes(n_tokens, d);
   if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  trace_mark(stream);
   if (dt == POP_BF16)
     launch_importance<bf16s>((hipStream_t)stream, X, n_tokens, d, W_up, d_ff, importance, (char*)ws);
   else
@@ -250,7 +251,8 @@ extern "C" pop_status pop_partition_select(const float* importance, int32_t d_ff
   if (importance == nullptr || (c.n_R > 0 && R == nullptr) || (c.n_C > 0 && C == nullptr) ||
       (c.n_P > 0 && P == nullptr))
     return fail(POP_ERR_INVALID_ARGUMENT, "importance or an output list with a nonzero size is NULL");
-  hipLaunchKernelGGL(k_partition, dim3(1), dim3(kPartThreads), 0, (hipStream_t)stream, importance, d_ff, c.c_low,
+  trace_mark(stream);
+  POP_LAUNCH(k_partition, dim3(1), dim3(kPartThreads), 0, (hipStream_t)stream, importance, d_ff, c.c_low,
                      c.c_high, R, C, P);
   return launched();
 }
@@ -273,11 +275,12 @@ extern "C" pop_status pop_prefill_partition(const void* X, int64_t n_tokens, int
   const size_t iw = importance_ws_bytes(n_tokens, d);
   float* I = importance ? importance : (float*)((char*)ws + iw);
   hipStream_t st = (hipStream_t)stream;
+  trace_mark(st);
   if (dt == POP_BF16)
     launch_importance<bf16s>(st, X, n_tokens, d, W_up, d_ff, I, (char*)ws);
   else
     launch_importance<float>(st, X, n_tokens, d, W_up, d_ff, I, (char*)ws);
-  hipLaunchKernelGGL(k_partition, dim3(1), dim3(kPartThreads), 0, st, (const float*)I, d_ff, c.c_low, c.c_high, R, C,
+  POP_LAUNCH(k_partition, dim3(1), dim3(kPartThreads), 0, st, (const float*)I, d_ff, c.c_low, c.c_high, R, C,
                      P);
   return launched();
 }

@@ -15,6 +15,18 @@ def gateup_bytes(d: int, n_A: int, n_C: int, batch: int, e: int) -> int:
     return 2 * n_A * d * e + batch * d * e + 4 * n_A + 4 * batch * n_A + 4 * n_C
 
 
+def candidate_scores_bytes(d: int, n_C: int, e: int) -> int:
+    """Candidate launch at batch 1: gate/up rows of C, x, C, z and scores written."""
+    return 2 * n_C * d * e + d * e + 4 * n_C + 4 * n_C + 4 * n_C
+
+
+def retained_stream_bytes(d: int, n_R: int, n_C: int, k: int, e: int) -> int:
+    """Retained launch at batch 1: gate, up and W_downT rows of R, x, R, z of R
+    written, the partial y per block not counted; plus the top-k beside it
+    (scores and C read, 2k indices written)."""
+    return 3 * n_R * d * e + d * e + 4 * n_R + 4 * n_R + 8 * n_C + 8 * k
+
+
 def select_bytes(n_C: int, k: int) -> int:
     return 4 * n_C + 4 * k * 2 + 4 * k
 

@@ -15,7 +15,8 @@ import re
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpop.so")
+# POP_LIBRARY selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("POP_LIBRARY") or os.path.join(_HERE, "libpop.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "pop.h")
 
 POP_F32, POP_BF16 = 0, 1
@@ -56,6 +57,11 @@ def _load():
                                              _c_vp, _c_i32, _c_vp, _c_vp, _c_vp]),
         "pop_decode_select": (ctypes.c_int, [_c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp]),
         "pop_decode_down_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32]),
+        "pop_set_trace_events": (ctypes.c_int, [ctypes.POINTER(_c_vp), _c_i32]),
+        "pop_decode_ffn_2s": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
+                                             _c_vp, _c_i32, _c_vp, _c_i32, _c_dbl, _c_vp, _c_vp, _c_vp, _c_size,
+                                             _c_vp, _c_vp, _c_vp, _c_vp]),
+        "pop_trace_recorded": (_c_i32, []),
         "pop_decode_down": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, ctypes.c_int, _c_vp, _c_i32,
                                            _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_size, _c_vp]),
     }
@@ -123,7 +129,8 @@ def pop_decode_workspace_bytes(batch: int, d: int, d_ff: int) -> int:
 
 
 def workspace(nbytes: int, device=None) -> torch.Tensor:
-    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device or "cuda")
+    """A device workspace (zero-filled; the library does not require it)."""
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device or "cuda")
 
 
 # ---------------------------------------------------------------- device calls
@@ -170,6 +177,40 @@ def pop_decode_ffn(x, W_gate, W_up, W_downT, R, C, r: float, *, y=None, selected
         _ptr(x), batch, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
         _ptr(R), R.numel(), _ptr(C), C.numel(), float(r), _ptr(y), _ptr(S), _ptr(ws), ws.numel(),
         _stream(stream)))
+    return (y, S) if selected else y
+
+
+class TwoStream:
+    """An auxiliary stream and the fork/join events pop_decode_ffn_2s needs
+    (created once; reusable across calls and graph captures)."""
+
+    def __init__(self, device=None):
+        self.aux = torch.cuda.Stream(device=device)
+        self.fork = torch.cuda.Event()
+        self.join = torch.cuda.Event()
+        # torch creates the underlying events lazily: record once so they exist
+        self.fork.record()
+        self.join.record()
+        torch.cuda.synchronize()
+
+
+def pop_decode_ffn_2s(x, W_gate, W_up, W_downT, R, C, r: float, two: TwoStream, *, y=None, selected: bool = False,
+                      ws=None, stream=None):
+    """pop_decode_ffn with the candidate chain on two.aux (same result)."""
+    _dev(x, W_gate, W_up, W_downT, R, C)
+    batch, d = x.shape
+    d_ff = W_gate.shape[0]
+    dev = W_gate.device
+    if y is None:
+        y = torch.empty((batch, d), dtype=torch.float32, device=dev)
+    S = torch.empty(_k(d_ff, r, R.numel(), C.numel()), dtype=torch.int32, device=dev) if selected else None
+    if ws is None:
+        ws = workspace(pop_decode_workspace_bytes(batch, d, d_ff), dev)
+    _check("pop_decode_ffn_2s", lib.pop_decode_ffn_2s(
+        _ptr(x), batch, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
+        _ptr(R), R.numel(), _ptr(C), C.numel(), float(r), _ptr(y), _ptr(S), _ptr(ws), ws.numel(),
+        _stream(stream), ctypes.c_void_p(two.aux.cuda_stream), ctypes.c_void_p(two.fork.cuda_event),
+        ctypes.c_void_p(two.join.cuda_event)))
     return (y, S) if selected else y
 
 
@@ -268,3 +309,48 @@ def pop_decode_down(z, W_downT, R, selected, positions, *, n_R=None, y=None, ws=
         _ptr(z), batch, n_A, _ptr(W_downT), d, d_ff, _dtype(W_downT), _ptr(R), nR, _ptr(selected), _ptr(positions), k,
         _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+# ---------------------------------------------------------------- kernel tracing
+class Tracer:
+    """Arms libpop's kernel tracing with raw HIP events (created through the HIP
+    runtime) and reads the per-kernel elapsed times back.
+
+        with Tracer(n) as tr:
+            ... libpop calls ...
+        torch.cuda.synchronize(); tr.intervals_ms()
+    """
+
+    def __init__(self, n_events: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(_c_vp)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _c_vp, _c_vp]
+        self.hip.hipEventDestroy.argtypes = [_c_vp]
+        self.n = int(n_events)
+        self.events = (_c_vp * self.n)()
+        for i in range(self.n):
+            h = _c_vp()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[i] = h
+        self.used = 0
+
+    def __enter__(self):
+        _check("pop_set_trace_events", lib.pop_set_trace_events(self.events, self.n))
+        return self
+
+    def __exit__(self, *exc):
+        self.used = int(lib.pop_trace_recorded())
+        lib.pop_set_trace_events(None, 0)
+        return False
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), self.events[i], self.events[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.events[i])
+        self.n = 0

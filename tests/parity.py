@@ -85,9 +85,9 @@ def check_decode(y, S, ws, x, w, R, C, r, dtype, z_ref=None):
     assert len(S) == k
     ref = oracle.decode_step(x, w["W_gate"], w["W_up"], w["W_down"], R, C, r)
     n_A = n_R + n_C
-    wsf = host(ws).view(np.float32)
+    wsf = host(ws).view(np.float32)[64:]          # z starts at byte 256
     z_dev = wsf[: B * n_A].reshape(B, n_A).astype(np.float64)
-    zb = (B * d_ff * 4 + 16 + 255) // 256 * 256 // 4   # scores start at align_up(4*B*d_ff + 16, 256) bytes
+    zb = (B * d_ff * 4 + 16 + 255) // 256 * 256 // 4   # scores: 256 + align_up(4*B*d_ff + 16, 256) bytes
     sc_dev = wsf[zb: zb + n_C].astype(np.float64)
     # intermediate and scores
     zr = ref["z"]

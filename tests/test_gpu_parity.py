@@ -260,3 +260,121 @@ def test_stages_compose_bitwise():
     yref = pop.pop_dense_ffn_decode(xd, Wg, Wu, WdT)
     torch.cuda.synchronize()
     assert torch.equal(yd, yref)
+
+
+@pytest.mark.parametrize("dtype,d,d_ff", [("bf16", 4096, 11008), ("bf16", 1032, 2900), ("f32", 256, 688)])
+def test_decode_b1_fused_graph_replay(dtype, d, d_ff):
+    """Batch 1 runs the row-streaming kernels: every replay of a captured step
+    must match eager, bit for bit."""
+    say(f"[decode b1] fused path, graph replay, {dtype} d={d} d_ff={d_ff}")
+    c = synth.random_case(61 + d, 64, d, d_ff, 1, dtype)
+    Xd = dev(c["X"], dtype)
+    Wg, Wu, WdT = dev(c["W_gate"], dtype), dev(c["W_up"], dtype), dev(c["W_downT"], dtype)
+    R, C, P = pop.pop_prefill_partition(Xd, Wu, 0.299, 0.1)
+    ws = pop.workspace(pop.pop_decode_workspace_bytes(1, d, d_ff))
+    xs = [synth.random_case(70 + t, 1, d, 1, 1, dtype)["x"] for t in range(3)]
+    eager = []
+    for xt in xs:
+        y, S = pop.pop_decode_ffn(dev(xt, dtype), Wg, Wu, WdT, R, C, 0.299, selected=True, ws=ws)
+        torch.cuda.synchronize()
+        check_decode(y, S, ws, xt, c, host(R), host(C), 0.299, dtype)
+        eager.append(y)
+    x_in = dev(xs[0], dtype)
+    yg = torch.empty_like(eager[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pop.pop_decode_ffn(x_in, Wg, Wu, WdT, R, C, 0.299, y=yg, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pop.pop_decode_ffn(x_in, Wg, Wu, WdT, R, C, 0.299, y=yg, ws=ws)
+    for rep in range(6):
+        t = rep % 3
+        x_in.copy_(dev(xs[t], dtype))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, eager[t]), f"replay {rep} differs from eager"
+
+
+@pytest.mark.parametrize("n,kind", [(1, "rand"), (7, "ties"), (64, "rand"), (65, "ties"), (2201, "rand"),
+                                    (2201, "ties"), (3788, "zeros"), (4096, "rand"), (4097, "rand"),
+                                    (4097, "ties"), (9000, "rand"), (32768, "ties")])
+def test_select_stage_exact(n, kind):
+    """pop_decode_select against the oracle's selection rule on the same fp32
+    scores, at sizes on both sides of the one-wave limit (4096), with heavy
+    ties and every k from 0 to n on small sizes."""
+    say(f"[select] n={n} {kind}")
+    g = np.random.default_rng(n + len(kind))
+    if kind == "rand":
+        sc = g.uniform(0, 2, n).astype(np.float32)
+    elif kind == "ties":
+        sc = g.integers(0, 5, n).astype(np.float32)
+    else:
+        sc = np.zeros(n, np.float32)
+    C = np.sort(g.choice(max(n * 3, 8), n, replace=False)).astype(np.int32)
+    ks = range(0, n + 1) if n <= 65 else sorted({0, 1, n // 3, n // 2, n - 1, n})
+    scd = torch.from_numpy(sc).cuda()
+    Cd = torch.from_numpy(C).cuda()
+    for k in ks:
+        Q, S = pop.pop_decode_select(scd, Cd, k)
+        torch.cuda.synchronize()
+        exp_S = oracle.select_candidates(C, sc.astype(np.float64), k)
+        assert np.array_equal(host(S), exp_S), (n, kind, k)
+        assert np.array_equal(C[host(Q)], exp_S)
+
+
+@pytest.mark.parametrize("n,kind", [(1, "rand"), (10, "ties"), (688, "ties"), (11008, "rand"), (18944, "ties"),
+                                    (32768, "rand")])
+def test_partition_select_stage_exact(n, kind):
+    """pop_partition_select against the oracle's partition of the same fp32 importance."""
+    say(f"[partition select] n={n} {kind}")
+    g = np.random.default_rng(7 * n + len(kind))
+    I = (g.uniform(0, 3, n) if kind == "rand" else g.integers(0, 4, n)).astype(np.float32)
+    Id = torch.from_numpy(I).cuda()
+    for r, gam in ((0.3, 0.1), (0.0, 0.1), (0.5, 0.5), (0.9, 0.05)):
+        R, C, P = pop.pop_partition_select(Id, r, gam)
+        torch.cuda.synchronize()
+        eR, eC, eP = oracle.partition(I.astype(np.float64), r, gam)
+        assert np.array_equal(host(R), eR) and np.array_equal(host(C), eC) and np.array_equal(host(P), eP), (n, r, gam)
+
+
+@pytest.mark.parametrize("d,d_ff,r", [(4096, 11008, 0.299), (3584, 18944, 0.5), (1032, 2900, 0.3)])
+def test_decode_two_streams_bitwise(d, d_ff, r):
+    """pop_decode_ffn_2s gives the bits of pop_decode_ffn, eager and as a
+    captured graph replayed several times with other eager work between."""
+    say(f"[decode 2s] d={d} d_ff={d_ff} r={r}")
+    c = synth.random_case(91 + d, 32, d, d_ff, 1, "bf16")
+    Xd = dev(c["X"], "bf16")
+    Wg, Wu, WdT = dev(c["W_gate"], "bf16"), dev(c["W_up"], "bf16"), dev(c["W_downT"], "bf16")
+    R, C, P = pop.pop_prefill_partition(Xd, Wu, r, 0.1)
+    two = pop.TwoStream()
+    ws1 = pop.workspace(pop.pop_decode_workspace_bytes(1, d, d_ff))
+    ws2 = pop.workspace(pop.pop_decode_workspace_bytes(1, d, d_ff))
+    xs = [dev(synth.random_case(95 + t, 1, d, 1, 1, "bf16")["x"], "bf16") for t in range(3)]
+    ref = []
+    for xt in xs:
+        y1, S1 = pop.pop_decode_ffn(xt, Wg, Wu, WdT, R, C, r, selected=True, ws=ws1)
+        y2, S2 = pop.pop_decode_ffn_2s(xt, Wg, Wu, WdT, R, C, r, two, selected=True, ws=ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(S1, S2)
+        ref.append(y1)
+    x_in = xs[0].clone()
+    yg = torch.empty_like(ref[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pop.pop_decode_ffn_2s(x_in, Wg, Wu, WdT, R, C, r, two, y=yg, ws=ws2)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pop.pop_decode_ffn_2s(x_in, Wg, Wu, WdT, R, C, r, two, y=yg, ws=ws2)
+    for rep in range(6):
+        t = rep % 3
+        x_in.copy_(xs[t])
+        g.replay()
+        pop.pop_decode_ffn(xs[(t + 1) % 3], Wg, Wu, WdT, R, C, r, ws=ws1)  # other eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ref[t]), f"replay {rep} differs"
