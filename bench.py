@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing sample")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run 3 device-to-device copies of this many MiB (a known-size kernel that "
+                         "calibrates the profiler's HBM byte counters)")
     ap.add_argument("--two-streams", action="store_true",
                     help="decode through pop_decode_ffn_2s (candidate chain on a second stream)")
     return ap.parse_args()
@@ -76,7 +79,7 @@ def main():
     import numpy as np
     import torch
 
-    from online_structured_ffn_amd import configs, metrics, pop, synth
+    from online_structured_ffn_amd import configs, metrics, pop, profiling, synth
 
     w = configs.BY_NAME[args.workload]
     if w.experts:
@@ -117,6 +120,17 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs generated on the device in {time.time() - t0:.1f} s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 3 copies of {args.copy_probe_mib} MiB ({n} bytes read and written each)")
+        del src, dst
 
     def prefill():
         for l in range(L):
@@ -220,13 +234,13 @@ def main():
     S = min(args.kernel_steps, T)
     # which kernels each call launches (the library's dispatch rules)
     vec = 8 if e == 2 else 4
-    fused = B == 1 and d <= 8 * 64 * vec
+    fused = B == 1 and d <= 4 * 256 * vec
     labels_pre = ["k_colsq_partial", "k_sum_chunks(s2)", "k_importance", "k_partition"]
     if fused:
-        labels_dec = ((["k_decode_fused(candidates)"] if n_C > 0 else []) + (["k_topk"] if n_C > 4096 else [])
-                      + ["k_decode_fused(top-k + retained)"] + (["k_down_selected"] if k > 0 else [])
+        labels_dec = ((["k_candidate_rows"] if n_C > 0 else []) + (["k_topk"] if n_C > 4096 else [])
+                      + ["k_retained_rows(+top-k)"] + (["k_down_selected"] if k > 0 else [])
                       + ["k_sum_chunks(y)"])
-        labels_dense = ["k_decode_fused(dense)", "k_sum_chunks(y)"]
+        labels_dense = ["k_retained_rows(dense)", "k_sum_chunks(y)"]
     else:
         labels_dec = ["k_gateup"] + (["k_topk"] if n_C > 0 else []) + ["k_down_partial", "k_sum_chunks(y)"]
         labels_dense = ["k_gateup(dense)", "k_down_partial(dense)", "k_sum_chunks(y)"]
@@ -250,52 +264,66 @@ def main():
                 marks.append((labels_dense, a, pop.lib.pop_trace_recorded()))
 
     n_ev = L * (len(labels_pre) + 1) + S * L * (len(labels_dec) + len(labels_dense) + 2) + 8
-    tracer = pop.Tracer(n_ev)
-    torch.cuda.synchronize()
-    h0 = time.perf_counter()
-    with tracer:
-        kernel_pass([])
-    host_s = time.perf_counter() - h0
-    torch.cuda.synchronize()
-    torch.cuda._sleep(1000)
-    torch.cuda.synchronize()
-    a = Ev(torch).record()
-    torch.cuda._sleep(20_000_000)
-    b = Ev(torch).record()
-    torch.cuda.synchronize()
-    cyc_per_ms = 20_000_000 / max(a.ms(b), 1e-3)
-    lead_ms = max(50.0, 3.0 * host_s * 1e3)
-    torch.cuda._sleep(int(cyc_per_ms * lead_ms))
-    marks = []
-    with tracer:
-        kernel_pass(marks)
-    torch.cuda.synchronize()
-    per = {}
-    gaps = 0.0
-    span = tracer.elapsed_ms(marks[0][1], marks[-1][2] - 1)
-    busy = 0.0
-    for labels, i0, i1 in marks:
-        assert i1 - i0 == len(labels) + 1, (labels, i0, i1)
-        for j, name in enumerate(labels):
-            dt = tracer.elapsed_ms(i0 + j, i0 + j + 1)
-            per.setdefault(name, []).append(dt)
-            busy += dt
-    tracer.close()
-    kus = {name: float(np.mean(v)) * 1e3 for name, v in per.items()}
-    log(f"[bench] kernel pass: host enqueue {host_s * 1e3:.1f} ms, lead {lead_ms:.0f} ms, "
-        f"traced kernels cover {busy / span:.3f} of the span")
-    log("[bench] kernels (us): " + ", ".join(f"{n} {v:.2f}" for n, v in kus.items()))
+
+    def traced(flags):
+        tracer = pop.Tracer(n_ev, flags)
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        with tracer:
+            kernel_pass([])
+        host_s = time.perf_counter() - h0
+        torch.cuda.synchronize()
+        torch.cuda._sleep(1000)
+        torch.cuda.synchronize()
+        a = Ev(torch).record()
+        torch.cuda._sleep(20_000_000)
+        b = Ev(torch).record()
+        torch.cuda.synchronize()
+        cyc_per_ms = 20_000_000 / max(a.ms(b), 1e-3)
+        lead_ms = max(50.0, 3.0 * host_s * 1e3)
+        torch.cuda._sleep(int(cyc_per_ms * lead_ms))
+        marks = []
+        with tracer:
+            kernel_pass(marks)
+        torch.cuda.synchronize()
+        per = {}
+        span = tracer.elapsed_ms(marks[0][1], marks[-1][2] - 1)
+        busy = 0.0
+        for labels, i0, i1 in marks:
+            assert i1 - i0 == len(labels) + 1, (labels, i0, i1)
+            for j, name in enumerate(labels):
+                dt = tracer.elapsed_ms(i0 + j, i0 + j + 1)
+                per.setdefault(name, []).append(dt)
+                busy += dt
+        tracer.close()
+        kus = {name: float(np.mean(v)) * 1e3 for name, v in per.items()}
+        log(f"[bench] kernel pass (event flags {flags:#x}): host enqueue {host_s * 1e3:.1f} ms, "
+            f"lead {lead_ms:.0f} ms, traced kernels cover {busy / span:.3f} of the span")
+        log("[bench] kernels (us): " + ", ".join(f"{n} {v:.2f}" for n, v in kus.items()))
+        return kus, busy / span
+
+    # Events without the system-scope fence disturb the kernels between them
+    # least; the default events are reported beside them.
+    kus_fenced, _ = traced(0)
+    kus, coverage = traced(pop.Tracer.DISABLE_SYSTEM_FENCE)
 
     if fused:
-        dom = "k_decode_fused(top-k + retained)"
-        dom_desc = ("k_decode_fused, retained launch (batch-1 decode: gate, up and W_downT rows of every retained "
-                    "channel in one stream, with the one-workgroup candidate top-k beside it)")
+        dom = "k_retained_rows(+top-k)"
+        dom_desc = ("k_retained_rows (batch-1 decode: gate, up and W_downT rows of every retained channel in one "
+                    "stream, with the one-workgroup candidate top-k beside it)")
         dom_bytes = metrics.retained_stream_bytes(d, n_R, n_C, k, e)
     else:
         dom = "k_gateup"
         dom_desc = "k_gateup (decode gate/up over R u C, fused SiLU*up and candidate score)"
         dom_bytes = metrics.gateup_bytes(d, n_A, n_C, B, e)
     dom_us = kus[dom]
+    tname = "pop::bf16s" if e == 2 else "float"
+    if fused:
+        nv = -(-d // (256 * vec))
+        dom_symbol = f"pop::k_retained_rows<{tname}, {1 if nv <= 1 else 2 if nv <= 2 else 4}, false>"
+    else:
+        dom_symbol = None
+    tb = profiling.traffic_bytes(dom_symbol) if dom_symbol and w.name == "llama2_7b_ffn_b1" else None
     dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
     imp_bytes = metrics.importance_bytes(n_tok, d, d_ff, e)
     out = {
@@ -324,7 +352,10 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": None if tb is None else tb[0] + tb[1],
+            "traffic_source": (None if tb is None else
+                               "rocprofv3 FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a 256 MiB copy "
+                               "(profiles/decode_kernels_llama2_7b_b1_hbm_traffic.md)"),
             "bytes_per_launch": dom_bytes,
             "avg_launch_us": round(dom_us, 3),
         },
@@ -347,8 +378,9 @@ def main():
         "prefill_partition_us_per_layer": round(ms_prefill / L * 1e3, 2),
         "prefill_partition_hbm_frac": round(metrics.partition_bytes(n_tok, d, d_ff, e) / (ms_prefill / L * 1e-3)
                                             / 1e9 / HBM_PEAK_GBPS, 4),
-        "kernel_pass_coverage": round(busy / span, 4),
+        "kernel_pass_coverage": round(coverage, 4),
         "kernels_us": {n: round(v, 3) for n, v in kus.items()},
+        "kernels_us_default_events": {n: round(v, 3) for n, v in kus_fenced.items()},
         "importance_gbps": round(imp_bytes / (kus["k_importance"] * 1e-6) / 1e9, 1),
         "cpu_baseline": None,
     }

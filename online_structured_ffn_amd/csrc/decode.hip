@@ -159,25 +159,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 // thread.  Rows go in batches of two, double-buffered: the next batch's loads
 // are in flight while the current batch's dot products are reduced (DPP
 // within each wave, LDS across the four waves, fixed order).
-// k_decode_fused gives its blocks one of three roles by block index:
-//   [0, nbT)            top-k over candidate scores written by an earlier launch;
-//   [nbT, nbT + nbC)    candidate rows: z = SiLU(W_gate x) * (W_up x), score |z|;
-//   [nbT + nbC, grid)   retained rows (block rb_base + ...): z and
-//                       z * W_downT[ch, :] into the thread's accumulators; one
-//                       partial y per block.
-// A decode step launches it twice: the candidates with the first share of the
-// retained blocks, then the top-k block beside the rest of them, so the
-// one-CU top-k runs under the retained stream.  No block waits on another
-// inside a launch.
+// A decode step runs this as two launches: k_candidate_rows (gate/up rows of
+// C: z and scores), then k_retained_rows, whose first block runs the top-k over
+// those scores while the others stream the retained rows (gate, up and W_downT
+// rows: z and a partial y per block), so the one-CU top-k hides under the
+// retained stream.  No block waits on another inside a launch.
 // Launch-shape tunables (overridable with -D for sweeps).
 #ifndef POP_FUSED_RBLOCKS
 #define POP_FUSED_RBLOCKS 512  // most blocks for the retained rows
 #endif
 #ifndef POP_FUSED_CROWS
 #define POP_FUSED_CROWS 4  // candidate rows per block
-#endif
-#ifndef POP_FUSED_R1_PERCENT
-#define POP_FUSED_R1_PERCENT 0  // share of the retained blocks that run with the candidates
 #endif
 #ifndef POP_SEL_ROWS
 #define POP_SEL_ROWS 8  // selected rows per block of k_down_selected
@@ -368,54 +360,71 @@ __global__ __launch_bounds__(kFusedThreads) void k_down_selected(const float* __
   for (int v = 0; v < V; ++v) out[v] = acc[v];
 }
 
+// Loads this thread's x vectors and clears its down accumulators.
+template <typename T, int NV>
+__device__ __forceinline__ void fused_setup(const T* __restrict__ x, int d, u32x4 (&xv)[NV],
+                                            float (&acc)[NV][Vec<T>::N]) {
+  constexpr int V = Vec<T>::N;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int col = j * kFusedThreads * V + (int)threadIdx.x * V;
+    xv[j] = col < d ? ld16(x + col) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[j][v] = 0.f;
+  }
+}
+
+// Candidate rows: block b takes C[b * rows_per_block, ...) and writes their z
+// (after the n_R retained entries) and scores |z|.
+template <typename T, int NV>
+__global__ __launch_bounds__(kFusedThreads) void k_candidate_rows(
+    const T* __restrict__ x, int d, const T* __restrict__ Wg, const T* __restrict__ Wu, int d_ff,
+    const int32_t* __restrict__ C, int n_R, int n_C, float* __restrict__ z, float* __restrict__ score,
+    int rows_per_block) {
+  __shared__ int rows[kFusedMaxRows];
+  __shared__ float part[2][4][2 * kFusedP];
+  u32x4 xv[NV];
+  float acc[NV][Vec<T>::N];
+  fused_setup<T, NV>(x, d, xv, acc);
+  const int r0 = blockIdx.x * rows_per_block;
+  const int nrows = max(0, min(n_C, r0 + rows_per_block) - r0);
+  for (int i = threadIdx.x; i < nrows; i += kFusedThreads) rows[i] = clamp_channel(C[r0 + i], d_ff);
+  __syncthreads();
+  fused_rows<T, NV, false>(rows, nrows, Wg, Wu, (const T*)nullptr, d, xv, part, acc, z, n_R + r0, score + r0);
+}
+
+// Retained rows, with the top-k beside them: blocks [0, nbT) run the top-k
+// over the scores an earlier launch wrote; block nbT + b takes
+// R[b * rows_per_block, ...) (rows b * rows_per_block, ... with kIdentity),
+// writes their z and its partial y = sum over its rows of z * W_downT[ch, :].
 template <typename T, int NV, bool kIdentity>
-__global__ __launch_bounds__(kFusedThreads) void k_decode_fused(
+__global__ __launch_bounds__(kFusedThreads) void k_retained_rows(
     const T* __restrict__ x, int d, const T* __restrict__ Wg, const T* __restrict__ Wu, const T* __restrict__ WdT,
-    int d_ff, const int32_t* __restrict__ R, int n_R, const int32_t* __restrict__ C, int n_C, int k,
-    float* __restrict__ z, float* __restrict__ score, int32_t* __restrict__ positions,
-    int32_t* __restrict__ selected, float* __restrict__ partial, int nbT, int nbC, int rows_per_cblock,
-    int rows_per_rblock, int rb_base) {
+    int d_ff, const int32_t* __restrict__ R, int n_R, const float* __restrict__ score,
+    const int32_t* __restrict__ C, int n_C, int k, int32_t* __restrict__ positions,
+    int32_t* __restrict__ selected, float* __restrict__ z, float* __restrict__ partial, int nbT,
+    int rows_per_block) {
   constexpr int V = Vec<T>::N;
   __shared__ SelShared<kFusedThreads, kFusedTopkMaxN> sel;
   __shared__ int rows[kFusedMaxRows];
   __shared__ float part[2][4][2 * kFusedP];
-  const int tid = threadIdx.x;
-  const int bid = blockIdx.x;
-  if (bid < nbT) {  // the top-k over scores an earlier launch wrote
+  if ((int)blockIdx.x < nbT) {
     topk_block(score, n_C, k, C, positions, selected, sel);
     return;
   }
   u32x4 xv[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int col = j * kFusedThreads * V + tid * V;
-    xv[j] = col < d ? ld16(x + col) : u32x4{0u, 0u, 0u, 0u};
-  }
   float acc[NV][V];
-#pragma unroll
-  for (int j = 0; j < NV; ++j)
-#pragma unroll
-    for (int v = 0; v < V; ++v) acc[j][v] = 0.f;
-
-  if (bid < nbT + nbC) {  // candidate rows: z and scores
-    const int r0 = (bid - nbT) * rows_per_cblock;
-    const int nrows = max(0, min(n_C, r0 + rows_per_cblock) - r0);
-    for (int i = tid; i < nrows; i += kFusedThreads) rows[i] = clamp_channel(C[r0 + i], d_ff);
-    __syncthreads();
-    fused_rows<T, NV, false>(rows, nrows, Wg, Wu, WdT, d, xv, part, acc, z, n_R + r0, score + r0);
-    return;
-  }
-
-  const int rb = rb_base + bid - nbT - nbC;  // retained rows: z and the down contribution
-  const int r0 = rb * rows_per_rblock;
-  const int nrows = max(0, min(n_R, r0 + rows_per_rblock) - r0);
-  for (int i = tid; i < nrows; i += kFusedThreads) rows[i] = kIdentity ? r0 + i : clamp_channel(R[r0 + i], d_ff);
+  fused_setup<T, NV>(x, d, xv, acc);
+  const int rb = blockIdx.x - nbT;
+  const int r0 = rb * rows_per_block;
+  const int nrows = max(0, min(n_R, r0 + rows_per_block) - r0);
+  for (int i = threadIdx.x; i < nrows; i += kFusedThreads) rows[i] = kIdentity ? r0 + i : clamp_channel(R[r0 + i], d_ff);
   __syncthreads();
   fused_rows<T, NV, true>(rows, nrows, Wg, Wu, WdT, d, xv, part, acc, z, r0, nullptr);
   float* out = partial + (int64_t)rb * d;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int col = j * kFusedThreads * V + tid * V;
+    const int col = j * kFusedThreads * V + (int)threadIdx.x * V;
     if (col < d) {
 #pragma unroll
       for (int v = 0; v < V; ++v) out[col + v] = acc[j][v];
@@ -662,7 +671,7 @@ static void launch_down(hipStream_t st, const float* z, int B, int n_A, const vo
                      n_live > 0 ? p.n_chunks : 0, n_out, y, (unsigned int*)nullptr, 0);
 }
 
-// Batch-1 decode step through k_decode_fused: false when d is too wide for
+// Batch-1 decode step through k_candidate_rows and k_retained_rows: false when d is too wide for
 // the kernel's per-thread columns (the caller then runs the stage kernels).
 template <typename T>
 static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, const void* Wu, const void* WdT,
@@ -688,9 +697,6 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
   }
   if (rows_per_cblock > kFusedMaxRows || rows_per_rblock > kFusedMaxRows) return false;
   const bool fuse_topk = n_C > 0 && n_C <= kFusedTopkMaxN;
-  // Retained blocks in launch 1 (with the candidates); the rest go beside the top-k.
-  const int nbR1 = (n_C > 0 && k > 0) ? nbR * POP_FUSED_R1_PERCENT / 100 : nbR;
-  const int nbR2 = nbR - nbR1;
   const int n_schunks = k > 0 ? (k + POP_SEL_ROWS - 1) / POP_SEL_ROWS : 0;
   float* partial = (float*)w.down;
   float* partial_s = partial + (int64_t)nbR * d;
@@ -702,20 +708,28 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
   } else {                     \
     MACRO(4);                  \
   }
-  auto fused = [&](hipStream_t sx, int nbT_, int nbC_, int nbR_, int rb_base) {
-    const dim3 grid(nbT_ + nbC_ + nbR_);
-    hipStream_t st = sx;
-#define POP_FUSED(NVT)                                                                                          \
-  if (identity)                                                                                                 \
-    POP_LAUNCH((k_decode_fused<T, NVT, true>), grid, dim3(kFusedThreads), 0, st, (const T*)x, d, (const T*)Wg,   \
-               (const T*)Wu, (const T*)WdT, d_ff, R, n_R, C, n_C, k, w.z, w.score, w.Q, w.sel, partial, nbT_,     \
-               nbC_, rows_per_cblock, rows_per_rblock, rb_base);                                                 \
-  else                                                                                                          \
-    POP_LAUNCH((k_decode_fused<T, NVT, false>), grid, dim3(kFusedThreads), 0, st, (const T*)x, d, (const T*)Wg,  \
-               (const T*)Wu, (const T*)WdT, d_ff, R, n_R, C, n_C, k, w.z, w.score, w.Q, w.sel, partial, nbT_,     \
-               nbC_, rows_per_cblock, rows_per_rblock, rb_base)
-    POP_NV_DISPATCH(POP_FUSED)
-#undef POP_FUSED
+  auto candidates = [&](hipStream_t sx) {
+    if (nbC == 0) return;
+#define POP_CAND(NVT)                                                                                         \
+  POP_LAUNCH((k_candidate_rows<T, NVT>), dim3(nbC), dim3(kFusedThreads), 0, sx, (const T*)x, d, (const T*)Wg, \
+             (const T*)Wu, d_ff, C, n_R, n_C, w.z, w.score, rows_per_cblock)
+    POP_NV_DISPATCH(POP_CAND)
+#undef POP_CAND
+  };
+  auto retained = [&](hipStream_t sx, int nbT) {
+    if (nbT + nbR == 0) return;
+    const dim3 grid(nbT + nbR);
+#define POP_RET(NVT)                                                                                                \
+  if (identity)                                                                                                     \
+    POP_LAUNCH((k_retained_rows<T, NVT, true>), grid, dim3(kFusedThreads), 0, sx, (const T*)x, d, (const T*)Wg,     \
+               (const T*)Wu, (const T*)WdT, d_ff, R, n_R, (const float*)w.score, C, n_C, k, w.Q, w.sel, w.z,       \
+               partial, nbT, rows_per_rblock);                                                                      \
+  else                                                                                                              \
+    POP_LAUNCH((k_retained_rows<T, NVT, false>), grid, dim3(kFusedThreads), 0, sx, (const T*)x, d, (const T*)Wg,    \
+               (const T*)Wu, (const T*)WdT, d_ff, R, n_R, (const float*)w.score, C, n_C, k, w.Q, w.sel, w.z,       \
+               partial, nbT, rows_per_rblock)
+    POP_NV_DISPATCH(POP_RET)
+#undef POP_RET
   };
 #undef POP_NV_DISPATCH
   auto selected_rows = [&](hipStream_t sx) {
@@ -730,21 +744,17 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
     // `aux` beside the retained stream on `st`, joined before the sum.
     (void)hipEventRecord(fork, st);
     (void)hipStreamWaitEvent(aux, fork, 0);
-    if (nbC > 0) fused(aux, 0, nbC, 0, 0);
-    if (nbR > 0) fused(st, 0, 0, nbR, 0);
+    candidates(aux);
+    retained(st, 0);
     launch_select(aux, w.score, n_C, C, k, w.Q, w.sel);
     selected_rows(aux);
     (void)hipEventRecord(join, aux);
     (void)hipStreamWaitEvent(st, join, 0);
   } else {
-    // launch 1: candidate rows (scores) and the first retained blocks
-    if (nbC + nbR1 > 0) fused(st, 0, nbC, nbR1, 0);
+    candidates(st);                                                          // launch 1
     if (n_C > 0 && !fuse_topk) launch_select(st, w.score, n_C, C, k, w.Q, w.sel);
-    // launch 2: the top-k block beside the remaining retained blocks
-    const int nbT = fuse_topk ? 1 : 0;
-    if (nbT + nbR2 > 0) fused(st, nbT, 0, nbR2, nbR1);
-    // launch 3: the selected candidates' down rows
-    selected_rows(st);
+    retained(st, fuse_topk ? 1 : 0);                                         // launch 2
+    selected_rows(st);                                                       // launch 3
   }
   // launch 4: fixed-order sum of every partial
   POP_LAUNCH(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(1024), 0, st, (const float*)partial, nbR + n_schunks,

@@ -321,17 +321,21 @@ class Tracer:
         torch.cuda.synchronize(); tr.intervals_ms()
     """
 
-    def __init__(self, n_events: int):
+    # hipEventDisableSystemFence: the event's record skips the system-scope
+    # release (a cache writeback between every two kernels otherwise).
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n_events: int, flags: int = 0):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(_c_vp)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(_c_vp), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _c_vp, _c_vp]
         self.hip.hipEventDestroy.argtypes = [_c_vp]
         self.n = int(n_events)
         self.events = (_c_vp * self.n)()
         for i in range(self.n):
             h = _c_vp()
-            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(h), ctypes.c_uint(flags)) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self.events[i] = h
         self.used = 0
 
