@@ -2,15 +2,16 @@
 """Benchmark of the POP channel-pruned gated-MLP path on one MI355X.
 
 One step is one whole request of the workload with every input already in
-HBM: the prefill partition of every layer (column norm, importance, three-region
-select) followed by every decode step over every layer (gate/up over R u C with
-fused scores, candidate top-k, gathered down-projection).  The layers do not
+HBM: the prefill of every layer (the dense prompt FFN on the matrix cores, then
+the partition: column norm, importance, three-region select) followed by every
+decode step over every layer (gate/up over R u C with fused scores, candidate
+top-k, gathered down-projection).  The layers do not
 chain: each has its own seeded prompt and decode inputs.  Steps are replayed as
 HIP graphs.
 
 Printed: ONE JSON line on stdout.  value = decode tokens per second per layer
-over the whole step (B * T * layers / step time), i.e. the prefill partition is
-included in the denominator.
+over the whole step (B * T * layers / step time), i.e. the prefill is included
+in the denominator.
 
 Per-kernel durations for the roofline come from a second, eager pass in which
 HIP events bracket each stage call; a spin kernel queued first keeps the GPU
@@ -116,6 +117,8 @@ def main():
     x_buf = torch.empty((L, B, d), dtype=Xdec.dtype, device=dev)
     y = torch.empty((L, B, d), dtype=torch.float32, device=dev)
     ws_pre = pop.workspace(pop.pop_prefill_workspace_bytes(n_tok, d, d_ff), dev)
+    ws_ffn = pop.workspace(max(pop.pop_dense_ffn_prefill_workspace_bytes(n_tok, d, d_ff, w.dtype), 256), dev)
+    Yp = torch.empty((n_tok, d), dtype=torch.float32, device=dev)   # prompt FFN output (layers do not chain)
     ws_dec = pop.workspace(pop.pop_decode_workspace_bytes(B, d, d_ff), dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs generated on the device in {time.time() - t0:.1f} s "
@@ -132,9 +135,24 @@ def main():
         log(f"[bench] copy probe: 3 copies of {args.copy_probe_mib} MiB ({n} bytes read and written each)")
         del src, dst
 
+    def prompt_ffn(l):
+        pop.pop_dense_ffn_prefill(X[l], Wg[l], Wu[l], WdT[l], Y=Yp, ws=ws_ffn)
+
+    def partition(l):
+        pop.pop_prefill_partition(X[l], Wu[l], w.r, w.gamma, out=(R[l], C[l], P[l], None), ws=ws_pre)
+
     def prefill():
         for l in range(L):
-            pop.pop_prefill_partition(X[l], Wu[l], w.r, w.gamma, out=(R[l], C[l], P[l], None), ws=ws_pre)
+            prompt_ffn(l)
+            partition(l)
+
+    def prompt_ffn_layers():
+        for l in range(L):
+            prompt_ffn(l)
+
+    def partition_layers():
+        for l in range(L):
+            partition(l)
 
     two = pop.TwoStream() if args.two_streams else None
 
@@ -164,8 +182,8 @@ def main():
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graphs = {}
-    for name, fn in (("prefill", prefill), ("decode", decode_layers), ("decode_1s", decode_layers_1s),
-                     ("dense", dense_layers)):
+    for name, fn in (("prefill", prefill), ("prompt_ffn", prompt_ffn_layers), ("partition", partition_layers),
+                     ("decode", decode_layers), ("decode_1s", decode_layers_1s), ("dense", dense_layers)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
@@ -197,7 +215,10 @@ def main():
     log(f"[bench] step {ms_step:.2f} ms -> {value:,.0f} tokens/s/layer")
 
     # ------------------------------------------------------------ component timings (graphs)
-    ms_prefill = timed(lambda: graphs["prefill"].replay(), 5)
+    ms_prefill = timed(lambda: graphs["partition"].replay(), 5)
+    ms_pffn = timed(lambda: graphs["prompt_ffn"].replay(), 3)
+    pffn_flops = metrics.prefill_ffn_flops(n_tok, d, d_ff)
+    pffn_tflops = pffn_flops / (ms_pffn / L * 1e-3) / 1e12
 
     def decode_only():
         for t in range(T):
@@ -224,7 +245,8 @@ def main():
     log(f"[bench] decode {t_ls * 1e3:.1f} us/layer-step ({bytes_ls / (t_ls * 1e-3) / 1e9:.0f} GB/s; "
         f"pop_decode_ffn graph {ms_dec_1s / (T * L) * 1e3:.1f} us), "
         f"dense {t_ls_dense * 1e3:.1f} us ({bytes_dense / (t_ls_dense * 1e-3) / 1e9:.0f} GB/s), "
-        f"prefill partition {ms_prefill / L * 1e3:.1f} us/layer")
+        f"prefill partition {ms_prefill / L * 1e3:.1f} us/layer, "
+        f"prompt FFN {ms_pffn / L * 1e3:.1f} us/layer ({pffn_tflops:.0f} TFLOP/s)")
 
     # ------------------------------------------------------------ per-kernel pass (eager, queued ahead)
     # The same composite calls as the timed region, with libpop's trace hook
@@ -236,6 +258,9 @@ def main():
     vec = 8 if e == 2 else 4
     fused = B == 1 and d <= 4 * 256 * vec
     labels_pre = ["k_colsq_partial", "k_sum_chunks(s2)", "k_importance", "k_partition"]
+    n_pass = -(-n_tok // 4096)
+    labels_ffn = (["k_prompt_gateup", "k_prompt_down"] if e == 2 else
+                  ["k_prompt_gateup_f32", "k_prompt_down_f32"]) * n_pass
     if fused:
         labels_dec = ((["k_candidate_rows"] if n_C > 0 else []) + (["k_topk"] if n_C > 4096 else [])
                       + ["k_retained_rows(+top-k)"] + (["k_down_selected"] if k > 0 else [])
@@ -247,8 +272,12 @@ def main():
 
     def kernel_pass(marks):
         for l in range(L):
+            if n_tok > 0:
+                a = pop.lib.pop_trace_recorded()
+                prompt_ffn(l)
+                marks.append((labels_ffn, a, pop.lib.pop_trace_recorded()))
             a = pop.lib.pop_trace_recorded()
-            pop.pop_prefill_partition(X[l], Wu[l], w.r, w.gamma, out=(R[l], C[l], P[l], None), ws=ws_pre)
+            partition(l)
             marks.append((labels_pre, a, pop.lib.pop_trace_recorded()))
         for t in range(S):
             x_buf.copy_(Xdec[t])
@@ -263,7 +292,7 @@ def main():
                 pop.pop_dense_ffn_decode(x_buf[l], Wg[l], Wu[l], WdT[l], y=y[l], ws=ws_dec)
                 marks.append((labels_dense, a, pop.lib.pop_trace_recorded()))
 
-    n_ev = L * (len(labels_pre) + 1) + S * L * (len(labels_dec) + len(labels_dense) + 2) + 8
+    n_ev = L * (len(labels_pre) + len(labels_ffn) + 2) + S * L * (len(labels_dec) + len(labels_dense) + 2) + 8
 
     def traced(flags):
         tracer = pop.Tracer(n_ev, flags)
@@ -343,7 +372,7 @@ def main():
             "workload": w.name, "layers": L, "d": d, "d_ff": d_ff, "r_ffn": w.r, "gamma": w.gamma,
             "prompt_tokens": n_tok, "decode_steps": T, "decode_batch": B, "hip_graphs": True,
             "streams": 1 if two is None else 2,
-            "step": "prefill partition of every layer + every decode step over every layer",
+            "step": "prefill (dense prompt FFN + partition) of every layer + every decode step over every layer",
         },
         "roofline": {
             "kernel": dom_desc,
@@ -376,6 +405,13 @@ def main():
         "speedup_vs_dense": round(t_ls_dense / t_ls, 4),
         "ideal_speedup_bytes": round(bytes_dense / bytes_ls, 4),
         "prefill_partition_us_per_layer": round(ms_prefill / L * 1e3, 2),
+        "prompt_ffn": {
+            "us_per_layer": round(ms_pffn / L * 1e3, 2),
+            "flops_per_layer": pffn_flops,
+            "tflops": round(pffn_tflops, 1),
+            "mfma_frac_bf16_dense_peak": round(pffn_tflops / 2500.0, 4) if e == 2 else None,
+            "kernels": "k_prompt_gateup + k_prompt_down (v_mfma_f32_16x16x32_bf16)" if e == 2 else "fp32 FMA",
+        },
         "prefill_partition_hbm_frac": round(metrics.partition_bytes(n_tok, d, d_ff, e) / (ms_prefill / L * 1e-3)
                                             / 1e9 / HBM_PEAK_GBPS, 4),
         "kernel_pass_coverage": round(coverage, 4),
@@ -399,9 +435,9 @@ def main():
 
 def cpu_baseline(w, T, budget_s):
     """The CPU oracle, as it stands, on layer 0 of the same workload: one
-    prefill partition and as many decode layer-steps as fit in the budget.
-    Scaled to tokens/s/layer the way the GPU value is: the partition's time is
-    spread over the T decode steps of the request."""
+    prefill (dense prompt FFN and partition) and as many decode layer-steps as
+    fit in the budget.  Scaled to tokens/s/layer the way the GPU value is: the
+    prefill's time is spread over the T decode steps of the request."""
     import numpy as np
 
     import oracle
@@ -414,6 +450,7 @@ def cpu_baseline(w, T, budget_s):
     wts = synth.layer_weights(w, 0)
     X = synth.prompt(w, 0)
     t0 = time.perf_counter()
+    oracle.dense_ffn(X, wts["W_gate"], wts["W_up"], wts["W_down"])
     R, C, _ = oracle.partition(oracle.importance(wts["W_up"], oracle.column_norm(X)), w.r, w.gamma)
     t_part = time.perf_counter() - t0
     times = []
@@ -434,8 +471,9 @@ def cpu_baseline(w, T, budget_s):
         "cores": blas_threads if blas_threads is not None else len(os.sched_getaffinity(0)),
         "host_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
-        "sample": f"layer 0 of {w.name}: 1 prefill partition ({t_part:.2f} s) + {len(times)} decode layer-steps "
-                  f"(median {t_dec * 1e3:.1f} ms), numpy fp64; value = B*T / (t_partition + T * t_step)",
+        "sample": f"layer 0 of {w.name}: 1 prefill (dense prompt FFN + partition, {t_part:.2f} s) + {len(times)} "
+                  f"decode layer-steps (median {t_dec * 1e3:.1f} ms), numpy fp64; "
+                  "value = B*T / (t_prefill + T * t_step)",
     }
 
 

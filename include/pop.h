@@ -267,6 +267,38 @@ pop_status pop_dense_ffn_decode(const void* x, int32_t batch, int32_t d, const v
                                 pop_dtype dt, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Dense prompt FFN (the prefill forward).
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes of pop_dense_ffn_prefill (0 for invalid arguments). */
+size_t pop_dense_ffn_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff, pop_dtype dt);
+
+/*
+ * pop_dense_ffn_prefill — the dense gated MLP over every prompt token, the
+ * prefill forward whose input the partition is computed from (POP notes,
+ * "Loss / training strategy": the online masking starts from the second step,
+ * so the prompt itself runs through all d_ff channels).  Gated MLP of
+ * equation (1), section 3.1 of the batch-wise pruning page:
+ *   Z = SiLU(X W_gate^T) * (X W_up^T),   Y = Z W_down^T = Z W_downT.
+ *
+ *   X        [n_tokens, d] row-major, dtype dt
+ *   W_gate, W_up, W_downT   [d_ff, d] row-major, dtype dt (W_downT is the
+ *            transpose of the nn.Linear weight W_down [d, d_ff])
+ *   Y        [n_tokens, d] fp32, written
+ *   ws       pop_dense_ffn_prefill_workspace_bytes(n_tokens, d, d_ff, dt)
+ *            bytes; holds Z for up to 4096 tokens at a time (the call works
+ *            through the prompt in passes of 4096 tokens).
+ * POP_BF16 multiplies on the matrix cores (bf16 x bf16, fp32 accumulation) and
+ * keeps Z in bf16 (round to nearest even); POP_F32 computes in fp32 FMA.
+ * n_tokens = 0 enqueues nothing.  Errors: BAD_SHAPE (d, d_ff or n_tokens out
+ * of range, d not a multiple of the vector width), INVALID_ARGUMENT (NULL
+ * buffers), MISALIGNED, WORKSPACE_TOO_SMALL, HIP (launch failure).
+ */
+pop_status pop_dense_ffn_prefill(const void* X, int64_t n_tokens, int32_t d, const void* W_gate,
+                                 const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
+                                 float* Y, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Kernel tracing (measurement hook).
  * ------------------------------------------------------------------------- */
 

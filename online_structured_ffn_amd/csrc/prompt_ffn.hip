@@ -1,0 +1,389 @@
+// Dense gated MLP over the prompt tokens: the prefill forward that precedes
+// the pruned decode (POP notes, "Loss / training strategy": the online masking
+// starts from the second step, so the prompt's own FFN runs dense).  The gated
+// MLP is equation (1) of "Batch-wise adaptive pruning ... for language
+// reasoning models", section 3.1:
+//
+//   Z = SiLU(X W_gate^T) * (X W_up^T)      [n_tokens, d_ff]   (workspace)
+//   Y = Z W_down^T = Z W_downT             [n_tokens, d]      fp32
+//
+// bf16: two MFMA GEMMs (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Z is
+// stored in bf16 (round to nearest even), the operand type of the second GEMM.
+// fp32: the same two products as LDS-tiled fp32 FMA.
+//
+// Both bf16 GEMMs use 256-thread blocks of 128 tokens x 64 output columns, a
+// 64-wide reduction slice per stage, double-buffered in LDS through registers.
+// Every operand tile is stored K-contiguous in LDS with a 144-byte row pitch,
+// which makes the 16-lane groups of a fragment read hit all 64 banks once.
+// W_downT is [d_ff, d] (K-major for the second GEMM), so its tile is
+// transposed on the way into LDS.
+#include <hip/hip_runtime.h>
+
+#include "pop_device.h"
+#include "pop_internal.h"
+
+namespace pop {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGThreads = 256;
+constexpr int kBM = 128;         // tokens per block
+constexpr int kBN = 64;          // output columns per block (per matrix)
+constexpr int kBK = 64;          // reduction slice per stage
+constexpr int kLd = kBK + 8;     // LDS row pitch in bf16 elements (144 bytes)
+constexpr int kZPad = 64;        // Z row pitch = d_ff rounded up to this
+constexpr int64_t kChunkTokens = 4096;  // tokens per pass (bounds the workspace)
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Tile order: workgroups are handed to the eight XCDs round robin by index, so
+// block b runs on XCD b % 8.  Tiles are renumbered so that each XCD takes a
+// contiguous run of tiles in (token tile fastest) order: the token tiles that
+// share one weight tile run on the same XCD, close in time, and share its L2.
+__device__ __forceinline__ void tile_of(int bid, int nb, int mt, int& m_tile, int& n_tile) {
+  const int nb8 = nb & ~7;
+  const int q = bid < nb8 ? (bid & 7) * (nb8 >> 3) + (bid >> 3) : bid;
+  m_tile = q % mt;
+  n_tile = q / mt;
+}
+
+// A-operand tile: kBM rows of a K-contiguous matrix (row pitch ld), columns
+// [k0, k0 + kBK); rows >= M and columns >= K read as zero.
+struct ATile {
+  static constexpr int PER = kBM * (kBK / 8) / kGThreads;  // 16-byte chunks per thread
+  u32x4 r[PER];
+  __device__ __forceinline__ void load(const bf16s* __restrict__ A, int64_t ld, int M, int K, int m0, int k0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = threadIdx.x + i * kGThreads;
+      const int row = q >> 3, k = k0 + (q & 7) * 8;
+      const int m = m0 + row;
+      r[i] = (m < M && k < K) ? ld16(A + (int64_t)m * ld + k) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* s) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = threadIdx.x + i * kGThreads;
+      *reinterpret_cast<u32x4*>(s + (q >> 3) * kLd + (q & 7) * 8) = r[i];
+    }
+  }
+};
+
+// ---------------------------------------------------------------- gate / up
+// Wave w covers tokens (w >> 1) * 64 + [0, 64) and channels (w & 1) * 32 +
+// [0, 32) of the block's tile, for both matrices: 4 x 2 fragments each.
+__global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __restrict__ X, int M, int d,
+                                                             const bf16s* __restrict__ Wg,
+                                                             const bf16s* __restrict__ Wu, int d_ff,
+                                                             uint16_t* __restrict__ Z, int ldz, int mt, int nt) {
+  __shared__ __align__(16) uint16_t As[2][kBM * kLd];
+  __shared__ __align__(16) uint16_t Bs[2][2 * kBN * kLd];  // gate rows, then up rows
+  constexpr int BPER = 2 * kBN * (kBK / 8) / kGThreads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int m_tile, n_tile;
+  tile_of(blockIdx.x, mt * nt, mt, m_tile, n_tile);
+  const int m0 = m_tile * kBM, n0 = n_tile * kBN;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  ATile a;
+  u32x4 rb[BPER];
+  auto load_b = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < BPER; ++i) {
+      const int q = tid + i * kGThreads;
+      const int row = q >> 3, k = k0 + (q & 7) * 8;
+      const int ch = n0 + (row & (kBN - 1));
+      const bf16s* W = row < kBN ? Wg : Wu;
+      rb[i] = (ch < d_ff && k < d) ? ld16(W + (int64_t)ch * d + k) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_b = [&](uint16_t* s) {
+#pragma unroll
+    for (int i = 0; i < BPER; ++i) {
+      const int q = tid + i * kGThreads;
+      *reinterpret_cast<u32x4*>(s + (q >> 3) * kLd + (q & 7) * 8) = rb[i];
+    }
+  };
+
+  f32x4 ag[4][2], au[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      ag[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      au[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  const int nk = (d + kBK - 1) / kBK;
+  a.load(X, d, M, d, m0, 0);
+  load_b(0);
+  a.store(As[0]);
+  store_b(Bs[0]);
+  __syncthreads();
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int s = kt & 1;
+    if (kt + 1 < nk) {
+      a.load(X, d, M, d, m0, (kt + 1) * kBK);
+      load_b((kt + 1) * kBK);
+    }
+#pragma unroll
+    for (int kk = 0; kk < kBK; kk += 32) {
+      bf16x8 fa[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = lds_frag(&As[s][(wm * 64 + i * 16 + fr) * kLd + kk + fk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 fg = lds_frag(&Bs[s][(wn * 32 + j * 16 + fr) * kLd + kk + fk]);
+        const bf16x8 fu = lds_frag(&Bs[s][(kBN + wn * 32 + j * 16 + fr) * kLd + kk + fk]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ag[i][j] = mfma(fa[i], fg, ag[i][j]);
+          au[i][j] = mfma(fa[i], fu, au[i][j]);
+        }
+      }
+    }
+    if (kt + 1 < nk) {
+      a.store(As[s ^ 1]);
+      store_b(Bs[s ^ 1]);
+    }
+    __syncthreads();
+  }
+  // Output fragment layout: element e of lane l is row (l >> 4) * 4 + e,
+  // column l & 15 of the 16 x 16 tile.  Columns in [d_ff, ldz) come out as
+  // SiLU(0) * 0 = 0, which keeps Z's padding zero for the second GEMM.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 32 + j * 16 + fr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+        if (m < M && n < ldz) Z[(int64_t)m * ldz + n] = bf16_rne(silu(ag[i][j][e]) * au[i][j][e]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------- down
+// Y[m, n] = sum_k Z[m, k] W_downT[k, n].  The W_downT tile (kBK rows of kBN
+// columns, row-major in HBM) is written to LDS as [n][k]: thread t loads rows
+// k0 + 2 (t & 31) and the next one at columns (t >> 5) * 8 + [0, 8) and writes
+// eight 4-byte (k, k + 1) pairs; the 32 k-pairs of a half-wave cover all 64
+// banks.  Wave w covers tokens (w >> 1) * 64 + [0, 64), columns (w & 1) * 32 +
+// [0, 32).
+__global__ __launch_bounds__(kGThreads) void k_prompt_down(const uint16_t* __restrict__ Z, int M, int ldz,
+                                                           const bf16s* __restrict__ WdT, int d_ff, int d,
+                                                           float* __restrict__ Y, int mt, int nt) {
+  __shared__ __align__(16) uint16_t As[2][kBM * kLd];
+  __shared__ __align__(16) uint16_t Bs[2][kBN * kLd];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int m_tile, n_tile;
+  tile_of(blockIdx.x, mt * nt, mt, m_tile, n_tile);
+  const int m0 = m_tile * kBM, n0 = n_tile * kBN;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int kp = tid & 31, cb = (tid >> 5) * 8;
+
+  ATile a;
+  u32x4 rb0, rb1;
+  auto load_b = [&](int k0) {
+    const int k = k0 + 2 * kp, n = n0 + cb;
+    const bool nin = n < d;
+    rb0 = (nin && k < d_ff) ? ld16(WdT + (int64_t)k * d + n) : u32x4{0u, 0u, 0u, 0u};
+    rb1 = (nin && k + 1 < d_ff) ? ld16(WdT + (int64_t)(k + 1) * d + n) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto store_b = [&](uint16_t* s) {
+    uint32_t* s32 = reinterpret_cast<uint32_t*>(s);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t lo = (rb0[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+      const uint32_t hi = (rb1[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+      s32[((cb + j) * kLd) / 2 + kp] = lo | (hi << 16);
+    }
+  };
+
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bf16s* Zb = reinterpret_cast<const bf16s*>(Z);
+  const int nk = (d_ff + kBK - 1) / kBK;  // Z's pitch ldz >= nk * kBK, its padding is zero
+  a.load(Zb, ldz, M, ldz, m0, 0);
+  load_b(0);
+  a.store(As[0]);
+  store_b(Bs[0]);
+  __syncthreads();
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int s = kt & 1;
+    if (kt + 1 < nk) {
+      a.load(Zb, ldz, M, ldz, m0, (kt + 1) * kBK);
+      load_b((kt + 1) * kBK);
+    }
+#pragma unroll
+    for (int kk = 0; kk < kBK; kk += 32) {
+      bf16x8 fa[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = lds_frag(&As[s][(wm * 64 + i * 16 + fr) * kLd + kk + fk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 fb = lds_frag(&Bs[s][(wn * 32 + j * 16 + fr) * kLd + kk + fk]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = mfma(fa[i], fb, acc[i][j]);
+      }
+    }
+    if (kt + 1 < nk) {
+      a.store(As[s ^ 1]);
+      store_b(Bs[s ^ 1]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 32 + j * 16 + fr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+        if (m < M && n < d) Y[(int64_t)m * d + n] = acc[i][j][e];
+      }
+    }
+}
+
+// ---------------------------------------------------------------- fp32
+// 16 x 16 output tiles, 16-wide reduction slices staged in LDS; thread (ty, tx)
+// owns output (m0 + ty, n0 + tx).
+constexpr int kFT = 16;
+
+__global__ __launch_bounds__(kFT* kFT) void k_prompt_gateup_f32(const float* __restrict__ X, int M, int d,
+                                                                 const float* __restrict__ Wg,
+                                                                 const float* __restrict__ Wu, int d_ff,
+                                                                 float* __restrict__ Z, int ldz) {
+  __shared__ float xs[kFT][kFT + 1], gs[kFT][kFT + 1], us[kFT][kFT + 1];
+  const int tx = threadIdx.x % kFT, ty = threadIdx.x / kFT;
+  const int m0 = blockIdx.y * kFT, n0 = blockIdx.x * kFT;
+  float g = 0.f, u = 0.f;
+  for (int k0 = 0; k0 < d; k0 += kFT) {
+    const int k = k0 + tx;
+    xs[ty][tx] = (m0 + ty < M && k < d) ? X[(int64_t)(m0 + ty) * d + k] : 0.f;
+    gs[ty][tx] = (n0 + ty < d_ff && k < d) ? Wg[(int64_t)(n0 + ty) * d + k] : 0.f;
+    us[ty][tx] = (n0 + ty < d_ff && k < d) ? Wu[(int64_t)(n0 + ty) * d + k] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kFT; ++j) {
+      g = fmaf(xs[ty][j], gs[tx][j], g);
+      u = fmaf(xs[ty][j], us[tx][j], u);
+    }
+    __syncthreads();
+  }
+  const int m = m0 + ty, n = n0 + tx;
+  if (m < M && n < d_ff) Z[(int64_t)m * ldz + n] = silu(g) * u;
+}
+
+__global__ __launch_bounds__(kFT* kFT) void k_prompt_down_f32(const float* __restrict__ Z, int M, int ldz,
+                                                              const float* __restrict__ WdT, int d_ff, int d,
+                                                              float* __restrict__ Y) {
+  __shared__ float zs[kFT][kFT + 1], ws[kFT][kFT + 1];
+  const int tx = threadIdx.x % kFT, ty = threadIdx.x / kFT;
+  const int m0 = blockIdx.y * kFT, n0 = blockIdx.x * kFT;
+  float acc = 0.f;
+  for (int k0 = 0; k0 < d_ff; k0 += kFT) {
+    zs[ty][tx] = (m0 + ty < M && k0 + tx < d_ff) ? Z[(int64_t)(m0 + ty) * ldz + k0 + tx] : 0.f;
+    ws[ty][tx] = (k0 + ty < d_ff && n0 + tx < d) ? WdT[(int64_t)(k0 + ty) * d + n0 + tx] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kFT; ++j) acc = fmaf(zs[ty][j], ws[j][tx], acc);
+    __syncthreads();
+  }
+  const int m = m0 + ty, n = n0 + tx;
+  if (m < M && n < d) Y[(int64_t)m * d + n] = acc;
+}
+
+// ---------------------------------------------------------------- host
+static int z_pitch(int32_t d_ff) { return (int)align_up((size_t)d_ff, kZPad); }
+
+static size_t prompt_ffn_ws_bytes(int64_t n_tokens, int32_t d_ff, int e) {
+  const int64_t rows = n_tokens < kChunkTokens ? n_tokens : kChunkTokens;
+  return align_up((size_t)align_up((size_t)rows, kBM) * (size_t)z_pitch(d_ff) * (size_t)e, 256);
+}
+
+static pop_status launched() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(POP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return POP_OK;
+}
+
+static void launch_prompt_ffn(hipStream_t st, const void* X, int64_t n_tokens, int32_t d, const void* Wg,
+                              const void* Wu, const void* WdT, int32_t d_ff, pop_dtype dt, float* Y, void* ws) {
+  const int ldz = z_pitch(d_ff);
+  for (int64_t t0 = 0; t0 < n_tokens; t0 += kChunkTokens) {
+    const int M = (int)(n_tokens - t0 < kChunkTokens ? n_tokens - t0 : kChunkTokens);
+    float* Yc = Y + t0 * d;
+    if (dt == POP_BF16) {
+      const bf16s* Xc = (const bf16s*)X + t0 * d;
+      const int mt = (M + kBM - 1) / kBM;
+      const int nt1 = ldz / kBN;
+      POP_LAUNCH(k_prompt_gateup, dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
+                 (const bf16s*)Wu, (int)d_ff, (uint16_t*)ws, ldz, mt, nt1);
+      const int nt2 = (d + kBN - 1) / kBN;
+      POP_LAUNCH(k_prompt_down, dim3(mt * nt2), dim3(kGThreads), 0, st, (const uint16_t*)ws, M, ldz,
+                 (const bf16s*)WdT, (int)d_ff, (int)d, Yc, mt, nt2);
+    } else {
+      const float* Xc = (const float*)X + t0 * d;
+      const int mt = (M + kFT - 1) / kFT;
+      POP_LAUNCH(k_prompt_gateup_f32, dim3((d_ff + kFT - 1) / kFT, mt), dim3(kFT * kFT), 0, st, Xc, M, (int)d,
+                 (const float*)Wg, (const float*)Wu, (int)d_ff, (float*)ws, ldz);
+      POP_LAUNCH(k_prompt_down_f32, dim3((d + kFT - 1) / kFT, mt), dim3(kFT * kFT), 0, st, (const float*)ws, M,
+                 ldz, (const float*)WdT, (int)d_ff, (int)d, Yc);
+    }
+  }
+}
+
+}  // namespace pop
+
+using namespace pop;
+
+extern "C" size_t pop_dense_ffn_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff, pop_dtype dt) {
+  if (n_tokens < 0 || d <= 0 || d_ff <= 0 || (dt != POP_BF16 && dt != POP_F32)) return 0;
+  return prompt_ffn_ws_bytes(n_tokens, d_ff, elem_bytes(dt));
+}
+
+extern "C" pop_status pop_dense_ffn_prefill(const void* X, int64_t n_tokens, int32_t d, const void* W_gate,
+                                            const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
+                                            float* Y, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  pop_status s = check_dtype_width(dt, d);
+  if (s != POP_OK) return s;
+  if (d > POP_MAX_D) return fail(POP_ERR_BAD_SHAPE, "d=%d above %d", d, POP_MAX_D);
+  if (d_ff < 1 || d_ff > POP_MAX_D_FF) return fail(POP_ERR_BAD_SHAPE, "d_ff=%d outside [1, %d]", d_ff, POP_MAX_D_FF);
+  if (n_tokens < 0 || n_tokens > ((int64_t)1 << 40) / d)
+    return fail(POP_ERR_BAD_SHAPE, "n_tokens=%lld out of range", (long long)n_tokens);
+  if (W_gate == nullptr || W_up == nullptr || W_downT == nullptr)
+    return fail(POP_ERR_INVALID_ARGUMENT, "W_gate, W_up and W_downT must be non-NULL");
+  if (n_tokens > 0 && (X == nullptr || Y == nullptr || ws == nullptr))
+    return fail(POP_ERR_INVALID_ARGUMENT, "X, Y and ws must be non-NULL when n_tokens > 0");
+  if (!aligned16(X) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_downT) || !aligned16(Y) ||
+      !aligned16(ws))
+    return fail(POP_ERR_MISALIGNED, "buffers must be 16-byte aligned");
+  const size_t need = prompt_ffn_ws_bytes(n_tokens, d_ff, elem_bytes(dt));
+  if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  trace_mark(st);
+  launch_prompt_ffn(st, X, n_tokens, d, W_gate, W_up, W_downT, d_ff, dt, Y, ws);
+  return launched();
+}

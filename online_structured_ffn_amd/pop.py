@@ -62,6 +62,9 @@ def _load():
                                              _c_vp, _c_i32, _c_vp, _c_i32, _c_dbl, _c_vp, _c_vp, _c_vp, _c_size,
                                              _c_vp, _c_vp, _c_vp, _c_vp]),
         "pop_trace_recorded": (_c_i32, []),
+        "pop_dense_ffn_prefill_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32, ctypes.c_int]),
+        "pop_dense_ffn_prefill": (ctypes.c_int, [_c_vp, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
+                                                 _c_vp, _c_vp, _c_size, _c_vp]),
         "pop_decode_down": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, ctypes.c_int, _c_vp, _c_i32,
                                            _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_size, _c_vp]),
     }
@@ -232,6 +235,27 @@ def pop_dense_ffn_decode(x, W_gate, W_up, W_downT, *, y=None, ws=None, stream=No
         _ptr(x), batch, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
         _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+def pop_dense_ffn_prefill_workspace_bytes(n_tokens: int, d: int, d_ff: int, dtype: str) -> int:
+    return int(lib.pop_dense_ffn_prefill_workspace_bytes(n_tokens, d, d_ff, POP_BF16 if dtype == "bf16" else POP_F32))
+
+
+def pop_dense_ffn_prefill(X, W_gate, W_up, W_downT, *, Y=None, ws=None, stream=None):
+    """Y [n_tokens, d] (fp32): the dense gated MLP over the prompt tokens."""
+    _dev(X, W_gate, W_up, W_downT)
+    n_tokens, d = X.shape
+    d_ff = W_gate.shape[0]
+    dev = W_gate.device
+    if Y is None:
+        Y = torch.empty((n_tokens, d), dtype=torch.float32, device=dev)
+    if ws is None:
+        dt = "bf16" if W_gate.dtype == torch.bfloat16 else "f32"
+        ws = workspace(max(pop_dense_ffn_prefill_workspace_bytes(n_tokens, d, d_ff, dt), 256), dev)
+    _check("pop_dense_ffn_prefill", lib.pop_dense_ffn_prefill(
+        _ptr(X), n_tokens, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
+        _ptr(Y), _ptr(ws), ws.numel(), _stream(stream)))
+    return Y
 
 
 # ---------------------------------------------------------------- stages

@@ -102,3 +102,29 @@ def test_dense_decode_validation():
     f = pop.lib.pop_dense_ffn_decode
     assert f(A, 1, 256, A, A, A, 688, 0, A, A, 10, None) == WS
     assert f(A, 1, 256, None, A, A, 688, 0, A, A, 1 << 30, None) == INVALID
+
+
+def _prompt(X=A, n=512, d=256, Wg=A, Wu=A, Wd=A, d_ff=688, dt=1, Y=A, ws=A, wsb=1 << 30):
+    return pop.lib.pop_dense_ffn_prefill(X, n, d, Wg, Wu, Wd, d_ff, dt, Y, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), DTYPE), (dict(d=12), SHAPE), (dict(d=0), SHAPE), (dict(d=32768), SHAPE), (dict(d_ff=0), SHAPE),
+    (dict(d_ff=40000), SHAPE), (dict(n=-3), SHAPE), (dict(Wg=None), INVALID), (dict(Wd=None), INVALID),
+    (dict(X=None), INVALID), (dict(Y=None), INVALID), (dict(ws=None), INVALID), (dict(Wu=A + 2), MISALIGNED),
+    (dict(Y=A + 4), MISALIGNED), (dict(wsb=1000), WS),
+])
+def test_prompt_ffn_validation(kw, status):
+    assert _prompt(**kw) == status
+    assert pop.lib.pop_last_error().decode()
+
+
+def test_prompt_ffn_workspace_sizes():
+    f = pop.pop_dense_ffn_prefill_workspace_bytes
+    # Z for one pass of up to 4096 tokens, rows padded to 128, pitch d_ff rounded up to 64
+    assert f(512, 4096, 11008, "bf16") >= 512 * 11008 * 2
+    assert f(512, 4096, 11008, "f32") >= 512 * 11008 * 4
+    assert f(32768, 4096, 11008, "bf16") == f(4096, 4096, 11008, "bf16")
+    assert f(1, 256, 688, "bf16") >= 128 * 704 * 2
+    assert f(0, 256, 688, "bf16") == 0
+    assert pop.lib.pop_dense_ffn_prefill_workspace_bytes(-1, 256, 688, 1) == 0
