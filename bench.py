@@ -235,6 +235,46 @@ def main():
             x_buf.copy_(Xdec[t])
             graphs["decode_1s"].replay()
 
+    # ------------------------------------------------------------ ablation variants (POP notes, ablation table)
+    # (1) static prefill mask: the n_live channels of highest prefill importance, no candidates;
+    # (2) full re-evaluation: every channel a candidate at every step.
+    I_l = [torch.empty(d_ff, dtype=torch.float32, device=dev) for _ in range(L)]
+    Rs = []
+    for l in range(L):
+        pop.pop_prefill_partition(X[l], Wu[l], w.r, w.gamma, out=(R[l], C[l], P[l], I_l[l]), ws=ws_pre)
+        Rs.append(pop.pop_partition_select(I_l[l], w.r, 0.0)[0])
+    R_none = torch.empty(0, dtype=torch.int32, device=dev)
+    C_all = torch.arange(d_ff, dtype=torch.int32, device=dev)
+
+    def static_layers():
+        for l in range(L):
+            pop.pop_decode_ffn(x_buf[l], Wg[l], Wu[l], WdT[l], Rs[l], R_none, w.r, y=y[l], ws=ws_dec)
+
+    def full_layers():
+        for l in range(L):
+            pop.pop_decode_ffn(x_buf[l], Wg[l], Wu[l], WdT[l], R_none, C_all, w.r, y=y[l], ws=ws_dec)
+
+    with torch.cuda.stream(side):
+        static_layers()
+        full_layers()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for name, fn in (("static", static_layers), ("full", full_layers)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs[name] = g
+
+    def steps_of(name):
+        def run():
+            for t in range(T):
+                x_buf.copy_(Xdec[t])
+                graphs[name].replay()
+        return run
+
+    ms_static = timed(steps_of("static"), 1)
+    ms_full = timed(steps_of("full"), 1)
+
     ms_dec = timed(decode_only, 1)
     ms_dec_1s = timed(decode_only_1s, 1)
     ms_dense = timed(dense_only, 1)
@@ -245,6 +285,7 @@ def main():
     log(f"[bench] decode {t_ls * 1e3:.1f} us/layer-step ({bytes_ls / (t_ls * 1e-3) / 1e9:.0f} GB/s; "
         f"pop_decode_ffn graph {ms_dec_1s / (T * L) * 1e3:.1f} us), "
         f"dense {t_ls_dense * 1e3:.1f} us ({bytes_dense / (t_ls_dense * 1e-3) / 1e9:.0f} GB/s), "
+        f"static mask {ms_static / (T * L) * 1e3:.1f} us, full re-evaluation {ms_full / (T * L) * 1e3:.1f} us, "
         f"prefill partition {ms_prefill / L * 1e3:.1f} us/layer, "
         f"prompt FFN {ms_pffn / L * 1e3:.1f} us/layer ({pffn_tflops:.0f} TFLOP/s)")
 
@@ -404,6 +445,15 @@ def main():
         "decode_pop_decode_ffn_us_per_layer_step": round(ms_dec_1s / (T * L) * 1e3, 3),
         "speedup_vs_dense": round(t_ls_dense / t_ls, 4),
         "ideal_speedup_bytes": round(bytes_dense / bytes_ls, 4),
+        "ablation": {
+            "static_prefill_mask": {"us_per_layer_step": round(ms_static / (T * L) * 1e3, 3),
+                                    "algorithmic_bytes": metrics.decode_bytes(d, n_live, 0, 0, B, e)},
+            "full_reevaluation": {"us_per_layer_step": round(ms_full / (T * L) * 1e3, 3),
+                                  "algorithmic_bytes": metrics.decode_bytes(d, 0, d_ff, n_live, B, e)},
+            "pop": {"us_per_layer_step": round(t_ls * 1e3, 3), "algorithmic_bytes": bytes_ls},
+            "pop_time_over_static": round(t_ls * T * L / ms_static - 1.0, 4),
+            "full_time_over_static": round(ms_full / ms_static - 1.0, 4),
+        },
         "prefill_partition_us_per_layer": round(ms_prefill / L * 1e3, 2),
         "prompt_ffn": {
             "us_per_layer": round(ms_pffn / L * 1e3, 2),

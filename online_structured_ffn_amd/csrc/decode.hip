@@ -622,8 +622,10 @@ static void launch_gateup(hipStream_t st, const void* x, int B, int d, const voi
   const int n_A = n_R + n_C;
   int grid = (n_A + 3) / 4;
   if (grid < 1) grid = 1;
+  // R == NULL means identity rows (the dense baseline) only when there are no
+  // candidate rows; with n_R == 0 R is never read.
 #define POP_GATEUP(BT)                                                                                        \
-  if (R == nullptr)                                                                                           \
+  if (R == nullptr && n_C == 0)                                                                               \
     POP_LAUNCH((k_gateup<T, BT, true>), dim3(grid), dim3(256), 0, st, (const T*)x, B, d, (const T*)Wg, \
                        (const T*)Wu, d_ff, R, n_R, C, n_C, z, score);                                         \
   else                                                                                                        \
@@ -651,8 +653,9 @@ static void launch_down(hipStream_t st, const float* z, int B, int n_A, const vo
   if (B == 0) return;
   const int n_live = n_R + k;
   const DownPlan p = plan_down(n_live, B, d, Vec<T>::N);
+  // Identity rows only for the dense baseline (no selected rows).
 #define POP_DOWN(BT)                                                                                          \
-  if (R == nullptr)                                                                                           \
+  if (R == nullptr && k == 0)                                                                                 \
     POP_LAUNCH((k_down_partial<T, BT, true>), dim3(p.col_blocks, p.n_chunks), dim3(256), 0, st, z, n_A, \
                        B, (const T*)WdT, d, d_ff, R, n_R, sel, Q, n_R, n_live, p.rows_per_chunk, partial);  \
   else                                                                                                        \
