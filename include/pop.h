@@ -81,6 +81,9 @@ typedef struct {
 #define POP_MAX_D 16384
 /* Largest decode batch that shares one mask. */
 #define POP_MAX_BATCH 256
+/* Largest prompt routed by one MoE call, and the expert count range. */
+#define POP_MAX_MOE_TOKENS (1 << 22)
+#define POP_MAX_EXPERTS 64
 
 /* Human-readable name of a status code (static storage). */
 const char* pop_status_string(pop_status s);
@@ -297,6 +300,73 @@ size_t pop_dense_ffn_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_
 pop_status pop_dense_ffn_prefill(const void* X, int64_t n_tokens, int32_t d, const void* W_gate,
                                  const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
                                  float* Y, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Mixture of experts.
+ *
+ * The POP notes ("Key experimental data") apply the method to MoE models; the
+ * pages give no routing detail.  Readings taken: a token goes to the experts
+ * of its two largest router logits (on equal logits the lower expert id
+ * first), weighted by the softmax of those two logits; every expert keeps its
+ * own R/C/P partition, built from the prompt tokens routed to it; in a decode
+ * step every expert runs the POP step on the tokens routed to it (candidate
+ * score = max over those tokens), and a token's output is the weighted sum of
+ * its two experts' outputs, lower expert id first.  An expert no token reaches
+ * does nothing.
+ *
+ * Expert tensors are stacked: W_gate, W_up, W_downT are [E, d_ff, d] (expert
+ * e's [d_ff, d] matrix at offset e * d_ff * d); R, C, P are [E, n_R], [E, n_C],
+ * [E, n_P] with the sizes of pop_partition_counts (equal for every expert);
+ * router logits are fp32 [n_tokens, E].  2 <= E <= POP_MAX_EXPERTS.
+ * ------------------------------------------------------------------------- */
+
+/*
+ * pop_moe_route_top2 — the routing alone.  experts [n_tokens, 2] (best expert
+ * first), weights [n_tokens, 2] (fp32), offsets [E + 1], tokens [2 n_tokens],
+ * slots [n_tokens, 2]: the pairs of expert e are tokens[offsets[e] ..
+ * offsets[e + 1]) in ascending token order, and pair (t, experts[t, j]) sits at
+ * tokens[slots[t, j]].  0 <= n_tokens <= POP_MAX_MOE_TOKENS.
+ */
+pop_status pop_moe_route_top2(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t* experts,
+                              float* weights, int32_t* offsets, int32_t* tokens, int32_t* slots, void* stream);
+
+size_t pop_moe_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff, int32_t n_experts);
+
+/*
+ * pop_moe_prefill_partition — "Key design 1" per expert: for every expert,
+ * s over the prompt tokens routed to it, I = ||W_up[e][i, :] * s||_2, and its
+ * R/C/P.  X [n_tokens, d] and W_up [E, d_ff, d] in dtype dt; logits fp32
+ * [n_tokens, E]; importance [E, d_ff] (optional).  bf16 supports E <= 32
+ * (the per-expert accumulators live in LDS).  Errors as
+ * pop_prefill_partition, and BAD_SHAPE for E or n_tokens out of range.
+ */
+pop_status pop_moe_prefill_partition(const void* X, int64_t n_tokens, int32_t d, const float* logits,
+                                     int32_t n_experts, const void* W_up, int32_t d_ff, pop_dtype dt, double r,
+                                     double gamma, int32_t* R, int32_t* C, int32_t* P, float* importance,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+size_t pop_moe_decode_workspace_bytes(int32_t n_tokens, int32_t d, int32_t d_ff, int32_t n_experts);
+
+/*
+ * pop_moe_decode_ffn — one MoE decode step over n_tokens tokens
+ * (0 <= n_tokens <= POP_MAX_BATCH): routing, then per expert the POP step of
+ * pop_decode_ffn on its routed tokens, then y = the weighted sum (fp32
+ * [n_tokens, d], every row written).  selected (optional) is [E, k]: expert
+ * e's selected candidates, ascending, written only for experts that received
+ * a token.  k = clamp(round((1 - r) d_ff) - n_R, 0, n_C) as for one layer.
+ * Deterministic: the same inputs give the same bits.  Errors as
+ * pop_decode_ffn, and BAD_SHAPE for E out of range.
+ * After the call the workspace holds, each region starting on a 256-byte
+ * boundary in this order (P = 2 n_tokens routed pairs): experts [P] int32,
+ * weights [P] fp32, offsets [E + 1] int32, tokens [P] int32, slots [P] int32,
+ * z fp32 with rows of n_R + n_C values (row p: pair p's z over its expert's R
+ * then C; the region is sized for P rows of d_ff), scores fp32 [E][n_C]
+ * (region sized for E * d_ff).
+ */
+pop_status pop_moe_decode_ffn(const void* x, int32_t n_tokens, int32_t d, const float* logits, int32_t n_experts,
+                              const void* W_gate, const void* W_up, const void* W_downT, int32_t d_ff,
+                              pop_dtype dt, const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C,
+                              double r, float* y, int32_t* selected, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Kernel tracing (measurement hook).

@@ -115,35 +115,8 @@ __global__ __launch_bounds__(256) void k_gateup(const T* __restrict__ x, int B, 
 }
 
 // ---------------------------------------------------------------- K5
-// S = the k most important candidates (score descending, position ascending on
-// ties), written in ascending order as positions into C and as channels.
+// The candidate top-k as its own one-workgroup launch (topk_block).
 constexpr int kTopkThreads = 256;
-
-template <int NTH, int MAXN>
-__device__ void topk_block(const float* __restrict__ score, int n, int k, const int32_t* __restrict__ C,
-                           int32_t* __restrict__ positions, int32_t* __restrict__ selected, SelShared<NTH, MAXN>& sh) {
-  sel_load(score, n, sh);
-  const int ranks[1] = {n - k};
-  select_thresholds(n, ranks, sh);
-  const SelTarget t = sh.tgt[0];
-  const int E = (n + NTH - 1) / NTH;
-  const int base = threadIdx.x * E;
-  const int end = min(n, base + E);
-  int pos[3] = {0, 0, 0};
-  for (int i = base; i < end; ++i)
-    if (!sel_less(t, sel_key(sh.vals[i], i))) ++pos[0];
-  int tot[3];
-  block_exclusive_scan3(pos, tot, sh);
-  for (int i = base; i < end; ++i) {
-    if (!sel_less(t, sel_key(sh.vals[i], i))) {
-      if (pos[0] < k) {  // an exact select never reaches the cap
-        positions[pos[0]] = i;
-        if (selected != nullptr) selected[pos[0]] = C[i];
-      }
-      ++pos[0];
-    }
-  }
-}
 
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ score, int n, int k,
                                                        const int32_t* __restrict__ C, int32_t* __restrict__ positions,

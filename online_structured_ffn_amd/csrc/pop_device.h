@@ -474,6 +474,36 @@ __device__ __forceinline__ void block_exclusive_scan3(int (&v)[3], int (&total)[
   __syncthreads();
 }
 
+// S = the k most important of n candidates (score descending, position
+// ascending on ties), written in ascending order as positions into C and, when
+// `selected` is not NULL, as channels C[position].  One workgroup.
+template <int NTH, int MAXN>
+__device__ void topk_block(const float* __restrict__ score, int n, int k, const int32_t* __restrict__ C,
+                           int32_t* __restrict__ positions, int32_t* __restrict__ selected, SelShared<NTH, MAXN>& sh) {
+  sel_load(score, n, sh);
+  const int ranks[1] = {n - k};
+  select_thresholds(n, ranks, sh);
+  const SelTarget t = sh.tgt[0];
+  const int E = (n + NTH - 1) / NTH;
+  const int base = threadIdx.x * E;
+  const int end = min(n, base + E);
+  int pos[3] = {0, 0, 0};
+  for (int i = base; i < end; ++i)
+    if (!sel_less(t, sel_key(sh.vals[i], i))) ++pos[0];
+  int tot[3];
+  block_exclusive_scan3(pos, tot, sh);
+  for (int i = base; i < end; ++i) {
+    if (!sel_less(t, sel_key(sh.vals[i], i))) {
+      if (pos[0] < k) {  // an exact select never reaches the cap
+        positions[pos[0]] = i;
+        if (selected != nullptr) selected[pos[0]] = C[i];
+      }
+      ++pos[0];
+    }
+  }
+}
+
+
 // ---------------------------------------------------------------- fixed-order chunk sum
 // out[i] = sum_{c < n_chunks} partial[c * n_out + i].  A block of 1024 threads
 // covers 32 outputs; the chunks are dealt to 32 groups as contiguous ranges,

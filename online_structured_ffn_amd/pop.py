@@ -63,6 +63,15 @@ def _load():
                                              _c_vp, _c_vp, _c_vp, _c_vp]),
         "pop_trace_recorded": (_c_i32, []),
         "pop_dense_ffn_prefill_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32, ctypes.c_int]),
+        "pop_moe_route_top2": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+        "pop_moe_prefill_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32, _c_i32]),
+        "pop_moe_prefill_partition": (ctypes.c_int, [_c_vp, _c_i64, _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, ctypes.c_int,
+                                                     _c_dbl, _c_dbl, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_size,
+                                                     _c_vp]),
+        "pop_moe_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32]),
+        "pop_moe_decode_ffn": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32,
+                                              ctypes.c_int, _c_vp, _c_i32, _c_vp, _c_i32, _c_dbl, _c_vp, _c_vp, _c_vp,
+                                              _c_size, _c_vp]),
         "pop_dense_ffn_prefill": (ctypes.c_int, [_c_vp, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
                                                  _c_vp, _c_vp, _c_size, _c_vp]),
         "pop_decode_down": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, ctypes.c_int, _c_vp, _c_i32,
@@ -256,6 +265,70 @@ def pop_dense_ffn_prefill(X, W_gate, W_up, W_downT, *, Y=None, ws=None, stream=N
         _ptr(X), n_tokens, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
         _ptr(Y), _ptr(ws), ws.numel(), _stream(stream)))
     return Y
+
+
+# ---------------------------------------------------------------- mixture of experts
+def pop_moe_route_top2(logits, *, stream=None):
+    """(experts [T, 2], weights [T, 2], offsets [E + 1], tokens [2T], slots [T, 2])."""
+    _dev(logits)
+    T, E = logits.shape
+    dev = logits.device
+    ex = torch.empty((T, 2), dtype=torch.int32, device=dev)
+    wt = torch.empty((T, 2), dtype=torch.float32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    tok = torch.empty(2 * T, dtype=torch.int32, device=dev)
+    slot = torch.empty((T, 2), dtype=torch.int32, device=dev)
+    _check("pop_moe_route_top2", lib.pop_moe_route_top2(
+        _ptr(logits), T, E, _ptr(ex), _ptr(wt), _ptr(off), _ptr(tok), _ptr(slot), _stream(stream)))
+    return ex, wt, off, tok, slot
+
+
+def pop_moe_prefill_partition(X, logits, W_up, r: float, gamma: float, *, importance: bool = False, out=None,
+                              ws=None, stream=None):
+    """(R [E, n_R], C [E, n_C], P [E, n_P][, I [E, d_ff]]) for stacked W_up [E, d_ff, d]."""
+    _dev(X, logits, W_up)
+    n_tokens, d = X.shape
+    E, d_ff, _ = W_up.shape
+    c = pop_partition_counts(d_ff, r, gamma)
+    dev = W_up.device
+    if out is None:
+        R, C, P = (torch.empty((E, c[n]), dtype=torch.int32, device=dev) for n in ("n_R", "n_C", "n_P"))
+        I = torch.empty((E, d_ff), dtype=torch.float32, device=dev) if importance else None
+    else:
+        R, C, P, I = out
+    if ws is None:
+        ws = workspace(lib.pop_moe_prefill_workspace_bytes(n_tokens, d, d_ff, E), dev)
+    _check("pop_moe_prefill_partition", lib.pop_moe_prefill_partition(
+        _ptr(X), n_tokens, d, _ptr(logits), E, _ptr(W_up), d_ff, _dtype(W_up), float(r), float(gamma),
+        _ptr(R), _ptr(C), _ptr(P), _ptr(I), _ptr(ws), ws.numel(), _stream(stream)))
+    return (R, C, P, I) if importance else (R, C, P)
+
+
+def pop_moe_decode_workspace_bytes(n_tokens: int, d: int, d_ff: int, n_experts: int) -> int:
+    return int(lib.pop_moe_decode_workspace_bytes(n_tokens, d, d_ff, n_experts))
+
+
+def pop_moe_decode_ffn(x, logits, W_gate, W_up, W_downT, R, C, r: float, *, y=None, selected: bool = False,
+                       ws=None, stream=None):
+    """y [T, d] (fp32) for one MoE decode step; optionally the selected
+    candidates [E, k] (rows of experts that received no token are left as they
+    were: zero-initialised here)."""
+    _dev(x, logits, W_gate, W_up, W_downT, R, C)
+    T, d = x.shape
+    E, d_ff, _ = W_gate.shape
+    dev = W_gate.device
+    if y is None:
+        y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    S = None
+    if selected:
+        S = torch.zeros((E, _k(d_ff, r, R.shape[1], C.shape[1])), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(pop_moe_decode_workspace_bytes(T, d, d_ff, E), dev)
+    _check("pop_moe_decode_ffn", lib.pop_moe_decode_ffn(
+        _ptr(x), T, d, _ptr(logits), E, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
+        _ptr(R), R.shape[1], _ptr(C), C.shape[1], float(r), _ptr(y), _ptr(S), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return (y, S) if selected else y
 
 
 # ---------------------------------------------------------------- stages

@@ -118,3 +118,16 @@ def check_decode(y, S, ws, x, w, R, C, r, dtype, z_ref=None):
     err = np.abs(y_dev - y_ref).max() / m
     assert err <= TOL[dtype], f"max|dy|/max|y| = {err:.3e} > {TOL[dtype]}"
     return err, len(diff)
+
+
+def moe_decode_views(ws, n_tokens, d_ff, n_experts, n_A, n_C):
+    """(z [2T, n_A], scores [E, n_C]) of a pop_moe_decode_ffn workspace, after
+    the layout the header documents."""
+    a = lambda b: (b + 255) // 256 * 256
+    P = 2 * max(n_tokens, 1)
+    o = a(P * 4) + a(P * 4) + a((n_experts + 1) * 4) + a(P * 4) + a(P * 4)
+    raw = host(ws)
+    z = raw[o: o + P * n_A * 4].view(np.float32).reshape(P, n_A)
+    o += a(P * d_ff * 4)
+    sc = raw[o: o + n_experts * n_C * 4].view(np.float32).reshape(n_experts, n_C)
+    return z, sc

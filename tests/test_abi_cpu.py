@@ -128,3 +128,45 @@ def test_prompt_ffn_workspace_sizes():
     assert f(1, 256, 688, "bf16") >= 128 * 704 * 2
     assert f(0, 256, 688, "bf16") == 0
     assert pop.lib.pop_dense_ffn_prefill_workspace_bytes(-1, 256, 688, 1) == 0
+
+
+def test_moe_validation():
+    lib = pop.lib
+    # routing: expert count range, NULL outputs
+    assert lib.pop_moe_route_top2(A, 4, 1, A, A, A, A, A, None) == SHAPE
+    assert lib.pop_moe_route_top2(A, 4, 65, A, A, A, A, A, None) == SHAPE
+    assert lib.pop_moe_route_top2(A, -1, 8, A, A, A, A, A, None) == SHAPE
+    assert lib.pop_moe_route_top2(A, 4, 8, None, A, A, A, A, None) == INVALID
+    assert lib.pop_moe_route_top2(A, 4, 8, A, A, None, A, A, None) == INVALID
+    # prefill
+    f = lib.pop_moe_prefill_partition
+    ok = dict(X=A, n=64, d=256, L=A, E=8, W=A, d_ff=688, dt=1, r=0.3, g=0.1, R=A, C=A, P=A, I=None, ws=A,
+              wsb=1 << 30)
+
+    def pre(**kw):
+        a = dict(ok, **kw)
+        return f(a["X"], a["n"], a["d"], a["L"], a["E"], a["W"], a["d_ff"], a["dt"], a["r"], a["g"], a["R"],
+                 a["C"], a["P"], a["I"], a["ws"], a["wsb"], None)
+    assert pre(E=1) == SHAPE and pre(E=33) == SHAPE and pre(E=65, dt=0) == SHAPE
+    assert pre(L=None) == INVALID and pre(R=None) == INVALID and pre(r=1.2) == INVALID
+    assert pre(L=A + 4) == MISALIGNED and pre(wsb=64) == WS and pre(dt=4) == DTYPE
+    # decode
+    g = lib.pop_moe_decode_ffn
+    okd = dict(x=A, T=32, d=256, L=A, E=8, Wg=A, Wu=A, Wd=A, d_ff=688, dt=1, R=A, nR=413, C=A, nC=137, r=0.3,
+               y=A, S=None, ws=A, wsb=1 << 30)
+
+    def dec(**kw):
+        a = dict(okd, **kw)
+        return g(a["x"], a["T"], a["d"], a["L"], a["E"], a["Wg"], a["Wu"], a["Wd"], a["d_ff"], a["dt"], a["R"],
+                 a["nR"], a["C"], a["nC"], a["r"], a["y"], a["S"], a["ws"], a["wsb"], None)
+    assert dec(E=1) == SHAPE and dec(T=300) == SHAPE and dec(d=12) == SHAPE
+    assert dec(nR=600) == INVALID and dec(L=None) == INVALID and dec(C=None) == INVALID and dec(r=1.0) == INVALID
+    assert dec(y=A + 8) == MISALIGNED and dec(wsb=1000) == WS
+
+
+def test_moe_workspace_sizes():
+    assert pop.lib.pop_moe_prefill_workspace_bytes(8192, 4096, 14336, 8) >= 8 * (4096 + 14336) * 4
+    assert pop.lib.pop_moe_prefill_workspace_bytes(8192, 4096, 14336, 1) == 0
+    b = pop.pop_moe_decode_workspace_bytes(32, 4096, 14336, 8)
+    assert b >= 64 * 14336 * 4 + 8 * 14336 * 4   # z of every routed pair, scores of every expert
+    assert pop.pop_moe_decode_workspace_bytes(32, 4096, 14336, 100) == 0
