@@ -303,10 +303,12 @@ def main():
     labels_ffn = (["k_prompt_gateup", "k_prompt_down"] if e == 2 else
                   ["k_prompt_gateup_f32", "k_prompt_down_f32"]) * n_pass
     if fused:
-        labels_dec = ((["k_candidate_rows"] if n_C > 0 else []) + (["k_topk"] if n_C > 4096 else [])
-                      + ["k_retained_rows(+top-k)"] + (["k_down_selected"] if k > 0 else [])
+        plan = metrics.fused_plan(n_R, n_C, k, d, e)
+        labels_dec = ([f"k_pop_step.{ph}" for ph in (1, 2, 3) if plan["launch"][ph]]
                       + ["k_sum_chunks(y)"])
-        labels_dense = ["k_retained_rows(dense)", "k_sum_chunks(y)"]
+        if n_C > 4096 and k > 0:
+            labels_dec.insert(1, "k_topk")
+        labels_dense = ["k_pop_step.0(dense)", "k_sum_chunks(y)"]
     else:
         labels_dec = ["k_gateup"] + (["k_topk"] if n_C > 0 else []) + ["k_down_partial", "k_sum_chunks(y)"]
         labels_dense = ["k_gateup(dense)", "k_down_partial(dense)", "k_sum_chunks(y)"]
@@ -360,7 +362,8 @@ def main():
         span = tracer.elapsed_ms(marks[0][1], marks[-1][2] - 1)
         busy = 0.0
         for labels, i0, i1 in marks:
-            assert i1 - i0 == len(labels) + 1, (labels, i0, i1)
+            if i1 - i0 != len(labels) + 1:  # a launch shape other than the one assumed: number them
+                labels = [f"{labels[0]}#{j}" for j in range(i1 - i0 - 1)]
             for j, name in enumerate(labels):
                 dt = tracer.elapsed_ms(i0 + j, i0 + j + 1)
                 per.setdefault(name, []).append(dt)
@@ -378,10 +381,15 @@ def main():
     kus, coverage = traced(pop.Tracer.DISABLE_SYSTEM_FENCE)
 
     if fused:
-        dom = "k_retained_rows(+top-k)"
-        dom_desc = ("k_retained_rows (batch-1 decode: gate, up and W_downT rows of every retained channel in one "
-                    "stream, with the one-workgroup candidate top-k beside it)")
-        dom_bytes = metrics.retained_stream_bytes(d, n_R, n_C, k, e)
+        ph = max((p for p in (1, 2, 3) if plan["launch"][p]), key=lambda p: plan["bytes"][p])
+        dom = f"k_pop_step.{ph}"
+        dom_desc = {1: "k_pop_step phase 1 (batch-1 decode: candidate gate/up rows with fused SiLU*up and score, "
+                       "beside a share of the retained rows' gate, up and W_downT stream)",
+                    2: "k_pop_step phase 2 (batch-1 decode: gate, up and W_downT rows of the retained channels in "
+                       "one stream, with the one-workgroup candidate top-k beside it)",
+                    3: "k_pop_step phase 3 (batch-1 decode: selected candidates' W_downT rows beside a share of the "
+                       "retained stream)"}[ph]
+        dom_bytes = plan["bytes"][ph]
     else:
         dom = "k_gateup"
         dom_desc = "k_gateup (decode gate/up over R u C, fused SiLU*up and candidate score)"
@@ -390,7 +398,7 @@ def main():
     tname = "pop::bf16s" if e == 2 else "float"
     if fused:
         nv = -(-d // (256 * vec))
-        dom_symbol = f"pop::k_retained_rows<{tname}, {1 if nv <= 1 else 2 if nv <= 2 else 4}, false>"
+        dom_symbol = f"pop::k_pop_step<{tname}, {1 if nv <= 1 else 2 if nv <= 2 else 4}, false, {ph}>"
     else:
         dom_symbol = None
     tb = profiling.traffic_bytes(dom_symbol) if dom_symbol and w.name == "llama2_7b_ffn_b1" else None

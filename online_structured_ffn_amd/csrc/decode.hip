@@ -9,6 +9,8 @@
 //   K6r fixed-order reduction of the partial sums into y
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "pop_device.h"
 #include "pop_internal.h"
 
@@ -132,11 +134,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 // thread.  Rows go in batches of two, double-buffered: the next batch's loads
 // are in flight while the current batch's dot products are reduced (DPP
 // within each wave, LDS across the four waves, fixed order).
-// A decode step runs this as two launches: k_candidate_rows (gate/up rows of
-// C: z and scores), then k_retained_rows, whose first block runs the top-k over
-// those scores while the others stream the retained rows (gate, up and W_downT
-// rows: z and a partial y per block), so the one-CU top-k hides under the
-// retained stream.  No block waits on another inside a launch.
+// A decode step is three launches of k_pop_step and a sum.  Each launch gives
+// its first blocks to a step of the candidate chain and the rest to a share of
+// the retained rows (gate, up and W_downT rows: z and a partial y per block),
+// so every link of the chain runs beside retained work instead of alone:
+//   phase 1: candidate rows (z and scores)            + retained share A
+//   phase 2: the top-k over those scores (one block)  + retained share B
+//   phase 3: the selected rows' W_downT (chunks x column slices) + share C
+// then k_sum_chunks adds every partial y in a fixed order.  No block waits on
+// another inside a launch: each link reads what an earlier launch wrote.
 // Launch-shape tunables (overridable with -D for sweeps).
 #ifndef POP_FUSED_RBLOCKS
 #define POP_FUSED_RBLOCKS 512  // most blocks for the retained rows
@@ -145,7 +151,13 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 #define POP_FUSED_CROWS 4  // candidate rows per block
 #endif
 #ifndef POP_SEL_ROWS
-#define POP_SEL_ROWS 8  // selected rows per block of k_down_selected
+#define POP_SEL_ROWS 8  // selected rows per chunk
+#endif
+#ifndef POP_SPLIT_B
+#define POP_SPLIT_B 100  // percent of the retained blocks beside the top-k
+#endif
+#ifndef POP_SPLIT_C
+#define POP_SPLIT_C 0  // percent of the retained blocks beside the selected rows
 #endif
 constexpr int kFusedThreads = 256;
 constexpr int kFusedTopkMaxN = 4096;
@@ -164,25 +176,28 @@ __device__ __forceinline__ void fused_issue(FusedRowBuf<T, NV>& b, const int* ro
                                             const T* __restrict__ Wg, const T* __restrict__ Wu,
                                             const T* __restrict__ WdT, int d) {
   constexpr int V = Vec<T>::N;
+  // Lanes past the row's end load its last vector (same cache line, results
+  // unused): the loads carry no per-lane condition, which keeps the compiler's
+  // wait counting exact across the double buffer.
 #pragma unroll
   for (int p = 0; p < kFusedP; ++p) {
     if (i0 + p < nrows) {
       const int64_t base = (int64_t)rows[i0 + p] * d;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int col = j * kFusedThreads * V + (int)threadIdx.x * V;
-        if (col < d) {
-          b.g[p][j] = ld16_stream(Wg + base + col);
-          b.u[p][j] = ld16_stream(Wu + base + col);
-          if (kDown) b.w[p][j] = ld16_stream(WdT + base + col);
-        }
+        const int col = min(j * kFusedThreads * V + (int)threadIdx.x * V, d - V);
+        b.g[p][j] = ld16_stream(Wg + base + col);
+        b.u[p][j] = ld16_stream(Wu + base + col);
+        if (kDown) b.w[p][j] = ld16_stream(WdT + base + col);
       }
     }
   }
 }
 
 // Reduces the batch's dot products across the block and applies them.
-// Returns through zs the batch's z values (valid for i0 + p < nrows).
+// Returns through zs the batch's z values (0 for rows past nrows).  No lane or
+// row condition guards the arithmetic: columns past d hold x = 0, rows past
+// nrows get z = 0, and the buffers start zeroed, so every operand is finite.
 template <typename T, int NV, bool kDown, int PB>
 __device__ __forceinline__ void fused_consume(const FusedRowBuf<T, NV>& b, const u32x4 (&xv)[NV], int i0, int nrows,
                                               int d, float (&part)[2][4][2 * kFusedP], float (&acc)[NV][Vec<T>::N],
@@ -195,21 +210,16 @@ __device__ __forceinline__ void fused_consume(const FusedRowBuf<T, NV>& b, const
   for (int p = 0; p < kFusedP; ++p) {
     pg[p] = 0.f;
     pu[p] = 0.f;
-    if (i0 + p < nrows) {
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int col = j * kFusedThreads * V + (int)threadIdx.x * V;
-        if (col < d) {
-          float g[V], u[V], xx[V];
-          unpack(b.g[p][j], g, T{});
-          unpack(b.u[p][j], u, T{});
-          unpack(xv[j], xx, T{});
+    for (int j = 0; j < NV; ++j) {
+      float g[V], u[V], xx[V];
+      unpack(b.g[p][j], g, T{});
+      unpack(b.u[p][j], u, T{});
+      unpack(xv[j], xx, T{});
 #pragma unroll
-          for (int v = 0; v < V; ++v) {
-            pg[p] = fmaf(g[v], xx[v], pg[p]);
-            pu[p] = fmaf(u[v], xx[v], pu[p]);
-          }
-        }
+      for (int v = 0; v < V; ++v) {
+        pg[p] = fmaf(g[v], xx[v], pg[p]);
+        pu[p] = fmaf(u[v], xx[v], pu[p]);
       }
     }
   }
@@ -234,22 +244,17 @@ __device__ __forceinline__ void fused_consume(const FusedRowBuf<T, NV>& b, const
       g += part[PB][w][2 * p];
       u += part[PB][w][2 * p + 1];
     }
-    zs[p] = silu(g) * u;
+    zs[p] = i0 + p < nrows ? silu(g) * u : 0.f;
   }
   if (kDown) {
 #pragma unroll
     for (int p = 0; p < kFusedP; ++p) {
-      if (i0 + p < nrows) {
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const int col = j * kFusedThreads * V + (int)threadIdx.x * V;
-          if (col < d) {
-            float f[V];
-            unpack(b.w[p][j], f, T{});
+      for (int j = 0; j < NV; ++j) {
+        float f[V];
+        unpack(b.w[p][j], f, T{});
 #pragma unroll
-            for (int v = 0; v < V; ++v) acc[j][v] = fmaf(zs[p], f[v], acc[j][v]);
-          }
-        }
+        for (int v = 0; v < V; ++v) acc[j][v] = fmaf(zs[p], f[v], acc[j][v]);
       }
     }
   }
@@ -261,6 +266,13 @@ __device__ __forceinline__ void fused_rows(const int* rows, int nrows, const T* 
                                            float (&part)[2][4][2 * kFusedP], float (&acc)[NV][Vec<T>::N],
                                            float* __restrict__ zout, int zbase, float* __restrict__ score) {
   FusedRowBuf<T, NV> A, Bf;
+#pragma unroll
+  for (int p = 0; p < kFusedP; ++p)
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      A.g[p][j] = A.u[p][j] = A.w[p][j] = u32x4{0u, 0u, 0u, 0u};
+      Bf.g[p][j] = Bf.u[p][j] = Bf.w[p][j] = u32x4{0u, 0u, 0u, 0u};
+    }
   float zs[kFusedP];
   fused_issue<T, NV, kDown>(A, rows, 0, nrows, Wg, Wu, WdT, d);
   for (int i0 = 0; i0 < nrows; i0 += 2 * kFusedP) {
@@ -288,20 +300,18 @@ __device__ __forceinline__ void fused_rows(const int* rows, int nrows, const T* 
   }
 }
 
-// Down-projection of the selected candidates: block (c, cs) takes rows
-// [c * rows_per_schunk, (c + 1) * rows_per_schunk) of S and the column slice
-// cs * 256 * V + [0, 256 * V), every row's load in flight at once, and writes
-// its share of the chunk's partial partial_s[c].  Row j of S is
+// Down-projection of the selected candidates: chunk c takes rows
+// [c * ROWS, (c + 1) * ROWS) of S and the column slice cs * 256 * V +
+// [0, 256 * V), every row's load in flight at once, and writes its share of
+// the chunk's partial partial_s[c].  Row j of S is
 // (ch, z) = (sel[j], z[zoff + pos[j]]).
 template <typename T, int ROWS>
-__global__ __launch_bounds__(kFusedThreads) void k_down_selected(const float* __restrict__ z, int zoff, int n_A,
-                                                                 const T* __restrict__ WdT, int d, int d_ff,
-                                                                 const int32_t* __restrict__ sel,
-                                                                 const int32_t* __restrict__ pos, int k,
-                                                                 float* __restrict__ partial_s) {
+__device__ __forceinline__ void selected_rows_block(int c, int cs, const float* __restrict__ z, int zoff, int n_A,
+                                                    const T* __restrict__ WdT, int d, int d_ff,
+                                                    const int32_t* __restrict__ sel, const int32_t* __restrict__ pos,
+                                                    int k, float* __restrict__ partial_s) {
   constexpr int V = Vec<T>::N;
-  const int c = blockIdx.x;
-  const int col = (blockIdx.y * kFusedThreads + threadIdx.x) * V;
+  const int col = (cs * kFusedThreads + (int)threadIdx.x) * V;
   const int j0 = c * ROWS;
   const int nr = min(ROWS, k - j0);
   u32x4 w[ROWS];
@@ -347,50 +357,61 @@ __device__ __forceinline__ void fused_setup(const T* __restrict__ x, int d, u32x
   }
 }
 
-// Candidate rows: block b takes C[b * rows_per_block, ...) and writes their z
-// (after the n_R retained entries) and scores |z|.
-template <typename T, int NV>
-__global__ __launch_bounds__(kFusedThreads) void k_candidate_rows(
-    const T* __restrict__ x, int d, const T* __restrict__ Wg, const T* __restrict__ Wu, int d_ff,
-    const int32_t* __restrict__ C, int n_R, int n_C, float* __restrict__ z, float* __restrict__ score,
-    int rows_per_block) {
-  __shared__ int rows[kFusedMaxRows];
-  __shared__ float part[2][4][2 * kFusedP];
-  u32x4 xv[NV];
-  float acc[NV][Vec<T>::N];
-  fused_setup<T, NV>(x, d, xv, acc);
-  const int r0 = blockIdx.x * rows_per_block;
-  const int nrows = max(0, min(n_C, r0 + rows_per_block) - r0);
-  for (int i = threadIdx.x; i < nrows; i += kFusedThreads) rows[i] = clamp_channel(C[r0 + i], d_ff);
-  __syncthreads();
-  fused_rows<T, NV, false>(rows, nrows, Wg, Wu, (const T*)nullptr, d, xv, part, acc, z, n_R + r0, score + r0);
-}
+// Launch-invariant arguments of k_pop_step, kept as separate restrict-qualified
+// kernel parameters (a by-value struct loses the no-alias information and the
+// retained stream measured about 8% slower that way).
+#define POP_STEP_PARAMS                                                                                          \
+  const T *__restrict__ x, const T *__restrict__ Wg, const T *__restrict__ Wu, const T *__restrict__ WdT,        \
+      const int32_t *__restrict__ R, const int32_t *__restrict__ C, float *__restrict__ z,                       \
+      float *__restrict__ score, int32_t *__restrict__ Q, int32_t *__restrict__ sel, float *__restrict__ partial, \
+      float *__restrict__ partial_s, int d, int d_ff, int n_R, int n_C, int k, int rows_per_cblock,              \
+      int rows_per_rblock, int n_slices, int nb0, int rb_base
 
-// Retained rows, with the top-k beside them: blocks [0, nbT) run the top-k
-// over the scores an earlier launch wrote; block nbT + b takes
-// R[b * rows_per_block, ...) (rows b * rows_per_block, ... with kIdentity),
-// writes their z and its partial y = sum over its rows of z * W_downT[ch, :].
-template <typename T, int NV, bool kIdentity>
-__global__ __launch_bounds__(kFusedThreads) void k_retained_rows(
-    const T* __restrict__ x, int d, const T* __restrict__ Wg, const T* __restrict__ Wu, const T* __restrict__ WdT,
-    int d_ff, const int32_t* __restrict__ R, int n_R, const float* __restrict__ score,
-    const int32_t* __restrict__ C, int n_C, int k, int32_t* __restrict__ positions,
-    int32_t* __restrict__ selected, float* __restrict__ z, float* __restrict__ partial, int nbT,
-    int rows_per_block) {
+struct NoSel {};
+
+// One launch of the batch-1 step.  Blocks [0, nb0) run the phase's link of the
+// candidate chain (see above; PHASE 0 has no chain link: every block is a
+// retained block, compiled without the chain's code); block nb0 + b runs
+// retained block rb_base + b: rows R[rb * rows_per_rblock, ...) (rows
+// rb * rows_per_rblock, ... with kIdentity), their z, and its partial
+// y = sum of z * W_downT[ch, :].
+template <typename T, int NV, bool kIdentity, int PHASE>
+__global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
   constexpr int V = Vec<T>::N;
-  __shared__ SelShared<kFusedThreads, kFusedTopkMaxN> sel;
+#ifdef POP_STEP_SELSHARED_ALL
+  using SelT = SelShared<kFusedThreads, kFusedTopkMaxN>;
+#else
+  using SelT = typename std::conditional<PHASE == 2, SelShared<kFusedThreads, kFusedTopkMaxN>, NoSel>::type;
+#endif
+  __shared__ SelT sh_sel;
   __shared__ int rows[kFusedMaxRows];
   __shared__ float part[2][4][2 * kFusedP];
-  if ((int)blockIdx.x < nbT) {
-    topk_block(score, n_C, k, C, positions, selected, sel);
+  const int bid = blockIdx.x;
+  if (PHASE != 0 && bid < nb0) {
+    if constexpr (PHASE == 0) {
+    } else if constexpr (PHASE == 1) {  // candidate rows: z (after the n_R retained entries) and scores |z|
+      u32x4 xv[NV];
+      float acc[NV][V];
+      fused_setup<T, NV>(x, d, xv, acc);
+      const int r0 = bid * rows_per_cblock;
+      const int nrows = max(0, min(n_C, r0 + rows_per_cblock) - r0);
+      for (int i = threadIdx.x; i < nrows; i += kFusedThreads) rows[i] = clamp_channel(C[r0 + i], d_ff);
+      __syncthreads();
+      fused_rows<T, NV, false>(rows, nrows, Wg, Wu, (const T*)nullptr, d, xv, part, acc, z, n_R + r0, score + r0);
+    } else if constexpr (PHASE == 2) {  // the top-k over the scores phase 1 wrote
+      topk_block(score, n_C, k, C, Q, sel, sh_sel);
+    } else {  // the selected rows' down-projection
+      selected_rows_block<T, POP_SEL_ROWS>(bid / n_slices, bid % n_slices, z, n_R, n_R + n_C, WdT, d, d_ff, sel, Q,
+                                           k, partial_s);
+    }
     return;
   }
   u32x4 xv[NV];
   float acc[NV][V];
   fused_setup<T, NV>(x, d, xv, acc);
-  const int rb = blockIdx.x - nbT;
-  const int r0 = rb * rows_per_block;
-  const int nrows = max(0, min(n_R, r0 + rows_per_block) - r0);
+  const int rb = rb_base + bid - nb0;
+  const int r0 = rb * rows_per_rblock;
+  const int nrows = max(0, min(n_R, r0 + rows_per_rblock) - r0);
   for (int i = threadIdx.x; i < nrows; i += kFusedThreads) rows[i] = kIdentity ? r0 + i : clamp_channel(R[r0 + i], d_ff);
   __syncthreads();
   fused_rows<T, NV, true>(rows, nrows, Wg, Wu, WdT, d, xv, part, acc, z, r0, nullptr);
@@ -404,6 +425,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_retained_rows(
     }
   }
 }
+#undef POP_STEP_PARAMS
 
 // ---------------------------------------------------------------- K6
 // Block: 256 threads = 4 waves sharing one column slice of 64*V columns.  The
@@ -647,8 +669,11 @@ static void launch_down(hipStream_t st, const float* z, int B, int n_A, const vo
                      n_live > 0 ? p.n_chunks : 0, n_out, y, (unsigned int*)nullptr, 0);
 }
 
-// Batch-1 decode step through k_candidate_rows and k_retained_rows: false when d is too wide for
-// the kernel's per-thread columns (the caller then runs the stage kernels).
+// Batch-1 decode step through k_pop_step: false when d is too wide for the
+// kernel's per-thread columns (the caller then runs the stage kernels).
+// With aux set, the candidate chain (phases 1-3 without retained shares) runs
+// on aux beside one launch of every retained block on st, joined before the
+// sum; the partial sums and their order are the same as on one stream.
 template <typename T>
 static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, const void* Wu, const void* WdT,
                          int d_ff, const int32_t* R, int n_R, const int32_t* C, int n_C, int k, float* y,
@@ -672,67 +697,66 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
     nbR = (n_R + rows_per_rblock - 1) / rows_per_rblock;
   }
   if (rows_per_cblock > kFusedMaxRows || rows_per_rblock > kFusedMaxRows) return false;
-  const bool fuse_topk = n_C > 0 && n_C <= kFusedTopkMaxN;
+  const bool fuse_topk = n_C > 0 && k > 0 && n_C <= kFusedTopkMaxN;
   const int n_schunks = k > 0 ? (k + POP_SEL_ROWS - 1) / POP_SEL_ROWS : 0;
+  const int n_slices = (d + kFusedThreads * V - 1) / (kFusedThreads * V);
+  // retained shares of the three launches
+  const int nbR2 = fuse_topk ? nbR * POP_SPLIT_B / 100 : 0;
+  const int nbR3 = n_schunks > 0 ? nbR * POP_SPLIT_C / 100 : 0;
+  const int nbR1 = nbR - nbR2 - nbR3;
   float* partial = (float*)w.down;
   float* partial_s = partial + (int64_t)nbR * d;
-#define POP_NV_DISPATCH(MACRO) \
-  if (nv <= 1) {               \
-    MACRO(1);                  \
-  } else if (nv <= 2) {        \
-    MACRO(2);                  \
+  auto step = [&](int phase, hipStream_t sx, int nb0, int rb_base, int n_ret) {
+    if (nb0 + n_ret <= 0) return;
+    const dim3 grid(nb0 + n_ret);
+#define POP_STEP(NVT, ID, PH)                                                                                   \
+  POP_LAUNCH((k_pop_step<T, NVT, ID, PH>), grid, dim3(kFusedThreads), 0, sx, (const T*)x, (const T*)Wg,          \
+             (const T*)Wu, (const T*)WdT, R, C, w.z, w.score, w.Q, w.sel, partial, partial_s, d, d_ff, n_R, n_C, k, \
+             rows_per_cblock, rows_per_rblock, n_slices, nb0, rb_base)
+#define POP_STEP_PH(NVT, ID)   \
+  if (nb0 == 0) {              \
+    POP_STEP(NVT, ID, 0);      \
+  } else if (phase == 1) {     \
+    POP_STEP(NVT, ID, 1);      \
+  } else if (phase == 2) {     \
+    POP_STEP(NVT, ID, 2);      \
   } else {                     \
-    MACRO(4);                  \
+    POP_STEP(NVT, ID, 3);      \
   }
-  auto candidates = [&](hipStream_t sx) {
-    if (nbC == 0) return;
-#define POP_CAND(NVT)                                                                                         \
-  POP_LAUNCH((k_candidate_rows<T, NVT>), dim3(nbC), dim3(kFusedThreads), 0, sx, (const T*)x, d, (const T*)Wg, \
-             (const T*)Wu, d_ff, C, n_R, n_C, w.z, w.score, rows_per_cblock)
-    POP_NV_DISPATCH(POP_CAND)
-#undef POP_CAND
-  };
-  auto retained = [&](hipStream_t sx, int nbT) {
-    if (nbT + nbR == 0) return;
-    const dim3 grid(nbT + nbR);
-#define POP_RET(NVT)                                                                                                \
-  if (identity)                                                                                                     \
-    POP_LAUNCH((k_retained_rows<T, NVT, true>), grid, dim3(kFusedThreads), 0, sx, (const T*)x, d, (const T*)Wg,     \
-               (const T*)Wu, (const T*)WdT, d_ff, R, n_R, (const float*)w.score, C, n_C, k, w.Q, w.sel, w.z,       \
-               partial, nbT, rows_per_rblock);                                                                      \
-  else                                                                                                              \
-    POP_LAUNCH((k_retained_rows<T, NVT, false>), grid, dim3(kFusedThreads), 0, sx, (const T*)x, d, (const T*)Wg,    \
-               (const T*)Wu, (const T*)WdT, d_ff, R, n_R, (const float*)w.score, C, n_C, k, w.Q, w.sel, w.z,       \
-               partial, nbT, rows_per_rblock)
-    POP_NV_DISPATCH(POP_RET)
-#undef POP_RET
-  };
-#undef POP_NV_DISPATCH
-  auto selected_rows = [&](hipStream_t sx) {
-    if (n_schunks > 0) {
-      const dim3 g3(n_schunks, (d + kFusedThreads * V - 1) / (kFusedThreads * V));
-      POP_LAUNCH((k_down_selected<T, POP_SEL_ROWS>), g3, dim3(kFusedThreads), 0, sx, (const float*)w.z, n_R,
-                 n_R + n_C, (const T*)WdT, d, d_ff, (const int32_t*)w.sel, (const int32_t*)w.Q, k, partial_s);
+#define POP_STEP_ID(NVT)         \
+  if (identity) {                \
+    POP_STEP_PH(NVT, true)       \
+  } else {                       \
+    POP_STEP_PH(NVT, false)      \
+  }
+    if (nv <= 1) {
+      POP_STEP_ID(1)
+    } else if (nv <= 2) {
+      POP_STEP_ID(2)
+    } else {
+      POP_STEP_ID(4)
     }
+#undef POP_STEP_ID
+#undef POP_STEP_PH
+#undef POP_STEP
   };
+  const int nb_sel = n_schunks * n_slices;
   if (aux != nullptr) {
-    // Two streams: the candidate chain (scores -> top-k -> selected rows) on
-    // `aux` beside the retained stream on `st`, joined before the sum.
     (void)hipEventRecord(fork, st);
     (void)hipStreamWaitEvent(aux, fork, 0);
-    candidates(aux);
-    retained(st, 0);
-    launch_select(aux, w.score, n_C, C, k, w.Q, w.sel);
-    selected_rows(aux);
+    step(1, aux, nbC, 0, 0);
+    if (n_C > 0 && k > 0 && !fuse_topk) launch_select(aux, w.score, n_C, C, k, w.Q, w.sel);
+    step(2, aux, fuse_topk ? 1 : 0, 0, 0);
+    step(3, aux, nb_sel, 0, 0);
+    step(1, st, 0, 0, nbR);
     (void)hipEventRecord(join, aux);
     (void)hipStreamWaitEvent(st, join, 0);
   } else {
-    candidates(st);                                                          // launch 1
-    if (n_C > 0 && !fuse_topk) launch_select(st, w.score, n_C, C, k, w.Q, w.sel);
-    retained(st, fuse_topk ? 1 : 0);                                         // launch 2
-    selected_rows(st);                                                       // launch 3
+    step(1, st, nbC, 0, nbR1);
+    if (n_C > 0 && k > 0 && !fuse_topk) launch_select(st, w.score, n_C, C, k, w.Q, w.sel);
+    step(2, st, fuse_topk ? 1 : 0, nbR1, nbR2);
+    step(3, st, nb_sel, nbR1 + nbR2, nbR3);
   }
-  // launch 4: fixed-order sum of every partial
   POP_LAUNCH(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(1024), 0, st, (const float*)partial, nbR + n_schunks,
              (int64_t)d, y, (unsigned int*)nullptr, 0);
   return true;
