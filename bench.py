@@ -309,8 +309,12 @@ def main():
         if n_C > 4096 and k > 0:
             labels_dec.insert(1, "k_topk")
         labels_dense = ["k_pop_step.0(dense)", "k_sum_chunks(y)"]
+    elif e == 2 and 8 <= B <= 64:   # matrix-core batched decode
+        labels_dec = (["k_gateup_mfma"] + (["k_topk"] if n_C > 0 and k > 0 else [])
+                      + ["k_gather_zlive", "k_down_mfma", "k_sum_chunks(y)"])
+        labels_dense = ["k_gateup_mfma(dense)", "k_gather_zlive(dense)", "k_down_mfma(dense)", "k_sum_chunks(y)"]
     else:
-        labels_dec = ["k_gateup"] + (["k_topk"] if n_C > 0 else []) + ["k_down_partial", "k_sum_chunks(y)"]
+        labels_dec = ["k_gateup"] + (["k_topk"] if n_C > 0 and k > 0 else []) + ["k_down_partial", "k_sum_chunks(y)"]
         labels_dense = ["k_gateup(dense)", "k_down_partial(dense)", "k_sum_chunks(y)"]
 
     def kernel_pass(marks):
@@ -391,8 +395,8 @@ def main():
                        "retained stream)"}[ph]
         dom_bytes = plan["bytes"][ph]
     else:
-        dom = "k_gateup"
-        dom_desc = "k_gateup (decode gate/up over R u C, fused SiLU*up and candidate score)"
+        dom = labels_dec[0]
+        dom_desc = f"{dom} (batched decode gate/up over R u C, fused SiLU*up and batch-max candidate score)"
         dom_bytes = metrics.gateup_bytes(d, n_A, n_C, B, e)
     dom_us = kus[dom]
     tname = "pop::bf16s" if e == 2 else "float"

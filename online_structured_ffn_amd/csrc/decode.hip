@@ -11,6 +11,7 @@
 
 #include <type_traits>
 
+#include "decode_mfma.h"
 #include "pop_device.h"
 #include "pop_internal.h"
 
@@ -562,13 +563,30 @@ static DownPlan plan_down(int n_live, int B, int d, int vec) {
   return p;
 }
 
+// Live-row chunks of the matrix-core down-projection: about 2048 blocks over
+// the 64-column slices, at most kDownMaxChunk rows each (never decreasing in
+// n_live, so the value at n_live = d_ff bounds every call).
+static int down_mfma_chunks(int n_live, int d) {
+  const int slices = (d + 63) / 64;
+  int want = (2048 + slices - 1) / slices;
+  const int by_rows = (n_live + kDownTileRows - 1) / kDownTileRows;
+  if (want > by_rows) want = by_rows;
+  const int least = (n_live + kDownMaxChunk - 1) / kDownMaxChunk;
+  if (want < least) want = least;
+  return want < 1 ? 1 : want;
+}
+
 static size_t down_ws_bytes(int32_t batch, int32_t d, int32_t n_live) {
   // The chunk count only grows with n_live; bf16 (fewer column blocks) wants at least as many as fp32.
   const int c8 = down_chunks_wanted(n_live, batch, d, 8);
   const int c4 = down_chunks_wanted(n_live, batch, d, 4);
-  const int chunks = c8 > c4 ? c8 : c4;
+  const int cm = down_mfma_chunks(n_live, d);
+  int chunks = c8 > c4 ? c8 : c4;
+  if (cm > chunks) chunks = cm;
   const int b = batch > 0 ? batch : 1;
-  return align_up((size_t)chunks * b * d * sizeof(float), 256);
+  // partial sums, and the matrix-core path's gathered bf16 z ahead of them
+  return align_up((size_t)chunks * b * d * sizeof(float), 256) +
+         align_up((size_t)b * (align_up((size_t)(n_live > 0 ? n_live : 1), 8) + kDownTileRows) * 2, 256);
 }
 
 struct DecodeWs {
@@ -611,10 +629,41 @@ static size_t decode_ws_layout(int32_t batch, int32_t d, int32_t d_ff, char* bas
 }
 
 // ---- stage launchers (arguments already validated)
+// Batches of 8..64 rows in bf16 run on the matrix cores (below 8 the FMA
+// kernels measured faster).
+#ifndef POP_MFMA_MIN_BATCH
+#define POP_MFMA_MIN_BATCH 8
+#endif
+template <typename T>
+static bool use_mfma(int B) {
+  return std::is_same<T, bf16s>::value && B >= POP_MFMA_MIN_BATCH && B <= 16 * kDecMaxTiles;
+}
+
 template <typename T>
 static void launch_gateup(hipStream_t st, const void* x, int B, int d, const void* Wg, const void* Wu, int d_ff,
                           const int32_t* R, int n_R, const int32_t* C, int n_C, float* z, float* score) {
   const int n_A = n_R + n_C;
+  if (use_mfma<T>(B)) {
+    if (n_A == 0) return;
+    const bool identity = R == nullptr && n_C == 0;
+    const dim3 grid((n_A + 16 * kGuNT - 1) / (16 * kGuNT));
+#define POP_GU_MFMA(MT)                                                                                      \
+  if (identity)                                                                                              \
+    POP_LAUNCH((k_gateup_mfma<MT, true>), grid, dim3(256), 0, st, (const bf16s*)x, B, d, (const bf16s*)Wg,   \
+               (const bf16s*)Wu, d_ff, R, n_R, C, n_C, z, score);                                             \
+  else                                                                                                       \
+    POP_LAUNCH((k_gateup_mfma<MT, false>), grid, dim3(256), 0, st, (const bf16s*)x, B, d, (const bf16s*)Wg,  \
+               (const bf16s*)Wu, d_ff, R, n_R, C, n_C, z, score)
+    if (B <= 16) {
+      POP_GU_MFMA(1);
+    } else if (B <= 32) {
+      POP_GU_MFMA(2);
+    } else {
+      POP_GU_MFMA(4);
+    }
+#undef POP_GU_MFMA
+    return;
+  }
   int grid = (n_A + 3) / 4;
   if (grid < 1) grid = 1;
   // R == NULL means identity rows (the dense baseline) only when there are no
@@ -647,6 +696,41 @@ static void launch_down(hipStream_t st, const float* z, int B, int n_A, const vo
                         float* partial) {
   if (B == 0) return;
   const int n_live = n_R + k;
+  if (use_mfma<T>(B)) {
+    const int n_chunks = n_live > 0 ? down_mfma_chunks(n_live, d) : 0;
+    if (n_chunks > 0) {
+      // chunks start on multiples of 8 rows (aligned A vectors); kDownMaxChunk is one too
+      const int rows_per_chunk = (int)align_up((size_t)((n_live + n_chunks - 1) / n_chunks), 8);
+      const int used = (n_live + rows_per_chunk - 1) / rows_per_chunk;
+      const dim3 grid((d + 63) / 64, used);
+      const bool identity = R == nullptr && k == 0;
+      // region: gathered bf16 z [B][ldl] (a tile of zeros past n_live), then the partial sums
+      const int ldl = (int)align_up((size_t)n_live, 8) + kDownTileRows;
+      uint16_t* zl = (uint16_t*)partial;
+      partial = (float*)((char*)partial + align_up((size_t)B * ldl * 2, 256));
+      const int pairs = B * ldl / 2;
+      POP_LAUNCH(k_gather_zlive, dim3((pairs + 255) / 256), dim3(256), 0, st, z, n_A, B, n_R, Q, n_live, ldl, zl);
+#define POP_DN_MFMA(MT)                                                                                           \
+  if (identity)                                                                                                   \
+    POP_LAUNCH((k_down_mfma<MT, true>), grid, dim3(256), 0, st, (const uint16_t*)zl, ldl, B, (const bf16s*)WdT, d,  \
+               d_ff, R, n_R, sel, n_live, rows_per_chunk, partial);                                               \
+  else                                                                                                            \
+    POP_LAUNCH((k_down_mfma<MT, false>), grid, dim3(256), 0, st, (const uint16_t*)zl, ldl, B, (const bf16s*)WdT, d, \
+               d_ff, R, n_R, sel, n_live, rows_per_chunk, partial)
+      if (B <= 16) {
+        POP_DN_MFMA(1);
+      } else if (B <= 32) {
+        POP_DN_MFMA(2);
+      } else {
+        POP_DN_MFMA(4);
+      }
+#undef POP_DN_MFMA
+      const int64_t n_out = (int64_t)B * d;
+      POP_LAUNCH(k_sum_chunks<0>, dim3((unsigned)((n_out + 31) / 32)), dim3(1024), 0, st, (const float*)partial, used,
+                 n_out, y, (unsigned int*)nullptr, 0);
+      return;
+    }
+  }
   const DownPlan p = plan_down(n_live, B, d, Vec<T>::N);
   // Identity rows only for the dense baseline (no selected rows).
 #define POP_DOWN(BT)                                                                                          \

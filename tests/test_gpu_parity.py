@@ -130,6 +130,13 @@ DEC_CASES = [
     ("bf16_r0", 12, 256, 500, 2, "bf16", 0.0, 0.1),
     ("bf16_gamma0", 12, 256, 500, 2, "bf16", 0.4, 0.0),
     ("f32_high_r", 12, 128, 300, 1, "f32", 0.95, 0.1),
+    # matrix-core batches: one, two and four 16-token tiles, ragged d; 65 falls back to the FMA kernels
+    ("bf16_b8_mfma", 30, 520, 1501, 8, "bf16", 0.3, 0.1),
+    ("bf16_b16_mfma_tail_chunk", 30, 264, 1000, 16, "bf16", 0.3, 0.1),
+    ("bf16_b17_mfma", 30, 264, 1000, 17, "bf16", 0.3, 0.1),
+    ("bf16_b40_mfma", 30, 1032, 1501, 40, "bf16", 0.299, 0.1),
+    ("bf16_b64_mfma", 30, 520, 700, 64, "bf16", 0.5, 0.1),
+    ("bf16_b65_fma", 30, 256, 600, 65, "bf16", 0.3, 0.1),
 ]
 
 
