@@ -108,10 +108,10 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(const bf16s* __restrict__ x
     const int ca = S.on_a ? ka : 0, cb = S.on_b ? kb8 : 0;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      S.g0[n] = ld16_stream(wg[n] + ca);
-      S.g1[n] = ld16_stream(wg[n] + cb);
-      S.u0[n] = ld16_stream(wu[n] + ca);
-      S.u1[n] = ld16_stream(wu[n] + cb);
+      S.g0[n] = ld16(wg[n] + ca);  // plain loads measured faster than non-temporal here
+      S.g1[n] = ld16(wg[n] + cb);
+      S.u0[n] = ld16(wu[n] + ca);
+      S.u1[n] = ld16(wu[n] + cb);
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -258,8 +258,8 @@ __global__ __launch_bounds__(256) void k_down_mfma(const uint16_t* __restrict__ 
 #pragma unroll
   for (int h = 0; h < kDownPairs; ++h) {
     const int qa = 64 * h + 2 * kp;
-    va[h] = ld16_stream(WdT + (int64_t)rch[qa] * d + col_c);
-    vb[h] = ld16_stream(WdT + (int64_t)rch[qa + 1] * d + col_c);
+    va[h] = ld16(WdT + (int64_t)rch[qa] * d + col_c);  // plain loads: measured faster than non-temporal
+    vb[h] = ld16(WdT + (int64_t)rch[qa + 1] * d + col_c);
   }
   // the A fragments: tokens past B read token 0 (their sums are never
   // stored); q0 is a multiple of 8 and zl carries kDownTileRows rows of zero
