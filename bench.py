@@ -304,11 +304,10 @@ def main():
                   ["k_prompt_gateup_f32", "k_prompt_down_f32"]) * n_pass
     if fused:
         plan = metrics.fused_plan(n_R, n_C, k, d, e)
-        labels_dec = ([f"k_pop_step.{ph}" for ph in (1, 2, 3) if plan["launch"][ph]]
-                      + ["k_sum_chunks(y)"])
+        labels_dec = [f"k_pop_step.{ph}" for ph in (1, 2) if plan["launch"][ph]] + ["k_pop_finish"]
         if n_C > 4096 and k > 0:
             labels_dec.insert(1, "k_topk")
-        labels_dense = ["k_pop_step.0(dense)", "k_sum_chunks(y)"]
+        labels_dense = ["k_pop_step.0(dense)", "k_pop_finish(dense)"]
     elif e == 2 and 8 <= B <= 64:   # matrix-core batched decode
         labels_dec = (["k_gateup_mfma"] + (["k_topk"] if n_C > 0 and k > 0 else [])
                       + ["k_gather_zlive", "k_down_mfma", "k_sum_chunks(y)"])
@@ -386,13 +385,13 @@ def main():
 
     if fused:
         ph = max((p for p in (1, 2, 3) if plan["launch"][p]), key=lambda p: plan["bytes"][p])
-        dom = f"k_pop_step.{ph}"
+        dom = f"k_pop_step.{ph}" if ph < 3 else "k_pop_finish"
         dom_desc = {1: "k_pop_step phase 1 (batch-1 decode: candidate gate/up rows with fused SiLU*up and score, "
                        "beside a share of the retained rows' gate, up and W_downT stream)",
                     2: "k_pop_step phase 2 (batch-1 decode: gate, up and W_downT rows of the retained channels in "
                        "one stream, with the one-workgroup candidate top-k beside it)",
-                    3: "k_pop_step phase 3 (batch-1 decode: selected candidates' W_downT rows beside a share of the "
-                       "retained stream)"}[ph]
+                    3: "k_pop_finish (batch-1 decode: retained partial sums and the selected candidates' W_downT "
+                       "rows, per column slice of y)"}[ph]
         dom_bytes = plan["bytes"][ph]
     else:
         dom = labels_dec[0]
@@ -402,7 +401,8 @@ def main():
     tname = "pop::bf16s" if e == 2 else "float"
     if fused:
         nv = -(-d // (256 * vec))
-        dom_symbol = f"pop::k_pop_step<{tname}, {1 if nv <= 1 else 2 if nv <= 2 else 4}, false, {ph}>"
+        dom_symbol = (f"pop::k_pop_step<{tname}, {1 if nv <= 1 else 2 if nv <= 2 else 4}, false, {ph}>" if ph < 3
+                      else f"pop::k_pop_finish<{tname}>")
     else:
         dom_symbol = None
     tb = profiling.traffic_bytes(dom_symbol) if dom_symbol and w.name == "llama2_7b_ffn_b1" else None

@@ -135,15 +135,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 // thread.  Rows go in batches of two, double-buffered: the next batch's loads
 // are in flight while the current batch's dot products are reduced (DPP
 // within each wave, LDS across the four waves, fixed order).
-// A decode step is three launches of k_pop_step and a sum.  Each launch gives
-// its first blocks to a step of the candidate chain and the rest to a share of
-// the retained rows (gate, up and W_downT rows: z and a partial y per block),
-// so every link of the chain runs beside retained work instead of alone:
+// A decode step is two launches of k_pop_step and one of k_pop_finish.  Each
+// k_pop_step launch gives its first blocks to a link of the candidate chain and
+// the rest to a share of the retained rows (gate, up and W_downT rows: z and a
+// partial y per block), so the chain's links run beside retained work instead
+// of alone:
 //   phase 1: candidate rows (z and scores)            + retained share A
 //   phase 2: the top-k over those scores (one block)  + retained share B
-//   phase 3: the selected rows' W_downT (chunks x column slices) + share C
-// then k_sum_chunks adds every partial y in a fixed order.  No block waits on
-// another inside a launch: each link reads what an earlier launch wrote.
+// k_pop_finish then owns y: each block takes a slice of columns and adds, in a
+// fixed order, every retained partial and the selected rows' z * W_downT.  No
+// block waits on another inside a launch: each link reads what an earlier
+// launch wrote.
 // Launch-shape tunables (overridable with -D for sweeps).
 #ifndef POP_FUSED_RBLOCKS
 #define POP_FUSED_RBLOCKS 512  // most blocks for the retained rows
@@ -151,15 +153,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 #ifndef POP_FUSED_CROWS
 #define POP_FUSED_CROWS 4  // candidate rows per block
 #endif
-#ifndef POP_SEL_ROWS
-#define POP_SEL_ROWS 8  // selected rows per chunk
-#endif
 #ifndef POP_SPLIT_B
 #define POP_SPLIT_B 100  // percent of the retained blocks beside the top-k
 #endif
-#ifndef POP_SPLIT_C
-#define POP_SPLIT_C 0  // percent of the retained blocks beside the selected rows
+#ifndef POP_FIN_COLS
+#define POP_FIN_COLS 16  // columns of y per k_pop_finish block (16, 32 or 64)
 #endif
+// Retained partial sums are stored slice-major: the value of column c of
+// retained block rb sits at ((c / kFinCols) * n_part + rb) * kFinCols +
+// c % kFinCols, so the rows k_pop_finish reads for one column slice are one
+// contiguous run of n_part * kFinCols floats.
+constexpr int kFinCols = POP_FIN_COLS;
 constexpr int kFusedThreads = 256;
 constexpr int kFusedTopkMaxN = 4096;
 constexpr int kFusedMaxRows = 512;  // rows per block
@@ -301,49 +305,6 @@ __device__ __forceinline__ void fused_rows(const int* rows, int nrows, const T* 
   }
 }
 
-// Down-projection of the selected candidates: chunk c takes rows
-// [c * ROWS, (c + 1) * ROWS) of S and the column slice cs * 256 * V +
-// [0, 256 * V), every row's load in flight at once, and writes its share of
-// the chunk's partial partial_s[c].  Row j of S is
-// (ch, z) = (sel[j], z[zoff + pos[j]]).
-template <typename T, int ROWS>
-__device__ __forceinline__ void selected_rows_block(int c, int cs, const float* __restrict__ z, int zoff, int n_A,
-                                                    const T* __restrict__ WdT, int d, int d_ff,
-                                                    const int32_t* __restrict__ sel, const int32_t* __restrict__ pos,
-                                                    int k, float* __restrict__ partial_s) {
-  constexpr int V = Vec<T>::N;
-  const int col = (cs * kFusedThreads + (int)threadIdx.x) * V;
-  const int j0 = c * ROWS;
-  const int nr = min(ROWS, k - j0);
-  u32x4 w[ROWS];
-  float zv[ROWS];
-#pragma unroll
-  for (int u = 0; u < ROWS; ++u) {
-    zv[u] = 0.f;
-    if (u < nr) {
-      const int ch = clamp_channel(sel[j0 + u], d_ff);
-      zv[u] = z[min(zoff + max(pos[j0 + u], 0), n_A - 1)];
-      if (col < d) w[u] = ld16_stream(WdT + (int64_t)ch * d + col);
-    }
-  }
-  if (col >= d) return;
-  float acc[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) acc[v] = 0.f;
-#pragma unroll
-  for (int u = 0; u < ROWS; ++u) {
-    if (u < nr) {
-      float f[V];
-      unpack(w[u], f, T{});
-#pragma unroll
-      for (int v = 0; v < V; ++v) acc[v] = fmaf(zv[u], f[v], acc[v]);
-    }
-  }
-  float* out = partial_s + (int64_t)c * d + col;
-#pragma unroll
-  for (int v = 0; v < V; ++v) out[v] = acc[v];
-}
-
 // Loads this thread's x vectors and clears its down accumulators.
 template <typename T, int NV>
 __device__ __forceinline__ void fused_setup(const T* __restrict__ x, int d, u32x4 (&xv)[NV],
@@ -365,8 +326,8 @@ __device__ __forceinline__ void fused_setup(const T* __restrict__ x, int d, u32x
   const T *__restrict__ x, const T *__restrict__ Wg, const T *__restrict__ Wu, const T *__restrict__ WdT,        \
       const int32_t *__restrict__ R, const int32_t *__restrict__ C, float *__restrict__ z,                       \
       float *__restrict__ score, int32_t *__restrict__ Q, int32_t *__restrict__ sel, float *__restrict__ partial, \
-      float *__restrict__ partial_s, int d, int d_ff, int n_R, int n_C, int k, int rows_per_cblock,              \
-      int rows_per_rblock, int n_slices, int nb0, int rb_base
+      int d, int d_ff, int n_R, int n_C, int k, int rows_per_cblock, int rows_per_rblock, int nb0, int rb_base,  \
+      int n_part
 
 struct NoSel {};
 
@@ -378,6 +339,7 @@ struct NoSel {};
 // y = sum of z * W_downT[ch, :].
 template <typename T, int NV, bool kIdentity, int PHASE>
 __global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
+  static_assert(PHASE >= 0 && PHASE <= 2, "phases 0, 1, 2");
   constexpr int V = Vec<T>::N;
 #ifdef POP_STEP_SELSHARED_ALL
   using SelT = SelShared<kFusedThreads, kFusedTopkMaxN>;
@@ -399,11 +361,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
       for (int i = threadIdx.x; i < nrows; i += kFusedThreads) rows[i] = clamp_channel(C[r0 + i], d_ff);
       __syncthreads();
       fused_rows<T, NV, false>(rows, nrows, Wg, Wu, (const T*)nullptr, d, xv, part, acc, z, n_R + r0, score + r0);
-    } else if constexpr (PHASE == 2) {  // the top-k over the scores phase 1 wrote
+    } else {  // the top-k over the scores phase 1 wrote
       topk_block(score, n_C, k, C, Q, sel, sh_sel);
-    } else {  // the selected rows' down-projection
-      selected_rows_block<T, POP_SEL_ROWS>(bid / n_slices, bid % n_slices, z, n_R, n_R + n_C, WdT, d, d_ff, sel, Q,
-                                           k, partial_s);
     }
     return;
   }
@@ -416,17 +375,171 @@ __global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
   for (int i = threadIdx.x; i < nrows; i += kFusedThreads) rows[i] = kIdentity ? r0 + i : clamp_channel(R[r0 + i], d_ff);
   __syncthreads();
   fused_rows<T, NV, true>(rows, nrows, Wg, Wu, WdT, d, xv, part, acc, z, r0, nullptr);
-  float* out = partial + (int64_t)rb * d;
+  static_assert(kFinCols % V == 0, "a thread's columns lie in one slice");
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int col = j * kFusedThreads * V + (int)threadIdx.x * V;
     if (col < d) {
+      float* out = partial + ((int64_t)(col / kFinCols) * n_part + rb) * kFinCols + col % kFinCols;
 #pragma unroll
-      for (int v = 0; v < V; ++v) out[col + v] = acc[j][v];
+      for (int v = 0; v < V; ++v) out[v] = acc[j][v];
     }
   }
 }
 #undef POP_STEP_PARAMS
+
+// The last launch of the batch-1 step.  Block s owns the kFinCols columns
+// c0 = s * kFinCols + [0, kFinCols) of y and adds, in a fixed order, the
+// n_part retained partial sums and (kSel) the k selected rows' z * W_downT,
+// then writes y itself (no partial of its own).  1024 threads = 16 waves:
+//   partial rows (slice-major, contiguous): kFinCols / 4 lanes x 4 floats per row;
+//   selected rows: kFinCols / V lanes x 16 bytes per row; row j of S is
+//   (ch, z) = (sel[j], z[zoff + pos[j]]).
+// Issue order: the first batch's selected-row indices, the first batch of
+// partial rows, then (once the indices are in) the selected rows' z and
+// W_downT, and only then the partial sums are consumed: for up to
+// kFinRowsPerBatch selected rows and kFinPB * PPB partials every load is in
+// flight at once.  The per-lane sums are reduced across lanes (shuffles), then
+// across waves in wave order (LDS).
+constexpr int kFinThreads = 1024;
+constexpr int kFinRowsPerBatch = 1280;  // selected rows whose loads are in flight together
+constexpr int kFinPartials = 512;       // partial rows whose loads are in flight together
+
+// Block b's column slice.  With slices narrower than 64 columns, the slices
+// of one 128-byte bf16 W_downT line go to blocks on the same XCD (blocks are
+// dealt to the eight XCDs round-robin), so the line is fetched into one L2.
+__device__ __forceinline__ int fin_slice(int b, int nb) {
+  constexpr int SP = kFinCols >= 64 ? 1 : 64 / kFinCols;  // slices per line
+  constexpr int G = 8 * SP;                                // blocks per group
+  if (SP == 1 || (b | (G - 1)) >= nb) return b;            // the last, partial group keeps its order
+  const int q = b / G, h = (b / 8) % SP, x = b % 8;
+  return (q * 8 + x) * SP + h;
+}
+
+template <typename T, bool kSel>
+__global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restrict__ partial, int n_part,
+                                                            const float* __restrict__ z, int zoff, int n_A,
+                                                            const int32_t* __restrict__ sel,
+                                                            const int32_t* __restrict__ pos, int k,
+                                                            const T* __restrict__ WdT, int d, int d_ff,
+                                                            float* __restrict__ y) {
+  constexpr int V = Vec<T>::N;
+  constexpr int LR = kFinCols / V;       // lanes per W_downT row
+  constexpr int RPW = 64 / LR;           // W_downT rows per wave instruction
+  constexpr int RPB = RPW * (kFinThreads / 64);
+  constexpr int LP = kFinCols / 4;       // lanes per partial row
+  constexpr int PPW = 64 / LP;           // partial rows per wave instruction
+  constexpr int PPB = PPW * (kFinThreads / 64);
+  constexpr int PB = (kFinPartials + PPB - 1) / PPB;           // partial-row loads in flight per lane
+  constexpr int SB = (kFinRowsPerBatch + RPB - 1) / RPB;       // selected-row loads in flight per lane
+  __shared__ float red[kFinThreads / 64][kFinCols];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c0 = fin_slice(blockIdx.x, gridDim.x) * kFinCols;
+  const int jl = wave * RPW + lane / LR;  // this lane's selected row within a block instruction
+  const int pl = wave * PPW + lane / LP;  // this lane's partial row within a block instruction
+  const float* pslice = partial + (int64_t)(c0 / kFinCols) * n_part * kFinCols + (lane % LP) * 4;
+  const int colw = min(c0 + (lane % LR) * V, d - V);
+  float ap[4] = {0.f, 0.f, 0.f, 0.f};
+  float as[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) as[v] = 0.f;
+  // raw indices; clamped where they are used, so nothing waits on them early
+  int ch[SB], zi[SB];
+  float zv[SB];
+  u32x4 w[SB];
+  float4 pv[PB];
+  auto load_idx = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int j = max(0, min(j0 + u * RPB + jl, k - 1));
+      ch[u] = sel[j];
+      zi[u] = pos[j];
+    }
+  };
+  auto issue_sel = [&]() {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      zv[u] = z[min(zoff + max(zi[u], 0), n_A - 1)];
+      w[u] = ld16_stream(WdT + (int64_t)clamp_channel(ch[u], d_ff) * d + colw);
+    }
+  };
+  auto consume_sel = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const float zz = j0 + u * RPB + jl < k ? zv[u] : 0.f;
+      float f[V];
+      unpack(w[u], f, T{});
+#pragma unroll
+      for (int v = 0; v < V; ++v) as[v] = fmaf(zz, f[v], as[v]);
+    }
+  };
+  auto issue_part = [&](int p0) {
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int p = max(0, min(p0 + u * PPB + pl, n_part - 1));
+      pv[u] = *reinterpret_cast<const float4*>(pslice + (int64_t)p * kFinCols);
+    }
+  };
+  auto consume_part = [&](int p0) {
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      // a select, not a product: rows past n_part may hold anything
+      const bool on = p0 + u * PPB + pl < n_part;
+      ap[0] += on ? pv[u].x : 0.f;
+      ap[1] += on ? pv[u].y : 0.f;
+      ap[2] += on ? pv[u].z : 0.f;
+      ap[3] += on ? pv[u].w : 0.f;
+    }
+  };
+  // first batches: every load in flight before any is consumed (sel, pos and
+  // partial hold at least one entry, so the loads carry no condition)
+  if constexpr (kSel) load_idx(0);
+  issue_part(0);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kSel) issue_sel();
+  __builtin_amdgcn_sched_barrier(0);
+  consume_part(0);
+  for (int p0 = PB * PPB; p0 < n_part; p0 += PB * PPB) {
+    issue_part(p0);
+    consume_part(p0);
+  }
+  if constexpr (kSel) {
+    consume_sel(0);
+    for (int j0 = SB * RPB; j0 < k; j0 += SB * RPB) {
+      load_idx(j0);
+      issue_sel();
+      consume_sel(j0);
+    }
+  }
+  // ---- lanes with the same columns: fixed butterfly order
+#pragma unroll
+  for (int o = LP; o < 64; o <<= 1)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) ap[v] += __shfl_xor(ap[v], o);
+#pragma unroll
+  for (int o = LR; o < 64; o <<= 1)
+#pragma unroll
+    for (int v = 0; v < V; ++v) as[v] += __shfl_xor(as[v], o);
+  // lanes 0..LP-1 hold the partials' sums of columns 4 * lane + [0, 4);
+  // lanes 0..LR-1 hold the selected rows' sums of columns V * lane + [0, V)
+  if (lane < LP) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][lane * 4 + v] = ap[v];
+  }
+  __syncthreads();
+  if (lane < LR) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) red[wave][lane * V + v] += as[v];
+  }
+  __syncthreads();
+  if (threadIdx.x < kFinCols && c0 + (int)threadIdx.x < d) {
+    float t = red[0][threadIdx.x];
+#pragma unroll
+    for (int w2 = 1; w2 < kFinThreads / 64; ++w2) t += red[w2][threadIdx.x];
+    y[c0 + threadIdx.x] = t;
+  }
+}
 
 // ---------------------------------------------------------------- K6
 // Block: 256 threads = 4 waves sharing one column slice of 64*V columns.  The
@@ -602,8 +715,9 @@ struct DecodeWs {
 constexpr int kFusedRBlocks = POP_FUSED_RBLOCKS;
 
 static size_t fused_partial_bytes(int32_t d, int32_t d_ff) {
-  const int chunks = kFusedRBlocks + (d_ff + POP_SEL_ROWS - 1) / POP_SEL_ROWS;  // retained blocks + selected chunks
-  return align_up((size_t)chunks * d * sizeof(float), 256);
+  (void)d_ff;
+  // one partial y per retained block, slice-major over whole slices
+  return align_up((size_t)kFusedRBlocks * align_up((size_t)d, kFinCols) * sizeof(float), 256);
 }
 
 static size_t decode_ws_layout(int32_t batch, int32_t d, int32_t d_ff, char* base, DecodeWs* out) {
@@ -782,30 +896,24 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
   }
   if (rows_per_cblock > kFusedMaxRows || rows_per_rblock > kFusedMaxRows) return false;
   const bool fuse_topk = n_C > 0 && k > 0 && n_C <= kFusedTopkMaxN;
-  const int n_schunks = k > 0 ? (k + POP_SEL_ROWS - 1) / POP_SEL_ROWS : 0;
-  const int n_slices = (d + kFusedThreads * V - 1) / (kFusedThreads * V);
-  // retained shares of the three launches
+  // retained shares of the two launches
   const int nbR2 = fuse_topk ? nbR * POP_SPLIT_B / 100 : 0;
-  const int nbR3 = n_schunks > 0 ? nbR * POP_SPLIT_C / 100 : 0;
-  const int nbR1 = nbR - nbR2 - nbR3;
+  const int nbR1 = nbR - nbR2;
   float* partial = (float*)w.down;
-  float* partial_s = partial + (int64_t)nbR * d;
   auto step = [&](int phase, hipStream_t sx, int nb0, int rb_base, int n_ret) {
     if (nb0 + n_ret <= 0) return;
     const dim3 grid(nb0 + n_ret);
 #define POP_STEP(NVT, ID, PH)                                                                                   \
   POP_LAUNCH((k_pop_step<T, NVT, ID, PH>), grid, dim3(kFusedThreads), 0, sx, (const T*)x, (const T*)Wg,          \
-             (const T*)Wu, (const T*)WdT, R, C, w.z, w.score, w.Q, w.sel, partial, partial_s, d, d_ff, n_R, n_C, k, \
-             rows_per_cblock, rows_per_rblock, n_slices, nb0, rb_base)
+             (const T*)Wu, (const T*)WdT, R, C, w.z, w.score, w.Q, w.sel, partial, d, d_ff, n_R, n_C, k,         \
+             rows_per_cblock, rows_per_rblock, nb0, rb_base, nbR)
 #define POP_STEP_PH(NVT, ID)   \
   if (nb0 == 0) {              \
     POP_STEP(NVT, ID, 0);      \
   } else if (phase == 1) {     \
     POP_STEP(NVT, ID, 1);      \
-  } else if (phase == 2) {     \
-    POP_STEP(NVT, ID, 2);      \
   } else {                     \
-    POP_STEP(NVT, ID, 3);      \
+    POP_STEP(NVT, ID, 2);      \
   }
 #define POP_STEP_ID(NVT)         \
   if (identity) {                \
@@ -824,14 +932,12 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
 #undef POP_STEP_PH
 #undef POP_STEP
   };
-  const int nb_sel = n_schunks * n_slices;
   if (aux != nullptr) {
     (void)hipEventRecord(fork, st);
     (void)hipStreamWaitEvent(aux, fork, 0);
     step(1, aux, nbC, 0, 0);
     if (n_C > 0 && k > 0 && !fuse_topk) launch_select(aux, w.score, n_C, C, k, w.Q, w.sel);
     step(2, aux, fuse_topk ? 1 : 0, 0, 0);
-    step(3, aux, nb_sel, 0, 0);
     step(1, st, 0, 0, nbR);
     (void)hipEventRecord(join, aux);
     (void)hipStreamWaitEvent(st, join, 0);
@@ -839,10 +945,17 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
     step(1, st, nbC, 0, nbR1);
     if (n_C > 0 && k > 0 && !fuse_topk) launch_select(st, w.score, n_C, C, k, w.Q, w.sel);
     step(2, st, fuse_topk ? 1 : 0, nbR1, nbR2);
-    step(3, st, nb_sel, nbR1 + nbR2, nbR3);
   }
-  POP_LAUNCH(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(1024), 0, st, (const float*)partial, nbR + n_schunks,
-             (int64_t)d, y, (unsigned int*)nullptr, 0);
+  const dim3 fgrid((d + kFinCols - 1) / kFinCols);
+  if (k > 0) {
+    POP_LAUNCH((k_pop_finish<T, true>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
+               (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, k, (const T*)WdT, d,
+               d_ff, y);
+  } else {
+    POP_LAUNCH((k_pop_finish<T, false>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
+               (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, 0, (const T*)WdT, d,
+               d_ff, y);
+  }
   return true;
 }
 

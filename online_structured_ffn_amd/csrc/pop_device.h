@@ -95,14 +95,16 @@ __device__ __forceinline__ uint32_t value_bits(float v) { return __float_as_uint
 //            passes scan only the bucket;
 //   passes   8-bit digits below the known bits until a bucket holds at most
 //            kSelBrute keys;
-//   rank     the last bucket is ranked by direct comparison (one thread per key)
-//            and the key of the target rank becomes the threshold.
+//   rank     the last bucket's keys are copied to LDS and ranked by direct
+//            comparison (one thread per key, the comparisons' LDS reads
+//            independent of each other), and the key of the target rank
+//            becomes the threshold.
 // Every loop is bounded; every LDS write index is checked against its array.
 // ---------------------------------------------------------------------------
 constexpr int kSelMaxN = 32768;
 constexpr int kSelBins1 = 2048;
 constexpr int kSelListCap = 2048;
-constexpr int kSelBrute = 128;
+constexpr int kSelBrute = 32;
 
 struct SelTarget {
   unsigned long long prefix;  // key bits at positions >= known (the whole key once state == 1)
@@ -117,7 +119,7 @@ struct SelShared {
   uint32_t vals[MAXN];
   unsigned int hist[kSelBins1];
   int list[2][kSelListCap];
-  int small[2][kSelBrute];
+  unsigned long long skey[2][kSelBrute];
   int list_n[2];   // -1: the bucket is scanned in the full array
   int small_n[2];
   SelTarget tgt[2];
@@ -387,16 +389,18 @@ __device__ void select_thresholds(int n, const int (&ranks)[NT], SelShared<NTH, 
       if (ln >= 0) {
         for (int j = tid; j < ln && j < kSelListCap; j += NTH) {
           const int i = sh.list[t][j];
-          if (sel_in_bucket(g, sel_key(sh.vals[i], i))) {
+          const unsigned long long key = sel_key(sh.vals[i], i);
+          if (sel_in_bucket(g, key)) {
             const int pos = atomicAdd(&sh.small_n[t], 1);
-            if (pos < kSelBrute) sh.small[t][pos] = i;
+            if (pos < kSelBrute) sh.skey[t][pos] = key;
           }
         }
       } else {
         for (int i = base; i < end; ++i) {
-          if (sel_in_bucket(g, sel_key(sh.vals[i], i))) {
+          const unsigned long long key = sel_key(sh.vals[i], i);
+          if (sel_in_bucket(g, key)) {
             const int pos = atomicAdd(&sh.small_n[t], 1);
-            if (pos < kSelBrute) sh.small[t][pos] = i;
+            if (pos < kSelBrute) sh.skey[t][pos] = key;
           }
         }
       }
@@ -416,13 +420,10 @@ __device__ void select_thresholds(int n, const int (&ranks)[NT], SelShared<NTH, 
       const SelTarget g = (t == 0) ? snap2[0] : snap2[NT - 1];  // no runtime-indexed register array
       const int m = (t == 0) ? msnap[0] : msnap[NT - 1];
       if (g.state != 0 || j >= m) continue;
-      const int ij = sh.small[t][j];
-      const unsigned long long kj = sel_key(sh.vals[ij], ij);
+      const unsigned long long kj = sh.skey[t][j];
       int r = 0;
-      for (int q = 0; q < m; ++q) {
-        const int iq = sh.small[t][q];
-        r += sel_key(sh.vals[iq], iq) < kj ? 1 : 0;
-      }
+#pragma unroll 8
+      for (int q = 0; q < kSelBrute; ++q) r += (q < m && sh.skey[t][q] < kj) ? 1 : 0;
       if (r == g.rank) {
         SelTarget h = g;
         h.prefix = kj;
@@ -480,25 +481,49 @@ __device__ __forceinline__ void block_exclusive_scan3(int (&v)[3], int (&total)[
 template <int NTH, int MAXN>
 __device__ void topk_block(const float* __restrict__ score, int n, int k, const int32_t* __restrict__ C,
                            int32_t* __restrict__ positions, int32_t* __restrict__ selected, SelShared<NTH, MAXN>& sh) {
+  // For up to 16 keys per thread, this thread's channels C[base, end) are
+  // fetched with the scores, so the final write waits on no further global
+  // load; wider launches read them at the end.
+  constexpr int EM = (MAXN + NTH - 1) / NTH;
+  constexpr int EP = EM <= 16 ? EM : 1;
+  const int E = (n + NTH - 1) / NTH;
+  const int base = threadIdx.x * E;
+  const int end = min(n, base + E);
+  int cv[EP];
+  if (EM <= 16 && selected != nullptr) {
+#pragma unroll
+    for (int j = 0; j < EP; ++j) cv[j] = C[max(0, min(base + j, n - 1))];
+  }
   sel_load(score, n, sh);
   const int ranks[1] = {n - k};
   select_thresholds(n, ranks, sh);
   const SelTarget t = sh.tgt[0];
-  const int E = (n + NTH - 1) / NTH;
-  const int base = threadIdx.x * E;
-  const int end = min(n, base + E);
   int pos[3] = {0, 0, 0};
   for (int i = base; i < end; ++i)
     if (!sel_less(t, sel_key(sh.vals[i], i))) ++pos[0];
   int tot[3];
   block_exclusive_scan3(pos, tot, sh);
-  for (int i = base; i < end; ++i) {
-    if (!sel_less(t, sel_key(sh.vals[i], i))) {
-      if (pos[0] < k) {  // an exact select never reaches the cap
-        positions[pos[0]] = i;
-        if (selected != nullptr) selected[pos[0]] = C[i];
+  if constexpr (EM <= 16) {
+#pragma unroll
+    for (int j = 0; j < EP; ++j) {
+      const int i = base + j;
+      if (i < end && !sel_less(t, sel_key(sh.vals[i], i))) {
+        if (pos[0] < k) {  // an exact select never reaches the cap
+          positions[pos[0]] = i;
+          if (selected != nullptr) selected[pos[0]] = cv[j];
+        }
+        ++pos[0];
       }
-      ++pos[0];
+    }
+  } else {
+    for (int i = base; i < end; ++i) {
+      if (!sel_less(t, sel_key(sh.vals[i], i))) {
+        if (pos[0] < k) {
+          positions[pos[0]] = i;
+          if (selected != nullptr) selected[pos[0]] = C[i];
+        }
+        ++pos[0];
+      }
     }
   }
 }

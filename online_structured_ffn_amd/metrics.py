@@ -67,29 +67,29 @@ def prefill_ffn_flops(n_tokens: int, d: int, d_ff: int) -> int:
 
 
 # Launch shape of the batch-1 step (mirrors the library's defaults: at most
-# 512 retained blocks of at least 8 rows, candidate blocks of 4 rows, selected
-# chunks of 8 rows, every retained block beside the top-k, none beside the
-# candidates or the selected rows).
-FUSED_RBLOCKS, FUSED_CROWS, SEL_ROWS, SPLIT_B, SPLIT_C = 512, 4, 8, 100, 0
+# 512 retained blocks of at least 8 rows, candidate blocks of 4 rows, every
+# retained block beside the top-k, none beside the candidates).
+FUSED_RBLOCKS, FUSED_CROWS, SPLIT_B = 512, 4, 100
 
 
 def fused_plan(n_R: int, n_C: int, k: int, d: int, e: int) -> dict:
-    """Blocks and algorithmic bytes of each launch of the batch-1 step."""
+    """Blocks and algorithmic bytes of each launch of the batch-1 step:
+    1 and 2 are the two k_pop_step launches, 3 is k_pop_finish (its bytes
+    count the retained partial sums it reads)."""
     nbR = min(-(-n_R // 8), FUSED_RBLOCKS) if n_R > 0 else 0
     rpb = -(-n_R // nbR) if nbR else 1
     if nbR:
         nbR = -(-n_R // rpb)
     fuse_topk = 0 < n_C <= 4096 and k > 0
-    n_schunks = -(-k // SEL_ROWS) if k > 0 else 0
     nbR2 = nbR * SPLIT_B // 100 if fuse_topk else 0
-    nbR3 = nbR * SPLIT_C // 100 if n_schunks else 0
-    nbR1 = nbR - nbR2 - nbR3
+    nbR1 = nbR - nbR2
     rows = lambda b0, nb: max(0, min(n_R, (b0 + nb) * rpb) - b0 * rpb)
-    r1, r2, r3 = rows(0, nbR1), rows(nbR1, nbR2), rows(nbR1 + nbR2, nbR3)
+    r1, r2 = rows(0, nbR1), rows(nbR1, nbR2)
     ret = lambda r: 3 * r * d * e + 8 * r + (d * e if r else 0)
     b1 = (candidate_scores_bytes(d, n_C, e) if n_C else 0) + ret(r1)
     b2 = (8 * n_C + 8 * k if fuse_topk else 0) + ret(r2)
-    b3 = (k * d * e + 12 * k) + ret(r3)
+    b3 = 4 * nbR * d + k * d * e + 12 * k + 4 * d
     nbC = -(-n_C // FUSED_CROWS) if n_C else 0
-    return {"launch": {1: nbC + nbR1 > 0, 2: (1 if fuse_topk else 0) + nbR2 > 0, 3: n_schunks + nbR3 > 0},
-            "bytes": {1: b1, 2: b2, 3: b3}, "retained_rows": {1: r1, 2: r2, 3: r3}}
+    return {"launch": {1: nbC + nbR1 > 0, 2: (1 if fuse_topk else 0) + nbR2 > 0, 3: True},
+            "bytes": {1: b1, 2: b2, 3: b3}, "retained_rows": {1: r1, 2: r2, 3: 0},
+            "partials": nbR}
