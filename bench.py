@@ -298,7 +298,8 @@ def main():
     # which kernels each call launches (the library's dispatch rules)
     vec = 8 if e == 2 else 4
     fused = B == 1 and d <= 4 * 256 * vec
-    labels_pre = ["k_colsq_partial", "k_sum_chunks(s2)", "k_importance", "k_partition"]
+    labels_pre = (["k_colsq_slices"] if n_tok <= 8192 else ["k_colsq_partial", "k_sum_chunks(s2)"]) + [
+        "k_importance", "k_partition"]
     n_pass = -(-n_tok // 4096)
     labels_ffn = (["k_prompt_gateup", "k_prompt_down"] if e == 2 else
                   ["k_prompt_gateup_f32", "k_prompt_down_f32"]) * n_pass
@@ -479,7 +480,8 @@ def main():
         "kernel_pass_coverage": round(coverage, 4),
         "kernels_us": {n: round(v, 3) for n, v in kus.items()},
         "kernels_us_default_events": {n: round(v, 3) for n, v in kus_fenced.items()},
-        "importance_gbps": round(imp_bytes / (kus["k_importance"] * 1e-6) / 1e9, 1),
+        "importance_gbps": (round(imp_bytes / (kus["k_importance"] * 1e-6) / 1e9, 1)
+                            if "k_importance" in kus else None),
         "cpu_baseline": None,
     }
 

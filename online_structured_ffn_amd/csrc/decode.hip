@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void k_gateup(const T* __restrict__ x, int B, 
 
 // ---------------------------------------------------------------- K5
 // The candidate top-k as its own one-workgroup launch (topk_block).
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 1024;
 
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ score, int n, int k,
                                                        const int32_t* __restrict__ C, int32_t* __restrict__ positions,

@@ -111,11 +111,11 @@ __global__ __launch_bounds__(256) void k_moe_gateup(const T* __restrict__ x, int
 }
 
 // ---------------------------------------------------------------- top-k
-template <int MAXN>
-__global__ __launch_bounds__(256) void k_moe_topk(const float* __restrict__ score, int n_C, int k,
+template <int MAXN, int NTH>
+__global__ __launch_bounds__(NTH) void k_moe_topk(const float* __restrict__ score, int n_C, int k,
                                                   const int32_t* __restrict__ C, const int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ Q, int32_t* __restrict__ S) {
-  __shared__ SelShared<256, MAXN> sh;
+  __shared__ SelShared<NTH, MAXN> sh;
   const int e = blockIdx.x;
   if (offsets[e + 1] == offsets[e]) return;
   topk_block(score + (int64_t)e * n_C, n_C, k, C + (int64_t)e * n_C, Q + (int64_t)e * k, S + (int64_t)e * k, sh);
@@ -330,10 +330,10 @@ static void launch_moe_decode(hipStream_t st, const void* x, int Tn, int d, cons
                (const T*)Wu, d_ff, R, n_R, C, n_C, (const int32_t*)w.offsets, (const int32_t*)w.tokens, w.z, w.score);
   if (n_C > 0 && k > 0) {
     if (n_C <= 4096)
-      POP_LAUNCH(k_moe_topk<4096>, dim3(E), dim3(256), 0, st, (const float*)w.score, n_C, k, C,
+      POP_LAUNCH((k_moe_topk<4096, 256>), dim3(E), dim3(256), 0, st, (const float*)w.score, n_C, k, C,
                  (const int32_t*)w.offsets, w.Q, S);
     else
-      POP_LAUNCH(k_moe_topk<kSelMaxN>, dim3(E), dim3(256), 0, st, (const float*)w.score, n_C, k, C,
+      POP_LAUNCH((k_moe_topk<kSelMaxN, 1024>), dim3(E), dim3(1024), 0, st, (const float*)w.score, n_C, k, C,
                  (const int32_t*)w.offsets, w.Q, S);
   }
   const int n_live = n_R + k;

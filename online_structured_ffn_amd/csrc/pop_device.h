@@ -78,383 +78,107 @@ __device__ __forceinline__ float silu(float a) {
 __device__ __forceinline__ uint32_t value_bits(float v) { return __float_as_uint(v) & 0x7fffffffu; }
 
 // ---------------------------------------------------------------------------
-// One-workgroup exact selection over n <= kSelMaxN keys.
+// One-workgroup exact selection over n <= MAXN keys.
 //
-// Element i (0 <= i < n) has the 64-bit key  (value_bits << 32) | (0xffffffff - i):
-// a larger value is more important and, on equal values, the lower index is
-// more important.  All keys are distinct, so "the key of ascending rank c" is
-// unique.  For each of NT targets (ascending ranks) the select finds the key T
-// of that rank; less(key) := key < T then holds for exactly c keys.
+// Element i (0 <= i < n) has the 64-bit key (value_bits << 32) | (0xffffffff - i):
+// a larger value is more important and, on equal values, the lower index is.
+// All keys are distinct.  For each of NT <= 2 targets (ascending ranks c) the
+// select finds the value v of the key of rank c, the number m of elements
+// whose value is v, and q, how many of those lie below rank c (they are the q
+// equal elements with the largest indices).  "Below target t" then reads
+//   value < v,  or  value == v and fewer than q equal elements have a larger index,
+// which holds for exactly c elements.
 //
-// The value bits sit in LDS (sh.vals).  Thread t owns the consecutive elements
-// [t*E, min(n, (t+1)*E)), E = ceil(n / NTH).
-//   pass 1   an 11-bit digit taken just below the common leading bits of all n
-//            keys (so the digit always splits the set), one 2048-bin histogram
-//            and a block scan locate each target's bucket;
-//   compact  a bucket of at most kSelListCap keys is copied to a list, so later
-//            passes scan only the bucket;
-//   passes   8-bit digits below the known bits until a bucket holds at most
-//            kSelBrute keys;
-//   rank     the last bucket's keys are copied to LDS and ranked by direct
-//            comparison (one thread per key, the comparisons' LDS reads
-//            independent of each other), and the key of the target rank
-//            becomes the threshold.
-// Every loop is bounded; every LDS write index is checked against its array.
+// Thread t holds the values of its elements [t*E, min(n, (t+1)*E)),
+// E = ceil(n / NTH), in registers.  The value bits are resolved from the top,
+// below the leading bits that all n values share (one OR/AND reduction), in at
+// most three radix passes of 12, 11 and up to 8 bits: each pass counts digits
+// into an LDS histogram with atomics, and one block scan over the bins (DPP
+// within a wave, LDS across waves) finds each target's bin.  Every loop is
+// bounded and every LDS index lies inside its array.
 // ---------------------------------------------------------------------------
 constexpr int kSelMaxN = 32768;
-constexpr int kSelBins1 = 2048;
-constexpr int kSelListCap = 2048;
-constexpr int kSelBrute = 32;
+constexpr int kSelBins = 4096;
+// LDS slot of histogram bin g: one pad word per 32 bins, so that the threads
+// of a wave reading their own runs of consecutive bins hit distinct banks.
+__host__ __device__ constexpr int sel_slot(int g) { return g + (g >> 5); }
+constexpr int kSelSlots = kSelBins + kSelBins / 32;
 
 struct SelTarget {
-  unsigned long long prefix;  // key bits at positions >= known (the whole key once state == 1)
-  int known;                  // lowest known bit position (0 once state == 1)
-  int rank;                   // remaining rank inside the current bucket
-  int count;                  // keys in the current bucket
-  int state;                  // 0 searching, 1 found, 2 rank >= n (every key is below)
+  uint32_t prefix;  // value bits resolved so far (the whole value v once shift == 0)
+  int shift;        // value bits below shift are still open
+  int rank;         // rank still to find inside the current bucket (q once shift == 0)
+  int count;        // elements in the current bucket (m once shift == 0)
+  int beyond;       // rank >= n: every element is below
 };
 
 template <int NTH, int MAXN = kSelMaxN>
 struct SelShared {
-  uint32_t vals[MAXN];
-  unsigned int hist[kSelBins1];
-  int list[2][kSelListCap];
-  unsigned long long skey[2][kSelBrute];
-  int list_n[2];   // -1: the bucket is scanned in the full array
-  int small_n[2];
+  static constexpr int kPerThread = (MAXN + NTH - 1) / NTH;
+  unsigned int hA[kSelSlots];
+  unsigned int hB[kSelSlots];
   SelTarget tgt[2];
-  uint32_t red[NTH / 64][4];
+  uint32_t red[NTH / 64][2];
   int scan[NTH / 64][3];
 };
 
-__device__ __forceinline__ unsigned long long sel_key(uint32_t vb, int i) {
-  return ((unsigned long long)vb << 32) | (unsigned long long)(0xffffffffu - (uint32_t)i);
+// DPP move within a wave; lanes whose source is outside the row, and rows
+// outside ROW_MASK, read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
 }
 
-__device__ __forceinline__ bool sel_less(const SelTarget& t, unsigned long long key) {
-  if (t.state == 2) return true;
-  return (key >> t.known) < (t.prefix >> t.known);
+// Inclusive prefix sum over the 64 lanes of a wave (no LDS).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_i<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_i<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_i<0x118, 0xf>(v);  // row_shr:8   (prefix sums within each row of 16)
+  v += dpp_i<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_i<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
 }
 
-__device__ __forceinline__ bool sel_in_bucket(const SelTarget& t, unsigned long long key) {
-  return t.known >= 64 || ((key ^ t.prefix) >> t.known) == 0ull;
-}
-
-// Loads value_bits of src[0..n) into sh.vals, then a barrier.
-template <int NTH, int MAXN>
-__device__ __forceinline__ void sel_load(const float* __restrict__ src, int n, SelShared<NTH, MAXN>& sh) {
-  // 8 loads in flight per thread before any LDS store.
-  for (int i0 = threadIdx.x; i0 < n; i0 += 8 * NTH) {
-    float v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (i0 + j * NTH < n) ? src[i0 + j * NTH] : 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (i0 + j * NTH < n) sh.vals[i0 + j * NTH] = value_bits(v[j]);
-  }
-  __syncthreads();
+// Bitwise OR over the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= (uint32_t)dpp_i<0xb1, 0xf>((int)v);   // quad_perm [1,0,3,2]
+  v |= (uint32_t)dpp_i<0x4e, 0xf>((int)v);   // quad_perm [2,3,0,1]
+  v |= (uint32_t)dpp_i<0x141, 0xf>((int)v);  // row_half_mirror
+  v |= (uint32_t)dpp_i<0x140, 0xf>((int)v);  // row_mirror: every lane holds its row's OR
+  return (uint32_t)(__builtin_amdgcn_readlane((int)v, 0) | __builtin_amdgcn_readlane((int)v, 16) |
+                    __builtin_amdgcn_readlane((int)v, 32) | __builtin_amdgcn_readlane((int)v, 48));
 }
 
 // Block-wide exclusive scan of one int per thread; returns the exclusive
-// prefix and (through total) the block sum.  Contains two barriers.
+// prefix and (through total) the block sum.  One barrier; sh.scan may be
+// written again only after a later barrier.
 template <int NTH, int MAXN>
 __device__ __forceinline__ int block_excl_scan1(int v, int& total, SelShared<NTH, MAXN>& sh) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o);
-    if (lane >= o) incl += u;
-  }
+  const int incl = wave_incl_scan(v);
   if (lane == 63) sh.scan[wave][0] = incl;
   __syncthreads();
   int off = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NTH / 64; ++w) {
     const int x = sh.scan[w][0];
-    off += (w < wave) ? x : 0;
+    off += w < wave ? x : 0;
     tot += x;
   }
   total = tot;
-  __syncthreads();
   return off + incl - v;
 }
 
-template <int NTH, int NT, int MAXN>
-__device__ void select_thresholds(int n, const int (&ranks)[NT], SelShared<NTH, MAXN>& sh) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int E = (n + NTH - 1) / NTH;
-  const int base = tid * E;
-  const int end = min(n, base + E);
-
-  // ---- A. common leading bits of all keys
-  uint32_t hor = 0u, hand = 0xffffffffu, lor = 0u, land = 0xffffffffu;
-  for (int i = base; i < end; ++i) {
-    const uint32_t v = sh.vals[i];
-    const uint32_t lo = 0xffffffffu - (uint32_t)i;
-    hor |= v;
-    hand &= v;
-    lor |= lo;
-    land &= lo;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    hor |= __shfl_xor(hor, o);
-    hand &= __shfl_xor(hand, o);
-    lor |= __shfl_xor(lor, o);
-    land &= __shfl_xor(land, o);
-  }
-  if (lane == 0) {
-    sh.red[wave][0] = hor;
-    sh.red[wave][1] = hand;
-    sh.red[wave][2] = lor;
-    sh.red[wave][3] = land;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t a0 = 0u, b0 = 0xffffffffu, a1 = 0u, b1 = 0xffffffffu;
-    for (int w = 0; w < NTH / 64; ++w) {
-      a0 |= sh.red[w][0];
-      b0 &= sh.red[w][1];
-      a1 |= sh.red[w][2];
-      b1 &= sh.red[w][3];
-    }
-    const unsigned long long kor = ((unsigned long long)a0 << 32) | a1;
-    const unsigned long long kand = ((unsigned long long)b0 << 32) | b1;
-    const unsigned long long diff = kor ^ kand;
-    const int known = diff ? 64 - __clzll(diff) : 0;  // bits >= known are common to all keys
-    const unsigned long long prefix = known >= 64 ? 0ull : (kand >> known) << known;
-    for (int t = 0; t < NT; ++t) {
-      SelTarget g;
-      g.prefix = prefix;
-      g.known = known;
-      g.rank = ranks[t];
-      g.count = n;
-      g.state = ranks[t] >= n ? 2 : (n == 1 ? 1 : 0);
-      if (g.state == 1) {  // a single key: it is the threshold
-        g.prefix = kand;
-        g.known = 0;
-      }
-      sh.tgt[t] = g;
-      sh.list_n[t] = -1;
-    }
-  }
-  __syncthreads();
-
-  // ---- B. first pass: 11-bit digit just below the common bits
-  bool any = false;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) any |= sh.tgt[t].state == 0;
-  if (any) {
-    const int known0 = sh.tgt[0].known;  // every target starts from the same common bits
-    const int s1 = known0 > 11 ? known0 - 11 : 0;
-    const unsigned long long mask1 = (1ull << (known0 - s1)) - 1ull;
-    for (int i = tid; i < kSelBins1; i += NTH) sh.hist[i] = 0u;
-    __syncthreads();
-    for (int i = base; i < end; ++i)
-      atomicAdd(&sh.hist[(int)((sel_key(sh.vals[i], i) >> s1) & mask1)], 1u);
-    __syncthreads();
-    constexpr int BPT = kSelBins1 / NTH;  // bins per thread
-    unsigned int c[BPT];
-    int sum = 0;
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      c[j] = sh.hist[tid * BPT + j];
-      sum += (int)c[j];
-    }
-    // Snapshot the targets before the scan: its barriers order every read
-    // here before the single write per target below.
-    SelTarget snap[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) snap[t] = sh.tgt[t];
-    int total;
-    const int before0 = block_excl_scan1(sum, total, sh);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const SelTarget g = snap[t];
-      if (g.state != 0) continue;
-      int before = before0;
-#pragma unroll
-      for (int j = 0; j < BPT; ++j) {
-        if (c[j] > 0u && before <= g.rank && g.rank < before + (int)c[j]) {
-          SelTarget h = g;
-          h.prefix = g.prefix | ((unsigned long long)(tid * BPT + j) << s1);
-          h.known = s1;
-          h.rank = g.rank - before;
-          h.count = (int)c[j];
-          sh.tgt[t] = h;
-        }
-        before += (int)c[j];
-      }
-    }
-    __syncthreads();
-    // compact small-enough buckets into lists
-    if (tid < NT) sh.list_n[tid] = (sh.tgt[tid].state == 0 && sh.tgt[tid].count <= kSelListCap) ? 0 : -1;
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const SelTarget g = sh.tgt[t];
-      if (g.state != 0 || sh.list_n[t] < 0) continue;
-      for (int i = base; i < end; ++i) {
-        if (sel_in_bucket(g, sel_key(sh.vals[i], i))) {
-          const int pos = atomicAdd(&sh.list_n[t], 1);
-          if (pos < kSelListCap) sh.list[t][pos] = i;
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- C. 8-bit passes until every bucket is small, then rank directly
-  for (int pass = 0; pass < 16; ++pass) {
-    bool big = false, active = false;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      active |= sh.tgt[t].state == 0;
-      big |= sh.tgt[t].state == 0 && sh.tgt[t].count > kSelBrute;
-    }
-    if (!active) break;
-    if (big) {
-      for (int i = tid; i < NT * 256; i += NTH) sh.hist[i] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const SelTarget g = sh.tgt[t];
-        if (g.state != 0 || g.count <= kSelBrute) continue;
-        const int s = g.known > 8 ? g.known - 8 : 0;
-        const unsigned long long mask = (1ull << (g.known - s)) - 1ull;
-        const int ln = sh.list_n[t];
-        if (ln >= 0) {
-          for (int j = tid; j < ln && j < kSelListCap; j += NTH) {
-            const int i = sh.list[t][j];
-            const unsigned long long key = sel_key(sh.vals[i], i);
-            if (sel_in_bucket(g, key)) atomicAdd(&sh.hist[t * 256 + (int)((key >> s) & mask)], 1u);
-          }
-        } else {
-          for (int i = base; i < end; ++i) {
-            const unsigned long long key = sel_key(sh.vals[i], i);
-            if (sel_in_bucket(g, key)) atomicAdd(&sh.hist[t * 256 + (int)((key >> s) & mask)], 1u);
-          }
-        }
-      }
-      __syncthreads();
-      if (wave < NT) {
-        const int t = wave;
-        const SelTarget g = sh.tgt[t];
-        if (g.state == 0 && g.count > kSelBrute) {
-          const int s = g.known > 8 ? g.known - 8 : 0;
-          unsigned int cc[4];
-          unsigned int sum = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            cc[j] = sh.hist[t * 256 + lane * 4 + j];
-            sum += cc[j];
-          }
-          unsigned int incl = sum;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const unsigned int v = __shfl_up(incl, o);
-            if (lane >= o) incl += v;
-          }
-          unsigned int before = incl - sum;
-          const unsigned int rk = (unsigned int)g.rank;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (cc[j] > 0u && before <= rk && rk < before + cc[j]) {
-              SelTarget h = g;
-              h.prefix = g.prefix | ((unsigned long long)(lane * 4 + j) << s);
-              h.known = s;
-              h.rank = (int)(rk - before);
-              h.count = (int)cc[j];
-              sh.tgt[t] = h;
-            }
-            before += cc[j];
-          }
-        }
-      }
-      __syncthreads();
-      continue;
-    }
-    // every active bucket holds at most kSelBrute keys: gather and rank them
-    if (tid < NT) sh.small_n[tid] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const SelTarget g = sh.tgt[t];
-      if (g.state != 0) continue;
-      const int ln = sh.list_n[t];
-      if (ln >= 0) {
-        for (int j = tid; j < ln && j < kSelListCap; j += NTH) {
-          const int i = sh.list[t][j];
-          const unsigned long long key = sel_key(sh.vals[i], i);
-          if (sel_in_bucket(g, key)) {
-            const int pos = atomicAdd(&sh.small_n[t], 1);
-            if (pos < kSelBrute) sh.skey[t][pos] = key;
-          }
-        }
-      } else {
-        for (int i = base; i < end; ++i) {
-          const unsigned long long key = sel_key(sh.vals[i], i);
-          if (sel_in_bucket(g, key)) {
-            const int pos = atomicAdd(&sh.small_n[t], 1);
-            if (pos < kSelBrute) sh.skey[t][pos] = key;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    SelTarget snap2[NT];
-    int msnap[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      snap2[t] = sh.tgt[t];
-      msnap[t] = min(sh.small_n[t], kSelBrute);
-    }
-    __syncthreads();  // every thread holds its snapshot before any target is rewritten
-    for (int slot = tid; slot < NT * kSelBrute; slot += NTH) {
-      const int t = slot / kSelBrute;
-      const int j = slot % kSelBrute;
-      const SelTarget g = (t == 0) ? snap2[0] : snap2[NT - 1];  // no runtime-indexed register array
-      const int m = (t == 0) ? msnap[0] : msnap[NT - 1];
-      if (g.state != 0 || j >= m) continue;
-      const unsigned long long kj = sh.skey[t][j];
-      int r = 0;
-#pragma unroll 8
-      for (int q = 0; q < kSelBrute; ++q) r += (q < m && sh.skey[t][q] < kj) ? 1 : 0;
-      if (r == g.rank) {
-        SelTarget h = g;
-        h.prefix = kj;
-        h.known = 0;
-        h.rank = 0;
-        h.count = 1;
-        h.state = 1;
-        sh.tgt[t] = h;
-      }
-    }
-    __syncthreads();
-    break;
-  }
-}
-
-// Block-wide exclusive scan of three per-thread counters.
+// Block-wide exclusive scan of three per-thread counters (two barriers).
 template <int NTH, int MAXN>
 __device__ __forceinline__ void block_exclusive_scan3(int (&v)[3], int (&total)[3], SelShared<NTH, MAXN>& sh) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   int incl[3];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    incl[j] = v[j];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(incl[j], o);
-      if (lane >= o) incl[j] += u;
-    }
-  }
+  for (int j = 0; j < 3; ++j) incl[j] = wave_incl_scan(v[j]);
   if (lane == 63) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) sh.scan[wave][j] = incl[j];
@@ -463,64 +187,261 @@ __device__ __forceinline__ void block_exclusive_scan3(int (&v)[3], int (&total)[
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     int off = 0, tot = 0;
+#pragma unroll
     for (int w = 0; w < NTH / 64; ++w) {
       const int x = sh.scan[w][j];
-      if (w < wave) off += x;
+      off += w < wave ? x : 0;
       tot += x;
     }
-    const int excl = off + incl[j] - v[j];
-    v[j] = excl;
+    v[j] = off + incl[j] - v[j];
     total[j] = tot;
   }
   __syncthreads();
 }
 
+// Loads value_bits(src[base + j]) for j < E into registers (n >= 1).
+template <int EM>
+__device__ __forceinline__ void sel_load_regs(const float* __restrict__ src, int n, int base, int E,
+                                              uint32_t (&v)[EM]) {
+#pragma unroll
+  for (int j = 0; j < EM; ++j) v[j] = j < E ? value_bits(src[min(base + j, n - 1)]) : 0u;
+}
+
+// The select itself (see above).  v holds this thread's values; on return
+// every thread's t[] holds the resolved targets (v, q, m in prefix, rank,
+// count).  Ends with a barrier.
+template <int NTH, int NT, int EM, int MAXN>
+__device__ void select_targets(const uint32_t (&v)[EM], int n, int base, int E, const int (&ranks)[NT],
+                               SelShared<NTH, MAXN>& sh, SelTarget (&t)[NT]) {
+  static_assert(NT >= 1 && NT <= 2, "one or two targets");
+  static_assert(kSelBins % NTH == 0 && kSelBins / NTH <= 16, "bins per thread");
+  constexpr int BPT = kSelBins / NTH;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int cnt = max(0, min(E, n - base));  // this thread's elements
+  for (int i = tid; i < kSelSlots; i += NTH) {
+    sh.hA[i] = 0u;
+    sh.hB[i] = 0u;
+  }
+  // ---- leading bits shared by all values
+  uint32_t o = 0u, a = 0xffffffffu;
+#pragma unroll
+  for (int j = 0; j < EM; ++j) {
+    if (j >= E) break;  // block-uniform
+    o |= j < cnt ? v[j] : 0u;
+    a &= j < cnt ? v[j] : 0xffffffffu;
+  }
+  o = wave_or(o);
+  a = ~wave_or(~a);
+  if (lane == 0) {
+    sh.red[wave][0] = o;
+    sh.red[wave][1] = a;
+  }
+  __syncthreads();  // also orders the histogram clears before the first pass
+  uint32_t O = 0u, A = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < NTH / 64; ++w) {
+    O |= sh.red[w][0];
+    A &= sh.red[w][1];
+  }
+  const uint32_t diff = O ^ A;                      // values are 31-bit: diff < 2^31
+  const int top = diff ? 32 - __clz((int)diff) : 0;  // bits >= top are common
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    t[i].prefix = top >= 31 ? 0u : (A >> top) << top;
+    t[i].shift = top;
+    t[i].rank = ranks[i];
+    t[i].count = n;
+    t[i].beyond = ranks[i] >= n ? 1 : 0;
+  }
+  // ---- radix passes
+  const int widths[3] = {12, 11, 8};
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    bool active = false;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) active |= !t[i].beyond && t[i].shift > 0;
+    if (!active) break;  // block-uniform
+    const int shift = t[0].beyond ? t[NT - 1].shift : t[0].shift;  // the same for every active target
+    const int wdt = min(widths[p], shift);
+    const int s_new = shift - wdt;
+    const uint32_t mask = (1u << wdt) - 1u;
+    unsigned int* h = p == 1 ? sh.hB : sh.hA;
+    const int per_t = p == 0 ? kSelBins : (p == 1 ? 2048 : 256);  // bins per target's section
+    if (p == 1) {
+      // pass 3 counts into hA again: clear it (pass 1's reads of hA ended at
+      // the previous barrier; pass 3 starts two barriers later)
+      for (int i = tid; i < kSelSlots; i += NTH) sh.hA[i] = 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < EM; ++j) {
+      if (j >= E) break;  // block-uniform
+      if (j < cnt) {
+        const uint32_t val = v[j];
+        const int dg = (int)((val >> s_new) & mask);
+        if (p == 0) {
+          atomicAdd(&h[sel_slot(dg)], 1u);
+        } else {
+#pragma unroll
+          for (int i = 0; i < NT; ++i)
+            if (!t[i].beyond && t[i].shift > 0 && (val >> shift) == (t[i].prefix >> shift))
+              atomicAdd(&h[sel_slot(i * per_t + dg)], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    // this thread's bins [tid * BPT, tid * BPT + BPT)
+    unsigned int hb[BPT];
+    int local = 0;
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+      hb[b] = h[sel_slot(tid * BPT + b)];
+      local += (int)hb[b];
+    }
+    int total;
+    const int excl = block_excl_scan1(local, total, sh);
+    const int sec0 = (p > 0 && !t[0].beyond) ? t[0].count : 0;  // elements counted in target 0's section
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      if (t[i].beyond || t[i].shift == 0) continue;
+      const int r = t[i].rank + (i == 1 && p > 0 ? sec0 : 0);
+      if (r >= excl && r < excl + local) {
+        int cum = excl;
+#pragma unroll
+        for (int b = 0; b < BPT; ++b) {
+          const int c = (int)hb[b];
+          if (r >= cum && r < cum + c) {
+            const int g = tid * BPT + b - (p > 0 ? i * per_t : 0);  // bin inside the target's section
+            SelTarget u = t[i];
+            u.prefix = t[i].prefix | ((uint32_t)g << s_new);
+            u.shift = s_new;
+            u.rank = r - cum;
+            u.count = c;
+            sh.tgt[i] = u;
+          }
+          cum += c;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      if (!t[i].beyond && t[i].shift > 0) t[i] = sh.tgt[i];
+  }
+  __syncthreads();  // sh.tgt and the histograms may be reused after this
+}
+
+// Whether an element of value val with eq_after equal elements at larger
+// indices lies below the resolved target t.
+__device__ __forceinline__ bool sel_below(const SelTarget& t, uint32_t val, int eq_after) {
+  if (t.beyond) return true;
+  return val < t.prefix || (val == t.prefix && eq_after < t.rank);
+}
+
+// Counts of equal-valued elements before this thread's range, for targets
+// whose equal group is split by the cut (0 < q < m); others get 0.  The scan
+// runs only when some target needs it (block-uniform).
+template <int NTH, int NT, int EM, int MAXN>
+__device__ __forceinline__ void sel_eq_before(const uint32_t (&v)[EM], int E, int cnt, const SelTarget (&t)[NT],
+                                              SelShared<NTH, MAXN>& sh, int (&eqb)[2]) {
+  eqb[0] = eqb[1] = 0;
+  bool need = false;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) need |= !t[i].beyond && t[i].rank > 0 && t[i].rank < t[i].count;
+  if (!need) return;
+  int c[3] = {0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < EM; ++j) {
+    if (j >= E) break;  // block-uniform
+#pragma unroll
+    for (int i = 0; i < NT; ++i) c[i] += (j < cnt && v[j] == t[i].prefix) ? 1 : 0;
+  }
+  int tot[3];
+  block_exclusive_scan3(c, tot, sh);
+  eqb[0] = c[0];
+  eqb[1] = c[1];
+}
+
 // S = the k most important of n candidates (score descending, position
 // ascending on ties), written in ascending order as positions into C and, when
-// `selected` is not NULL, as channels C[position].  One workgroup.
+// `selected` is not NULL, as channels C[position].  One workgroup; n <= MAXN.
 template <int NTH, int MAXN>
 __device__ void topk_block(const float* __restrict__ score, int n, int k, const int32_t* __restrict__ C,
                            int32_t* __restrict__ positions, int32_t* __restrict__ selected, SelShared<NTH, MAXN>& sh) {
-  // For up to 16 keys per thread, this thread's channels C[base, end) are
-  // fetched with the scores, so the final write waits on no further global
-  // load; wider launches read them at the end.
-  constexpr int EM = (MAXN + NTH - 1) / NTH;
-  constexpr int EP = EM <= 16 ? EM : 1;
+  constexpr int EM = SelShared<NTH, MAXN>::kPerThread;
+  if (n <= 0 || k <= 0) return;
+  k = min(k, n);
   const int E = (n + NTH - 1) / NTH;
   const int base = threadIdx.x * E;
-  const int end = min(n, base + E);
-  int cv[EP];
-  if (EM <= 16 && selected != nullptr) {
+  const int cnt = max(0, min(E, n - base));
+  // This thread's channels come with its scores, so the final write waits on
+  // no further global load.  When the keys fit the histogram buffers, scores
+  // and channels are read coalesced (element tid + j * NTH) and handed to
+  // their owners through LDS: a block sharing its CU with streaming work then
+  // waits on few memory requests.
+  int cv[EM];
+  uint32_t v[EM];
+  if constexpr (sel_slot(MAXN - 1) < kSelSlots) {
+    uint32_t a[EM];
+    int c[EM];
 #pragma unroll
-    for (int j = 0; j < EP; ++j) cv[j] = C[max(0, min(base + j, n - 1))];
-  }
-  sel_load(score, n, sh);
-  const int ranks[1] = {n - k};
-  select_thresholds(n, ranks, sh);
-  const SelTarget t = sh.tgt[0];
-  int pos[3] = {0, 0, 0};
-  for (int i = base; i < end; ++i)
-    if (!sel_less(t, sel_key(sh.vals[i], i))) ++pos[0];
-  int tot[3];
-  block_exclusive_scan3(pos, tot, sh);
-  if constexpr (EM <= 16) {
+    for (int j = 0; j < EM; ++j) {
+      const int i = min((int)threadIdx.x + j * NTH, n - 1);
+      a[j] = value_bits(score[i]);
+      c[j] = selected != nullptr ? C[i] : 0;
+    }
 #pragma unroll
-    for (int j = 0; j < EP; ++j) {
-      const int i = base + j;
-      if (i < end && !sel_less(t, sel_key(sh.vals[i], i))) {
-        if (pos[0] < k) {  // an exact select never reaches the cap
-          positions[pos[0]] = i;
-          if (selected != nullptr) selected[pos[0]] = cv[j];
-        }
-        ++pos[0];
+    for (int j = 0; j < EM; ++j) {
+      const int i = (int)threadIdx.x + j * NTH;
+      if (i < n) {
+        sh.hA[sel_slot(i)] = a[j];
+        sh.hB[sel_slot(i)] = (unsigned int)c[j];
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EM; ++j) {
+      const int i = min(base + j, n - 1);
+      v[j] = sh.hA[sel_slot(i)];
+      cv[j] = (int)sh.hB[sel_slot(i)];
+    }
+    __syncthreads();  // the select clears the buffers next
   } else {
-    for (int i = base; i < end; ++i) {
-      if (!sel_less(t, sel_key(sh.vals[i], i))) {
-        if (pos[0] < k) {
-          positions[pos[0]] = i;
-          if (selected != nullptr) selected[pos[0]] = C[i];
+    if (selected != nullptr) {
+#pragma unroll
+      for (int j = 0; j < EM; ++j) cv[j] = j < E ? C[min(base + j, n - 1)] : 0;
+    }
+    sel_load_regs(score, n, base, E, v);
+  }
+  const int ranks[1] = {n - k};
+  SelTarget t[1];
+  select_targets<NTH, 1, EM, MAXN>(v, n, base, E, ranks, sh, t);
+  int eqb[2];
+  sel_eq_before<NTH, 1, EM, MAXN>(v, E, cnt, t, sh, eqb);
+  // selected = not below the cut
+  int pos[3] = {0, 0, 0};
+  {
+    int eq = eqb[0];
+#pragma unroll
+    for (int j = 0; j < EM; ++j) {
+      if (j >= E) break;  // block-uniform
+      eq += v[j] == t[0].prefix ? 1 : 0;
+      pos[0] += (j < cnt && !sel_below(t[0], v[j], t[0].count - eq)) ? 1 : 0;
+    }
+  }
+  int tot[3];
+  block_exclusive_scan3(pos, tot, sh);
+  int eq = eqb[0];
+#pragma unroll
+  for (int j = 0; j < EM; ++j) {
+    if (j >= E) break;  // block-uniform
+    if (j < cnt) {
+      eq += v[j] == t[0].prefix ? 1 : 0;
+      if (!sel_below(t[0], v[j], t[0].count - eq)) {
+        if (pos[0] < k) {  // an exact select never reaches the cap
+          positions[pos[0]] = base + j;
+          if (selected != nullptr) selected[pos[0]] = cv[j];
         }
         ++pos[0];
       }

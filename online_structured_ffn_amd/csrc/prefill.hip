@@ -1,7 +1,8 @@
 // Prefill three-region partition (POP notes, "Key design 1").
 //
 //   K1  column sum of squares  s2[k] = sum_n X[n,k]^2         (HBM-bound on X)
-//   K1r fixed-order reduction of the K1 partial sums
+//       one pass per column slice for prompts of up to 8192 tokens, else
+//       partial sums over row chunks and (K1r) their fixed-order reduction
 //   K2  importance  I[i] = sqrt(sum_k W_up[i,k]^2 * s2[k])    (HBM-bound on W_up)
 //   K3  one-workgroup radix select of the keys at ranks c_low and c_high and an
 //       order-preserving compaction into P, C, R            (latency-bound)
@@ -55,6 +56,72 @@ __global__ __launch_bounds__(64) void k_colsq_partial(const T* __restrict__ X, i
   for (int v = 0; v < V; ++v) out[v] = acc[v];
 }
 
+// ---------------------------------------------------------------- K1, one pass
+// For prompts of up to kCsOnePassMax tokens: block b owns kCsCols columns and
+// reads them from every row, so s2 comes out of one launch with no partial
+// sums.  1024 threads = 16 waves; a row's kCsCols columns are kCsCols / V
+// lanes x 16 bytes, so one wave instruction covers 64 / (kCsCols / V) rows.
+// Per-lane sums are reduced across lanes (shuffles), then across waves in wave
+// order (LDS): the same bits on every run.  Blocks sharing a 128-byte line of
+// X are dealt to one XCD (blocks go to the eight XCDs round-robin).
+constexpr int kCsCols = 16;
+constexpr int kCsThreads = 1024;
+constexpr int64_t kCsOnePassMax = 8192;
+
+template <typename T>
+__global__ __launch_bounds__(kCsThreads) void k_colsq_slices(const T* __restrict__ X, int64_t n_tokens, int d,
+                                                             float* __restrict__ s2) {
+  constexpr int V = Vec<T>::N;
+  constexpr int LR = kCsCols / V;                       // lanes per row
+  constexpr int RPW = 64 / LR;                          // rows per wave instruction
+  constexpr int RPB = RPW * (kCsThreads / 64);          // rows per block instruction
+  constexpr int NB = 4;                                 // row loads in flight per lane
+  constexpr int SP = 128 / (kCsCols * (int)sizeof(T));  // slices per 128-byte line
+  constexpr int G = 8 * SP;
+  __shared__ float red[kCsThreads / 64][kCsCols];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int b = blockIdx.x;
+  if (SP > 1 && (b | (G - 1)) < (int)gridDim.x) b = (b / G * 8 + b % 8) * SP + (b / 8) % SP;
+  const int c0 = b * kCsCols;
+  const int col = min(c0 + (lane % LR) * V, d - V);
+  const int rl = wave * RPW + lane / LR;
+  float acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  for (int64_t r0 = 0; r0 < n_tokens; r0 += NB * RPB) {
+    u32x4 q[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int64_t r = min(r0 + u * RPB + rl, n_tokens - 1);
+      q[u] = ld16_stream(X + r * d + col);
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const bool on = r0 + u * RPB + rl < n_tokens;
+      float f[V];
+      unpack(q[u], f, T{});
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] += on ? f[v] * f[v] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int o = LR; o < 64; o <<= 1)
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] += __shfl_xor(acc[v], o);
+  if (lane < LR) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) red[wave][lane * V + v] = acc[v];
+  }
+  __syncthreads();
+  if (threadIdx.x < kCsCols && c0 + (int)threadIdx.x < d) {
+    float t = red[0][threadIdx.x];
+#pragma unroll
+    for (int w = 1; w < kCsThreads / 64; ++w) t += red[w][threadIdx.x];
+    s2[c0 + threadIdx.x] = t;
+  }
+}
+
 // ---------------------------------------------------------------- K1, MoE
 // The column sums of squares of every expert in one pass over X: row r adds
 // its squares to the accumulators of its two experts ex[2r], ex[2r + 1].  The
@@ -97,51 +164,96 @@ __global__ __launch_bounds__(64) void k_moe_colsq_partial(const T* __restrict__ 
 }
 
 // ---------------------------------------------------------------- K2
-// Block: 256 threads = 4 waves, one W_up row per wave at a time.  s2 sits in
-// LDS; each lane reads 16-byte vectors of its row, 4 in flight.
+// Block: 256 threads = 4 waves; wave w of block b takes rows b*4 + w,
+// b*4 + w + 4*gridDim.x, ...  A row is read in chunks of kImpChunk columns
+// (kImpLoads 16-byte vectors per lane, all issued together), and the next
+// chunk's loads are in flight while the current one is reduced (double
+// buffer over the wave's (row, chunk) items).  s2 sits in LDS, zero-padded to
+// whole chunks, so the loads need no column mask (columns past d are clamped
+// to the row's last vector and meet s2 = 0).  The order of the products in
+// the sum is the same as for s2 in plain column order.
 // blockIdx.y selects an expert (MoE): its W_up, s2 and I follow the previous
 // expert's contiguously; gridDim.y = 1 otherwise.
+constexpr int kImpLoads = 8;
+#ifndef POP_IMP_BLOCKS
+#define POP_IMP_BLOCKS 512
+#endif
+constexpr int kImpBlocks = POP_IMP_BLOCKS;
+
+template <typename T>
+struct ImpBuf {
+  u32x4 q[kImpLoads];
+};
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_importance(const T* __restrict__ W, int d_ff, int d,
                                                     const float* __restrict__ s2, float* __restrict__ I) {
   constexpr int V = Vec<T>::N;
+  constexpr int CH = kImpLoads * 64 * V;  // columns per chunk
   extern __shared__ float s2_lds[];
   W += (int64_t)blockIdx.y * d_ff * d;
   s2 += (int64_t)blockIdx.y * d;
   I += (int64_t)blockIdx.y * d_ff;
-  for (int k = threadIdx.x; k < d; k += 256) s2_lds[k] = s2[k];
+  const int n_ch = (d + CH - 1) / CH;
+  // LDS layout: within each run of 64 * V columns (one load instruction of a
+  // wave), lane l's V values are stored as V / 4 float4 groups at
+  // (group * 64 + l) * 4, so that every LDS read below is a 16-byte read with
+  // consecutive lanes 16 bytes apart (no bank conflicts).
+  for (int k = threadIdx.x; k < n_ch * CH; k += 256) {
+    const int run = k / (64 * V), l = (k / V) % 64, v = k % V;
+    s2_lds[run * 64 * V + ((v / 4) * 64 + l) * 4 + v % 4] = k < d ? s2[k] : 0.f;
+  }
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  constexpr int STEP = 64 * V;
-  for (int row = blockIdx.x * 4 + wave; row < d_ff; row += gridDim.x * 4) {
-    const T* w = W + (int64_t)row * d;
-    float acc = 0.f;
-    int k0 = 0;
-    for (; k0 + 4 * STEP <= d; k0 += 4 * STEP) {
-      u32x4 q[4];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = blockIdx.x * 4 + wave;
+  const int rstep = gridDim.x * 4;
+  const int n_rows = row0 < d_ff ? (d_ff - row0 + rstep - 1) / rstep : 0;
+  const int n_items = n_rows * n_ch;
+  if (n_items == 0) return;
+  auto issue = [&](ImpBuf<T>& b, int it) {
+    it = min(it, n_items - 1);  // past the end: reload the last item (unused)
+    const int r = row0 + (it / n_ch) * rstep;
+    const int c = it % n_ch;
+    const T* w = W + (int64_t)r * d;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) q[j] = ld16_stream(w + k0 + j * STEP + lane * V);
+    for (int j = 0; j < kImpLoads; ++j) b.q[j] = ld16_stream(w + min(c * CH + j * 64 * V + lane * V, d - V));
+  };
+  float acc = 0.f;
+  auto consume = [&](const ImpBuf<T>& b, int it) {
+    if (it >= n_items) return;  // wave-uniform
+    const int c = it % n_ch;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float f[V];
-        unpack(q[j], f, T{});
-        const float* sp = s2_lds + k0 + j * STEP + lane * V;
+    for (int j = 0; j < kImpLoads; ++j) {
+      float f[V];
+      unpack(b.q[j], f, T{});
+      const float* sp = s2_lds + c * CH + j * 64 * V + lane * 4;
 #pragma unroll
-        for (int v = 0; v < V; ++v) acc = fmaf(f[v] * f[v], sp[v], acc);
+      for (int g = 0; g < V / 4; ++g) {
+        const float4 q4 = *reinterpret_cast<const float4*>(sp + g * 256);
+        acc = fmaf(f[4 * g] * f[4 * g], q4.x, acc);
+        acc = fmaf(f[4 * g + 1] * f[4 * g + 1], q4.y, acc);
+        acc = fmaf(f[4 * g + 2] * f[4 * g + 2], q4.z, acc);
+        acc = fmaf(f[4 * g + 3] * f[4 * g + 3], q4.w, acc);
       }
     }
-    for (; k0 < d; k0 += STEP) {
-      const int k = k0 + lane * V;
-      if (k < d) {
-        float f[V];
-        unpack(ld16_stream(w + k), f, T{});
-#pragma unroll
-        for (int v = 0; v < V; ++v) acc = fmaf(f[v] * f[v], s2_lds[k + v], acc);
-      }
+    if (c == n_ch - 1) {
+      const float t = wave_sum(acc);
+      if (lane == 0) I[row0 + (it / n_ch) * rstep] = sqrtf(t);
+      acc = 0.f;
     }
-    acc = wave_sum(acc);
-    if (lane == 0) I[row] = sqrtf(acc);
+  };
+  ImpBuf<T> A, B;
+  issue(A, 0);
+  for (int it = 0; it < n_items; it += 2) {
+    issue(B, it + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(A, it);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(A, it + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(B, it + 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -153,42 +265,65 @@ constexpr int kPartThreads = 1024;
 __global__ __launch_bounds__(kPartThreads) void k_partition(const float* __restrict__ I, int n, int c_low, int c_high,
                                                            int32_t* __restrict__ R, int32_t* __restrict__ C,
                                                            int32_t* __restrict__ P) {
-  __shared__ SelShared<kPartThreads> sh;
+  using Sh = SelShared<kPartThreads>;
+  constexpr int EM = Sh::kPerThread;
+  __shared__ Sh sh;
   I += (int64_t)blockIdx.x * n;
   R += (int64_t)blockIdx.x * (n - c_high);
   C += (int64_t)blockIdx.x * (c_high - c_low);
   P += (int64_t)blockIdx.x * c_low;
-  sel_load(I, n, sh);
-  const int ranks[2] = {c_low, c_high};
-  select_thresholds(n, ranks, sh);
-  const SelTarget lo = sh.tgt[0];
-  const SelTarget hi = sh.tgt[1];
+  if (n <= 0) return;
   const int E = (n + kPartThreads - 1) / kPartThreads;
   const int base = threadIdx.x * E;
-  const int end = min(n, base + E);
-  int pos[3] = {0, 0, 0};  // P, C, R
-  for (int i = base; i < end; ++i) {
-    const unsigned long long key = sel_key(sh.vals[i], i);
-    if (sel_less(lo, key)) ++pos[0];
-    else if (sel_less(hi, key)) ++pos[1];
-    else ++pos[2];
+  const int cnt = max(0, min(E, n - base));
+  uint32_t v[EM];
+  sel_load_regs(I, n, base, E, v);
+  const int ranks[2] = {c_low, c_high};
+  SelTarget t[2];
+  select_targets<kPartThreads, 2, EM, kSelMaxN>(v, n, base, E, ranks, sh, t);
+  int eqb[2];
+  sel_eq_before<kPartThreads, 2, EM, kSelMaxN>(v, E, cnt, t, sh, eqb);
+  // class of element j: 0 = P (below c_low), 1 = C, 2 = R (not below c_high)
+  auto cls = [&](int j, int& e0, int& e1) {
+    e0 += v[j] == t[0].prefix ? 1 : 0;
+    e1 += v[j] == t[1].prefix ? 1 : 0;
+    if (sel_below(t[0], v[j], t[0].count - e0)) return 0;
+    return sel_below(t[1], v[j], t[1].count - e1) ? 1 : 2;
+  };
+  int pos[3] = {0, 0, 0};
+  {
+    int e0 = eqb[0], e1 = eqb[1];
+#pragma unroll
+    for (int j = 0; j < EM; ++j) {
+      if (j >= E) break;  // block-uniform
+      const int c = cls(j, e0, e1);
+      pos[0] += (j < cnt && c == 0) ? 1 : 0;
+      pos[1] += (j < cnt && c == 1) ? 1 : 0;
+      pos[2] += (j < cnt && c == 2) ? 1 : 0;
+    }
   }
   int tot[3];
   block_exclusive_scan3(pos, tot, sh);
   // Positions are capped at the list sizes the host derived from the counts;
   // an exact select never reaches the caps.
   const int n_P = c_low, n_C = c_high - c_low, n_R = n - c_high;
-  for (int i = base; i < end; ++i) {
-    const unsigned long long key = sel_key(sh.vals[i], i);
-    if (sel_less(lo, key)) {
-      if (pos[0] < n_P) P[pos[0]] = i;
-      ++pos[0];
-    } else if (sel_less(hi, key)) {
-      if (pos[1] < n_C) C[pos[1]] = i;
-      ++pos[1];
-    } else {
-      if (pos[2] < n_R) R[pos[2]] = i;
-      ++pos[2];
+  int e0 = eqb[0], e1 = eqb[1];
+#pragma unroll
+  for (int j = 0; j < EM; ++j) {
+    if (j >= E) break;  // block-uniform
+    if (j < cnt) {
+      const int i = base + j;
+      const int c = cls(j, e0, e1);
+      if (c == 0) {
+        if (pos[0] < n_P) P[pos[0]] = i;
+        ++pos[0];
+      } else if (c == 1) {
+        if (pos[1] < n_C) C[pos[1]] = i;
+        ++pos[1];
+      } else {
+        if (pos[2] < n_R) R[pos[2]] = i;
+        ++pos[2];
+      }
     }
   }
 }
@@ -216,6 +351,17 @@ static PrefillPlan plan_prefill(int64_t n_tokens, int32_t d, int vec) {
   return p;
 }
 
+static int imp_blocks(int32_t d_ff) {
+  const int want = (d_ff + 3) / 4;
+  return want < kImpBlocks ? want : kImpBlocks;
+}
+
+template <typename T>
+static size_t imp_lds_bytes(int32_t d) {
+  constexpr int CH = kImpLoads * 64 * Vec<T>::N;
+  return (size_t)((d + CH - 1) / CH) * CH * sizeof(float);
+}
+
 static size_t importance_ws_bytes(int64_t n_tokens, int32_t d) {
   // Widest plan over both dtypes (bf16 has fewer column blocks, hence more chunks).
   const PrefillPlan p = plan_prefill(n_tokens, d, 8);
@@ -233,14 +379,18 @@ static void launch_importance(hipStream_t st, const void* X, int64_t n_tokens, i
   const int max_chunks = pb.n_chunks > pf.n_chunks ? pb.n_chunks : pf.n_chunks;
   float* partial = (float*)ws;
   float* s2 = (float*)(ws + align_up((size_t)max_chunks * d * sizeof(float), 256));
-  if (n_tokens > 0)
-    POP_LAUNCH(k_colsq_partial<T>, dim3(p.col_blocks, p.n_chunks), dim3(64), 0, st, (const T*)X, n_tokens,
-                       d, p.rows_per_chunk, partial);
-  // With no prompt token the sum runs over zero chunks: s = 0, hence I = 0.
-  POP_LAUNCH(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(1024), 0, st, (const float*)partial,
-                     n_tokens > 0 ? p.n_chunks : 0, (int64_t)d, s2, (unsigned int*)nullptr, 0);
-  POP_LAUNCH(k_importance<T>, dim3((d_ff + 3) / 4), dim3(256), (size_t)d * sizeof(float), st, (const T*)W_up,
-                     d_ff, d, (const float*)s2, I);
+  if (n_tokens <= kCsOnePassMax) {
+    // With no prompt token every column sum is 0, hence I = 0.
+    POP_LAUNCH(k_colsq_slices<T>, dim3((d + kCsCols - 1) / kCsCols), dim3(kCsThreads), 0, st, (const T*)X, n_tokens,
+               d, s2);
+  } else {
+    POP_LAUNCH(k_colsq_partial<T>, dim3(p.col_blocks, p.n_chunks), dim3(64), 0, st, (const T*)X, n_tokens, d,
+               p.rows_per_chunk, partial);
+    POP_LAUNCH(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(1024), 0, st, (const float*)partial, p.n_chunks,
+               (int64_t)d, s2, (unsigned int*)nullptr, 0);
+  }
+  POP_LAUNCH(k_importance<T>, dim3(imp_blocks(d_ff)), dim3(256), imp_lds_bytes<T>(d), st, (const T*)W_up, d_ff, d,
+             (const float*)s2, I);
 }
 
 // ---- MoE prefill
@@ -306,7 +456,7 @@ static void launch_moe_prefill(hipStream_t st, const void* X, int64_t n_tokens, 
   POP_LAUNCH(k_sum_chunks<0>, dim3((unsigned)(((int64_t)E * d + 31) / 32)), dim3(1024), 0, st,
              (const float*)w.partial, n_tokens > 0 ? p.n_chunks : 0, (int64_t)E * d, w.s2, (unsigned int*)nullptr,
              0);
-  POP_LAUNCH(k_importance<T>, dim3((d_ff + 3) / 4, E), dim3(256), (size_t)d * sizeof(float), st, (const T*)W_up,
+  POP_LAUNCH(k_importance<T>, dim3(imp_blocks(d_ff), E), dim3(256), imp_lds_bytes<T>(d), st, (const T*)W_up,
              d_ff, d, (const float*)w.s2, I);
   POP_LAUNCH(k_partition, dim3(E), dim3(kPartThreads), 0, st, (const float*)I, d_ff, c.c_low, c.c_high, R, C, P);
 }
