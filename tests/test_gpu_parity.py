@@ -51,6 +51,9 @@ PART_CASES = [
     ("bf16_max_d_ff", 4, 64, 32768, "bf16", 0.3, 0.1),
     ("bf16_max_d", 3, 16384, 40, "bf16", 0.3, 0.1),
     ("f32_long_prompt", 5000, 256, 700, "f32", 0.25, 0.1),
+    # prompts at and past the one-pass column-norm limit (8192 tokens)
+    ("f32_prompt_at_one_pass_limit", 8192, 72, 150, "f32", 0.3, 0.1),
+    ("bf16_prompt_past_one_pass", 9000, 136, 300, "bf16", 0.3, 0.1),
 ]
 
 
