@@ -2,8 +2,9 @@
 """Benchmark of the POP channel-pruned gated-MLP path on one MI355X.
 
 One step is one whole request of the workload with every input already in
-HBM: the prefill of every layer (the dense prompt FFN on the matrix cores, then
-the partition: column norm, importance, three-region select) followed by every
+HBM: the prefill of every layer (one pop_prefill_ffn_partition call: column
+norms, the dense prompt FFN on the matrix cores with the importance taken in its
+gate/up pass, the three-region select) followed by every
 decode step over every layer (gate/up over R u C with fused scores, candidate
 top-k, gathered down-projection).  The layers do not
 chain: each has its own seeded prompt and decode inputs.  Steps are replayed as
@@ -118,6 +119,7 @@ def main():
     y = torch.empty((L, B, d), dtype=torch.float32, device=dev)
     ws_pre = pop.workspace(pop.pop_prefill_workspace_bytes(n_tok, d, d_ff), dev)
     ws_ffn = pop.workspace(max(pop.pop_dense_ffn_prefill_workspace_bytes(n_tok, d, d_ff, w.dtype), 256), dev)
+    ws_fused = pop.workspace(pop.pop_prefill_ffn_partition_workspace_bytes(n_tok, d, d_ff, w.dtype), dev)
     Yp = torch.empty((n_tok, d), dtype=torch.float32, device=dev)   # prompt FFN output (layers do not chain)
     ws_dec = pop.workspace(pop.pop_decode_workspace_bytes(B, d, d_ff), dev)
     torch.cuda.synchronize()
@@ -141,7 +143,17 @@ def main():
     def partition(l):
         pop.pop_prefill_partition(X[l], Wu[l], w.r, w.gamma, out=(R[l], C[l], P[l], None), ws=ws_pre)
 
+    def prefill_fused(l):
+        pop.pop_prefill_ffn_partition(X[l], Wg[l], Wu[l], WdT[l], w.r, w.gamma, Y=Yp, out=(R[l], C[l], P[l], None),
+                                      ws=ws_fused)
+
     def prefill():
+        # the whole prefill of each layer in one call: the importance comes out of
+        # the prompt FFN's gate/up pass (one W_up sweep instead of two)
+        for l in range(L):
+            prefill_fused(l)
+
+    def prefill_unfused():
         for l in range(L):
             prompt_ffn(l)
             partition(l)
@@ -176,13 +188,15 @@ def main():
     with torch.cuda.stream(side):
         x_buf.copy_(Xdec[0])
         prefill()
+        prefill_unfused()
         decode_layers_1s()
         decode_layers()
         dense_layers()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graphs = {}
-    for name, fn in (("prefill", prefill), ("prompt_ffn", prompt_ffn_layers), ("partition", partition_layers),
+    for name, fn in (("prefill", prefill), ("prefill_unfused", prefill_unfused), ("prompt_ffn", prompt_ffn_layers),
+                     ("partition", partition_layers),
                      ("decode", decode_layers), ("decode_1s", decode_layers_1s), ("dense", dense_layers)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -217,6 +231,8 @@ def main():
     # ------------------------------------------------------------ component timings (graphs)
     ms_prefill = timed(lambda: graphs["partition"].replay(), 5)
     ms_pffn = timed(lambda: graphs["prompt_ffn"].replay(), 3)
+    ms_pre_fused = timed(lambda: graphs["prefill"].replay(), 3)
+    ms_pre_unfused = timed(lambda: graphs["prefill_unfused"].replay(), 3)
     pffn_flops = metrics.prefill_ffn_flops(n_tok, d, d_ff)
     pffn_tflops = pffn_flops / (ms_pffn / L * 1e-3) / 1e12
 
@@ -287,6 +303,7 @@ def main():
         f"dense {t_ls_dense * 1e3:.1f} us ({bytes_dense / (t_ls_dense * 1e-3) / 1e9:.0f} GB/s), "
         f"static mask {ms_static / (T * L) * 1e3:.1f} us, full re-evaluation {ms_full / (T * L) * 1e3:.1f} us, "
         f"prefill partition {ms_prefill / L * 1e3:.1f} us/layer, "
+        f"prefill fused {ms_pre_fused / L * 1e3:.1f} (unfused {ms_pre_unfused / L * 1e3:.1f}) us/layer, "
         f"prompt FFN {ms_pffn / L * 1e3:.1f} us/layer ({pffn_tflops:.0f} TFLOP/s)")
 
     # ------------------------------------------------------------ per-kernel pass (eager, queued ahead)
@@ -303,6 +320,9 @@ def main():
     n_pass = -(-n_tok // 4096)
     labels_ffn = (["k_prompt_gateup", "k_prompt_down"] if e == 2 else
                   ["k_prompt_gateup_f32", "k_prompt_down_f32"]) * n_pass
+    labels_fused = ((["k_colsq_slices"] if n_tok <= 8192 else ["k_colsq_partial", "k_sum_chunks(s2)"])
+                    + ([labels_ffn[0] + "+I(fused)"] + labels_ffn[1:] if n_tok > 0 else ["k_zero_f32"])
+                    + ["k_partition"])
     if fused:
         plan = metrics.fused_plan(n_R, n_C, k, d, e)
         labels_dec = [f"k_pop_step.{ph}" for ph in (1, 2) if plan["launch"][ph]] + ["k_pop_finish"]
@@ -326,6 +346,9 @@ def main():
             a = pop.lib.pop_trace_recorded()
             partition(l)
             marks.append((labels_pre, a, pop.lib.pop_trace_recorded()))
+            a = pop.lib.pop_trace_recorded()
+            prefill_fused(l)
+            marks.append((labels_fused, a, pop.lib.pop_trace_recorded()))
         for t in range(S):
             x_buf.copy_(Xdec[t])
             for l in range(L):
@@ -426,7 +449,7 @@ def main():
             "workload": w.name, "layers": L, "d": d, "d_ff": d_ff, "r_ffn": w.r, "gamma": w.gamma,
             "prompt_tokens": n_tok, "decode_steps": T, "decode_batch": B, "hip_graphs": True,
             "streams": 1 if two is None else 2,
-            "step": "prefill (dense prompt FFN + partition) of every layer + every decode step over every layer",
+            "step": "prefill (fused dense prompt FFN + partition) of every layer + every decode step over every layer",
         },
         "roofline": {
             "kernel": dom_desc,
@@ -468,6 +491,12 @@ def main():
             "full_time_over_static": round(ms_full / ms_static - 1.0, 4),
         },
         "prefill_partition_us_per_layer": round(ms_prefill / L * 1e3, 2),
+        "prefill_layer_us": {
+            "fused": round(ms_pre_fused / L * 1e3, 2),
+            "unfused": round(ms_pre_unfused / L * 1e3, 2),
+            "fused_call": "pop_prefill_ffn_partition (column norms, prompt FFN with the importance in its gate/up "
+                          "pass, partition); unfused: pop_dense_ffn_prefill + pop_prefill_partition",
+        },
         "prompt_ffn": {
             "us_per_layer": round(ms_pffn / L * 1e3, 2),
             "flops_per_layer": pffn_flops,

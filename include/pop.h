@@ -301,6 +301,32 @@ pop_status pop_dense_ffn_prefill(const void* X, int64_t n_tokens, int32_t d, con
                                  const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
                                  float* Y, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes of pop_prefill_ffn_partition (0 for invalid arguments). */
+size_t pop_prefill_ffn_partition_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff, pop_dtype dt);
+
+/*
+ * pop_prefill_ffn_partition — the whole prefill of one FFN layer in one call:
+ * the dense prompt FFN (as pop_dense_ffn_prefill) and the three-region
+ * partition of POP notes, "Key design 1" (as pop_prefill_partition), with the
+ * importance I_i = || W_up[i, :] * s ||_2 computed inside the gate/up pass from
+ * the W_up tiles it already reads, so W_up is swept once instead of twice.
+ * The column norms s (over all n_tokens rows of X) are computed first.
+ *
+ *   X, W_gate, W_up, W_downT, Y   as for pop_dense_ffn_prefill
+ *   r, gamma, R, C, P             as for pop_prefill_partition
+ *   importance  optional device fp32 [d_ff] output (NULL: kept in ws)
+ *   ws          pop_prefill_ffn_partition_workspace_bytes(n_tokens, d, d_ff, dt)
+ * The sums behind I run in another order than pop_prefill_importance's, so
+ * the two I agree to fp32 rounding, and the partitions agree except where a
+ * channel's I lies within that rounding of a cut.  n_tokens = 0: Y is not
+ * touched, I = 0 and the partition goes by index.  Errors: as for the two
+ * calls it combines.
+ */
+pop_status pop_prefill_ffn_partition(const void* X, int64_t n_tokens, int32_t d, const void* W_gate,
+                                     const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
+                                     double r, double gamma, float* Y, int32_t* R, int32_t* C, int32_t* P,
+                                     float* importance, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Mixture of experts.
  *

@@ -25,6 +25,16 @@ pop_status check_rate(double r, double gamma);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Prefill pieces shared with the fused prefill FFN (defined in prefill.hip;
+// stream is a hipStream_t).  colsq_ws_bytes sizes the column-norm workspace
+// (partial sums, then s2); launch_colsq writes s2 = sum over the prompt rows of
+// X^2 into that workspace and returns it; launch_partition_lists launches the
+// one-workgroup select and compaction into R, C, P.
+size_t colsq_ws_bytes(int64_t n_tokens, int32_t d);
+float* launch_colsq(void* stream, const void* X, int64_t n_tokens, int32_t d, pop_dtype dt, char* ws);
+void launch_partition_lists(void* stream, const float* I, int32_t d_ff, int32_t c_low, int32_t c_high, int32_t* R,
+                            int32_t* C, int32_t* P);
+
 // Records the next caller-provided trace event on `stream` (no-op unless
 // pop_set_trace_events armed this thread).
 void trace_mark(void* stream);

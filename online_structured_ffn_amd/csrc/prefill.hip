@@ -371,9 +371,9 @@ static size_t importance_ws_bytes(int64_t n_tokens, int32_t d) {
          + align_up((size_t)d * sizeof(float), 256);        // s2
 }
 
+// s2 into the workspace's s2 slot (after the partial sums); returns it.
 template <typename T>
-static void launch_importance(hipStream_t st, const void* X, int64_t n_tokens, int32_t d, const void* W_up,
-                              int32_t d_ff, float* I, char* ws) {
+static float* launch_colsq_t(hipStream_t st, const void* X, int64_t n_tokens, int32_t d, char* ws) {
   const PrefillPlan p = plan_prefill(n_tokens, d, Vec<T>::N);
   const PrefillPlan pb = plan_prefill(n_tokens, d, 8), pf = plan_prefill(n_tokens, d, 4);
   const int max_chunks = pb.n_chunks > pf.n_chunks ? pb.n_chunks : pf.n_chunks;
@@ -389,8 +389,27 @@ static void launch_importance(hipStream_t st, const void* X, int64_t n_tokens, i
     POP_LAUNCH(k_sum_chunks<0>, dim3((d + 31) / 32), dim3(1024), 0, st, (const float*)partial, p.n_chunks,
                (int64_t)d, s2, (unsigned int*)nullptr, 0);
   }
+  return s2;
+}
+
+template <typename T>
+static void launch_importance(hipStream_t st, const void* X, int64_t n_tokens, int32_t d, const void* W_up,
+                              int32_t d_ff, float* I, char* ws) {
+  const float* s2 = launch_colsq_t<T>(st, X, n_tokens, d, ws);
   POP_LAUNCH(k_importance<T>, dim3(imp_blocks(d_ff)), dim3(256), imp_lds_bytes<T>(d), st, (const T*)W_up, d_ff, d,
-             (const float*)s2, I);
+             s2, I);
+}
+
+size_t colsq_ws_bytes(int64_t n_tokens, int32_t d) { return importance_ws_bytes(n_tokens, d); }
+
+float* launch_colsq(void* stream, const void* X, int64_t n_tokens, int32_t d, pop_dtype dt, char* ws) {
+  return dt == POP_BF16 ? launch_colsq_t<bf16s>((hipStream_t)stream, X, n_tokens, d, ws)
+                        : launch_colsq_t<float>((hipStream_t)stream, X, n_tokens, d, ws);
+}
+
+void launch_partition_lists(void* stream, const float* I, int32_t d_ff, int32_t c_low, int32_t c_high, int32_t* R,
+                            int32_t* C, int32_t* P) {
+  POP_LAUNCH(k_partition, dim3(1), dim3(kPartThreads), 0, (hipStream_t)stream, I, d_ff, c_low, c_high, R, C, P);
 }
 
 // ---- MoE prefill

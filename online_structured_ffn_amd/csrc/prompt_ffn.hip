@@ -84,10 +84,23 @@ struct ATile {
 // ---------------------------------------------------------------- gate / up
 // Wave w covers tokens (w >> 1) * 64 + [0, 64) and channels (w & 1) * 32 +
 // [0, 32) of the block's tile, for both matrices: 4 x 2 fragments each.
+//
+// IMP > 0: the blocks also compute the importance
+// I_i = sqrt(sum_k W_up[i,k]^2 * s2[k]) of the block's channels from the W_up
+// tiles already in LDS (the column norms s2 of the whole prompt are an input),
+// so the prefill needs no second sweep of W_up.  IMP = 16: the blocks of the
+// first four token tiles take 16 of the 64 channels each (m_tile * 16 + [0,
+// 16)), so the extra work is spread evenly; IMP = 64 (fewer than four token
+// tiles): the first token tile takes all 64.  Thread t takes channel
+// t % IMP and the KPT = 64 * IMP / 256 columns (t / IMP) * KPT + [0, KPT) of
+// every 64-column stage, in ascending order; the 256 / IMP column groups of a
+// channel are added in order at the end.
+template <int IMP>
 __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __restrict__ X, int M, int d,
                                                              const bf16s* __restrict__ Wg,
                                                              const bf16s* __restrict__ Wu, int d_ff,
-                                                             uint16_t* __restrict__ Z, int ldz, int mt, int nt) {
+                                                             uint16_t* __restrict__ Z, int ldz, int mt, int nt,
+                                                             const float* __restrict__ s2, float* __restrict__ I) {
   __shared__ __align__(16) uint16_t As[2][kBM * kLd];
   __shared__ __align__(16) uint16_t Bs[2][2 * kBN * kLd];  // gate rows, then up rows
   constexpr int BPER = 2 * kBN * (kBK / 8) / kGThreads;
@@ -127,6 +140,32 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __rest
     }
 
   const int nk = (d + kBK - 1) / kBK;
+  // importance state (block-uniform)
+  constexpr int IC = IMP > 0 ? IMP : 64;       // channels per importance block
+  constexpr int KPT = 64 * IC / kGThreads;     // columns per thread per stage (4 or 16)
+  const bool imp = IMP > 0 && m_tile < (IMP == 16 ? 4 : 1);
+  const int c_base = IMP == 16 ? m_tile * 16 : 0;
+  const int ir = tid % IC, ig = tid / IC;
+  float ia = 0.f;
+  float s2c[KPT], s2n[KPT];
+  // Columns past d read s2 at d - 4 (finite); their W_up values in LDS are 0,
+  // so they add nothing and the loaded values need no select (a select right
+  // after the load would make the compiler wait for every load in flight).
+  auto load_s2 = [&](float (&v)[KPT], int k0) {
+#pragma unroll
+    for (int q = 0; q < KPT; q += 4) {
+      const int k = k0 + ig * KPT + q;  // d is a multiple of 4
+      const float4 f = *reinterpret_cast<const float4*>(s2 + min(k, d - 4));
+      v[q] = f.x;
+      v[q + 1] = f.y;
+      v[q + 2] = f.z;
+      v[q + 3] = f.w;
+    }
+  };
+  // Every block of an IMP > 0 launch runs the importance arithmetic (a few
+  // FMAs per stage, no branch in the loop: a condition around the loads would
+  // make the compiler wait for the tile prefetch); only imp blocks write I.
+  if constexpr (IMP > 0) load_s2(s2c, 0);
   a.load(X, d, M, d, m0, 0);
   load_b(0);
   a.store(As[0]);
@@ -138,6 +177,18 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __rest
     if (kt + 1 < nk) {
       a.load(X, d, M, d, m0, (kt + 1) * kBK);
       load_b((kt + 1) * kBK);
+      if constexpr (IMP > 0) load_s2(s2n, (kt + 1) * kBK);
+    }
+    if constexpr (IMP > 0) {
+      // W_up row n0 + c_base + ir of this stage: columns ig * KPT + [0, KPT)
+      const uint16_t* wr = &Bs[s][(kBN + c_base + ir) * kLd + ig * KPT];
+#pragma unroll
+      for (int q = 0; q < KPT; q += 2) {
+        const uint32_t w2 = *reinterpret_cast<const uint32_t*>(wr + q);
+        const float f0 = __uint_as_float(w2 << 16), f1 = __uint_as_float(w2 & 0xffff0000u);
+        ia = fmaf(f0 * f0, s2c[q], ia);
+        ia = fmaf(f1 * f1, s2c[q + 1], ia);
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < kBK; kk += 32) {
@@ -158,8 +209,23 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __rest
     if (kt + 1 < nk) {
       a.store(As[s ^ 1]);
       store_b(Bs[s ^ 1]);
+      if constexpr (IMP > 0) {
+#pragma unroll
+        for (int q = 0; q < KPT; ++q) s2c[q] = s2n[q];
+      }
     }
     __syncthreads();
+  }
+  if (imp) {  // block-uniform; the loop's last barrier freed As
+    float* red = reinterpret_cast<float*>(As[0]);
+    red[ig * IC + ir] = ia;
+    __syncthreads();
+    if (ig == 0 && n0 + c_base + ir < d_ff) {
+      float t = red[ir];
+#pragma unroll
+      for (int g = 1; g < kGThreads / IC; ++g) t += red[g * IC + ir];
+      I[n0 + c_base + ir] = sqrtf(t);
+    }
   }
   // Output fragment layout: element e of lane l is row (l >> 4) * 4 + e,
   // column l & 15 of the 16 x 16 tile.  Columns in [d_ff, ldz) come out as
@@ -270,20 +336,28 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_down(const uint16_t* __res
 // owns output (m0 + ty, n0 + tx).
 constexpr int kFT = 16;
 
+// kImp: the blocks of the first token tile also compute I for their 16
+// channels (thread (ty, tx) sums column tx of channel n0 + ty over the
+// stages; the 16 partial sums of a channel are added in column order).
+template <bool kImp>
 __global__ __launch_bounds__(kFT* kFT) void k_prompt_gateup_f32(const float* __restrict__ X, int M, int d,
                                                                  const float* __restrict__ Wg,
                                                                  const float* __restrict__ Wu, int d_ff,
-                                                                 float* __restrict__ Z, int ldz) {
+                                                                 float* __restrict__ Z, int ldz,
+                                                                 const float* __restrict__ s2,
+                                                                 float* __restrict__ I) {
   __shared__ float xs[kFT][kFT + 1], gs[kFT][kFT + 1], us[kFT][kFT + 1];
   const int tx = threadIdx.x % kFT, ty = threadIdx.x / kFT;
   const int m0 = blockIdx.y * kFT, n0 = blockIdx.x * kFT;
-  float g = 0.f, u = 0.f;
+  const bool imp = kImp && blockIdx.y == 0;
+  float g = 0.f, u = 0.f, ia = 0.f;
   for (int k0 = 0; k0 < d; k0 += kFT) {
     const int k = k0 + tx;
     xs[ty][tx] = (m0 + ty < M && k < d) ? X[(int64_t)(m0 + ty) * d + k] : 0.f;
     gs[ty][tx] = (n0 + ty < d_ff && k < d) ? Wg[(int64_t)(n0 + ty) * d + k] : 0.f;
     us[ty][tx] = (n0 + ty < d_ff && k < d) ? Wu[(int64_t)(n0 + ty) * d + k] : 0.f;
     __syncthreads();
+    if (imp) ia = fmaf(us[ty][tx] * us[ty][tx], k < d ? s2[k] : 0.f, ia);
 #pragma unroll
     for (int j = 0; j < kFT; ++j) {
       g = fmaf(xs[ty][j], gs[tx][j], g);
@@ -293,6 +367,16 @@ __global__ __launch_bounds__(kFT* kFT) void k_prompt_gateup_f32(const float* __r
   }
   const int m = m0 + ty, n = n0 + tx;
   if (m < M && n < d_ff) Z[(int64_t)m * ldz + n] = silu(g) * u;
+  if (imp) {  // block-uniform
+    xs[ty][tx] = ia;
+    __syncthreads();
+    if (tx == 0 && n0 + ty < d_ff) {
+      float t = xs[ty][0];
+#pragma unroll
+      for (int j = 1; j < kFT; ++j) t += xs[ty][j];
+      I[n0 + ty] = sqrtf(t);
+    }
+  }
 }
 
 __global__ __launch_bounds__(kFT* kFT) void k_prompt_down_f32(const float* __restrict__ Z, int M, int ldz,
@@ -314,6 +398,12 @@ __global__ __launch_bounds__(kFT* kFT) void k_prompt_down_f32(const float* __res
   if (m < M && n < d) Y[(int64_t)m * d + n] = acc;
 }
 
+// I = 0 for an empty prompt (every column norm is 0).
+__global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
 // ---------------------------------------------------------------- host
 static int z_pitch(int32_t d_ff) { return (int)align_up((size_t)d_ff, kZPad); }
 
@@ -328,26 +418,41 @@ static pop_status launched() {
   return POP_OK;
 }
 
+// With s2 and I set, the first chunk's gate/up launch also writes I.
 static void launch_prompt_ffn(hipStream_t st, const void* X, int64_t n_tokens, int32_t d, const void* Wg,
-                              const void* Wu, const void* WdT, int32_t d_ff, pop_dtype dt, float* Y, void* ws) {
+                              const void* Wu, const void* WdT, int32_t d_ff, pop_dtype dt, float* Y, void* ws,
+                              const float* s2 = nullptr, float* I = nullptr) {
   const int ldz = z_pitch(d_ff);
   for (int64_t t0 = 0; t0 < n_tokens; t0 += kChunkTokens) {
     const int M = (int)(n_tokens - t0 < kChunkTokens ? n_tokens - t0 : kChunkTokens);
     float* Yc = Y + t0 * d;
+    const bool imp = I != nullptr && t0 == 0;
     if (dt == POP_BF16) {
       const bf16s* Xc = (const bf16s*)X + t0 * d;
       const int mt = (M + kBM - 1) / kBM;
       const int nt1 = ldz / kBN;
-      POP_LAUNCH(k_prompt_gateup, dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
-                 (const bf16s*)Wu, (int)d_ff, (uint16_t*)ws, ldz, mt, nt1);
+      if (imp && mt >= 4)
+        POP_LAUNCH(k_prompt_gateup<16>, dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
+                   (const bf16s*)Wu, (int)d_ff, (uint16_t*)ws, ldz, mt, nt1, s2, I);
+      else if (imp)
+        POP_LAUNCH(k_prompt_gateup<64>, dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
+                   (const bf16s*)Wu, (int)d_ff, (uint16_t*)ws, ldz, mt, nt1, s2, I);
+      else
+        POP_LAUNCH(k_prompt_gateup<0>, dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
+                   (const bf16s*)Wu, (int)d_ff, (uint16_t*)ws, ldz, mt, nt1, (const float*)nullptr, (float*)nullptr);
       const int nt2 = (d + kBN - 1) / kBN;
       POP_LAUNCH(k_prompt_down, dim3(mt * nt2), dim3(kGThreads), 0, st, (const uint16_t*)ws, M, ldz,
                  (const bf16s*)WdT, (int)d_ff, (int)d, Yc, mt, nt2);
     } else {
       const float* Xc = (const float*)X + t0 * d;
       const int mt = (M + kFT - 1) / kFT;
-      POP_LAUNCH(k_prompt_gateup_f32, dim3((d_ff + kFT - 1) / kFT, mt), dim3(kFT * kFT), 0, st, Xc, M, (int)d,
-                 (const float*)Wg, (const float*)Wu, (int)d_ff, (float*)ws, ldz);
+      if (imp)
+        POP_LAUNCH(k_prompt_gateup_f32<true>, dim3((d_ff + kFT - 1) / kFT, mt), dim3(kFT * kFT), 0, st, Xc, M,
+                   (int)d, (const float*)Wg, (const float*)Wu, (int)d_ff, (float*)ws, ldz, s2, I);
+      else
+        POP_LAUNCH(k_prompt_gateup_f32<false>, dim3((d_ff + kFT - 1) / kFT, mt), dim3(kFT * kFT), 0, st, Xc, M,
+                   (int)d, (const float*)Wg, (const float*)Wu, (int)d_ff, (float*)ws, ldz, (const float*)nullptr,
+                   (float*)nullptr);
       POP_LAUNCH(k_prompt_down_f32, dim3((d + kFT - 1) / kFT, mt), dim3(kFT * kFT), 0, st, (const float*)ws, M,
                  ldz, (const float*)WdT, (int)d_ff, (int)d, Yc);
     }
@@ -361,6 +466,58 @@ using namespace pop;
 extern "C" size_t pop_dense_ffn_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff, pop_dtype dt) {
   if (n_tokens < 0 || d <= 0 || d_ff <= 0 || (dt != POP_BF16 && dt != POP_F32)) return 0;
   return prompt_ffn_ws_bytes(n_tokens, d_ff, elem_bytes(dt));
+}
+
+// Fused prefill: column norms, then the prompt FFN whose gate/up pass also
+// yields the importance, then the partition.  Workspace: the Z buffer, the
+// column-norm workspace, and I when the caller passes none.
+static size_t fused_prefill_ws_bytes(int64_t n_tokens, int32_t d, int32_t d_ff, pop_dtype dt) {
+  return prompt_ffn_ws_bytes(n_tokens, d_ff, elem_bytes(dt)) + colsq_ws_bytes(n_tokens, d) +
+         align_up((size_t)d_ff * sizeof(float), 256);
+}
+
+extern "C" size_t pop_prefill_ffn_partition_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff, pop_dtype dt) {
+  if (n_tokens < 0 || d <= 0 || d_ff <= 0 || (dt != POP_BF16 && dt != POP_F32)) return 0;
+  return fused_prefill_ws_bytes(n_tokens, d, d_ff, dt);
+}
+
+extern "C" pop_status pop_prefill_ffn_partition(const void* X, int64_t n_tokens, int32_t d, const void* W_gate,
+                                                const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
+                                                double r, double gamma, float* Y, int32_t* R, int32_t* C, int32_t* P,
+                                                float* importance, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  pop_status s = check_dtype_width(dt, d);
+  if (s != POP_OK) return s;
+  if ((s = check_rate(r, gamma)) != POP_OK) return s;
+  if (d > POP_MAX_D) return fail(POP_ERR_BAD_SHAPE, "d=%d above %d", d, POP_MAX_D);
+  if (d_ff < 1 || d_ff > POP_MAX_D_FF) return fail(POP_ERR_BAD_SHAPE, "d_ff=%d outside [1, %d]", d_ff, POP_MAX_D_FF);
+  if (n_tokens < 0 || n_tokens > ((int64_t)1 << 40) / d)
+    return fail(POP_ERR_BAD_SHAPE, "n_tokens=%lld out of range", (long long)n_tokens);
+  if (W_gate == nullptr || W_up == nullptr || W_downT == nullptr || ws == nullptr)
+    return fail(POP_ERR_INVALID_ARGUMENT, "W_gate, W_up, W_downT and ws must be non-NULL");
+  if (n_tokens > 0 && (X == nullptr || Y == nullptr))
+    return fail(POP_ERR_INVALID_ARGUMENT, "X and Y must be non-NULL when n_tokens > 0");
+  const pop_counts c = counts(d_ff, r, gamma);
+  if ((c.n_R > 0 && R == nullptr) || (c.n_C > 0 && C == nullptr) || (c.n_P > 0 && P == nullptr))
+    return fail(POP_ERR_INVALID_ARGUMENT, "an output list with a nonzero size is NULL");
+  if (!aligned16(X) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_downT) || !aligned16(Y) ||
+      !aligned16(ws) || !aligned16(importance))
+    return fail(POP_ERR_MISALIGNED, "buffers must be 16-byte aligned");
+  const size_t need = fused_prefill_ws_bytes(n_tokens, d, d_ff, dt);
+  if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  char* base = (char*)ws;
+  char* zws = base;
+  char* cws = zws + prompt_ffn_ws_bytes(n_tokens, d_ff, elem_bytes(dt));
+  float* I = importance ? importance : (float*)(cws + colsq_ws_bytes(n_tokens, d));
+  hipStream_t st = (hipStream_t)stream;
+  trace_mark(st);
+  const float* s2 = launch_colsq(st, X, n_tokens, d, dt, cws);
+  if (n_tokens > 0)
+    launch_prompt_ffn(st, X, n_tokens, d, W_gate, W_up, W_downT, d_ff, dt, Y, zws, s2, I);
+  else
+    POP_LAUNCH(k_zero_f32, dim3((d_ff + 255) / 256), dim3(256), 0, st, I, (int)d_ff);
+  launch_partition_lists(st, I, d_ff, c.c_low, c.c_high, R, C, P);
+  return launched();
 }
 
 extern "C" pop_status pop_dense_ffn_prefill(const void* X, int64_t n_tokens, int32_t d, const void* W_gate,

@@ -74,6 +74,10 @@ def _load():
                                               _c_size, _c_vp]),
         "pop_dense_ffn_prefill": (ctypes.c_int, [_c_vp, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
                                                  _c_vp, _c_vp, _c_size, _c_vp]),
+        "pop_prefill_ffn_partition_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32, ctypes.c_int]),
+        "pop_prefill_ffn_partition": (ctypes.c_int, [_c_vp, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
+                                                     _c_dbl, _c_dbl, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_size,
+                                                     _c_vp]),
         "pop_decode_down": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, ctypes.c_int, _c_vp, _c_i32,
                                            _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_size, _c_vp]),
     }
@@ -268,6 +272,38 @@ def pop_dense_ffn_prefill(X, W_gate, W_up, W_downT, *, Y=None, ws=None, stream=N
 
 
 # ---------------------------------------------------------------- mixture of experts
+def pop_prefill_ffn_partition_workspace_bytes(n_tokens: int, d: int, d_ff: int, dtype: str) -> int:
+    return int(lib.pop_prefill_ffn_partition_workspace_bytes(n_tokens, d, d_ff,
+                                                             POP_BF16 if dtype == "bf16" else POP_F32))
+
+
+def pop_prefill_ffn_partition(X, W_gate, W_up, W_downT, r: float, gamma: float, *, importance: bool = False,
+                              Y=None, out=None, ws=None, stream=None):
+    """(Y, R, C, P[, I]): the dense prompt FFN and the partition in one call, the
+    importance taken inside the gate/up pass."""
+    _dev(X, W_gate, W_up, W_downT)
+    n_tokens, d = X.shape
+    d_ff = W_gate.shape[0]
+    dev = W_gate.device
+    c = pop_partition_counts(d_ff, r, gamma)
+    if Y is None:
+        Y = torch.empty((n_tokens, d), dtype=torch.float32, device=dev)
+    if out is None:
+        R = torch.empty(c["n_R"], dtype=torch.int32, device=dev)
+        C = torch.empty(c["n_C"], dtype=torch.int32, device=dev)
+        P = torch.empty(c["n_P"], dtype=torch.int32, device=dev)
+        I = torch.empty(d_ff, dtype=torch.float32, device=dev) if importance else None
+    else:
+        R, C, P, I = out
+    if ws is None:
+        dt = "bf16" if W_gate.dtype == torch.bfloat16 else "f32"
+        ws = workspace(pop_prefill_ffn_partition_workspace_bytes(n_tokens, d, d_ff, dt), dev)
+    _check("pop_prefill_ffn_partition", lib.pop_prefill_ffn_partition(
+        _ptr(X), n_tokens, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate), float(r),
+        float(gamma), _ptr(Y), _ptr(R), _ptr(C), _ptr(P), _ptr(I), _ptr(ws), ws.numel(), _stream(stream)))
+    return (Y, R, C, P, I) if importance else (Y, R, C, P)
+
+
 def pop_moe_route_top2(logits, *, stream=None):
     """(experts [T, 2], weights [T, 2], offsets [E + 1], tokens [2T], slots [T, 2])."""
     _dev(logits)

@@ -130,6 +130,40 @@ def test_prompt_ffn_workspace_sizes():
     assert pop.lib.pop_dense_ffn_prefill_workspace_bytes(-1, 256, 688, 1) == 0
 
 
+def _fused(X=A, n=512, d=256, Wg=A, Wu=A, Wd=A, d_ff=688, dt=1, r=0.3, g=0.1, Y=A, R=A, C=A, P=A, I=None, ws=A,
+           wsb=1 << 30):
+    return pop.lib.pop_prefill_ffn_partition(X, n, d, Wg, Wu, Wd, d_ff, dt, r, g, Y, R, C, P, I, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), DTYPE), (dict(d=12), SHAPE), (dict(d=0), SHAPE), (dict(d=32768), SHAPE), (dict(d_ff=0), SHAPE),
+    (dict(d_ff=40000), SHAPE), (dict(n=-3), SHAPE), (dict(r=1.5), INVALID), (dict(g=-0.1), INVALID),
+    (dict(Wg=None), INVALID), (dict(Wu=None), INVALID), (dict(Wd=None), INVALID), (dict(X=None), INVALID),
+    (dict(Y=None), INVALID), (dict(ws=None), INVALID), (dict(R=None), INVALID), (dict(C=None), INVALID),
+    (dict(P=None), INVALID), (dict(Wu=A + 2), MISALIGNED), (dict(Y=A + 4), MISALIGNED),
+    (dict(I=A + 8), MISALIGNED), (dict(wsb=1000), WS),
+])
+def test_fused_prefill_validation(kw, status):
+    assert _fused(**kw) == status
+    assert pop.lib.pop_last_error().decode()
+
+
+def test_fused_prefill_empty_prompt_needs_no_activations():
+    # n_tokens = 0: X and Y may be NULL; validation passes up to the workspace size check
+    assert _fused(X=None, Y=None, n=0, wsb=16) == WS
+
+
+def test_fused_prefill_workspace_sizes():
+    f = pop.pop_prefill_ffn_partition_workspace_bytes
+    for n, d, d_ff, dt in ((512, 4096, 11008, "bf16"), (1, 256, 688, "f32"), (0, 256, 688, "bf16"),
+                           (9000, 136, 300, "bf16")):
+        # the prompt FFN's Z buffer, the column-norm workspace and I
+        assert f(n, d, d_ff, dt) >= (pop.pop_dense_ffn_prefill_workspace_bytes(n, d, d_ff, dt)
+                                     + pop.lib.pop_prefill_importance_workspace_bytes(n, d) + 4 * d_ff)
+    assert pop.lib.pop_prefill_ffn_partition_workspace_bytes(-1, 256, 688, 1) == 0
+    assert pop.lib.pop_prefill_ffn_partition_workspace_bytes(5, 256, 688, 9) == 0
+
+
 def test_moe_validation():
     lib = pop.lib
     # routing: expert count range, NULL outputs
