@@ -164,7 +164,11 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 // c % kFinCols, so the rows k_pop_finish reads for one column slice are one
 // contiguous run of n_part * kFinCols floats.
 constexpr int kFinCols = POP_FIN_COLS;
-constexpr int kFusedThreads = 256;
+#ifndef POP_FUSED_THREADS
+#define POP_FUSED_THREADS 256  // threads of a k_pop_step block
+#endif
+constexpr int kFusedThreads = POP_FUSED_THREADS;
+constexpr int kFusedWaves = kFusedThreads / 64;
 constexpr int kFusedTopkMaxN = 4096;
 constexpr int kFusedMaxRows = 512;  // rows per block
 constexpr int kFusedP = 2;          // rows per batch
@@ -205,7 +209,7 @@ __device__ __forceinline__ void fused_issue(FusedRowBuf<T, NV>& b, const int* ro
 // nrows get z = 0, and the buffers start zeroed, so every operand is finite.
 template <typename T, int NV, bool kDown, int PB>
 __device__ __forceinline__ void fused_consume(const FusedRowBuf<T, NV>& b, const u32x4 (&xv)[NV], int i0, int nrows,
-                                              int d, float (&part)[2][4][2 * kFusedP], float (&acc)[NV][Vec<T>::N],
+                                              int d, float (&part)[2][kFusedWaves][2 * kFusedP], float (&acc)[NV][Vec<T>::N],
                                               float (&zs)[kFusedP]) {
   constexpr int V = Vec<T>::N;
   const int lane = threadIdx.x & 63;
@@ -245,7 +249,7 @@ __device__ __forceinline__ void fused_consume(const FusedRowBuf<T, NV>& b, const
   for (int p = 0; p < kFusedP; ++p) {
     float g = part[PB][0][2 * p], u = part[PB][0][2 * p + 1];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
+    for (int w = 1; w < kFusedWaves; ++w) {
       g += part[PB][w][2 * p];
       u += part[PB][w][2 * p + 1];
     }
@@ -268,7 +272,7 @@ __device__ __forceinline__ void fused_consume(const FusedRowBuf<T, NV>& b, const
 template <typename T, int NV, bool kDown>
 __device__ __forceinline__ void fused_rows(const int* rows, int nrows, const T* __restrict__ Wg, const T* __restrict__ Wu,
                                            const T* __restrict__ WdT, int d, const u32x4 (&xv)[NV],
-                                           float (&part)[2][4][2 * kFusedP], float (&acc)[NV][Vec<T>::N],
+                                           float (&part)[2][kFusedWaves][2 * kFusedP], float (&acc)[NV][Vec<T>::N],
                                            float* __restrict__ zout, int zbase, float* __restrict__ score) {
   FusedRowBuf<T, NV> A, Bf;
 #pragma unroll
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
 #endif
   __shared__ SelT sh_sel;
   __shared__ int rows[kFusedMaxRows];
-  __shared__ float part[2][4][2 * kFusedP];
+  __shared__ float part[2][kFusedWaves][2 * kFusedP];
   const int bid = blockIdx.x;
   if (PHASE != 0 && bid < nb0) {
     if constexpr (PHASE == 0) {
