@@ -11,8 +11,12 @@
 // stored in bf16 (round to nearest even), the operand type of the second GEMM.
 // fp32: the same two products as LDS-tiled fp32 FMA.
 //
-// Both bf16 GEMMs use 256-thread blocks of 128 tokens x 64 output columns, a
-// 64-wide reduction slice per stage, double-buffered in LDS through registers.
+// Both bf16 GEMMs use 256-thread blocks of 128 tokens x 64 output columns and a
+// 64-wide reduction slice per stage: each stage's global loads go to a ring of
+// register slots (2 for gate/up, 4 for the down-projection) and stay in flight
+// under the MFMAs of the stages before it; a stage then moves to one of two
+// LDS buffers.  Whole stages load with no condition (clamped rows and
+// channels), which keeps the compiler from waiting on the loads in flight.
 // Every operand tile is stored K-contiguous in LDS with a 144-byte row pitch,
 // which makes the 16-lane groups of a fragment read hit all 64 banks once.
 // W_downT is [d_ff, d] (K-major for the second GEMM), so its tile is
@@ -34,6 +38,15 @@ constexpr int kBK = 64;          // reduction slice per stage
 constexpr int kLd = kBK + 8;     // LDS row pitch in bf16 elements (144 bytes)
 constexpr int kZPad = 64;        // Z row pitch = d_ff rounded up to this
 constexpr int64_t kChunkTokens = 4096;  // tokens per pass (bounds the workspace)
+#ifndef POP_GATEUP_NS
+#define POP_GATEUP_NS 2  // register stages of the gate/up pass's load pipeline (3 drops to one wave per SIMD)
+#endif
+#ifndef POP_DOWN_NS
+#define POP_DOWN_NS 4  // register stages of the down-projection's load pipeline
+#endif
+#ifndef POP_DOWN_BM64_BELOW
+#define POP_DOWN_BM64_BELOW 0  // down-projection tiles of 128 tokens below which 64-token tiles are used
+#endif
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t b = __float_as_uint(f);
@@ -58,29 +71,6 @@ __device__ __forceinline__ void tile_of(int bid, int nb, int mt, int& m_tile, in
   n_tile = q / mt;
 }
 
-// A-operand tile: kBM rows of a K-contiguous matrix (row pitch ld), columns
-// [k0, k0 + kBK); rows >= M and columns >= K read as zero.
-struct ATile {
-  static constexpr int PER = kBM * (kBK / 8) / kGThreads;  // 16-byte chunks per thread
-  u32x4 r[PER];
-  __device__ __forceinline__ void load(const bf16s* __restrict__ A, int64_t ld, int M, int K, int m0, int k0) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int q = threadIdx.x + i * kGThreads;
-      const int row = q >> 3, k = k0 + (q & 7) * 8;
-      const int m = m0 + row;
-      r[i] = (m < M && k < K) ? ld16(A + (int64_t)m * ld + k) : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* s) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int q = threadIdx.x + i * kGThreads;
-      *reinterpret_cast<u32x4*>(s + (q >> 3) * kLd + (q & 7) * 8) = r[i];
-    }
-  }
-};
-
 // ---------------------------------------------------------------- gate / up
 // Wave w covers tokens (w >> 1) * 64 + [0, 64) and channels (w & 1) * 32 +
 // [0, 32) of the block's tile, for both matrices: 4 x 2 fragments each.
@@ -95,7 +85,16 @@ struct ATile {
 // t % IMP and the KPT = 64 * IMP / 256 columns (t / IMP) * KPT + [0, KPT) of
 // every 64-column stage, in ascending order; the 256 / IMP column groups of a
 // channel are added in order at the end.
-template <int IMP>
+//
+// Pipeline (as in the down-projection): each stage's loads go to one of NS
+// register slots and stay in flight for NS - 1 stages of MFMA work, then the
+// stage is written to one of two LDS buffers, followed by one barrier.  The
+// stages that lie wholly below d (in groups of NS) load unconditionally: rows
+// past M are clamped to row M - 1 (their outputs are not written) and channels
+// past d_ff to channel d_ff - 1 (their Z columns are written as 0 below).  The
+// last stages (fewer than NS, or a stage that crosses d) load with a column
+// mask so that columns past d are 0, one stage at a time.
+template <int IMP, int NS>
 __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __restrict__ X, int M, int d,
                                                              const bf16s* __restrict__ Wg,
                                                              const bf16s* __restrict__ Wu, int d_ff,
@@ -103,6 +102,7 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __rest
                                                              const float* __restrict__ s2, float* __restrict__ I) {
   __shared__ __align__(16) uint16_t As[2][kBM * kLd];
   __shared__ __align__(16) uint16_t Bs[2][2 * kBN * kLd];  // gate rows, then up rows
+  constexpr int APER = kBM * (kBK / 8) / kGThreads;
   constexpr int BPER = 2 * kBN * (kBK / 8) / kGThreads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int m_tile, n_tile;
@@ -110,23 +110,82 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __rest
   const int m0 = m_tile * kBM, n0 = n_tile * kBN;
   const int wm = wave >> 1, wn = wave & 1;
 
-  ATile a;
-  u32x4 rb[BPER];
-  auto load_b = [&](int k0) {
+  // importance state (block-uniform)
+  constexpr int IC = IMP > 0 ? IMP : 64;       // channels per importance block
+  constexpr int KPT = 64 * IC / kGThreads;     // columns per thread per stage (4 or 16)
+  constexpr int SPS = IMP > 0 ? KPT : 1;       // s2 values per slot
+  const bool imp = IMP > 0 && m_tile < (IMP == 16 ? 4 : 1);
+  const int c_base = IMP == 16 ? m_tile * 16 : 0;
+  const int ir = tid % IC, ig = tid / IC;
+  float ia = 0.f;
+
+  u32x4 ra[NS][APER], rb[NS][BPER];
+  float rs[NS][SPS];
+  // Whole stages: unconditional loads.  Columns of s2 past d are read at
+  // d - 4 (finite); they only ever meet W_up columns that are 0 in LDS.
+  auto issue = [&](int slot, int k0) {
+#pragma unroll
+    for (int i = 0; i < APER; ++i) {
+      const int q = tid + i * kGThreads;
+      const int m = min(m0 + (q >> 3), M - 1);
+      ra[slot][i] = ld16(X + (int64_t)m * d + k0 + (q & 7) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < BPER; ++i) {
+      const int q = tid + i * kGThreads;
+      const int row = q >> 3;
+      const int ch = min(n0 + (row & (kBN - 1)), d_ff - 1);
+      const bf16s* W = row < kBN ? Wg : Wu;
+      rb[slot][i] = ld16(W + (int64_t)ch * d + k0 + (q & 7) * 8);
+    }
+    if constexpr (IMP > 0) {
+#pragma unroll
+      for (int q = 0; q < KPT; q += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(s2 + min(k0 + ig * KPT + q, d - 4));
+        rs[slot][q] = f.x;
+        rs[slot][q + 1] = f.y;
+        rs[slot][q + 2] = f.z;
+        rs[slot][q + 3] = f.w;
+      }
+    }
+  };
+  // Tail stages: columns past d load as 0.
+  auto issue_masked = [&](int slot, int k0) {
+#pragma unroll
+    for (int i = 0; i < APER; ++i) {
+      const int q = tid + i * kGThreads;
+      const int m = min(m0 + (q >> 3), M - 1), k = k0 + (q & 7) * 8;
+      ra[slot][i] = k < d ? ld16(X + (int64_t)m * d + k) : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int i = 0; i < BPER; ++i) {
       const int q = tid + i * kGThreads;
       const int row = q >> 3, k = k0 + (q & 7) * 8;
-      const int ch = n0 + (row & (kBN - 1));
+      const int ch = min(n0 + (row & (kBN - 1)), d_ff - 1);
       const bf16s* W = row < kBN ? Wg : Wu;
-      rb[i] = (ch < d_ff && k < d) ? ld16(W + (int64_t)ch * d + k) : u32x4{0u, 0u, 0u, 0u};
+      rb[slot][i] = k < d ? ld16(W + (int64_t)ch * d + k) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (IMP > 0) {
+#pragma unroll
+      for (int q = 0; q < KPT; q += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(s2 + min(k0 + ig * KPT + q, d - 4));
+        rs[slot][q] = f.x;
+        rs[slot][q + 1] = f.y;
+        rs[slot][q + 2] = f.z;
+        rs[slot][q + 3] = f.w;
+      }
     }
   };
-  auto store_b = [&](uint16_t* s) {
+  auto put = [&](int slot, int buf) {
+#pragma unroll
+    for (int i = 0; i < APER; ++i) {
+      const int q = tid + i * kGThreads;
+      *reinterpret_cast<u32x4*>(&As[buf][(q >> 3) * kLd + (q & 7) * 8]) = ra[slot][i];
+    }
 #pragma unroll
     for (int i = 0; i < BPER; ++i) {
       const int q = tid + i * kGThreads;
-      *reinterpret_cast<u32x4*>(s + (q >> 3) * kLd + (q & 7) * 8) = rb[i];
+      *reinterpret_cast<u32x4*>(&Bs[buf][(q >> 3) * kLd + (q & 7) * 8]) = rb[slot][i];
     }
   };
 
@@ -138,67 +197,28 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __rest
       ag[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       au[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-
-  const int nk = (d + kBK - 1) / kBK;
-  // importance state (block-uniform)
-  constexpr int IC = IMP > 0 ? IMP : 64;       // channels per importance block
-  constexpr int KPT = 64 * IC / kGThreads;     // columns per thread per stage (4 or 16)
-  const bool imp = IMP > 0 && m_tile < (IMP == 16 ? 4 : 1);
-  const int c_base = IMP == 16 ? m_tile * 16 : 0;
-  const int ir = tid % IC, ig = tid / IC;
-  float ia = 0.f;
-  float s2c[KPT], s2n[KPT];
-  // Columns past d read s2 at d - 4 (finite); their W_up values in LDS are 0,
-  // so they add nothing and the loaded values need no select (a select right
-  // after the load would make the compiler wait for every load in flight).
-  auto load_s2 = [&](float (&v)[KPT], int k0) {
-#pragma unroll
-    for (int q = 0; q < KPT; q += 4) {
-      const int k = k0 + ig * KPT + q;  // d is a multiple of 4
-      const float4 f = *reinterpret_cast<const float4*>(s2 + min(k, d - 4));
-      v[q] = f.x;
-      v[q + 1] = f.y;
-      v[q + 2] = f.z;
-      v[q + 3] = f.w;
-    }
-  };
-  // Every block of an IMP > 0 launch runs the importance arithmetic (a few
-  // FMAs per stage, no branch in the loop: a condition around the loads would
-  // make the compiler wait for the tile prefetch); only imp blocks write I.
-  if constexpr (IMP > 0) load_s2(s2c, 0);
-  a.load(X, d, M, d, m0, 0);
-  load_b(0);
-  a.store(As[0]);
-  store_b(Bs[0]);
-  __syncthreads();
   const int fr = lane & 15, fk = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int s = kt & 1;
-    if (kt + 1 < nk) {
-      a.load(X, d, M, d, m0, (kt + 1) * kBK);
-      load_b((kt + 1) * kBK);
-      if constexpr (IMP > 0) load_s2(s2n, (kt + 1) * kBK);
-    }
+  auto compute = [&](int slot, int buf) {
     if constexpr (IMP > 0) {
       // W_up row n0 + c_base + ir of this stage: columns ig * KPT + [0, KPT)
-      const uint16_t* wr = &Bs[s][(kBN + c_base + ir) * kLd + ig * KPT];
+      const uint16_t* wr = &Bs[buf][(kBN + c_base + ir) * kLd + ig * KPT];
 #pragma unroll
       for (int q = 0; q < KPT; q += 2) {
         const uint32_t w2 = *reinterpret_cast<const uint32_t*>(wr + q);
         const float f0 = __uint_as_float(w2 << 16), f1 = __uint_as_float(w2 & 0xffff0000u);
-        ia = fmaf(f0 * f0, s2c[q], ia);
-        ia = fmaf(f1 * f1, s2c[q + 1], ia);
+        ia = fmaf(f0 * f0, rs[slot][q], ia);
+        ia = fmaf(f1 * f1, rs[slot][q + 1], ia);
       }
     }
 #pragma unroll
     for (int kk = 0; kk < kBK; kk += 32) {
       bf16x8 fa[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = lds_frag(&As[s][(wm * 64 + i * 16 + fr) * kLd + kk + fk]);
+      for (int i = 0; i < 4; ++i) fa[i] = lds_frag(&As[buf][(wm * 64 + i * 16 + fr) * kLd + kk + fk]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const bf16x8 fg = lds_frag(&Bs[s][(wn * 32 + j * 16 + fr) * kLd + kk + fk]);
-        const bf16x8 fu = lds_frag(&Bs[s][(kBN + wn * 32 + j * 16 + fr) * kLd + kk + fk]);
+        const bf16x8 fg = lds_frag(&Bs[buf][(wn * 32 + j * 16 + fr) * kLd + kk + fk]);
+        const bf16x8 fu = lds_frag(&Bs[buf][(kBN + wn * 32 + j * 16 + fr) * kLd + kk + fk]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ag[i][j] = mfma(fa[i], fg, ag[i][j]);
@@ -206,17 +226,32 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __rest
         }
       }
     }
-    if (kt + 1 < nk) {
-      a.store(As[s ^ 1]);
-      store_b(Bs[s ^ 1]);
-      if constexpr (IMP > 0) {
+  };
+
+  const int nk = (d + kBK - 1) / kBK;
+  const int nmain = d / kBK / NS * NS;  // whole stages, in groups of NS
+  if (nmain > 0) {
 #pragma unroll
-        for (int q = 0; q < KPT; ++q) s2c[q] = s2n[q];
-      }
-    }
-    __syncthreads();
+    for (int u = 0; u < NS - 1; ++u) issue(u, u * kBK);
   }
-  if (imp) {  // block-uniform; the loop's last barrier freed As
+  for (int kt0 = 0; kt0 < nmain; kt0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int kt = kt0 + u;
+      issue((u + NS - 1) % NS, min(kt + NS - 1, nmain - 1) * kBK);  // past the end: reload (unused)
+      put(u, kt & 1);
+      __syncthreads();
+      compute(u, kt & 1);
+    }
+  }
+  for (int kt = nmain; kt < nk; ++kt) {  // the last stages, one at a time
+    issue_masked(0, kt * kBK);
+    put(0, kt & 1);
+    __syncthreads();
+    compute(0, kt & 1);
+  }
+  __syncthreads();  // every wave is done with As before it holds the importance sums
+  if (imp) {  // block-uniform
     float* red = reinterpret_cast<float*>(As[0]);
     red[ig * IC + ir] = ia;
     __syncthreads();
@@ -228,8 +263,8 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __rest
     }
   }
   // Output fragment layout: element e of lane l is row (l >> 4) * 4 + e,
-  // column l & 15 of the 16 x 16 tile.  Columns in [d_ff, ldz) come out as
-  // SiLU(0) * 0 = 0, which keeps Z's padding zero for the second GEMM.
+  // column l & 15 of the 16 x 16 tile.  Columns in [d_ff, ldz) are written as
+  // 0: Z's padding must be zero for the second GEMM.
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -238,7 +273,8 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __rest
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
-        if (m < M && n < ldz) Z[(int64_t)m * ldz + n] = bf16_rne(silu(ag[i][j][e]) * au[i][j][e]);
+        if (m < M && n < ldz)
+          Z[(int64_t)m * ldz + n] = n < d_ff ? bf16_rne(silu(ag[i][j][e]) * au[i][j][e]) : (uint16_t)0;
       }
     }
 }
@@ -248,81 +284,111 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __rest
 // columns, row-major in HBM) is written to LDS as [n][k]: thread t loads rows
 // k0 + 2 (t & 31) and the next one at columns (t >> 5) * 8 + [0, 8) and writes
 // eight 4-byte (k, k + 1) pairs; the 32 k-pairs of a half-wave cover all 64
-// banks.  Wave w covers tokens (w >> 1) * 64 + [0, 64), columns (w & 1) * 32 +
-// [0, 32).
+// banks.  BM = 128: wave w covers tokens (w >> 1) * 64 + [0, 64) and columns
+// (w & 1) * 32 + [0, 32); BM = 64 (twice the blocks, for short prompts): wave w
+// covers all 64 tokens and columns w * 16 + [0, 16).
+//
+// Pipeline: the loads of a stage go to one of NS register slots and stay in
+// flight for NS - 1 stages of MFMA work (a stage's loads take far longer than
+// its arithmetic); each stage is then written to one of two LDS buffers,
+// followed by one barrier.  Every load is unconditional: a Z row past M is
+// clamped to row M - 1 (it only feeds output rows that are not written),
+// W_downT rows past d_ff are clamped to row d_ff - 1 (they meet Z's zero
+// padding) and columns past d to the last vector (their outputs are not
+// written).  No branch or select follows a load.
+template <int BM, int NS>
 __global__ __launch_bounds__(kGThreads) void k_prompt_down(const uint16_t* __restrict__ Z, int M, int ldz,
                                                            const bf16s* __restrict__ WdT, int d_ff, int d,
                                                            float* __restrict__ Y, int mt, int nt) {
-  __shared__ __align__(16) uint16_t As[2][kBM * kLd];
+  constexpr int WM = BM / 64;            // waves along the tokens
+  constexpr int WN = 4 / WM;             // waves along the columns
+  constexpr int JF = kBN / WN / 16;      // 16-column fragments per wave
+  constexpr int PER = BM * (kBK / 8) / kGThreads;
+  __shared__ __align__(16) uint16_t As[2][BM * kLd];
   __shared__ __align__(16) uint16_t Bs[2][kBN * kLd];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int m_tile, n_tile;
   tile_of(blockIdx.x, mt * nt, mt, m_tile, n_tile);
-  const int m0 = m_tile * kBM, n0 = n_tile * kBN;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = m_tile * BM, n0 = n_tile * kBN;
+  const int wm = wave / WN, wn = wave % WN;
   const int kp = tid & 31, cb = (tid >> 5) * 8;
+  const bf16s* Zb = reinterpret_cast<const bf16s*>(Z);
+  const int nb = min(n0 + cb, d - 8);
 
-  ATile a;
-  u32x4 rb0, rb1;
-  auto load_b = [&](int k0) {
-    const int k = k0 + 2 * kp, n = n0 + cb;
-    const bool nin = n < d;
-    rb0 = (nin && k < d_ff) ? ld16(WdT + (int64_t)k * d + n) : u32x4{0u, 0u, 0u, 0u};
-    rb1 = (nin && k + 1 < d_ff) ? ld16(WdT + (int64_t)(k + 1) * d + n) : u32x4{0u, 0u, 0u, 0u};
+  u32x4 ra[NS][PER], rb0[NS], rb1[NS];
+  auto issue = [&](int slot, int k0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = tid + i * kGThreads;
+      const int m = min(m0 + (q >> 3), M - 1);
+      ra[slot][i] = ld16(Zb + (int64_t)m * ldz + k0 + (q & 7) * 8);
+    }
+    const int k = min(k0 + 2 * kp, d_ff - 1), k1 = min(k0 + 2 * kp + 1, d_ff - 1);
+    rb0[slot] = ld16(WdT + (int64_t)k * d + nb);
+    rb1[slot] = ld16(WdT + (int64_t)k1 * d + nb);
   };
-  auto store_b = [&](uint16_t* s) {
-    uint32_t* s32 = reinterpret_cast<uint32_t*>(s);
+  auto put = [&](int slot, int buf) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = tid + i * kGThreads;
+      *reinterpret_cast<u32x4*>(&As[buf][(q >> 3) * kLd + (q & 7) * 8]) = ra[slot][i];
+    }
+    uint32_t* s32 = reinterpret_cast<uint32_t*>(Bs[buf]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t lo = (rb0[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
-      const uint32_t hi = (rb1[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+      const uint32_t lo = (rb0[slot][j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+      const uint32_t hi = (rb1[slot][j >> 1] >> ((j & 1) * 16)) & 0xffffu;
       s32[((cb + j) * kLd) / 2 + kp] = lo | (hi << 16);
     }
   };
-
-  f32x4 acc[4][2];
+  f32x4 acc[4][JF];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const bf16s* Zb = reinterpret_cast<const bf16s*>(Z);
-  const int nk = (d_ff + kBK - 1) / kBK;  // Z's pitch ldz >= nk * kBK, its padding is zero
-  a.load(Zb, ldz, M, ldz, m0, 0);
-  load_b(0);
-  a.store(As[0]);
-  store_b(Bs[0]);
-  __syncthreads();
+    for (int j = 0; j < JF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fk = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int s = kt & 1;
-    if (kt + 1 < nk) {
-      a.load(Zb, ldz, M, ldz, m0, (kt + 1) * kBK);
-      load_b((kt + 1) * kBK);
-    }
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < kBK; kk += 32) {
       bf16x8 fa[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = lds_frag(&As[s][(wm * 64 + i * 16 + fr) * kLd + kk + fk]);
+      for (int i = 0; i < 4; ++i) fa[i] = lds_frag(&As[buf][(wm * 64 + i * 16 + fr) * kLd + kk + fk]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 fb = lds_frag(&Bs[s][(wn * 32 + j * 16 + fr) * kLd + kk + fk]);
+      for (int j = 0; j < JF; ++j) {
+        const bf16x8 fb = lds_frag(&Bs[buf][(wn * JF * 16 + j * 16 + fr) * kLd + kk + fk]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i][j] = mfma(fa[i], fb, acc[i][j]);
       }
     }
-    if (kt + 1 < nk) {
-      a.store(As[s ^ 1]);
-      store_b(Bs[s ^ 1]);
+  };
+
+  const int nk = (d_ff + kBK - 1) / kBK;  // Z's pitch ldz >= nk * kBK, its padding is zero
+  const int nmain = nk / NS * NS;
+  if (nmain > 0) {
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) issue(u, u * kBK);
+  }
+  for (int kt0 = 0; kt0 < nmain; kt0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int kt = kt0 + u;
+      issue((u + NS - 1) % NS, min(kt + NS - 1, nmain - 1) * kBK);  // past the end: reload (unused)
+      put(u, kt & 1);
+      __syncthreads();
+      compute(kt & 1);
     }
+  }
+  for (int kt = nmain; kt < nk; ++kt) {  // fewer than NS stages left
+    issue(0, kt * kBK);
+    put(0, kt & 1);
     __syncthreads();
+    compute(kt & 1);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 32 + j * 16 + fr;
+    for (int j = 0; j < JF; ++j) {
+      const int n = n0 + wn * JF * 16 + j * 16 + fr;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
@@ -432,17 +498,23 @@ static void launch_prompt_ffn(hipStream_t st, const void* X, int64_t n_tokens, i
       const int mt = (M + kBM - 1) / kBM;
       const int nt1 = ldz / kBN;
       if (imp && mt >= 4)
-        POP_LAUNCH(k_prompt_gateup<16>, dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
+        POP_LAUNCH((k_prompt_gateup<16, POP_GATEUP_NS>), dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
                    (const bf16s*)Wu, (int)d_ff, (uint16_t*)ws, ldz, mt, nt1, s2, I);
       else if (imp)
-        POP_LAUNCH(k_prompt_gateup<64>, dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
+        POP_LAUNCH((k_prompt_gateup<64, POP_GATEUP_NS>), dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
                    (const bf16s*)Wu, (int)d_ff, (uint16_t*)ws, ldz, mt, nt1, s2, I);
       else
-        POP_LAUNCH(k_prompt_gateup<0>, dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
+        POP_LAUNCH((k_prompt_gateup<0, POP_GATEUP_NS>), dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
                    (const bf16s*)Wu, (int)d_ff, (uint16_t*)ws, ldz, mt, nt1, (const float*)nullptr, (float*)nullptr);
       const int nt2 = (d + kBN - 1) / kBN;
-      POP_LAUNCH(k_prompt_down, dim3(mt * nt2), dim3(kGThreads), 0, st, (const uint16_t*)ws, M, ldz,
-                 (const bf16s*)WdT, (int)d_ff, (int)d, Yc, mt, nt2);
+      // short prompts: 64-token tiles, for twice the blocks (a block's K loop is latency-bound)
+      const int mt64 = (M + 63) / 64;
+      if (mt * nt2 < POP_DOWN_BM64_BELOW)
+        POP_LAUNCH((k_prompt_down<64, POP_DOWN_NS>), dim3(mt64 * nt2), dim3(kGThreads), 0, st, (const uint16_t*)ws,
+                   M, ldz, (const bf16s*)WdT, (int)d_ff, (int)d, Yc, mt64, nt2);
+      else
+        POP_LAUNCH((k_prompt_down<128, POP_DOWN_NS>), dim3(mt * nt2), dim3(kGThreads), 0, st, (const uint16_t*)ws,
+                   M, ldz, (const bf16s*)WdT, (int)d_ff, (int)d, Yc, mt, nt2);
     } else {
       const float* Xc = (const float*)X + t0 * d;
       const int mt = (M + kFT - 1) / kFT;
