@@ -330,9 +330,13 @@ def main():
             labels_dec.insert(1, "k_topk")
         labels_dense = ["k_pop_step.0(dense)", "k_pop_finish(dense)"]
     elif e == 2 and 8 <= B <= 64:   # matrix-core batched decode
-        labels_dec = (["k_gateup_mfma"] + (["k_topk"] if n_C > 0 and k > 0 else [])
-                      + ["k_gather_zlive", "k_down_mfma", "k_sum_chunks(y)"])
-        labels_dense = ["k_gateup_mfma(dense)", "k_gather_zlive(dense)", "k_down_mfma(dense)", "k_sum_chunks(y)"]
+        # the top-k of up to 4096 candidates shares the retained rows' down launch
+        topk = n_C > 0 and k > 0
+        labels_dec = (["k_gateup_lds"] + (["k_topk"] if topk and n_C > 4096 else [])
+                      + (["k_down_stream.R+topk" if topk and n_C <= 4096 else "k_down_stream.R"]
+                         if n_R > 0 or (topk and n_C <= 4096) else [])
+                      + (["k_down_stream.S"] if k > 0 else []) + ["k_sum_few(y)"])
+        labels_dense = ["k_gateup_lds(dense)", "k_down_stream(dense)", "k_sum_few(y)"]
     else:
         labels_dec = ["k_gateup"] + (["k_topk"] if n_C > 0 and k > 0 else []) + ["k_down_partial", "k_sum_chunks(y)"]
         labels_dense = ["k_gateup(dense)", "k_down_partial(dense)", "k_sum_chunks(y)"]
@@ -362,7 +366,8 @@ def main():
                 pop.pop_dense_ffn_decode(x_buf[l], Wg[l], Wu[l], WdT[l], y=y[l], ws=ws_dec)
                 marks.append((labels_dense, a, pop.lib.pop_trace_recorded()))
 
-    n_ev = L * (len(labels_pre) + len(labels_ffn) + 2) + S * L * (len(labels_dec) + len(labels_dense) + 2) + 8
+    n_ev = (L * (len(labels_pre) + len(labels_ffn) + len(labels_fused) + 3)
+            + S * L * (len(labels_dec) + len(labels_dense) + 2) + 8)
 
     def traced(flags):
         tracer = pop.Tracer(n_ev, flags)

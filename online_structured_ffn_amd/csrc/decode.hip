@@ -680,30 +680,48 @@ static DownPlan plan_down(int n_live, int B, int d, int vec) {
   return p;
 }
 
-// Live-row chunks of the matrix-core down-projection: about 2048 blocks over
-// the 64-column slices, at most kDownMaxChunk rows each (never decreasing in
-// n_live, so the value at n_live = d_ff bounds every call).
-static int down_mfma_chunks(int n_live, int d) {
+// Row chunks of the matrix-core down-projection: about `blocks` blocks over
+// the 64-column slices, at least 64 and at most kDsMaxRows rows each (never
+// decreasing in n, so the value at n = d_ff bounds every call).  The retained
+// rows aim at POP_DOWN_BLOCKS blocks; the selected rows, whose launch waits
+// for the top-k, at POP_DOWN_S_BLOCKS.
+#ifndef POP_DOWN_BLOCKS
+#define POP_DOWN_BLOCKS 1024
+#endif
+#ifndef POP_DOWN_S_BLOCKS
+#define POP_DOWN_S_BLOCKS 512
+#endif
+static int down_mfma_chunks(int n, int d, int blocks = POP_DOWN_BLOCKS) {
   const int slices = (d + 63) / 64;
-  int want = (2048 + slices - 1) / slices;
-  const int by_rows = (n_live + kDownTileRows - 1) / kDownTileRows;
+  int want = (blocks + slices - 1) / slices;
+  const int by_rows = (n + kDsRows - 1) / kDsRows;
   if (want > by_rows) want = by_rows;
-  const int least = (n_live + kDownMaxChunk - 1) / kDownMaxChunk;
+  const int least = (n + kDsMaxRows - 1) / kDsMaxRows;
   if (want < least) want = least;
   return want < 1 ? 1 : want;
+}
+
+// Rows per chunk and the number of (non-empty) chunks for n rows.
+static void down_mfma_plan(int n, int d, int blocks, int* rows_per_chunk, int* chunks) {
+  if (n <= 0) {
+    *rows_per_chunk = 1;
+    *chunks = 0;
+    return;
+  }
+  const int want = down_mfma_chunks(n, d, blocks);
+  *rows_per_chunk = (n + want - 1) / want;
+  *chunks = (n + *rows_per_chunk - 1) / *rows_per_chunk;
 }
 
 static size_t down_ws_bytes(int32_t batch, int32_t d, int32_t n_live) {
   // The chunk count only grows with n_live; bf16 (fewer column blocks) wants at least as many as fp32.
   const int c8 = down_chunks_wanted(n_live, batch, d, 8);
   const int c4 = down_chunks_wanted(n_live, batch, d, 4);
-  const int cm = down_mfma_chunks(n_live, d);
+  const int cm = down_mfma_chunks(n_live, d) + down_mfma_chunks(n_live, d, POP_DOWN_S_BLOCKS);
   int chunks = c8 > c4 ? c8 : c4;
   if (cm > chunks) chunks = cm;
   const int b = batch > 0 ? batch : 1;
-  // partial sums, and the matrix-core path's gathered bf16 z ahead of them
-  return align_up((size_t)chunks * b * d * sizeof(float), 256) +
-         align_up((size_t)b * (align_up((size_t)(n_live > 0 ? n_live : 1), 8) + kDownTileRows) * 2, 256);
+  return align_up((size_t)chunks * b * d * sizeof(float), 256);
 }
 
 struct DecodeWs {
@@ -764,22 +782,22 @@ static void launch_gateup(hipStream_t st, const void* x, int B, int d, const voi
   if (use_mfma<T>(B)) {
     if (n_A == 0) return;
     const bool identity = R == nullptr && n_C == 0;
-    const dim3 grid((n_A + 16 * kGuNT - 1) / (16 * kGuNT));
-#define POP_GU_MFMA(MT)                                                                                      \
-  if (identity)                                                                                              \
-    POP_LAUNCH((k_gateup_mfma<MT, true>), grid, dim3(256), 0, st, (const bf16s*)x, B, d, (const bf16s*)Wg,   \
-               (const bf16s*)Wu, d_ff, R, n_R, C, n_C, z, score);                                             \
-  else                                                                                                       \
-    POP_LAUNCH((k_gateup_mfma<MT, false>), grid, dim3(256), 0, st, (const bf16s*)x, B, d, (const bf16s*)Wg,  \
-               (const bf16s*)Wu, d_ff, R, n_R, C, n_C, z, score)
+    const int nb = gateup_lds_blocks(n_A);
+#define POP_GL(MT)                                                                                            \
+  if (identity)                                                                                               \
+    POP_LAUNCH((k_gateup_lds<MT, true>), dim3(nb), dim3(256), 0, st, (const bf16s*)x, B, d, (const bf16s*)Wg,  \
+               (const bf16s*)Wu, d_ff, R, n_R, C, n_C, z, score, nb);                                          \
+  else                                                                                                        \
+    POP_LAUNCH((k_gateup_lds<MT, false>), dim3(nb), dim3(256), 0, st, (const bf16s*)x, B, d, (const bf16s*)Wg, \
+               (const bf16s*)Wu, d_ff, R, n_R, C, n_C, z, score, nb)
     if (B <= 16) {
-      POP_GU_MFMA(1);
+      POP_GL(1);
     } else if (B <= 32) {
-      POP_GU_MFMA(2);
+      POP_GL(2);
     } else {
-      POP_GU_MFMA(4);
+      POP_GL(4);
     }
-#undef POP_GU_MFMA
+#undef POP_GL
     return;
   }
   int grid = (n_A + 3) / 4;
@@ -808,47 +826,70 @@ static void launch_select(hipStream_t st, const float* score, int n_C, const int
   if (n_C > 0) POP_LAUNCH(k_topk, dim3(1), dim3(kTopkThreads), 0, st, score, n_C, k, C, Q, selected);
 }
 
+// The down-projection over the live rows (R, then the selected rows).  With
+// score set, the candidate top-k runs first: it writes topk_Q and topk_sel,
+// which must then be the positions and channels the down stage reads (Q and
+// sel).  On the matrix cores the top-k (up to 4096 candidates) shares a launch
+// with the retained rows' product, and the selected rows follow.
 template <typename T>
 static void launch_down(hipStream_t st, const float* z, int B, int n_A, const void* WdT, int d, int d_ff,
                         const int32_t* R, int n_R, const int32_t* sel, const int32_t* Q, int k, float* y,
-                        float* partial) {
-  if (B == 0) return;
-  const int n_live = n_R + k;
-  if (use_mfma<T>(B)) {
-    const int n_chunks = n_live > 0 ? down_mfma_chunks(n_live, d) : 0;
-    if (n_chunks > 0) {
-      // chunks start on multiples of 8 rows (aligned A vectors); kDownMaxChunk is one too
-      const int rows_per_chunk = (int)align_up((size_t)((n_live + n_chunks - 1) / n_chunks), 8);
-      const int used = (n_live + rows_per_chunk - 1) / rows_per_chunk;
-      const dim3 grid((d + 63) / 64, used);
-      const bool identity = R == nullptr && k == 0;
-      // region: gathered bf16 z [B][ldl] (a tile of zeros past n_live), then the partial sums
-      const int ldl = (int)align_up((size_t)n_live, 8) + kDownTileRows;
-      uint16_t* zl = (uint16_t*)partial;
-      partial = (float*)((char*)partial + align_up((size_t)B * ldl * 2, 256));
-      const int pairs = B * ldl / 2;
-      POP_LAUNCH(k_gather_zlive, dim3((pairs + 255) / 256), dim3(256), 0, st, z, n_A, B, n_R, Q, n_live, ldl, zl);
-#define POP_DN_MFMA(MT)                                                                                           \
-  if (identity)                                                                                                   \
-    POP_LAUNCH((k_down_mfma<MT, true>), grid, dim3(256), 0, st, (const uint16_t*)zl, ldl, B, (const bf16s*)WdT, d,  \
-               d_ff, R, n_R, sel, n_live, rows_per_chunk, partial);                                               \
-  else                                                                                                            \
-    POP_LAUNCH((k_down_mfma<MT, false>), grid, dim3(256), 0, st, (const uint16_t*)zl, ldl, B, (const bf16s*)WdT, d, \
-               d_ff, R, n_R, sel, n_live, rows_per_chunk, partial)
-      if (B <= 16) {
-        POP_DN_MFMA(1);
-      } else if (B <= 32) {
-        POP_DN_MFMA(2);
-      } else {
-        POP_DN_MFMA(4);
-      }
-#undef POP_DN_MFMA
-      const int64_t n_out = (int64_t)B * d;
-      POP_LAUNCH(k_sum_chunks<0>, dim3((unsigned)((n_out + 31) / 32)), dim3(1024), 0, st, (const float*)partial, used,
-                 n_out, y, (unsigned int*)nullptr, 0);
-      return;
-    }
+                        float* partial, const float* score = nullptr, const int32_t* C = nullptr, int n_C = 0,
+                        int32_t* topk_Q = nullptr, int32_t* topk_sel = nullptr) {
+  const bool topk = score != nullptr && n_C > 0 && k > 0;
+  if (B == 0) {
+    if (topk) launch_select(st, score, n_C, C, k, topk_Q, topk_sel);
+    return;
   }
+  const int n_live = n_R + k;
+  if (use_mfma<T>(B) && n_live > 0) {
+    const bool identity = R == nullptr && k == 0;
+    int rpcR, nRc, rpcS, nSc;
+    down_mfma_plan(n_R, d, POP_DOWN_BLOCKS, &rpcR, &nRc);
+    down_mfma_plan(k, d, POP_DOWN_S_BLOCKS, &rpcS, &nSc);
+    const int ncol = (d + 63) / 64;
+    const bool topk_in = topk && n_C <= 4096;
+    if (topk && !topk_in) launch_select(st, score, n_C, C, k, topk_Q, topk_sel);
+    const int nb0 = topk_in ? 1 : 0;
+#define POP_DN_MFMA(MT, ID, PH, grid, rb, re, rpc, cb, nb)                                                        \
+  POP_LAUNCH((k_down_stream<MT, ID, PH>), dim3(grid), dim3(256), 0, st, z, n_A, B, (const bf16s*)WdT, d, d_ff, R, \
+             n_R, sel, Q, rb, re, rpc, cb, partial, nb, score, n_C, k, C, topk_Q, topk_sel)
+#define POP_DN_MFMA_MT(...)      \
+  if (B <= 16) {                 \
+    POP_DN_MFMA(1, __VA_ARGS__); \
+  } else if (B <= 32) {          \
+    POP_DN_MFMA(2, __VA_ARGS__); \
+  } else {                       \
+    POP_DN_MFMA(4, __VA_ARGS__); \
+  }
+    if (identity) {
+      POP_DN_MFMA_MT(true, 0, ncol * nRc, 0, n_R, rpcR, 0, 0)
+    } else {
+      if (nb0 + nRc > 0) {
+        POP_DN_MFMA_MT(false, 1, nb0 + ncol * nRc, 0, n_R, rpcR, 0, nb0)
+      }
+      if (nSc > 0) {
+        POP_DN_MFMA_MT(false, 0, ncol * nSc, n_R, n_live, rpcS, nRc, 0)
+      }
+    }
+#undef POP_DN_MFMA_MT
+#undef POP_DN_MFMA
+    const int64_t n_out = (int64_t)B * d;
+    const int nch = nRc + nSc;
+    const dim3 sgrid((unsigned)((n_out + 255) / 256));
+    if (nch <= 16) {
+      POP_LAUNCH(k_sum_few<16>, sgrid, dim3(256), 0, st, (const float*)partial, nch, n_out, y);
+    } else if (nch <= 32) {
+      POP_LAUNCH(k_sum_few<32>, sgrid, dim3(256), 0, st, (const float*)partial, nch, n_out, y);
+    } else if (nch <= 64) {
+      POP_LAUNCH(k_sum_few<64>, sgrid, dim3(256), 0, st, (const float*)partial, nch, n_out, y);
+    } else {
+      POP_LAUNCH(k_sum_chunks<0>, dim3((unsigned)((n_out + 31) / 32)), dim3(1024), 0, st, (const float*)partial, nch,
+                 n_out, y, (unsigned int*)nullptr, 0);
+    }
+    return;
+  }
+  if (topk) launch_select(st, score, n_C, C, k, topk_Q, topk_sel);
   const DownPlan p = plan_down(n_live, B, d, Vec<T>::N);
   // Identity rows only for the dense baseline (no selected rows).
 #define POP_DOWN(BT)                                                                                          \
@@ -1090,9 +1131,8 @@ extern "C" pop_status pop_decode_ffn(const void* x, int32_t batch, int32_t d, co
     return launched();
   POP_DISPATCH(dt, launch_gateup, st, x, batch, d, W_gate, W_up, d_ff, Rk, n_R, Ck, n_C, w.z, w.score);
   int32_t* sel = selected != nullptr ? selected : w.sel;  // the down stage reads the selected channels here
-  launch_select(st, w.score, n_C, Ck, k, w.Q, sel);
   POP_DISPATCH(dt, launch_down, st, w.z, batch, n_R + n_C, W_downT, d, d_ff, Rk, n_R, sel, w.Q, k, y,
-               (float*)w.down);
+               (float*)w.down, w.score, Ck, n_C, w.Q, sel);
   return launched();
 }
 

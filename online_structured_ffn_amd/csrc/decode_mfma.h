@@ -10,8 +10,10 @@
 // Fragment layout of the 16x16x32 product (lane l of a wave): A row l & 15,
 // B column l & 15, each with the 8 consecutive reduction indices
 // 8 (l >> 4) + [0, 8); accumulator element e is row 4 (l >> 4) + e, column
-// l & 15.  One load instruction thus reads 64 contiguous bytes of each of 16
-// rows.
+// l & 15.  A fragment load straight from memory would read only 64 contiguous
+// bytes of each of 16 rows, so both stages stage the weights through LDS:
+// the gate/up rows by LDS-direct loads of whole 128-byte lines, the W_downT
+// rows through registers (transposed on the way into LDS).
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -38,129 +40,194 @@ __device__ __forceinline__ uint32_t bf16_pack_rne(float lo, float hi) {
   return (a >> 16) | (b & 0xffff0000u);
 }
 
-// ---------------------------------------------------------------- gate / up
-// Block b: rows p0 = 16 NT b + [0, 16 NT) of R u C (identity rows with
-// kIdentity) in NT tiles of 16 that share the token fragments, every token.
-// Wave w reduces over k in [w * kq, (w + 1) * kq), kq a multiple of 64; the
-// four partial products meet in LDS, then z = SiLU(g) * u is written for every
-// (token, row) and, for candidate rows, the score max over tokens of |z|.
-#ifndef POP_GU_NT
-#define POP_GU_NT 1
+// ---------------------------------------------------------------- gate / up, rows streamed through LDS
+// The same product with the weight rows read by LDS-direct loads: one load
+// instruction moves 1 KB of one or a few rows (full 128-byte lines; a
+// register-fragment load can only cover 64 bytes of each of 16 rows) into a
+// ring of kGlNS LDS stages of kGlKC reduction elements, so that many stages
+// are in flight without holding registers.
+//
+// Block b takes the rows [b n_A / nb, (b + 1) n_A / nb) of R u C (at most
+// kGlRows; nb is chosen so that every block of the grid is resident at once
+// and the rows are balanced).  Wave w computes the 32-wide k-blocks
+// w (kGlKC / 128) + [0, kGlKC / 128) of each stage for both row tiles and
+// every token tile; the four partial products meet in LDS at the end.
+//
+// LDS stage layout: [matrix][row][kGlKC] bf16.  Row rho's 16-byte chunk c of
+// the stage sits in slot c ^ (rho & 15) (c, slot < kGlKC / 8), so the sixteen
+// lanes of a fragment read (rows 16 t + [0, 16), one chunk) hit distinct
+// banks.  The load lanes pick their source chunk accordingly: lane slot s of
+// row rho loads chunk s ^ (rho & 15).
+#ifndef POP_GL_KC
+#define POP_GL_KC 256
 #endif
-constexpr int kGuNT = POP_GU_NT;  // row tiles per block
+#ifndef POP_GL_NS
+#define POP_GL_NS 3
+#endif
+constexpr int kGlRows = 24;                          // rows per block at most
+constexpr int kGlKC = POP_GL_KC;                     // reduction elements per stage (128 or 256)
+constexpr int kGlNS = POP_GL_NS;                     // stages in the LDS ring
+constexpr int kGlSlots = kGlKC / 8;                  // 16-byte chunks per row and stage
+constexpr int kGlRowsPerLoad = 64 / kGlSlots;        // rows one load instruction covers
+constexpr int kGlLoads = 2 * kGlRows / kGlRowsPerLoad / 4;  // load instructions per wave and stage
+constexpr int kGlStage = 2 * kGlRows * kGlKC;        // bf16 elements per stage
+constexpr int kGlKB = kGlKC / 128;                   // 32-wide k-blocks per wave and stage
+static_assert(kGlKC == 128 || kGlKC == 256, "stage width");
+static_assert((2 * kGlRows / kGlRowsPerLoad) % 4 == 0, "loads split evenly over the waves");
+static_assert(kGlNS >= 2 && kGlNS <= 4, "ring depth");
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// [3:0] and [15:14], expcnt and lgkmcnt at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// The host's grid for k_gateup_lds: every block resident (two per CU) and at
+// most kGlRows rows each.
+__host__ __device__ constexpr int gateup_lds_blocks(int n_A) {
+  return (n_A + kGlRows - 1) / kGlRows > 512 ? (n_A + kGlRows - 1) / kGlRows : 512;
+}
 
 template <int MT, bool kIdentity>
-__global__ __launch_bounds__(256) void k_gateup_mfma(const bf16s* __restrict__ x, int B, int d,
-                                                     const bf16s* __restrict__ Wg, const bf16s* __restrict__ Wu,
-                                                     int d_ff, const int32_t* __restrict__ R, int n_R,
-                                                     const int32_t* __restrict__ C, int n_C, float* __restrict__ z,
-                                                     float* __restrict__ score) {
-  constexpr int NT = kGuNT;
-  __shared__ f32x4_t red[3][2 * MT * NT][64];
-  // The wave index as a scalar: the K range and every loop condition below
-  // are then uniform branches, not exec-mask regions.
+__global__ __launch_bounds__(256) void k_gateup_lds(const bf16s* __restrict__ x, int B, int d,
+                                                    const bf16s* __restrict__ Wg, const bf16s* __restrict__ Wu,
+                                                    int d_ff, const int32_t* __restrict__ R, int n_R,
+                                                    const int32_t* __restrict__ C, int n_C, float* __restrict__ z,
+                                                    float* __restrict__ score, int nb) {
+  constexpr int NT = 2;  // row tiles (kGlRows <= 32)
+  __shared__ __align__(16) uint16_t smem[kGlNS * kGlStage];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int n_A = n_R + n_C;
-  const int p0 = blockIdx.x * 16 * NT;
-  // this lane's weight rows (rows past n_A repeat the last one; never stored)
-  const bf16s* wg[NT];
-  const bf16s* wu[NT];
+  const int r0 = (int)((int64_t)blockIdx.x * n_A / nb);
+  const int nr = (int)((int64_t)(blockIdx.x + 1) * n_A / nb) - r0;
+  if (nr <= 0) return;  // block-uniform
+  // load instruction m of this wave: j = wave + 4 m covers matrix j / jm,
+  // rows kGlRowsPerLoad (j % jm) + [0, kGlRowsPerLoad) (past nr: the last row)
+  constexpr int jm = kGlRows / kGlRowsPerLoad;
+  const bf16s* src[kGlLoads];  // the row
+  int co[kGlLoads];             // this lane's chunk offset in the stage
+  int lds_row[kGlLoads];
+  const int slot = lane % kGlSlots;
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int p = min(p0 + 16 * n + r, n_A - 1);
+  for (int m = 0; m < kGlLoads; ++m) {
+    const int j = wave + 4 * m;
+    const int rho = kGlRowsPerLoad * (j % jm) + lane / kGlSlots;
+    const int p = r0 + min(rho, nr - 1);
     const int ch = kIdentity ? p : clamp_ch(p < n_R ? R[p] : C[p - n_R], d_ff);
-    wg[n] = Wg + (int64_t)ch * d;
-    wu[n] = Wu + (int64_t)ch * d;
+    src[m] = (j < jm ? Wg : Wu) + (int64_t)ch * d;
+    co[m] = 8 * (slot ^ (rho & 15));
+    lds_row[m] = (j / jm) * kGlRows + kGlRowsPerLoad * (j % jm);  // first row of the instruction
   }
-  // this lane's token rows of x
+  // this lane's token rows (tokens past B read token 0: never stored)
   const bf16s* xr[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int tok = 16 * t + r;
-    xr[t] = x + (int64_t)(tok < B ? tok : 0) * d;
-  }
-  const int kq = ((d + 255) / 256) * 64;  // per-wave share, a multiple of 64
-  const int kb = wave * kq, ke = min(d, kb + kq);
+  for (int t = 0; t < MT; ++t) xr[t] = x + (int64_t)(16 * t + r < B ? 16 * t + r : 0) * d;
+  const int nst = (d + kGlKC - 1) / kGlKC;
+  u32x4 xs[kGlNS][kGlKB][MT];
+  // stage st into ring slot q: this wave's token fragments, then its share of the rows
+  auto issue = [&](int st, u32x4 (&xq)[kGlKB][MT], int q) {
+    const int kbase = st * kGlKC;
+#pragma unroll
+    for (int i = 0; i < kGlKB; ++i) {
+      const int k = min(kbase + 32 * (kGlKB * wave + i) + 8 * g, d - 8);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) xq[i][t] = ld16(xr[t] + k);
+    }
+#pragma unroll
+    for (int m = 0; m < kGlLoads; ++m) {
+      // chunks past the row's end re-read its last one (their token operands are zero)
+      const bf16s* a = src[m] + min(kbase + co[m], d - 8);
+      __builtin_amdgcn_global_load_lds((const void*)a,
+                                       (__attribute__((address_space(3))) void*)(smem + q * kGlStage +
+                                                                                 lds_row[m] * kGlKC),
+                                       16, 0, 0);
+    }
+  };
   f32x4_t ag[NT][MT], au[NT][MT];
 #pragma unroll
   for (int n = 0; n < NT; ++n)
 #pragma unroll
     for (int t = 0; t < MT; ++t) ag[n][t] = au[n][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  // One 64-wide step: the lane's 16-byte vectors at k0 + 8 g and k0 + 32 + 8 g
-  // of each gate and up row and of every token row; token vectors past ke are
-  // zero (d % 8 == 0, so a vector is all in or all out) and the weight loads
-  // stay in the row.
-  // The buffers hold the raw loads; the zeroing of vectors past ke happens at
-  // use, so no wait is forced between issuing a step's loads and using the
-  // previous step's (the memory counter is in order: an early wait on the
-  // newest load would drain the whole pipeline).  Tokens past B read token 0's
-  // row: their products are never stored.
-  struct Step {
-    u32x4 g0[NT], g1[NT], u0[NT], u1[NT], xa[MT], xb[MT];
-    bool on_a, on_b;
-  };
-  auto load = [&](Step& S, int k0, bool valid) {
-    const int ka = k0 + 8 * g, kb8 = ka + 32;
-    S.on_a = valid && ka < ke;
-    S.on_b = valid && kb8 < ke;
-    const int ca = S.on_a ? ka : 0, cb = S.on_b ? kb8 : 0;
+  auto compute = [&](int st, const u32x4 (&xq)[kGlKB][MT], int q) {
+    const uint16_t* base = smem + q * kGlStage;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      S.g0[n] = ld16(wg[n] + ca);  // plain loads measured faster than non-temporal here
-      S.g1[n] = ld16(wg[n] + cb);
-      S.u0[n] = ld16(wu[n] + ca);
-      S.u1[n] = ld16(wu[n] + cb);
-    }
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      S.xa[t] = ld16(xr[t] + ca);
-      S.xb[t] = ld16(xr[t] + cb);
-    }
-  };
-  auto use = [&](const Step& S) {
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const u32x4 xa = S.on_a ? S.xa[t] : zero, xb = S.on_b ? S.xb[t] : zero;
+    for (int i = 0; i < kGlKB; ++i) {
+      const int kb = kGlKB * wave + i;
+      const bool on = st * kGlKC + 32 * kb + 8 * g < d;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        ag[n][t] = mfma16(xa, S.g0[n], ag[n][t]);
-        ag[n][t] = mfma16(xb, S.g1[n], ag[n][t]);
-        au[n][t] = mfma16(xa, S.u0[n], au[n][t]);
-        au[n][t] = mfma16(xb, S.u1[n], au[n][t]);
+        const int row = min(16 * n + r, kGlRows - 1);
+        const int sl = (4 * kb + g) ^ (row & 15);
+        const u32x4 bg = *reinterpret_cast<const u32x4*>(base + row * kGlKC + 8 * sl);
+        const u32x4 bu = *reinterpret_cast<const u32x4*>(base + (kGlRows + row) * kGlKC + 8 * sl);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const u32x4 a = on ? xq[i][t] : zero;
+          ag[n][t] = mfma16(a, bg, ag[n][t]);
+          au[n][t] = mfma16(a, bu, au[n][t]);
+        }
       }
     }
   };
-  // A ring of DEPTH steps in flight.  The loop body has no branch: the step
-  // count is padded to a multiple of DEPTH, steps past the last one re-read it
-  // (cache hits) with their operands zeroed, and the scheduling barriers keep
-  // each prefetch ahead of the products it hides.
-  constexpr int DEPTH = MT <= 2 ? 4 : 2;
-  const int nsteps = ke > kb ? (ke - kb + 63) / 64 : 0;
-  const int last = nsteps > 0 ? nsteps - 1 : 0;
-  auto kstep = [&](int st) { return kb + 64 * min(st, last); };
-  Step S[DEPTH];
-  if (nsteps > 0) {
+  // Ring: stages 0 .. kGlNS - 2 ahead; step st waits for its own loads (the
+  // loads of the later stages already issued may stay in flight), passes a
+  // barrier (every wave's share landed, every wave done with stage st - 1),
+  // refills stage st - 1's slot with stage st + kGlNS - 1, then computes.
+  // The stage count is padded to a multiple of kGlNS (stages past the row's
+  // end load its last chunk and compute with zero token operands) and the
+  // body is straight-line: the compiler then counts the memory instructions
+  // in flight exactly and waits for each token fragment no longer than it
+  // must.
+  constexpr int kPer = kGlKB * MT + kGlLoads;  // vector-memory instructions per stage
+  const int T = (nst + kGlNS - 1) / kGlNS * kGlNS;
+  auto step = [&](int st, auto jc, auto issuec, auto laterc) {
+    constexpr int j = decltype(jc)::value;
+    wait_vmcnt<decltype(laterc)::value * kPer>();
+    // the empty asm statements keep every LDS access on its side of the barrier
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(issuec)::value) issue(st + kGlNS - 1, xs[(j + kGlNS - 1) % kGlNS], (j + kGlNS - 1) % kGlNS);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(st, xs[j], j);
+  };
+  using std::integral_constant;
 #pragma unroll
-    for (int j = 0; j < DEPTH - 1; ++j) load(S[j], kstep(j), j < nsteps);
-    for (int st = 0; st < nsteps; st += DEPTH) {
-#pragma unroll
-      for (int j = 0; j < DEPTH; ++j) {
-        const int ahead = st + j + DEPTH - 1;
-        load(S[(j + DEPTH - 1) % DEPTH], kstep(ahead), ahead < nsteps);
-        __builtin_amdgcn_sched_barrier(0);
-        use(S[j]);
-      }
-    }
+  for (int j = 0; j < kGlNS - 1; ++j) issue(j, xs[j], j);
+  for (int s0 = 0; s0 < T - kGlNS; s0 += kGlNS) {
+    step(s0, integral_constant<int, 0>(), integral_constant<bool, true>(), integral_constant<int, kGlNS - 2>());
+    step(s0 + 1, integral_constant<int, 1>(), integral_constant<bool, true>(), integral_constant<int, kGlNS - 2>());
+    if constexpr (kGlNS > 2)
+      step(s0 + 2, integral_constant<int, 2>(), integral_constant<bool, true>(), integral_constant<int, kGlNS - 2>());
+    if constexpr (kGlNS > 3)
+      step(s0 + 3, integral_constant<int, 3>(), integral_constant<bool, true>(), integral_constant<int, kGlNS - 2>());
   }
+  {  // the last group issues only its first step's refill
+    const int s0 = T - kGlNS;
+    step(s0, integral_constant<int, 0>(), integral_constant<bool, true>(), integral_constant<int, kGlNS - 2>());
+    step(s0 + 1, integral_constant<int, 1>(), integral_constant<bool, false>(), integral_constant<int, kGlNS - 2>());
+    if constexpr (kGlNS > 2)
+      step(s0 + 2, integral_constant<int, 2>(), integral_constant<bool, false>(), integral_constant<int, kGlNS - 3>());
+    if constexpr (kGlNS > 3)
+      step(s0 + 3, integral_constant<int, 3>(), integral_constant<bool, false>(), integral_constant<int, 0>());
+  }
+  // the four waves' partial products meet in the (now idle) stage buffers
+  wait_vmcnt<0>();
+  __syncthreads();
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);  // [wave - 1][2 NT MT][64]
+  static_assert(3 * 2 * NT * 4 * 64 * 16 <= kGlNS * kGlStage * 2, "reduction fits the ring");
   if (wave > 0) {
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        red[wave - 1][2 * (n * MT + t)][lane] = ag[n][t];
-        red[wave - 1][2 * (n * MT + t) + 1][lane] = au[n][t];
+        red[((wave - 1) * 2 * NT * MT + 2 * (n * MT + t)) * 64 + lane] = ag[n][t];
+        red[((wave - 1) * 2 * NT * MT + 2 * (n * MT + t) + 1) * 64 + lane] = au[n][t];
       }
   }
   __syncthreads();
@@ -168,146 +235,229 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(const bf16s* __restrict__ x
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     float smax = 0.f;
-    const int prow = p0 + 16 * n + r;
+    const int rl = 16 * n + r;
+    const int prow = r0 + rl;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       f32x4_t gs = ag[n][t], us = au[n][t];
 #pragma unroll
       for (int w = 0; w < 3; ++w) {
-        gs += red[w][2 * (n * MT + t)][lane];
-        us += red[w][2 * (n * MT + t) + 1][lane];
+        gs += red[(w * 2 * NT * MT + 2 * (n * MT + t)) * 64 + lane];
+        us += red[(w * 2 * NT * MT + 2 * (n * MT + t) + 1) * 64 + lane];
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tok = 16 * t + 4 * g + e;
         if (tok < B) {
           const float zz = silu(gs[e]) * us[e];
-          if (prow < n_A) z[(int64_t)tok * n_A + prow] = zz;
+          if (rl < nr) z[(int64_t)tok * n_A + prow] = zz;
           smax = fmaxf(smax, fabsf(zz));
         }
       }
     }
-    // max over the four lane groups (tokens) of the same row
     smax = fmaxf(smax, __shfl_xor(smax, 16));
     smax = fmaxf(smax, __shfl_xor(smax, 32));
-    if (g == 0 && prow >= n_R && prow < n_A && score != nullptr) score[prow - n_R] = smax;
+    if (g == 0 && rl < nr && prow >= n_R && score != nullptr) score[prow - n_R] = smax;
   }
 }
 
-// ---------------------------------------------------------------- down
-// zl[b][q] = bf16(z[b][column of live row q]) for q < n_live (R first, then the
-// selected channels at n_R + pos), zero up to the row pitch ldl (a multiple of
-// 8 at least one tile past n_live): the down-projection's A operand in live
-// order, gathered once.
-__global__ __launch_bounds__(256) void k_gather_zlive(const float* __restrict__ z, int n_A, int B, int n_R,
-                                                      const int32_t* __restrict__ pos, int n_live, int ldl,
-                                                      uint16_t* __restrict__ zl) {
-  const int i = blockIdx.x * 256 + threadIdx.x;  // a pair of columns
-  const int q = 2 * (i % (ldl / 2)), b = i / (ldl / 2);
-  if (b >= B) return;
-  const float* zr = z + (int64_t)b * n_A;
-  auto col = [&](int qq) { return qq < n_R ? qq : min(n_R + max(pos[qq - n_R], 0), n_A - 1); };
-  const float a = q < n_live ? zr[col(q)] : 0.f;
-  const float c = q + 1 < n_live ? zr[col(q + 1)] : 0.f;
-  reinterpret_cast<uint32_t*>(zl + (int64_t)b * ldl)[q / 2] = bf16_pack_rne(a, c);
-}
+// ---------------------------------------------------------------- down, streamed
+// Block (slice, chunk): output columns slice * 64 + [0, 64) over the live
+// rows q0 = row_begin + chunk * rows_per_chunk + [0, rows_per_chunk)
+// (clipped at row_end; at most kDsMaxRows), taken as sub-chunks of kDsRows
+// rows in a pipelined loop that keeps the products of all sub-chunks in the
+// accumulators: one partial sum per block, however long its range.
+//   * The range's channels and z columns go to LDS first (one round trip);
+//     live row q is (R[q], q) for q < n_R and (sel[q - n_R], n_R + pos[q - n_R])
+//     after, or (q, q) with kIdentity.
+//   * A ring of kDsNS sub-chunks of loads is in flight in registers: each
+//     thread's two rows (pairs 2 (t >> 3) + [0, 2), eight lanes per row read
+//     its 128 contiguous bytes of the slice) and the z values of its row pair
+//     for its tokens.
+//   * Each sub-chunk goes to LDS (double-buffered, one barrier per
+//     sub-chunk): rows transposed as (row, row + 1) pairs into Bt[column][row]
+//     with the pair index XOR-swizzled by 4 ((column >> 3) & 7) (conflict-free
+//     writes), z rounded to bf16 into zs[token][row]; then the four waves run
+//     their 16 columns' products.
+// Rows past the range read its last row with z = 0; columns past d and tokens
+// past B read valid memory and produce outputs that are never stored.
+//
+// PHASE 1: blocks [0, nb0) run the candidate top-k instead (one block), so it
+// overlaps the retained rows' product; the selected rows follow in a PHASE 0
+// launch.
+#ifndef POP_DS_NS
+#define POP_DS_NS 4
+#endif
+constexpr int kDsRows = 64;                // rows per sub-chunk
+constexpr int kDsMaxRows = 1024;           // rows per block at most
+constexpr int kDsNS = POP_DS_NS;           // sub-chunks of loads in flight
+constexpr int kDsLd = kDsRows + 8;         // Bt and zs pitch in bf16 (144 bytes)
+static_assert(kDsNS >= 2 && kDsNS <= 4, "ring depth");
 
-// Block (cs, c): output columns cs * 64 + [0, 64) over the live rows
-// [c * rows_per_chunk, ...) (R first, then the selected channels; at most
-// kDownMaxChunk rows, a multiple of 8).  Every W_downT load of the chunk is
-// issued at once (the 128 contiguous bytes of each row); the rows then go to
-// LDS transposed as (row, row + 1) pairs — thread t takes row pairs 32 i +
-// (t & 31) at columns (t >> 5) * 8 + [0, 8), so a half-wave's 32 pairs cover
-// all 64 banks.  The A operand comes straight from zl (16-byte vectors of 8
-// live rows).  Wave w owns the 16 columns 16 w + [0, 16).  Writes
-// partial[c][token][col].
-constexpr int kDownMaxChunk = 256;                 // live rows per block
-constexpr int kDownTileRows = kDownMaxChunk;        // padding of zl past n_live
-constexpr int kDownLd = kDownMaxChunk + 8;         // Bt pitch in bf16 (528 bytes)
-constexpr int kDownPairs = kDownMaxChunk / 64;     // row pairs per thread
+template <int MT>
+struct DsShared {
+  uint16_t Bt[2][64 * kDsLd];       // [column][row of the sub-chunk]
+  uint16_t zs[2][16 * MT * kDsLd];  // [token][row of the sub-chunk]
+  int rch[kDsMaxRows];
+  int zcol[kDsMaxRows];
+};
 
-template <int MT, bool kIdentity>
-__global__ __launch_bounds__(256) void k_down_mfma(const uint16_t* __restrict__ zl, int ldl, int B,
-                                                   const bf16s* __restrict__ WdT, int d, int d_ff,
-                                                   const int32_t* __restrict__ R, int n_R,
-                                                   const int32_t* __restrict__ sel, int n_live, int rows_per_chunk,
-                                                   float* __restrict__ partial) {
-  __shared__ __align__(16) uint16_t Bt[64 * kDownLd];  // [column][row of the chunk]
-  __shared__ int rch[kDownMaxChunk];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, g = lane >> 4;
-  const int c0 = blockIdx.x * 64;
-  const int q0 = blockIdx.y * rows_per_chunk;
-  const int nrows = max(0, min(n_live, q0 + rows_per_chunk) - q0);
-  // channel of every live row of the chunk
-  for (int i = tid; i < kDownMaxChunk; i += 256) {
-    int chv = 0;
-    if (i < nrows) {
-      const int q = q0 + i;
-      chv = kIdentity ? q : clamp_ch(q < n_R ? R[q] : sel[q - n_R], d_ff);
+template <int MT, bool kIdentity, int PHASE>
+__global__ __launch_bounds__(256) void k_down_stream(const float* __restrict__ z, int n_A, int B,
+                                                     const bf16s* __restrict__ WdT, int d, int d_ff,
+                                                     const int32_t* __restrict__ R, int n_R,
+                                                     const int32_t* __restrict__ sel, const int32_t* __restrict__ pos,
+                                                     int row_begin, int row_end, int rows_per_chunk, int chunk_base,
+                                                     float* __restrict__ partial, int nb0,
+                                                     const float* __restrict__ score, int n_C, int k,
+                                                     const int32_t* __restrict__ C, int32_t* __restrict__ Q,
+                                                     int32_t* __restrict__ S) {
+  using DS = DsShared<MT>;
+  using TS = SelShared<256, 4096>;
+  constexpr size_t kSmem = sizeof(DS) > (PHASE == 1 ? sizeof(TS) : 0) ? sizeof(DS) : sizeof(TS);
+  __shared__ __align__(16) unsigned char smem[kSmem];
+  if constexpr (PHASE == 1) {
+    if ((int)blockIdx.x < nb0) {
+      topk_block(score, n_C, k, C, Q, S, *reinterpret_cast<TS*>(smem));
+      return;
     }
-    rch[i] = chv;
+  }
+  DS& sh = *reinterpret_cast<DS*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int ncol = (d + 63) / 64;
+  const int idx = (int)blockIdx.x - (PHASE == 1 ? nb0 : 0);
+  const int c0 = (idx % ncol) * 64;
+  const int cl = idx / ncol;
+  const int q0 = row_begin + cl * rows_per_chunk;
+  const int nrows = min(row_end, q0 + rows_per_chunk) - q0;  // >= 1: the host launches no empty chunk
+  {  // every index load in flight at once (clamped to the range; stores masked)
+    constexpr int kPer = kDsMaxRows / 256;
+    int a[kPer], b[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int q = q0 + min(tid + 256 * u, nrows - 1);
+      if (kIdentity) {
+        a[u] = q;
+        b[u] = q;
+      } else if (q < n_R) {  // a chunk holds retained or selected rows only
+        a[u] = R[q];
+        b[u] = q;
+      } else {
+        a[u] = sel[q - n_R];
+        b[u] = pos[q - n_R];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + 256 * u;
+      if (i < nrows) {
+        sh.rch[i] = kIdentity ? a[u] : clamp_ch(a[u], d_ff);
+        sh.zcol[i] = (kIdentity || q0 < n_R) ? b[u] : min(n_R + max(b[u], 0), n_A - 1);
+      }
+    }
   }
   __syncthreads();
-  const int kp = tid & 31, cc = (tid >> 5) * 8;
-  const bool col_on = c0 + cc < d;  // d % 8 == 0
-  const int col_c = col_on ? c0 + cc : d - 8;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  // every row pair of the chunk (clamped, unconditional loads; zeroed below)
-  u32x4 va[kDownPairs], vb[kDownPairs];
+  // loads: row pair kp (rows 2 kp, 2 kp + 1 of a sub-chunk), columns cc + [0, 8)
+  const int kp = tid >> 3, cc = (tid & 7) * 8;
+  const bf16s* wcol = WdT + min(c0 + cc, d - 8);
+  // z: row pair zp (rows 2 zp, 2 zp + 1), tokens zt + 8 m
+  const int zp = tid & 31, zt = tid >> 5;
+  struct Ld {
+    u32x4 va, vb;
+    float za[2 * MT], zb[2 * MT];
+  };
+  auto issue = [&](int i, Ld& L) {
+    const int ra = min(kDsRows * i + 2 * kp, nrows - 1), rb = min(kDsRows * i + 2 * kp + 1, nrows - 1);
+    L.va = ld16(wcol + (int64_t)sh.rch[ra] * d);
+    L.vb = ld16(wcol + (int64_t)sh.rch[rb] * d);
+    const int ca = sh.zcol[min(kDsRows * i + 2 * zp, nrows - 1)];
+    const int cb = sh.zcol[min(kDsRows * i + 2 * zp + 1, nrows - 1)];
 #pragma unroll
-  for (int h = 0; h < kDownPairs; ++h) {
-    const int qa = 64 * h + 2 * kp;
-    va[h] = ld16(WdT + (int64_t)rch[qa] * d + col_c);  // plain loads: measured faster than non-temporal
-    vb[h] = ld16(WdT + (int64_t)rch[qa + 1] * d + col_c);
-  }
-  // the A fragments: tokens past B read token 0 (their sums are never
-  // stored); q0 is a multiple of 8 and zl carries kDownTileRows rows of zero
-  // padding past n_live, so the vectors are aligned and inside the row
-  const uint16_t* zrow[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) zrow[t] = zl + (int64_t)min(16 * t + r, B - 1) * ldl + q0 + 8 * g;
-  const int nk = (nrows + 31) / 32;  // 32-row product steps
-  u32x4 fa[MT][kDownMaxChunk / 32];
-#pragma unroll
-  for (int t = 0; t < MT; ++t)
-#pragma unroll
-    for (int kk = 0; kk < kDownMaxChunk / 32; ++kk)
-      fa[t][kk] = kk < nk ? *reinterpret_cast<const u32x4*>(zrow[t] + 32 * kk) : zero;
-  uint32_t* b32 = reinterpret_cast<uint32_t*>(Bt);
-#pragma unroll
-  for (int h = 0; h < kDownPairs; ++h) {
-    if (64 * h >= nrows) continue;  // rows past 32 * nk are never read
-    const int qa = 64 * h + 2 * kp;
-    const u32x4 ta = (col_on && qa < nrows) ? va[h] : zero;
-    const u32x4 tb = (col_on && qa + 1 < nrows) ? vb[h] : zero;
+    for (int m = 0; m < 2 * MT; ++m) {
+      const float* zr = z + (int64_t)min(zt + 8 * m, B - 1) * n_A;
+      L.za[m] = zr[ca];
+      L.zb[m] = zr[cb];
+    }
+  };
+  auto put = [&](int i, const Ld& L, int buf) {
+    uint32_t* b32 = reinterpret_cast<uint32_t*>(sh.Bt[buf]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t lo = (ta[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
-      const uint32_t hi = (tb[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
-      b32[((cc + j) * kDownLd) / 2 + 32 * h + kp] = lo | (hi << 16);
+      const int col = cc + j;
+      const uint32_t lo = (L.va[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+      const uint32_t hi = (L.vb[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+      b32[col * (kDsLd / 2) + (kp ^ (4 * ((col >> 3) & 7)))] = lo | (hi << 16);
     }
-  }
-  __syncthreads();
+    const bool on0 = kDsRows * i + 2 * zp < nrows, on1 = kDsRows * i + 2 * zp + 1 < nrows;
+    uint32_t* z32 = reinterpret_cast<uint32_t*>(sh.zs[buf]);
+#pragma unroll
+    for (int m = 0; m < 2 * MT; ++m)
+      z32[(zt + 8 * m) * (kDsLd / 2) + zp] = bf16_pack_rne(on0 ? L.za[m] : 0.f, on1 ? L.zb[m] : 0.f);
+  };
   f32x4_t acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int bcol = wave * 16 + r;
+  const int bsw = 4 * ((bcol >> 3) & 7);
+  auto compute = [&](int buf) {
 #pragma unroll
-  for (int kk = 0; kk < kDownMaxChunk / 32; ++kk) {
-    if (kk < nk) {
-      const u32x4 fb = *reinterpret_cast<const u32x4*>(&Bt[(wave * 16 + r) * kDownLd + 32 * kk + 8 * g]);
+    for (int kk = 0; kk < kDsRows / 32; ++kk) {
+      const uint32_t* b32 = reinterpret_cast<const uint32_t*>(sh.Bt[buf]);
+      const u32x4 fb = *reinterpret_cast<const u32x4*>(b32 + bcol * (kDsLd / 2) + ((16 * kk + 4 * g) ^ bsw));
 #pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = mfma16(fa[t][kk], fb, acc[t]);
+      for (int t = 0; t < MT; ++t) {
+        const u32x4 fa = *reinterpret_cast<const u32x4*>(&sh.zs[buf][(16 * t + r) * kDsLd + 32 * kk + 8 * g]);
+        acc[t] = mfma16(fa, fb, acc[t]);
+      }
+    }
+  };
+  // Straight-line ring (the count of sub-chunks padded to a multiple of kDsNS;
+  // padded ones carry z = 0): the compiler then waits for each sub-chunk's
+  // loads and no more.
+  const int nsub = (nrows + kDsRows - 1) / kDsRows;
+  const int T = (nsub + kDsNS - 1) / kDsNS * kDsNS;
+  Ld ring[kDsNS];
+  auto step = [&](int i, auto jc, auto issuec) {
+    constexpr int j = decltype(jc)::value;
+    // the scheduling barriers keep each step's unpacking after the loads it
+    // waits for were given their time (no hoisting of a later step's work)
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(issuec)::value) issue(i + kDsNS - 1, ring[(j + kDsNS - 1) % kDsNS]);
+    __builtin_amdgcn_sched_barrier(0);
+    put(i, ring[j], j & 1);
+    __syncthreads();
+    compute(j & 1);
+  };
+  static_assert(kDsNS % 2 == 0, "the LDS buffer of step i is i & 1 = j & 1");
+  using std::integral_constant;
+#pragma unroll
+  for (int j = 0; j < kDsNS - 1; ++j) issue(j, ring[j]);
+  for (int i0 = 0; i0 < T - kDsNS; i0 += kDsNS) {
+    step(i0, integral_constant<int, 0>(), integral_constant<bool, true>());
+    step(i0 + 1, integral_constant<int, 1>(), integral_constant<bool, true>());
+    if constexpr (kDsNS > 2) {
+      step(i0 + 2, integral_constant<int, 2>(), integral_constant<bool, true>());
+      step(i0 + 3, integral_constant<int, 3>(), integral_constant<bool, true>());
     }
   }
-  const int col = c0 + wave * 16 + r;
+  {
+    const int i0 = T - kDsNS;
+    step(i0, integral_constant<int, 0>(), integral_constant<bool, true>());
+    step(i0 + 1, integral_constant<int, 1>(), integral_constant<bool, false>());
+    if constexpr (kDsNS > 2) {
+      step(i0 + 2, integral_constant<int, 2>(), integral_constant<bool, false>());
+      step(i0 + 3, integral_constant<int, 3>(), integral_constant<bool, false>());
+    }
+  }
+  const int col = c0 + bcol;
   if (col < d) {
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tok = 16 * t + 4 * g + e;
-        if (tok < B) partial[((int64_t)blockIdx.y * B + tok) * d + col] = acc[t][e];
+        if (tok < B) partial[((int64_t)(chunk_base + cl) * B + tok) * d + col] = acc[t][e];
       }
   }
 }

@@ -367,7 +367,7 @@ __device__ __forceinline__ void sel_eq_before(const uint32_t (&v)[EM], int E, in
 // ascending on ties), written in ascending order as positions into C and, when
 // `selected` is not NULL, as channels C[position].  One workgroup; n <= MAXN.
 template <int NTH, int MAXN>
-__device__ void topk_block(const float* __restrict__ score, int n, int k, const int32_t* __restrict__ C,
+__device__ __forceinline__ void topk_block(const float* __restrict__ score, int n, int k, const int32_t* __restrict__ C,
                            int32_t* __restrict__ positions, int32_t* __restrict__ selected, SelShared<NTH, MAXN>& sh) {
   constexpr int EM = SelShared<NTH, MAXN>::kPerThread;
   if (n <= 0 || k <= 0) return;
@@ -488,6 +488,26 @@ __global__ __launch_bounds__(1024) void k_sum_chunks(const float* __restrict__ p
     for (int j = 1; j < 32; ++j) t += part[j][o];
     out[i] = t;
   }
+}
+
+// out[i] = sum_{c < n_chunks} partial[c * n_out + i] in chunk order, one
+// thread per output with all n_chunks <= MAXC loads in flight at once (padded
+// loads re-read the last chunk and add nothing): for the few dozen chunks of
+// the matrix-core down-projection, where the grouped sum above would leave
+// most of its threads idle.
+template <int MAXC>
+__global__ __launch_bounds__(256) void k_sum_few(const float* __restrict__ partial, int n_chunks, int64_t n_out,
+                                                 float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_out) return;
+  float a[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) a[c] = partial[(int64_t)min(c, n_chunks - 1) * n_out + i];
+  float s = a[0];
+#pragma unroll
+  for (int c = 1; c < MAXC; ++c)
+    if (c < n_chunks) s += a[c];
+  out[i] = s;
 }
 
 }  // namespace pop

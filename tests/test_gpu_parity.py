@@ -139,6 +139,9 @@ DEC_CASES = [
     ("bf16_b17_mfma", 30, 264, 1000, 17, "bf16", 0.3, 0.1),
     ("bf16_b40_mfma", 30, 1032, 1501, 40, "bf16", 0.299, 0.1),
     ("bf16_b64_mfma", 30, 520, 700, 64, "bf16", 0.5, 0.1),
+    # no retained rows: 4000 candidates (top-k alone in the retained launch), 6000 (top-k as its own launch)
+    ("bf16_b16_mfma_only_C", 20, 264, 4000, 16, "bf16", 0.2, 0.8),
+    ("bf16_b16_mfma_wide_C", 20, 264, 6000, 16, "bf16", 0.2, 0.8),
     ("bf16_b65_fma", 30, 256, 600, 65, "bf16", 0.3, 0.1),
 ]
 
@@ -247,10 +250,12 @@ def test_full_size_layer(wname, layer, steps):
     _decode_case(X, xs, wts, w.dtype, w.r, w.gamma, w.name)
 
 
-def test_stages_compose_bitwise():
-    """The stage entry points run the same kernels as the composite calls."""
-    say("[stages] importance + select == partition; gate/up + select + down == decode")
-    c = synth.random_case(51, 100, 1032, 2900, 3, "bf16")
+@pytest.mark.parametrize("batch", [3, 16])
+def test_stages_compose_bitwise(batch):
+    """The stage entry points run the same kernels as the composite calls (the
+    FMA kernels at batch 3, the matrix-core ones at 16)."""
+    say(f"[stages] batch {batch}: importance + select == partition; gate/up + select + down == decode")
+    c = synth.random_case(51, 100, 1032, 2900, batch, "bf16")
     Xd, xd = dev(c["X"], "bf16"), dev(c["x"], "bf16")
     Wg, Wu, WdT = dev(c["W_gate"], "bf16"), dev(c["W_up"], "bf16"), dev(c["W_downT"], "bf16")
     R, C, P, I = pop.pop_prefill_partition(Xd, Wu, 0.3, 0.1, importance=True)
