@@ -62,9 +62,15 @@ __device__ __forceinline__ uint32_t bf16_pack_rne(float lo, float hi) {
 #define POP_GL_KC 256
 #endif
 #ifndef POP_GL_NS
-#define POP_GL_NS 3
+#define POP_GL_NS 2
 #endif
-constexpr int kGlRows = 24;                          // rows per block at most
+#ifndef POP_GL_ROWS
+#define POP_GL_ROWS 24
+#endif
+#ifndef POP_GL_BLOCKS
+#define POP_GL_BLOCKS 512
+#endif
+constexpr int kGlRows = POP_GL_ROWS;                 // rows per block at most (16 or 24)
 constexpr int kGlKC = POP_GL_KC;                     // reduction elements per stage (128 or 256)
 constexpr int kGlNS = POP_GL_NS;                     // stages in the LDS ring
 constexpr int kGlSlots = kGlKC / 8;                  // 16-byte chunks per row and stage
@@ -87,7 +93,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // The host's grid for k_gateup_lds: every block resident (two per CU) and at
 // most kGlRows rows each.
 __host__ __device__ constexpr int gateup_lds_blocks(int n_A) {
-  return (n_A + kGlRows - 1) / kGlRows > 512 ? (n_A + kGlRows - 1) / kGlRows : 512;
+  return (n_A + kGlRows - 1) / kGlRows > POP_GL_BLOCKS ? (n_A + kGlRows - 1) / kGlRows : POP_GL_BLOCKS;
 }
 
 template <int MT, bool kIdentity>
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(256) void k_gateup_lds(const bf16s* __restrict__ x,
                                                     int d_ff, const int32_t* __restrict__ R, int n_R,
                                                     const int32_t* __restrict__ C, int n_C, float* __restrict__ z,
                                                     float* __restrict__ score, int nb) {
-  constexpr int NT = 2;  // row tiles (kGlRows <= 32)
+  constexpr int NT = (kGlRows + 15) / 16;  // row tiles
   __shared__ __align__(16) uint16_t smem[kGlNS * kGlStage];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;

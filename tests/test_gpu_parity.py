@@ -133,6 +133,8 @@ DEC_CASES = [
     ("bf16_r0", 12, 256, 500, 2, "bf16", 0.0, 0.1),
     ("bf16_gamma0", 12, 256, 500, 2, "bf16", 0.4, 0.0),
     ("f32_high_r", 12, 128, 300, 1, "f32", 0.95, 0.1),
+    # batch 1 past 4096 candidates: the top-k is its own launch, the selected-row helpers do not wait
+    ("bf16_b1_wide_C", 20, 264, 6000, 1, "bf16", 0.2, 0.8),
     # matrix-core batches: one, two and four 16-token tiles, ragged d; 65 falls back to the FMA kernels
     ("bf16_b8_mfma", 30, 520, 1501, 8, "bf16", 0.3, 0.1),
     ("bf16_b16_mfma_tail_chunk", 30, 264, 1000, 16, "bf16", 0.3, 0.1),
