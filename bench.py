@@ -329,7 +329,7 @@ def main():
         if n_C > 4096 and k > 0:
             labels_dec.insert(1, "k_topk")
         labels_dense = ["k_pop_step.0(dense)", "k_pop_finish(dense)"]
-    elif e == 2 and 8 <= B <= 64:   # matrix-core batched decode
+    elif e == 2 and 2 <= B <= 64:   # matrix-core batched decode
         # the top-k of up to 4096 candidates shares the retained rows' down launch
         topk = n_C > 0 and k > 0
         labels_dec = (["k_gateup_lds"] + (["k_topk"] if topk and n_C > 4096 else [])

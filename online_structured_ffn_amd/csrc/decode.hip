@@ -765,10 +765,11 @@ static size_t decode_ws_layout(int32_t batch, int32_t d, int32_t d_ff, char* bas
 }
 
 // ---- stage launchers (arguments already validated)
-// Batches of 8..64 rows in bf16 run on the matrix cores (below 8 the FMA
-// kernels measured faster).
+// Batches of 2..64 rows in bf16 run on the matrix cores (16-token tiles, the
+// unused token rows cost matrix-core time only, which the weight stream
+// hides); fp32 and wider batches run the FMA kernels.
 #ifndef POP_MFMA_MIN_BATCH
-#define POP_MFMA_MIN_BATCH 8
+#define POP_MFMA_MIN_BATCH 2
 #endif
 template <typename T>
 static bool use_mfma(int B) {

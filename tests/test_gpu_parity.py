@@ -252,14 +252,14 @@ def test_full_size_layer(wname, layer, steps):
     _decode_case(X, xs, wts, w.dtype, w.r, w.gamma, w.name)
 
 
-@pytest.mark.parametrize("batch", [3, 16])
-def test_stages_compose_bitwise(batch):
+@pytest.mark.parametrize("batch,dtype", [(3, "f32"), (3, "bf16"), (16, "bf16")])
+def test_stages_compose_bitwise(batch, dtype):
     """The stage entry points run the same kernels as the composite calls (the
-    FMA kernels at batch 3, the matrix-core ones at 16)."""
-    say(f"[stages] batch {batch}: importance + select == partition; gate/up + select + down == decode")
-    c = synth.random_case(51, 100, 1032, 2900, batch, "bf16")
-    Xd, xd = dev(c["X"], "bf16"), dev(c["x"], "bf16")
-    Wg, Wu, WdT = dev(c["W_gate"], "bf16"), dev(c["W_up"], "bf16"), dev(c["W_downT"], "bf16")
+    FMA kernels in fp32, the matrix-core ones in bf16)."""
+    say(f"[stages] batch {batch} {dtype}: importance + select == partition; gate/up + select + down == decode")
+    c = synth.random_case(51, 100, 1032, 2900, batch, dtype)
+    Xd, xd = dev(c["X"], dtype), dev(c["x"], dtype)
+    Wg, Wu, WdT = dev(c["W_gate"], dtype), dev(c["W_up"], dtype), dev(c["W_downT"], dtype)
     R, C, P, I = pop.pop_prefill_partition(Xd, Wu, 0.3, 0.1, importance=True)
     I2 = pop.pop_prefill_importance(Xd, Wu)
     R2, C2, P2 = pop.pop_partition_select(I2, 0.3, 0.1)
