@@ -85,8 +85,8 @@ def main():
 
     w = configs.BY_NAME[args.workload]
     if w.experts:
-        print("the MoE workload has no bench line yet", file=sys.stderr)
-        sys.exit(2)
+        bench_moe(args, w, np, torch, metrics, pop, synth)
+        return
     L = args.layers or w.layers
     T = args.decode_steps or w.decode_steps
     B = w.decode_batch
@@ -524,6 +524,219 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, T, args.cpu_seconds)
         log(f"[bench] cpu baseline: {out['cpu_baseline']}")
 
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+def bench_moe(args, w, np, torch, metrics, pop, synth):
+    """The mixture-of-experts workload: per layer, the per-expert partition of
+    the prompt (routed tokens only), then every decode step through
+    pop_moe_decode_ffn (routing, per-expert POP step, weighted combine).  The
+    step is the partition of every layer + every decode step over every layer
+    (there is no MoE prompt FFN in this library).  The dense comparator runs
+    the same kernels with every channel retained and no candidates."""
+    L = args.layers or w.layers
+    T = args.decode_steps or w.decode_steps
+    B, E, d, d_ff = w.decode_batch, w.experts, w.d, w.d_ff
+    e = 2 if w.dtype == "bf16" else 4
+    n_tok = w.prompt_batch * w.prompt_len
+    dev = torch.device("cuda")
+    cnt = pop.pop_partition_counts(d_ff, w.r, w.gamma)
+    n_R, n_C, n_P, k = cnt["n_R"], cnt["n_C"], cnt["n_P"], cnt["k"]
+    log(f"[bench] {w.name}: {L} layers x {E} experts, d={d}, d_ff={d_ff}, prompt {n_tok} tokens, T={T}, "
+        f"{B} tokens per step, top-2; per expert |R|={n_R} |C|={n_C} |P|={n_P} k={k}")
+    t0 = time.time()
+    Wg, Wu, WdT, X = [], [], [], []
+    for l in range(L):
+        parts = [synth.torch_layer_weights(w, l * E + x, dev) for x in range(E)]
+        for dst, name in ((Wg, "W_gate"), (Wu, "W_up"), (WdT, "W_downT")):
+            dst.append(torch.stack([q[name] for q in parts]).contiguous())
+        del parts
+        X.append(synth.torch_activations(w, (n_tok, d), l, 0, dev))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.SEED_ROOT ^ 0x5EED)
+    logits_pre = torch.randn((L, n_tok, E), generator=gen, device=dev, dtype=torch.float32)
+    logits_dec = torch.randn((T, L, B, E), generator=gen, device=dev, dtype=torch.float32)
+    Xdec = synth.torch_activations(w, (T * L * B, d), 0, 1, dev).view(T, L, B, d)
+    R = [torch.empty((E, n_R), dtype=torch.int32, device=dev) for _ in range(L)]
+    C = [torch.empty((E, n_C), dtype=torch.int32, device=dev) for _ in range(L)]
+    P = [torch.empty((E, n_P), dtype=torch.int32, device=dev) for _ in range(L)]
+    R_all = torch.arange(d_ff, dtype=torch.int32, device=dev).repeat(E, 1).contiguous()
+    C_none = torch.empty((E, 0), dtype=torch.int32, device=dev)
+    x_buf = torch.empty((L, B, d), dtype=Xdec.dtype, device=dev)
+    lg_buf = torch.empty((L, B, E), dtype=torch.float32, device=dev)
+    y = torch.empty((L, B, d), dtype=torch.float32, device=dev)
+    ws_pre = pop.workspace(int(pop.lib.pop_moe_prefill_workspace_bytes(n_tok, d, d_ff, E)), dev)
+    ws_dec = pop.workspace(pop.pop_moe_decode_workspace_bytes(B, d, d_ff, E), dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated on the device in {time.time() - t0:.1f} s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+
+    def prefill():
+        for l in range(L):
+            pop.pop_moe_prefill_partition(X[l], logits_pre[l], Wu[l], w.r, w.gamma, out=(R[l], C[l], P[l], None),
+                                          ws=ws_pre)
+
+    def decode_layers():
+        for l in range(L):
+            pop.pop_moe_decode_ffn(x_buf[l], lg_buf[l], Wg[l], Wu[l], WdT[l], R[l], C[l], w.r, y=y[l], ws=ws_dec)
+
+    def dense_layers():
+        for l in range(L):
+            pop.pop_moe_decode_ffn(x_buf[l], lg_buf[l], Wg[l], Wu[l], WdT[l], R_all, C_none, 0.0, y=y[l], ws=ws_dec)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        x_buf.copy_(Xdec[0])
+        lg_buf.copy_(logits_dec[0])
+        prefill()
+        decode_layers()
+        dense_layers()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = {}
+    for name, fn in (("prefill", prefill), ("decode", decode_layers), ("dense", dense_layers)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs[name] = g
+    torch.cuda.synchronize()
+
+    def steps(name):
+        def run():
+            for t in range(T):
+                x_buf.copy_(Xdec[t])
+                lg_buf.copy_(logits_dec[t])
+                graphs[name].replay()
+        return run
+
+    def job():
+        graphs["prefill"].replay()
+        steps("decode")()
+
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        a = Ev(torch).record()
+        for _ in range(reps):
+            fn()
+        b = Ev(torch).record()
+        torch.cuda.synchronize()
+        return a.ms(b) / reps
+
+    for _ in range(args.warmup):
+        job()
+    torch.cuda.synchronize()
+    ms_step = timed(job, args.steps)
+    value = B * T * L / (ms_step / 1e3)
+    log(f"[bench] step {ms_step:.2f} ms -> {value:,.0f} tokens/s/layer")
+    ms_pre = timed(lambda: graphs["prefill"].replay(), 3)
+    ms_dec = timed(steps("decode"), 1)
+    ms_dense = timed(steps("dense"), 1)
+    t_ls, t_ls_dense = ms_dec / (T * L), ms_dense / (T * L)
+
+    # experts reached per step (top-2 of the step's logits), for the byte counts
+    top2 = torch.topk(logits_dec, 2, dim=-1).indices.view(T, L, B * 2).cpu().numpy()
+    active = float(np.mean([[len(np.unique(top2[t, l])) for l in range(L)] for t in range(T)]))
+    bytes_ls = metrics.moe_decode_bytes(d, n_R, n_C, k, active, B, e)
+    bytes_dense = metrics.moe_decode_bytes(d, d_ff, 0, 0, active, B, e)
+    gateup_bytes = active * (2 * (n_R + n_C) * d * e)
+    log(f"[bench] MoE decode {t_ls * 1e3:.1f} us/layer-step ({bytes_ls / (t_ls * 1e-3) / 1e9:.0f} GB/s, "
+        f"{active:.2f} experts reached per step), dense {t_ls_dense * 1e3:.1f} us "
+        f"({bytes_dense / (t_ls_dense * 1e-3) / 1e9:.0f} GB/s), partition {ms_pre / L * 1e3:.1f} us/layer")
+
+    # per-kernel pass: the decode calls with libpop's trace hook
+    S = min(args.kernel_steps, T)
+    mfma = e == 2 and B <= 64   # the library's dispatch: bf16 steps of up to 64 tokens on the matrix cores
+    topk = n_C > 0 and k > 0
+    if mfma:
+        gu = "k_gateup_lds"
+        labels_dec = (["k_moe_top2", "k_moe_bucket", gu] + (["k_moe_topk"] if topk and n_C > 4096 else [])
+                      + ["k_down_stream.R+topk" if topk and n_C <= 4096 else "k_down_stream.R"]
+                      + (["k_down_stream.S"] if k > 0 else []) + ["k_moe_combine"])
+        labels_dense = ["k_moe_top2", "k_moe_bucket", gu + "(dense)", "k_down_stream.R(dense)", "k_moe_combine"]
+    else:
+        gu = "k_moe_gateup"
+        labels_dec = ["k_moe_top2", "k_moe_bucket", gu] + (["k_moe_topk"] if topk else []) + [
+            "k_moe_down", "k_moe_combine"]
+        labels_dense = ["k_moe_top2", "k_moe_bucket", gu + "(dense)", "k_moe_down(dense)", "k_moe_combine"]
+    tracer = pop.Tracer(S * L * (len(labels_dec) + len(labels_dense) + 2) + 8, pop.Tracer.DISABLE_SYSTEM_FENCE)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    marks = []
+    with tracer:
+        for t in range(S):
+            x_buf.copy_(Xdec[t])
+            lg_buf.copy_(logits_dec[t])
+            for l in range(L):
+                a = pop.lib.pop_trace_recorded()
+                pop.pop_moe_decode_ffn(x_buf[l], lg_buf[l], Wg[l], Wu[l], WdT[l], R[l], C[l], w.r, y=y[l], ws=ws_dec)
+                marks.append((labels_dec, a, pop.lib.pop_trace_recorded()))
+            for l in range(L):
+                a = pop.lib.pop_trace_recorded()
+                pop.pop_moe_decode_ffn(x_buf[l], lg_buf[l], Wg[l], Wu[l], WdT[l], R_all, C_none, 0.0, y=y[l],
+                                       ws=ws_dec)
+                marks.append((labels_dense, a, pop.lib.pop_trace_recorded()))
+    torch.cuda.synchronize()
+    per = {}
+    for labels, i0, i1 in marks:
+        if i1 - i0 != len(labels) + 1:
+            labels = [f"{labels[0]}#{j}" for j in range(i1 - i0 - 1)]
+        for j, name in enumerate(labels):
+            per.setdefault(name, []).append(tracer.elapsed_ms(i0 + j, i0 + j + 1))
+    tracer.close()
+    kus = {n: float(np.mean(v)) * 1e3 for n, v in per.items()}
+    log("[bench] kernels (us): " + ", ".join(f"{n} {v:.2f}" for n, v in kus.items()))
+    dom_us = kus.get(gu)
+    dom_gbps = gateup_bytes / (dom_us * 1e-6) / 1e9 if dom_us else None
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded device-drawn expert weights N(0,0.02^2), activations and N(0,1) router logits)",
+        "config": {
+            "workload": w.name, "layers": L, "experts": E, "route_top_k": 2, "d": d, "d_ff": d_ff, "r_ffn": w.r,
+            "gamma": w.gamma, "prompt_tokens": n_tok, "decode_steps": T, "tokens_per_step": B, "hip_graphs": True,
+            "step": "per-expert prefill partition of every layer + every decode step over every layer",
+        },
+        "roofline": {
+            "kernel": f"{gu} (MoE decode gate/up over each reached expert's R u C for its routed tokens)",
+            "bound": "hbm",
+            "achieved": None if dom_gbps is None else round(dom_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": None if dom_gbps is None else round(dom_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": round(gateup_bytes),
+            "avg_launch_us": None if dom_us is None else round(dom_us, 3),
+        },
+        "decode": {
+            "us_per_layer_step": round(t_ls * 1e3, 3),
+            "experts_reached_per_step": round(active, 3),
+            "algorithmic_bytes_per_layer_step": round(bytes_ls),
+            "hbm_gbps": round(bytes_ls / (t_ls * 1e-3) / 1e9, 1),
+        },
+        "dense_decode": {
+            "us_per_layer_step": round(t_ls_dense * 1e3, 3),
+            "algorithmic_bytes_per_layer_step": round(bytes_dense),
+            "hbm_gbps": round(bytes_dense / (t_ls_dense * 1e-3) / 1e9, 1),
+        },
+        "speedup_vs_dense": round(t_ls_dense / t_ls, 4),
+        "prefill_partition_us_per_layer": round(ms_pre / L * 1e3, 2),
+        "kernels_us": {n: round(v, 3) for n, v in kus.items()},
+        "cpu_baseline": None,
+    }
     line = json.dumps(out)
     print(line, flush=True)
     if args.json_out:

@@ -40,6 +40,18 @@ __device__ __forceinline__ uint32_t bf16_pack_rne(float lo, float hi) {
   return (a >> 16) | (b & 0xffff0000u);
 }
 
+// Mixture-of-experts form of a launch (kMoe): grid row blockIdx.y is expert e,
+// whose weight matrices sit w_stride elements after expert e - 1's, whose
+// lists (R, C, and S, positions, scores) are its slices of E stacked lists,
+// and whose tokens are the routed pairs offsets[e] .. offsets[e + 1] (pair p
+// is token tokens[p]; z row p).  Every expert gets at most as many pairs as
+// there are tokens, so the launch's token tiles cover it.
+struct MoeRows {
+  const int32_t* offsets;
+  const int32_t* tokens;
+  int64_t w_stride;
+};
+
 // ---------------------------------------------------------------- gate / up, rows streamed through LDS
 // The same product with the weight rows read by LDS-direct loads: one load
 // instruction moves 1 KB of one or a few rows (full 128-byte lines; a
@@ -96,17 +108,30 @@ __host__ __device__ constexpr int gateup_lds_blocks(int n_A) {
   return (n_A + kGlRows - 1) / kGlRows > POP_GL_BLOCKS ? (n_A + kGlRows - 1) / kGlRows : POP_GL_BLOCKS;
 }
 
-template <int MT, bool kIdentity>
+template <int MT, bool kIdentity, bool kMoe = false>
 __global__ __launch_bounds__(256) void k_gateup_lds(const bf16s* __restrict__ x, int B, int d,
                                                     const bf16s* __restrict__ Wg, const bf16s* __restrict__ Wu,
                                                     int d_ff, const int32_t* __restrict__ R, int n_R,
                                                     const int32_t* __restrict__ C, int n_C, float* __restrict__ z,
-                                                    float* __restrict__ score, int nb) {
+                                                    float* __restrict__ score, int nb, MoeRows moe = {}) {
   constexpr int NT = (kGlRows + 15) / 16;  // row tiles
   __shared__ __align__(16) uint16_t smem[kGlNS * kGlStage];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int n_A = n_R + n_C;
+  int o0 = 0;  // first routed pair of the expert
+  if constexpr (kMoe) {
+    const int e = blockIdx.y;
+    o0 = moe.offsets[e];
+    B = moe.offsets[e + 1] - o0;
+    if (B <= 0) return;  // block-uniform: no token reached the expert
+    Wg += e * moe.w_stride;
+    Wu += e * moe.w_stride;
+    R += (int64_t)e * n_R;
+    C += (int64_t)e * n_C;
+    if (score != nullptr) score += (int64_t)e * n_C;
+    z += (int64_t)o0 * n_A;
+  }
   const int r0 = (int)((int64_t)blockIdx.x * n_A / nb);
   const int nr = (int)((int64_t)(blockIdx.x + 1) * n_A / nb) - r0;
   if (nr <= 0) return;  // block-uniform
@@ -130,7 +155,10 @@ __global__ __launch_bounds__(256) void k_gateup_lds(const bf16s* __restrict__ x,
   // this lane's token rows (tokens past B read token 0: never stored)
   const bf16s* xr[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) xr[t] = x + (int64_t)(16 * t + r < B ? 16 * t + r : 0) * d;
+  for (int t = 0; t < MT; ++t) {
+    const int tok = 16 * t + r < B ? 16 * t + r : 0;
+    xr[t] = x + (int64_t)(kMoe ? moe.tokens[o0 + tok] : tok) * d;
+  }
   const int nst = (d + kGlKC - 1) / kGlKC;
   u32x4 xs[kGlNS][kGlKB][MT];
   // stage st into ring slot q: this wave's token fragments, then its share of the rows
@@ -308,7 +336,7 @@ struct DsShared {
   int zcol[kDsMaxRows];
 };
 
-template <int MT, bool kIdentity, int PHASE>
+template <int MT, bool kIdentity, int PHASE, bool kMoe = false>
 __global__ __launch_bounds__(256) void k_down_stream(const float* __restrict__ z, int n_A, int B,
                                                      const bf16s* __restrict__ WdT, int d, int d_ff,
                                                      const int32_t* __restrict__ R, int n_R,
@@ -317,11 +345,27 @@ __global__ __launch_bounds__(256) void k_down_stream(const float* __restrict__ z
                                                      float* __restrict__ partial, int nb0,
                                                      const float* __restrict__ score, int n_C, int k,
                                                      const int32_t* __restrict__ C, int32_t* __restrict__ Q,
-                                                     int32_t* __restrict__ S) {
+                                                     int32_t* __restrict__ S, MoeRows moe = {}) {
   using DS = DsShared<MT>;
   using TS = SelShared<256, 4096>;
   constexpr size_t kSmem = sizeof(DS) > (PHASE == 1 ? sizeof(TS) : 0) ? sizeof(DS) : sizeof(TS);
   __shared__ __align__(16) unsigned char smem[kSmem];
+  int o0 = 0, cnt = B;  // the launch's z rows: all B, or the expert's routed pairs (B = every pair)
+  if constexpr (kMoe) {
+    const int e = blockIdx.y;
+    o0 = moe.offsets[e];
+    cnt = moe.offsets[e + 1] - o0;
+    if (cnt <= 0) return;  // block-uniform: no token reached the expert
+    WdT += e * moe.w_stride;
+    R += (int64_t)e * n_R;
+    sel += (int64_t)e * k;
+    pos += (int64_t)e * k;
+    C += (int64_t)e * n_C;
+    Q += (int64_t)e * k;
+    S += (int64_t)e * k;
+    if (score != nullptr) score += (int64_t)e * n_C;
+    z += (int64_t)o0 * n_A;
+  }
   if constexpr (PHASE == 1) {
     if ((int)blockIdx.x < nb0) {
       topk_block(score, n_C, k, C, Q, S, *reinterpret_cast<TS*>(smem));
@@ -381,7 +425,7 @@ __global__ __launch_bounds__(256) void k_down_stream(const float* __restrict__ z
     const int cb = sh.zcol[min(kDsRows * i + 2 * zp + 1, nrows - 1)];
 #pragma unroll
     for (int m = 0; m < 2 * MT; ++m) {
-      const float* zr = z + (int64_t)min(zt + 8 * m, B - 1) * n_A;
+      const float* zr = z + (int64_t)min(zt + 8 * m, cnt - 1) * n_A;
       L.za[m] = zr[ca];
       L.zb[m] = zr[cb];
     }
@@ -463,7 +507,7 @@ __global__ __launch_bounds__(256) void k_down_stream(const float* __restrict__ z
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tok = 16 * t + 4 * g + e;
-        if (tok < B) partial[((int64_t)(chunk_base + cl) * B + tok) * d + col] = acc[t][e];
+        if (tok < cnt) partial[((int64_t)(chunk_base + cl) * B + o0 + tok) * d + col] = acc[t][e];
       }
   }
 }

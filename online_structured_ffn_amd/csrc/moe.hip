@@ -8,16 +8,23 @@
 //
 // Kernels of one step (all experts in each launch, no host synchronisation):
 //   k_moe_top2, k_moe_bucket   routing (moe_route.h)
-//   k_moe_gateup               z and candidate scores, one wave per (expert, row)
-//   k_moe_topk                 one workgroup per expert
-//   k_moe_down                 (column slice, live-row chunk, expert) blocks ->
-//                              partial y per (chunk, routed pair)
+//   bf16 steps of up to 64 tokens: the batched decode's matrix-core kernels in
+//   their expert form (grid row = expert, its routed pairs as the tokens):
+//     k_gateup_lds             z and candidate scores
+//     k_down_stream            the retained rows, with each expert's top-k as
+//                              one block of the launch; then the selected rows
+//   otherwise:
+//     k_moe_gateup             z and candidate scores, one wave per (expert, row)
+//     k_moe_topk               one workgroup per expert
+//     k_moe_down               (column slice, live-row chunk, expert) blocks
+//   both write partial y per (chunk, routed pair), then
 //   k_moe_combine              fixed-order sum over chunks, then over the two
 //                              experts with their weights
 // An expert that no token of the step reaches does nothing: its blocks exit at
 // once and its selected list is left as it was.
 #include <hip/hip_runtime.h>
 
+#include "decode_mfma.h"
 #include "moe_route.h"
 #include "pop_device.h"
 #include "pop_internal.h"
@@ -276,6 +283,19 @@ struct MoeDecodeWs {
   size_t bytes;
 };
 
+// Row chunks of the matrix-core down-projection for one expert: about 1024
+// blocks over all experts and 64-column slices, 64 to kDsMaxRows rows each
+// (never decreasing in n, so the value at n = d_ff bounds every call).
+static int moe_mfma_chunks(int n, int d, int E) {
+  const int slices = (d + 63) / 64;
+  int want = (1024 + E * slices - 1) / (E * slices);
+  const int by_rows = (n + kDsRows - 1) / kDsRows;
+  if (want > by_rows) want = by_rows;
+  const int least = (n + kDsMaxRows - 1) / kDsMaxRows;
+  if (want < least) want = least;
+  return want < 1 ? 1 : want;
+}
+
 // Layout for n_tokens routed tokens; sized for the widest plan (bf16 vectors,
 // every channel live) so that one size serves every dtype and rate.
 static MoeDecodeWs moe_decode_ws(int32_t n_tokens, int32_t d, int32_t d_ff, int32_t E, char* base) {
@@ -283,7 +303,10 @@ static MoeDecodeWs moe_decode_ws(int32_t n_tokens, int32_t d, int32_t d_ff, int3
   // Every plan has n_chunks <= its wanted count, which is largest for bf16
   // (fewer column blocks) before the per-row cap: a bound for every n_live.
   const int cb8 = (d + 64 * 8 - 1) / (64 * 8);
-  const int chunks = (1024 + E * cb8 - 1) / (E * cb8);
+  int chunks = (1024 + E * cb8 - 1) / (E * cb8);
+  // the matrix-core plan: retained and selected rows chunked apart
+  const int mc = 2 * moe_mfma_chunks(d_ff, d, E);
+  if (mc > chunks) chunks = mc;
   MoeDecodeWs w;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -318,6 +341,38 @@ static void launch_route(hipStream_t st, const float* logits, int T, int E, int3
              slot);
 }
 
+// bf16 steps of up to 64 tokens on the matrix cores (see the top of the file).
+template <int MT>
+static void launch_moe_decode_mfma(hipStream_t st, const void* x, int Tn, int d, int E, const void* Wg,
+                                   const void* Wu, const void* WdT, int d_ff, const int32_t* R, int n_R,
+                                   const int32_t* C, int n_C, int k, int32_t* S, const MoeDecodeWs& w) {
+  const int n_A = n_R + n_C, n_pairs = 2 * Tn, n_live = n_R + k;
+  const MoeRows mr{w.offsets, w.tokens, (int64_t)d_ff * d};
+  if (n_A > 0) {
+    const int nb = (n_A + kGlRows - 1) / kGlRows;
+    POP_LAUNCH((k_gateup_lds<MT, false, true>), dim3(nb, E), dim3(256), 0, st, (const bf16s*)x, Tn, d,
+               (const bf16s*)Wg, (const bf16s*)Wu, d_ff, R, n_R, C, n_C, w.z, w.score, nb, mr);
+  }
+  const int ncol = (d + 63) / 64;
+  const int nRc = n_R > 0 ? moe_mfma_chunks(n_R, d, E) : 0, nSc = k > 0 ? moe_mfma_chunks(k, d, E) : 0;
+  const int rpcR = nRc > 0 ? (n_R + nRc - 1) / nRc : 1, rpcS = nSc > 0 ? (k + nSc - 1) / nSc : 1;
+  const int usedR = nRc > 0 ? (n_R + rpcR - 1) / rpcR : 0, usedS = nSc > 0 ? (k + rpcS - 1) / rpcS : 0;
+  const bool topk = n_C > 0 && k > 0, topk_in = topk && n_C <= 4096;
+  if (topk && !topk_in)
+    POP_LAUNCH((k_moe_topk<kSelMaxN, 1024>), dim3(E), dim3(1024), 0, st, (const float*)w.score, n_C, k, C,
+               (const int32_t*)w.offsets, w.Q, S);
+  const int nb0 = topk_in ? 1 : 0;
+  if (nb0 + usedR > 0)
+    POP_LAUNCH((k_down_stream<MT, false, 1, true>), dim3(nb0 + ncol * usedR, E), dim3(256), 0, st,
+               (const float*)w.z, n_A, n_pairs, (const bf16s*)WdT, d, d_ff, R, n_R, (const int32_t*)S,
+               (const int32_t*)w.Q, 0, n_R, rpcR, 0, w.partial, nb0, (const float*)w.score, n_C, k, C, w.Q, S, mr);
+  if (usedS > 0)
+    POP_LAUNCH((k_down_stream<MT, false, 0, true>), dim3(ncol * usedS, E), dim3(256), 0, st, (const float*)w.z,
+               n_A, n_pairs, (const bf16s*)WdT, d, d_ff, R, n_R, (const int32_t*)S, (const int32_t*)w.Q, n_R, n_live,
+               rpcS, usedR, w.partial, 0, (const float*)nullptr, n_C, k, C, w.Q, S, mr);
+  (void)n_live;
+}
+
 template <typename T>
 static void launch_moe_decode(hipStream_t st, const void* x, int Tn, int d, const float* logits, int E,
                               const void* Wg, const void* Wu, const void* WdT, int d_ff, const int32_t* R, int n_R,
@@ -325,6 +380,20 @@ static void launch_moe_decode(hipStream_t st, const void* x, int Tn, int d, cons
   const int n_A = n_R + n_C;
   const int n_pairs = 2 * Tn;
   launch_route(st, logits, Tn, E, w.ex, w.wt, w.offsets, w.tokens, w.slot);
+  if (std::is_same<T, bf16s>::value && Tn <= 16 * kDecMaxTiles) {
+    if (Tn <= 16)
+      launch_moe_decode_mfma<1>(st, x, Tn, d, E, Wg, Wu, WdT, d_ff, R, n_R, C, n_C, k, S, w);
+    else if (Tn <= 32)
+      launch_moe_decode_mfma<2>(st, x, Tn, d, E, Wg, Wu, WdT, d_ff, R, n_R, C, n_C, k, S, w);
+    else
+      launch_moe_decode_mfma<4>(st, x, Tn, d, E, Wg, Wu, WdT, d_ff, R, n_R, C, n_C, k, S, w);
+    const int nRc = n_R > 0 ? moe_mfma_chunks(n_R, d, E) : 0, nSc = k > 0 ? moe_mfma_chunks(k, d, E) : 0;
+    const int rpcR = nRc > 0 ? (n_R + nRc - 1) / nRc : 1, rpcS = nSc > 0 ? (k + nSc - 1) / nSc : 1;
+    const int used = (nRc > 0 ? (n_R + rpcR - 1) / rpcR : 0) + (nSc > 0 ? (k + rpcS - 1) / rpcS : 0);
+    POP_LAUNCH(k_moe_combine, dim3((d + 255) / 256, Tn), dim3(256), 0, st, (const float*)w.partial, used, n_pairs,
+               d, (const int32_t*)w.ex, (const float*)w.wt, (const int32_t*)w.slot, y);
+    return;
+  }
   if (n_A > 0)
     POP_LAUNCH(k_moe_gateup<T>, dim3((n_A + 3) / 4, E), dim3(256), 0, st, (const T*)x, d, (const T*)Wg,
                (const T*)Wu, d_ff, R, n_R, C, n_C, (const int32_t*)w.offsets, (const int32_t*)w.tokens, w.z, w.score);

@@ -93,3 +93,11 @@ def fused_plan(n_R: int, n_C: int, k: int, d: int, e: int) -> dict:
     return {"launch": {1: nbC + nbR1 > 0, 2: (1 if fuse_topk else 0) + nbR2 > 0, 3: True},
             "bytes": {1: b1, 2: b2, 3: b3}, "retained_rows": {1: r1, 2: r2, 3: 0},
             "partials": nbR}
+
+
+def moe_decode_bytes(d: int, n_R: int, n_C: int, k: int, experts_reached: float, tokens: int, e: int) -> float:
+    """One MoE decode layer-step: every reached expert's gate and up rows over
+    R u C and W_downT rows over R u S, the tokens' inputs (once per routed
+    pair) and outputs."""
+    per_expert = 2 * (n_R + n_C) * d * e + (n_R + k) * d * e
+    return experts_reached * per_expert + 2 * tokens * d * e + 4 * tokens * d

@@ -156,6 +156,10 @@ DECODE = [
     ("bf16_T1_E8", 1, 520, 700, 8, "bf16", 0.3, ()),
     ("f32_T20_E3_r0", 20, 64, 150, 3, "f32", 0.0, ()),
     ("bf16_T64_E16", 64, 128, 300, 16, "bf16", 0.5, ()),
+    # past 4096 candidates per expert: the per-expert top-k as its own launch
+    ("bf16_T8_E4_wide_C", 8, 64, 21000, 4, "bf16", 0.3, ()),
+    # past 64 tokens: the FMA kernels
+    ("bf16_T80_E8_fma", 80, 128, 300, 8, "bf16", 0.3, ()),
 ]
 
 
