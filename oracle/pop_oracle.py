@@ -15,7 +15,9 @@ Sources (cited by title and section; the pages are web notes and abstracts):
   [BWP]  "Batch-wise adaptive pruning ... for language reasoning models",
          section 3.1 equation (1) (gated MLP), section 1 and figure 2(a) (a
          batch shares one mask; per-sample scores aggregated by element-wise
-         max).
+         max), figure 1 and figure 2(b) (the mask refreshed by a top-k only
+         periodically, an activation memory carrying importance to the next
+         refresh).
 
 Everything is float64.  Inputs given in bf16 enter as the exact float64 value
 of their bits.  Each stage follows the pages' steps in their order; where the
@@ -36,6 +38,14 @@ pages leave a step open the reading taken is named in the docstring:
   R8  MoE: top-2 routing (ties to the lower expert), weights = softmax of the
       two chosen logits; one partition per expert over its routed prompt
       tokens; per step, the batch max runs over the tokens routed to it.
+  R17 periodic refresh ([BWP] figures 1 and 2(b); its own definition is cut
+      off in the pages): inside POP's candidate set, step t refreshes the
+      selection when t % period == 0.  The activation memory holds, per
+      candidate, the sum of its step scores (R5) over the steps since the last
+      refresh on which it was computed (every candidate on a refresh step, the
+      selected ones in between); a refresh ranks the candidates by the memory
+      including its own step's scores, keeps the k best (R4, R6) and clears it;
+      the other steps compute R plus the kept selection only.
 
 Parity unpinned by the pages (no worked example is printed): the decode score
 formula (R5), the quantile convention (R3) and the tie rule (R4) are fixed
@@ -53,7 +63,7 @@ __all__ = [
     "total_order", "partition", "partition_by_sort", "silu", "restricted_forward",
     "candidate_scores", "select_candidates", "pruned_ffn", "masked_ffn",
     "dense_ffn", "decode_step", "moe_route_top2", "moe_partitions", "moe_decode_step",
-    "static_mask_ffn", "full_reeval_ffn",
+    "static_mask_ffn", "full_reeval_ffn", "periodic_decode",
 ]
 
 
@@ -282,6 +292,45 @@ def full_reeval_ffn(x, W_gate, W_up, W_down, r: float):
     n_live = round_half_away((1.0 - float(r)) * d_ff)
     S = select_candidates(allc, sc, n_live)
     return {"y": z[:, S] @ _f64(W_down)[:, S].T, "S": S}
+
+
+# ------------------------------------------------------------------ periodic refresh
+def periodic_decode(xs, W_gate, W_up, W_down, R, C, r: float, period: int):
+    """[BWP] figure 1 and figure 2(b) read into POP's candidate set (reading
+    R17): the candidate selection is refreshed by a top-k only every
+    ``period`` steps, ranking by an activation memory of accumulated step
+    scores.  xs: the inputs of consecutive steps, each [B, D].  Returns one
+    dict per step: y [B, D], S (selected channels, ascending), refresh (bool)
+    and memory (after the step, per position of C)."""
+    R = np.asarray(R, dtype=np.int64)
+    C = np.asarray(C, dtype=np.int64)
+    n_R = len(R)
+    d_ff = _f64(W_gate).shape[0]
+    k = _k_for(d_ff, r, n_R, len(C))
+    Wd = _f64(W_down)
+    pos_of = {int(c): j for j, c in enumerate(C)}
+    memory = np.zeros(len(C))
+    S = np.zeros(0, dtype=np.int64)
+    out = []
+    for t, x in enumerate(xs):
+        refresh = t % int(period) == 0
+        if refresh:
+            # every candidate computed: its score joins the memory, which ranks them
+            z = restricted_forward(x, W_gate, W_up, R, C)
+            memory = memory + candidate_scores(z, n_R)
+            S = select_candidates(C, memory, k)
+            spos = np.array([pos_of[int(c)] for c in S], dtype=np.int64)
+            z_live = np.concatenate([z[:, :n_R], z[:, n_R + spos]], axis=1)
+            memory = np.zeros(len(C))
+        else:
+            # R plus the kept selection: only the selected candidates are observed
+            z_live = restricted_forward(x, W_gate, W_up, R, S)
+            spos = np.array([pos_of[int(c)] for c in S], dtype=np.int64)
+            memory[spos] += candidate_scores(z_live, n_R)
+        live = np.concatenate([R, S])
+        y = z_live @ Wd[:, live].T
+        out.append({"y": y, "S": S.copy(), "refresh": refresh, "memory": memory.copy()})
+    return out
 
 
 # ------------------------------------------------------------------ MoE

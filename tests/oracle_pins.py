@@ -374,4 +374,66 @@ def pin_ablation_variants(o):
                                rtol=1e-12, atol=1e-12)
 
 
+def pin_periodic_special_cases(o):
+    """Refreshing every step is POP's per-step selection; never refreshing
+    after step 0 is the dense FFN with the step-0 mask (torch)."""
+    g = _rng(17)
+    d, dff, T = 6, 40, 5
+    Wg, Wu, Wd = g.standard_normal((dff, d)), g.standard_normal((dff, d)), g.standard_normal((d, dff))
+    R, C, P = o.partition(g.uniform(0, 1, dff), 0.3, 0.1)
+    xs = [g.standard_normal((2, d)) for _ in range(T)]
+    every = o.periodic_decode(xs, Wg, Wu, Wd, R, C, 0.3, 1)
+    for t in range(T):
+        ref = o.decode_step(xs[t], Wg, Wu, Wd, R, C, 0.3)
+        assert np.array_equal(every[t]["S"], ref["S"]) and every[t]["refresh"]
+        np.testing.assert_allclose(every[t]["y"], ref["y"], rtol=1e-12, atol=1e-13)
+    once = o.periodic_decode(xs, Wg, Wu, Wd, R, C, 0.3, T + 3)
+    S0 = o.decode_step(xs[0], Wg, Wu, Wd, R, C, 0.3)["S"]
+    live = np.concatenate([R, S0])
+    Wd_m = np.zeros_like(Wd)
+    Wd_m[:, live] = Wd[:, live]
+    for t in range(1, T):
+        assert np.array_equal(once[t]["S"], S0) and not once[t]["refresh"]
+        np.testing.assert_allclose(once[t]["y"], _torch_ffn(xs[t], Wg, Wu, Wd_m), rtol=1e-12, atol=1e-12)
+
+
+def pin_periodic_brute_force(o):
+    """The refresh schedule and the activation memory, simulated on the dense
+    activations of every channel (torch) with an explicit lexicographic
+    ranking; at least one refresh must pick differently from the step's own
+    scores, so the memory is exercised."""
+    g = _rng(18)
+    t_ = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
+    memory_mattered = False
+    for trial in range(12):
+        d, dff, T = int(g.integers(3, 9)), int(g.integers(20, 60)), 7
+        period = int(g.integers(2, 4))
+        Wg, Wu, Wd = g.standard_normal((dff, d)), g.standard_normal((dff, d)), g.standard_normal((d, dff))
+        R, C, P = o.partition(g.uniform(0, 1, dff), 0.3, 0.1)
+        k = o.partition_counts(dff, 0.3, 0.1)["k"]
+        xs = [g.standard_normal((int(g.integers(1, 4)), d)) for _ in range(T)]
+        got = o.periodic_decode(xs, Wg, Wu, Wd, R, C, 0.3, period)
+        mem = np.zeros(len(C))
+        keep = np.zeros(0, dtype=np.int64)          # positions into C
+        for t in range(T):
+            zf = (F.silu(F.linear(t_(xs[t]), t_(Wg))) * F.linear(t_(xs[t]), t_(Wu))).numpy()
+            sc = np.abs(zf[:, C]).max(axis=0)
+            if t % period == 0:
+                mem = mem + sc
+                order = np.lexsort((C, -mem))          # memory descending, then channel ascending
+                keep = np.sort(order[:k])
+                alone = np.sort(np.lexsort((C, -sc))[:k])
+                memory_mattered |= not np.array_equal(alone, keep)
+                mem = np.zeros(len(C))
+            else:
+                mem[keep] += sc[keep]
+            live = np.concatenate([R, C[keep]])
+            Wd_m = np.zeros_like(Wd)
+            Wd_m[:, live] = Wd[:, live]
+            assert np.array_equal(got[t]["S"], C[keep]), (trial, t)
+            np.testing.assert_allclose(got[t]["memory"], mem, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(got[t]["y"], zf @ Wd_m.T, rtol=1e-10, atol=1e-11)
+    assert memory_mattered
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

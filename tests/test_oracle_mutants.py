@@ -44,6 +44,12 @@ MUTANTS = [
     ("routing weights not normalised", "weights[t] = (w1 / (w1 + w2), w2 / (w1 + w2))", "weights[t] = (w1, w2)"),
     ("expert partition over all prompt tokens", "toks = np.flatnonzero((ex == e).any(axis=1))", "toks = np.arange(len(X))"),
     ("full re-evaluation keeps one channel too few", "S = select_candidates(allc, sc, n_live)", "S = select_candidates(allc, sc, n_live - 1)"),
+    ("periodic memory kept across a refresh", "            memory = np.zeros(len(C))\n        else:", "        else:"),
+    ("periodic memory ignores the steps between refreshes", "memory[spos] += candidate_scores(z_live, n_R)",
+     "memory[spos] += 0.0"),
+    ("periodic refresh ranks by its own step only", "S = select_candidates(C, memory, k)",
+     "S = select_candidates(C, candidate_scores(z, n_R), k)"),
+    ("periodic refresh every other period", "refresh = t % int(period) == 0", "refresh = t % (2 * int(period)) == 0"),
 ]
 
 
