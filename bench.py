@@ -291,6 +291,38 @@ def main():
     ms_static = timed(steps_of("static"), 1)
     ms_full = timed(steps_of("full"), 1)
 
+    # ------------------------------------------------------------ periodic refresh mode (batch-wise pruning page,
+    # figures 1 and 2(b), read into POP's candidate set): one graph per step kind, replayed by t % period
+    periodic = {}
+    ws_per = pop.workspace(pop.pop_decode_periodic_workspace_bytes(B, d, d_ff), dev)
+    for period in (8, 32):
+        states = [pop.PeriodicState(d_ff, w.r, n_R, n_C, dev) for _ in range(L)]
+
+        def per_layers(t, states=states, period=period):
+            for l in range(L):
+                pop.pop_decode_ffn_periodic(x_buf[l], Wg[l], Wu[l], WdT[l], R[l], C[l], w.r, t, period, states[l],
+                                            y=y[l], ws=ws_per)
+
+        with torch.cuda.stream(side):
+            per_layers(0)
+            per_layers(1)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gp = []
+        for t in (0, 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                per_layers(t)
+            gp.append(g)
+
+        def run(gp=gp, period=period):
+            for t in range(T):
+                x_buf.copy_(Xdec[t])
+                gp[0 if t % period == 0 else 1].replay()
+
+        periodic[period] = timed(run, 1) / (T * L)
+        del gp
+
     ms_dec = timed(decode_only, 1)
     ms_dec_1s = timed(decode_only_1s, 1)
     ms_dense = timed(dense_only, 1)
@@ -302,6 +334,7 @@ def main():
         f"pop_decode_ffn graph {ms_dec_1s / (T * L) * 1e3:.1f} us), "
         f"dense {t_ls_dense * 1e3:.1f} us ({bytes_dense / (t_ls_dense * 1e-3) / 1e9:.0f} GB/s), "
         f"static mask {ms_static / (T * L) * 1e3:.1f} us, full re-evaluation {ms_full / (T * L) * 1e3:.1f} us, "
+        f"periodic refresh " + ", ".join(f"every {p}: {v * 1e3:.1f} us" for p, v in periodic.items()) + ", "
         f"prefill partition {ms_prefill / L * 1e3:.1f} us/layer, "
         f"prefill fused {ms_pre_fused / L * 1e3:.1f} (unfused {ms_pre_unfused / L * 1e3:.1f}) us/layer, "
         f"prompt FFN {ms_pffn / L * 1e3:.1f} us/layer ({pffn_tflops:.0f} TFLOP/s)")
@@ -493,6 +526,9 @@ def main():
                                   "algorithmic_bytes": metrics.decode_bytes(d, 0, d_ff, n_live, B, e)},
             "pop": {"us_per_layer_step": round(t_ls * 1e3, 3), "algorithmic_bytes": bytes_ls},
             "pop_time_over_static": round(t_ls * T * L / ms_static - 1.0, 4),
+            "periodic_refresh": {str(p): {"us_per_layer_step": round(v * 1e3, 3), "refresh_every": p,
+                                          "kernels": "stage entry points (gate/up, select, down) + memory kernels"}
+                                 for p, v in periodic.items()},
             "full_time_over_static": round(ms_full / ms_static - 1.0, 4),
         },
         "prefill_partition_us_per_layer": round(ms_prefill / L * 1e3, 2),

@@ -206,6 +206,37 @@ pop_status pop_decode_ffn_2s(const void* x, int32_t batch, int32_t d, const void
                              float* y, int32_t* selected, void* ws, size_t ws_bytes, void* stream,
                              void* aux_stream, void* fork_event, void* join_event);
 
+/* Workspace bytes of pop_decode_ffn_periodic (independent of r and the lists). */
+size_t pop_decode_periodic_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff);
+
+/*
+ * pop_decode_ffn_periodic — an alternative decode mode: the candidate
+ * selection refreshed only every `period` steps, with an activation memory
+ * ("Batch-wise adaptive pruning ... for language reasoning models", figure 1
+ * and figure 2(b); its definition is cut off in the pages and is read into
+ * POP's candidate set).  Step `step` (0-based) refreshes when
+ * step % period == 0: gate/up over R u C, each candidate's score (max over
+ * the batch of |z|) is added to memory[position], the k candidates of highest
+ * memory (ties: lower position) become the selection, written to
+ * positions [k] (into C, ascending) and selected [k] (channels), and memory is
+ * cleared; rows [n_R + k] receives R followed by the selection.  Any other
+ * step computes the retained rows `rows` (those of the last refresh) with no
+ * candidates, and adds the selected candidates' scores to their memory at
+ * `positions`.  y [batch, d] fp32 as pop_decode_ffn.  memory [n_C] fp32 is
+ * caller-owned state (zero before the first step); positions, selected and
+ * rows are state too.  k, x, weights and lists as pop_decode_ffn;
+ * period >= 1, step >= 0.  ws: at least
+ * pop_decode_periodic_workspace_bytes(batch, d, d_ff) bytes, 16-byte aligned.
+ * Errors as pop_decode_ffn and INVALID_ARGUMENT for period < 1 or step < 0.
+ * Calls that share memory or ws must be ordered on one stream.
+ */
+pop_status pop_decode_ffn_periodic(const void* x, int32_t batch, int32_t d, const void* W_gate,
+                                   const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
+                                   const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C, double r,
+                                   int32_t step, int32_t period, float* memory, int32_t* positions,
+                                   int32_t* selected, int32_t* rows, float* y, void* ws, size_t ws_bytes,
+                                   void* stream);
+
 /* ---------------------------------------------------------------------------
  * Stages of pop_decode_ffn, callable on their own (also the building blocks of
  * the static-mask and full re-evaluation variants of the POP notes' ablation

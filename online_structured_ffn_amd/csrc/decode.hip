@@ -1038,6 +1038,14 @@ using namespace pop;
 #define POP_DISPATCH(dt, FN, ...) \
   ((dt) == POP_BF16 ? FN<bf16s>(__VA_ARGS__) : FN<float>(__VA_ARGS__))
 
+namespace pop {
+float* decode_ws_z(void* ws, int32_t batch, int32_t d, int32_t d_ff) {
+  DecodeWs w;
+  decode_ws_layout(batch, d, d_ff, (char*)ws, &w);
+  return w.z;
+}
+}  // namespace pop
+
 extern "C" size_t pop_decode_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff) {
   if (batch < 0 || d <= 0 || d_ff <= 0) return 0;
   return decode_ws_layout(batch, d, d_ff, nullptr, nullptr);

@@ -35,6 +35,10 @@ float* launch_colsq(void* stream, const void* X, int64_t n_tokens, int32_t d, po
 void launch_partition_lists(void* stream, const float* I, int32_t d_ff, int32_t c_low, int32_t c_high, int32_t* R,
                             int32_t* C, int32_t* P);
 
+// Where pop_decode_ffn leaves z in its workspace (batch rows of the step's
+// live R u C columns, R first; defined in decode.hip).
+float* decode_ws_z(void* ws, int32_t batch, int32_t d, int32_t d_ff);
+
 // Records the next caller-provided trace event on `stream` (no-op unless
 // pop_set_trace_events armed this thread).
 void trace_mark(void* stream);

@@ -80,6 +80,10 @@ def _load():
                                                      _c_vp]),
         "pop_decode_down": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, ctypes.c_int, _c_vp, _c_i32,
                                            _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_size, _c_vp]),
+        "pop_decode_periodic_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32]),
+        "pop_decode_ffn_periodic": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
+                                                   _c_vp, _c_i32, _c_vp, _c_i32, _c_dbl, _c_i32, _c_i32, _c_vp, _c_vp,
+                                                   _c_vp, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -194,6 +198,43 @@ def pop_decode_ffn(x, W_gate, W_up, W_downT, R, C, r: float, *, y=None, selected
         _ptr(R), R.numel(), _ptr(C), C.numel(), float(r), _ptr(y), _ptr(S), _ptr(ws), ws.numel(),
         _stream(stream)))
     return (y, S) if selected else y
+
+
+class PeriodicState:
+    """The state pop_decode_ffn_periodic carries between steps: the activation
+    memory [n_C] (fp32, zero at the start), the current selection as
+    positions into C and as channels [k], and the kept steps' rows [n_R + k]."""
+
+    def __init__(self, d_ff: int, r: float, n_R: int, n_C: int, device):
+        k = _k(d_ff, r, n_R, n_C)
+        self.memory = torch.zeros(n_C, dtype=torch.float32, device=device)
+        self.positions = torch.zeros(k, dtype=torch.int32, device=device)
+        self.selected = torch.zeros(k, dtype=torch.int32, device=device)
+        self.rows = torch.zeros(n_R + k, dtype=torch.int32, device=device)
+
+
+def pop_decode_periodic_workspace_bytes(batch: int, d: int, d_ff: int) -> int:
+    return int(lib.pop_decode_periodic_workspace_bytes(batch, d, d_ff))
+
+
+def pop_decode_ffn_periodic(x, W_gate, W_up, W_downT, R, C, r: float, step: int, period: int,
+                            state: "PeriodicState", *, y=None, ws=None, stream=None):
+    """y [batch, d] (fp32) for decode step ``step`` of the periodic-refresh
+    mode; ``state`` (memory, positions, selected) is read and updated."""
+    _dev(x, W_gate, W_up, W_downT, R, C)
+    batch, d = x.shape
+    d_ff = W_gate.shape[0]
+    dev = W_gate.device
+    if y is None:
+        y = torch.empty((batch, d), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(pop_decode_periodic_workspace_bytes(batch, d, d_ff), dev)
+    _check("pop_decode_ffn_periodic", lib.pop_decode_ffn_periodic(
+        _ptr(x), batch, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
+        _ptr(R), R.numel(), _ptr(C), C.numel(), float(r), int(step), int(period), _ptr(state.memory),
+        _ptr(state.positions), _ptr(state.selected), _ptr(state.rows), _ptr(y), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return y
 
 
 class TwoStream:

@@ -98,6 +98,32 @@ def test_decode_validation(kw, status):
     assert _decode(**kw) == status
 
 
+def _periodic(x=A, b=1, d=256, Wg=A, Wu=A, Wd=A, d_ff=688, dt=0, R=A, nR=413, C=A, nC=137, r=0.3, step=0, period=4,
+              mem=A, pos=A, S=A, rows=A, y=A, ws=A, wsb=1 << 30):
+    return pop.lib.pop_decode_ffn_periodic(x, b, d, Wg, Wu, Wd, d_ff, dt, R, nR, C, nC, r, step, period, mem, pos, S,
+                                           rows, y, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(period=0), INVALID), (dict(step=-1), INVALID), (dict(r=1.0), INVALID), (dict(nR=600), INVALID),
+    (dict(mem=None), INVALID), (dict(S=None), INVALID), (dict(C=None), INVALID), (dict(rows=None), INVALID),
+    (dict(ws=A + 4), MISALIGNED),
+    (dict(wsb=100), WS),
+])
+def test_periodic_validation(kw, status):
+    assert _periodic(**kw) == status
+    assert pop.lib.pop_last_error().decode()
+
+
+def test_periodic_workspace_sizes():
+    f = pop.pop_decode_periodic_workspace_bytes
+    for b in (1, 4, 16, 64):
+        n = f(b, 4096, 11008)
+        assert n >= pop.lib.pop_decode_down_workspace_bytes(b, 4096, 11008) + 4 * b * 11008
+        assert n % 256 == 0
+    assert f(-1, 4096, 11008) == 0 and f(1, 0, 11008) == 0
+
+
 def test_dense_decode_validation():
     f = pop.lib.pop_dense_ffn_decode
     assert f(A, 1, 256, A, A, A, 688, 0, A, A, 10, None) == WS
