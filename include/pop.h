@@ -426,6 +426,107 @@ pop_status pop_moe_decode_ffn(const void* x, int32_t n_tokens, int32_t d, const 
                               double r, float* y, int32_t* selected, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * A whole decoder layer around the pruned FFN.
+ *
+ * "POP: Online Structural Pruning ..." (paper notes), "Key design 3" and
+ * "Limitations": attention keeps every parameter and runs dense; only the FFN
+ * is pruned (at the rate the global budget gives it: 20% global is 29.9% of
+ * LLaMA-2-7B's FFN).  The layer is the pre-norm LLaMA decoder layer of the
+ * model family the notes evaluate:
+ *   h   = x + Attn(RMSNorm(x; attn_norm)) Wo_T
+ *   out = h + FFN(RMSNorm(h; ffn_norm))
+ * with RMSNorm(v) = v / sqrt(mean(v^2) + eps) * gain (Zhang & Sennrich 2019,
+ * eq. 4); [q | k | v] = RMSNorm(x) Wqkv_T; q and k turned by the rotary
+ * embedding of RoFormer (Su et al. 2021, eqs. 14-15): pair (2i, 2i+1) of each
+ * head by the angle pos * theta^(-2i/hd), evaluated in double precision;
+ * causal scaled dot-product attention (Vaswani et al. 2017, sec. 3.2.1), scale
+ * 1/sqrt(hd), query head h reading key/value head h / (H / H_kv).
+ * With POP_BF16 the layer stores bf16 (round to nearest even) where a bf16
+ * model stores its values: both RMSNorm outputs, the key/value cache and the
+ * attention output.  q, every sum and the residual stream x stay fp32.
+ * Key/value caches: device [batch, H_kv, cache_len, hd] in dt each, caller-owned.
+ * ------------------------------------------------------------------------- */
+typedef struct pop_layer_shape {
+  int32_t d;           /* model width D: D % 64 == 0, D <= POP_MAX_D */
+  int32_t n_heads;     /* H, 1..1024 */
+  int32_t n_kv_heads;  /* H_kv >= 1, dividing H */
+  int32_t head_dim;    /* hd: 64 or 128 */
+  int32_t d_ff;        /* FFN width, 1..POP_MAX_D_FF */
+  int32_t cache_len;   /* positions one sequence's cache holds, 1..2^20 */
+  double eps;          /* RMSNorm epsilon, >= 0 */
+  double rope_theta;   /* rotary base, > 0 */
+} pop_layer_shape;
+
+typedef struct pop_layer_weights {
+  const float* attn_norm; /* device fp32 [D]: gain of the attention's RMSNorm */
+  const void* Wqkv_T;     /* device [D, (H + 2 H_kv) hd] in dt: the q, k, v column blocks */
+  const void* Wo_T;       /* device [H hd, D] in dt */
+  const float* ffn_norm;  /* device fp32 [D]: gain of the FFN's RMSNorm */
+  const void* W_gate;     /* device [d_ff, D] in dt */
+  const void* W_up;       /* device [d_ff, D] in dt */
+  const void* W_downT;    /* device [d_ff, D] in dt (transpose of W_down) */
+} pop_layer_weights;
+
+/* Workspace bytes of pop_layer_prefill; 0 for an invalid shape. */
+size_t pop_layer_prefill_workspace_bytes(int32_t batch, int32_t n_tokens, const pop_layer_shape* s, pop_dtype dt);
+
+/*
+ * pop_layer_prefill — the prompt's pass through one layer: dense attention,
+ * the dense FFN, and the FFN's partition from its input ("Key design 1"; the
+ * prompt runs dense, masking starts at the first decode step).
+ *   x          device fp32 [batch, n_tokens, D], updated in place to the
+ *              layer's output.  1 <= n_tokens <= cache_len,
+ *              batch * n_tokens <= 2^22.
+ *   s, w, dt   shape (host struct), weights (host struct of device pointers).
+ *   K_cache, V_cache  positions 0 .. n_tokens - 1 of every sequence written.
+ *   r, gamma, R, C, P, importance  as pop_prefill_partition, over the FFN
+ *              inputs of all batch * n_tokens tokens (one partition).
+ *   ws         >= pop_layer_prefill_workspace_bytes; after the call byte 0
+ *              holds the FFN's input RMSNorm(h) (dt, [batch * n_tokens, D]).
+ * Kernels: RMSNorm; the q|k|v GEMM and the output GEMM on the prompt FFN's
+ * matrix-core kernel (bf16) or LDS-tiled FMA (fp32); the rotation and cache
+ * write; causal attention over 16-query x 32-key LDS tiles; the fused prompt
+ * FFN and partition of pop_prefill_ffn_partition; residual adds.
+ * Errors: BAD_SHAPE / UNSUPPORTED_DTYPE / INVALID_ARGUMENT / MISALIGNED /
+ * WORKSPACE_TOO_SMALL as the other calls; nothing is enqueued on an error.
+ */
+pop_status pop_layer_prefill(float* x, int32_t batch, int32_t n_tokens, const pop_layer_shape* s,
+                             const pop_layer_weights* w, pop_dtype dt, void* K_cache, void* V_cache, double r,
+                             double gamma, int32_t* R, int32_t* C, int32_t* P, float* importance, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* Workspace bytes of pop_layer_decode (1 <= batch <= 64); 0 for an invalid shape. */
+size_t pop_layer_decode_workspace_bytes(int32_t batch, const pop_layer_shape* s, pop_dtype dt);
+
+/*
+ * pop_layer_decode — one decode step of one layer: dense attention over the
+ * cache, then POP's FFN step ("Key design 2") on R u C, or the dense FFN.
+ *   x          device fp32 [batch, D] (1 <= batch <= 64): this step's token of
+ *              every sequence, updated in place to the layer's output.
+ *   pos        device int32 [1]: the token's position (= tokens already in the
+ *              cache), read on the device so that a captured graph can be
+ *              replayed as it advances.  The call writes cache entry pos and
+ *              attends to entries 0 .. pos.  A value outside [0, cache_len)
+ *              writes no cache entry and leaves x undefined; no memory outside
+ *              the buffers is touched.
+ *   R, n_R, C, n_C, r, selected   as pop_decode_ffn (unused with dense_ffn).
+ *   dense_ffn  0: POP's step; 1: every FFN channel (pop_dense_ffn_decode).
+ *   ws         >= pop_layer_decode_workspace_bytes; after the call byte 0
+ *              holds the FFN's input RMSNorm(h) (dt, [batch, D]).
+ * Kernels: RMSNorm; the q|k|v projection as a K-major GEMV (one wave per 512
+ * bf16 or 256 fp32 columns and a chunk of rows, fp32 partial sums); the chunk
+ * sums with the rotation and cache write; attention split into 64-key slices
+ * and a log-sum-exp merge; the output projection GEMV and the residual; the
+ * FFN's RMSNorm; pop_decode_ffn or pop_dense_ffn_decode; the residual.
+ * Deterministic.  Errors as pop_layer_prefill and pop_decode_ffn; nothing is
+ * enqueued on an error.
+ */
+pop_status pop_layer_decode(float* x, int32_t batch, const pop_layer_shape* s, const pop_layer_weights* w,
+                            pop_dtype dt, void* K_cache, void* V_cache, const int32_t* pos, const int32_t* R,
+                            int32_t n_R, const int32_t* C, int32_t n_C, double r, int32_t dense_ffn,
+                            int32_t* selected, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Kernel tracing (measurement hook).
  * ------------------------------------------------------------------------- */
 

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libpop.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["pop_host.cpp", "trace.hip", "prefill.hip", "decode.hip", "prompt_ffn.hip", "moe.hip", "periodic.hip"]
+SOURCES = ["pop_host.cpp", "trace.hip", "prefill.hip", "decode.hip", "prompt_ffn.hip", "moe.hip", "periodic.hip", "layer.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

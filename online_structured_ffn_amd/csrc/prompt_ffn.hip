@@ -25,6 +25,7 @@
 
 #include "pop_device.h"
 #include "pop_internal.h"
+#include "prompt_gemm.h"
 
 namespace pop {
 
@@ -527,6 +528,23 @@ static void launch_prompt_ffn(hipStream_t st, const void* X, int64_t n_tokens, i
                    (float*)nullptr);
       POP_LAUNCH(k_prompt_down_f32, dim3((d + kFT - 1) / kFT, mt), dim3(kFT * kFT), 0, st, (const float*)ws, M,
                  ldz, (const float*)WdT, (int)d_ff, (int)d, Yc);
+    }
+  }
+}
+
+void launch_gemm_kmajor(void* stream, const void* A, int M, int lda, const void* Bk, int K, int N, pop_dtype dt,
+                        float* Y) {
+  hipStream_t st = (hipStream_t)stream;
+  for (int m0 = 0; m0 < M; m0 += (int)kChunkTokens) {  // row chunks keep every grid dimension small
+    const int Mc = M - m0 < (int)kChunkTokens ? M - m0 : (int)kChunkTokens;
+    float* Yc = Y + (int64_t)m0 * N;
+    if (dt == POP_BF16) {
+      const int mt = (Mc + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;
+      POP_LAUNCH((k_prompt_down<128, POP_DOWN_NS>), dim3(mt * nt), dim3(kGThreads), 0, st,
+                 (const uint16_t*)A + (int64_t)m0 * lda, Mc, lda, (const bf16s*)Bk, K, N, Yc, mt, nt);
+    } else {
+      POP_LAUNCH(k_prompt_down_f32, dim3((N + kFT - 1) / kFT, (Mc + kFT - 1) / kFT), dim3(kFT * kFT), 0, st,
+                 (const float*)A + (int64_t)m0 * lda, Mc, lda, (const float*)Bk, K, N, Yc);
     }
   }
 }

@@ -27,6 +27,19 @@ class PopCounts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("d_ff", "c_low", "c_high", "n_P", "n_C", "n_R", "n_live", "k")]
 
 
+class LayerShape(ctypes.Structure):
+    """pop_layer_shape."""
+    _fields_ = [("d", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("cache_len", ctypes.c_int32),
+                ("eps", ctypes.c_double), ("rope_theta", ctypes.c_double)]
+
+
+class LayerWeights(ctypes.Structure):
+    """pop_layer_weights (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "Wqkv_T", "Wo_T", "ffn_norm", "W_gate", "W_up",
+                                               "W_downT")]
+
+
 class PopError(RuntimeError):
     def __init__(self, func, status, detail):
         self.status = status
@@ -84,6 +97,14 @@ def _load():
         "pop_decode_ffn_periodic": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
                                                    _c_vp, _c_i32, _c_vp, _c_i32, _c_dbl, _c_i32, _c_i32, _c_vp, _c_vp,
                                                    _c_vp, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
+        "pop_layer_prefill_workspace_bytes": (_c_size, [_c_i32, _c_i32, ctypes.POINTER(LayerShape), ctypes.c_int]),
+        "pop_layer_prefill": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, ctypes.POINTER(LayerShape),
+                                             ctypes.POINTER(LayerWeights), ctypes.c_int, _c_vp, _c_vp, _c_dbl, _c_dbl,
+                                             _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
+        "pop_layer_decode_workspace_bytes": (_c_size, [_c_i32, ctypes.POINTER(LayerShape), ctypes.c_int]),
+        "pop_layer_decode": (ctypes.c_int, [_c_vp, _c_i32, ctypes.POINTER(LayerShape), ctypes.POINTER(LayerWeights),
+                                            ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, _c_dbl,
+                                            _c_i32, _c_vp, _c_vp, _c_size, _c_vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -532,3 +553,78 @@ class Tracer:
         for i in range(self.n):
             self.hip.hipEventDestroy(self.events[i])
         self.n = 0
+
+
+# ---------------------------------------------------------------- decoder layer
+class Layer:
+    """One decoder layer's shape, weights and dtype for the pop_layer_* calls.
+
+    weights: dict of device tensors attn_norm [d] (fp32), Wqkv_T [d, (H + 2 H_kv) hd],
+    Wo_T [H hd, d], ffn_norm [d] (fp32), W_gate, W_up, W_downT [d_ff, d] (all in one
+    dtype).  The tensors must outlive every call made with this object."""
+
+    def __init__(self, d: int, n_heads: int, n_kv_heads: int, head_dim: int, d_ff: int, cache_len: int,
+                 weights: dict, eps: float = 1e-5, rope_theta: float = 10000.0):
+        self.shape = LayerShape(d, n_heads, n_kv_heads, head_dim, d_ff, cache_len, eps, rope_theta)
+        _dev(*weights.values())
+        self.weights = dict(weights)
+        self.ptrs = LayerWeights(*[weights[n].data_ptr() for n, _ in LayerWeights._fields_])
+        self.dt = _dtype(weights["W_gate"])
+
+    def cache(self, batch: int, device=None):
+        """Zeroed (K, V) caches [batch, H_kv, cache_len, hd] in the weights' dtype."""
+        s = self.shape
+        shp = (batch, s.n_kv_heads, s.cache_len, s.head_dim)
+        dtype = self.weights["W_gate"].dtype
+        dev = device or self.weights["W_gate"].device
+        return torch.zeros(shp, dtype=dtype, device=dev), torch.zeros(shp, dtype=dtype, device=dev)
+
+
+def pop_layer_prefill_workspace_bytes(batch: int, n_tokens: int, layer: Layer) -> int:
+    return int(lib.pop_layer_prefill_workspace_bytes(int(batch), int(n_tokens), ctypes.byref(layer.shape), layer.dt))
+
+
+def pop_layer_decode_workspace_bytes(batch: int, layer: Layer) -> int:
+    return int(lib.pop_layer_decode_workspace_bytes(int(batch), ctypes.byref(layer.shape), layer.dt))
+
+
+def pop_layer_prefill(x, layer: Layer, K, V, r: float, gamma: float, *, importance: bool = False, out=None,
+                      ws=None, stream=None):
+    """The prompt's pass: x [batch, n_tokens, d] (fp32) is updated in place; the
+    caches get positions 0 .. n_tokens - 1.  Returns (R, C, P[, I])."""
+    _dev(x, K, V)
+    batch, n_tokens, d = x.shape
+    d_ff = layer.shape.d_ff
+    c = pop_partition_counts(d_ff, r, gamma)
+    dev = x.device
+    if out is None:
+        R = torch.empty(c["n_R"], dtype=torch.int32, device=dev)
+        C = torch.empty(c["n_C"], dtype=torch.int32, device=dev)
+        P = torch.empty(c["n_P"], dtype=torch.int32, device=dev)
+        I = torch.empty(d_ff, dtype=torch.float32, device=dev) if importance else None
+    else:
+        R, C, P, I = out
+    if ws is None:
+        ws = workspace(pop_layer_prefill_workspace_bytes(batch, n_tokens, layer), dev)
+    _check("pop_layer_prefill", lib.pop_layer_prefill(
+        _ptr(x), batch, n_tokens, ctypes.byref(layer.shape), ctypes.byref(layer.ptrs), layer.dt, _ptr(K), _ptr(V),
+        float(r), float(gamma), _ptr(R), _ptr(C), _ptr(P), _ptr(I), _ptr(ws), ws.numel(), _stream(stream)))
+    return (R, C, P, I) if importance else (R, C, P)
+
+
+def pop_layer_decode(x, layer: Layer, K, V, pos, R, C, r: float, *, dense_ffn: bool = False, selected=None,
+                     ws=None, stream=None):
+    """One decode step: x [batch, d] (fp32) is updated in place; pos is a device
+    int32 tensor [1] holding the token's position.  ``selected`` (optional,
+    int32 [k]) receives the chosen candidates.  Returns x."""
+    _dev(x, K, V, pos, R, C, selected)
+    batch = x.shape[0]
+    if ws is None:
+        ws = workspace(pop_layer_decode_workspace_bytes(batch, layer), x.device)
+    nR = 0 if R is None else R.numel()
+    nC = 0 if C is None else C.numel()
+    _check("pop_layer_decode", lib.pop_layer_decode(
+        _ptr(x), batch, ctypes.byref(layer.shape), ctypes.byref(layer.ptrs), layer.dt, _ptr(K), _ptr(V), _ptr(pos),
+        _ptr(R), nR, _ptr(C), nC, float(r), int(bool(dense_ffn)), _ptr(selected), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return x
