@@ -84,6 +84,9 @@ def main():
     from online_structured_ffn_amd import configs, metrics, pop, profiling, synth
 
     w = configs.BY_NAME[args.workload]
+    if "attention" in w.extra:
+        bench_layer(args, w, np, torch, metrics, pop, synth)
+        return
     if w.experts:
         bench_moe(args, w, np, torch, metrics, pop, synth)
         return
@@ -778,6 +781,275 @@ def bench_moe(args, w, np, torch, metrics, pop, synth):
     if args.json_out:
         with open(args.json_out, "w") as f:
             f.write(line + "\n")
+
+
+def bench_layer(args, w, np, torch, metrics, pop, synth):
+    """Chained decoder layers (dense attention, POP's FFN): the prompt's pass
+    through every layer (pop_layer_prefill: attention over the prompt, the
+    dense prompt FFN and the partition, the key/value caches filled), then every
+    decode step through every layer (pop_layer_decode), the position advanced on
+    the device inside each step's graph.  The dense comparator runs the same
+    layers with the dense FFN."""
+    a = w.extra["attention"]
+    H, Hkv, hd = a["n_heads"], a["n_kv_heads"], a["head_dim"]
+    L = args.layers or w.layers
+    T = args.decode_steps or w.decode_steps
+    B, N, d, d_ff = w.decode_batch, w.prompt_len, w.d, w.d_ff
+    if w.prompt_batch != B:
+        raise ValueError("the decoder-layer workload decodes the sequences it prompted (prompt_batch == decode_batch)")
+    e = 2 if w.dtype == "bf16" else 4
+    Lc = N + T
+    dev = torch.device("cuda")
+    cnt = pop.pop_partition_counts(d_ff, w.r, w.gamma)
+    n_R, n_C, n_P, k = cnt["n_R"], cnt["n_C"], cnt["n_P"], cnt["k"]
+    log(f"[bench] {w.name}: {L} chained layers, d={d}, {H} heads ({Hkv} kv) of {hd}, d_ff={d_ff}, "
+        f"prompt {B}x{N}, T={T}; FFN |R|={n_R} |C|={n_C} |P|={n_P} k={k}")
+    t0 = time.time()
+    layers = []
+    for l in range(L):
+        wts = dict(synth.torch_layer_weights(w, l, dev))
+        wts.update(synth.torch_attention_weights(w, l, dev))
+        layers.append(pop.Layer(d, H, Hkv, hd, d_ff, Lc, wts, eps=a["eps"], rope_theta=a["rope_theta"]))
+    caches = [lay.cache(B) for lay in layers]
+    X0 = synth.torch_activations(w, (B * N, d), 0, 0, dev).float().view(B, N, d).contiguous()
+    Xdec = synth.torch_activations(w, (T * B, d), 0, 1, dev).float().view(T, B, d).contiguous()
+    x_pre = torch.empty_like(X0)
+    x_buf = torch.empty((B, d), dtype=torch.float32, device=dev)
+    pos = torch.zeros(1, dtype=torch.int32, device=dev)
+    R = [torch.empty(n_R, dtype=torch.int32, device=dev) for _ in range(L)]
+    C = [torch.empty(n_C, dtype=torch.int32, device=dev) for _ in range(L)]
+    P = [torch.empty(n_P, dtype=torch.int32, device=dev) for _ in range(L)]
+    ws_pre = pop.workspace(pop.pop_layer_prefill_workspace_bytes(B, N, layers[0]), dev)
+    ws_dec = pop.workspace(pop.pop_layer_decode_workspace_bytes(B, layers[0]), dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated on the device in {time.time() - t0:.1f} s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+
+    def prefill():
+        x_pre.copy_(X0)
+        for l in range(L):
+            pop.pop_layer_prefill(x_pre, layers[l], *caches[l], w.r, w.gamma, out=(R[l], C[l], P[l], None),
+                                  ws=ws_pre)
+        pos.fill_(N)
+
+    def step(dense):
+        def run():
+            for l in range(L):
+                pop.pop_layer_decode(x_buf, layers[l], *caches[l], pos, R[l], C[l], w.r, dense_ffn=dense, ws=ws_dec)
+            pos.add_(1)
+        return run
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        prefill()
+        x_buf.copy_(Xdec[0])
+        step(False)()
+        step(True)()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = {}
+    for name, fn in (("prefill", prefill), ("decode", step(False)), ("dense", step(True))):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs[name] = g
+    torch.cuda.synchronize()
+
+    def steps(name):
+        def run():
+            for t in range(T):
+                x_buf.copy_(Xdec[t])
+                graphs[name].replay()
+        return run
+
+    def job():
+        graphs["prefill"].replay()
+        steps("decode")()
+
+    def timed(fn, reps, before=None):
+        if before is not None:
+            before()
+        torch.cuda.synchronize()
+        a_ = Ev(torch).record()
+        for _ in range(reps):
+            fn()
+        b_ = Ev(torch).record()
+        torch.cuda.synchronize()
+        return a_.ms(b_) / reps
+
+    for _ in range(args.warmup):
+        job()
+    torch.cuda.synchronize()
+    ms_step = timed(job, args.steps)
+    value = B * T * L / (ms_step / 1e3)
+    log(f"[bench] step {ms_step:.2f} ms -> {value:,.0f} tokens/s/layer ({B * T / (ms_step / 1e3):,.1f} tokens/s "
+        f"through all {L} layers)")
+    ms_pre = timed(lambda: graphs["prefill"].replay(), 3)
+    reset = lambda: pos.fill_(N)
+    ms_dec = timed(steps("decode"), 1, reset)
+    ms_dense = timed(steps("dense"), 1, reset)
+    t_ls, t_ls_dense = ms_dec / (T * L), ms_dense / (T * L)
+    n_keys_avg = N + (T + 1) / 2
+    att = metrics.attention_decode_bytes(d, H, Hkv, hd, n_keys_avg, B, e)
+    att_bytes = sum(att.values())
+    bytes_ls = att_bytes + metrics.decode_bytes(d, n_R, n_C, k, B, e) + 2 * B * d * 4
+    bytes_dense = att_bytes + metrics.dense_decode_bytes(d, d_ff, B, e) + 2 * B * d * 4
+    log(f"[bench] layer decode {t_ls * 1e3:.1f} us/layer-step ({bytes_ls / (t_ls * 1e-3) / 1e9:.0f} GB/s), "
+        f"dense FFN {t_ls_dense * 1e3:.1f} us ({bytes_dense / (t_ls_dense * 1e-3) / 1e9:.0f} GB/s); "
+        f"prefill {ms_pre / L * 1e3:.1f} us/layer")
+
+    # per-kernel pass: the decode calls with libpop's trace hook
+    S = min(args.kernel_steps, T)
+    head = ["k_rmsnorm", "k_gemv_kmajor(qkv)", "k_qkv_rope", "k_attn_decode", "k_attn_combine", "k_gemv_kmajor(o)",
+            "k_sum_residual", "k_rmsnorm(ffn)", "-"]
+    fused = B == 1 and 0 < n_C <= 4096 and k > 0
+    labels_pop = head + (["k_pop_step.1", "k_pop_step.2", "k_pop_finish"] if fused else ["ffn#0"]) + ["k_add"]
+    labels_dense = head + (["k_pop_step.0(dense)", "k_pop_finish(dense)"] if B == 1 else ["ffn#0"]) + ["k_add"]
+    tracer = pop.Tracer(S * L * (len(labels_pop) + len(labels_dense) + 2) + 8, pop.Tracer.DISABLE_SYSTEM_FENCE)
+    marks = []
+    for dense, labels in ((False, labels_pop), (True, labels_dense)):
+        pos.fill_(N)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(50_000_000)
+        with tracer:
+            for t in range(S):
+                x_buf.copy_(Xdec[t])
+                for l in range(L):
+                    i0 = pop.lib.pop_trace_recorded()
+                    pop.pop_layer_decode(x_buf, layers[l], *caches[l], pos, R[l], C[l], w.r, dense_ffn=dense,
+                                         ws=ws_dec)
+                    marks.append((labels, i0, pop.lib.pop_trace_recorded()))
+                pos.add_(1)
+        torch.cuda.synchronize()
+        # the tracer's events are re-armed for the second pass: read this pass now
+        per_pass = {}
+        for labels_, a0, a1 in marks:
+            if a1 - a0 != len(labels_) + 1:
+                labels_ = [f"{labels_[0]}#{j}" for j in range(a1 - a0 - 1)]
+            for j, name in enumerate(labels_):
+                per_pass.setdefault(name, []).append(tracer.elapsed_ms(a0 + j, a0 + j + 1))
+        marks = []
+        if not dense:
+            per_pop = per_pass
+        else:
+            per_dense = per_pass
+    tracer.close()
+    kus = {n: float(np.mean(v)) * 1e3 for n, v in per_pop.items() if n != "-"}
+    kus_dense = {n: float(np.mean(v)) * 1e3 for n, v in per_dense.items() if n != "-"}
+    log("[bench] kernels (us): " + ", ".join(f"{n} {v:.2f}" for n, v in kus.items()))
+    log("[bench] dense-FFN layer kernels (us): " + ", ".join(f"{n} {v:.2f}" for n, v in kus_dense.items()))
+    plan = metrics.fused_plan(n_R, n_C, k, d, e)
+    att_k = metrics.attention_decode_bytes(d, H, Hkv, hd, N + (S + 1) / 2, B, e)
+    kbytes = {"k_gemv_kmajor(qkv)": att_k["qkv"], "k_gemv_kmajor(o)": att_k["o"], "k_attn_decode": att_k["attn"]}
+    if fused:
+        kbytes.update({"k_pop_step.1": plan["bytes"][1], "k_pop_step.2": plan["bytes"][2],
+                       "k_pop_finish": plan["bytes"][3]})
+    dom = max((n for n in kbytes if n in kus), key=lambda n: kus[n], default=None)
+    dom_gbps = kbytes[dom] / (kus[dom] * 1e-6) / 1e9 if dom else None
+    cpu = None if args.no_cpu_baseline else cpu_baseline_layer(w, T, args.cpu_seconds)
+    out = {
+        "metric": "decoder-layer decode tokens/s per layer (dense attention + POP FFN); HBM GB/s vs peak",
+        "value": round(value, 1),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded device-drawn weights N(0,0.02^2), RMSNorm gains 1, token inputs N(0,1); "
+                "no dataset, no trained weights)",
+        "config": {
+            "workload": w.name, "layers": L, "d": d, "n_heads": H, "n_kv_heads": Hkv, "head_dim": hd,
+            "d_ff": d_ff, "r_ffn": w.r, "gamma": w.gamma, "prompt_tokens": B * N, "decode_steps": T,
+            "decode_batch": B, "cache_len": Lc, "hip_graphs": True, "streams": 1,
+            "step": "the prompt's pass through every chained layer + every decode step through every layer",
+        },
+        "roofline": {
+            "kernel": f"{dom} (the decoder layer's longest decode kernel)",
+            "bound": "hbm",
+            "achieved": None if dom_gbps is None else round(dom_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": None if dom_gbps is None else round(dom_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": None if dom is None else round(kbytes[dom]),
+            "avg_launch_us": None if dom is None else round(kus[dom], 3),
+        },
+        "decode": {
+            "us_per_layer_step": round(t_ls * 1e3, 3),
+            "tokens_per_s_through_the_stack": round(B / (t_ls * L * 1e-3), 1),
+            "algorithmic_bytes_per_layer_step": round(bytes_ls),
+            "hbm_gbps": round(bytes_ls / (t_ls * 1e-3) / 1e9, 1),
+            "hbm_frac": round(bytes_ls / (t_ls * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        },
+        "dense_ffn_decode": {
+            "us_per_layer_step": round(t_ls_dense * 1e3, 3),
+            "algorithmic_bytes_per_layer_step": round(bytes_dense),
+            "hbm_gbps": round(bytes_dense / (t_ls_dense * 1e-3) / 1e9, 1),
+        },
+        "speedup_vs_dense_ffn": round(t_ls_dense / t_ls, 4),
+        "ideal_speedup_bytes": round(bytes_dense / bytes_ls, 4),
+        "prefill_layer_us": round(ms_pre / L * 1e3, 2),
+        "kernels_us": {n: round(v, 3) for n, v in kus.items()},
+        "kernels_us_dense_ffn": {n: round(v, 3) for n, v in kus_dense.items()},
+        "kernel_bytes": {n: round(v) for n, v in kbytes.items()},
+        "cpu_baseline": cpu,
+    }
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+def cpu_baseline_layer(w, T, budget_s):
+    """The layer oracle, as it stands, on layer 0 of the decoder-layer
+    workload: the prompt's pass, then as many decode steps as fit in the
+    budget, scaled to tokens/s/layer as the GPU value is."""
+    import numpy as np
+
+    import oracle
+    from online_structured_ffn_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = None
+    a = w.extra["attention"]
+    cfg = {"H": a["n_heads"], "H_kv": a["n_kv_heads"], "hd": a["head_dim"], "eps": a["eps"],
+           "theta": a["rope_theta"]}
+    lw = dict(synth.attention_weights(w, 0))
+    lw.update(synth.layer_weights(w, 0))
+    B, N = w.decode_batch, w.prompt_len
+    X = synth.prompt(w, 0).reshape(B, N, w.d)
+    t0 = time.perf_counter()
+    pre = oracle.layer.layer_prefill(X, lw, cfg, w.r, w.gamma, w.dtype, N + T)
+    t_pre = time.perf_counter() - t0
+    K, V = pre["K"], pre["V"]
+    times = []
+    t_start = time.perf_counter()
+    step = 0
+    while step < T and (time.perf_counter() - t_start) < budget_s:
+        x = synth.decode_input(w, 0, step)
+        t0 = time.perf_counter()
+        oracle.layer.layer_decode(x, lw, cfg, K, V, N + step, pre["R"], pre["C"], w.r, w.dtype)
+        times.append(time.perf_counter() - t0)
+        step += 1
+    t_dec = float(np.median(times))
+    value = B * T / (t_pre + T * t_dec)
+    return {
+        "value": round(value, 3),
+        "unit": "tokens/s/layer",
+        "cores": blas_threads if blas_threads is not None else len(os.sched_getaffinity(0)),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"layer 0 of {w.name}: the {N}-token prompt pass ({t_pre:.2f} s) + {len(times)} decode steps "
+                  f"(median {t_dec * 1e3:.1f} ms), numpy fp64; value = B*T / (t_prefill + T * t_step)",
+    }
 
 
 def cpu_baseline(w, T, budget_s):

@@ -1,7 +1,9 @@
 """The five synthetic workloads of the channel-pruned gated-MLP path.
 
-Each workload is one stack of independent gated-MLP layers (the layers do not
-chain: every layer gets its own seeded prompt activations and decode inputs).
+Each FFN workload is one stack of independent gated-MLP layers (the layers do
+not chain: every layer gets its own seeded prompt activations and decode
+inputs).  The decoder-layer workload chains whole layers (attention and FFN)
+over one residual stream, as a model's forward pass does.
 Shapes follow the model families the POP notes evaluate (LLaMA-2-7B, Qwen2-7B,
 a Mixtral-like MoE); the distributions are synthetic stand-ins for the QA and
 generation benchmarks the notes measure on, since no dataset or trained weight
@@ -75,5 +77,12 @@ MIXTRAL_MOE = Workload(
     notes="one MoE layer, 8 experts, top-2 routing of N(0,1) logits; one partition "
           "per expert over the prompt tokens routed to it")
 
-WORKLOADS = [TINY, LLAMA2_7B, LLAMA2_7B_B16, QWEN2_7B, MIXTRAL_MOE]
+LLAMA2_7B_LAYER = Workload(
+    name="llama2_7b_layer_b1", dtype="bf16", layers=32, d=4096, d_ff=11008, r=0.299, gamma=0.1,
+    prompt_batch=1, prompt_len=512, decode_steps=256, decode_batch=1,
+    extra={"attention": {"n_heads": 32, "n_kv_heads": 32, "head_dim": 128, "eps": 1e-5, "rope_theta": 10000.0}},
+    notes="32 chained LLaMA-2-7B-shaped decoder layers: dense attention over a key/value cache, the FFN pruned "
+          "at the 29.9% that a 20% global budget gives it; RMSNorm gains 1, token inputs N(0,1)")
+
+WORKLOADS = [TINY, LLAMA2_7B, LLAMA2_7B_B16, QWEN2_7B, MIXTRAL_MOE, LLAMA2_7B_LAYER]
 BY_NAME = {w.name: w for w in WORKLOADS}

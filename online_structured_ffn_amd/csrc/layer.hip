@@ -43,7 +43,12 @@ namespace pop {
 constexpr int kAttnKeys = 64;       // keys per decode slice
 constexpr int kPfQ = 16;            // queries per prompt-attention block
 constexpr int kPfK = 32;            // keys per prompt-attention tile
-constexpr int kGemvTarget = 2048;   // waves a decode projection aims for
+#ifndef POP_GEMV_WAVES
+#define POP_GEMV_WAVES 2048
+#endif
+constexpr int kGemvTarget = POP_GEMV_WAVES;  // waves a decode projection aims for
+constexpr int kGemvInflight = 16;            // row loads in flight per lane
+constexpr int kSumLanes = 16;                // lanes that share one output's chunk sum
 constexpr int kLayerMaxBatch = 64;  // decode rows per layer call
 
 __device__ __forceinline__ float elem_f(const float* p, int64_t i) { return p[i]; }
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
 // ---------------------------------------------------------------- decode projections
 // part[chunk][b][n] = sum over rows k of the chunk of x[b][k] W[k][n].
 // One wave per block: lane l owns columns n0 + V*l .. + V (one 16-byte load
-// per row); the wave streams rows_per_chunk rows, 8 loads in flight, for BT
+// per row); the wave streams rows_per_chunk rows, 16 loads in flight, for BT
 // tokens (blockIdx.z picks the token group).  Rows past the chunk are clamped
 // for the load and their x taken as 0; token slots past B read row B - 1 and
 // are not written.  N % V == 0; a lane whose columns lie past N loads the last
@@ -112,12 +117,12 @@ __global__ __launch_bounds__(64) void k_gemv_kmajor(const T* __restrict__ x, int
   for (int t = 0; t < BT; ++t)
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[t][v] = 0.f;
-  for (int r = r0; r < r1; r += 8) {
-    u32x4 w[8];
+  for (int r = r0; r < r1; r += kGemvInflight) {
+    u32x4 w[kGemvInflight];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) w[u] = ld16_stream(W + (int64_t)min(r + u, r1 - 1) * N + nc);
+    for (int u = 0; u < kGemvInflight; ++u) w[u] = ld16_stream(W + (int64_t)min(r + u, r1 - 1) * N + nc);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kGemvInflight; ++u) {
       float wf[V];
       unpack(w[u], wf, T{});
       const bool ok = r + u < r1;
@@ -142,29 +147,38 @@ __global__ __launch_bounds__(64) void k_gemv_kmajor(const T* __restrict__ x, int
 }
 
 // ---------------------------------------------------------------- q, k, v
-// Thread per (row m, column pair 2p, 2p+1) of q|k|v, rows outermost: the pair's sums over the
-// chunks (ascending), then for q and k the rotation of the pair by
+// G lanes per (row m, column pair 2p, 2p+1) of q|k|v, rows outermost: lane j
+// of the group adds chunks j, j + G, ... (ascending), and a butterfly over the
+// G lanes (fp addition commutes, so every lane ends with the same bits) gives
+// the pair's sums; then for q and k the rotation of the pair by
 // pos * theta^(-2i/hd) (i = pair index inside the head; the angle, its sine
 // and cosine in double precision).  Row m is token m % rows_per_seq of
 // sequence m / rows_per_seq, at position pos0 + (*pos_ptr if given) +
 // m % rows_per_seq.  q goes to q_out [M, H, hd] (fp32); k and v to the caches
 // [seq, H_kv, L, hd] (dtype) when 0 <= pos < L, else nowhere.
-template <typename T>
+template <typename T, int G>
 __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ part, int chunks, int M, int H, int Hkv,
                                                   int hd, int rows_per_seq, int pos0, const int32_t* __restrict__ pos_ptr,
                                                   double theta, int L, float* __restrict__ q_out, T* __restrict__ Kc,
                                                   T* __restrict__ Vc) {
   const int Nqkv = (H + 2 * Hkv) * hd;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (int64_t)M * (Nqkv / 2)) return;
+  const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) / G;
+  const int j = threadIdx.x % G;
+  if (t >= (int64_t)M * (Nqkv / 2)) return;  // whole groups leave together (256 % G == 0)
   const int m = (int)(t / (Nqkv / 2));
   const int col = 2 * (int)(t % (Nqkv / 2));
   float a = 0.f, b = 0.f;
-  for (int c = 0; c < chunks; ++c) {
+  for (int c = j; c < chunks; c += G) {
     const float2 v = *reinterpret_cast<const float2*>(part + ((int64_t)c * M + m) * Nqkv + col);
     a += v.x;
     b += v.y;
   }
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) {
+    a += __shfl_xor(a, o);
+    b += __shfl_xor(b, o);
+  }
+  if (j != 0) return;
   const int seq = m / rows_per_seq;
   const int pos = pos0 + (pos_ptr != nullptr ? *pos_ptr : 0) + m % rows_per_seq;
   const int head = col / hd, dd = col % hd;
@@ -385,14 +399,19 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------- residual
-// x[i] += sum over chunks of part[c][i], chunks in order.
+// x[i] += sum over chunks of part[c][i]: G lanes per output, lane j adding
+// chunks j, j + G, ... in order, then a butterfly over the G lanes.
+template <int G>
 __global__ __launch_bounds__(256) void k_sum_residual(const float* __restrict__ part, int chunks, int64_t n,
                                                       float* __restrict__ x) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) / G;
+  const int j = threadIdx.x % G;
+  if (i >= n) return;  // whole groups leave together
   float s = 0.f;
-  for (int c = 0; c < chunks; ++c) s += part[c * n + i];
-  x[i] += s;
+  for (int c = j; c < chunks; c += G) s += part[c * n + i];
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (j == 0) x[i] += s;
 }
 
 __global__ __launch_bounds__(256) void k_add(float* __restrict__ x, const float* __restrict__ y, int64_t n) {
@@ -418,7 +437,7 @@ static GemvPlan gemv_plan(int B, int K, int N, int esz) {
   if (want > cap) want = (int)(cap > 1 ? cap : 1);
   if (want < 1) want = 1;
   int rpc = (K + want - 1) / want;
-  rpc = (rpc + 7) / 8 * 8;
+  rpc = (rpc + kGemvInflight - 1) / kGemvInflight * kGemvInflight;
   p.rows_per_chunk = rpc;
   p.chunks = (K + rpc - 1) / rpc;
   return p;
@@ -441,8 +460,8 @@ static void launch_gemv(hipStream_t st, const GemvPlan& p, const void* x, int B,
 
 static int n_qkv(const pop_layer_shape& s) { return (s.n_heads + 2 * s.n_kv_heads) * s.head_dim; }
 static int n_slices(const pop_layer_shape& s) { return (s.cache_len + kAttnKeys - 1) / kAttnKeys; }
-static dim3 qkv_grid(int64_t M, const pop_layer_shape& s) {
-  return dim3((unsigned)((M * (n_qkv(s) / 2) + 255) / 256));
+static dim3 qkv_grid(int64_t M, const pop_layer_shape& s, int G) {
+  return dim3((unsigned)((M * (n_qkv(s) / 2) * G + 255) / 256));
 }
 
 static pop_status check_layer(const pop_layer_shape* s, pop_dtype dt) {
@@ -616,7 +635,7 @@ extern "C" pop_status pop_layer_decode(float* x, int32_t batch, const pop_layer_
   if (dt == POP_BF16) {
     POP_LAUNCH(k_rmsnorm<bf16s>, dim3(batch), dim3(256), 0, h, x, D, w->attn_norm, (float)s->eps, (bf16s*)lw.xn);
     launch_gemv<bf16s>(h, pq, lw.xn, batch, D, w->Wqkv_T, n_qkv(*s), lw.part);
-    POP_LAUNCH(k_qkv_rope<bf16s>, qkv_grid(batch, *s), dim3(256), 0, h, lw.part, pq.chunks, batch,
+    POP_LAUNCH((k_qkv_rope<bf16s, kSumLanes>), qkv_grid(batch, *s, kSumLanes), dim3(256), 0, h, lw.part, pq.chunks, batch,
                s->n_heads, s->n_kv_heads, s->head_dim, 1, 0, pos, s->rope_theta, s->cache_len, lw.q,
                (bf16s*)K_cache, (bf16s*)V_cache);
     launch_attn_decode<bf16s>(h, *s, batch, K_cache, V_cache, pos, lw);
@@ -624,14 +643,15 @@ extern "C" pop_status pop_layer_decode(float* x, int32_t batch, const pop_layer_
   } else {
     POP_LAUNCH(k_rmsnorm<float>, dim3(batch), dim3(256), 0, h, x, D, w->attn_norm, (float)s->eps, (float*)lw.xn);
     launch_gemv<float>(h, pq, lw.xn, batch, D, w->Wqkv_T, n_qkv(*s), lw.part);
-    POP_LAUNCH(k_qkv_rope<float>, qkv_grid(batch, *s), dim3(256), 0, h, lw.part, pq.chunks, batch,
+    POP_LAUNCH((k_qkv_rope<float, kSumLanes>), qkv_grid(batch, *s, kSumLanes), dim3(256), 0, h, lw.part, pq.chunks, batch,
                s->n_heads, s->n_kv_heads, s->head_dim, 1, 0, pos, s->rope_theta, s->cache_len, lw.q,
                (float*)K_cache, (float*)V_cache);
     launch_attn_decode<float>(h, *s, batch, K_cache, V_cache, pos, lw);
     launch_gemv<float>(h, po, lw.ao, batch, Hd, w->Wo_T, D, lw.part);
   }
   const int64_t n = (int64_t)batch * D;
-  POP_LAUNCH(k_sum_residual, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, h, lw.part, po.chunks, n, x);
+  POP_LAUNCH(k_sum_residual<kSumLanes>, dim3((unsigned)((n * kSumLanes + 255) / 256)), dim3(256), 0, h, lw.part,
+             po.chunks, n, x);
   if (dt == POP_BF16)
     POP_LAUNCH(k_rmsnorm<bf16s>, dim3(batch), dim3(256), 0, h, x, D, w->ffn_norm, (float)s->eps, (bf16s*)lw.xn);
   else
@@ -675,14 +695,14 @@ extern "C" pop_status pop_layer_prefill(float* x, int32_t batch, int32_t n_token
   else
     POP_LAUNCH(k_rmsnorm<float>, dim3((unsigned)M), dim3(256), 0, h, x, D, w->attn_norm, (float)s->eps, (float*)lw.xn);
   launch_gemm_kmajor(h, lw.xn, (int)M, D, w->Wqkv_T, D, n_qkv(*s), dt, lw.Y);
-  const dim3 gq = qkv_grid(M, *s);
+  const dim3 gq = qkv_grid(M, *s, 1);
   if (dt == POP_BF16) {
-    POP_LAUNCH(k_qkv_rope<bf16s>, gq, dim3(256), 0, h, lw.Y, 1, (int)M, s->n_heads, s->n_kv_heads, s->head_dim,
+    POP_LAUNCH((k_qkv_rope<bf16s, 1>), gq, dim3(256), 0, h, lw.Y, 1, (int)M, s->n_heads, s->n_kv_heads, s->head_dim,
                n_tokens, 0, (const int32_t*)nullptr, s->rope_theta, s->cache_len, lw.q, (bf16s*)K_cache,
                (bf16s*)V_cache);
     launch_attn_prefill<bf16s>(h, *s, batch, n_tokens, K_cache, V_cache, lw);
   } else {
-    POP_LAUNCH(k_qkv_rope<float>, gq, dim3(256), 0, h, lw.Y, 1, (int)M, s->n_heads, s->n_kv_heads, s->head_dim,
+    POP_LAUNCH((k_qkv_rope<float, 1>), gq, dim3(256), 0, h, lw.Y, 1, (int)M, s->n_heads, s->n_kv_heads, s->head_dim,
                n_tokens, 0, (const int32_t*)nullptr, s->rope_theta, s->cache_len, lw.q, (float*)K_cache,
                (float*)V_cache);
     launch_attn_prefill<float>(h, *s, batch, n_tokens, K_cache, V_cache, lw);

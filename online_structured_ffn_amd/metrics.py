@@ -101,3 +101,20 @@ def moe_decode_bytes(d: int, n_R: int, n_C: int, k: int, experts_reached: float,
     pair) and outputs."""
     per_expert = 2 * (n_R + n_C) * d * e + (n_R + k) * d * e
     return experts_reached * per_expert + 2 * tokens * d * e + 4 * tokens * d
+
+
+def attention_decode_bytes(d: int, n_heads: int, n_kv_heads: int, head_dim: int, n_keys: int, batch: int,
+                           e: int) -> dict:
+    """The attention half of one decode layer-step, per kernel: the q|k|v and
+    output projections read their weights and inputs once and write their
+    outputs (the partial sums of split reductions not counted); attention reads
+    the n_keys cached keys and values of every sequence once; RMSNorm reads x
+    and writes its output."""
+    nqkv = (n_heads + 2 * n_kv_heads) * head_dim
+    hd_all = n_heads * head_dim
+    return {
+        "qkv": d * nqkv * e + batch * d * e + batch * nqkv * 4,
+        "attn": 2 * batch * n_kv_heads * n_keys * head_dim * e + batch * hd_all * 4 + batch * hd_all * e,
+        "o": hd_all * d * e + batch * hd_all * e + batch * d * 4,
+        "norms": 2 * (batch * d * 4 + batch * d * e),
+    }

@@ -21,7 +21,7 @@ import numpy as np
 from .configs import WORKLOADS, Workload
 
 SEED_ROOT = 0x504F50
-T_GATE, T_UP, T_DOWN, T_PROMPT, T_DECODE, T_OUTLIER, T_ROUTER = range(7)
+T_GATE, T_UP, T_DOWN, T_PROMPT, T_DECODE, T_OUTLIER, T_ROUTER, T_QKV, T_O = range(9)
 
 
 def workload_id(w: Workload) -> int:
@@ -69,6 +69,22 @@ def layer_weights(w: Workload, layer: int, wid: int | None = None) -> dict:
         a = g.standard_normal(shape, dtype=np.float32) * np.float32(w.weight_std)
         out[name] = to_dtype(a, w.dtype)
     out["W_downT"] = np.ascontiguousarray(out["W_down"].T)
+    return out
+
+
+def attention_weights(w: Workload, layer: int, wid: int | None = None) -> dict:
+    """The attention half of a decoder layer: Wqkv_T [D, (H + 2 H_kv) hd] and
+    Wo_T [H hd, D] ~ N(0, weight_std^2) rounded to the workload dtype, RMSNorm
+    gains of 1 (fp32)."""
+    wid = workload_id(w) if wid is None else wid
+    a = w.extra["attention"]
+    H, Hkv, hd = a["n_heads"], a["n_kv_heads"], a["head_dim"]
+    out = {}
+    for name, tid, shape in (("Wqkv_T", T_QKV, (w.d, (H + 2 * Hkv) * hd)), ("Wo_T", T_O, (H * hd, w.d))):
+        g = rng(wid, layer, tid)
+        out[name] = to_dtype(g.standard_normal(shape, dtype=np.float32) * np.float32(w.weight_std), w.dtype)
+    out["attn_norm"] = np.ones(w.d, dtype=np.float32)
+    out["ffn_norm"] = np.ones(w.d, dtype=np.float32)
     return out
 
 
@@ -173,6 +189,24 @@ def torch_layer_weights(w: Workload, layer: int, device, wid: int | None = None)
         gen.manual_seed((SEED_ROOT << 24) ^ (wid << 16) ^ (layer << 4) ^ tid)
         t = torch.randn((w.d_ff, w.d), generator=gen, device=device, dtype=torch.float32)
         out[name] = (t * w.weight_std).to(dt).contiguous()
+    return out
+
+
+def torch_attention_weights(w: Workload, layer: int, device, wid: int | None = None):
+    """Device-drawn counterpart of :func:`attention_weights` (same
+    distribution, different random stream)."""
+    import torch
+    wid = workload_id(w) if wid is None else wid
+    a = w.extra["attention"]
+    H, Hkv, hd = a["n_heads"], a["n_kv_heads"], a["head_dim"]
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = {}
+    for name, tid, shape in (("Wqkv_T", T_QKV, (w.d, (H + 2 * Hkv) * hd)), ("Wo_T", T_O, (H * hd, w.d))):
+        gen = torch.Generator(device=device)
+        gen.manual_seed((SEED_ROOT << 24) ^ (wid << 16) ^ (layer << 4) ^ tid)
+        out[name] = (torch.randn(shape, generator=gen, device=device) * w.weight_std).to(dt).contiguous()
+    out["attn_norm"] = torch.ones(w.d, dtype=torch.float32, device=device)
+    out["ffn_norm"] = torch.ones(w.d, dtype=torch.float32, device=device)
     return out
 
 
