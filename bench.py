@@ -901,8 +901,9 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
 
     # per-kernel pass: the decode calls with libpop's trace hook
     S = min(args.kernel_steps, T)
-    head = ["k_rmsnorm", "k_gemv_kmajor(qkv)", "k_qkv_rope", "k_attn_decode", "k_attn_combine", "k_gemv_kmajor(o)",
-            "k_sum_residual", "k_rmsnorm(ffn)", "-"]
+    # the library's batch <= 2 form runs the attention RMSNorm inside the q|k|v projection
+    head = ((["k_gemv_kmajor(norm+qkv)"] if B <= 2 else ["k_rmsnorm", "k_gemv_kmajor(qkv)"])
+            + ["k_qkv_rope", "k_attn_decode", "k_gemv_kmajor(merge+o)", "k_sum_residual", "k_rmsnorm(ffn)", "-"])
     fused = B == 1 and 0 < n_C <= 4096 and k > 0
     labels_pop = head + (["k_pop_step.1", "k_pop_step.2", "k_pop_finish"] if fused else ["ffn#0"]) + ["k_add"]
     labels_dense = head + (["k_pop_step.0(dense)", "k_pop_finish(dense)"] if B == 1 else ["ffn#0"]) + ["k_add"]
@@ -941,7 +942,8 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
     log("[bench] dense-FFN layer kernels (us): " + ", ".join(f"{n} {v:.2f}" for n, v in kus_dense.items()))
     plan = metrics.fused_plan(n_R, n_C, k, d, e)
     att_k = metrics.attention_decode_bytes(d, H, Hkv, hd, N + (S + 1) / 2, B, e)
-    kbytes = {"k_gemv_kmajor(qkv)": att_k["qkv"], "k_gemv_kmajor(o)": att_k["o"], "k_attn_decode": att_k["attn"]}
+    kbytes = {"k_gemv_kmajor(norm+qkv)" if B <= 2 else "k_gemv_kmajor(qkv)": att_k["qkv"],
+              "k_gemv_kmajor(merge+o)": att_k["o"], "k_attn_decode": att_k["attn"]}
     if fused:
         kbytes.update({"k_pop_step.1": plan["bytes"][1], "k_pop_step.2": plan["bytes"][2],
                        "k_pop_finish": plan["bytes"][3]})

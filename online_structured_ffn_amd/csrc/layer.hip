@@ -16,13 +16,15 @@
 //   k_gemv_kmajor   decode projections y = x W (W K-major [K, N]): one wave per
 //                   (512 or 256 columns, chunk of rows, group of tokens), fp32
 //                   partial sums per row chunk.  HBM-bound: every weight byte
-//                   is read once.
+//                   is read once.  Its input is x itself, the RMSNorm of the
+//                   residual stream computed in the wave (the q|k|v
+//                   projection at batch <= 2), or the merge of the attention
+//                   slices (the output projection).
 //   k_qkv_rope      sums the row chunks of q|k|v, turns q and k, writes the
 //                   key/value cache entries (dtype) and q (fp32).
 //   k_attn_decode   one query per (sequence, head): the keys are split into
 //                   64-key slices, one block each, online softmax inside the
 //                   slice; (max, sum, unnormalised output) per slice.
-//   k_attn_combine  merges the slices (log-sum-exp rescaling, slice order).
 //   k_attn_prefill  the prompt: a block per (16 queries, head, sequence) runs
 //                   over 32-key tiles of the causal window in LDS.
 //   k_sum_residual, k_add   the residual updates of the stream x (fp32).
@@ -47,7 +49,10 @@ constexpr int kPfK = 32;            // keys per prompt-attention tile
 #define POP_GEMV_WAVES 2048
 #endif
 constexpr int kGemvTarget = POP_GEMV_WAVES;  // waves a decode projection aims for
-constexpr int kGemvInflight = 16;            // row loads in flight per lane
+#ifndef POP_GEMV_INFLIGHT
+#define POP_GEMV_INFLIGHT 16
+#endif
+constexpr int kGemvInflight = POP_GEMV_INFLIGHT;  // row loads in flight per lane
 constexpr int kSumLanes = 16;                // lanes that share one output's chunk sum
 constexpr int kLayerMaxBatch = 64;  // decode rows per layer call
 
@@ -94,16 +99,68 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
 }
 
 // ---------------------------------------------------------------- decode projections
+// The projection's input x[b][k], by mode:
+//   kXPlain  x in the dtype, [B, K];
+//   kXNorm   RMSNorm of the fp32 residual stream res [B, K] with gain g,
+//            rounded to the dtype as a stored RMSNorm output would be: each
+//            wave first sums res[b]^2 itself (lane l over the float4 slots
+//            l, l + 64, ..., then a butterfly: every wave gets the same bits);
+//   kXCombine the attention output: the log-sum-exp merge of the 64-key slices
+//            (ml [B, H, S, 2], po [B, H, S, hd]) for row k = head * hd + d,
+//            rounded to the dtype; lane u of the wave merges row r0 + u of its
+//            chunk (rows_per_chunk <= 64) and the values are broadcast by lane.
+constexpr int kXPlain = 0, kXNorm = 1, kXCombine = 2;
+
+struct GemvIn {
+  const void* x;       // kXPlain
+  const float* res;    // kXNorm
+  const float* gain;
+  float eps;
+  const float* ml;     // kXCombine
+  const float* po;
+  int slices, hd, H;
+};
+
+template <typename T>
+__device__ __forceinline__ float round_to(float v) {
+  if constexpr (sizeof(T) == 2) {
+    uint32_t b = __float_as_uint(v);
+    b += 0x7fffu + ((b >> 16) & 1u);
+    return __uint_as_float((b >> 16) << 16);
+  } else {
+    return v;
+  }
+}
+
+// Merged attention output of (sequence b, row k = head * hd + d), in the
+// order k_attn_combine uses.
+__device__ __forceinline__ float combine_row(const float* __restrict__ ml, const float* __restrict__ po, int S,
+                                             int hd, int H, int b, int k) {
+  const int h = k / hd, d = k % hd;
+  const int64_t base = ((int64_t)b * H + h) * S;
+  float M = -INFINITY;
+#pragma unroll 4
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * (base + s)]);
+  float l = 0.f, o = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < S; ++s) {
+    const float e = expf(ml[2 * (base + s)] - M);
+    l = fmaf(ml[2 * (base + s) + 1], e, l);
+    o = fmaf(po[(base + s) * hd + d], e, o);
+  }
+  return o / l;
+}
+
 // part[chunk][b][n] = sum over rows k of the chunk of x[b][k] W[k][n].
 // One wave per block: lane l owns columns n0 + V*l .. + V (one 16-byte load
-// per row); the wave streams rows_per_chunk rows, 16 loads in flight, for BT
-// tokens (blockIdx.z picks the token group).  Rows past the chunk are clamped
-// for the load and their x taken as 0; token slots past B read row B - 1 and
-// are not written.  N % V == 0; a lane whose columns lie past N loads the last
-// vector and writes nothing.
-template <typename T, int BT>
-__global__ __launch_bounds__(64) void k_gemv_kmajor(const T* __restrict__ x, int B, int K, const T* __restrict__ W,
-                                                    int N, int rows_per_chunk, float* __restrict__ part) {
+// per row); the wave streams rows_per_chunk rows, kGemvInflight loads in
+// flight, for BT tokens (blockIdx.z picks the token group).  Rows past the
+// chunk are clamped for the load and their x taken as 0; token slots past B
+// read row B - 1 and are not written.  N % V == 0; a lane whose columns lie
+// past N loads the last vector and writes nothing.
+template <typename T, int BT, int XM>
+__global__ __launch_bounds__(64) void k_gemv_kmajor(GemvIn in, int B, int K, const T* __restrict__ W, int N,
+                                                    int rows_per_chunk, float* __restrict__ part) {
   constexpr int V = Vec<T>::N;
   const int lane = threadIdx.x;
   const int n0 = (blockIdx.x * 64 + lane) * V;
@@ -112,25 +169,62 @@ __global__ __launch_bounds__(64) void k_gemv_kmajor(const T* __restrict__ x, int
   const int b0 = blockIdx.z * BT;
   const int r0 = chunk * rows_per_chunk;
   const int r1 = min(r0 + rows_per_chunk, K);
+  u32x4 w[kGemvInflight];
+#pragma unroll
+  for (int u = 0; u < kGemvInflight; ++u) w[u] = ld16_stream(W + (int64_t)min(r0 + u, r1 - 1) * N + nc);
+  float inv[BT];    // kXNorm: 1 / rms of each token's residual row
+  float mine[BT];   // kXCombine: the merged value of row r0 + lane
+#pragma unroll
+  for (int t = 0; t < BT; ++t) {
+    const int b = min(b0 + t, B - 1);
+    inv[t] = 0.f;
+    mine[t] = 0.f;
+    if constexpr (XM == kXNorm) {
+      const float4* xr = reinterpret_cast<const float4*>(in.res + (int64_t)b * K);
+      float q = 0.f;
+      for (int i = lane; i < K / 4; i += 64) {
+        const float4 v = xr[i];
+        q += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+      q = wave_sum(q);
+      inv[t] = 1.0f / sqrtf(q / (float)K + in.eps);
+    }
+    if constexpr (XM == kXCombine) {
+      if (r0 + lane < r1) mine[t] = round_to<T>(combine_row(in.ml, in.po, in.slices, in.hd, in.H, b, r0 + lane));
+    }
+  }
+  auto xval = [&](int t, int row) -> float {
+    const int b = min(b0 + t, B - 1);
+    if constexpr (XM == kXPlain) {
+      return elem_f((const T*)in.x, (int64_t)b * K + row);
+    } else if constexpr (XM == kXNorm) {
+      return round_to<T>(in.res[(int64_t)b * K + row] * inv[t] * in.gain[row]);
+    } else {
+      return __shfl(mine[t], row - r0);
+    }
+  };
   float acc[BT][V];
 #pragma unroll
   for (int t = 0; t < BT; ++t)
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[t][v] = 0.f;
   for (int r = r0; r < r1; r += kGemvInflight) {
-    u32x4 w[kGemvInflight];
+    if (r != r0) {
 #pragma unroll
-    for (int u = 0; u < kGemvInflight; ++u) w[u] = ld16_stream(W + (int64_t)min(r + u, r1 - 1) * N + nc);
+      for (int u = 0; u < kGemvInflight; ++u) w[u] = ld16_stream(W + (int64_t)min(r + u, r1 - 1) * N + nc);
+    }
 #pragma unroll
     for (int u = 0; u < kGemvInflight; ++u) {
       float wf[V];
       unpack(w[u], wf, T{});
       const bool ok = r + u < r1;
+      const int row = min(r + u, r1 - 1);
 #pragma unroll
       for (int t = 0; t < BT; ++t) {
-        const float xv = ok ? elem_f(x, (int64_t)min(b0 + t, B - 1) * K + min(r + u, r1 - 1)) : 0.f;
+        const float xv = xval(t, row);
+        const float xs = ok ? xv : 0.f;
 #pragma unroll
-        for (int v = 0; v < V; ++v) acc[t][v] = fmaf(xv, wf[v], acc[t][v]);
+        for (int v = 0; v < V; ++v) acc[t][v] = fmaf(xs, wf[v], acc[t][v]);
       }
     }
   }
@@ -298,25 +392,6 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
   }
 }
 
-// out[b, h*hd + d] = sum_s o_s[d] e^(m_s - M) / sum_s l_s e^(m_s - M),
-// M = max_s m_s, slices in order; one block of hd threads per (head, sequence).
-template <typename T>
-__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_ml, const float* __restrict__ part_o,
-                                                      int n_slices, int H, int hd, T* __restrict__ out) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  if (d >= hd) return;
-  const int64_t base = ((int64_t)b * H + h) * n_slices;
-  float M = -INFINITY;
-  for (int s = 0; s < n_slices; ++s) M = fmaxf(M, part_ml[2 * (base + s)]);
-  float l = 0.f, o = 0.f;
-  for (int s = 0; s < n_slices; ++s) {
-    const float e = expf(part_ml[2 * (base + s)] - M);
-    l = fmaf(part_ml[2 * (base + s) + 1], e, l);
-    o = fmaf(part_o[(base + s) * hd + d], e, o);
-  }
-  put_elem(out, ((int64_t)b * H + h) * hd + d, o / l);
-}
-
 // ---------------------------------------------------------------- prompt attention
 // Block (query tile qt, head h, sequence b): queries q0 .. q0 + 15 (q0 = 16 qt)
 // of the sequence's N prompt tokens, keys 0 .. q0 + 15 in 32-key tiles staged
@@ -426,7 +501,7 @@ struct GemvPlan {
 
 // Rows per chunk: enough waves to fill the chip, but the partial sums kept
 // under an eighth of the weight bytes (they are written and read once more).
-static GemvPlan gemv_plan(int B, int K, int N, int esz) {
+static GemvPlan gemv_plan(int B, int K, int N, int esz, int max_rows = 0) {
   GemvPlan p;
   p.bt = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 16;
   p.groups = (B + p.bt - 1) / p.bt;
@@ -438,23 +513,23 @@ static GemvPlan gemv_plan(int B, int K, int N, int esz) {
   if (want < 1) want = 1;
   int rpc = (K + want - 1) / want;
   rpc = (rpc + kGemvInflight - 1) / kGemvInflight * kGemvInflight;
+  if (max_rows > 0 && rpc > max_rows) rpc = max_rows;
   p.rows_per_chunk = rpc;
   p.chunks = (K + rpc - 1) / rpc;
   return p;
 }
 
-template <typename T>
-static void launch_gemv(hipStream_t st, const GemvPlan& p, const void* x, int B, int K, const void* W, int N,
+template <typename T, int XM>
+static void launch_gemv(hipStream_t st, const GemvPlan& p, const GemvIn& in, int B, int K, const void* W, int N,
                         float* part) {
   const dim3 grid(p.col_blocks, p.chunks, p.groups);
-  const T* xx = (const T*)x;
   const T* ww = (const T*)W;
   switch (p.bt) {
-    case 1: POP_LAUNCH((k_gemv_kmajor<T, 1>), grid, dim3(64), 0, st, xx, B, K, ww, N, p.rows_per_chunk, part); break;
-    case 2: POP_LAUNCH((k_gemv_kmajor<T, 2>), grid, dim3(64), 0, st, xx, B, K, ww, N, p.rows_per_chunk, part); break;
-    case 4: POP_LAUNCH((k_gemv_kmajor<T, 4>), grid, dim3(64), 0, st, xx, B, K, ww, N, p.rows_per_chunk, part); break;
-    case 8: POP_LAUNCH((k_gemv_kmajor<T, 8>), grid, dim3(64), 0, st, xx, B, K, ww, N, p.rows_per_chunk, part); break;
-    default: POP_LAUNCH((k_gemv_kmajor<T, 16>), grid, dim3(64), 0, st, xx, B, K, ww, N, p.rows_per_chunk, part); break;
+    case 1: POP_LAUNCH((k_gemv_kmajor<T, 1, XM>), grid, dim3(64), 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
+    case 2: POP_LAUNCH((k_gemv_kmajor<T, 2, XM>), grid, dim3(64), 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
+    case 4: POP_LAUNCH((k_gemv_kmajor<T, 4, XM>), grid, dim3(64), 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
+    case 8: POP_LAUNCH((k_gemv_kmajor<T, 8, XM>), grid, dim3(64), 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
+    default: POP_LAUNCH((k_gemv_kmajor<T, 16, XM>), grid, dim3(64), 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
   }
 }
 
@@ -497,7 +572,6 @@ struct DecodeLayerWs {
   float* q;     // [B, H, hd]
   float* ml;    // [B, H, slices, 2]
   float* po;    // [B, H, slices, hd]
-  char* ao;     // attention output, dtype [B, H hd]
   float* y;     // FFN output [B, D]
   char* ffn;    // FFN workspace
   size_t total;
@@ -505,7 +579,7 @@ struct DecodeLayerWs {
 
 static DecodeLayerWs decode_layer_ws(int B, const pop_layer_shape& s, pop_dtype dt, char* base) {
   const int e = elem_bytes(dt), Hd = s.n_heads * s.head_dim, S = n_slices(s);
-  const GemvPlan a = gemv_plan(B, s.d, n_qkv(s), e), o = gemv_plan(B, Hd, s.d, e);
+  const GemvPlan a = gemv_plan(B, s.d, n_qkv(s), e), o = gemv_plan(B, Hd, s.d, e, 64);
   const size_t part = (size_t)std::max((int64_t)a.chunks * n_qkv(s), (int64_t)o.chunks * s.d) * B * 4;
   DecodeLayerWs w;
   size_t off = 0;
@@ -519,7 +593,6 @@ static DecodeLayerWs decode_layer_ws(int B, const pop_layer_shape& s, pop_dtype 
   w.q = (float*)take((size_t)B * Hd * 4);
   w.ml = (float*)take((size_t)B * s.n_heads * S * 2 * 4);
   w.po = (float*)take((size_t)B * s.n_heads * S * s.head_dim * 4);
-  w.ao = take((size_t)B * Hd * e);
   w.y = (float*)take((size_t)B * s.d * 4);
   w.ffn = take(pop_decode_workspace_bytes(B, s.d, s.d_ff));
   w.total = off;
@@ -564,7 +637,6 @@ static void launch_attn_decode(hipStream_t st, const pop_layer_shape& s, int B, 
   else
     POP_LAUNCH((k_attn_decode<T, 128>), grid, dim3(256), 0, st, w.q, (const T*)Kc, (const T*)Vc, s.cache_len, s.n_heads,
                s.n_kv_heads, pos, S, w.ml, w.po);
-  POP_LAUNCH(k_attn_combine<T>, dim3(s.n_heads, B), dim3(128), 0, st, w.ml, w.po, S, s.n_heads, s.head_dim, (T*)w.ao);
 }
 
 template <typename T>
@@ -577,6 +649,46 @@ static void launch_attn_prefill(hipStream_t st, const pop_layer_shape& s, int B,
   else
     POP_LAUNCH((k_attn_prefill<T, 128>), grid, dim3(256), 0, st, w.q, (const T*)Kc, (const T*)Vc, N, s.cache_len,
                s.n_heads, s.n_kv_heads, (T*)w.ao);
+}
+
+// The attention half of a decode step, through the FFN's RMSNorm: x becomes h
+// and lw.xn RMSNorm(h).  At batch <= 2 the attention RMSNorm runs inside the
+// q|k|v projection; the slices' merge always runs inside the output
+// projection.
+template <typename T>
+static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, const pop_layer_shape& s,
+                                           const pop_layer_weights* w, void* Kc, void* Vc, const int32_t* pos,
+                                           const DecodeLayerWs& lw) {
+  const int D = s.d, Hd = s.n_heads * s.head_dim, e = sizeof(T);
+  const GemvPlan pq = gemv_plan(batch, D, n_qkv(s), e), po = gemv_plan(batch, Hd, D, e, 64);
+  const bool fuse_norm = batch <= 2;
+  GemvIn qin{};
+  if (fuse_norm) {
+    qin.res = x;
+    qin.gain = w->attn_norm;
+    qin.eps = (float)s.eps;
+    launch_gemv<T, kXNorm>(h, pq, qin, batch, D, w->Wqkv_T, n_qkv(s), lw.part);
+  } else {
+    POP_LAUNCH(k_rmsnorm<T>, dim3(batch), dim3(256), 0, h, x, D, w->attn_norm, (float)s.eps, (T*)lw.xn);
+    qin.x = lw.xn;
+    launch_gemv<T, kXPlain>(h, pq, qin, batch, D, w->Wqkv_T, n_qkv(s), lw.part);
+  }
+  POP_LAUNCH((k_qkv_rope<T, kSumLanes>), qkv_grid(batch, s, kSumLanes), dim3(256), 0, h, lw.part, pq.chunks, batch,
+             s.n_heads, s.n_kv_heads, s.head_dim, 1, 0, pos, s.rope_theta, s.cache_len, lw.q, (T*)Kc, (T*)Vc);
+  launch_attn_decode<T>(h, s, batch, Kc, Vc, pos, lw);
+  GemvIn oin{};
+  oin.ml = lw.ml;
+  oin.po = lw.po;
+  oin.slices = n_slices(s);
+  oin.hd = s.head_dim;
+  oin.H = s.n_heads;
+  launch_gemv<T, kXCombine>(h, po, oin, batch, Hd, w->Wo_T, D, lw.part);
+  // (A last-block-done fusion of the next two launches measured slower: every
+  // block's device-scope release writes back its XCD's L2.)
+  const int64_t n = (int64_t)batch * D;
+  POP_LAUNCH(k_sum_residual<kSumLanes>, dim3((unsigned)((n * kSumLanes + 255) / 256)), dim3(256), 0, h, lw.part,
+             po.chunks, n, x);
+  POP_LAUNCH(k_rmsnorm<T>, dim3(batch), dim3(256), 0, h, x, D, w->ffn_norm, (float)s.eps, (T*)lw.xn);
 }
 
 static pop_status launched_layer() {
@@ -629,33 +741,13 @@ extern "C" pop_status pop_layer_decode(float* x, int32_t batch, const pop_layer_
       return fail(POP_ERR_INVALID_ARGUMENT, "R or C is NULL with a nonzero size");
   }
   hipStream_t h = (hipStream_t)stream;
-  const int D = s->d, Hd = s->n_heads * s->head_dim, e = elem_bytes(dt);
-  const GemvPlan pq = gemv_plan(batch, D, n_qkv(*s), e), po = gemv_plan(batch, Hd, D, e);
   trace_mark(h);
-  if (dt == POP_BF16) {
-    POP_LAUNCH(k_rmsnorm<bf16s>, dim3(batch), dim3(256), 0, h, x, D, w->attn_norm, (float)s->eps, (bf16s*)lw.xn);
-    launch_gemv<bf16s>(h, pq, lw.xn, batch, D, w->Wqkv_T, n_qkv(*s), lw.part);
-    POP_LAUNCH((k_qkv_rope<bf16s, kSumLanes>), qkv_grid(batch, *s, kSumLanes), dim3(256), 0, h, lw.part, pq.chunks, batch,
-               s->n_heads, s->n_kv_heads, s->head_dim, 1, 0, pos, s->rope_theta, s->cache_len, lw.q,
-               (bf16s*)K_cache, (bf16s*)V_cache);
-    launch_attn_decode<bf16s>(h, *s, batch, K_cache, V_cache, pos, lw);
-    launch_gemv<bf16s>(h, po, lw.ao, batch, Hd, w->Wo_T, D, lw.part);
-  } else {
-    POP_LAUNCH(k_rmsnorm<float>, dim3(batch), dim3(256), 0, h, x, D, w->attn_norm, (float)s->eps, (float*)lw.xn);
-    launch_gemv<float>(h, pq, lw.xn, batch, D, w->Wqkv_T, n_qkv(*s), lw.part);
-    POP_LAUNCH((k_qkv_rope<float, kSumLanes>), qkv_grid(batch, *s, kSumLanes), dim3(256), 0, h, lw.part, pq.chunks, batch,
-               s->n_heads, s->n_kv_heads, s->head_dim, 1, 0, pos, s->rope_theta, s->cache_len, lw.q,
-               (float*)K_cache, (float*)V_cache);
-    launch_attn_decode<float>(h, *s, batch, K_cache, V_cache, pos, lw);
-    launch_gemv<float>(h, po, lw.ao, batch, Hd, w->Wo_T, D, lw.part);
-  }
-  const int64_t n = (int64_t)batch * D;
-  POP_LAUNCH(k_sum_residual<kSumLanes>, dim3((unsigned)((n * kSumLanes + 255) / 256)), dim3(256), 0, h, lw.part,
-             po.chunks, n, x);
   if (dt == POP_BF16)
-    POP_LAUNCH(k_rmsnorm<bf16s>, dim3(batch), dim3(256), 0, h, x, D, w->ffn_norm, (float)s->eps, (bf16s*)lw.xn);
+    enqueue_layer_decode_attention<bf16s>(h, x, batch, *s, w, K_cache, V_cache, pos, lw);
   else
-    POP_LAUNCH(k_rmsnorm<float>, dim3(batch), dim3(256), 0, h, x, D, w->ffn_norm, (float)s->eps, (float*)lw.xn);
+    enqueue_layer_decode_attention<float>(h, x, batch, *s, w, K_cache, V_cache, pos, lw);
+  const int D = s->d;
+  const int64_t n = (int64_t)batch * D;
   st = dense_ffn ? pop_dense_ffn_decode(lw.xn, batch, D, w->W_gate, w->W_up, w->W_downT, s->d_ff, dt, lw.y, lw.ffn,
                                         ffn_bytes, stream)
                  : pop_decode_ffn(lw.xn, batch, D, w->W_gate, w->W_up, w->W_downT, s->d_ff, dt, R, n_R, C, n_C, r,
