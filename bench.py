@@ -790,6 +790,7 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
     decode step through every layer (pop_layer_decode), the position advanced on
     the device inside each step's graph.  The dense comparator runs the same
     layers with the dense FFN."""
+    from online_structured_ffn_amd import profiling
     a = w.extra["attention"]
     H, Hkv, hd = a["n_heads"], a["n_kv_heads"], a["head_dim"]
     L = args.layers or w.layers
@@ -949,6 +950,9 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
                        "k_pop_finish": plan["bytes"][3]})
     dom = max((n for n in kbytes if n in kus), key=lambda n: kus[n], default=None)
     dom_gbps = kbytes[dom] / (kus[dom] * 1e-6) / 1e9 if dom else None
+    # the same kernel at the same shape as the FFN workload's profiled one: its counters apply
+    same_ffn = dom == "k_pop_step.2" and (d, d_ff, w.r, w.gamma, B, w.dtype) == (4096, 11008, 0.299, 0.1, 1, "bf16")
+    tb = profiling.traffic_bytes("pop::k_pop_step<pop::bf16s, 2, false, 2>") if same_ffn else None
     cpu = None if args.no_cpu_baseline else cpu_baseline_layer(w, T, args.cpu_seconds)
     out = {
         "metric": "decoder-layer decode tokens/s per layer (dense attention + POP FFN); HBM GB/s vs peak",
@@ -977,7 +981,11 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": None if dom_gbps is None else round(dom_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": None if tb is None else tb[0] + tb[1],
+            "traffic_source": (None if tb is None else
+                               "rocprofv3 FETCH_SIZE + WRITE_SIZE per dispatch of the same kernel at the same shape "
+                               "in the FFN workload, scaled by a 256 MiB copy "
+                               "(profiles/decode_kernels_llama2_7b_b1_hbm_traffic.md)"),
             "bytes_per_launch": None if dom is None else round(kbytes[dom]),
             "avg_launch_us": None if dom is None else round(kus[dom], 3),
         },
