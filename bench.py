@@ -906,8 +906,9 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
     head = ((["k_gemv_kmajor(norm+qkv)"] if B <= 2 else ["k_rmsnorm", "k_gemv_kmajor(qkv)"])
             + ["k_qkv_rope", "k_attn_decode", "k_gemv_kmajor(merge+o)", "k_sum_residual", "k_rmsnorm(ffn)", "-"])
     fused = B == 1 and 0 < n_C <= 4096 and k > 0
-    labels_pop = head + (["k_pop_step.1", "k_pop_step.2", "k_pop_finish"] if fused else ["ffn#0"]) + ["k_add"]
-    labels_dense = head + (["k_pop_step.0(dense)", "k_pop_finish(dense)"] if B == 1 else ["ffn#0"]) + ["k_add"]
+    # at batch 1 the FFN's last kernel adds its output into the residual stream (no k_add)
+    labels_pop = head + (["k_pop_step.1", "k_pop_step.2", "k_pop_finish(+h)"] if fused else ["ffn#0", "k_add"])
+    labels_dense = head + (["k_pop_step.0(dense)", "k_pop_finish(dense,+h)"] if B == 1 else ["ffn#0", "k_add"])
     tracer = pop.Tracer(S * L * (len(labels_pop) + len(labels_dense) + 2) + 8, pop.Tracer.DISABLE_SYSTEM_FENCE)
     marks = []
     for dense, labels in ((False, labels_pop), (True, labels_dense)):
@@ -947,7 +948,7 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
               "k_gemv_kmajor(merge+o)": att_k["o"], "k_attn_decode": att_k["attn"]}
     if fused:
         kbytes.update({"k_pop_step.1": plan["bytes"][1], "k_pop_step.2": plan["bytes"][2],
-                       "k_pop_finish": plan["bytes"][3]})
+                       "k_pop_finish(+h)": plan["bytes"][3] + 4 * d})
     dom = max((n for n in kbytes if n in kus), key=lambda n: kus[n], default=None)
     dom_gbps = kbytes[dom] / (kus[dom] * 1e-6) / 1e9 if dom else None
     # the same kernel at the same shape as the FFN workload's profiled one: its counters apply

@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
                                                             const int32_t* __restrict__ sel,
                                                             const int32_t* __restrict__ pos, int k,
                                                             const T* __restrict__ WdT, int d, int d_ff,
-                                                            float* __restrict__ y) {
+                                                            float* __restrict__ y, int accumulate) {
   constexpr int V = Vec<T>::N;
   constexpr int LR = kFinCols / V;       // lanes per W_downT row
   constexpr int RPW = 64 / LR;           // W_downT rows per wave instruction
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
     float t = red[0][threadIdx.x];
 #pragma unroll
     for (int w2 = 1; w2 < kFinThreads / 64; ++w2) t += red[w2][threadIdx.x];
-    y[c0 + threadIdx.x] = t;
+    y[c0 + threadIdx.x] = accumulate ? y[c0 + threadIdx.x] + t : t;  // accumulate: y += FFN(x)
   }
 }
 
@@ -922,7 +922,7 @@ template <typename T>
 static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, const void* Wu, const void* WdT,
                          int d_ff, const int32_t* R, int n_R, const int32_t* C, int n_C, int k, float* y,
                          const DecodeWs& w, hipStream_t aux = nullptr, hipEvent_t fork = nullptr,
-                         hipEvent_t join = nullptr) {
+                         hipEvent_t join = nullptr, bool accumulate = false) {
   constexpr int V = Vec<T>::N;
   const int nv = (d + kFusedThreads * V - 1) / (kFusedThreads * V);
   if (nv > 4) return false;
@@ -996,12 +996,26 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
   if (k > 0) {
     POP_LAUNCH((k_pop_finish<T, true>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
                (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, k, (const T*)WdT, d,
-               d_ff, y);
+               d_ff, y, (int)accumulate);
   } else {
     POP_LAUNCH((k_pop_finish<T, false>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
                (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, 0, (const T*)WdT, d,
-               d_ff, y);
+               d_ff, y, (int)accumulate);
   }
+  return true;
+}
+
+// The fused path's launch conditions (launch_fused returns false, before any
+// launch, when they fail).
+template <typename T>
+static bool fused_fits(int d, int n_R, int n_C) {
+  constexpr int V = Vec<T>::N;
+  if ((d + kFusedThreads * V - 1) / (kFusedThreads * V) > 4) return false;
+  const int nbC = n_C > 0 ? (n_C + POP_FUSED_CROWS - 1) / POP_FUSED_CROWS : 0;
+  if (nbC > 0 && (n_C + nbC - 1) / nbC > kFusedMaxRows) return false;
+  int nbR = n_R > 0 ? (n_R + 7) / 8 : 0;
+  if (nbR > kFusedRBlocks) nbR = kFusedRBlocks;
+  if (nbR > 0 && (n_R + nbR - 1) / nbR > kFusedMaxRows) return false;
   return true;
 }
 
@@ -1039,6 +1053,31 @@ using namespace pop;
   ((dt) == POP_BF16 ? FN<bf16s>(__VA_ARGS__) : FN<float>(__VA_ARGS__))
 
 namespace pop {
+bool decode_ffn_accumulate_b1(const void* x, int32_t d, const void* W_gate, const void* W_up, const void* W_downT,
+                              int32_t d_ff, pop_dtype dt, bool dense, const int32_t* R, int32_t n_R,
+                              const int32_t* C, int32_t n_C, double r, float* y, int32_t* selected, void* ws,
+                              void* stream) {
+  if (dense) {
+    R = nullptr;
+    n_R = d_ff;
+    C = nullptr;
+    n_C = 0;
+  }
+  if (n_R + n_C <= 0) return false;
+  if (!(dt == POP_BF16 ? fused_fits<bf16s>(d, n_R, n_C) : fused_fits<float>(d, n_R, n_C))) return false;
+  const int32_t k = dense ? 0 : topk_count(d_ff, r, n_R, n_C);
+  DecodeWs w;
+  decode_ws_layout(1, d, d_ff, (char*)ws, &w);
+  const int32_t* Rk = dense ? nullptr : (R != nullptr ? R : w.Q);  // NULL R: identity (every channel)
+  const int32_t* Ck = C != nullptr ? C : w.Q;
+  DecodeWs wf = w;
+  if (selected != nullptr) wf.sel = selected;
+  hipStream_t st = (hipStream_t)stream;
+  trace_mark(st);
+  return POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, Rk, n_R, Ck, n_C, k, y, wf, nullptr,
+                      nullptr, nullptr, true);
+}
+
 float* decode_ws_z(void* ws, int32_t batch, int32_t d, int32_t d_ff) {
   DecodeWs w;
   decode_ws_layout(batch, d, d_ff, (char*)ws, &w);

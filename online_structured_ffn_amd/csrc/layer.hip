@@ -27,7 +27,9 @@
 //                   slice; (max, sum, unnormalised output) per slice.
 //   k_attn_prefill  the prompt: a block per (16 queries, head, sequence) runs
 //                   over 32-key tiles of the causal window in LDS.
-//   k_sum_residual, k_add   the residual updates of the stream x (fp32).
+//   k_sum_residual, k_add   the residual updates of the stream x (fp32); at
+//                   batch 1 the FFN's last kernel adds its output into x instead
+//                   of k_add.
 // The prompt's projections use the prompt FFN's matrix-core GEMM
 // (launch_gemm_kmajor).  The FFN is pop_decode_ffn / pop_dense_ffn_decode /
 // pop_prefill_ffn_partition.
@@ -234,8 +236,10 @@ __global__ __launch_bounds__(64) void k_gemv_kmajor(GemvIn in, int B, int K, con
     if (b0 + t < B) {
       float* o = part + ((int64_t)chunk * B + b0 + t) * N + n0;
 #pragma unroll
-      for (int v = 0; v < V; v += 4)
+      for (int v = 0; v < V; v += 4) {
+        // (non-temporal stores here measured slower: the next kernel then misses in L2)
         *reinterpret_cast<float4*>(o + v) = make_float4(acc[t][v], acc[t][v + 1], acc[t][v + 2], acc[t][v + 3]);
+      }
     }
   }
 }
@@ -748,6 +752,10 @@ extern "C" pop_status pop_layer_decode(float* x, int32_t batch, const pop_layer_
     enqueue_layer_decode_attention<float>(h, x, batch, *s, w, K_cache, V_cache, pos, lw);
   const int D = s->d;
   const int64_t n = (int64_t)batch * D;
+  // batch 1: the FFN's last kernel adds its output to x (= h) itself
+  if (batch == 1 && decode_ffn_accumulate_b1(lw.xn, D, w->W_gate, w->W_up, w->W_downT, s->d_ff, dt, dense_ffn != 0, R,
+                                             n_R, C, n_C, r, x, selected, lw.ffn, stream))
+    return launched_layer();
   st = dense_ffn ? pop_dense_ffn_decode(lw.xn, batch, D, w->W_gate, w->W_up, w->W_downT, s->d_ff, dt, lw.y, lw.ffn,
                                         ffn_bytes, stream)
                  : pop_decode_ffn(lw.xn, batch, D, w->W_gate, w->W_up, w->W_downT, s->d_ff, dt, R, n_R, C, n_C, r,

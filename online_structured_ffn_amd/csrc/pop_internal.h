@@ -39,6 +39,17 @@ void launch_partition_lists(void* stream, const float* I, int32_t d_ff, int32_t 
 // live R u C columns, R first; defined in decode.hip).
 float* decode_ws_z(void* ws, int32_t batch, int32_t d, int32_t d_ff);
 
+// pop_decode_ffn (or, with dense, pop_dense_ffn_decode) at batch 1 with
+// y += FFN(x) instead of y = FFN(x), for a caller that adds the FFN to a
+// residual stream; the caller has validated the arguments and ws holds
+// pop_decode_workspace_bytes(1, d, d_ff).  Returns false, having enqueued
+// nothing, when the step does not take the fused three-launch path (defined
+// in decode.hip).
+bool decode_ffn_accumulate_b1(const void* x, int32_t d, const void* W_gate, const void* W_up, const void* W_downT,
+                              int32_t d_ff, pop_dtype dt, bool dense, const int32_t* R, int32_t n_R,
+                              const int32_t* C, int32_t n_C, double r, float* y, int32_t* selected, void* ws,
+                              void* stream);
+
 // Records the next caller-provided trace event on `stream` (no-op unless
 // pop_set_trace_events armed this thread).
 void trace_mark(void* stream);
