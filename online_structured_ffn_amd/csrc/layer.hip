@@ -56,6 +56,10 @@ constexpr int kGemvTarget = POP_GEMV_WAVES;  // waves a decode projection aims f
 #endif
 constexpr int kGemvInflight = POP_GEMV_INFLIGHT;  // row loads in flight per lane
 constexpr int kSumLanes = 16;                // lanes that share one output's chunk sum
+#ifndef POP_GEMV_WPB
+#define POP_GEMV_WPB 1
+#endif
+constexpr int kGemvWaves = POP_GEMV_WPB;     // waves per block, on adjacent column groups of the same rows
 constexpr int kLayerMaxBatch = 64;  // decode rows per layer call
 
 __device__ __forceinline__ float elem_f(const float* p, int64_t i) { return p[i]; }
@@ -161,11 +165,11 @@ __device__ __forceinline__ float combine_row(const float* __restrict__ ml, const
 // read row B - 1 and are not written.  N % V == 0; a lane whose columns lie
 // past N loads the last vector and writes nothing.
 template <typename T, int BT, int XM>
-__global__ __launch_bounds__(64) void k_gemv_kmajor(GemvIn in, int B, int K, const T* __restrict__ W, int N,
-                                                    int rows_per_chunk, float* __restrict__ part) {
+__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_kmajor(GemvIn in, int B, int K, const T* __restrict__ W,
+                                                                 int N, int rows_per_chunk, float* __restrict__ part) {
   constexpr int V = Vec<T>::N;
-  const int lane = threadIdx.x;
-  const int n0 = (blockIdx.x * 64 + lane) * V;
+  const int lane = threadIdx.x & 63;
+  const int n0 = ((blockIdx.x * kGemvWaves + (int)(threadIdx.x >> 6)) * 64 + lane) * V;
   const int nc = min(n0, N - V);
   const int chunk = blockIdx.y;
   const int b0 = blockIdx.z * BT;
@@ -526,14 +530,15 @@ static GemvPlan gemv_plan(int B, int K, int N, int esz, int max_rows = 0) {
 template <typename T, int XM>
 static void launch_gemv(hipStream_t st, const GemvPlan& p, const GemvIn& in, int B, int K, const void* W, int N,
                         float* part) {
-  const dim3 grid(p.col_blocks, p.chunks, p.groups);
+  const dim3 grid((p.col_blocks + kGemvWaves - 1) / kGemvWaves, p.chunks, p.groups);
+  const dim3 blk(64 * kGemvWaves);
   const T* ww = (const T*)W;
   switch (p.bt) {
-    case 1: POP_LAUNCH((k_gemv_kmajor<T, 1, XM>), grid, dim3(64), 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
-    case 2: POP_LAUNCH((k_gemv_kmajor<T, 2, XM>), grid, dim3(64), 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
-    case 4: POP_LAUNCH((k_gemv_kmajor<T, 4, XM>), grid, dim3(64), 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
-    case 8: POP_LAUNCH((k_gemv_kmajor<T, 8, XM>), grid, dim3(64), 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
-    default: POP_LAUNCH((k_gemv_kmajor<T, 16, XM>), grid, dim3(64), 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
+    case 1: POP_LAUNCH((k_gemv_kmajor<T, 1, XM>), grid, blk, 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
+    case 2: POP_LAUNCH((k_gemv_kmajor<T, 2, XM>), grid, blk, 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
+    case 4: POP_LAUNCH((k_gemv_kmajor<T, 4, XM>), grid, blk, 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
+    case 8: POP_LAUNCH((k_gemv_kmajor<T, 8, XM>), grid, blk, 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
+    default: POP_LAUNCH((k_gemv_kmajor<T, 16, XM>), grid, blk, 0, st, in, B, K, ww, N, p.rows_per_chunk, part); break;
   }
 }
 
