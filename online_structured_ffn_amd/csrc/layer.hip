@@ -481,6 +481,188 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
   for (int i = 0; i < DI; ++i) put_elem(dst, u + 16 * i, o[i] / l_run);
 }
 
+// ---------------------------------------------------------------- prompt attention, matrix cores
+// bf16: S = Q K^T and O += P V on v_mfma_f32_16x16x32_bf16.  Block (query tile
+// of 64, head h, sequence b); wave w owns queries q0 + 16 w + [0, 16).  Per
+// 64-key tile of the causal window: K staged in LDS key-major (the B operand of
+// Q K^T reads 8 consecutive dims of one key), V staged transposed (the B
+// operand of P V reads 8 consecutive keys of one dim), both with padded pitches.
+// The fp32 operands q and P enter as two bf16 parts each, hi = bf16(v) and
+// lo = bf16(v - hi), and both parts are multiplied (about 16 significant bits,
+// so the products carry fp32-level error, not bf16 rounding of q and P); K
+// and V are bf16 already.  The scores are scaled by 1/sqrt(hd) in fp32.
+// Online softmax on the accumulators: lane l holds rows 4 (l >> 4) + e,
+// columns l & 15 of each 16 x 16 tile, so a row's max and sum are butterflies
+// over the 16 lanes sharing l >> 4.  P's parts go to the wave's LDS slices and
+// are read back as A operands.  Query rows past N load row N - 1 and are not
+// written.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kMq = 64, kMk = 64;
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restrict__ q, const bf16s* __restrict__ Kc,
+                                                           const bf16s* __restrict__ Vc, int N, int L, int H, int Hkv,
+                                                           bf16s* __restrict__ out) {
+  constexpr int KP = HD + 8;    // Ks pitch (bf16)
+  constexpr int VP = kMk + 8;   // Vt and Ps pitch (bf16)
+  constexpr int KS = HD / 32;   // k-steps of Q K^T
+  constexpr int DT = HD / 16;   // 16-dim output tiles
+  __shared__ __align__(16) uint16_t Ks[kMk * KP];
+  __shared__ __align__(16) uint16_t Vt[HD * VP];
+  __shared__ __align__(16) uint16_t Ps[4][2][16 * VP];  // per wave: P's hi and lo parts
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q0 = qt * kMq;
+  const int kvh = h / (H / Hkv);
+  const bf16s* Kb = Kc + ((int64_t)b * Hkv + kvh) * L * HD;
+  const bf16s* Vb = Vc + ((int64_t)b * Hkv + kvh) * L * HD;
+  const int fr = lane & 15, fg = lane >> 4;
+  // Q fragments: row q0 + 16 wave + fr, dims 8 fg + 32 ks
+  bf16x8_t qa[KS], qb[KS];  // q's hi and lo parts
+  {
+    const int row = min(q0 + 16 * wave + fr, N - 1);
+    const float* qr = q + (((int64_t)b * N + row) * H + h) * HD;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4 a = *reinterpret_cast<const float4*>(qr + 32 * ks + 8 * fg);
+      const float4 c = *reinterpret_cast<const float4*>(qr + 32 * ks + 8 * fg + 4);
+      const float f[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+      u32x4 uh, ul;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t h0 = bf16_bits_rne(f[2 * x]), h1 = bf16_bits_rne(f[2 * x + 1]);
+        const uint32_t l0 = bf16_bits_rne(f[2 * x] - __uint_as_float(h0 << 16));
+        const uint32_t l1 = bf16_bits_rne(f[2 * x + 1] - __uint_as_float(h1 << 16));
+        uh[x] = h0 | (h1 << 16);
+        ul[x] = l0 | (l1 << 16);
+      }
+      qa[ks] = __builtin_bit_cast(bf16x8_t, uh);
+      qb[ks] = __builtin_bit_cast(bf16x8_t, ul);
+    }
+  }
+  const float scale = 1.0f / sqrtf((float)HD);
+  float m_run[4], l_run[4];
+  f32x4_t acc_o[DT];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m_run[e] = -INFINITY;
+    l_run[e] = 0.f;
+  }
+#pragma unroll
+  for (int t = 0; t < DT; ++t) acc_o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int kend = min(q0 + kMq, N);
+  for (int t0 = 0; t0 < kend; t0 += kMk) {
+    __syncthreads();
+    // K tile: row j = key t0 + j (clamped), 16-byte pieces
+    for (int i = tid; i < kMk * HD / 8; i += 256) {
+      const int j = i / (HD / 8), c = (i % (HD / 8)) * 8;
+      const int key = min(t0 + j, kend - 1);
+      *reinterpret_cast<u32x4*>(&Ks[j * KP + c]) = ld16(Kb + (int64_t)key * HD + c);
+    }
+    // V tile transposed: a thread takes keys 2p, 2p + 1 and dims c .. c + 7
+    for (int i = tid; i < (kMk / 2) * (HD / 8); i += 256) {
+      const int pr = i / (HD / 8), c = (i % (HD / 8)) * 8;
+      const int k0 = min(t0 + 2 * pr, kend - 1), k1 = min(t0 + 2 * pr + 1, kend - 1);
+      const u32x4 v0 = ld16(Vb + (int64_t)k0 * HD + c), v1 = ld16(Vb + (int64_t)k1 * HD + c);
+      uint32_t* vt32 = reinterpret_cast<uint32_t*>(Vt);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const uint32_t lo = (v0[x >> 1] >> ((x & 1) * 16)) & 0xffffu;
+        const uint32_t hi = (v1[x >> 1] >> ((x & 1) * 16)) & 0xffffu;
+        vt32[((c + x) * VP) / 2 + pr] = lo | (hi << 16);
+      }
+    }
+    __syncthreads();
+    // S = Q K^T for 4 tiles of 16 keys
+    f32x4_t sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t kb = *reinterpret_cast<const bf16x8_t*>(&Ks[(16 * j + fr) * KP + 32 * ks + 8 * fg]);
+        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, sc[j], 0, 0, 0);
+        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[ks], kb, sc[j], 0, 0, 0);
+      }
+    }
+    // mask, scale, online softmax per row (rows 4 fg + e of the wave's 16)
+    float corr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int qrow = q0 + 16 * wave + 4 * fg + e;
+      float mt = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = t0 + 16 * j + fr;
+        float v = sc[j][e] * scale;
+        if (key > qrow) v = qrow < N ? -INFINITY : 0.f;  // causal mask; padding rows stay finite
+        sc[j][e] = v;
+        mt = fmaxf(mt, v);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
+      const float m_new = fmaxf(m_run[e], mt);  // finite: key 0 is in every row's window
+      corr[e] = expf(m_run[e] - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pv = expf(sc[j][e] - m_new);
+        sc[j][e] = pv;
+        ps += pv;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o);
+      l_run[e] = l_run[e] * corr[e] + ps;
+      m_run[e] = m_new;
+    }
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc_o[t][e] *= corr[e];
+    // P's two bf16 parts to this wave's LDS slices: row 4 fg + e, key 16 j + fr
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t hp = bf16_bits_rne(sc[j][e]);
+        Ps[wave][0][(4 * fg + e) * VP + 16 * j + fr] = (uint16_t)hp;
+        Ps[wave][1][(4 * fg + e) * VP + 16 * j + fr] = (uint16_t)bf16_bits_rne(sc[j][e] - __uint_as_float(hp << 16));
+      }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes land before its reads
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    // O += P V: 2 k-steps of 32 keys per 16-dim tile
+#pragma unroll
+    for (int kk = 0; kk < kMk / 32; ++kk) {
+      const bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(&Ps[wave][0][fr * VP + 32 * kk + 8 * fg]);
+      const bf16x8_t pb = *reinterpret_cast<const bf16x8_t*>(&Ps[wave][1][fr * VP + 32 * kk + 8 * fg]);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const bf16x8_t vb = *reinterpret_cast<const bf16x8_t*>(&Vt[(16 * t + fr) * VP + 32 * kk + 8 * fg]);
+        acc_o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc_o[t], 0, 0, 0);
+        acc_o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, vb, acc_o[t], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int qrow = q0 + 16 * wave + 4 * fg + e;
+    if (qrow >= N) continue;
+    bf16s* dst = out + (((int64_t)b * N + qrow) * H + h) * HD;
+    const float inv = 1.0f / l_run[e];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) dst[16 * t + fr].bits = (uint16_t)bf16_bits_rne(acc_o[t][e] * inv);
+  }
+}
+
 // ---------------------------------------------------------------- residual
 // x[i] += sum over chunks of part[c][i]: G lanes per output, lane j adding
 // chunks j, j + G, ... in order, then a butterfly over the G lanes.
@@ -651,6 +833,16 @@ static void launch_attn_decode(hipStream_t st, const pop_layer_shape& s, int B, 
 template <typename T>
 static void launch_attn_prefill(hipStream_t st, const pop_layer_shape& s, int B, int N, const void* Kc, const void* Vc,
                                 const PrefillLayerWs& w) {
+  if constexpr (sizeof(T) == 2) {  // bf16: matrix cores
+    const dim3 grid((N + kMq - 1) / kMq, s.n_heads, B);
+    if (s.head_dim == 64)
+      POP_LAUNCH((k_attn_prefill_mfma<64>), grid, dim3(256), 0, st, w.q, (const bf16s*)Kc, (const bf16s*)Vc, N,
+                 s.cache_len, s.n_heads, s.n_kv_heads, (bf16s*)w.ao);
+    else
+      POP_LAUNCH((k_attn_prefill_mfma<128>), grid, dim3(256), 0, st, w.q, (const bf16s*)Kc, (const bf16s*)Vc, N,
+                 s.cache_len, s.n_heads, s.n_kv_heads, (bf16s*)w.ao);
+    return;
+  }
   const dim3 grid((N + kPfQ - 1) / kPfQ, s.n_heads, B);
   if (s.head_dim == 64)
     POP_LAUNCH((k_attn_prefill<T, 64>), grid, dim3(256), 0, st, w.q, (const T*)Kc, (const T*)Vc, N, s.cache_len,

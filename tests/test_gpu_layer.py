@@ -123,6 +123,9 @@ PREFILL = [
     ("bf16_mha_hd128_b2_n16", "bf16", 512, 4, 4, 128, 1376, 40, 2, 16),
     ("f32_mha_hd128_b2_n50", "f32", 512, 4, 4, 128, 1376, 64, 2, 50),
     ("bf16_one_token", "bf16", 256, 4, 1, 64, 688, 8, 2, 1),
+    # several 64-query and 64-key tiles of the matrix-core prompt attention, ragged ends
+    ("bf16_hd128_n150", "bf16", 512, 4, 4, 128, 1376, 160, 1, 150),
+    ("bf16_gqa_hd64_b2_n100", "bf16", 256, 4, 2, 64, 688, 128, 2, 100),
 ]
 
 
