@@ -485,8 +485,10 @@ size_t pop_layer_prefill_workspace_bytes(int32_t batch, int32_t n_tokens, const 
  *              holds the FFN's input RMSNorm(h) (dt, [batch * n_tokens, D]).
  * Kernels: RMSNorm; the q|k|v GEMM and the output GEMM on the prompt FFN's
  * matrix-core kernel (bf16) or LDS-tiled FMA (fp32); the rotation and cache
- * write; causal attention over 16-query x 32-key LDS tiles; the fused prompt
- * FFN and partition of pop_prefill_ffn_partition; residual adds.
+ * write; causal attention, for bf16 on the matrix cores over 64-query x 64-key
+ * tiles (q and the softmax weights enter as bf16 hi + lo parts, keeping
+ * fp32-level error), for fp32 over 16 x 32 LDS tiles; the fused prompt FFN
+ * and partition of pop_prefill_ffn_partition; residual adds.
  * Errors: BAD_SHAPE / UNSUPPORTED_DTYPE / INVALID_ARGUMENT / MISALIGNED /
  * WORKSPACE_TOO_SMALL as the other calls; nothing is enqueued on an error.
  */
@@ -513,13 +515,15 @@ size_t pop_layer_decode_workspace_bytes(int32_t batch, const pop_layer_shape* s,
  *   dense_ffn  0: POP's step; 1: every FFN channel (pop_dense_ffn_decode).
  *   ws         >= pop_layer_decode_workspace_bytes; after the call byte 0
  *              holds the FFN's input RMSNorm(h) (dt, [batch, D]).
- * Kernels: RMSNorm; the q|k|v projection as a K-major GEMV (one wave per 512
- * bf16 or 256 fp32 columns and a chunk of rows, fp32 partial sums); the chunk
- * sums with the rotation and cache write; attention split into 64-key slices
- * and a log-sum-exp merge; the output projection GEMV and the residual; the
- * FFN's RMSNorm; pop_decode_ffn or pop_dense_ffn_decode; the residual.
- * Deterministic.  Errors as pop_layer_prefill and pop_decode_ffn; nothing is
- * enqueued on an error.
+ * Kernels: the q|k|v projection as a K-major GEMV (one wave per 512 bf16 or
+ * 256 fp32 columns and a chunk of rows, fp32 partial sums), with the RMSNorm
+ * computed inside its waves at batch <= 2 (a separate RMSNorm launch above);
+ * the chunk sums with the rotation and cache write; attention split into
+ * 64-key slices; the output projection GEMV, whose waves merge the slices
+ * (log-sum-exp) on the fly; the residual; the FFN's RMSNorm; pop_decode_ffn
+ * or pop_dense_ffn_decode, whose last kernel adds its output into x at batch
+ * 1 (a residual add launch above).  Deterministic.  Errors as
+ * pop_layer_prefill and pop_decode_ffn; nothing is enqueued on an error.
  */
 pop_status pop_layer_decode(float* x, int32_t batch, const pop_layer_shape* s, const pop_layer_weights* w,
                             pop_dtype dt, void* K_cache, void* V_cache, const int32_t* pos, const int32_t* R,
