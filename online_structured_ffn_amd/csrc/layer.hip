@@ -138,8 +138,8 @@ __device__ __forceinline__ float round_to(float v) {
   }
 }
 
-// Merged attention output of (sequence b, row k = head * hd + d), in the
-// order k_attn_combine uses.
+// Merged attention output of (sequence b, row k = head * hd + d): the slices
+// in order, each rescaled by exp(m_s - max m) (log-sum-exp merge).
 __device__ __forceinline__ float combine_row(const float* __restrict__ ml, const float* __restrict__ po, int S,
                                              int hd, int H, int b, int k) {
   const int h = k / hd, d = k % hd;
