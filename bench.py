@@ -825,6 +825,16 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
     torch.cuda.synchronize()
     log(f"[bench] inputs generated on the device in {time.time() - t0:.1f} s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+    if args.copy_probe_mib > 0:  # a copy of known size, to scale the profiler's byte counters
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 3 copies of {args.copy_probe_mib} MiB ({n} bytes read and written each)")
+        del src, dst
 
     def prefill():
         x_pre.copy_(X0)
