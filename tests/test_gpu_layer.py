@@ -126,6 +126,8 @@ PREFILL = [
     # several 64-query and 64-key tiles of the matrix-core prompt attention, ragged ends
     ("bf16_hd128_n150", "bf16", 512, 4, 4, 128, 1376, 160, 1, 150),
     ("bf16_gqa_hd64_b2_n100", "bf16", 256, 4, 2, 64, 688, 128, 2, 100),
+    # the largest model width the library accepts (q|k|v narrower than D)
+    ("bf16_max_d_16384_n33", "bf16", 16384, 2, 2, 128, 688, 40, 1, 33),
 ]
 
 
@@ -164,6 +166,9 @@ DECODE = [
     ("f32_hd128_b2_pos700", "f32", 512, 4, 4, 128, 1376, 800, 2, 700),
     ("bf16_hd128_b16_pos333", "bf16", 512, 8, 2, 128, 1376, 400, 16, 333),
     ("bf16_b64_pos63", "bf16", 256, 4, 2, 64, 688, 64, 64, 63),
+    # the largest model width, and a 4096-position cache at its last slot (64 slices merged)
+    ("bf16_max_d_16384_b2_pos50", "bf16", 16384, 2, 1, 128, 688, 64, 2, 50),
+    ("f32_cache_4096_last_slot", "f32", 256, 4, 2, 64, 688, 4096, 1, 4095),
 ]
 
 
