@@ -914,11 +914,21 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
     S = min(args.kernel_steps, T)
     # the library's batch <= 2 form runs the attention RMSNorm inside the q|k|v projection
     head = ((["k_gemv_kmajor(norm+qkv)"] if B <= 2 else ["k_rmsnorm", "k_gemv_kmajor(qkv)"])
-            + ["k_qkv_rope", "k_attn_decode", "k_gemv_kmajor(merge+o)", "k_sum_residual", "k_rmsnorm(ffn)", "-"])
+            + ["k_qkv_rope", "k_attn_decode"]
+            + (["k_gemv_kmajor(merge+o)"] if B <= 2 else ["k_attn_merge", "k_gemv_kmajor(o)"])
+            + ["k_sum_residual", "k_rmsnorm(ffn)", "-"])
+    if B > 1:   # the library's batch-2..64 FFN kernels (bf16, matrix cores), then the residual add
+        mfma_tail = (["k_gateup_lds"] + (["k_topk"] if n_C > 4096 else [])
+                     + ["k_down_stream.R+topk" if n_C <= 4096 else "k_down_stream.R", "k_down_stream.S", "k_sum_few(y)"])
+        dense_tail = ["k_gateup_lds(dense)", "k_down_stream(dense)", "k_sum_few(y)"]
     fused = B == 1 and 0 < n_C <= 4096 and k > 0
     # at batch 1 the FFN's last kernel adds its output into the residual stream (no k_add)
-    labels_pop = head + (["k_pop_step.1", "k_pop_step.2", "k_pop_finish(+h)"] if fused else ["ffn#0", "k_add"])
-    labels_dense = head + (["k_pop_step.0(dense)", "k_pop_finish(dense,+h)"] if B == 1 else ["ffn#0", "k_add"])
+    if B == 1:
+        labels_pop = head + (["k_pop_step.1", "k_pop_step.2", "k_pop_finish(+h)"] if fused else ["ffn#0"])
+        labels_dense = head + ["k_pop_step.0(dense)", "k_pop_finish(dense,+h)"]
+    else:
+        labels_pop = head + mfma_tail + ["k_add"]
+        labels_dense = head + dense_tail + ["k_add"]
     tracer = pop.Tracer(S * L * (len(labels_pop) + len(labels_dense) + 2) + 8, pop.Tracer.DISABLE_SYSTEM_FENCE)
     marks = []
     for dense, labels in ((False, labels_pop), (True, labels_dense)):
@@ -955,7 +965,7 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
     plan = metrics.fused_plan(n_R, n_C, k, d, e)
     att_k = metrics.attention_decode_bytes(d, H, Hkv, hd, N + (S + 1) / 2, B, e)
     kbytes = {"k_gemv_kmajor(norm+qkv)" if B <= 2 else "k_gemv_kmajor(qkv)": att_k["qkv"],
-              "k_gemv_kmajor(merge+o)": att_k["o"], "k_attn_decode": att_k["attn"]}
+              "k_gemv_kmajor(merge+o)" if B <= 2 else "k_gemv_kmajor(o)": att_k["o"], "k_attn_decode": att_k["attn"]}
     if fused:
         kbytes.update({"k_pop_step.1": plan["bytes"][1], "k_pop_step.2": plan["bytes"][2],
                        "k_pop_finish(+h)": plan["bytes"][3] + 4 * d})

@@ -84,5 +84,11 @@ LLAMA2_7B_LAYER = Workload(
     notes="32 chained LLaMA-2-7B-shaped decoder layers: dense attention over a key/value cache, the FFN pruned "
           "at the 29.9% that a 20% global budget gives it; RMSNorm gains 1, token inputs N(0,1)")
 
-WORKLOADS = [TINY, LLAMA2_7B, LLAMA2_7B_B16, QWEN2_7B, MIXTRAL_MOE, LLAMA2_7B_LAYER]
+LLAMA2_7B_LAYER_B16 = Workload(
+    name="llama2_7b_layer_b16", dtype="bf16", layers=32, d=4096, d_ff=11008, r=0.299, gamma=0.1,
+    prompt_batch=16, prompt_len=512, decode_steps=256, decode_batch=16,
+    extra={"attention": {"n_heads": 32, "n_kv_heads": 32, "head_dim": 128, "eps": 1e-5, "rope_theta": 10000.0}},
+    notes="the decoder-layer stack decoding 16 sequences at once (one FFN mask per step for the batch)")
+
+WORKLOADS = [TINY, LLAMA2_7B, LLAMA2_7B_B16, QWEN2_7B, MIXTRAL_MOE, LLAMA2_7B_LAYER, LLAMA2_7B_LAYER_B16]
 BY_NAME = {w.name: w for w in WORKLOADS}

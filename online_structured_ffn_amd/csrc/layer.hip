@@ -56,6 +56,9 @@ constexpr int kGemvTarget = POP_GEMV_WAVES;  // waves a decode projection aims f
 #endif
 constexpr int kGemvInflight = POP_GEMV_INFLIGHT;  // row loads in flight per lane
 constexpr int kSumLanes = 16;                // lanes that share one output's chunk sum
+#ifndef POP_GEMV_PART_DIV
+#define POP_GEMV_PART_DIV 8  // partial sums kept under (weight bytes) * 4 / POP_GEMV_PART_DIV
+#endif
 #ifndef POP_GEMV_WPB
 #define POP_GEMV_WPB 1
 #endif
@@ -400,6 +403,18 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
   }
 }
 
+// The slices' merge as a kernel of its own (batches above 2, where merging
+// inside every wave of the output projection would repeat it per token):
+// out[b, h*hd + d] = combine_row(b, h*hd + d), rounded to the dtype; one block
+// of hd threads per (head, sequence).
+template <typename T>
+__global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ ml, const float* __restrict__ po, int S,
+                                                    int H, int hd, T* __restrict__ out) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  if (d >= hd) return;
+  put_elem(out, ((int64_t)b * H + h) * hd + d, combine_row(ml, po, S, hd, H, b, h * hd + d));
+}
+
 // ---------------------------------------------------------------- prompt attention
 // Block (query tile qt, head h, sequence b): queries q0 .. q0 + 15 (q0 = 16 qt)
 // of the sequence's N prompt tokens, keys 0 .. q0 + 15 in 32-key tiles staged
@@ -698,7 +713,7 @@ static GemvPlan gemv_plan(int B, int K, int N, int esz, int max_rows = 0) {
   const int V = 16 / esz;
   p.col_blocks = (N + 64 * V - 1) / (64 * V);
   int want = (kGemvTarget + p.col_blocks * p.groups - 1) / (p.col_blocks * p.groups);
-  const int64_t cap = ((int64_t)K * esz) / (32 * (int64_t)(B > 0 ? B : 1));
+  const int64_t cap = ((int64_t)K * esz) / (POP_GEMV_PART_DIV * (int64_t)(B > 0 ? B : 1));
   if (want > cap) want = (int)(cap > 1 ? cap : 1);
   if (want < 1) want = 1;
   int rpc = (K + want - 1) / want;
@@ -763,6 +778,7 @@ struct DecodeLayerWs {
   float* q;     // [B, H, hd]
   float* ml;    // [B, H, slices, 2]
   float* po;    // [B, H, slices, hd]
+  char* ao;     // merged attention output, dtype [B, H hd] (batches above 2)
   float* y;     // FFN output [B, D]
   char* ffn;    // FFN workspace
   size_t total;
@@ -784,6 +800,7 @@ static DecodeLayerWs decode_layer_ws(int B, const pop_layer_shape& s, pop_dtype 
   w.q = (float*)take((size_t)B * Hd * 4);
   w.ml = (float*)take((size_t)B * s.n_heads * S * 2 * 4);
   w.po = (float*)take((size_t)B * s.n_heads * S * s.head_dim * 4);
+  w.ao = take((size_t)B * Hd * e);
   w.y = (float*)take((size_t)B * s.d * 4);
   w.ffn = take(pop_decode_workspace_bytes(B, s.d, s.d_ff));
   w.total = off;
@@ -854,8 +871,8 @@ static void launch_attn_prefill(hipStream_t st, const pop_layer_shape& s, int B,
 
 // The attention half of a decode step, through the FFN's RMSNorm: x becomes h
 // and lw.xn RMSNorm(h).  At batch <= 2 the attention RMSNorm runs inside the
-// q|k|v projection; the slices' merge always runs inside the output
-// projection.
+// q|k|v projection and the slices' merge inside the output projection; above,
+// each is a launch of its own.
 template <typename T>
 static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, const pop_layer_shape& s,
                                            const pop_layer_weights* w, void* Kc, void* Vc, const int32_t* pos,
@@ -878,12 +895,19 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
              s.n_heads, s.n_kv_heads, s.head_dim, 1, 0, pos, s.rope_theta, s.cache_len, lw.q, (T*)Kc, (T*)Vc);
   launch_attn_decode<T>(h, s, batch, Kc, Vc, pos, lw);
   GemvIn oin{};
-  oin.ml = lw.ml;
-  oin.po = lw.po;
-  oin.slices = n_slices(s);
-  oin.hd = s.head_dim;
-  oin.H = s.n_heads;
-  launch_gemv<T, kXCombine>(h, po, oin, batch, Hd, w->Wo_T, D, lw.part);
+  if (batch <= 2) {
+    oin.ml = lw.ml;
+    oin.po = lw.po;
+    oin.slices = n_slices(s);
+    oin.hd = s.head_dim;
+    oin.H = s.n_heads;
+    launch_gemv<T, kXCombine>(h, po, oin, batch, Hd, w->Wo_T, D, lw.part);
+  } else {
+    POP_LAUNCH(k_attn_merge<T>, dim3(s.n_heads, batch), dim3(128), 0, h, lw.ml, lw.po, n_slices(s), s.n_heads,
+               s.head_dim, (T*)lw.ao);
+    oin.x = lw.ao;
+    launch_gemv<T, kXPlain>(h, po, oin, batch, Hd, w->Wo_T, D, lw.part);
+  }
   // (A last-block-done fusion of the next two launches measured slower: every
   // block's device-scope release writes back its XCD's L2.)
   const int64_t n = (int64_t)batch * D;
