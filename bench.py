@@ -917,6 +917,9 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
             + ["k_qkv_rope", "k_attn_decode"]
             + (["k_gemv_kmajor(merge+o)"] if B <= 2 else ["k_attn_merge", "k_gemv_kmajor(o)"])
             + ["k_sum_residual", "k_rmsnorm(ffn)", "-"])
+    if B >= 12 and e == 2:   # the library's bf16 form from 12 tokens: both projections on the prompt GEMM
+        head = [{"k_gemv_kmajor(qkv)": "k_prompt_down(qkv)", "k_gemv_kmajor(o)": "k_prompt_down(o)",
+                 "k_sum_residual": "k_add(h)"}.get(n, n) for n in head]
     if B > 1:   # the library's batch-2..64 FFN kernels (bf16, matrix cores), then the residual add
         mfma_tail = (["k_gateup_lds"] + (["k_topk"] if n_C > 4096 else [])
                      + ["k_down_stream.R+topk" if n_C <= 4096 else "k_down_stream.R", "k_down_stream.S", "k_sum_few(y)"])
@@ -964,8 +967,8 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
     log("[bench] dense-FFN layer kernels (us): " + ", ".join(f"{n} {v:.2f}" for n, v in kus_dense.items()))
     plan = metrics.fused_plan(n_R, n_C, k, d, e)
     att_k = metrics.attention_decode_bytes(d, H, Hkv, hd, N + (S + 1) / 2, B, e)
-    kbytes = {"k_gemv_kmajor(norm+qkv)" if B <= 2 else "k_gemv_kmajor(qkv)": att_k["qkv"],
-              "k_gemv_kmajor(merge+o)" if B <= 2 else "k_gemv_kmajor(o)": att_k["o"], "k_attn_decode": att_k["attn"]}
+    kbytes = {head[0] if B <= 2 else head[1]: att_k["qkv"],
+              "k_gemv_kmajor(merge+o)" if B <= 2 else head[5]: att_k["o"], "k_attn_decode": att_k["attn"]}
     if fused:
         kbytes.update({"k_pop_step.1": plan["bytes"][1], "k_pop_step.2": plan["bytes"][2],
                        "k_pop_finish(+h)": plan["bytes"][3] + 4 * d})

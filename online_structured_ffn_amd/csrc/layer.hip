@@ -56,6 +56,12 @@ constexpr int kGemvTarget = POP_GEMV_WAVES;  // waves a decode projection aims f
 #endif
 constexpr int kGemvInflight = POP_GEMV_INFLIGHT;  // row loads in flight per lane
 constexpr int kSumLanes = 16;                // lanes that share one output's chunk sum
+#ifndef POP_LAYER_GEMM_BATCH
+// bf16 decode batches from this size take both projections on the matrix cores: the scalar GEMV's time
+// grows with the batch (16 FMAs per weight element at batch 16: 60 us for q|k|v), the prompt GEMM's stays
+// near its weight stream (46 us at batch 16)
+#define POP_LAYER_GEMM_BATCH 12
+#endif
 #ifndef POP_GEMV_PART_DIV
 #define POP_GEMV_PART_DIV 8  // partial sums kept under (weight bytes) * 4 / POP_GEMV_PART_DIV
 #endif
@@ -880,6 +886,9 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
   const int D = s.d, Hd = s.n_heads * s.head_dim, e = sizeof(T);
   const GemvPlan pq = gemv_plan(batch, D, n_qkv(s), e), po = gemv_plan(batch, Hd, D, e, 64);
   const bool fuse_norm = batch <= 2;
+  // bf16 from POP_LAYER_GEMM_BATCH tokens: both projections on the prompt pass's matrix-core GEMM (complete
+  // sums: the rotation reads one chunk, a plain add replaces the chunk sum)
+  const bool gemm_path = sizeof(T) == 2 && batch >= POP_LAYER_GEMM_BATCH;
   GemvIn qin{};
   if (fuse_norm) {
     qin.res = x;
@@ -889,10 +898,17 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
   } else {
     POP_LAUNCH(k_rmsnorm<T>, dim3(batch), dim3(256), 0, h, x, D, w->attn_norm, (float)s.eps, (T*)lw.xn);
     qin.x = lw.xn;
-    launch_gemv<T, kXPlain>(h, pq, qin, batch, D, w->Wqkv_T, n_qkv(s), lw.part);
+    if (gemm_path)
+      launch_gemm_kmajor(h, lw.xn, batch, D, w->Wqkv_T, D, n_qkv(s), POP_BF16, lw.part);
+    else
+      launch_gemv<T, kXPlain>(h, pq, qin, batch, D, w->Wqkv_T, n_qkv(s), lw.part);
   }
-  POP_LAUNCH((k_qkv_rope<T, kSumLanes>), qkv_grid(batch, s, kSumLanes), dim3(256), 0, h, lw.part, pq.chunks, batch,
-             s.n_heads, s.n_kv_heads, s.head_dim, 1, 0, pos, s.rope_theta, s.cache_len, lw.q, (T*)Kc, (T*)Vc);
+  if (gemm_path)
+    POP_LAUNCH((k_qkv_rope<T, 1>), qkv_grid(batch, s, 1), dim3(256), 0, h, lw.part, 1, batch, s.n_heads, s.n_kv_heads,
+               s.head_dim, 1, 0, pos, s.rope_theta, s.cache_len, lw.q, (T*)Kc, (T*)Vc);
+  else
+    POP_LAUNCH((k_qkv_rope<T, kSumLanes>), qkv_grid(batch, s, kSumLanes), dim3(256), 0, h, lw.part, pq.chunks, batch,
+               s.n_heads, s.n_kv_heads, s.head_dim, 1, 0, pos, s.rope_theta, s.cache_len, lw.q, (T*)Kc, (T*)Vc);
   launch_attn_decode<T>(h, s, batch, Kc, Vc, pos, lw);
   GemvIn oin{};
   if (batch <= 2) {
@@ -906,13 +922,19 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
     POP_LAUNCH(k_attn_merge<T>, dim3(s.n_heads, batch), dim3(128), 0, h, lw.ml, lw.po, n_slices(s), s.n_heads,
                s.head_dim, (T*)lw.ao);
     oin.x = lw.ao;
-    launch_gemv<T, kXPlain>(h, po, oin, batch, Hd, w->Wo_T, D, lw.part);
+    if (gemm_path)
+      launch_gemm_kmajor(h, lw.ao, batch, Hd, w->Wo_T, Hd, D, POP_BF16, lw.part);
+    else
+      launch_gemv<T, kXPlain>(h, po, oin, batch, Hd, w->Wo_T, D, lw.part);
   }
   // (A last-block-done fusion of the next two launches measured slower: every
   // block's device-scope release writes back its XCD's L2.)
   const int64_t n = (int64_t)batch * D;
-  POP_LAUNCH(k_sum_residual<kSumLanes>, dim3((unsigned)((n * kSumLanes + 255) / 256)), dim3(256), 0, h, lw.part,
-             po.chunks, n, x);
+  if (gemm_path)
+    POP_LAUNCH(k_add, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, h, x, (const float*)lw.part, n);
+  else
+    POP_LAUNCH(k_sum_residual<kSumLanes>, dim3((unsigned)((n * kSumLanes + 255) / 256)), dim3(256), 0, h, lw.part,
+               po.chunks, n, x);
   POP_LAUNCH(k_rmsnorm<T>, dim3(batch), dim3(256), 0, h, x, D, w->ffn_norm, (float)s.eps, (T*)lw.xn);
 }
 
