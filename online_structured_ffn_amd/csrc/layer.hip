@@ -62,6 +62,7 @@ constexpr int kSumLanes = 16;                // lanes that share one output's ch
 // near its weight stream (46 us at batch 16)
 #define POP_LAYER_GEMM_BATCH 12
 #endif
+constexpr int kLayerKsplit = 8;  // reduction slices of those GEMMs (64-192 blocks would not fill the chip)
 #ifndef POP_GEMV_PART_DIV
 #define POP_GEMV_PART_DIV 8  // partial sums kept under (weight bytes) * 4 / POP_GEMV_PART_DIV
 #endif
@@ -793,7 +794,10 @@ struct DecodeLayerWs {
 static DecodeLayerWs decode_layer_ws(int B, const pop_layer_shape& s, pop_dtype dt, char* base) {
   const int e = elem_bytes(dt), Hd = s.n_heads * s.head_dim, S = n_slices(s);
   const GemvPlan a = gemv_plan(B, s.d, n_qkv(s), e), o = gemv_plan(B, Hd, s.d, e, 64);
-  const size_t part = (size_t)std::max((int64_t)a.chunks * n_qkv(s), (int64_t)o.chunks * s.d) * B * 4;
+  const int ks = std::max(gemm_kslices(s.d, kLayerKsplit), gemm_kslices(Hd, kLayerKsplit));
+  const size_t part =
+      (size_t)std::max({(int64_t)a.chunks * n_qkv(s), (int64_t)o.chunks * s.d, (int64_t)ks * n_qkv(s),
+                        (int64_t)ks * s.d}) * B * 4;
   DecodeLayerWs w;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -886,8 +890,8 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
   const int D = s.d, Hd = s.n_heads * s.head_dim, e = sizeof(T);
   const GemvPlan pq = gemv_plan(batch, D, n_qkv(s), e), po = gemv_plan(batch, Hd, D, e, 64);
   const bool fuse_norm = batch <= 2;
-  // bf16 from POP_LAYER_GEMM_BATCH tokens: both projections on the prompt pass's matrix-core GEMM (complete
-  // sums: the rotation reads one chunk, a plain add replaces the chunk sum)
+  // bf16 from POP_LAYER_GEMM_BATCH tokens: both projections on the prompt pass's matrix-core GEMM, split
+  // into kLayerKsplit reduction slices that the rotation and the residual sum add up
   const bool gemm_path = sizeof(T) == 2 && batch >= POP_LAYER_GEMM_BATCH;
   GemvIn qin{};
   if (fuse_norm) {
@@ -899,13 +903,14 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
     POP_LAUNCH(k_rmsnorm<T>, dim3(batch), dim3(256), 0, h, x, D, w->attn_norm, (float)s.eps, (T*)lw.xn);
     qin.x = lw.xn;
     if (gemm_path)
-      launch_gemm_kmajor(h, lw.xn, batch, D, w->Wqkv_T, D, n_qkv(s), POP_BF16, lw.part);
+      launch_gemm_kmajor(h, lw.xn, batch, D, w->Wqkv_T, D, n_qkv(s), POP_BF16, lw.part, kLayerKsplit);
     else
       launch_gemv<T, kXPlain>(h, pq, qin, batch, D, w->Wqkv_T, n_qkv(s), lw.part);
   }
   if (gemm_path)
-    POP_LAUNCH((k_qkv_rope<T, 1>), qkv_grid(batch, s, 1), dim3(256), 0, h, lw.part, 1, batch, s.n_heads, s.n_kv_heads,
-               s.head_dim, 1, 0, pos, s.rope_theta, s.cache_len, lw.q, (T*)Kc, (T*)Vc);
+    POP_LAUNCH((k_qkv_rope<T, kLayerKsplit>), qkv_grid(batch, s, kLayerKsplit), dim3(256), 0, h, lw.part,
+               gemm_kslices(D, kLayerKsplit), batch, s.n_heads, s.n_kv_heads, s.head_dim, 1, 0, pos, s.rope_theta,
+               s.cache_len, lw.q, (T*)Kc, (T*)Vc);
   else
     POP_LAUNCH((k_qkv_rope<T, kSumLanes>), qkv_grid(batch, s, kSumLanes), dim3(256), 0, h, lw.part, pq.chunks, batch,
                s.n_heads, s.n_kv_heads, s.head_dim, 1, 0, pos, s.rope_theta, s.cache_len, lw.q, (T*)Kc, (T*)Vc);
@@ -923,7 +928,7 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
                s.head_dim, (T*)lw.ao);
     oin.x = lw.ao;
     if (gemm_path)
-      launch_gemm_kmajor(h, lw.ao, batch, Hd, w->Wo_T, Hd, D, POP_BF16, lw.part);
+      launch_gemm_kmajor(h, lw.ao, batch, Hd, w->Wo_T, Hd, D, POP_BF16, lw.part, kLayerKsplit);
     else
       launch_gemv<T, kXPlain>(h, po, oin, batch, Hd, w->Wo_T, D, lw.part);
   }
@@ -931,7 +936,8 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
   // block's device-scope release writes back its XCD's L2.)
   const int64_t n = (int64_t)batch * D;
   if (gemm_path)
-    POP_LAUNCH(k_add, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, h, x, (const float*)lw.part, n);
+    POP_LAUNCH(k_sum_residual<kLayerKsplit>, dim3((unsigned)((n * kLayerKsplit + 255) / 256)), dim3(256), 0, h,
+               lw.part, gemm_kslices(Hd, kLayerKsplit), n, x);
   else
     POP_LAUNCH(k_sum_residual<kSumLanes>, dim3((unsigned)((n * kSumLanes + 255) / 256)), dim3(256), 0, h, lw.part,
                po.chunks, n, x);

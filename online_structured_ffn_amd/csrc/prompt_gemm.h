@@ -12,8 +12,18 @@ namespace pop {
 // lda elements.  bf16: the down-projection kernel of the prompt FFN
 // (v_mfma_f32_16x16x32_bf16), which needs K % 64 == 0 (or zeros in A past K up
 // to the next multiple of 64), N % 8 == 0 and M >= 1; fp32: LDS-tiled FMA.
-// Enqueued on `stream` (a hipStream_t); no checks.
+// ksplit > 1 (bf16, M <= 4096): the reduction is split into ksplit_eff =
+// ceil(K / kslice) slices of kslice = K / ksplit rounded up to 64 rows, and Y
+// holds one partial product per slice, [ksplit_eff][M][N] (the caller sums
+// them).  Enqueued on `stream` (a hipStream_t); no checks.
 void launch_gemm_kmajor(void* stream, const void* A, int M, int lda, const void* Bk, int K, int N, pop_dtype dt,
-                        float* Y);
+                        float* Y, int ksplit = 1);
+
+// The number of slices launch_gemm_kmajor makes for (K, ksplit).
+inline int gemm_kslices(int K, int ksplit) {
+  if (ksplit <= 1) return 1;
+  const int kslice = (K / ksplit + 63) / 64 * 64;
+  return (K + kslice - 1) / kslice;
+}
 
 }  // namespace pop
