@@ -166,6 +166,9 @@ DECODE = [
     ("f32_hd128_b2_pos700", "f32", 512, 4, 4, 128, 1376, 800, 2, 700),
     ("bf16_hd128_b16_pos333", "bf16", 512, 8, 2, 128, 1376, 400, 16, 333),
     ("bf16_b64_pos63", "bf16", 256, 4, 2, 64, 688, 64, 64, 63),
+    # fp32 above batch 2 (separate merge kernel, plain projections); bf16 at the matrix-core projections' threshold
+    ("f32_gqa_b5_pos77", "f32", 256, 4, 2, 64, 688, 96, 5, 77),
+    ("bf16_hd128_b12_pos130", "bf16", 512, 4, 2, 128, 1376, 160, 12, 130),
     # the largest model width, and a 4096-position cache at its last slot (64 slices merged)
     ("bf16_max_d_16384_b2_pos50", "bf16", 16384, 2, 1, 128, 688, 64, 2, 50),
     ("f32_cache_4096_last_slot", "f32", 256, 4, 2, 64, 688, 4096, 1, 4095),
