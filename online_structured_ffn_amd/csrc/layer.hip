@@ -893,6 +893,7 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
   // bf16 from POP_LAYER_GEMM_BATCH tokens: both projections on the prompt pass's matrix-core GEMM, split
   // into kLayerKsplit reduction slices that the rotation and the residual sum add up
   const bool gemm_path = sizeof(T) == 2 && batch >= POP_LAYER_GEMM_BATCH;
+  int qkv_slices = 1, o_slices = 1;  // partial products the matrix-core projections leave
   GemvIn qin{};
   if (fuse_norm) {
     qin.res = x;
@@ -903,13 +904,13 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
     POP_LAUNCH(k_rmsnorm<T>, dim3(batch), dim3(256), 0, h, x, D, w->attn_norm, (float)s.eps, (T*)lw.xn);
     qin.x = lw.xn;
     if (gemm_path)
-      launch_gemm_kmajor(h, lw.xn, batch, D, w->Wqkv_T, D, n_qkv(s), POP_BF16, lw.part, kLayerKsplit);
+      qkv_slices = launch_gemm_kmajor(h, lw.xn, batch, D, w->Wqkv_T, D, n_qkv(s), POP_BF16, lw.part, kLayerKsplit);
     else
       launch_gemv<T, kXPlain>(h, pq, qin, batch, D, w->Wqkv_T, n_qkv(s), lw.part);
   }
   if (gemm_path)
     POP_LAUNCH((k_qkv_rope<T, kLayerKsplit>), qkv_grid(batch, s, kLayerKsplit), dim3(256), 0, h, lw.part,
-               gemm_kslices(D, kLayerKsplit), batch, s.n_heads, s.n_kv_heads, s.head_dim, 1, 0, pos, s.rope_theta,
+               qkv_slices, batch, s.n_heads, s.n_kv_heads, s.head_dim, 1, 0, pos, s.rope_theta,
                s.cache_len, lw.q, (T*)Kc, (T*)Vc);
   else
     POP_LAUNCH((k_qkv_rope<T, kSumLanes>), qkv_grid(batch, s, kSumLanes), dim3(256), 0, h, lw.part, pq.chunks, batch,
@@ -928,7 +929,7 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
                s.head_dim, (T*)lw.ao);
     oin.x = lw.ao;
     if (gemm_path)
-      launch_gemm_kmajor(h, lw.ao, batch, Hd, w->Wo_T, Hd, D, POP_BF16, lw.part, kLayerKsplit);
+      o_slices = launch_gemm_kmajor(h, lw.ao, batch, Hd, w->Wo_T, Hd, D, POP_BF16, lw.part, kLayerKsplit);
     else
       launch_gemv<T, kXPlain>(h, po, oin, batch, Hd, w->Wo_T, D, lw.part);
   }
@@ -937,7 +938,7 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
   const int64_t n = (int64_t)batch * D;
   if (gemm_path)
     POP_LAUNCH(k_sum_residual<kLayerKsplit>, dim3((unsigned)((n * kLayerKsplit + 255) / 256)), dim3(256), 0, h,
-               lw.part, gemm_kslices(Hd, kLayerKsplit), n, x);
+               lw.part, o_slices, n, x);
   else
     POP_LAUNCH(k_sum_residual<kSumLanes>, dim3((unsigned)((n * kSumLanes + 255) / 256)), dim3(256), 0, h, lw.part,
                po.chunks, n, x);

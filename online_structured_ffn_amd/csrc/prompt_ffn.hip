@@ -542,8 +542,8 @@ static void launch_prompt_ffn(hipStream_t st, const void* X, int64_t n_tokens, i
   }
 }
 
-void launch_gemm_kmajor(void* stream, const void* A, int M, int lda, const void* Bk, int K, int N, pop_dtype dt,
-                        float* Y, int ksplit) {
+int launch_gemm_kmajor(void* stream, const void* A, int M, int lda, const void* Bk, int K, int N, pop_dtype dt,
+                       float* Y, int ksplit) {
   hipStream_t st = (hipStream_t)stream;
   if (ksplit > 1 && dt == POP_BF16 && M <= (int)kChunkTokens) {  // slices of the reduction, one Y each
     const int kslice = (K / ksplit + kBK - 1) / kBK * kBK;
@@ -551,7 +551,7 @@ void launch_gemm_kmajor(void* stream, const void* A, int M, int lda, const void*
     const int mt = (M + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;
     POP_LAUNCH((k_prompt_down<128, POP_DOWN_NS>), dim3(mt * nt * ns), dim3(kGThreads), 0, st, (const uint16_t*)A, M,
                lda, (const bf16s*)Bk, K, N, Y, mt, nt, kslice);
-    return;
+    return ns;
   }
   for (int m0 = 0; m0 < M; m0 += (int)kChunkTokens) {  // row chunks keep every grid dimension small
     const int Mc = M - m0 < (int)kChunkTokens ? M - m0 : (int)kChunkTokens;
@@ -565,6 +565,7 @@ void launch_gemm_kmajor(void* stream, const void* A, int M, int lda, const void*
                  (const float*)A + (int64_t)m0 * lda, Mc, lda, (const float*)Bk, K, N, Yc);
     }
   }
+  return 1;
 }
 
 }  // namespace pop
