@@ -917,8 +917,8 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
             + ["k_qkv_rope", "k_attn_decode"]
             + (["k_gemv_kmajor(merge+o)"] if B <= 2 else ["k_attn_merge", "k_gemv_kmajor(o)"])
             + ["k_sum_residual", "k_rmsnorm(ffn)", "-"])
-    if B >= 12 and e == 2:   # the library's bf16 form from 12 tokens: both projections on the prompt GEMM
-        head = [{"k_gemv_kmajor(qkv)": "k_prompt_down(qkv, split K)", "k_gemv_kmajor(o)": "k_prompt_down(o, split K)"
+    if B >= 12 and e == 2:   # the library bf16 form from 12 tokens: both projections on the matrix cores
+        head = [{"k_gemv_kmajor(qkv)": "k_gemm_decode(qkv)", "k_gemv_kmajor(o)": "k_gemm_decode(o)"
                  }.get(n, n) for n in head]
     if B > 1:   # the library's batch-2..64 FFN kernels (bf16, matrix cores), then the residual add
         mfma_tail = (["k_gateup_lds"] + (["k_topk"] if n_C > 4096 else [])

@@ -20,6 +20,8 @@
 //                   residual stream computed in the wave (the q|k|v
 //                   projection at batch <= 2), or the merge of the attention
 //                   slices (the output projection).
+//   k_gemm_decode   the same projections for 12 or more bf16 tokens on the
+//                   matrix cores (256-column tiles, slices of the reduction).
 //   k_qkv_rope      sums the row chunks of q|k|v, turns q and k, writes the
 //                   key/value cache entries (dtype) and q (fp32).
 //   k_attn_decode   one query per (sequence, head): the keys are split into
@@ -44,6 +46,8 @@
 
 namespace pop {
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kAttnKeys = 64;       // keys per decode slice
 constexpr int kPfQ = 16;            // queries per prompt-attention block
 constexpr int kPfK = 32;            // keys per prompt-attention tile
@@ -57,12 +61,12 @@ constexpr int kGemvTarget = POP_GEMV_WAVES;  // waves a decode projection aims f
 constexpr int kGemvInflight = POP_GEMV_INFLIGHT;  // row loads in flight per lane
 constexpr int kSumLanes = 16;                // lanes that share one output's chunk sum
 #ifndef POP_LAYER_GEMM_BATCH
-// bf16 decode batches from this size take both projections on the matrix cores: the scalar GEMV's time
-// grows with the batch (16 FMAs per weight element at batch 16: 60 us for q|k|v), the prompt GEMM's stays
-// near its weight stream (46 us at batch 16)
+// bf16 decode batches from this size take both projections on the matrix cores (k_gemm_decode): the
+// scalar GEMV's time grows with the batch (16 FMAs per weight element at batch 16: 60 us for q|k|v), the
+// matrix-core kernel's stays near its weight stream (33 us at batch 16)
 #define POP_LAYER_GEMM_BATCH 12
 #endif
-constexpr int kLayerKsplit = 8;  // reduction slices of those GEMMs (64-192 blocks would not fill the chip)
+constexpr int kGdLanes = 8;  // lanes per output that add up k_gemm_decode's reduction slices
 #ifndef POP_GEMV_PART_DIV
 #define POP_GEMV_PART_DIV 8  // partial sums kept under (weight bytes) * 4 / POP_GEMV_PART_DIV
 #endif
@@ -518,8 +522,6 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
 // over the 16 lanes sharing l >> 4.  P's parts go to the wave's LDS slices and
 // are read back as A operands.  Query rows past N load row N - 1 and are not
 // written.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kMq = 64, kMk = 64;
 
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
@@ -685,6 +687,86 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
   }
 }
 
+// ---------------------------------------------------------------- decode projections, matrix cores
+// bf16, 12 or more tokens: part[slice][b][n] = sum over rows k of the slice of
+// x[b][k] W[k][n] on v_mfma_f32_16x16x32_bf16.  Block (256-column tile, slice
+// of the reduction, group of 16 tokens); wave w owns columns 64 w + [0, 64) of
+// the tile (four 16-column MFMA tiles).  A stage is 32 rows x 256 columns of W
+// (512 contiguous bytes per row): loaded to registers one stage ahead, written
+// to LDS transposed (two rows packed per 32-bit word, so a column's 8
+// consecutive k are one 16-byte read: the B operand), two LDS buffers.  The A
+// operand (16 tokens x 32 k of x) is read from global memory (small, cached);
+// token slots past B read token B - 1 and are not written; columns past N read
+// the last vector and are not written.  K-range and slice length are
+// multiples of 32.
+constexpr int kGdBN = 256, kGdBK = 32, kGdKP = kGdBK + 8;
+
+__global__ __launch_bounds__(256) void k_gemm_decode(const bf16s* __restrict__ x, int B, int K,
+                                                     const bf16s* __restrict__ W, int N, int kslice,
+                                                     float* __restrict__ part) {
+  __shared__ __align__(16) uint16_t Bt[2][kGdBN * kGdKP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * kGdBN, sl = blockIdx.y, b0 = blockIdx.z * 16;
+  const int k0 = sl * kslice, k1 = min(k0 + kslice, K);
+  const int ns = (k1 - k0) / kGdBK;
+  // staging units: (row pair p, 8-column group g); 16 x 32 units, two per thread;
+  // consecutive threads take consecutive row pairs, so their packed LDS words are
+  // consecutive (the 16 lanes of a column group hit 16 banks)
+  u32x4 r0[2], r1[2];
+  auto fetch = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int unit = tid + 256 * u, p = unit & 15, g = unit >> 4;
+      const int col = min(n0 + 8 * g, N - 8);
+      const int64_t row = k0 + st * kGdBK + 2 * p;
+      r0[u] = ld16_stream(W + row * N + col);
+      r1[u] = ld16_stream(W + (row + 1) * N + col);
+    }
+  };
+  auto stash = [&](int buf) {
+    uint32_t* b32 = reinterpret_cast<uint32_t*>(Bt[buf]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int unit = tid + 256 * u, p = unit & 15, g = unit >> 4;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t lo = (r0[u][j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+        const uint32_t hi = (r1[u][j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+        b32[((8 * g + j) * kGdKP) / 2 + p] = lo | (hi << 16);
+      }
+    }
+  };
+  const int fr = lane & 15, fg = lane >> 4;
+  const bf16s* xr = x + (int64_t)min(b0 + fr, B - 1) * K + 8 * fg;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int st = 0; st < ns; ++st) {
+    if (st + 1 < ns) fetch(st + 1);
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ld16(xr + k0 + st * kGdBK));
+    const uint16_t* bt = Bt[st & 1];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&bt[(64 * wave + 16 * t + fr) * kGdKP + 8 * fg]);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc[t], 0, 0, 0);
+    }
+    if (st + 1 < ns) stash((st + 1) & 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int col = n0 + 64 * wave + 16 * t + fr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int b = b0 + 4 * fg + e;
+      if (b < B && col < N) part[((int64_t)sl * B + b) * N + col] = acc[t][e];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- residual
 // x[i] += sum over chunks of part[c][i]: G lanes per output, lane j adding
 // chunks j, j + G, ... in order, then a butterfly over the G lanes.
@@ -746,6 +828,25 @@ static void launch_gemv(hipStream_t st, const GemvPlan& p, const GemvIn& in, int
   }
 }
 
+// Slices of the reduction for k_gemm_decode: enough blocks to fill the chip.
+static int gd_kslice(int B, int K, int N) {
+  const int blocks = ((N + kGdBN - 1) / kGdBN) * ((B + 15) / 16);
+  int want = (512 + blocks - 1) / blocks;  // (partial sums stay a fraction of the weight bytes)
+  if (want > K / kGdBK) want = K / kGdBK;
+  if (want < 1) want = 1;
+  return (K / want + kGdBK - 1) / kGdBK * kGdBK;
+}
+static int gd_slices(int B, int K, int N) {
+  const int ks = gd_kslice(B, K, N);
+  return (K + ks - 1) / ks;
+}
+static int launch_gemm_decode(hipStream_t st, const void* x, int B, int K, const void* W, int N, float* part) {
+  const int ks = gd_kslice(B, K, N), ns = (K + ks - 1) / ks;
+  POP_LAUNCH(k_gemm_decode, dim3((N + kGdBN - 1) / kGdBN, ns, (B + 15) / 16), dim3(256), 0, st, (const bf16s*)x, B,
+             K, (const bf16s*)W, N, ks, part);
+  return ns;
+}
+
 static int n_qkv(const pop_layer_shape& s) { return (s.n_heads + 2 * s.n_kv_heads) * s.head_dim; }
 static int n_slices(const pop_layer_shape& s) { return (s.cache_len + kAttnKeys - 1) / kAttnKeys; }
 static dim3 qkv_grid(int64_t M, const pop_layer_shape& s, int G) {
@@ -794,7 +895,7 @@ struct DecodeLayerWs {
 static DecodeLayerWs decode_layer_ws(int B, const pop_layer_shape& s, pop_dtype dt, char* base) {
   const int e = elem_bytes(dt), Hd = s.n_heads * s.head_dim, S = n_slices(s);
   const GemvPlan a = gemv_plan(B, s.d, n_qkv(s), e), o = gemv_plan(B, Hd, s.d, e, 64);
-  const int ks = std::max(gemm_kslices(s.d, kLayerKsplit), gemm_kslices(Hd, kLayerKsplit));
+  const int ks = std::max(gd_slices(B, s.d, n_qkv(s)), gd_slices(B, Hd, s.d));
   const size_t part =
       (size_t)std::max({(int64_t)a.chunks * n_qkv(s), (int64_t)o.chunks * s.d, (int64_t)ks * n_qkv(s),
                         (int64_t)ks * s.d}) * B * 4;
@@ -890,8 +991,8 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
   const int D = s.d, Hd = s.n_heads * s.head_dim, e = sizeof(T);
   const GemvPlan pq = gemv_plan(batch, D, n_qkv(s), e), po = gemv_plan(batch, Hd, D, e, 64);
   const bool fuse_norm = batch <= 2;
-  // bf16 from POP_LAYER_GEMM_BATCH tokens: both projections on the prompt pass's matrix-core GEMM, split
-  // into kLayerKsplit reduction slices that the rotation and the residual sum add up
+  // bf16 from POP_LAYER_GEMM_BATCH tokens: both projections on k_gemm_decode (matrix cores), in slices of
+  // the reduction that the rotation and the residual sum add up
   const bool gemm_path = sizeof(T) == 2 && batch >= POP_LAYER_GEMM_BATCH;
   int qkv_slices = 1, o_slices = 1;  // partial products the matrix-core projections leave
   GemvIn qin{};
@@ -904,12 +1005,12 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
     POP_LAUNCH(k_rmsnorm<T>, dim3(batch), dim3(256), 0, h, x, D, w->attn_norm, (float)s.eps, (T*)lw.xn);
     qin.x = lw.xn;
     if (gemm_path)
-      qkv_slices = launch_gemm_kmajor(h, lw.xn, batch, D, w->Wqkv_T, D, n_qkv(s), POP_BF16, lw.part, kLayerKsplit);
+      qkv_slices = launch_gemm_decode(h, lw.xn, batch, D, w->Wqkv_T, n_qkv(s), lw.part);
     else
       launch_gemv<T, kXPlain>(h, pq, qin, batch, D, w->Wqkv_T, n_qkv(s), lw.part);
   }
   if (gemm_path)
-    POP_LAUNCH((k_qkv_rope<T, kLayerKsplit>), qkv_grid(batch, s, kLayerKsplit), dim3(256), 0, h, lw.part,
+    POP_LAUNCH((k_qkv_rope<T, kGdLanes>), qkv_grid(batch, s, kGdLanes), dim3(256), 0, h, lw.part,
                qkv_slices, batch, s.n_heads, s.n_kv_heads, s.head_dim, 1, 0, pos, s.rope_theta,
                s.cache_len, lw.q, (T*)Kc, (T*)Vc);
   else
@@ -929,7 +1030,7 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
                s.head_dim, (T*)lw.ao);
     oin.x = lw.ao;
     if (gemm_path)
-      o_slices = launch_gemm_kmajor(h, lw.ao, batch, Hd, w->Wo_T, Hd, D, POP_BF16, lw.part, kLayerKsplit);
+      o_slices = launch_gemm_decode(h, lw.ao, batch, Hd, w->Wo_T, D, lw.part);
     else
       launch_gemv<T, kXPlain>(h, po, oin, batch, Hd, w->Wo_T, D, lw.part);
   }
@@ -937,7 +1038,7 @@ static void enqueue_layer_decode_attention(hipStream_t h, float* x, int batch, c
   // block's device-scope release writes back its XCD's L2.)
   const int64_t n = (int64_t)batch * D;
   if (gemm_path)
-    POP_LAUNCH(k_sum_residual<kLayerKsplit>, dim3((unsigned)((n * kLayerKsplit + 255) / 256)), dim3(256), 0, h,
+    POP_LAUNCH(k_sum_residual<kGdLanes>, dim3((unsigned)((n * kGdLanes + 255) / 256)), dim3(256), 0, h,
                lw.part, o_slices, n, x);
   else
     POP_LAUNCH(k_sum_residual<kSumLanes>, dim3((unsigned)((n * kSumLanes + 255) / 256)), dim3(256), 0, h, lw.part,

@@ -297,20 +297,10 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __rest
 // W_downT rows past d_ff are clamped to row d_ff - 1 (they meet Z's zero
 // padding) and columns past d to the last vector (their outputs are not
 // written).  No branch or select follows a load.
-// kslice > 0 splits the reduction: block b works on slice s = b / (mt * nt),
-// rows [s * kslice, (s + 1) * kslice) of W_downT (kslice % 64 == 0), and
-// writes its partial product to Y + s * M * d.
 template <int BM, int NS>
 __global__ __launch_bounds__(kGThreads) void k_prompt_down(const uint16_t* __restrict__ Z, int M, int ldz,
                                                            const bf16s* __restrict__ WdT, int d_ff, int d,
-                                                           float* __restrict__ Y, int mt, int nt, int kslice = 0) {
-  if (kslice > 0) {
-    const int sl = blockIdx.x / (mt * nt);
-    Z += (int64_t)sl * kslice;
-    WdT += (int64_t)sl * kslice * d;
-    Y += (int64_t)sl * M * d;
-    d_ff = min(kslice, d_ff - sl * kslice);
-  }
+                                                           float* __restrict__ Y, int mt, int nt) {
   constexpr int WM = BM / 64;            // waves along the tokens
   constexpr int WN = 4 / WM;             // waves along the columns
   constexpr int JF = kBN / WN / 16;      // 16-column fragments per wave
@@ -319,7 +309,7 @@ __global__ __launch_bounds__(kGThreads) void k_prompt_down(const uint16_t* __res
   __shared__ __align__(16) uint16_t Bs[2][kBN * kLd];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int m_tile, n_tile;
-  tile_of(kslice > 0 ? blockIdx.x % (mt * nt) : blockIdx.x, mt * nt, mt, m_tile, n_tile);
+  tile_of(blockIdx.x, mt * nt, mt, m_tile, n_tile);
   const int m0 = m_tile * BM, n0 = n_tile * kBN;
   const int wm = wave / WN, wn = wave % WN;
   const int kp = tid & 31, cb = (tid >> 5) * 8;
@@ -542,17 +532,9 @@ static void launch_prompt_ffn(hipStream_t st, const void* X, int64_t n_tokens, i
   }
 }
 
-int launch_gemm_kmajor(void* stream, const void* A, int M, int lda, const void* Bk, int K, int N, pop_dtype dt,
-                       float* Y, int ksplit) {
+void launch_gemm_kmajor(void* stream, const void* A, int M, int lda, const void* Bk, int K, int N, pop_dtype dt,
+                        float* Y) {
   hipStream_t st = (hipStream_t)stream;
-  if (ksplit > 1 && dt == POP_BF16 && M <= (int)kChunkTokens) {  // slices of the reduction, one Y each
-    const int kslice = (K / ksplit + kBK - 1) / kBK * kBK;
-    const int ns = (K + kslice - 1) / kslice;
-    const int mt = (M + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;
-    POP_LAUNCH((k_prompt_down<128, POP_DOWN_NS>), dim3(mt * nt * ns), dim3(kGThreads), 0, st, (const uint16_t*)A, M,
-               lda, (const bf16s*)Bk, K, N, Y, mt, nt, kslice);
-    return ns;
-  }
   for (int m0 = 0; m0 < M; m0 += (int)kChunkTokens) {  // row chunks keep every grid dimension small
     const int Mc = M - m0 < (int)kChunkTokens ? M - m0 : (int)kChunkTokens;
     float* Yc = Y + (int64_t)m0 * N;
@@ -565,7 +547,6 @@ int launch_gemm_kmajor(void* stream, const void* A, int M, int lda, const void* 
                  (const float*)A + (int64_t)m0 * lda, Mc, lda, (const float*)Bk, K, N, Yc);
     }
   }
-  return 1;
 }
 
 }  // namespace pop
