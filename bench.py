@@ -47,8 +47,6 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run 3 device-to-device copies of this many MiB (a known-size kernel that "
                          "calibrates the profiler's HBM byte counters)")
-    ap.add_argument("--two-streams", action="store_true",
-                    help="decode through pop_decode_ffn_2s (candidate chain on a second stream)")
     return ap.parse_args()
 
 
@@ -169,17 +167,9 @@ def main():
         for l in range(L):
             partition(l)
 
-    two = pop.TwoStream() if args.two_streams else None
-
-    def decode_layers_1s():
+    def decode_layers():
         for l in range(L):
             pop.pop_decode_ffn(x_buf[l], Wg[l], Wu[l], WdT[l], R[l], C[l], w.r, y=y[l], ws=ws_dec)
-
-    def decode_layers_2s():
-        for l in range(L):
-            pop.pop_decode_ffn_2s(x_buf[l], Wg[l], Wu[l], WdT[l], R[l], C[l], w.r, two, y=y[l], ws=ws_dec)
-
-    decode_layers = decode_layers_1s if two is None else decode_layers_2s
 
     def dense_layers():
         for l in range(L):
@@ -192,7 +182,7 @@ def main():
         x_buf.copy_(Xdec[0])
         prefill()
         prefill_unfused()
-        decode_layers_1s()
+        decode_layers()
         decode_layers()
         dense_layers()
     torch.cuda.current_stream().wait_stream(side)
@@ -200,7 +190,7 @@ def main():
     graphs = {}
     for name, fn in (("prefill", prefill), ("prefill_unfused", prefill_unfused), ("prompt_ffn", prompt_ffn_layers),
                      ("partition", partition_layers),
-                     ("decode", decode_layers), ("decode_1s", decode_layers_1s), ("dense", dense_layers)):
+                     ("decode", decode_layers), ("dense", dense_layers)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
@@ -248,11 +238,6 @@ def main():
         for t in range(T):
             x_buf.copy_(Xdec[t])
             graphs["dense"].replay()
-
-    def decode_only_1s():
-        for t in range(T):
-            x_buf.copy_(Xdec[t])
-            graphs["decode_1s"].replay()
 
     # ------------------------------------------------------------ ablation variants (POP notes, ablation table)
     # (1) static prefill mask: the n_live channels of highest prefill importance, no candidates;
@@ -327,14 +312,12 @@ def main():
         del gp
 
     ms_dec = timed(decode_only, 1)
-    ms_dec_1s = timed(decode_only_1s, 1)
     ms_dense = timed(dense_only, 1)
     t_ls = ms_dec / (T * L)          # ms per pruned layer-step
     t_ls_dense = ms_dense / (T * L)
     bytes_ls = metrics.decode_bytes(d, n_R, n_C, k, B, e)
     bytes_dense = metrics.dense_decode_bytes(d, d_ff, B, e)
-    log(f"[bench] decode {t_ls * 1e3:.1f} us/layer-step ({bytes_ls / (t_ls * 1e-3) / 1e9:.0f} GB/s; "
-        f"pop_decode_ffn graph {ms_dec_1s / (T * L) * 1e3:.1f} us), "
+    log(f"[bench] decode {t_ls * 1e3:.1f} us/layer-step ({bytes_ls / (t_ls * 1e-3) / 1e9:.0f} GB/s), "
         f"dense {t_ls_dense * 1e3:.1f} us ({bytes_dense / (t_ls_dense * 1e-3) / 1e9:.0f} GB/s), "
         f"static mask {ms_static / (T * L) * 1e3:.1f} us, full re-evaluation {ms_full / (T * L) * 1e3:.1f} us, "
         f"periodic refresh " + ", ".join(f"every {p}: {v * 1e3:.1f} us" for p, v in periodic.items()) + ", "
@@ -489,7 +472,7 @@ def main():
         "config": {
             "workload": w.name, "layers": L, "d": d, "d_ff": d_ff, "r_ffn": w.r, "gamma": w.gamma,
             "prompt_tokens": n_tok, "decode_steps": T, "decode_batch": B, "hip_graphs": True,
-            "streams": 1 if two is None else 2,
+            "streams": 1,
             "step": "prefill (fused dense prompt FFN + partition) of every layer + every decode step over every layer",
         },
         "roofline": {
@@ -519,7 +502,6 @@ def main():
             "algorithmic_bytes_per_layer_step": bytes_dense,
             "hbm_gbps": round(bytes_dense / (t_ls_dense * 1e-3) / 1e9, 1),
         },
-        "decode_pop_decode_ffn_us_per_layer_step": round(ms_dec_1s / (T * L) * 1e3, 3),
         "speedup_vs_dense": round(t_ls_dense / t_ls, 4),
         "ideal_speedup_bytes": round(bytes_dense / bytes_ls, 4),
         "ablation": {

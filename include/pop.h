@@ -34,9 +34,15 @@
  *     null stream).  The host never waits for the device and never reads device
  *     memory, so every call may be captured in a HIP graph.
  *   - The caller allocates and owns every buffer: inputs, outputs and the
- *     workspace.  The library keeps no pointer after it returns and holds no
- *     mutable global state; calls on different streams need distinct
- *     workspaces.
+ *     workspace.  The library keeps no pointer after it returns.  Its only
+ *     host-side state is per thread (the last error message and the trace
+ *     events of pop_set_trace_events) or a per-device cache of device
+ *     attributes (compute units, occupancy); no call's result depends on it.
+ *     Calls on different streams need distinct workspaces.
+ *   - A workspace starts zero-filled (the first call on it must see zeros).
+ *     Decode workspaces carry control words between calls: every call that
+ *     completes leaves them zero again, so a workspace stays valid for any
+ *     later call, of any shape, ordered after it on one stream.
  *   - Device buffers are contiguous, row-major and 16-byte aligned.
  *     dtype POP_BF16 needs d % 8 == 0, POP_F32 needs d % 4 == 0.
  *   - Index lists (R, C) are int32, strictly ascending, in [0, d_ff) and
@@ -155,6 +161,13 @@ pop_status pop_partition_select(const float* importance, int32_t d_ff, double r,
 /* Workspace bytes pop_decode_ffn / pop_dense_ffn_decode need. */
 size_t pop_decode_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff);
 
+/* Byte offset of z in a decode workspace.  The bytes before it are control
+ * and hand-over words of the single-launch batch-1 step, zero between calls;
+ * the 32-bit word at offset 0 is a sticky error code: nonzero after a batch-1
+ * step whose bounded in-kernel wait ran out (that step's y is then not
+ * valid).  The library never clears it. */
+#define POP_DECODE_WS_Z_OFFSET 66560
+
 /*
  * pop_decode_ffn — POP notes, "Key design 2" and "Overall framework".
  *   x          device, [batch, d] in dt: this step's FFN inputs; the batch
@@ -168,43 +181,36 @@ size_t pop_decode_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff);
  *   r          pruning rate; k = clamp(round((1 - r) d_ff) - n_R, 0, n_C).
  *   y          device fp32 [batch, d] output.
  *   selected   optional device int32 [k]: the selected candidates, ascending.
- *   ws         device workspace >= pop_decode_workspace_bytes(batch, d, d_ff).
- *              After the call completes, byte offset 256 holds the
- *              intermediate z (fp32 [batch, n_R + n_C], R columns first, then
- *              C) and byte offset 256 + align_up(4 * batch * d_ff + 16, 256)
- *              the candidate scores (fp32 [n_C]).
- * Kernels at batch 1: the candidates' gate/up rows and scores; then the
- * one-workgroup top-k running beside a stream over every retained row's gate,
- * up and W_downT rows (z and its down contribution in one pass); the selected
- * rows' down contributions; a fixed-order reduction.
- * At batch > 1: row-gathered gate/up GEMV with fused SiLU*up and candidate
- * score; one-workgroup radix top-k; gathered down-projection over R and the
- * selected rows of W_downT; fixed-order reduction.  Deterministic.
+ *   ws         device workspace >= pop_decode_workspace_bytes(batch, d, d_ff),
+ *              zero-filled before its first use.  After the call completes,
+ *              byte offset POP_DECODE_WS_Z_OFFSET holds the intermediate z
+ *              (fp32 [batch, n_R + n_C], R columns first, then C) and byte
+ *              offset POP_DECODE_WS_Z_OFFSET + align_up(4 * batch * d_ff + 16,
+ *              256) the candidate scores (fp32 [n_C]).
+ * Kernels at batch 1 (d <= 1024 vectors of 16 bytes, n_C <= 4096): ONE launch.
+ * Its first workgroup is the candidate top-k; every other workgroup streams
+ * an even share of the candidates' gate/up rows (handing each |z| to the
+ * top-k through a valid-tagged word), then of the retained channels' gate, up
+ * and W_downT rows (z and its down contribution in one pass), then adds the
+ * selected rows the top-k hands back; the last workgroups to finish add the
+ * per-workgroup partial sums, in a fixed order, into y.  The grid never
+ * exceeds what the device holds at once, and every in-kernel wait is bounded
+ * (see POP_DECODE_WS_Z_OFFSET for the error word).  Other batch-1 shapes:
+ * three launches (candidate rows; the top-k beside the retained stream; the
+ * selected rows and the fixed-order sum).
+ * Batches 2-64 in bf16: the matrix-core kernels (16-token tiles): gate/up
+ * over R u C with fused SiLU*up and the batch-max score; the down-projection
+ * over the retained rows with the candidate top-k as one of its workgroups;
+ * the down-projection over the selected rows; a fixed-order sum.  fp32 and
+ * wider batches: gate/up GEMV, one-workgroup radix top-k, gathered
+ * down-projection, fixed-order sum.  Deterministic (the same bits on every
+ * call with the same inputs).
  */
 pop_status pop_decode_ffn(const void* x, int32_t batch, int32_t d, const void* W_gate,
                           const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
                           const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C,
                           double r, float* y, int32_t* selected, void* ws, size_t ws_bytes,
                           void* stream);
-
-/*
- * pop_decode_ffn_2s — pop_decode_ffn with the candidate chain on a second
- * stream.  At batch 1 the candidates' gate/up rows and scores, the top-k and
- * the selected rows' down contributions depend on each other but not on the
- * retained rows; they run on `aux_stream` beside the retained-row stream on
- * `stream`, and the fixed-order sum on `stream` waits for both.  fork_event and
- * join_event are caller-created HIP events (no timing needed) used to order
- * the two streams; the call records them and makes the streams wait on them,
- * so it may be captured in a HIP graph from `stream`.  Same result, bit for
- * bit, as pop_decode_ffn.  Other batch sizes run pop_decode_ffn on `stream`.
- * Errors: INVALID_ARGUMENT when aux_stream, fork_event or join_event is NULL
- * or aux_stream == stream; otherwise as pop_decode_ffn.
- */
-pop_status pop_decode_ffn_2s(const void* x, int32_t batch, int32_t d, const void* W_gate,
-                             const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
-                             const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C, double r,
-                             float* y, int32_t* selected, void* ws, size_t ws_bytes, void* stream,
-                             void* aux_stream, void* fork_event, void* join_event);
 
 /* Workspace bytes of pop_decode_ffn_periodic (independent of r and the lists). */
 size_t pop_decode_periodic_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff);
@@ -293,8 +299,8 @@ pop_status pop_decode_down(const float* z, int32_t batch, int32_t n_A, const voi
  * pop_dense_ffn_decode — the unpruned gated MLP (equation (1) of the
  * batch-wise pruning page, section 3.1) for one decode step over all d_ff
  * channels: the dense baseline the pruned step is compared with.  Same
- * layouts and workspace as pop_decode_ffn; after the call, byte offset 256 of
- * the workspace holds z (fp32 [batch, d_ff]).
+ * layouts and workspace as pop_decode_ffn; after the call, byte offset
+ * POP_DECODE_WS_Z_OFFSET of the workspace holds z (fp32 [batch, d_ff]).
  */
 pop_status pop_dense_ffn_decode(const void* x, int32_t batch, int32_t d, const void* W_gate,
                                 const void* W_up, const void* W_downT, int32_t d_ff,

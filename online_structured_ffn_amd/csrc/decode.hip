@@ -9,7 +9,10 @@
 //   K6r fixed-order reduction of the partial sums into y
 #include <hip/hip_runtime.h>
 
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "decode_mfma.h"
 #include "pop_device.h"
@@ -273,7 +276,9 @@ template <typename T, int NV, bool kDown>
 __device__ __forceinline__ void fused_rows(const int* rows, int nrows, const T* __restrict__ Wg, const T* __restrict__ Wu,
                                            const T* __restrict__ WdT, int d, const u32x4 (&xv)[NV],
                                            float (&part)[2][kFusedWaves][2 * kFusedP], float (&acc)[NV][Vec<T>::N],
-                                           float* __restrict__ zout, int zbase, float* __restrict__ score) {
+                                           float* __restrict__ zout, int zbase, float* __restrict__ score,
+                                           uint64_t* __restrict__ pub = nullptr, float* zkeep = nullptr) {
+  if (nrows <= 0) return;  // block-uniform
   FusedRowBuf<T, NV> A, Bf;
 #pragma unroll
   for (int p = 0; p < kFusedP; ++p)
@@ -293,6 +298,8 @@ __device__ __forceinline__ void fused_rows(const int* rows, int nrows, const T* 
         if (i0 + p < nrows) {
           zout[zbase + i0 + p] = zs[p];
           if (score != nullptr) score[i0 + p] = fabsf(zs[p]);
+          if (pub != nullptr) st_coh(&pub[i0 + p], pack_valid(__float_as_uint(fabsf(zs[p])), __float_as_uint(zs[p])));
+          if (zkeep != nullptr) zkeep[i0 + p] = zs[p];
         }
     }
     if (i0 + kFusedP >= nrows) break;
@@ -304,9 +311,78 @@ __device__ __forceinline__ void fused_rows(const int* rows, int nrows, const T* 
         if (i0 + kFusedP + p < nrows) {
           zout[zbase + i0 + kFusedP + p] = zs[p];
           if (score != nullptr) score[i0 + kFusedP + p] = fabsf(zs[p]);
+          if (pub != nullptr)
+            st_coh(&pub[i0 + kFusedP + p], pack_valid(__float_as_uint(fabsf(zs[p])), __float_as_uint(zs[p])));
+          if (zkeep != nullptr) zkeep[i0 + kFusedP + p] = zs[p];
         }
     }
   }
+}
+
+// Up to NB candidate rows at once (gate and up rows only): every load issued
+// before any is used, so the batch costs one memory round trip, then one
+// cross-wave reduction for all its rows.  Threads p < nrows write row p's z,
+// |z| and, when pub is set, its hand-over word pack_valid(bits of |z|, bits of z).
+template <typename T, int NV, int NB>
+__device__ __forceinline__ void cand_rows(const int* rows, int nrows, const T* __restrict__ Wg, const T* __restrict__ Wu,
+                                          int d, const u32x4 (&xv)[NV], float (&part)[kFusedWaves][2 * NB],
+                                          float* __restrict__ zout, float* __restrict__ score,
+                                          uint64_t* __restrict__ pub) {
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  u32x4 g[NB][NV], u[NB][NV];
+#pragma unroll
+  for (int p = 0; p < NB; ++p) {
+    const int64_t base = (int64_t)rows[min(p, nrows - 1)] * d;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int col = min(j * kFusedThreads * V + (int)threadIdx.x * V, d - V);
+      g[p][j] = ld16_stream(Wg + base + col);
+      u[p][j] = ld16_stream(Wu + base + col);
+    }
+  }
+  float pg[NB], pu[NB];
+#pragma unroll
+  for (int p = 0; p < NB; ++p) {
+    pg[p] = pu[p] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float gf[V], uf[V], xx[V];
+      unpack(g[p][j], gf, T{});
+      unpack(u[p][j], uf, T{});
+      unpack(xv[j], xx, T{});
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        pg[p] = fmaf(gf[v], xx[v], pg[p]);
+        pu[p] = fmaf(uf[v], xx[v], pu[p]);
+      }
+    }
+    pg[p] = wave_sum_last(pg[p]);
+    pu[p] = wave_sum_last(pu[p]);
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int p = 0; p < NB; ++p) {
+      part[wave][2 * p] = pg[p];
+      part[wave][2 * p + 1] = pu[p];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < NB && (int)threadIdx.x < nrows) {
+    const int p = threadIdx.x;
+    float gs = part[0][2 * p], us = part[0][2 * p + 1];
+#pragma unroll
+    for (int w = 1; w < kFusedWaves; ++w) {
+      gs += part[w][2 * p];
+      us += part[w][2 * p + 1];
+    }
+    const float zz = silu(gs) * us;
+    zout[p] = zz;
+    score[p] = fabsf(zz);
+    if (pub != nullptr) st_coh(&pub[p], pack_valid(__float_as_uint(fabsf(zz)), __float_as_uint(zz)));
+  }
+  __syncthreads();  // part is reused by the next batch
 }
 
 // Loads this thread's x vectors and clears its down accumulators.
@@ -406,6 +482,11 @@ __global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
 // flight at once.  The per-lane sums are reduced across lanes (shuffles), then
 // across waves in wave order (LDS).
 constexpr int kFinThreads = 1024;
+// Control words of the single-launch batch-1 step (32-bit, 128 bytes apart):
+// the sticky error word, then counters that k_pop_finish clears for the next
+// call (words kCtlFirstCounter .. kCtlFirstCounter + kCtlResetWords - 1).
+constexpr int kCtlErr = 0, kCtlCdone = 32;
+constexpr int kCtlFirstCounter = 32, kCtlResetWords = 224;
 constexpr int kFinRowsPerBatch = 1280;  // selected rows whose loads are in flight together
 constexpr int kFinPartials = 512;       // partial rows whose loads are in flight together
 
@@ -426,7 +507,9 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
                                                             const int32_t* __restrict__ sel,
                                                             const int32_t* __restrict__ pos, int k,
                                                             const T* __restrict__ WdT, int d, int d_ff,
-                                                            float* __restrict__ y, int accumulate) {
+                                                            float* __restrict__ y, int accumulate,
+                                                            uint32_t* reset_word, uint64_t* reset_words,
+                                                            int n_reset_words) {
   constexpr int V = Vec<T>::N;
   constexpr int LR = kFinCols / V;       // lanes per W_downT row
   constexpr int RPW = 64 / LR;           // W_downT rows per wave instruction
@@ -437,6 +520,10 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
   constexpr int PB = (kFinPartials + PPB - 1) / PPB;           // partial-row loads in flight per lane
   constexpr int SB = (kFinRowsPerBatch + RPB - 1) / RPB;       // selected-row loads in flight per lane
   __shared__ float red[kFinThreads / 64][kFinCols];
+  // the single-launch step's counter and hand-over words, cleared for the next call
+  if (reset_word != nullptr && blockIdx.x == 0 && threadIdx.x < kCtlResetWords) st_coh(reset_word + threadIdx.x, 0u);
+  for (int i = blockIdx.x * kFinThreads + threadIdx.x; i < n_reset_words; i += gridDim.x * kFinThreads)
+    st_coh(&reset_words[i], (uint64_t)0);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = fin_slice(blockIdx.x, gridDim.x) * kFinCols;
@@ -542,6 +629,180 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
 #pragma unroll
     for (int w2 = 1; w2 < kFinThreads / 64; ++w2) t += red[w2][threadIdx.x];
     y[c0 + threadIdx.x] = accumulate ? y[c0 + threadIdx.x] + t : t;  // accumulate: y += FFN(x)
+  }
+}
+
+// ---------------------------------------------------------------- single-launch batch-1 step
+// The batch-1 step in two launches, the candidate chain running inside the
+// retained stream of the first.  Block 0 of k_pop_linked is the candidate
+// top-k; blocks 1 .. nW are workers, and worker w takes an even share
+// (split_at) of each list:
+//   1. its candidate rows: gate and up rows, z and |z|; each row's (|z|, z)
+//      goes to block 0 as one valid-tagged word; once they are all written
+//      (a wait on this wave's own stores, where no load is in flight) the
+//      worker counts itself done;
+//   2. its retained rows: gate, up and W_downT rows, z, and z * W_downT added
+//      into its partial y (registers);
+//   3. the cut: block 0 publishes (v, tie position) once it has selected; the
+//      worker reads one copy of it and adds z * W_downT[channel, :] for each of
+//      ITS candidate rows that the cut selects (z kept in LDS since step 1);
+//   4. its partial y, slice-major, with plain stores.
+// k_pop_finish then adds the nW partials in a fixed order into y and clears
+// the hand-over words for the next call.  Only block 0 waits on many
+// workgroups (one counter, one poller); a worker waits at most for the cut,
+// which is normally out long before its retained rows end.  Nothing waits on
+// a workgroup that is not running: the host keeps the grid within what the
+// device holds at once, and block 0 needs only the workers' first phase.  Every
+// wait is bounded (kPollLimit polls); one that runs out sets the sticky error
+// word ctl[kCtlErr] and the step goes on (its y is then wrong).
+#ifndef POP_LINKED_ON
+#define POP_LINKED_ON 1  // 0: batch-1 steps take the three-launch path
+#endif
+constexpr int kLinkedTopkMaxN = 4096;
+constexpr int kLinkedMaxWorkers = POP_FUSED_RBLOCKS - 1;
+constexpr int kPollLimit = 1 << 20;
+constexpr int kSelRowsPerPass = 8;
+constexpr int kThrCopies = 32;  // copies of the published cut
+constexpr int kThrStride = 16;  // 64-bit words between copies (128 bytes)
+constexpr int kCandBatch = 8;  // candidate rows whose loads a worker issues together
+// The control words (1 KB), then the hand-over words: the candidate words (at
+// most kLinkedTopkMaxN) and the copies of the cut.  A fixed region at the
+// start of every decode workspace that no other call writes; k_pop_finish
+// leaves it zero (the error word aside).
+constexpr size_t kCtlBytes = 1024;
+constexpr size_t kHandWords = kLinkedTopkMaxN + kThrCopies * kThrStride;
+constexpr size_t kHandBytes = 2 * kLinkedTopkMaxN * sizeof(uint64_t);
+static_assert(kHandWords * sizeof(uint64_t) <= kHandBytes, "hand-over region");
+
+__device__ __forceinline__ int split_at(int n, int parts, int i) { return (int)(((int64_t)n * i) / parts); }
+
+template <typename T, int NV, bool kIdentity>
+__global__ __launch_bounds__(kFusedThreads, 2) void k_pop_linked(
+    const T* __restrict__ x, const T* __restrict__ Wg, const T* __restrict__ Wu, const T* __restrict__ WdT,
+    const int32_t* __restrict__ R, const int32_t* __restrict__ C, float* __restrict__ z, float* __restrict__ score,
+    uint64_t* __restrict__ hand, int32_t* __restrict__ sel_out, float* __restrict__ partial,
+    uint32_t* __restrict__ ctl, int d, int d_ff, int n_R, int n_C, int k, int nW) {
+  constexpr int V = Vec<T>::N;
+  struct Work {
+    int rows[kFusedMaxRows];
+    uint64_t cw[kFusedMaxRows];  // hand-over words of this worker's share of C
+    float part[2][kFusedWaves][2 * kFusedP];
+    float cpart[kFusedWaves][2 * kCandBatch];
+    int crow[kFusedMaxRows];  // this worker's share of C (channels)
+    int s_ch[kSelRowsPerPass];
+    float s_z[kSelRowsPerPass];
+    int n_sel;
+    int sel_rows[kFusedMaxRows];  // this worker's selected candidates (indices into its rows)
+    uint64_t cut;
+  };
+  __shared__ union {
+    SelShared<kFusedThreads, kLinkedTopkMaxN> sel;
+    Work w;
+  } sh;
+  const int tid = threadIdx.x;
+  const bool chain = n_C > 0 && k > 0;  // a top-k runs
+  uint64_t* cand = hand;
+  uint64_t* thr = hand + kLinkedTopkMaxN;
+  if (blockIdx.x == 0) {
+    if (chain)
+      topk_threshold_linked(cand, n_C, k, ctl + kCtlCdone, n_C, C, (int32_t*)nullptr, sel_out, thr, kThrCopies,
+                            kThrStride, sh.sel, kPollLimit, ctl + kCtlErr);
+    return;
+  }
+  const int w = blockIdx.x - 1;
+  const int c0 = split_at(n_C, nW, w), nc = split_at(n_C, nW, w + 1) - c0;
+  const int r0 = split_at(n_R, nW, w), nr = split_at(n_R, nW, w + 1) - r0;
+  u32x4 xv[NV];
+  float acc[NV][V];
+  fused_setup<T, NV>(x, d, xv, acc);
+  for (int i = tid; i < nc; i += kFusedThreads) sh.w.crow[i] = clamp_channel(C[c0 + i], d_ff);
+  for (int i = tid; i < nr; i += kFusedThreads) sh.w.rows[i] = kIdentity ? r0 + i : clamp_channel(R[r0 + i], d_ff);
+  __syncthreads();
+  // 1. candidate rows, kCandBatch at a time (one round trip each)
+  for (int i0 = 0; i0 < nc; i0 += kCandBatch)
+    cand_rows<T, NV, kCandBatch>(sh.w.crow + i0, min(kCandBatch, nc - i0), Wg, Wu, d, xv, sh.w.cpart,
+                                 z + n_R + c0 + i0, score + c0 + i0, chain ? cand + c0 + i0 : nullptr);
+  if (chain && tid < kCandBatch) {
+    mem_wait();  // this wave's candidate words are out (no load is in flight here)
+    if (tid == 0 && nc > 0) add_coh(ctl + kCtlCdone, (uint32_t)nc);
+  }
+  __syncthreads();
+  // 2. retained rows
+  fused_rows<T, NV, true>(sh.w.rows, nr, Wg, Wu, WdT, d, xv, sh.w.part, acc, z, r0, nullptr);
+  __syncthreads();
+  // 3. this worker's candidates that the cut selects
+  //    (its static share of C: positions c0 .. c0 + nc - 1, z from their hand-over words)
+  if (chain && nc > 0) {
+    // the words are read beside the poll; one read before every word was
+    // written lacks its valid bit and is read again once the cut is out (the
+    // cut is published only after every word was seen valid)
+    for (int i = tid; i < nc; i += kFusedThreads) sh.w.cw[i] = ld_coh(&cand[c0 + i]);
+    if (tid == 0) {
+      bool ok;
+      const uint64_t e = poll_coh(&thr[(w % kThrCopies) * kThrStride], [](uint64_t v) { return is_valid(v); },
+                                  kPollLimit, ok);
+      if (!ok) st_coh(ctl + kCtlErr, 2u);
+      sh.w.cut = ok ? e : 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < nc; i += kFusedThreads)
+      if (!is_valid(sh.w.cw[i])) sh.w.cw[i] = ld_coh(&cand[c0 + i]);
+    __syncthreads();
+    if (tid == 0) {
+      const uint64_t e = sh.w.cut;
+      const uint32_t cv = (uint32_t)(e >> 32) & 0x7fffffffu;
+      const int tie = (int)(uint32_t)e;
+      int ns = 0;
+      for (int i = 0; i < nc; ++i) {
+        const uint32_t xb = (uint32_t)(sh.w.cw[i] >> 32) & 0x7fffffffu;  // bits of |z|
+        if (is_valid(e) && (xb > cv || (xb == cv && c0 + i <= tie))) sh.w.sel_rows[ns++] = i;
+      }
+      sh.w.n_sel = ns;
+    }
+    __syncthreads();
+    const int ns = sh.w.n_sel;
+    for (int j0 = 0; j0 < ns; j0 += kSelRowsPerPass) {
+      const int nb = min(kSelRowsPerPass, ns - j0);
+      if (tid < nb) {
+        const int i = sh.w.sel_rows[j0 + tid];
+        sh.w.s_ch[tid] = sh.w.crow[i];
+        sh.w.s_z[tid] = __uint_as_float((uint32_t)sh.w.cw[i]);
+      }
+      __syncthreads();
+      u32x4 wv[kSelRowsPerPass][NV];
+#pragma unroll
+      for (int p = 0; p < kSelRowsPerPass; ++p) {
+        const int ch = sh.w.s_ch[min(p, nb - 1)];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int col = min(j * kFusedThreads * V + tid * V, d - V);
+          wv[p][j] = ld16_stream(WdT + (int64_t)ch * d + col);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < kSelRowsPerPass; ++p) {
+        const float zz = p < nb ? sh.w.s_z[p] : 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          float f[V];
+          unpack(wv[p][j], f, T{});
+#pragma unroll
+          for (int v = 0; v < V; ++v) acc[j][v] = fmaf(zz, f[v], acc[j][v]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // 4. partial y, slice-major: column c of worker w at ((c / kFinCols) * nW + w) * kFinCols + c % kFinCols
+  static_assert(kFinCols % V == 0, "a thread's columns lie in one slice");
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int col = j * kFusedThreads * V + tid * V;
+    if (col < d) {
+      float* out = partial + ((int64_t)(col / kFinCols) * nW + w) * kFinCols + col % kFinCols;
+#pragma unroll
+      for (int v = 0; v < V; ++v) out[v] = acc[j][v];
+    }
   }
 }
 
@@ -725,11 +986,12 @@ static size_t down_ws_bytes(int32_t batch, int32_t d, int32_t n_live) {
 }
 
 struct DecodeWs {
-  unsigned int* ctl;  // reserved
+  uint32_t* ctl;  // control words of the single-launch step (zero between calls)
   float* z;
   float* score;
   int32_t* Q;    // selected positions into C
   int32_t* sel;  // selected channels
+  uint64_t* hand;  // single-launch step: hand-over words (zero between calls)
   char* down;
   size_t down_bytes;
 };
@@ -742,8 +1004,10 @@ static size_t fused_partial_bytes(int32_t d, int32_t d_ff) {
   return align_up((size_t)kFusedRBlocks * align_up((size_t)d, kFinCols) * sizeof(float), 256);
 }
 
+static_assert(kCtlBytes + kHandBytes == POP_DECODE_WS_Z_OFFSET, "z follows the control and hand-over words");
+
 static size_t decode_ws_layout(int32_t batch, int32_t d, int32_t d_ff, char* base, DecodeWs* out) {
-  const size_t tb = 256;
+  const size_t tb = kCtlBytes + kHandBytes;
   const size_t zb = align_up((size_t)batch * d_ff * sizeof(float) + 16, 256);
   const size_t sb = align_up((size_t)d_ff * sizeof(float), 256);
   const size_t qb = align_up((size_t)d_ff * sizeof(int32_t), 256);
@@ -753,12 +1017,14 @@ static size_t decode_ws_layout(int32_t batch, int32_t d, int32_t d_ff, char* bas
     if (fb > db) db = fb;
   }
   if (out) {
-    out->ctl = (unsigned int*)base;
-    out->z = (float*)(base + tb);
-    out->score = (float*)(base + tb + zb);
-    out->Q = (int32_t*)(base + tb + zb + sb);
-    out->sel = (int32_t*)(base + tb + zb + sb + qb);
-    out->down = base + tb + zb + sb + 2 * qb;
+    out->ctl = (uint32_t*)base;
+    out->hand = (uint64_t*)(base + kCtlBytes);
+    char* p = base + tb;
+    out->z = (float*)p;
+    out->score = (float*)(p += zb);
+    out->Q = (int32_t*)(p += sb);
+    out->sel = (int32_t*)(p += qb);
+    out->down = p + qb;
     out->down_bytes = db;
   }
   return tb + zb + sb + 2 * qb + db;
@@ -913,16 +1179,13 @@ static void launch_down(hipStream_t st, const float* z, int B, int n_A, const vo
                      n_live > 0 ? p.n_chunks : 0, n_out, y, (unsigned int*)nullptr, 0);
 }
 
-// Batch-1 decode step through k_pop_step: false when d is too wide for the
-// kernel's per-thread columns (the caller then runs the stage kernels).
-// With aux set, the candidate chain (phases 1-3 without retained shares) runs
-// on aux beside one launch of every retained block on st, joined before the
-// sum; the partial sums and their order are the same as on one stream.
+// Batch-1 decode step in three launches of k_pop_step / k_pop_finish (for
+// shapes the single-launch step does not take): false when d is too wide for
+// the kernel's per-thread columns (the caller then runs the stage kernels).
 template <typename T>
 static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, const void* Wu, const void* WdT,
                          int d_ff, const int32_t* R, int n_R, const int32_t* C, int n_C, int k, float* y,
-                         const DecodeWs& w, hipStream_t aux = nullptr, hipEvent_t fork = nullptr,
-                         hipEvent_t join = nullptr, bool accumulate = false) {
+                         const DecodeWs& w, bool accumulate = false) {
   constexpr int V = Vec<T>::N;
   const int nv = (d + kFusedThreads * V - 1) / (kFusedThreads * V);
   if (nv > 4) return false;
@@ -978,30 +1241,97 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
 #undef POP_STEP_PH
 #undef POP_STEP
   };
-  if (aux != nullptr) {
-    (void)hipEventRecord(fork, st);
-    (void)hipStreamWaitEvent(aux, fork, 0);
-    step(1, aux, nbC, 0, 0);
-    if (n_C > 0 && k > 0 && !fuse_topk) launch_select(aux, w.score, n_C, C, k, w.Q, w.sel);
-    step(2, aux, fuse_topk ? 1 : 0, 0, 0);
-    step(1, st, 0, 0, nbR);
-    (void)hipEventRecord(join, aux);
-    (void)hipStreamWaitEvent(st, join, 0);
-  } else {
-    step(1, st, nbC, 0, nbR1);
-    if (n_C > 0 && k > 0 && !fuse_topk) launch_select(st, w.score, n_C, C, k, w.Q, w.sel);
-    step(2, st, fuse_topk ? 1 : 0, nbR1, nbR2);
-  }
+  step(1, st, nbC, 0, nbR1);
+  if (n_C > 0 && k > 0 && !fuse_topk) launch_select(st, w.score, n_C, C, k, w.Q, w.sel);
+  step(2, st, fuse_topk ? 1 : 0, nbR1, nbR2);
   const dim3 fgrid((d + kFinCols - 1) / kFinCols);
   if (k > 0) {
     POP_LAUNCH((k_pop_finish<T, true>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
                (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, k, (const T*)WdT, d,
-               d_ff, y, (int)accumulate);
+               d_ff, y, (int)accumulate, (uint32_t*)nullptr, (uint64_t*)nullptr, 0);
   } else {
     POP_LAUNCH((k_pop_finish<T, false>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
                (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, 0, (const T*)WdT, d,
-               d_ff, y, (int)accumulate);
+               d_ff, y, (int)accumulate, (uint32_t*)nullptr, (uint64_t*)nullptr, 0);
   }
+  return true;
+}
+
+// Workgroups of `kernel` (kFusedThreads threads) the current device holds at
+// once: its compute units times the occupancy per unit (cached per device and
+// kernel; device attributes only, no stream work).
+static int resident_blocks(const void* kernel) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, kernel);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kFusedThreads, 0) != hipSuccess)
+    return 0;
+  return cache[key] = cus * per;
+}
+
+// The batch-1 step as k_pop_linked + k_pop_finish.  Returns false, having
+// launched nothing, when the step does not fit it (d wider than four 16-byte
+// vectors per thread, more than kLinkedTopkMaxN candidates, too many rows per
+// worker); the caller then takes the three-launch path.
+template <typename T>
+static bool launch_linked(hipStream_t st, const void* x, int d, const void* Wg, const void* Wu, const void* WdT,
+                          int d_ff, const int32_t* R, int n_R, const int32_t* C, int n_C, int k, float* y,
+                          const DecodeWs& w, int32_t* sel_out, bool accumulate) {
+  constexpr int V = Vec<T>::N;
+  const int nv = (d + kFusedThreads * V - 1) / (kFusedThreads * V);
+  if (nv > 4 || n_C > kLinkedTopkMaxN || n_R + n_C <= 0) return false;
+  const bool identity = R == nullptr;
+  const void* kern = nullptr;
+#define POP_LINKED_PICK(NVT)                                                   \
+  kern = identity ? reinterpret_cast<const void*>(&k_pop_linked<T, NVT, true>) \
+                  : reinterpret_cast<const void*>(&k_pop_linked<T, NVT, false>)
+  if (nv <= 1) {
+    POP_LINKED_PICK(1);
+  } else if (nv <= 2) {
+    POP_LINKED_PICK(2);
+  } else {
+    POP_LINKED_PICK(4);
+  }
+#undef POP_LINKED_PICK
+  int cap = resident_blocks(kern) - 1;  // block 0 is the top-k
+  if (cap > kLinkedMaxWorkers) cap = kLinkedMaxWorkers;
+  if (cap < 1) return false;
+  int nW = (n_R + n_C + 7) / 8;
+  if (nW > cap) nW = cap;
+  if (nW < 1) nW = 1;
+  if ((n_C + nW - 1) / nW + (n_R + nW - 1) / nW > kFusedMaxRows) return false;
+  const dim3 grid(1 + nW);
+  float* partial = (float*)w.down;
+#define POP_LINKED(NVT, ID)                                                                                         \
+  POP_LAUNCH((k_pop_linked<T, NVT, ID>), grid, dim3(kFusedThreads), 0, st, (const T*)x, (const T*)Wg,              \
+             (const T*)Wu, (const T*)WdT, R, C, w.z, w.score, w.hand, sel_out, partial, w.ctl, d, d_ff, n_R, n_C, k, \
+             nW)
+#define POP_LINKED_ID(NVT)  \
+  if (identity) {           \
+    POP_LINKED(NVT, true);  \
+  } else {                  \
+    POP_LINKED(NVT, false); \
+  }
+  if (nv <= 1) {
+    POP_LINKED_ID(1)
+  } else if (nv <= 2) {
+    POP_LINKED_ID(2)
+  } else {
+    POP_LINKED_ID(4)
+  }
+#undef POP_LINKED_ID
+#undef POP_LINKED
+  POP_LAUNCH((k_pop_finish<T, false>), dim3((d + kFinCols - 1) / kFinCols), dim3(kFinThreads), 0, st,
+             (const float*)partial, nW, (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel,
+             (const int32_t*)w.Q, 0, (const T*)WdT, d, d_ff, y, (int)accumulate, w.ctl + kCtlFirstCounter, w.hand,
+             (int)kHandWords);
   return true;
 }
 
@@ -1074,8 +1404,10 @@ bool decode_ffn_accumulate_b1(const void* x, int32_t d, const void* W_gate, cons
   if (selected != nullptr) wf.sel = selected;
   hipStream_t st = (hipStream_t)stream;
   trace_mark(st);
-  return POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, Rk, n_R, Ck, n_C, k, y, wf, nullptr,
-                      nullptr, nullptr, true);
+  if (POP_LINKED_ON && POP_DISPATCH(dt, launch_linked, st, x, d, W_gate, W_up, W_downT, d_ff, Rk, n_R, Ck, n_C, k, y,
+                                    w, selected, true))
+    return true;
+  return POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, Rk, n_R, Ck, n_C, k, y, wf, true);
 }
 
 float* decode_ws_z(void* ws, int32_t batch, int32_t d, int32_t d_ff) {
@@ -1175,52 +1507,15 @@ extern "C" pop_status pop_decode_ffn(const void* x, int32_t batch, int32_t d, co
   if (selected != nullptr) wf.sel = selected;  // the top-k writes the caller's list directly
   trace_mark(st);
   if (batch == 1 && n_R + n_C > 0 &&
-      POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, Rk, n_R, Ck, n_C, k, y, wf))
+      ((POP_LINKED_ON && POP_DISPATCH(dt, launch_linked, st, x, d, W_gate, W_up, W_downT, d_ff, Rk, n_R, Ck, n_C, k,
+                                      y, w, selected, false)) ||
+       POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, Rk, n_R, Ck, n_C, k, y, wf)))
     return launched();
   POP_DISPATCH(dt, launch_gateup, st, x, batch, d, W_gate, W_up, d_ff, Rk, n_R, Ck, n_C, w.z, w.score);
   int32_t* sel = selected != nullptr ? selected : w.sel;  // the down stage reads the selected channels here
   POP_DISPATCH(dt, launch_down, st, w.z, batch, n_R + n_C, W_downT, d, d_ff, Rk, n_R, sel, w.Q, k, y,
                (float*)w.down, w.score, Ck, n_C, w.Q, sel);
   return launched();
-}
-
-extern "C" pop_status pop_decode_ffn_2s(const void* x, int32_t batch, int32_t d, const void* W_gate,
-                                        const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
-                                        const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C, double r,
-                                        float* y, int32_t* selected, void* ws, size_t ws_bytes, void* stream,
-                                        void* aux_stream, void* fork_event, void* join_event) {
-  clear_error();
-  if (aux_stream == nullptr || fork_event == nullptr || join_event == nullptr || aux_stream == stream)
-    return fail(POP_ERR_INVALID_ARGUMENT, "aux_stream, fork_event and join_event must be set and aux != stream");
-  pop_status s = check_shape(batch, d, d_ff, dt);
-  if (s != POP_OK) return s;
-  if (!(r >= 0.0 && r < 1.0)) return fail(POP_ERR_INVALID_ARGUMENT, "r=%g outside [0, 1)", r);
-  if ((s = check_lists(d_ff, R, n_R, C, n_C, false)) != POP_OK) return s;
-  if ((batch > 0 && (x == nullptr || y == nullptr)) || W_gate == nullptr || W_up == nullptr || W_downT == nullptr ||
-      ws == nullptr)
-    return fail(POP_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
-  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_downT) || !aligned16(y) ||
-      !aligned16(ws))
-    return fail(POP_ERR_MISALIGNED, "x, weights, y and ws must be 16-byte aligned");
-  const size_t need = pop_decode_workspace_bytes(batch, d, d_ff);
-  if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
-  if (batch != 1)  // only the batch-1 pipeline has a candidate chain to overlap
-    return pop_decode_ffn(x, batch, d, W_gate, W_up, W_downT, d_ff, dt, R, n_R, C, n_C, r, y, selected, ws,
-                          ws_bytes, stream);
-  const int32_t k = topk_count(d_ff, r, n_R, n_C);
-  DecodeWs w;
-  decode_ws_layout(batch, d, d_ff, (char*)ws, &w);
-  const int32_t* Rk = R != nullptr ? R : w.Q;
-  const int32_t* Ck = C != nullptr ? C : w.Q;
-  hipStream_t st = (hipStream_t)stream;
-  DecodeWs wf = w;
-  if (selected != nullptr) wf.sel = selected;
-  trace_mark(st);
-  if (n_R + n_C > 0 && POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, Rk, n_R, Ck, n_C, k, y,
-                                    wf, (hipStream_t)aux_stream, (hipEvent_t)fork_event, (hipEvent_t)join_event))
-    return launched();
-  return pop_decode_ffn(x, batch, d, W_gate, W_up, W_downT, d_ff, dt, R, n_R, C, n_C, r, y, selected, ws, ws_bytes,
-                        stream);
 }
 
 extern "C" pop_status pop_dense_ffn_decode(const void* x, int32_t batch, int32_t d, const void* W_gate,
@@ -1242,7 +1537,9 @@ extern "C" pop_status pop_dense_ffn_decode(const void* x, int32_t batch, int32_t
   hipStream_t st = (hipStream_t)stream;
   trace_mark(st);
   if (batch == 1 &&
-      POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, nullptr, d_ff, nullptr, 0, 0, y, w))
+      ((POP_LINKED_ON && POP_DISPATCH(dt, launch_linked, st, x, d, W_gate, W_up, W_downT, d_ff, nullptr, d_ff,
+                                      nullptr, 0, 0, y, w, nullptr, false)) ||
+       POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, nullptr, d_ff, nullptr, 0, 0, y, w)))
     return launched();
   POP_DISPATCH(dt, launch_gateup, st, x, batch, d, W_gate, W_up, d_ff, nullptr, d_ff, nullptr, 0, w.z, nullptr);
   POP_DISPATCH(dt, launch_down, st, w.z, batch, d_ff, W_downT, d, d_ff, nullptr, d_ff, nullptr, nullptr, 0, y,

@@ -30,6 +30,51 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// ---- data handed between workgroups of one launch
+// Agent-scope relaxed atomics: every access below goes to the device's
+// coherence point, so a value one workgroup stores is the value another
+// workgroup loads, whichever XCD (and L2) each runs on.  No release or acquire
+// fence is used (a device-scope release writes back the whole L2 of the XCD and
+// costs microseconds per workgroup); ordering between locations comes from
+// mem_wait() below, or from a valid bit carried in the same 64-bit word as the
+// data it guards.
+__device__ __forceinline__ void st_coh(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_coh(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_coh(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_coh(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until every memory operation this wave issued has completed (its
+// coherent stores have reached the coherence point).  The signal fences keep
+// the compiler from moving memory operations across the wait.
+__device__ __forceinline__ void mem_wait() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Polls *p (coherent) until pred(value) holds, at most `limit` times, sleeping
+// briefly between polls; returns the last value read and sets ok.
+template <typename T, typename Pred>
+__device__ __forceinline__ T poll_coh(const T* p, Pred pred, int limit, bool& ok) {
+  T v = ld_coh(p);
+  int n = 0;
+  while (!pred(v) && ++n < limit) {
+    __builtin_amdgcn_s_sleep(2);
+    v = ld_coh(p);
+  }
+  ok = pred(v);
+  return v;
+}
+
 __device__ __forceinline__ void unpack(const u32x4 v, float (&f)[8], bf16s) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -112,6 +157,10 @@ struct SelTarget {
   int beyond;       // rank >= n: every element is below
 };
 
+// A bucket of at most kSelResolve keys is resolved directly (every key of the
+// bucket ranks itself against the others) instead of by further radix passes.
+constexpr int kSelResolve = 64;
+
 template <int NTH, int MAXN = kSelMaxN>
 struct SelShared {
   static constexpr int kPerThread = (MAXN + NTH - 1) / NTH;
@@ -120,6 +169,9 @@ struct SelShared {
   SelTarget tgt[2];
   uint32_t red[NTH / 64][2];
   int scan[NTH / 64][3];
+  uint32_t rv[kSelResolve];  // a small bucket's values and indices
+  int ri[kSelResolve];
+  int rcnt;
 };
 
 // DPP move within a wave; lanes whose source is outside the row, and rows
@@ -328,6 +380,59 @@ __device__ void select_targets(const uint32_t (&v)[EM], int n, int base, int E, 
 #pragma unroll
     for (int i = 0; i < NT; ++i)
       if (!t[i].beyond && t[i].shift > 0) t[i] = sh.tgt[i];
+    // ---- small buckets: the key of rank t.rank inside the bucket, directly.
+    // Ascending order (least important first): smaller value first, and on
+    // equal values the larger index first.  The target's value v, its
+    // multiplicity m (every key of value v lies in the bucket) and q = the
+    // keys of value v below the target rank complete the target as the last
+    // radix pass would.  Only when every open target's bucket is small: the
+    // passes above move all open targets in step (one shift, one histogram
+    // section per target).
+    bool small = true;
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      if (!t[i].beyond && t[i].shift > 0) small &= t[i].count <= kSelResolve;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      if (!small || t[i].beyond || t[i].shift == 0) continue;  // block-uniform
+      if (tid == 0) sh.rcnt = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < EM; ++j) {
+        if (j >= E) break;  // block-uniform
+        if (j < cnt && (v[j] >> t[i].shift) == (t[i].prefix >> t[i].shift)) {
+          const int slot = atomicAdd(&sh.rcnt, 1);
+          if (slot < kSelResolve) {
+            sh.rv[slot] = v[j];
+            sh.ri[slot] = base + j;
+          }
+        }
+      }
+      __syncthreads();
+      const int mb = t[i].count;  // == sh.rcnt
+      if (tid < mb) {
+        const uint32_t vv = sh.rv[tid];
+        const int ii = sh.ri[tid];
+        int below = 0, lt = 0, eqn = 0;
+        for (int e = 0; e < mb; ++e) {
+          const uint32_t ve = sh.rv[e];
+          lt += ve < vv ? 1 : 0;
+          eqn += ve == vv ? 1 : 0;
+          below += (ve < vv || (ve == vv && sh.ri[e] > ii)) ? 1 : 0;
+        }
+        if (below == t[i].rank) {
+          SelTarget u;
+          u.prefix = vv;
+          u.shift = 0;
+          u.rank = t[i].rank - lt;
+          u.count = eqn;
+          u.beyond = 0;
+          sh.tgt[i] = u;
+        }
+      }
+      __syncthreads();
+      t[i] = sh.tgt[i];
+    }
   }
   __syncthreads();  // sh.tgt and the histograms may be reused after this
 }
@@ -449,6 +554,125 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ score, int 
   }
 }
 
+// ---------------------------------------------------------------- linked top-k
+// A packed 64-bit hand-over word: high half = tag | 0x80000000 (the valid
+// bit), low half = payload bits; 0 means "not written yet".
+__device__ __forceinline__ uint64_t pack_valid(uint32_t tag, uint32_t payload) {
+  return ((uint64_t)(tag | 0x80000000u) << 32) | payload;
+}
+__device__ __forceinline__ bool is_valid(uint64_t w) { return (w >> 63) != 0; }
+
+// The candidate top-k of the single-launch batch-1 step, where the scores come
+// from other workgroups of the same launch.  It waits (thread 0 polling, at
+// most poll_limit rounds) until *c_done reaches n_writers, the number of
+// workgroups that publish candidate words, each having counted itself once
+// its words were complete; it then reads candidate i's word cand[i] =
+// pack_valid(bits of |z_i|, bits of z_i) and selects exactly as topk_block
+// does.  It publishes the cut rather than a list: candidate position p with
+// score bits x is selected iff
+//     x > v,  or  x == v and p <= tie_pos,
+// the pair written as pack_valid(v, tie_pos) into the n_copies words
+// thr[0], thr[stride], ... (coherent; each reader polls one copy, so no
+// single line is polled by every workgroup).  Then, when not NULL, it writes
+// positions (ascending, into C) and selected (channels C[p]) of the k
+// selected candidates with plain stores.  A round limit reached, or a word
+// found without its valid bit, sets *err (coherent); the step goes on with
+// score 0 for such candidates.
+template <int NTH, int MAXN>
+__device__ void topk_threshold_linked(const uint64_t* __restrict__ cand, int n, int k, const uint32_t* c_done,
+                                      int n_writers, const int32_t* __restrict__ C, int32_t* __restrict__ positions,
+                                      int32_t* __restrict__ selected, uint64_t* __restrict__ thr, int n_copies,
+                                      int stride, SelShared<NTH, MAXN>& sh, int poll_limit, uint32_t* err) {
+  constexpr int EM = SelShared<NTH, MAXN>::kPerThread;
+  static_assert(sel_slot(MAXN - 1) < kSelSlots, "keys handed over through the histogram buffers");
+  if (n <= 0 || k <= 0) return;
+  k = min(k, n);
+  const int E = (n + NTH - 1) / NTH;
+  const int base = threadIdx.x * E;
+  const int cnt = max(0, min(E, n - base));
+  if (threadIdx.x == 0) {
+    bool ok;
+    poll_coh(c_done, [n_writers](uint32_t v) { return v >= (uint32_t)n_writers; }, poll_limit, ok);
+    if (!ok) st_coh(err, 1u);
+  }
+  __syncthreads();
+  // ---- every candidate word, coalesced (element tid + j * NTH), then handed to its owner
+  uint64_t w[EM];
+  int c[EM];
+#pragma unroll
+  for (int j = 0; j < EM; ++j) {
+    const int i = min((int)threadIdx.x + j * NTH, n - 1);
+    w[j] = ld_coh(&cand[i]);
+    c[j] = C[i];
+  }
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < EM; ++j) {
+    const int i = (int)threadIdx.x + j * NTH;
+    if (i < n) {
+      bad |= !is_valid(w[j]);
+      sh.hA[sel_slot(i)] = is_valid(w[j]) ? (uint32_t)(w[j] >> 32) & 0x7fffffffu : 0u;
+      sh.hB[sel_slot(i)] = (unsigned int)c[j];
+    }
+  }
+  if (bad) st_coh(err, 3u);
+  __syncthreads();
+  uint32_t v[EM];
+  int cv[EM];
+#pragma unroll
+  for (int j = 0; j < EM; ++j) {
+    const int i = min(base + j, n - 1);
+    v[j] = sh.hA[sel_slot(i)];
+    cv[j] = (int)sh.hB[sel_slot(i)];
+  }
+  __syncthreads();  // the select clears the buffers next
+  const int ranks[1] = {n - k};
+  SelTarget t[1];
+  select_targets<NTH, 1, EM, MAXN>(v, n, base, E, ranks, sh, t);
+  int eqb[2];
+  sel_eq_before<NTH, 1, EM, MAXN>(v, E, cnt, t, sh, eqb);
+  // ---- the cut: the selected elements of value v are the (m - q) of lowest position
+  const int m = t[0].count, q = t[0].rank;
+  if (threadIdx.x == 0) sh.scan[0][0] = q == 0 ? n : -1;  // all, or none, of value v
+  __syncthreads();
+  if (q > 0 && q < m) {
+    int eq = eqb[0];
+#pragma unroll
+    for (int j = 0; j < EM; ++j) {
+      if (j >= E) break;  // block-uniform
+      if (j < cnt && v[j] == t[0].prefix) {
+        ++eq;
+        if (eq == m - q) sh.scan[0][0] = base + j;
+      }
+    }
+  }
+  __syncthreads();
+  const int tie_pos = sh.scan[0][0];
+  if ((int)threadIdx.x < n_copies) st_coh(&thr[threadIdx.x * stride], pack_valid(t[0].prefix, (uint32_t)tie_pos));
+  if (positions == nullptr && selected == nullptr) return;
+  // ---- the list, ascending (after the cut is out)
+  int pos[3] = {0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < EM; ++j) {
+    if (j >= E) break;  // block-uniform
+    const bool s = j < cnt && (v[j] > t[0].prefix || (v[j] == t[0].prefix && base + j <= tie_pos));
+    pos[0] += s ? 1 : 0;
+  }
+  int tot[3];
+  __syncthreads();  // sh.scan is reused by the scan
+  block_exclusive_scan3(pos, tot, sh);
+#pragma unroll
+  for (int j = 0; j < EM; ++j) {
+    if (j >= E) break;  // block-uniform
+    if (j < cnt && (v[j] > t[0].prefix || (v[j] == t[0].prefix && base + j <= tie_pos))) {
+      if (pos[0] < k) {
+        if (positions != nullptr) positions[pos[0]] = base + j;
+        if (selected != nullptr) selected[pos[0]] = cv[j];
+      }
+      ++pos[0];
+    }
+  }
+}
 
 // ---------------------------------------------------------------- fixed-order chunk sum
 // out[i] = sum_{c < n_chunks} partial[c * n_out + i].  A block of 1024 threads

@@ -71,9 +71,6 @@ def _load():
         "pop_decode_select": (ctypes.c_int, [_c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp]),
         "pop_decode_down_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32]),
         "pop_set_trace_events": (ctypes.c_int, [ctypes.POINTER(_c_vp), _c_i32]),
-        "pop_decode_ffn_2s": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
-                                             _c_vp, _c_i32, _c_vp, _c_i32, _c_dbl, _c_vp, _c_vp, _c_vp, _c_size,
-                                             _c_vp, _c_vp, _c_vp, _c_vp]),
         "pop_trace_recorded": (_c_i32, []),
         "pop_dense_ffn_prefill_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32, ctypes.c_int]),
         "pop_moe_route_top2": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
@@ -114,6 +111,17 @@ def _load():
 
 
 lib = _load()
+
+
+def _header_define(name: str) -> int:
+    m = re.search(rf"^#define {name} (\d+)", open(HEADER).read(), re.M)
+    if m is None:
+        raise ImportError(f"{name} is not defined in {HEADER}")
+    return int(m.group(1))
+
+
+# Byte offset of z in a decode workspace (the bytes before it are control words).
+DECODE_WS_Z_OFFSET = _header_define("POP_DECODE_WS_Z_OFFSET")
 
 
 def declared_functions() -> list[str]:
@@ -256,40 +264,6 @@ def pop_decode_ffn_periodic(x, W_gate, W_up, W_downT, R, C, r: float, step: int,
         _ptr(state.positions), _ptr(state.selected), _ptr(state.rows), _ptr(y), _ptr(ws), ws.numel(),
         _stream(stream)))
     return y
-
-
-class TwoStream:
-    """An auxiliary stream and the fork/join events pop_decode_ffn_2s needs
-    (created once; reusable across calls and graph captures)."""
-
-    def __init__(self, device=None):
-        self.aux = torch.cuda.Stream(device=device)
-        self.fork = torch.cuda.Event()
-        self.join = torch.cuda.Event()
-        # torch creates the underlying events lazily: record once so they exist
-        self.fork.record()
-        self.join.record()
-        torch.cuda.synchronize()
-
-
-def pop_decode_ffn_2s(x, W_gate, W_up, W_downT, R, C, r: float, two: TwoStream, *, y=None, selected: bool = False,
-                      ws=None, stream=None):
-    """pop_decode_ffn with the candidate chain on two.aux (same result)."""
-    _dev(x, W_gate, W_up, W_downT, R, C)
-    batch, d = x.shape
-    d_ff = W_gate.shape[0]
-    dev = W_gate.device
-    if y is None:
-        y = torch.empty((batch, d), dtype=torch.float32, device=dev)
-    S = torch.empty(_k(d_ff, r, R.numel(), C.numel()), dtype=torch.int32, device=dev) if selected else None
-    if ws is None:
-        ws = workspace(pop_decode_workspace_bytes(batch, d, d_ff), dev)
-    _check("pop_decode_ffn_2s", lib.pop_decode_ffn_2s(
-        _ptr(x), batch, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
-        _ptr(R), R.numel(), _ptr(C), C.numel(), float(r), _ptr(y), _ptr(S), _ptr(ws), ws.numel(),
-        _stream(stream), ctypes.c_void_p(two.aux.cuda_stream), ctypes.c_void_p(two.fork.cuda_event),
-        ctypes.c_void_p(two.join.cuda_event)))
-    return (y, S) if selected else y
 
 
 def _k(d_ff, r, n_R, n_C):

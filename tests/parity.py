@@ -19,8 +19,10 @@ import numpy as np
 import torch
 
 import oracle
+from online_structured_ffn_amd import pop
 
 TIE_REL = 1e-4
+Z_OFFSET = pop.DECODE_WS_Z_OFFSET
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 # Device importance / scores against fp64: fp32 sums of non-negative terms
 # (chunked, depth well under 200 additions) stay within 200 * 2^-24 ~ 1.2e-5;
@@ -85,9 +87,13 @@ def check_decode(y, S, ws, x, w, R, C, r, dtype, z_ref=None):
     assert len(S) == k
     ref = oracle.decode_step(x, w["W_gate"], w["W_up"], w["W_down"], R, C, r)
     n_A = n_R + n_C
-    wsf = host(ws).view(np.float32)[64:]          # z starts at byte 256
+    raw = host(ws)
+    # the first POP_DECODE_WS_Z_OFFSET bytes are control words, zero after every completed call
+    ctl = raw[:Z_OFFSET].view(np.uint32)
+    assert not ctl.any(), f"decode control words not zero after the call: {np.flatnonzero(ctl)}"
+    wsf = raw.view(np.float32)[Z_OFFSET // 4:]    # z starts at byte POP_DECODE_WS_Z_OFFSET
     z_dev = wsf[: B * n_A].reshape(B, n_A).astype(np.float64)
-    zb = (B * d_ff * 4 + 16 + 255) // 256 * 256 // 4   # scores: 256 + align_up(4*B*d_ff + 16, 256) bytes
+    zb = (B * d_ff * 4 + 16 + 255) // 256 * 256 // 4   # scores: Z_OFFSET + align_up(4*B*d_ff + 16, 256) bytes
     sc_dev = wsf[zb: zb + n_C].astype(np.float64)
     # intermediate and scores
     zr = ref["z"]

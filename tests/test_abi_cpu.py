@@ -61,8 +61,10 @@ def test_workspace_sizes():
     assert pop.pop_prefill_workspace_bytes(-1, 256, 688) == 0
     a = pop.pop_decode_workspace_bytes(1, 4096, 11008)
     b = pop.pop_decode_workspace_bytes(16, 4096, 11008)
-    # z and the candidate scores are always there
-    assert a >= 256 + 4 * 11008 * 2 and b >= 256 + 4 * 16 * 11008 + 4 * 11008
+    # control and hand-over words, then z and the candidate scores
+    Z = pop.DECODE_WS_Z_OFFSET
+    assert Z % 256 == 0 and Z >= 1024 + 2 * 4096 * 8
+    assert a >= Z + 4 * 11008 * 2 and b >= Z + 4 * 16 * 11008 + 4 * 11008
     assert pop.pop_decode_workspace_bytes(0, 4096, 11008) > 0
 
 

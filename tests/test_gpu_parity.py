@@ -358,36 +358,43 @@ def test_partition_select_stage_exact(n, kind):
 
 
 @pytest.mark.parametrize("d,d_ff,r", [(4096, 11008, 0.299), (3584, 18944, 0.5), (1032, 2900, 0.3)])
-def test_decode_two_streams_bitwise(d, d_ff, r):
-    """pop_decode_ffn_2s gives the bits of pop_decode_ffn, eager and as a
-    captured graph replayed several times with other eager work between."""
-    say(f"[decode 2s] d={d} d_ff={d_ff} r={r}")
+def test_decode_b1_single_launch_bitwise(d, d_ff, r):
+    """The single-launch batch-1 step: the same bits on every call, eager and
+    as a captured graph replayed several times with other eager work (on
+    another workspace) between replays; one workspace serving batch-1 steps
+    and a batch-16 step in turn; the control words zero after every call."""
+    say(f"[decode b1 single launch] d={d} d_ff={d_ff} r={r}")
     c = synth.random_case(91 + d, 32, d, d_ff, 1, "bf16")
     Xd = dev(c["X"], "bf16")
     Wg, Wu, WdT = dev(c["W_gate"], "bf16"), dev(c["W_up"], "bf16"), dev(c["W_downT"], "bf16")
     R, C, P = pop.pop_prefill_partition(Xd, Wu, r, 0.1)
-    two = pop.TwoStream()
-    ws1 = pop.workspace(pop.pop_decode_workspace_bytes(1, d, d_ff))
+    ws1 = pop.workspace(pop.pop_decode_workspace_bytes(16, d, d_ff))
     ws2 = pop.workspace(pop.pop_decode_workspace_bytes(1, d, d_ff))
+    Z = pop.DECODE_WS_Z_OFFSET
+    ctl_zero = lambda ws: not host(ws[:Z]).any()
     xs = [dev(synth.random_case(95 + t, 1, d, 1, 1, "bf16")["x"], "bf16") for t in range(3)]
-    ref = []
+    x16 = dev(synth.random_case(99, 1, d, 1, 16, "bf16")["x"], "bf16")
+    ref, refS = [], []
     for xt in xs:
         y1, S1 = pop.pop_decode_ffn(xt, Wg, Wu, WdT, R, C, r, selected=True, ws=ws1)
-        y2, S2 = pop.pop_decode_ffn_2s(xt, Wg, Wu, WdT, R, C, r, two, selected=True, ws=ws2)
+        y16 = pop.pop_decode_ffn(x16, Wg, Wu, WdT, R, C, r, ws=ws1)    # same workspace, batch 16
+        y2, S2 = pop.pop_decode_ffn(xt, Wg, Wu, WdT, R, C, r, selected=True, ws=ws2)
         torch.cuda.synchronize()
         assert torch.equal(y1, y2) and torch.equal(S1, S2)
+        assert ctl_zero(ws1) and ctl_zero(ws2)
         ref.append(y1)
+        refS.append(S1)
     x_in = xs[0].clone()
     yg = torch.empty_like(ref[0])
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        pop.pop_decode_ffn_2s(x_in, Wg, Wu, WdT, R, C, r, two, y=yg, ws=ws2)
+        pop.pop_decode_ffn(x_in, Wg, Wu, WdT, R, C, r, y=yg, ws=ws2)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        pop.pop_decode_ffn_2s(x_in, Wg, Wu, WdT, R, C, r, two, y=yg, ws=ws2)
+        pop.pop_decode_ffn(x_in, Wg, Wu, WdT, R, C, r, y=yg, ws=ws2)
     for rep in range(6):
         t = rep % 3
         x_in.copy_(xs[t])
@@ -395,3 +402,4 @@ def test_decode_two_streams_bitwise(d, d_ff, r):
         pop.pop_decode_ffn(xs[(t + 1) % 3], Wg, Wu, WdT, R, C, r, ws=ws1)  # other eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(yg, ref[t]), f"replay {rep} differs"
+        assert ctl_zero(ws1) and ctl_zero(ws2)
