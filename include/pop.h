@@ -187,17 +187,21 @@ size_t pop_decode_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff);
  *              (fp32 [batch, n_R + n_C], R columns first, then C) and byte
  *              offset POP_DECODE_WS_Z_OFFSET + align_up(4 * batch * d_ff + 16,
  *              256) the candidate scores (fp32 [n_C]).
- * Kernels at batch 1 (d <= 1024 vectors of 16 bytes, n_C <= 4096): ONE launch.
- * Its first workgroup is the candidate top-k; every other workgroup streams
- * an even share of the candidates' gate/up rows (handing each |z| to the
- * top-k through a valid-tagged word), then of the retained channels' gate, up
- * and W_downT rows (z and its down contribution in one pass), then adds the
- * selected rows the top-k hands back; the last workgroups to finish add the
- * per-workgroup partial sums, in a fixed order, into y.  The grid never
- * exceeds what the device holds at once, and every in-kernel wait is bounded
- * (see POP_DECODE_WS_Z_OFFSET for the error word).  Other batch-1 shapes:
- * three launches (candidate rows; the top-k beside the retained stream; the
- * selected rows and the fixed-order sum).
+ * Kernels at batch 1 with a candidate top-k (n_C >= 1, k >= 1, n_C <= 4096,
+ * d <= 1024 vectors of 16 bytes): two launches.  In the first, workgroup 0 is
+ * the candidate top-k and every other workgroup (a worker) streams an even
+ * share of the candidates' gate/up rows (handing each |z| to the top-k through
+ * a valid-tagged word), then of the retained channels' gate, up and W_downT
+ * rows (z and its down contribution in one pass); the top-k publishes the cut
+ * and each worker adds the W_downT rows of its own candidates that the cut
+ * selects (their loads issued with its last retained rows), then stores its
+ * partial y.  The second adds the partials in a fixed order into y and clears
+ * the hand-over words.  The grid never exceeds what the device holds at once
+ * and every in-kernel wait is bounded (see POP_DECODE_WS_Z_OFFSET for the
+ * error word).  Batch 1 without a top-k (no candidates, k = 0): the retained
+ * rows' gate, up and W_downT rows in one stream, then the fixed-order sum.
+ * Other batch-1 shapes: three launches (candidate rows; the one-workgroup
+ * top-k beside the retained stream; the selected rows and the sum).
  * Batches 2-64 in bf16: the matrix-core kernels (16-token tiles): gate/up
  * over R u C with fused SiLU*up and the batch-max score; the down-projection
  * over the retained rows with the candidate top-k as one of its workgroups;

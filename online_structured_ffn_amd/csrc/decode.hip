@@ -385,6 +385,101 @@ __device__ __forceinline__ void cand_rows(const int* rows, int nrows, const T* _
   __syncthreads();  // part is reused by the next batch
 }
 
+// The end of a worker's stream in one round trip: up to NR retained rows
+// (gate, up and W_downT rows) and up to NS selected candidate rows (W_downT
+// rows, z given) with every load issued before any is used.  The retained
+// rows' z (written by thread 0 to zout) and then the selected rows' z
+// multiply their W_downT rows into acc, in that fixed order.  Unused slots
+// load a clamped channel (the lists' entries there may hold anything) and
+// add nothing.
+template <typename T, int NV, int NR, int NS>
+__device__ __forceinline__ void tail_rows(const int* rrows, int nrr, const int* schan, const float* sz, int nss,
+                                          const T* __restrict__ Wg, const T* __restrict__ Wu,
+                                          const T* __restrict__ WdT, int d, int d_ff, const u32x4 (&xv)[NV],
+                                          float (&part)[kFusedWaves][2 * NR], float (&acc)[NV][Vec<T>::N],
+                                          float* __restrict__ zout) {
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  u32x4 g[NR][NV], u[NR][NV], wr[NR][NV], wsel[NS][NV];
+#pragma unroll
+  for (int p = 0; p < NR; ++p) {
+    const int64_t base = (int64_t)clamp_channel(rrows[min(p, max(nrr - 1, 0))], d_ff) * d;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int col = min(j * kFusedThreads * V + (int)threadIdx.x * V, d - V);
+      g[p][j] = ld16_stream(Wg + base + col);
+      u[p][j] = ld16_stream(Wu + base + col);
+      wr[p][j] = ld16_stream(WdT + base + col);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    const int64_t base = (int64_t)clamp_channel(schan[min(q, max(nss - 1, 0))], d_ff) * d;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int col = min(j * kFusedThreads * V + (int)threadIdx.x * V, d - V);
+      wsel[q][j] = ld16_stream(WdT + base + col);
+    }
+  }
+  float zr[NR];
+#pragma unroll
+  for (int p = 0; p < NR; ++p) {
+    float pg = 0.f, pu = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float gf[V], uf[V], xx[V];
+      unpack(g[p][j], gf, T{});
+      unpack(u[p][j], uf, T{});
+      unpack(xv[j], xx, T{});
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        pg = fmaf(gf[v], xx[v], pg);
+        pu = fmaf(uf[v], xx[v], pu);
+      }
+    }
+    pg = wave_sum_last(pg);
+    pu = wave_sum_last(pu);
+    if (lane == 63) {
+      part[wave][2 * p] = pg;
+      part[wave][2 * p + 1] = pu;
+    }
+  }
+  if (NR > 0) __syncthreads();
+#pragma unroll
+  for (int p = 0; p < NR; ++p) {
+    float gs = part[0][2 * p], us = part[0][2 * p + 1];
+#pragma unroll
+    for (int w = 1; w < kFusedWaves; ++w) {
+      gs += part[w][2 * p];
+      us += part[w][2 * p + 1];
+    }
+    zr[p] = p < nrr ? silu(gs) * us : 0.f;
+    if (threadIdx.x == 0 && p < nrr) zout[p] = zr[p];
+  }
+#pragma unroll
+  for (int p = 0; p < NR; ++p)
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float f[V];
+      unpack(wr[p][j], f, T{});
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[j][v] = fmaf(zr[p], f[v], acc[j][v]);
+    }
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    const float zz = q < nss ? sz[q] : 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float f[V];
+      unpack(wsel[q][j], f, T{});
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[j][v] = fmaf(zz, f[v], acc[j][v]);
+    }
+  }
+  __syncthreads();  // part and the caller's row lists are reused next
+}
+
 // Loads this thread's x vectors and clears its down accumulators.
 template <typename T, int NV>
 __device__ __forceinline__ void fused_setup(const T* __restrict__ x, int d, u32x4 (&xv)[NV],
@@ -482,11 +577,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
 // flight at once.  The per-lane sums are reduced across lanes (shuffles), then
 // across waves in wave order (LDS).
 constexpr int kFinThreads = 1024;
-// Control words of the single-launch batch-1 step (32-bit, 128 bytes apart):
-// the sticky error word, then counters that k_pop_finish clears for the next
-// call (words kCtlFirstCounter .. kCtlFirstCounter + kCtlResetWords - 1).
-constexpr int kCtlErr = 0, kCtlCdone = 32;
-constexpr int kCtlFirstCounter = 32, kCtlResetWords = 224;
+// Control word of the single-launch batch-1 step: the sticky error word.
+constexpr int kCtlErr = 0;
 constexpr int kFinRowsPerBatch = 1280;  // selected rows whose loads are in flight together
 constexpr int kFinPartials = 512;       // partial rows whose loads are in flight together
 
@@ -508,8 +600,7 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
                                                             const int32_t* __restrict__ pos, int k,
                                                             const T* __restrict__ WdT, int d, int d_ff,
                                                             float* __restrict__ y, int accumulate,
-                                                            uint32_t* reset_word, uint64_t* reset_words,
-                                                            int n_reset_words) {
+                                                            uint64_t* reset_words, int n_reset_words) {
   constexpr int V = Vec<T>::N;
   constexpr int LR = kFinCols / V;       // lanes per W_downT row
   constexpr int RPW = 64 / LR;           // W_downT rows per wave instruction
@@ -520,8 +611,7 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
   constexpr int PB = (kFinPartials + PPB - 1) / PPB;           // partial-row loads in flight per lane
   constexpr int SB = (kFinRowsPerBatch + RPB - 1) / RPB;       // selected-row loads in flight per lane
   __shared__ float red[kFinThreads / 64][kFinCols];
-  // the single-launch step's counter and hand-over words, cleared for the next call
-  if (reset_word != nullptr && blockIdx.x == 0 && threadIdx.x < kCtlResetWords) st_coh(reset_word + threadIdx.x, 0u);
+  // the single-launch step's hand-over words, cleared for the next call
   for (int i = blockIdx.x * kFinThreads + threadIdx.x; i < n_reset_words; i += gridDim.x * kFinThreads)
     st_coh(&reset_words[i], (uint64_t)0);
   const int lane = threadIdx.x & 63;
@@ -661,7 +751,8 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
 constexpr int kLinkedTopkMaxN = 4096;
 constexpr int kLinkedMaxWorkers = POP_FUSED_RBLOCKS - 1;
 constexpr int kPollLimit = 1 << 20;
-constexpr int kSelRowsPerPass = 8;
+constexpr int kSelRowsPerPass = 4;  // selected rows per tail pass
+constexpr int kTailR = 2;           // retained rows kept for the tail pass
 constexpr int kThrCopies = 32;  // copies of the published cut
 constexpr int kThrStride = 16;  // 64-bit words between copies (128 bytes)
 constexpr int kCandBatch = 8;  // candidate rows whose loads a worker issues together
@@ -689,10 +780,10 @@ __global__ __launch_bounds__(kFusedThreads, 2) void k_pop_linked(
     float part[2][kFusedWaves][2 * kFusedP];
     float cpart[kFusedWaves][2 * kCandBatch];
     int crow[kFusedMaxRows];  // this worker's share of C (channels)
-    int s_ch[kSelRowsPerPass];
-    float s_z[kSelRowsPerPass];
+    float tpart[kFusedWaves][2 * kTailR];
     int n_sel;
-    int sel_rows[kFusedMaxRows];  // this worker's selected candidates (indices into its rows)
+    int s_chan[kFusedMaxRows];  // this worker's selected candidates: channel and z
+    float s_zv[kFusedMaxRows];
     uint64_t cut;
   };
   __shared__ union {
@@ -705,8 +796,8 @@ __global__ __launch_bounds__(kFusedThreads, 2) void k_pop_linked(
   uint64_t* thr = hand + kLinkedTopkMaxN;
   if (blockIdx.x == 0) {
     if (chain)
-      topk_threshold_linked(cand, n_C, k, ctl + kCtlCdone, n_C, C, (int32_t*)nullptr, sel_out, thr, kThrCopies,
-                            kThrStride, sh.sel, kPollLimit, ctl + kCtlErr);
+      topk_threshold_linked(cand, n_C, k, C, (int32_t*)nullptr, sel_out, thr, kThrCopies, kThrStride, sh.sel,
+                            kPollLimit, ctl + kCtlErr);
     return;
   }
   const int w = blockIdx.x - 1;
@@ -722,17 +813,15 @@ __global__ __launch_bounds__(kFusedThreads, 2) void k_pop_linked(
   for (int i0 = 0; i0 < nc; i0 += kCandBatch)
     cand_rows<T, NV, kCandBatch>(sh.w.crow + i0, min(kCandBatch, nc - i0), Wg, Wu, d, xv, sh.w.cpart,
                                  z + n_R + c0 + i0, score + c0 + i0, chain ? cand + c0 + i0 : nullptr);
-  if (chain && tid < kCandBatch) {
-    mem_wait();  // this wave's candidate words are out (no load is in flight here)
-    if (tid == 0 && nc > 0) add_coh(ctl + kCtlCdone, (uint32_t)nc);
-  }
+  // 2. retained rows but the last kTailR (when this worker may have selected candidates)
+  const bool sel_here = chain && nc > 0;
+  const int nr_head = sel_here ? max(0, nr - kTailR) : nr;
+  fused_rows<T, NV, true>(sh.w.rows, nr_head, Wg, Wu, WdT, d, xv, sh.w.part, acc, z, r0, nullptr);
   __syncthreads();
-  // 2. retained rows
-  fused_rows<T, NV, true>(sh.w.rows, nr, Wg, Wu, WdT, d, xv, sh.w.part, acc, z, r0, nullptr);
-  __syncthreads();
-  // 3. this worker's candidates that the cut selects
-  //    (its static share of C: positions c0 .. c0 + nc - 1, z from their hand-over words)
-  if (chain && nc > 0) {
+  // 3. the cut, and this worker's candidates that it selects (its static share
+  //    of C: positions c0 .. c0 + nc - 1, z from their hand-over words)
+  int ns = 0;
+  if (sel_here) {
     // the words are read beside the poll; one read before every word was
     // written lacks its valid bit and is read again once the cut is out (the
     // cut is published only after every word was seen valid)
@@ -752,47 +841,25 @@ __global__ __launch_bounds__(kFusedThreads, 2) void k_pop_linked(
       const uint64_t e = sh.w.cut;
       const uint32_t cv = (uint32_t)(e >> 32) & 0x7fffffffu;
       const int tie = (int)(uint32_t)e;
-      int ns = 0;
+      int m = 0;
       for (int i = 0; i < nc; ++i) {
         const uint32_t xb = (uint32_t)(sh.w.cw[i] >> 32) & 0x7fffffffu;  // bits of |z|
-        if (is_valid(e) && (xb > cv || (xb == cv && c0 + i <= tie))) sh.w.sel_rows[ns++] = i;
+        if (is_valid(e) && (xb > cv || (xb == cv && c0 + i <= tie))) {
+          sh.w.s_chan[m] = sh.w.crow[i];
+          sh.w.s_zv[m] = __uint_as_float((uint32_t)sh.w.cw[i]);
+          ++m;
+        }
       }
-      sh.w.n_sel = ns;
+      sh.w.n_sel = m;
     }
     __syncthreads();
-    const int ns = sh.w.n_sel;
-    for (int j0 = 0; j0 < ns; j0 += kSelRowsPerPass) {
-      const int nb = min(kSelRowsPerPass, ns - j0);
-      if (tid < nb) {
-        const int i = sh.w.sel_rows[j0 + tid];
-        sh.w.s_ch[tid] = sh.w.crow[i];
-        sh.w.s_z[tid] = __uint_as_float((uint32_t)sh.w.cw[i]);
-      }
-      __syncthreads();
-      u32x4 wv[kSelRowsPerPass][NV];
-#pragma unroll
-      for (int p = 0; p < kSelRowsPerPass; ++p) {
-        const int ch = sh.w.s_ch[min(p, nb - 1)];
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const int col = min(j * kFusedThreads * V + tid * V, d - V);
-          wv[p][j] = ld16_stream(WdT + (int64_t)ch * d + col);
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < kSelRowsPerPass; ++p) {
-        const float zz = p < nb ? sh.w.s_z[p] : 0.f;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          float f[V];
-          unpack(wv[p][j], f, T{});
-#pragma unroll
-          for (int v = 0; v < V; ++v) acc[j][v] = fmaf(zz, f[v], acc[j][v]);
-        }
-      }
-      __syncthreads();
-    }
+    ns = sh.w.n_sel;
   }
+  //    then the last retained rows and the selected rows, their loads together
+  for (int t0 = 0, s0 = 0; nr_head + t0 < nr || s0 < ns; t0 += kTailR, s0 += kSelRowsPerPass)
+    tail_rows<T, NV, kTailR, kSelRowsPerPass>(sh.w.rows + nr_head + t0, max(0, min(kTailR, nr - nr_head - t0)),
+                                              sh.w.s_chan + s0, sh.w.s_zv + s0, max(0, min(kSelRowsPerPass, ns - s0)),
+                                              Wg, Wu, WdT, d, d_ff, xv, sh.w.tpart, acc, z + r0 + nr_head + t0);
   // 4. partial y, slice-major: column c of worker w at ((c / kFinCols) * nW + w) * kFinCols + c % kFinCols
   static_assert(kFinCols % V == 0, "a thread's columns lie in one slice");
 #pragma unroll
@@ -1248,11 +1315,11 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
   if (k > 0) {
     POP_LAUNCH((k_pop_finish<T, true>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
                (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, k, (const T*)WdT, d,
-               d_ff, y, (int)accumulate, (uint32_t*)nullptr, (uint64_t*)nullptr, 0);
+               d_ff, y, (int)accumulate, (uint64_t*)nullptr, 0);
   } else {
     POP_LAUNCH((k_pop_finish<T, false>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
                (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, 0, (const T*)WdT, d,
-               d_ff, y, (int)accumulate, (uint32_t*)nullptr, (uint64_t*)nullptr, 0);
+               d_ff, y, (int)accumulate, (uint64_t*)nullptr, 0);
   }
   return true;
 }
@@ -1277,16 +1344,19 @@ static int resident_blocks(const void* kernel) {
 }
 
 // The batch-1 step as k_pop_linked + k_pop_finish.  Returns false, having
-// launched nothing, when the step does not fit it (d wider than four 16-byte
-// vectors per thread, more than kLinkedTopkMaxN candidates, too many rows per
-// worker); the caller then takes the three-launch path.
+// launched nothing, when the step has no candidate top-k (no candidates, or
+// k = 0) or does not fit (d wider than four 16-byte vectors per thread, more
+// than kLinkedTopkMaxN candidates, too many rows per worker); the caller then
+// takes launch_fused.
 template <typename T>
 static bool launch_linked(hipStream_t st, const void* x, int d, const void* Wg, const void* Wu, const void* WdT,
                           int d_ff, const int32_t* R, int n_R, const int32_t* C, int n_C, int k, float* y,
                           const DecodeWs& w, int32_t* sel_out, bool accumulate) {
   constexpr int V = Vec<T>::N;
   const int nv = (d + kFusedThreads * V - 1) / (kFusedThreads * V);
-  if (nv > 4 || n_C > kLinkedTopkMaxN || n_R + n_C <= 0) return false;
+  // Without candidates there is no chain to overlap: the retained-only
+  // k_pop_step (fewer registers) measured faster for the dense and static steps.
+  if (nv > 4 || n_C <= 0 || k <= 0 || n_C > kLinkedTopkMaxN || n_R + n_C <= 0) return false;
   const bool identity = R == nullptr;
   const void* kern = nullptr;
 #define POP_LINKED_PICK(NVT)                                                   \
@@ -1330,8 +1400,7 @@ static bool launch_linked(hipStream_t st, const void* x, int d, const void* Wg, 
 #undef POP_LINKED
   POP_LAUNCH((k_pop_finish<T, false>), dim3((d + kFinCols - 1) / kFinCols), dim3(kFinThreads), 0, st,
              (const float*)partial, nW, (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel,
-             (const int32_t*)w.Q, 0, (const T*)WdT, d, d_ff, y, (int)accumulate, w.ctl + kCtlFirstCounter, w.hand,
-             (int)kHandWords);
+             (const int32_t*)w.Q, 0, (const T*)WdT, d, d_ff, y, (int)accumulate, w.hand, (int)kHandWords);
   return true;
 }
 

@@ -563,111 +563,226 @@ __device__ __forceinline__ uint64_t pack_valid(uint32_t tag, uint32_t payload) {
 __device__ __forceinline__ bool is_valid(uint64_t w) { return (w >> 63) != 0; }
 
 // The candidate top-k of the single-launch batch-1 step, where the scores come
-// from other workgroups of the same launch.  It waits (thread 0 polling, at
-// most poll_limit rounds) until *c_done reaches n_writers, the number of
-// workgroups that publish candidate words, each having counted itself once
-// its words were complete; it then reads candidate i's word cand[i] =
-// pack_valid(bits of |z_i|, bits of z_i) and selects exactly as topk_block
-// does.  It publishes the cut rather than a list: candidate position p with
-// score bits x is selected iff
+// from other workgroups of the same launch.  Candidate i's word cand[i] is
+// pack_valid(bits of |z_i|, bits of z_i) once its row is done (0 before).  The
+// workgroup polls the words it has not seen yet (coherent loads, at most
+// poll_limit rounds) and counts each score, as it arrives, into a histogram of
+// its 12 leading value bits, so the counting overlaps the candidate rows.
+// Once all n are in, a scan finds the bin of the target rank n - k; a bin of
+// at most kSelResolve keys is resolved directly (every key ranks itself
+// against the bin), a larger one (many equal scores) by the general select.
+// The selection is the same as topk_block's.  It publishes the cut rather
+// than a list: candidate position p with score bits x is selected iff
 //     x > v,  or  x == v and p <= tie_pos,
-// the pair written as pack_valid(v, tie_pos) into the n_copies words
-// thr[0], thr[stride], ... (coherent; each reader polls one copy, so no
-// single line is polled by every workgroup).  Then, when not NULL, it writes
-// positions (ascending, into C) and selected (channels C[p]) of the k
-// selected candidates with plain stores.  A round limit reached, or a word
-// found without its valid bit, sets *err (coherent); the step goes on with
-// score 0 for such candidates.
+// written as pack_valid(v, tie_pos) into the n_copies words thr[0],
+// thr[stride], ... (coherent; each reader polls one copy, so no single line is
+// polled by every workgroup).  Then, when not NULL, it writes positions
+// (ascending, into C) and selected (channels C[p]) of the k selected
+// candidates with plain stores.  A round limit reached sets *err (coherent);
+// the step goes on with score 0 for the missing candidates.
 template <int NTH, int MAXN>
-__device__ void topk_threshold_linked(const uint64_t* __restrict__ cand, int n, int k, const uint32_t* c_done,
-                                      int n_writers, const int32_t* __restrict__ C, int32_t* __restrict__ positions,
-                                      int32_t* __restrict__ selected, uint64_t* __restrict__ thr, int n_copies,
-                                      int stride, SelShared<NTH, MAXN>& sh, int poll_limit, uint32_t* err) {
+__device__ void topk_threshold_linked(const uint64_t* __restrict__ cand, int n, int k, const int32_t* __restrict__ C,
+                                      int32_t* __restrict__ positions, int32_t* __restrict__ selected,
+                                      uint64_t* __restrict__ thr, int n_copies, int stride, SelShared<NTH, MAXN>& sh,
+                                      int poll_limit, uint32_t* err) {
   constexpr int EM = SelShared<NTH, MAXN>::kPerThread;
   static_assert(sel_slot(MAXN - 1) < kSelSlots, "keys handed over through the histogram buffers");
+  constexpr int kBinShift = 31 - 12;  // 12 leading value bits: 4096 bins
   if (n <= 0 || k <= 0) return;
   k = min(k, n);
-  const int E = (n + NTH - 1) / NTH;
-  const int base = threadIdx.x * E;
-  const int cnt = max(0, min(E, n - base));
-  if (threadIdx.x == 0) {
-    bool ok;
-    poll_coh(c_done, [n_writers](uint32_t v) { return v >= (uint32_t)n_writers; }, poll_limit, ok);
-    if (!ok) st_coh(err, 1u);
-  }
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kSelSlots; i += NTH) sh.hA[i] = 0u;
   __syncthreads();
-  // ---- every candidate word, coalesced (element tid + j * NTH), then handed to its owner
-  uint64_t w[EM];
-  int c[EM];
+  // ---- the scores as they arrive (element tid + j * NTH)
+  uint32_t vb[EM];
+  bool got[EM];
 #pragma unroll
   for (int j = 0; j < EM; ++j) {
-    const int i = min((int)threadIdx.x + j * NTH, n - 1);
-    w[j] = ld_coh(&cand[i]);
-    c[j] = C[i];
+    vb[j] = 0u;
+    got[j] = tid + j * NTH >= n;
   }
-  bool bad = false;
-#pragma unroll
-  for (int j = 0; j < EM; ++j) {
-    const int i = (int)threadIdx.x + j * NTH;
-    if (i < n) {
-      bad |= !is_valid(w[j]);
-      sh.hA[sel_slot(i)] = is_valid(w[j]) ? (uint32_t)(w[j] >> 32) & 0x7fffffffu : 0u;
-      sh.hB[sel_slot(i)] = (unsigned int)c[j];
-    }
-  }
-  if (bad) st_coh(err, 3u);
-  __syncthreads();
-  uint32_t v[EM];
-  int cv[EM];
-#pragma unroll
-  for (int j = 0; j < EM; ++j) {
-    const int i = min(base + j, n - 1);
-    v[j] = sh.hA[sel_slot(i)];
-    cv[j] = (int)sh.hB[sel_slot(i)];
-  }
-  __syncthreads();  // the select clears the buffers next
-  const int ranks[1] = {n - k};
-  SelTarget t[1];
-  select_targets<NTH, 1, EM, MAXN>(v, n, base, E, ranks, sh, t);
-  int eqb[2];
-  sel_eq_before<NTH, 1, EM, MAXN>(v, E, cnt, t, sh, eqb);
-  // ---- the cut: the selected elements of value v are the (m - q) of lowest position
-  const int m = t[0].count, q = t[0].rank;
-  if (threadIdx.x == 0) sh.scan[0][0] = q == 0 ? n : -1;  // all, or none, of value v
-  __syncthreads();
-  if (q > 0 && q < m) {
-    int eq = eqb[0];
+  for (int round = 0;; ++round) {
+    bool all = true;
 #pragma unroll
     for (int j = 0; j < EM; ++j) {
-      if (j >= E) break;  // block-uniform
-      if (j < cnt && v[j] == t[0].prefix) {
-        ++eq;
-        if (eq == m - q) sh.scan[0][0] = base + j;
+      if (!got[j]) {
+        const uint64_t w = ld_coh(&cand[tid + j * NTH]);
+        if (is_valid(w)) {
+          got[j] = true;
+          vb[j] = (uint32_t)(w >> 32) & 0x7fffffffu;
+          atomicAdd(&sh.hA[sel_slot((int)(vb[j] >> kBinShift))], 1u);
+        }
+      }
+      all &= got[j];
+    }
+    if (__syncthreads_and(all ? 1 : 0)) break;
+    if (round + 1 >= poll_limit) {
+      if (tid == 0) st_coh(err, 1u);
+      // missing scores count as 0
+#pragma unroll
+      for (int j = 0; j < EM; ++j)
+        if (!got[j]) {
+          got[j] = true;
+          atomicAdd(&sh.hA[sel_slot(0)], 1u);
+        }
+      __syncthreads();
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  // ---- the bin holding ascending rank r = n - k
+  constexpr int BPT = kSelBins / NTH;
+  const int r = n - k;
+  {
+    unsigned int hb[BPT];
+    int local = 0;
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+      hb[b] = sh.hA[sel_slot(tid * BPT + b)];
+      local += (int)hb[b];
+    }
+    int total;
+    const int excl = block_excl_scan1(local, total, sh);
+    if (r >= excl && r < excl + local) {
+      int cum = excl;
+#pragma unroll
+      for (int b = 0; b < BPT; ++b) {
+        const int c = (int)hb[b];
+        if (r >= cum && r < cum + c) {
+          SelTarget u;
+          u.prefix = (uint32_t)(tid * BPT + b) << kBinShift;
+          u.shift = kBinShift;
+          u.rank = r - cum;
+          u.count = c;
+          u.beyond = 0;
+          sh.tgt[0] = u;
+        }
+        cum += c;
       }
     }
   }
   __syncthreads();
-  const int tie_pos = sh.scan[0][0];
-  if ((int)threadIdx.x < n_copies) st_coh(&thr[threadIdx.x * stride], pack_valid(t[0].prefix, (uint32_t)tie_pos));
+  SelTarget t0 = sh.tgt[0];
+  int tie_pos;
+  if (t0.count <= kSelResolve) {
+    // ---- small bin: gather its keys and rank each against the others
+    if (tid == 0) sh.rcnt = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EM; ++j) {
+      const int i = tid + j * NTH;
+      if (i < n && (vb[j] >> kBinShift) == (t0.prefix >> kBinShift)) {
+        const int slot = atomicAdd(&sh.rcnt, 1);
+        if (slot < kSelResolve) {
+          sh.rv[slot] = vb[j];
+          sh.ri[slot] = i;
+        }
+      }
+    }
+    __syncthreads();
+    const int mb = t0.count;
+    // ascending order: smaller value first, on equal values the larger index first
+    if (tid < mb) {
+      const uint32_t vv = sh.rv[tid];
+      const int ii = sh.ri[tid];
+      int below = 0, lt = 0, eqn = 0;
+      for (int e = 0; e < mb; ++e) {
+        const uint32_t ve = sh.rv[e];
+        lt += ve < vv ? 1 : 0;
+        eqn += ve == vv ? 1 : 0;
+        below += (ve < vv || (ve == vv && sh.ri[e] > ii)) ? 1 : 0;
+      }
+      if (below == t0.rank) {
+        SelTarget u;
+        u.prefix = vv;
+        u.shift = 0;
+        u.rank = t0.rank - lt;  // q: keys of value v below the target rank
+        u.count = eqn;          // m: keys of value v
+        u.beyond = 0;
+        sh.tgt[0] = u;
+      }
+    }
+    __syncthreads();
+    t0 = sh.tgt[0];
+    // the selected keys of value v are the (m - q) of lowest index
+    const int m = t0.count, q = t0.rank;
+    if (tid == 0) sh.scan[0][0] = q == 0 ? n : -1;
+    __syncthreads();
+    if (q > 0 && q < m && tid < mb && sh.rv[tid] == t0.prefix) {
+      const int ii = sh.ri[tid];
+      int lower = 0;  // keys of value v with a lower index
+      for (int e = 0; e < mb; ++e) lower += (sh.rv[e] == t0.prefix && sh.ri[e] < ii) ? 1 : 0;
+      if (lower == m - q - 1) sh.scan[0][0] = ii;
+    }
+    __syncthreads();
+    tie_pos = sh.scan[0][0];
+  } else {
+    // ---- large bin: the general select over every key (owner layout)
+    const int E = (n + NTH - 1) / NTH;
+    const int base = tid * E;
+    const int cnt = max(0, min(E, n - base));
+#pragma unroll
+    for (int j = 0; j < EM; ++j) {
+      const int i = tid + j * NTH;
+      if (i < n) sh.hB[sel_slot(i)] = vb[j];
+    }
+    __syncthreads();
+    uint32_t v[EM];
+#pragma unroll
+    for (int j = 0; j < EM; ++j) v[j] = sh.hB[sel_slot(min(base + j, n - 1))];
+    __syncthreads();  // the select clears the buffers next
+    const int ranks[1] = {r};
+    SelTarget t[1];
+    select_targets<NTH, 1, EM, MAXN>(v, n, base, E, ranks, sh, t);
+    int eqb[2];
+    sel_eq_before<NTH, 1, EM, MAXN>(v, E, cnt, t, sh, eqb);
+    const int m = t[0].count, q = t[0].rank;
+    if (tid == 0) sh.scan[0][0] = q == 0 ? n : -1;
+    __syncthreads();
+    if (q > 0 && q < m) {
+      int eq = eqb[0];
+#pragma unroll
+      for (int j = 0; j < EM; ++j) {
+        if (j >= E) break;  // block-uniform
+        if (j < cnt && v[j] == t[0].prefix) {
+          ++eq;
+          if (eq == m - q) sh.scan[0][0] = base + j;
+        }
+      }
+    }
+    __syncthreads();
+    tie_pos = sh.scan[0][0];
+    t0 = t[0];
+  }
+  const uint32_t cv = t0.prefix;
+  if (tid < n_copies) st_coh(&thr[tid * stride], pack_valid(cv, (uint32_t)tie_pos));
   if (positions == nullptr && selected == nullptr) return;
-  // ---- the list, ascending (after the cut is out)
+  // ---- the list, ascending (after the cut is out): flags in LDS, then owner-layout scan
+  __syncthreads();  // sh.scan and the LDS buffers are reused below
+#pragma unroll
+  for (int j = 0; j < EM; ++j) {
+    const int i = tid + j * NTH;
+    if (i < n) sh.hB[sel_slot(i)] = (vb[j] > cv || (vb[j] == cv && i <= tie_pos)) ? 1u : 0u;
+  }
+  __syncthreads();
+  const int E = (n + NTH - 1) / NTH;
+  const int base = tid * E;
+  const int cnt = max(0, min(E, n - base));
   int pos[3] = {0, 0, 0};
 #pragma unroll
   for (int j = 0; j < EM; ++j) {
     if (j >= E) break;  // block-uniform
-    const bool s = j < cnt && (v[j] > t[0].prefix || (v[j] == t[0].prefix && base + j <= tie_pos));
-    pos[0] += s ? 1 : 0;
+    pos[0] += (j < cnt && sh.hB[sel_slot(base + j)] != 0u) ? 1 : 0;
   }
   int tot[3];
-  __syncthreads();  // sh.scan is reused by the scan
   block_exclusive_scan3(pos, tot, sh);
 #pragma unroll
   for (int j = 0; j < EM; ++j) {
     if (j >= E) break;  // block-uniform
-    if (j < cnt && (v[j] > t[0].prefix || (v[j] == t[0].prefix && base + j <= tie_pos))) {
+    if (j < cnt && sh.hB[sel_slot(base + j)] != 0u) {
       if (pos[0] < k) {
         if (positions != nullptr) positions[pos[0]] = base + j;
-        if (selected != nullptr) selected[pos[0]] = cv[j];
+        if (selected != nullptr) selected[pos[0]] = C[base + j];
       }
       ++pos[0];
     }
