@@ -105,6 +105,18 @@ const char* pop_last_error(void);
  */
 pop_status pop_partition_counts(int32_t d_ff, double r, double gamma, pop_counts* out);
 
+/*
+ * pop_decode_topk_count — pure host function, no device work.
+ * *k = the number of candidates one decode step selects for an existing
+ * partition (n_R retained, n_C candidates) at pruning rate r: k =
+ * clamp(round((1 - r) d_ff) - n_R, 0, n_C), so that n_R + k is the live count
+ * exactly whenever the partition allows it (POP notes, "Key design 2").  The
+ * size of pop_decode_ffn's `selected` output.
+ * Errors: BAD_SHAPE for d_ff outside [1, POP_MAX_D_FF]; INVALID_ARGUMENT for
+ * r outside [0, 1), negative counts, n_R + n_C > d_ff or k == NULL.
+ */
+pop_status pop_decode_topk_count(int32_t d_ff, double r, int32_t n_R, int32_t n_C, int32_t* k);
+
 /* Workspace bytes pop_prefill_partition needs for these sizes. */
 size_t pop_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff);
 
@@ -525,15 +537,24 @@ size_t pop_layer_decode_workspace_bytes(int32_t batch, const pop_layer_shape* s,
  *   dense_ffn  0: POP's step; 1: every FFN channel (pop_dense_ffn_decode).
  *   ws         >= pop_layer_decode_workspace_bytes; after the call byte 0
  *              holds the FFN's input RMSNorm(h) (dt, [batch, D]).
- * Kernels: the q|k|v projection as a K-major GEMV (one wave per 512 bf16 or
- * 256 fp32 columns and a chunk of rows, fp32 partial sums), with the RMSNorm
- * computed inside its waves at batch <= 2 (a separate RMSNorm launch above);
- * the chunk sums with the rotation and cache write; attention split into
- * 64-key slices; the output projection GEMV, whose waves merge the slices
- * (log-sum-exp) on the fly; the residual; the FFN's RMSNorm; pop_decode_ffn
- * or pop_dense_ffn_decode, whose last kernel adds its output into x at batch
- * 1 (a residual add launch above).  Deterministic.  Errors as
- * pop_layer_prefill and pop_decode_ffn; nothing is enqueued on an error.
+ * Kernels, in three batch regimes:
+ *   - batch <= 2: the q|k|v projection as a K-major GEMV (one wave per 512
+ *     bf16 or 256 fp32 columns and a chunk of rows, fp32 partial sums) with the
+ *     RMSNorm computed inside its waves; the chunk sums with the rotation and
+ *     cache write; attention split into 64-key slices; the output projection
+ *     GEMV, whose waves merge the slices (log-sum-exp) on the fly;
+ *   - batch 3-11, and fp32 at any batch above 2: a separate RMSNorm launch, the
+ *     same GEMV projections, and the attention slices merged by a kernel of
+ *     their own before a plain output projection;
+ *   - bf16 from 12 tokens: both projections on a matrix-core GEMM (16 tokens
+ *     as the A operand, 256-column W tiles; each 16-token group streams W
+ *     again), split into reduction slices whose partial products the rotation
+ *     kernel and the residual kernel add; the workspace grows with the slice
+ *     count.
+ * Then the residual, the FFN's RMSNorm, and pop_decode_ffn or
+ * pop_dense_ffn_decode, whose last kernel adds its output into x at batch 1
+ * (a residual add launch above).  Deterministic.  Errors as pop_layer_prefill
+ * and pop_decode_ffn; nothing is enqueued on an error.
  */
 pop_status pop_layer_decode(float* x, int32_t batch, const pop_layer_shape* s, const pop_layer_weights* w,
                             pop_dtype dt, void* K_cache, void* V_cache, const int32_t* pos, const int32_t* R,

@@ -106,4 +106,15 @@ pop_status pop_partition_counts(int32_t d_ff, double r, double gamma, pop_counts
   return POP_OK;
 }
 
+pop_status pop_decode_topk_count(int32_t d_ff, double r, int32_t n_R, int32_t n_C, int32_t* k) {
+  pop::clear_error();
+  if (k == nullptr) return pop::fail(POP_ERR_INVALID_ARGUMENT, "k is NULL");
+  if (d_ff < 1 || d_ff > POP_MAX_D_FF) return pop::fail(POP_ERR_BAD_SHAPE, "d_ff=%d outside [1, %d]", d_ff, POP_MAX_D_FF);
+  if (!(r >= 0.0 && r < 1.0)) return pop::fail(POP_ERR_INVALID_ARGUMENT, "r=%g outside [0, 1)", r);
+  if (n_R < 0 || n_C < 0 || (int64_t)n_R + n_C > d_ff)
+    return pop::fail(POP_ERR_INVALID_ARGUMENT, "n_R=%d, n_C=%d inconsistent with d_ff=%d", n_R, n_C, d_ff);
+  *k = pop::topk_count(d_ff, r, n_R, n_C);
+  return POP_OK;
+}
+
 }  // extern "C"

@@ -54,6 +54,7 @@ def _load():
         "pop_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pop_last_error": (ctypes.c_char_p, []),
         "pop_partition_counts": (ctypes.c_int, [_c_i32, _c_dbl, _c_dbl, ctypes.POINTER(PopCounts)]),
+        "pop_decode_topk_count": (ctypes.c_int, [_c_i32, _c_dbl, _c_i32, _c_i32, ctypes.POINTER(_c_i32)]),
         "pop_prefill_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32]),
         "pop_prefill_partition": (ctypes.c_int, [_c_vp, _c_i64, _c_i32, _c_vp, _c_i32, ctypes.c_int, _c_dbl, _c_dbl,
                                                  _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
@@ -219,7 +220,7 @@ def pop_decode_ffn(x, W_gate, W_up, W_downT, R, C, r: float, *, y=None, selected
         y = torch.empty((batch, d), dtype=torch.float32, device=dev)
     S = None
     if selected:
-        S = torch.empty(_k(d_ff, r, R.numel(), C.numel()), dtype=torch.int32, device=dev)
+        S = torch.empty(pop_decode_topk_count(d_ff, r, R.numel(), C.numel()), dtype=torch.int32, device=dev)
     if ws is None:
         ws = workspace(pop_decode_workspace_bytes(batch, d, d_ff), dev)
     _check("pop_decode_ffn", lib.pop_decode_ffn(
@@ -235,7 +236,7 @@ class PeriodicState:
     positions into C and as channels [k], and the kept steps' rows [n_R + k]."""
 
     def __init__(self, d_ff: int, r: float, n_R: int, n_C: int, device):
-        k = _k(d_ff, r, n_R, n_C)
+        k = pop_decode_topk_count(d_ff, r, n_R, n_C)
         self.memory = torch.zeros(n_C, dtype=torch.float32, device=device)
         self.positions = torch.zeros(k, dtype=torch.int32, device=device)
         self.selected = torch.zeros(k, dtype=torch.int32, device=device)
@@ -266,9 +267,11 @@ def pop_decode_ffn_periodic(x, W_gate, W_up, W_downT, R, C, r: float, step: int,
     return y
 
 
-def _k(d_ff, r, n_R, n_C):
-    live = pop_partition_counts(d_ff, r, 0.0)["n_live"]
-    return max(0, min(live - n_R, n_C))
+def pop_decode_topk_count(d_ff: int, r: float, n_R: int, n_C: int) -> int:
+    """k, the candidates one decode step selects (the library's count)."""
+    k = _c_i32()
+    _check("pop_decode_topk_count", lib.pop_decode_topk_count(int(d_ff), float(r), int(n_R), int(n_C), ctypes.byref(k)))
+    return int(k.value)
 
 
 def pop_dense_ffn_decode(x, W_gate, W_up, W_downT, *, y=None, ws=None, stream=None):
@@ -393,7 +396,7 @@ def pop_moe_decode_ffn(x, logits, W_gate, W_up, W_downT, R, C, r: float, *, y=No
         y = torch.empty((T, d), dtype=torch.float32, device=dev)
     S = None
     if selected:
-        S = torch.zeros((E, _k(d_ff, r, R.shape[1], C.shape[1])), dtype=torch.int32, device=dev)
+        S = torch.zeros((E, pop_decode_topk_count(d_ff, r, R.shape[1], C.shape[1])), dtype=torch.int32, device=dev)
     if ws is None:
         ws = workspace(pop_moe_decode_workspace_bytes(T, d, d_ff, E), dev)
     _check("pop_moe_decode_ffn", lib.pop_moe_decode_ffn(

@@ -365,10 +365,15 @@ def moe_partitions(X, logits, experts_W_up, r: float, gamma: float):
     return parts
 
 
-def moe_decode_step(x, logits, experts, parts, r: float):
+def moe_decode_step(x, logits, experts, parts, r: float, selections=None):
     """One MoE decode step: each expert runs POP decode on the tokens routed
-    to it (batch max over them), outputs combined with the routing weights.
-    ``experts`` is a list of dicts with W_gate, W_up, W_down."""
+    to it (batch max over them), outputs combined with the routing weights:
+    y_tok = sum over the token's two experts of w_e * y_e(tok) (reading R8).
+    ``experts`` is a list of dicts with W_gate, W_up, W_down.
+    ``selections`` (optional, per expert: its selected candidates, or None)
+    replaces each expert's own selection step, so that the output can be
+    evaluated on another implementation's selection (the parity protocol's
+    step for admissible near-tie flips); the rest of the step is unchanged."""
     x = _f64(x).reshape(-1, np.shape(x)[-1])
     ex, wt = moe_route_top2(logits)
     y = np.zeros((x.shape[0], _f64(experts[0]["W_down"]).shape[0]))
@@ -379,7 +384,12 @@ def moe_decode_step(x, logits, experts, parts, r: float):
             sel.append(None)
             continue
         R, C, _ = parts[e]
-        out = decode_step(x[rows], ew["W_gate"], ew["W_up"], ew["W_down"], R, C, r)
-        y[rows] += wt[rows, slot][:, None] * out["y"]
-        sel.append(out["S"])
+        if selections is not None and selections[e] is not None:
+            S = np.asarray(selections[e], dtype=np.int64)
+            ye = masked_ffn(x[rows], ew["W_gate"], ew["W_up"], ew["W_down"], np.concatenate([R, S]))
+        else:
+            out = decode_step(x[rows], ew["W_gate"], ew["W_up"], ew["W_down"], R, C, r)
+            S, ye = out["S"], out["y"]
+        y[rows] += wt[rows, slot][:, None] * ye
+        sel.append(S)
     return y, sel

@@ -335,6 +335,58 @@ def pin_moe_identical_experts(o):
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-13)
 
 
+def _dense_by_hand(x, w):
+    """W_down (SiLU(W_gate x) * (W_up x)) per row, SiLU from scipy's expit."""
+    g = x @ w["W_gate"].T
+    u = x @ w["W_up"].T
+    return (g * scipy.special.expit(g) * u) @ w["W_down"].T
+
+
+def pin_moe_weighted_combine_by_hand(o):
+    # 2 tokens, 3 distinct experts, r = 0 (each expert's step is its dense FFN,
+    # pinned by pin_r0_is_dense): logits chosen so the top-2 softmax weights
+    # are exact and unequal.  Token 0: experts 1 (ln 3) and 0 (0) -> 3/4, 1/4.
+    # Token 1: experts 2 (ln 4) and 1 (0) -> 4/5, 1/5.
+    g = _rng(17)
+    d, dff, E = 5, 9, 3
+    exps = [{"W_gate": g.standard_normal((dff, d)), "W_up": g.standard_normal((dff, d)),
+             "W_down": g.standard_normal((d, dff))} for _ in range(E)]
+    X = g.standard_normal((4, d))
+    parts = o.moe_partitions(X, g.standard_normal((4, E)), [e["W_up"] for e in exps], 0.0, 0.1)
+    x = g.standard_normal((2, d))
+    L = np.array([[0.0, np.log(3.0), -5.0], [-3.0, 0.0, np.log(4.0)]])
+    y, _ = o.moe_decode_step(x, L, exps, parts, 0.0)
+    ref = np.stack([0.75 * _dense_by_hand(x[:1], exps[1])[0] + 0.25 * _dense_by_hand(x[:1], exps[0])[0],
+                    0.8 * _dense_by_hand(x[1:], exps[2])[0] + 0.2 * _dense_by_hand(x[1:], exps[1])[0]])
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-13)
+
+
+def pin_moe_zeroed_expert(o):
+    # distinct experts, one with W_down = 0: a token routed to it and to expert
+    # e gets exactly w_e * y_e(token), its POP step on expert e alone
+    g = _rng(18)
+    d, dff, E = 6, 30, 4
+    exps = [{"W_gate": g.standard_normal((dff, d)), "W_up": g.standard_normal((dff, d)),
+             "W_down": g.standard_normal((d, dff))} for _ in range(E)]
+    exps[2]["W_down"] = np.zeros((d, dff))
+    X = g.standard_normal((12, d))
+    parts = o.moe_partitions(X, g.standard_normal((12, E)), [e["W_up"] for e in exps], 0.3, 0.1)
+    T = 7
+    x = g.standard_normal((T, d))
+    L = g.standard_normal((T, E))
+    L[:, 2] = 10.0  # expert 2 is every token's first choice
+    ex, wt = o.moe_route_top2(L)
+    y, _ = o.moe_decode_step(x, L, exps, parts, 0.3)
+    for e in (0, 1, 3):
+        rows = np.flatnonzero(ex[:, 1] == e)
+        if len(rows) == 0:
+            continue
+        R, C, _ = parts[e]
+        ye = o.decode_step(x[rows], exps[e]["W_gate"], exps[e]["W_up"], exps[e]["W_down"], R, C, 0.3)["y"]
+        np.testing.assert_allclose(y[rows], wt[rows, 1][:, None] * ye, rtol=1e-12, atol=1e-13)
+        assert np.all(wt[rows, 1] < 0.5)  # the second weight is the smaller one here
+
+
 def pin_moe_expert_subsets(o):
     # each expert's partition uses exactly the prompt tokens routed to it
     g = _rng(15)

@@ -49,6 +49,34 @@ def test_counts_errors(args, status):
     assert pop.lib.pop_last_error().decode() != ""
 
 
+def test_decode_topk_count_matches_oracle():
+    """k for existing lists: the oracle's live count less |R|, clamped to [0, |C|]
+    (the oracle's decode step selects exactly that many)."""
+    g = np.random.default_rng(3)
+    for _ in range(2000):
+        n = int(g.integers(1, 32769))
+        r = float(g.uniform(0, 0.999))
+        n_R = int(g.integers(0, n + 1))
+        n_C = int(g.integers(0, n - n_R + 1))
+        live = oracle.partition_counts(n, r, 0.0)["n_live"]
+        assert pop.pop_decode_topk_count(n, r, n_R, n_C) == min(max(live - n_R, 0), n_C), (n, r, n_R, n_C)
+    # the partition's own sizes give the partition's k
+    for n, r, gam in ((688, 0.3, 0.1), (11008, 0.299, 0.1), (18944, 0.5, 0.1), (14336, 0.3, 0.1)):
+        c = oracle.partition_counts(n, r, gam)
+        assert pop.pop_decode_topk_count(n, r, c["n_R"], c["n_C"]) == c["k"]
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 0.3, 0, 0), SHAPE), ((32769, 0.3, 0, 0), SHAPE), ((10, 1.0, 2, 2), INVALID),
+    ((10, -0.5, 2, 2), INVALID), ((10, 0.3, -1, 2), INVALID), ((10, 0.3, 6, 5), INVALID),
+])
+def test_decode_topk_count_errors(args, status):
+    k = ctypes.c_int32(-7)
+    assert pop.lib.pop_decode_topk_count(*args, ctypes.byref(k)) == status
+    assert k.value == -7 and pop.lib.pop_last_error().decode() != ""
+    assert pop.lib.pop_decode_topk_count(10, 0.3, 2, 2, None) == INVALID
+
+
 def test_counts_null_out():
     assert pop.lib.pop_partition_counts(10, 0.3, 0.1, None) == INVALID
     assert pop.status_string(INVALID) == "POP_ERR_INVALID_ARGUMENT"

@@ -169,6 +169,10 @@ DECODE = [
     # fp32 above batch 2 (separate merge kernel, plain projections); bf16 at the matrix-core projections' threshold
     ("f32_gqa_b5_pos77", "f32", 256, 4, 2, 64, 688, 96, 5, 77),
     ("bf16_hd128_b12_pos130", "bf16", 512, 4, 2, 128, 1376, 160, 12, 130),
+    # matrix-core projections past one stage: 96-row reduction slices of the
+    # q|k|v projection (3 stages), a 64-column partial tile of the output
+    # projection, and a partial second 16-token group (batch 20)
+    ("bf16_d4160_b20_pos40", "bf16", 4160, 4, 2, 128, 688, 64, 20, 40),
     # the largest model width, and a 4096-position cache at its last slot (64 slices merged)
     ("bf16_max_d_16384_b2_pos50", "bf16", 16384, 2, 1, 128, 688, 64, 2, 50),
     ("f32_cache_4096_last_slot", "f32", 256, 4, 2, 64, 688, 4096, 1, 4095),

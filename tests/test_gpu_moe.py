@@ -109,13 +109,13 @@ def _check_moe_step(x, L, exps, parts, r, dtype, y, S, ws):
     T = x.shape[0]
     E = len(exps)
     d_ff = exps[0]["W_gate"].shape[0]
-    ex, wt = oracle.moe_route_top2(L)
+    ex, _ = oracle.moe_route_top2(L)
     n_R, n_C = len(parts[0][0]), len(parts[0][1])
     z_dev, sc_dev = moe_decode_views(ws, T, d_ff, E, n_R + n_C, n_C)
     S = host(S).astype(np.int64)
-    y_ref = np.zeros((T, x.shape[1]))
     off = 0
     k = S.shape[1]
+    sel_dev = [None] * E
     for e in range(E):
         rows, slot = np.nonzero(ex == e)
         order = np.argsort(rows, kind="stable")
@@ -139,10 +139,11 @@ def _check_moe_step(x, L, exps, parts, r, dtype, y, S, ws):
             cuts = [srt[j] for j in (k - 1, k) if 0 <= j < len(C_e)]
             v = sr[np.searchsorted(C_e, ch)]
             assert any(abs(v - t) <= TIE_REL * max(t, 1e-30) for t in cuts), f"expert {e}: candidate {ch}"
-        live = np.concatenate([R_e, S[e]])
-        ye = oracle.masked_ffn(x[rows], exps[e]["W_gate"], exps[e]["W_up"], exps[e]["W_down"], live)
-        y_ref[rows] += wt[rows, slot][:, None] * ye
+        sel_dev[e] = S[e]
         off += len(rows)
+    # the output: the oracle's MoE step (routing, per-expert steps, weighted
+    # combine) evaluated on the device's selections
+    y_ref, _ = oracle.moe_decode_step(x, L, exps, parts, r, selections=sel_dev)
     err = np.abs(host(y) - y_ref).max() / max(np.abs(y_ref).max(), 1e-30)
     assert err <= TOL[dtype], f"max|dy|/max|y| = {err:.3e}"
     return err

@@ -43,6 +43,10 @@ MUTANTS = [
     ("routing tie toward the higher expert", "key=lambda e: (-L[t, e], e)", "key=lambda e: (-L[t, e], -e)"),
     ("routing weights not normalised", "weights[t] = (w1 / (w1 + w2), w2 / (w1 + w2))", "weights[t] = (w1, w2)"),
     ("expert partition over all prompt tokens", "toks = np.flatnonzero((ex == e).any(axis=1))", "toks = np.arange(len(X))"),
+    ("a token's two routing weights swapped", "y[rows] += wt[rows, slot][:, None] * ye",
+     "y[rows] += wt[rows, 1 - slot][:, None] * ye"),
+    ("constant routing weights of one half", "y[rows] += wt[rows, slot][:, None] * ye", "y[rows] += 0.5 * ye"),
+    ("an expert's output added without its weight", "y[rows] += wt[rows, slot][:, None] * ye", "y[rows] += ye"),
     ("full re-evaluation keeps one channel too few", "S = select_candidates(allc, sc, n_live)", "S = select_candidates(allc, sc, n_live - 1)"),
     ("periodic memory kept across a refresh", "            memory = np.zeros(len(C))\n        else:", "        else:"),
     ("periodic memory ignores the steps between refreshes", "memory[spos] += candidate_scores(z_live, n_R)",
