@@ -231,6 +231,31 @@ pop_status pop_decode_ffn(const void* x, int32_t batch, int32_t d, const void* W
 /* Workspace bytes of pop_decode_ffn_periodic (independent of r and the lists). */
 size_t pop_decode_periodic_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff);
 
+/* Bytes of the device array pop_decode_ffn_noalloc uses as its workspace. */
+#define POP_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * pop_decode_ffn_noalloc — pop_decode_ffn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same step, inputs, outputs and result, with the
+ * workspace taken from a library-owned device array of
+ * POP_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU instead of a caller buffer.  The
+ * call allocates nothing.  The array is held by each GPU the library runs on
+ * until the process ends; its address is looked up, and its control words
+ * cleared (a kernel on `stream`), at the first call on each device.  Every
+ * call on one GPU shares that GPU's array and finds the last call's contents:
+ * calls that overlap on one GPU (different streams, or graphs replayed
+ * concurrently) race and give wrong results; order them.  The sticky error
+ * word of POP_DECODE_WS_Z_OFFSET lives in the array too.
+ * Errors: as pop_decode_ffn, plus WORKSPACE_TOO_SMALL when
+ * pop_decode_workspace_bytes(batch, d, d_ff) exceeds POP_NOALLOC_SCRATCH_BYTES
+ * (nothing is enqueued), and HIP_ERROR when the array cannot be found.
+ */
+pop_status pop_decode_ffn_noalloc(const void* x, int32_t batch, int32_t d, const void* W_gate,
+                                  const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
+                                  const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C, double r,
+                                  float* y, int32_t* selected, void* stream);
+
 /*
  * pop_decode_ffn_periodic — an alternative decode mode: the candidate
  * selection refreshed only every `period` steps, with an activation memory

@@ -1615,3 +1615,66 @@ extern "C" pop_status pop_dense_ffn_decode(const void* x, int32_t batch, int32_t
                (float*)w.down);
   return launched();
 }
+
+// ---------------------------------------------------------------- allocation-free decode step
+// pop_decode_ffn with its workspace in a file-scope device array instead of a
+// caller buffer, for callers that cannot allocate (graph capture, tight
+// serving loops).  Every call on one GPU shares that GPU's array.
+namespace pop {
+constexpr size_t kScratchBytes = (size_t)POP_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Clears n 64-bit words (the control and hand-over words must start at 0).
+__global__ __launch_bounds__(256) void k_zero_u64(uint64_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // the array's device address, per device
+
+// The current device's address of `scratch`, looked up (and its control
+// words cleared, on `st`) on the first call on that device.  Host code uses
+// this address, never the array's name.
+pop_status device_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(POP_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(POP_ERR_HIP, "device %d beyond the %d devices supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(POP_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    const int words = (int)((kCtlBytes + kHandBytes) / sizeof(uint64_t));
+    hipLaunchKernelGGL(k_zero_u64, dim3((words + 255) / 256), dim3(256), 0, st, (uint64_t*)p, words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(POP_ERR_HIP, "clearing the scratch failed: %s", hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return POP_OK;
+}
+}  // namespace
+}  // namespace pop
+
+extern "C" pop_status pop_decode_ffn_noalloc(const void* x, int32_t batch, int32_t d, const void* W_gate,
+                                             const void* W_up, const void* W_downT, int32_t d_ff, pop_dtype dt,
+                                             const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C, double r,
+                                             float* y, int32_t* selected, void* stream) {
+  clear_error();
+  pop_status s = check_shape(batch, d, d_ff, dt);
+  if (s != POP_OK) return s;
+  const size_t need = pop_decode_workspace_bytes(batch, d, d_ff);
+  if (need > kScratchBytes)
+    return fail(POP_ERR_WORKSPACE_TOO_SMALL,
+                "batch=%d, d=%d, d_ff=%d needs %zu workspace bytes, beyond the %zu-byte scratch of "
+                "pop_decode_ffn_noalloc; use pop_decode_ffn with a caller workspace",
+                batch, d, d_ff, need, kScratchBytes);
+  void* ws = nullptr;
+  if ((s = device_scratch((hipStream_t)stream, &ws)) != POP_OK) return s;
+  return pop_decode_ffn(x, batch, d, W_gate, W_up, W_downT, d_ff, dt, R, n_R, C, n_C, r, y, selected, ws,
+                        kScratchBytes, stream);
+}

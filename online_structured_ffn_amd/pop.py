@@ -63,6 +63,8 @@ def _load():
                                           _c_vp, _c_i32, _c_vp, _c_i32, _c_dbl, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
         "pop_dense_ffn_decode": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
                                                 _c_vp, _c_vp, _c_size, _c_vp]),
+        "pop_decode_ffn_noalloc": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
+                                                  _c_vp, _c_i32, _c_vp, _c_i32, _c_dbl, _c_vp, _c_vp, _c_vp]),
         "pop_prefill_importance_workspace_bytes": (_c_size, [_c_i64, _c_i32]),
         "pop_prefill_importance": (ctypes.c_int, [_c_vp, _c_i64, _c_i32, _c_vp, _c_i32, ctypes.c_int, _c_vp, _c_vp,
                                                   _c_size, _c_vp]),
@@ -227,6 +229,25 @@ def pop_decode_ffn(x, W_gate, W_up, W_downT, R, C, r: float, *, y=None, selected
         _ptr(x), batch, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
         _ptr(R), R.numel(), _ptr(C), C.numel(), float(r), _ptr(y), _ptr(S), _ptr(ws), ws.numel(),
         _stream(stream)))
+    return (y, S) if selected else y
+
+
+def pop_decode_ffn_noalloc(x, W_gate, W_up, W_downT, R, C, r: float, *, y=None, selected: bool = False,
+                           stream=None):
+    """pop_decode_ffn with the library's own device scratch as workspace (the
+    C call allocates nothing; calls on one GPU must not overlap)."""
+    _dev(x, W_gate, W_up, W_downT, R, C)
+    batch, d = x.shape
+    d_ff = W_gate.shape[0]
+    dev = W_gate.device
+    if y is None:
+        y = torch.empty((batch, d), dtype=torch.float32, device=dev)
+    S = None
+    if selected:
+        S = torch.empty(pop_decode_topk_count(d_ff, r, R.numel(), C.numel()), dtype=torch.int32, device=dev)
+    _check("pop_decode_ffn_noalloc", lib.pop_decode_ffn_noalloc(
+        _ptr(x), batch, d, _ptr(W_gate), _ptr(W_up), _ptr(W_downT), d_ff, _dtype(W_gate),
+        _ptr(R), R.numel(), _ptr(C), C.numel(), float(r), _ptr(y), _ptr(S), _stream(stream)))
     return (y, S) if selected else y
 
 
