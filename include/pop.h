@@ -602,6 +602,18 @@ pop_status pop_set_trace_events(void* const* events, int32_t n_events);
 /* Events recorded since the last pop_set_trace_events call on this thread. */
 int32_t pop_trace_recorded(void);
 
+/*
+ * pop_hbm_read_probe — a measurement aid, not part of the path: reads the
+ * first bytes / 16 16-byte vectors of src once (device memory, 16-byte
+ * aligned), as `blocks` workgroups of 256 threads each streaming one
+ * contiguous chunk with non-temporal loads, eight in flight per thread (the
+ * decode streams' access pattern), and writes one folded word per thread to
+ * sink (device uint32 [blocks * 256]).  Timing it gives the HBM read rate the
+ * decode kernels can be held to.  Errors: INVALID_ARGUMENT, MISALIGNED,
+ * HIP_ERROR.
+ */
+pop_status pop_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,18 +15,6 @@ def gateup_bytes(d: int, n_A: int, n_C: int, batch: int, e: int) -> int:
     return 2 * n_A * d * e + batch * d * e + 4 * n_A + 4 * batch * n_A + 4 * n_C
 
 
-def candidate_scores_bytes(d: int, n_C: int, e: int) -> int:
-    """Candidate launch at batch 1: gate/up rows of C, x, C, z and scores written."""
-    return 2 * n_C * d * e + d * e + 4 * n_C + 4 * n_C + 4 * n_C
-
-
-def retained_stream_bytes(d: int, n_R: int, n_C: int, k: int, e: int) -> int:
-    """Retained launch at batch 1: gate, up and W_downT rows of R, x, R, z of R
-    written, the partial y per block not counted; plus the top-k beside it
-    (scores and C read, 2k indices written)."""
-    return 3 * n_R * d * e + d * e + 4 * n_R + 4 * n_R + 8 * n_C + 8 * k
-
-
 def select_bytes(n_C: int, k: int) -> int:
     return 4 * n_C + 4 * k * 2 + 4 * k
 
@@ -66,33 +54,27 @@ def prefill_ffn_flops(n_tokens: int, d: int, d_ff: int) -> int:
     return 6 * n_tokens * d * d_ff
 
 
-# Launch shape of the batch-1 step (mirrors the library's defaults: at most
-# 512 retained blocks of at least 8 rows, candidate blocks of 4 rows, every
-# retained block beside the top-k, none beside the candidates).
-FUSED_RBLOCKS, FUSED_CROWS, SPLIT_B = 512, 4, 100
+# Launch shape of the batch-1 step with candidates (mirrors the library: one
+# workgroup runs the top-k, the others take static shares of C and R, one per
+# 8 rows up to 511 of them; a second launch adds their partial sums).
+LINKED_MAX_WORKERS = 511
 
 
-def fused_plan(n_R: int, n_C: int, k: int, d: int, e: int) -> dict:
-    """Blocks and algorithmic bytes of each launch of the batch-1 step:
-    1 and 2 are the two k_pop_step launches, 3 is k_pop_finish (its bytes
-    count the retained partial sums it reads)."""
-    nbR = min(-(-n_R // 8), FUSED_RBLOCKS) if n_R > 0 else 0
-    rpb = -(-n_R // nbR) if nbR else 1
-    if nbR:
-        nbR = -(-n_R // rpb)
-    fuse_topk = 0 < n_C <= 4096 and k > 0
-    nbR2 = nbR * SPLIT_B // 100 if fuse_topk else 0
-    nbR1 = nbR - nbR2
-    rows = lambda b0, nb: max(0, min(n_R, (b0 + nb) * rpb) - b0 * rpb)
-    r1, r2 = rows(0, nbR1), rows(nbR1, nbR2)
-    ret = lambda r: 3 * r * d * e + 8 * r + (d * e if r else 0)
-    b1 = (candidate_scores_bytes(d, n_C, e) if n_C else 0) + ret(r1)
-    b2 = (8 * n_C + 8 * k if fuse_topk else 0) + ret(r2)
-    b3 = 4 * nbR * d + k * d * e + 12 * k + 4 * d
-    nbC = -(-n_C // FUSED_CROWS) if n_C else 0
-    return {"launch": {1: nbC + nbR1 > 0, 2: (1 if fuse_topk else 0) + nbR2 > 0, 3: True},
-            "bytes": {1: b1, 2: b2, 3: b3}, "retained_rows": {1: r1, 2: r2, 3: 0},
-            "partials": nbR}
+def linked_workers(n_R: int, n_C: int) -> int:
+    return max(1, min((n_R + n_C + 7) // 8, LINKED_MAX_WORKERS))
+
+
+def linked_bytes(d: int, n_R: int, n_C: int, k: int, e: int) -> int:
+    """The single-launch batch-1 step (k_pop_linked): everything
+    :func:`decode_bytes` counts except y's write, which the launch after it
+    does (the per-workgroup partial sums are not counted)."""
+    return decode_bytes(d, n_R, n_C, k, 1, e) - 4 * d
+
+
+def linked_finish_bytes(d: int, n_R: int, n_C: int) -> int:
+    """The launch after it (k_pop_finish): the per-workgroup partial sums
+    read, y written."""
+    return 4 * d * linked_workers(n_R, n_C) + 4 * d
 
 
 def moe_decode_bytes(d: int, n_R: int, n_C: int, k: int, experts_reached: float, tokens: int, e: int) -> float:

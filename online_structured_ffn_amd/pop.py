@@ -75,6 +75,7 @@ def _load():
         "pop_decode_down_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32]),
         "pop_set_trace_events": (ctypes.c_int, [ctypes.POINTER(_c_vp), _c_i32]),
         "pop_trace_recorded": (_c_i32, []),
+        "pop_hbm_read_probe": (ctypes.c_int, [_c_vp, _c_size, _c_vp, _c_i32, _c_vp]),
         "pop_dense_ffn_prefill_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32, ctypes.c_int]),
         "pop_moe_route_top2": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
         "pop_moe_prefill_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32, _c_i32]),
@@ -626,3 +627,10 @@ def pop_layer_decode(x, layer: Layer, K, V, pos, R, C, r: float, *, dense_ffn: b
         _ptr(R), nR, _ptr(C), nC, float(r), int(bool(dense_ffn)), _ptr(selected), _ptr(ws), ws.numel(),
         _stream(stream)))
     return x
+
+
+def pop_hbm_read_probe(src, sink, blocks: int = 1024, *, stream=None):
+    """Reads src (a device tensor) once; sink: device int32/uint32 [blocks * 256]."""
+    _dev(src, sink)
+    _check("pop_hbm_read_probe", lib.pop_hbm_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                                        int(blocks), _stream(stream)))
