@@ -243,19 +243,8 @@ def ffn_inputs(w, mods, L, T, dev):
         Wg.append(ws_["W_gate"])
         Wu.append(ws_["W_up"])
         WdT.append(ws_["W_downT"])
-        chans = synth.outlier_channels(w, l)
-        X.append(synth.torch_activations(w, (n_tok, d), l, 0, dev, chans))
-        if w.outlier_kind == "drift_scale" and w.outliers_in_decode:
-            sets = synth.drifting_outliers(w, l, T)
-            mult = np.ones((T, d), dtype=np.float32)
-            for t in range(T):
-                mult[t, sets[t + 1]] = w.outlier_factor
-            base = synth.torch_activations(w, (T * B, d), l, 1, dev).float().view(T, B, d)
-            xt = (base * torch.from_numpy(mult).to(dev)[:, None, :]).to(base.dtype)
-            dec.append(xt.to(X[-1].dtype))
-        else:
-            dch = chans if w.outliers_in_decode else None
-            dec.append(synth.torch_activations(w, (T * B, d), l, 1, dev, dch).view(T, B, d))
+        X.append(synth.torch_activations(w, (n_tok, d), l, 0, dev, synth.outlier_channels(w, l)))
+        dec.append(synth.torch_decode_inputs(w, l, T, dev))
     Xdec = torch.stack(dec, dim=1).contiguous()  # [T, L, B, d]
     del dec
     return Wg, Wu, WdT, X, Xdec
@@ -707,11 +696,7 @@ def bench_moe(args, w, mods, L, T, steps, warmup, detail):
             dst.append(torch.stack([q[name] for q in parts]).contiguous())
         del parts
         X.append(synth.torch_activations(w, (n_tok, d), l, 0, dev))
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(synth.SEED_ROOT ^ 0x5EED)
-    logits_pre = torch.randn((L, n_tok, E), generator=gen, device=dev, dtype=torch.float32)
-    logits_dec = torch.randn((T, L, B, E), generator=gen, device=dev, dtype=torch.float32)
-    Xdec = synth.torch_activations(w, (T * L * B, d), 0, 1, dev).view(T, L, B, d)
+    logits_pre, logits_dec, Xdec = synth.torch_moe_inputs(w, L, T, dev)
     R = [torch.empty((E, n_R), dtype=torch.int32, device=dev) for _ in range(L)]
     C = [torch.empty((E, n_C), dtype=torch.int32, device=dev) for _ in range(L)]
     P = [torch.empty((E, n_P), dtype=torch.int32, device=dev) for _ in range(L)]

@@ -229,3 +229,36 @@ def torch_activations(w: Workload, shape, layer: int, tag: int, device, chans=No
             t[:, idx] = z[..., 0] / torch.sqrt((z[..., 1:] ** 2).sum(-1) / nu)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     return t.to(dt).contiguous()
+
+
+def torch_decode_inputs(w: Workload, layer: int, steps: int, device):
+    """Device-drawn decode inputs of one layer for ``steps`` steps as
+    [steps, B, D]: N(0,1) with the layer's outlier channels (the prompt's set,
+    or with drifting outliers the set O_{t+1} at step t, one member swapped per
+    step as :func:`drifting_outliers` draws them)."""
+    import torch
+    B, d = w.decode_batch, w.d
+    if w.outlier_kind == "drift_scale" and w.outliers_in_decode:
+        sets = drifting_outliers(w, layer, steps)
+        mult = np.ones((steps, d), dtype=np.float32)
+        for t in range(steps):
+            mult[t, sets[t + 1]] = w.outlier_factor
+        base = torch_activations(w, (steps * B, d), layer, 1, device).float().view(steps, B, d)
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        return (base * torch.from_numpy(mult).to(device)[:, None, :]).to(dt).contiguous()
+    chans = outlier_channels(w, layer) if w.outliers_in_decode else None
+    return torch_activations(w, (steps * B, d), layer, 1, device, chans).view(steps, B, d)
+
+
+def torch_moe_inputs(w: Workload, layers: int, steps: int, device):
+    """Device-drawn inputs of a mixture-of-experts stack: N(0,1) router logits
+    of every layer's prompt [layers, n_tokens, E] and of every decode step
+    [steps, layers, B, E], and the decode inputs [steps, layers, B, D]."""
+    import torch
+    n_tok, E, B, d = w.prompt_batch * w.prompt_len, w.experts, w.decode_batch, w.d
+    gen = torch.Generator(device=device)
+    gen.manual_seed(SEED_ROOT ^ 0x5EED)
+    logits_pre = torch.randn((layers, n_tok, E), generator=gen, device=device, dtype=torch.float32)
+    logits_dec = torch.randn((steps, layers, B, E), generator=gen, device=device, dtype=torch.float32)
+    x = torch_activations(w, (steps * layers * B, d), 0, 1, device).view(steps, layers, B, d)
+    return logits_pre, logits_dec, x
