@@ -524,7 +524,7 @@ def bench_ffn(args, w, mods, L, T, steps, warmup, detail):
     fused = B == 1 and d <= 4 * 256 * vec
     linked = fused and 0 < n_C <= 4096 and k > 0
     labels_pre = (["k_colsq_slices"] if n_tok <= 8192 else ["k_colsq_partial", "k_sum_chunks(s2)"]) + [
-        "k_importance", "k_partition"]
+        "k_importance_items", "k_partition"]
     n_pass = -(-n_tok // 4096)
     labels_ffn = (["k_prompt_gateup", "k_prompt_down"] if e == 2 else
                   ["k_prompt_gateup_f32", "k_prompt_down_f32"]) * n_pass
@@ -659,8 +659,8 @@ def bench_ffn(args, w, mods, L, T, steps, warmup, detail):
     res["kernels_us"] = {n: round(v, 3) for n, v in kus.items()}
     res["kernels_us_default_events"] = {n: round(v, 3) for n, v in kus_fenced.items()}
     imp_bytes = metrics.importance_bytes(n_tok, d, d_ff, e)
-    res["importance_gbps"] = (round(imp_bytes / (kus["k_importance"] * 1e-6) / 1e9, 1)
-                              if "k_importance" in kus else None)
+    res["importance_gbps"] = (round(imp_bytes / (kus["k_importance_items"] * 1e-6) / 1e9, 1)
+                              if "k_importance_items" in kus else None)
     # host copies of layer 0 (as timed: the same device-drawn tensors) for the oracle's spot check
     x_buf.copy_(Xdec[0])
     _, S0 = pop.pop_decode_ffn(x_buf[0], Wg[0], Wu[0], WdT[0], R[0], C[0], w.r, y=y[0], selected=True, ws=ws_dec)

@@ -130,10 +130,12 @@ size_t pop_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff);
  *              pop_partition_counts), each written in ascending order.
  *   importance optional device fp32 [d_ff]: I_i (NULL to skip).
  *   ws         device workspace of at least pop_prefill_workspace_bytes().
- * Kernels: column sum of squares of X (two-stage, fixed order), weighted row
- * norm of W_up, one-workgroup radix select of the two cut keys and an
- * order-preserving compaction.  Deterministic: identical inputs give
- * bit-identical outputs.
+ * Kernels: column sums of squares of X (one pass per column slice, or
+ * partial sums and their fixed-order reduction for long prompts); the weighted
+ * sums of squares of W_up over pieces of each row, in equal shares per wave;
+ * one workgroup that adds each row's pieces in a fixed order, takes I and
+ * splits the rows (histogram select of the two cut keys, ordered compaction).
+ * Deterministic: identical inputs give bit-identical outputs.
  */
 pop_status pop_prefill_partition(const void* X, int64_t n_tokens, int32_t d, const void* W_up,
                                   int32_t d_ff, pop_dtype dt, double r, double gamma, int32_t* R,
@@ -144,8 +146,9 @@ pop_status pop_prefill_partition(const void* X, int64_t n_tokens, int32_t d, con
  * Stages of pop_prefill_partition, callable on their own.
  * ------------------------------------------------------------------------- */
 
-/* Workspace bytes pop_prefill_importance needs. */
-size_t pop_prefill_importance_workspace_bytes(int64_t n_tokens, int32_t d);
+/* Workspace bytes pop_prefill_importance needs (the same as
+ * pop_prefill_workspace_bytes). */
+size_t pop_prefill_importance_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff);
 
 /*
  * pop_prefill_importance — POP notes, "Key design 1", importance equation

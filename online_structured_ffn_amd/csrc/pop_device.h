@@ -61,6 +61,18 @@ __device__ __forceinline__ void mem_wait() {
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+// Workgroup barrier that orders LDS only: each wave waits for its own LDS
+// accesses (lgkmcnt(0); vmcnt and expcnt left at their maxima in the gfx9
+// encoding), then meets the others.  Unlike __syncthreads() it does not wait
+// for the wave's global loads in flight, so loads issued before it stay in
+// flight across it.  Global memory written before it is not made visible to
+// the other waves by it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 // Polls *p (coherent) until pred(value) holds, at most `limit` times, sleeping
 // briefly between polls; returns the last value read and sets ok.
 template <typename T, typename Pred>

@@ -3,12 +3,19 @@
 //   K1  column sum of squares  s2[k] = sum_n X[n,k]^2         (HBM-bound on X)
 //       one pass per column slice for prompts of up to 8192 tokens, else
 //       partial sums over row chunks and (K1r) their fixed-order reduction
-//   K2  importance  I[i] = sqrt(sum_k W_up[i,k]^2 * s2[k])    (HBM-bound on W_up)
-//   K3  one-workgroup radix select of the keys at ranks c_low and c_high and an
-//       order-preserving compaction into P, C, R            (latency-bound)
+//   K2  importance items: sum_k W_up[i,k]^2 * s2[k] over pieces of each row,
+//       in equal shares per wave                              (HBM-bound on W_up)
+//   K3  one workgroup: I[i] = sqrt of the sum of row i's pieces, then the
+//       select of the keys at ranks c_low and c_high and an order-preserving
+//       compaction into P, C, R                               (latency-bound)
+//   (k_importance, one row per wave, serves the per-expert MoE partition.)
 #include <hip/hip_runtime.h>
 
+#include <map>
+#include <mutex>
+
 #include "moe_route.h"
+#include "partition.h"
 #include "pop_device.h"
 #include "pop_internal.h"
 
@@ -260,71 +267,181 @@ __global__ __launch_bounds__(256) void k_importance(const T* __restrict__ W, int
 // ---------------------------------------------------------------- K3
 constexpr int kPartThreads = 1024;
 
-// blockIdx.x selects an expert (MoE): its I and lists follow the previous
-// expert's contiguously; one block otherwise.
-__global__ __launch_bounds__(kPartThreads) void k_partition(const float* __restrict__ I, int n, int c_low, int c_high,
-                                                           int32_t* __restrict__ R, int32_t* __restrict__ C,
-                                                           int32_t* __restrict__ P) {
-  using Sh = SelShared<kPartThreads>;
-  constexpr int EM = Sh::kPerThread;
-  __shared__ Sh sh;
-  I += (int64_t)blockIdx.x * n;
+// One workgroup per split of n channels.  src holds, for channel i, either
+// the importance itself (n_q = 0, src[i * stride]) or the n_q >= 1 item sums
+// of k_importance_items at src[i * stride] (I_i = sqrt of their sum in item
+// order, stored in I_out when it is not NULL).  blockIdx.x selects an expert (MoE), whose
+// values and lists follow the previous expert's contiguously.  do_split = 0:
+// I_out only.  Dynamic LDS: part_lds_bytes<kPartThreads>(n).
+__global__ __launch_bounds__(kPartThreads) void k_partition(const float* __restrict__ src, int n, int n_q, int stride,
+                                                           float* __restrict__ I_out, int c_low, int c_high,
+                                                           int do_split, int32_t* __restrict__ R,
+                                                           int32_t* __restrict__ C, int32_t* __restrict__ P) {
+  extern __shared__ __align__(16) char smem[];
+  uint32_t* keys = reinterpret_cast<uint32_t*>(smem);
+  PartShared<kPartThreads>& sh = *reinterpret_cast<PartShared<kPartThreads>*>(smem + part_keys_bytes<kPartThreads>(n));
+  src += (int64_t)blockIdx.x * n * stride;
   R += (int64_t)blockIdx.x * (n - c_high);
   C += (int64_t)blockIdx.x * (c_high - c_low);
   P += (int64_t)blockIdx.x * c_low;
   if (n <= 0) return;
-  const int E = (n + kPartThreads - 1) / kPartThreads;
-  const int base = threadIdx.x * E;
-  const int cnt = max(0, min(E, n - base));
-  uint32_t v[EM];
-  sel_load_regs(I, n, base, E, v);
-  const int ranks[2] = {c_low, c_high};
-  SelTarget t[2];
-  select_targets<kPartThreads, 2, EM, kSelMaxN>(v, n, base, E, ranks, sh, t);
-  int eqb[2];
-  sel_eq_before<kPartThreads, 2, EM, kSelMaxN>(v, E, cnt, t, sh, eqb);
-  // class of element j: 0 = P (below c_low), 1 = C, 2 = R (not below c_high)
-  auto cls = [&](int j, int& e0, int& e1) {
-    e0 += v[j] == t[0].prefix ? 1 : 0;
-    e1 += v[j] == t[1].prefix ? 1 : 0;
-    if (sel_below(t[0], v[j], t[0].count - e0)) return 0;
-    return sel_below(t[1], v[j], t[1].count - e1) ? 1 : 2;
-  };
-  int pos[3] = {0, 0, 0};
-  {
-    int e0 = eqb[0], e1 = eqb[1];
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  // kPartBatch rows per thread at a time: their loads are in flight together
+  constexpr int kPartBatch = 8;
+  for (int i0 = threadIdx.x; i0 < n; i0 += kPartBatch * kPartThreads) {
+    float v[kPartBatch];
+    if (n_q == 0) {
 #pragma unroll
-    for (int j = 0; j < EM; ++j) {
-      if (j >= E) break;  // block-uniform
-      const int c = cls(j, e0, e1);
-      pos[0] += (j < cnt && c == 0) ? 1 : 0;
-      pos[1] += (j < cnt && c == 1) ? 1 : 0;
-      pos[2] += (j < cnt && c == 2) ? 1 : 0;
-    }
-  }
-  int tot[3];
-  block_exclusive_scan3(pos, tot, sh);
-  // Positions are capped at the list sizes the host derived from the counts;
-  // an exact select never reaches the caps.
-  const int n_P = c_low, n_C = c_high - c_low, n_R = n - c_high;
-  int e0 = eqb[0], e1 = eqb[1];
+      for (int t = 0; t < kPartBatch; ++t) v[t] = src[(int64_t)min(i0 + t * kPartThreads, n - 1) * stride];
+    } else if (n_q == 4 && stride == 4) {
+      float4 q[kPartBatch];
 #pragma unroll
-  for (int j = 0; j < EM; ++j) {
-    if (j >= E) break;  // block-uniform
-    if (j < cnt) {
-      const int i = base + j;
-      const int c = cls(j, e0, e1);
-      if (c == 0) {
-        if (pos[0] < n_P) P[pos[0]] = i;
-        ++pos[0];
-      } else if (c == 1) {
-        if (pos[1] < n_C) C[pos[1]] = i;
-        ++pos[1];
-      } else {
-        if (pos[2] < n_R) R[pos[2]] = i;
-        ++pos[2];
+      for (int t = 0; t < kPartBatch; ++t)
+        q[t] = *reinterpret_cast<const float4*>(src + (int64_t)min(i0 + t * kPartThreads, n - 1) * 4);
+#pragma unroll
+      for (int t = 0; t < kPartBatch; ++t) v[t] = sqrtf(((q[t].x + q[t].y) + q[t].z) + q[t].w);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kPartBatch; ++t) {
+        const float* p = src + (int64_t)min(i0 + t * kPartThreads, n - 1) * stride;
+        float a = 0.f;
+        for (int k = 0; k < n_q; ++k) a += p[k];
+        v[t] = sqrtf(a);
       }
     }
+#pragma unroll
+    for (int t = 0; t < kPartBatch; ++t) {
+      const int i = i0 + t * kPartThreads;
+      if (i < n) {
+        if (n_q != 0 && I_out != nullptr) I_out[(int64_t)blockIdx.x * n + i] = v[t];
+        const uint32_t u = value_bits(v[t]);
+        keys[i] = u;
+        mn = min(mn, u);
+        mx = max(mx, u);
+      }
+    }
+  }
+  if (do_split) partition_block<kPartThreads>(keys, n, mn, mx, c_low, c_high, R, C, P, sh);
+}
+
+// ---------------------------------------------------------------- K2, balanced
+// k_importance_items: the weighted row norms in equal shares.  An item is
+// kImpItemLoads 16-byte vectors per lane of one row (QC columns); the d_ff *
+// n_q items are dealt to the gridDim.x * 16 waves in equal consecutive shares
+// (a row's items may fall to two waves), so no wave waits on a longer share.
+// Each wave issues its first chunk of W_up loads before staging s2 in LDS;
+// the next chunk is in flight while the current one is reduced.  Each item's
+// weighted sum of squares goes to ipart[row * n_qp + item]; k_partition adds
+// a row's items in item order.
+constexpr int kItemThreads = 1024;
+constexpr int kItemWaves = kItemThreads / 64;
+constexpr int kImpItemLoads = 2;  // 16-byte loads per lane per item
+constexpr int kImpChunk = 4;      // items per buffer
+
+template <typename T>
+__host__ __device__ constexpr int item_cols() {
+  return kImpItemLoads * 64 * Vec<T>::N;
+}
+__host__ __device__ inline int items_per_row(int d, int qc) { return (d + qc - 1) / qc; }
+__host__ __device__ inline int items_stride(int n_q) { return (n_q + 3) & ~3; }
+
+template <typename T>
+__global__ __launch_bounds__(kItemThreads) void k_importance_items(const T* __restrict__ W, int d_ff, int d,
+                                                                  const float* __restrict__ s2,
+                                                                  float* __restrict__ ipart, int n_qp) {
+  constexpr int V = Vec<T>::N;
+  constexpr int QC = item_cols<T>();
+  constexpr int NL = kImpChunk * kImpItemLoads;
+  extern __shared__ __align__(16) float s2l[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_q = items_per_row(d, QC);
+  const int64_t Q = (int64_t)d_ff * n_q;
+  const int64_t NWv = (int64_t)gridDim.x * kItemWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kItemWaves + wave;
+  const int i0 = (int)(Q * gw / NWv);
+  const int n_it = (int)(Q * (gw + 1) / NWv - i0);
+  const int n_ch = (n_it + kImpChunk - 1) / kImpChunk;
+  auto issue = [&](u32x4(&q)[NL], int ch) {
+#pragma unroll
+    for (int u = 0; u < kImpChunk; ++u) {
+      const int it = i0 + min(ch * kImpChunk + u, n_it - 1);  // past the share: its last item again (unused)
+      const int row = it / n_q, qq = it % n_q;
+      const T* w = W + (int64_t)row * d;
+#pragma unroll
+      for (int l = 0; l < kImpItemLoads; ++l)
+        q[u * kImpItemLoads + l] = ld16_stream(w + min(qq * QC + l * 64 * V + lane * V, d - V));
+    }
+  };
+  auto consume = [&](const u32x4(&q)[NL], int ch) {
+#pragma unroll
+    for (int u = 0; u < kImpChunk; ++u) {
+      const int k = ch * kImpChunk + u;
+      if (k >= n_it) break;  // wave-uniform
+      const int it = i0 + k;
+      const int row = it / n_q, qq = it % n_q;
+      float acc = 0.f;
+#pragma unroll
+      for (int l = 0; l < kImpItemLoads; ++l) {
+        float f[V];
+        unpack(q[u * kImpItemLoads + l], f, T{});
+        const float* sp = s2l + qq * QC + l * 64 * V + lane * 4;
+#pragma unroll
+        for (int g = 0; g < V / 4; ++g) {
+          const float4 q4 = *reinterpret_cast<const float4*>(sp + g * 256);
+          acc = fmaf(f[4 * g] * f[4 * g], q4.x, acc);
+          acc = fmaf(f[4 * g + 1] * f[4 * g + 1], q4.y, acc);
+          acc = fmaf(f[4 * g + 2] * f[4 * g + 2], q4.z, acc);
+          acc = fmaf(f[4 * g + 3] * f[4 * g + 3], q4.w, acc);
+        }
+      }
+      const float t = wave_sum(acc);
+      if (lane == 0) ipart[(int64_t)row * n_qp + qq] = t;
+    }
+  };
+  // s2 in LDS, zero-padded to whole items; within each run of 64 * V columns
+  // (one load instruction of a wave) lane l's V values sit as V / 4 float4
+  // groups at (group * 64 + l) * 4: the reads above are 16 bytes per lane
+  // with consecutive lanes 16 bytes apart.  Staged 16 bytes at a time (four
+  // consecutive columns land in one float4 group; d is a multiple of 4).  The
+  // s2 loads go out before the first W_up chunk's: loads return in issue
+  // order, and the staging waits only for its own.
+  constexpr int kS2Per = 4;  // float4 loads of s2 per thread in flight (n_q * QC <= kS2Per * 4 * 1024 here)
+  const int n4 = n_q * QC / 4;
+  float4 s2q[kS2Per];
+#pragma unroll
+  for (int r = 0; r < kS2Per; ++r) {
+    const int k = 4 * ((int)threadIdx.x + r * kItemThreads);
+    s2q[r] = k < d ? *reinterpret_cast<const float4*>(s2 + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  u32x4 A[NL], B[NL];
+  if (n_it > 0) issue(A, 0);  // wave-uniform; in flight while s2 is staged
+#pragma unroll
+  for (int r = 0; r < kS2Per; ++r) {
+    const int k4 = (int)threadIdx.x + r * kItemThreads;
+    if (k4 < n4) {
+      const int k = 4 * k4;
+      const int run = k / (64 * V), l = (k / V) % 64, v = k % V;
+      *reinterpret_cast<float4*>(s2l + run * 64 * V + ((v / 4) * 64 + l) * 4) = s2q[r];
+    }
+  }
+  // wider rows: the rest of s2, in order after the chunk
+  for (int k4 = (int)threadIdx.x + kS2Per * kItemThreads; k4 < n4; k4 += kItemThreads) {
+    const int k = 4 * k4;
+    const int run = k / (64 * V), l = (k / V) % 64, v = k % V;
+    const float4 q = k < d ? *reinterpret_cast<const float4*>(s2 + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(s2l + run * 64 * V + ((v / 4) * 64 + l) * 4) = q;
+  }
+  lds_barrier();  // the first chunk's loads stay in flight
+  for (int ch = 0; ch < n_ch; ch += 2) {  // wave-uniform
+    if (ch + 1 < n_ch) issue(B, ch + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(A, ch);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ch + 2 < n_ch) issue(A, ch + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ch + 1 < n_ch) consume(B, ch + 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -392,12 +509,49 @@ static float* launch_colsq_t(hipStream_t st, const void* X, int64_t n_tokens, in
   return s2;
 }
 
+
+// ---- the partition of one FFN: column norms, importance items, split
+// Workspace of pop_prefill_partition / pop_prefill_importance: the column-norm
+// workspace (partial sums, then s2), then the item sums [d_ff][stride].
+static size_t pre_ws_bytes(int64_t n_tokens, int32_t d, int32_t d_ff) {
+  // fp32 items are half as wide as bf16 ones: the larger stride
+  const int stride = items_stride(items_per_row(d, item_cols<float>()));
+  return importance_ws_bytes(n_tokens, d) + align_up((size_t)d_ff * stride * sizeof(float), 256);
+}
+
+static int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cache[dev] = cus;
+}
+
+// s2, then the item sums, then k_partition (split = false: I only, into I).
 template <typename T>
-static void launch_importance(hipStream_t st, const void* X, int64_t n_tokens, int32_t d, const void* W_up,
-                              int32_t d_ff, float* I, char* ws) {
+static void launch_prefill(hipStream_t st, const void* X, int64_t n_tokens, int32_t d, const void* W_up, int32_t d_ff,
+                           int c_low, int c_high, bool split, int32_t* R, int32_t* C, int32_t* P, float* I,
+                           char* ws) {
   const float* s2 = launch_colsq_t<T>(st, X, n_tokens, d, ws);
-  POP_LAUNCH(k_importance<T>, dim3(imp_blocks(d_ff)), dim3(256), imp_lds_bytes<T>(d), st, (const T*)W_up, d_ff, d,
-             s2, I);
+  float* ipart = (float*)(ws + importance_ws_bytes(n_tokens, d));
+  const int n_q = items_per_row(d, item_cols<T>());
+  const int stride = items_stride(n_q);
+  const int64_t items = (int64_t)d_ff * n_q;
+  // one workgroup per CU, fewer when there are under two items per wave
+  int64_t G = device_cus();
+  const int64_t want = (items + 2 * kItemWaves - 1) / (2 * kItemWaves);
+  if (G < 1 || G > want) G = want;
+  if (G < 1) G = 1;
+  const size_t lds = (size_t)n_q * item_cols<T>() * sizeof(float);
+  POP_LAUNCH(k_importance_items<T>, dim3((unsigned)G), dim3(kItemThreads), lds, st, (const T*)W_up, d_ff, d, s2,
+             ipart, stride);
+  POP_LAUNCH(k_partition, dim3(1), dim3(kPartThreads), part_lds_bytes<kPartThreads>(d_ff), st, (const float*)ipart,
+             d_ff, n_q, stride, I, c_low, c_high, split ? 1 : 0, R, C, P);
 }
 
 size_t colsq_ws_bytes(int64_t n_tokens, int32_t d) { return importance_ws_bytes(n_tokens, d); }
@@ -409,7 +563,8 @@ float* launch_colsq(void* stream, const void* X, int64_t n_tokens, int32_t d, po
 
 void launch_partition_lists(void* stream, const float* I, int32_t d_ff, int32_t c_low, int32_t c_high, int32_t* R,
                             int32_t* C, int32_t* P) {
-  POP_LAUNCH(k_partition, dim3(1), dim3(kPartThreads), 0, (hipStream_t)stream, I, d_ff, c_low, c_high, R, C, P);
+  POP_LAUNCH(k_partition, dim3(1), dim3(kPartThreads), part_lds_bytes<kPartThreads>(d_ff), (hipStream_t)stream, I,
+             d_ff, 0, 1, (float*)nullptr, c_low, c_high, 1, R, C, P);
 }
 
 // ---- MoE prefill
@@ -477,7 +632,8 @@ static void launch_moe_prefill(hipStream_t st, const void* X, int64_t n_tokens, 
              0);
   POP_LAUNCH(k_importance<T>, dim3(imp_blocks(d_ff), E), dim3(256), imp_lds_bytes<T>(d), st, (const T*)W_up,
              d_ff, d, (const float*)w.s2, I);
-  POP_LAUNCH(k_partition, dim3(E), dim3(kPartThreads), 0, st, (const float*)I, d_ff, c.c_low, c.c_high, R, C, P);
+  POP_LAUNCH(k_partition, dim3(E), dim3(kPartThreads), part_lds_bytes<kPartThreads>(d_ff), st, (const float*)I, d_ff,
+             0, 1, (float*)nullptr, c.c_low, c.c_high, 1, R, C, P);
 }
 
 static pop_status launched() {
@@ -503,14 +659,14 @@ static pop_status check_importance_args(const void* X, int64_t n_tokens, int32_t
 
 using namespace pop;
 
-extern "C" size_t pop_prefill_importance_workspace_bytes(int64_t n_tokens, int32_t d) {
-  if (n_tokens < 0 || d <= 0) return 0;
-  return importance_ws_bytes(n_tokens, d);
+extern "C" size_t pop_prefill_importance_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff) {
+  if (n_tokens < 0 || d <= 0 || d_ff <= 0) return 0;
+  return pre_ws_bytes(n_tokens, d, d_ff);
 }
 
 extern "C" size_t pop_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff) {
   if (n_tokens < 0 || d <= 0 || d_ff <= 0) return 0;
-  return importance_ws_bytes(n_tokens, d) + align_up((size_t)d_ff * sizeof(float), 256);
+  return pre_ws_bytes(n_tokens, d, d_ff);
 }
 
 extern "C" pop_status pop_prefill_importance(const void* X, int64_t n_tokens, int32_t d, const void* W_up,
@@ -521,13 +677,16 @@ extern "C" pop_status pop_prefill_importance(const void* X, int64_t n_tokens, in
   if (s != POP_OK) return s;
   if (importance == nullptr || ws == nullptr) return fail(POP_ERR_INVALID_ARGUMENT, "importance and ws must be non-NULL");
   if (!aligned16(ws)) return fail(POP_ERR_MISALIGNED, "ws must be 16-byte aligned");
-  const size_t need = importance_ws_bytes(n_tokens, d);
+  const size_t need = pre_ws_bytes(n_tokens, d, d_ff);
   if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
-  trace_mark(stream);
+  hipStream_t st = (hipStream_t)stream;
+  trace_mark(st);
   if (dt == POP_BF16)
-    launch_importance<bf16s>((hipStream_t)stream, X, n_tokens, d, W_up, d_ff, importance, (char*)ws);
+    launch_prefill<bf16s>(st, X, n_tokens, d, W_up, d_ff, 0, 0, false, nullptr, nullptr, nullptr, importance,
+                          (char*)ws);
   else
-    launch_importance<float>((hipStream_t)stream, X, n_tokens, d, W_up, d_ff, importance, (char*)ws);
+    launch_prefill<float>(st, X, n_tokens, d, W_up, d_ff, 0, 0, false, nullptr, nullptr, nullptr, importance,
+                          (char*)ws);
   return launched();
 }
 
@@ -542,8 +701,8 @@ extern "C" pop_status pop_partition_select(const float* importance, int32_t d_ff
       (c.n_P > 0 && P == nullptr))
     return fail(POP_ERR_INVALID_ARGUMENT, "importance or an output list with a nonzero size is NULL");
   trace_mark(stream);
-  POP_LAUNCH(k_partition, dim3(1), dim3(kPartThreads), 0, (hipStream_t)stream, importance, d_ff, c.c_low,
-                     c.c_high, R, C, P);
+  POP_LAUNCH(k_partition, dim3(1), dim3(kPartThreads), part_lds_bytes<kPartThreads>(d_ff), (hipStream_t)stream,
+             importance, d_ff, 0, 1, (float*)nullptr, c.c_low, c.c_high, 1, R, C, P);
   return launched();
 }
 
@@ -560,18 +719,14 @@ extern "C" pop_status pop_prefill_partition(const void* X, int64_t n_tokens, int
     return fail(POP_ERR_INVALID_ARGUMENT, "ws or an output list with a nonzero size is NULL");
   if (!aligned16(ws) || !aligned16(importance))
     return fail(POP_ERR_MISALIGNED, "importance and ws must be 16-byte aligned");
-  const size_t need = pop_prefill_workspace_bytes(n_tokens, d, d_ff);
+  const size_t need = pre_ws_bytes(n_tokens, d, d_ff);
   if (ws_bytes < need) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
-  const size_t iw = importance_ws_bytes(n_tokens, d);
-  float* I = importance ? importance : (float*)((char*)ws + iw);
   hipStream_t st = (hipStream_t)stream;
   trace_mark(st);
   if (dt == POP_BF16)
-    launch_importance<bf16s>(st, X, n_tokens, d, W_up, d_ff, I, (char*)ws);
+    launch_prefill<bf16s>(st, X, n_tokens, d, W_up, d_ff, c.c_low, c.c_high, true, R, C, P, importance, (char*)ws);
   else
-    launch_importance<float>(st, X, n_tokens, d, W_up, d_ff, I, (char*)ws);
-  POP_LAUNCH(k_partition, dim3(1), dim3(kPartThreads), 0, st, (const float*)I, d_ff, c.c_low, c.c_high, R, C,
-                     P);
+    launch_prefill<float>(st, X, n_tokens, d, W_up, d_ff, c.c_low, c.c_high, true, R, C, P, importance, (char*)ws);
   return launched();
 }
 

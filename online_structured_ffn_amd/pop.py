@@ -65,7 +65,7 @@ def _load():
                                                 _c_vp, _c_vp, _c_size, _c_vp]),
         "pop_decode_ffn_noalloc": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, ctypes.c_int,
                                                   _c_vp, _c_i32, _c_vp, _c_i32, _c_dbl, _c_vp, _c_vp, _c_vp]),
-        "pop_prefill_importance_workspace_bytes": (_c_size, [_c_i64, _c_i32]),
+        "pop_prefill_importance_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32]),
         "pop_prefill_importance": (ctypes.c_int, [_c_vp, _c_i64, _c_i32, _c_vp, _c_i32, ctypes.c_int, _c_vp, _c_vp,
                                                   _c_size, _c_vp]),
         "pop_partition_select": (ctypes.c_int, [_c_vp, _c_i32, _c_dbl, _c_dbl, _c_vp, _c_vp, _c_vp, _c_vp]),
@@ -436,7 +436,7 @@ def pop_prefill_importance(X, W_up, *, out=None, ws=None, stream=None):
     d_ff = W_up.shape[0]
     I = torch.empty(d_ff, dtype=torch.float32, device=W_up.device) if out is None else out
     if ws is None:
-        ws = workspace(lib.pop_prefill_importance_workspace_bytes(n_tokens, d), W_up.device)
+        ws = workspace(lib.pop_prefill_importance_workspace_bytes(n_tokens, d, d_ff), W_up.device)
     _check("pop_prefill_importance", lib.pop_prefill_importance(
         _ptr(X), n_tokens, d, _ptr(W_up), d_ff, _dtype(W_up), _ptr(I), _ptr(ws), ws.numel(), _stream(stream)))
     return I

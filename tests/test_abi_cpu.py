@@ -215,7 +215,7 @@ def test_fused_prefill_workspace_sizes():
                            (9000, 136, 300, "bf16")):
         # the prompt FFN's Z buffer, the column-norm workspace and I
         assert f(n, d, d_ff, dt) >= (pop.pop_dense_ffn_prefill_workspace_bytes(n, d, d_ff, dt)
-                                     + pop.lib.pop_prefill_importance_workspace_bytes(n, d) + 4 * d_ff)
+                                     + 4 * d + 4 * d_ff)
     assert pop.lib.pop_prefill_ffn_partition_workspace_bytes(-1, 256, 688, 1) == 0
     assert pop.lib.pop_prefill_ffn_partition_workspace_bytes(5, 256, 688, 9) == 0
 

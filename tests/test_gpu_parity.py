@@ -101,6 +101,43 @@ def test_partition_deterministic():
             assert torch.equal(a, b)
 
 
+def test_partition_graph_replay_shared_workspace():
+    """Replays of a captured partition (with calls of other shapes on the same
+    workspace between them) give the eager outputs bit for bit."""
+    say("[partition] graph replays on a shared workspace")
+    shapes = [(700, 1024, 3001, 0.3, 0.1), (37, 264, 1000, 0.5, 0.2), (4096, 4096, 11008, 0.299, 0.1)]
+    cases = []
+    for i, (n, d, d_ff, r, g) in enumerate(shapes):
+        c = synth.random_case(60 + i, n, d, d_ff, 1, "bf16")
+        cases.append((dev(c["X"], "bf16"), dev(c["W_up"], "bf16"), r, g))
+    ws = pop.workspace(max(pop.pop_prefill_workspace_bytes(n, d, d_ff) for n, d, d_ff, _, _ in shapes))
+    eager = [pop.pop_prefill_partition(X, W, r, g, importance=True, ws=ws) for X, W, r, g in cases]
+    torch.cuda.synchronize()
+    outs = tuple(torch.empty_like(t) for t in eager[0])
+    X0, W0, r0, g0_ = cases[0]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pop.pop_prefill_partition(X0, W0, r0, g0_, out=outs, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pop.pop_prefill_partition(X0, W0, r0, g0_, out=outs, ws=ws)
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager[0]):
+            assert torch.equal(a, b), f"replay {rep} differs from eager"
+        X, W, r, g = cases[1 + rep % 2]
+        o = pop.pop_prefill_partition(X, W, r, g, importance=True, ws=ws)
+        torch.cuda.synchronize()
+        for a, b in zip(o, eager[1 + rep % 2]):
+            assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------------ decode
 def _decode_case(X, x_steps, w, dtype, r, gamma, label):
     Xd = dev(X, dtype)
