@@ -621,9 +621,9 @@ def bench_ffn(args, w, mods, L, T, steps, warmup, detail):
             "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
             "traffic": None if tb is None else tb[0] + tb[1],
             "traffic_source": (None if tb is None else
-                               "rocprofv3 FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by the same counter's "
-                               "reading for a plain device copy in the same session "
-                               "(profiles/decode_kernels_llama2_7b_b1_hbm_traffic.md)"),
+                               "rocprofv3 L2-to-memory read and write requests per dispatch (every L2 instance), "
+                               "checked against a stream-read probe and a fill of known size in the same passes "
+                               "(profiles/ffn_kernels_llama2_7b_b1_hbm_traffic.md)"),
             "bytes_per_launch": dom_bytes,
             "avg_launch_us": round(dom_us, 3),
             "achieved_vs_read_probe": None,
@@ -1087,9 +1087,9 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
             "frac": None if dom_gbps is None else round(dom_gbps / HBM_PEAK_GBPS, 4),
             "traffic": None if tb is None else tb[0] + tb[1],
             "traffic_source": (None if tb is None else
-                               "rocprofv3 FETCH_SIZE + WRITE_SIZE per dispatch of the same kernel at the same shape "
-                               "in the FFN workload, scaled by a 256 MiB copy "
-                               "(profiles/decode_kernels_llama2_7b_b1_hbm_traffic.md)"),
+                               "rocprofv3 L2-to-memory read and write requests per dispatch of the same kernel at "
+                               "the same shape in the FFN workload "
+                               "(profiles/ffn_kernels_llama2_7b_b1_hbm_traffic.md)"),
             "bytes_per_launch": None if dom is None else round(kbytes[dom]),
             "avg_launch_us": None if dom is None else round(kus[dom], 3),
         },

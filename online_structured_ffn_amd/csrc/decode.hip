@@ -516,11 +516,7 @@ template <typename T, int NV, bool kIdentity, int PHASE>
 __global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
   static_assert(PHASE >= 0 && PHASE <= 2, "phases 0, 1, 2");
   constexpr int V = Vec<T>::N;
-#ifdef POP_STEP_SELSHARED_ALL
-  using SelT = SelShared<kFusedThreads, kFusedTopkMaxN>;
-#else
   using SelT = typename std::conditional<PHASE == 2, SelShared<kFusedThreads, kFusedTopkMaxN>, NoSel>::type;
-#endif
   __shared__ SelT sh_sel;
   __shared__ int rows[kFusedMaxRows];
   __shared__ float part[2][kFusedWaves][2 * kFusedP];
