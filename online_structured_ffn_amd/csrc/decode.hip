@@ -15,6 +15,7 @@
 #include <utility>
 
 #include "decode_mfma.h"
+#include "partition.h"
 #include "pop_device.h"
 #include "pop_internal.h"
 
@@ -121,14 +122,15 @@ __global__ __launch_bounds__(256) void k_gateup(const T* __restrict__ x, int B, 
 }
 
 // ---------------------------------------------------------------- K5
-// The candidate top-k as its own one-workgroup launch (topk_block).
+// The candidate top-k as its own one-workgroup launch (topk_select; dynamic
+// LDS topk_lds_bytes<kTopkThreads>(n)).
 constexpr int kTopkThreads = 1024;
 
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ score, int n, int k,
                                                        const int32_t* __restrict__ C, int32_t* __restrict__ positions,
                                                        int32_t* __restrict__ selected) {
-  __shared__ SelShared<kTopkThreads> sh;
-  topk_block(score, n, k, C, positions, selected, sh);
+  extern __shared__ __align__(16) unsigned char topk_smem[];
+  topk_select<kTopkThreads>(score, n, k, C, positions, selected, topk_smem);
 }
 
 // ---------------------------------------------------------------- fused decode step (batch 1)
@@ -1153,7 +1155,9 @@ static void launch_gateup(hipStream_t st, const void* x, int B, int d, const voi
 
 static void launch_select(hipStream_t st, const float* score, int n_C, const int32_t* C, int k, int32_t* Q,
                           int32_t* selected) {
-  if (n_C > 0) POP_LAUNCH(k_topk, dim3(1), dim3(kTopkThreads), 0, st, score, n_C, k, C, Q, selected);
+  if (n_C > 0)
+    POP_LAUNCH(k_topk, dim3(1), dim3(kTopkThreads), topk_lds_bytes<kTopkThreads>(n_C), st, score, n_C, k, C, Q,
+               selected);
 }
 
 // The down-projection over the live rows (R, then the selected rows).  With

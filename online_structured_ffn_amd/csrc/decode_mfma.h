@@ -17,6 +17,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include "partition.h"
 #include "pop_device.h"
 
 namespace pop {
@@ -347,8 +348,8 @@ __global__ __launch_bounds__(256) void k_down_stream(const float* __restrict__ z
                                                      const int32_t* __restrict__ C, int32_t* __restrict__ Q,
                                                      int32_t* __restrict__ S, MoeRows moe = {}) {
   using DS = DsShared<MT>;
-  using TS = SelShared<256, 4096>;
-  constexpr size_t kSmem = sizeof(DS) > (PHASE == 1 ? sizeof(TS) : 0) ? sizeof(DS) : sizeof(TS);
+  constexpr size_t kTs = PHASE == 1 ? topk_lds_bytes<256>(4096) : 0;  // the top-k block (up to 4096 candidates)
+  constexpr size_t kSmem = sizeof(DS) > kTs ? sizeof(DS) : kTs;
   __shared__ __align__(16) unsigned char smem[kSmem];
   int o0 = 0, cnt = B;  // the launch's z rows: all B, or the expert's routed pairs (B = every pair)
   if constexpr (kMoe) {
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(256) void k_down_stream(const float* __restrict__ z
   }
   if constexpr (PHASE == 1) {
     if ((int)blockIdx.x < nb0) {
-      topk_block(score, n_C, k, C, Q, S, *reinterpret_cast<TS*>(smem));
+      topk_select<256>(score, n_C, k, C, Q, S, smem);
       return;
     }
   }
@@ -476,7 +477,11 @@ __global__ __launch_bounds__(256) void k_down_stream(const float* __restrict__ z
     if constexpr (decltype(issuec)::value) issue(i + kDsNS - 1, ring[(j + kDsNS - 1) % kDsNS]);
     __builtin_amdgcn_sched_barrier(0);
     put(i, ring[j], j & 1);
-    __syncthreads();
+    // LDS only: the later sub-chunks' loads stay in flight across it (a
+    // workgroup-release barrier would wait for all of them at every step).
+    // The buffer put(i + 1) writes was last read by compute(i - 1), which
+    // every wave finished before this barrier of step i.
+    lds_barrier();
     compute(j & 1);
   };
   static_assert(kDsNS % 2 == 0, "the LDS buffer of step i is i & 1 = j & 1");

@@ -122,10 +122,11 @@ template <int MAXN, int NTH>
 __global__ __launch_bounds__(NTH) void k_moe_topk(const float* __restrict__ score, int n_C, int k,
                                                   const int32_t* __restrict__ C, const int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ Q, int32_t* __restrict__ S) {
-  __shared__ SelShared<NTH, MAXN> sh;
+  extern __shared__ __align__(16) unsigned char topk_smem[];  // topk_lds_bytes<NTH>(n_C)
   const int e = blockIdx.x;
   if (offsets[e + 1] == offsets[e]) return;
-  topk_block(score + (int64_t)e * n_C, n_C, k, C + (int64_t)e * n_C, Q + (int64_t)e * k, S + (int64_t)e * k, sh);
+  topk_select<NTH>(score + (int64_t)e * n_C, n_C, k, C + (int64_t)e * n_C, Q + (int64_t)e * k, S + (int64_t)e * k,
+                   topk_smem);
 }
 
 // ---------------------------------------------------------------- down
@@ -359,8 +360,8 @@ static void launch_moe_decode_mfma(hipStream_t st, const void* x, int Tn, int d,
   const int usedR = nRc > 0 ? (n_R + rpcR - 1) / rpcR : 0, usedS = nSc > 0 ? (k + rpcS - 1) / rpcS : 0;
   const bool topk = n_C > 0 && k > 0, topk_in = topk && n_C <= 4096;
   if (topk && !topk_in)
-    POP_LAUNCH((k_moe_topk<kSelMaxN, 1024>), dim3(E), dim3(1024), 0, st, (const float*)w.score, n_C, k, C,
-               (const int32_t*)w.offsets, w.Q, S);
+    POP_LAUNCH((k_moe_topk<kSelMaxN, 1024>), dim3(E), dim3(1024), topk_lds_bytes<1024>(n_C), st,
+               (const float*)w.score, n_C, k, C, (const int32_t*)w.offsets, w.Q, S);
   const int nb0 = topk_in ? 1 : 0;
   if (nb0 + usedR > 0)
     POP_LAUNCH((k_down_stream<MT, false, 1, true>), dim3(nb0 + ncol * usedR, E), dim3(256), 0, st,
@@ -399,11 +400,11 @@ static void launch_moe_decode(hipStream_t st, const void* x, int Tn, int d, cons
                (const T*)Wu, d_ff, R, n_R, C, n_C, (const int32_t*)w.offsets, (const int32_t*)w.tokens, w.z, w.score);
   if (n_C > 0 && k > 0) {
     if (n_C <= 4096)
-      POP_LAUNCH((k_moe_topk<4096, 256>), dim3(E), dim3(256), 0, st, (const float*)w.score, n_C, k, C,
-                 (const int32_t*)w.offsets, w.Q, S);
+      POP_LAUNCH((k_moe_topk<4096, 256>), dim3(E), dim3(256), topk_lds_bytes<256>(n_C), st, (const float*)w.score,
+                 n_C, k, C, (const int32_t*)w.offsets, w.Q, S);
     else
-      POP_LAUNCH((k_moe_topk<kSelMaxN, 1024>), dim3(E), dim3(1024), 0, st, (const float*)w.score, n_C, k, C,
-                 (const int32_t*)w.offsets, w.Q, S);
+      POP_LAUNCH((k_moe_topk<kSelMaxN, 1024>), dim3(E), dim3(1024), topk_lds_bytes<1024>(n_C), st,
+                 (const float*)w.score, n_C, k, C, (const int32_t*)w.offsets, w.Q, S);
   }
   const int n_live = n_R + k;
   const MoeDownPlan p = plan_moe_down(n_live, d, E, Vec<T>::N);

@@ -39,10 +39,11 @@ constexpr int kPartUnroll = 4;     // steps per pass iteration (independent LDS 
 template <int NTH>
 struct PartShared {
   static constexpr int kWaves = NTH / 64;
-  static_assert(2 * kPartResolve <= NTH, "one thread per gathered key of each cut");
+  // keys of a bin resolved directly: one thread per key of each cut
+  static constexpr int kRes = NTH / 2 < kPartResolve ? NTH / 2 : kPartResolve;
   unsigned int hist[kSelSlots];
-  __align__(16) uint32_t rv[2][kPartResolve];  // the keys of each cut's small bin (values, channels)
-  __align__(16) int ri[2][kPartResolve];
+  __align__(16) uint32_t rv[2][kRes];  // the keys of each cut's small bin (values, channels)
+  __align__(16) int ri[2][kRes];
   int rcnt[2];
   uint32_t red[kWaves][2];
   int scan[kWaves][4];
@@ -165,13 +166,14 @@ __device__ __forceinline__ void part_take_bin(PartCut& c, const uint32_t (&tb)[4
 }
 
 // Resolves the cuts whose bins hold more than one value (at most
-// kPartResolve keys each): one gather of both bins' keys, then every gathered
-// key ranks itself against the others of its bin (cut 0 on threads
-// [0, kPartResolve), cut 1 on [NTH / 2, NTH / 2 + kPartResolve)).  A cut whose
-// bin holds one value is complete without it.  sh.rcnt must be zero on entry.
+// PartShared::kRes keys each): one gather of both bins' keys, then every
+// gathered key ranks itself against the others of its bin (cut 0 on threads
+// [0, kRes), cut 1 on [NTH / 2, NTH / 2 + kRes)).  A cut whose bin holds one
+// value is complete without it.  sh.rcnt must be zero on entry.
 template <int NTH>
 __device__ __forceinline__ void part_resolve(const uint32_t* __restrict__ keys, int n, int jw, int base, PartCut& c0,
                                              PartCut& c1, PartShared<NTH>& sh) {
+  constexpr int kRes = PartShared<NTH>::kRes;
   const int tid = threadIdx.x;
   const bool g0 = !c0.beyond && c0.lo != c0.hi;
   const bool g1 = !c1.beyond && c1.lo != c1.hi;
@@ -189,14 +191,14 @@ __device__ __forceinline__ void part_resolve(const uint32_t* __restrict__ keys, 
   part_pass<NTH>(keys, n, jw, base, [&](int, int idx, bool ok, uint32_t u) {
     if (ok && g0 && u >= c0.lo && u <= c0.hi) {
       const int slot = atomicAdd(&sh.rcnt[0], 1);
-      if (slot < kPartResolve) {
+      if (slot < kRes) {
         sh.rv[0][slot] = u;
         sh.ri[0][slot] = idx;
       }
     }
     if (ok && g1 && u >= c1.lo && u <= c1.hi) {
       const int slot = atomicAdd(&sh.rcnt[1], 1);
-      if (slot < kPartResolve) {
+      if (slot < kRes) {
         sh.rv[1][slot] = u;
         sh.ri[1][slot] = idx;
       }
@@ -205,7 +207,7 @@ __device__ __forceinline__ void part_resolve(const uint32_t* __restrict__ keys, 
   __syncthreads();
   // neutral padding up to a multiple of 4 (a value above every key counts in
   // none of the sums below)
-  const int m0 = g0 ? min(c0.cnt, kPartResolve) : 0, m1 = g1 ? min(c1.cnt, kPartResolve) : 0;
+  const int m0 = g0 ? min(c0.cnt, kRes) : 0, m1 = g1 ? min(c1.cnt, kRes) : 0;
   const int p0 = (m0 + 3) & ~3, p1 = (m1 + 3) & ~3;
   if (tid < p0 - m0) {
     sh.rv[0][m0 + tid] = 0xffffffffu;
@@ -265,11 +267,9 @@ __device__ __forceinline__ bool part_below(const PartCut& c, uint32_t u, int eq_
 // (n - c_high), C (c_high - c_low), P (c_low) entries.  The first barrier
 // below orders the caller's stores of keys.  Ends with a barrier-free store
 // phase: keys and sh may be reused only after a barrier.
-template <int NTH>
-__device__ __forceinline__ void partition_block(const uint32_t* __restrict__ keys, int n, uint32_t mn, uint32_t mx,
-                                                int c_low, int c_high, int32_t* __restrict__ R,
-                                                int32_t* __restrict__ C, int32_t* __restrict__ P,
-                                                PartShared<NTH>& sh) {
+template <int NTH, typename Emit>
+__device__ __forceinline__ void split_block(const uint32_t* __restrict__ keys, int n, uint32_t mn, uint32_t mx,
+                                            int c_low, int c_high, Emit&& emit, PartShared<NTH>& sh) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int jw = (n + NTH - 1) / NTH;
@@ -306,13 +306,14 @@ __device__ __forceinline__ void partition_block(const uint32_t* __restrict__ key
     if (!c0.beyond) part_take_bin(c0, sh.tb[0]);
     if (!c1.beyond) part_take_bin(c1, sh.tb[nr - 1]);
   }
-  // a bin of more than kPartResolve keys and more than one value is narrowed
-  // by further rounds: at most two per cut (a first-round bin spans at most
+  // a bin of more than kRes keys and more than one value is narrowed by
+  // further rounds: at most two per cut (a first-round bin spans at most
   // 2^19 values, a second-round bin at most 2^7, a third-round bin one value)
+  constexpr int kRes = PartShared<NTH>::kRes;
 #pragma unroll 1
   for (int it = 0; it < 4; ++it) {  // block-uniform
-    const bool n0 = !c0.beyond && c0.lo != c0.hi && c0.cnt > kPartResolve;
-    const bool n1 = !c1.beyond && c1.lo != c1.hi && c1.cnt > kPartResolve;
+    const bool n0 = !c0.beyond && c0.lo != c0.hi && c0.cnt > kRes;
+    const bool n1 = !c1.beyond && c1.lo != c1.hi && c1.cnt > kRes;
     if (!n0 && !n1) break;
     part_round<NTH>(keys, n, jw, base, n0 ? c0.lo : c1.lo, n0 ? c0.hi : c1.hi, n0 ? c0.rk : c1.rk, 0, 1, sh);
     if (n0)
@@ -400,9 +401,7 @@ __device__ __forceinline__ void partition_block(const uint32_t* __restrict__ key
   int run0 = part_wave_prefix(sh, 0, wave, tot);
   int run1 = part_wave_prefix(sh, 1, wave, tot);
   int run2 = part_wave_prefix(sh, 2, wave, tot);
-  // ---- ordered, coalesced stores; positions capped at the list sizes (an
-  // exact split never reaches the caps)
-  const int n_P = c_low, n_C = c_high - c_low, n_R = n - c_high;
+  // ---- ordered, coalesced stores: emit(class, position in its list, channel)
   for (int j = 0; j < jw; ++j) {
     const int idx = base + j * 64;
     const bool ok = idx < n;
@@ -412,14 +411,67 @@ __device__ __forceinline__ void partition_block(const uint32_t* __restrict__ key
     const uint64_t k2 = all & ~(k0 | k1);
     const uint64_t mine = c == 0u ? k0 : (c == 1u ? k1 : k2);
     const int run = c == 0u ? run0 : (c == 1u ? run1 : run2);
-    const int cap = c == 0u ? n_P : (c == 1u ? n_C : n_R);
-    int32_t* const out = c == 0u ? P : (c == 1u ? C : R);
-    const int pos = run + __popcll(mine & lanes_below);
-    if (ok && pos < cap) out[pos] = idx;
+    if (ok) emit(c, run + __popcll(mine & lanes_below), idx);
     run0 += __popcll(k0);
     run1 += __popcll(k1);
     run2 += __popcll(k2);
   }
+}
+
+// The three-region split: P the c_low least important, C the next
+// c_high - c_low, R the rest, each ascending (positions capped at the list
+// sizes; an exact split never reaches the caps).  Arguments as split_block.
+template <int NTH>
+__device__ __forceinline__ void partition_block(const uint32_t* __restrict__ keys, int n, uint32_t mn, uint32_t mx,
+                                                int c_low, int c_high, int32_t* __restrict__ R,
+                                                int32_t* __restrict__ C, int32_t* __restrict__ P,
+                                                PartShared<NTH>& sh) {
+  const int n_P = c_low, n_C = c_high - c_low, n_R = n - c_high;
+  split_block<NTH>(keys, n, mn, mx, c_low, c_high, [=](uint32_t c, int pos, int idx) {
+    if (c == 0u) {
+      if (pos < n_P) P[pos] = idx;
+    } else if (c == 1u) {
+      if (pos < n_C) C[pos] = idx;
+    } else {
+      if (pos < n_R) R[pos] = idx;
+    }
+  }, sh);
+}
+
+// LDS bytes of topk_select<NTH> over n scores.
+template <int NTH>
+__host__ __device__ constexpr size_t topk_lds_bytes(int n) {
+  return part_lds_bytes<NTH>(n);
+}
+
+// S = the k most important of n candidates (score descending, position
+// ascending on ties: the order of the split), written in ascending order as
+// positions into C and, when `selected` is not NULL, as channels C[position].
+// One workgroup; 1 <= n <= kPartMaxN; smem: topk_lds_bytes<NTH>(n) bytes,
+// 16-byte aligned.  Scores are |z| >= 0.
+template <int NTH>
+__device__ __forceinline__ void topk_select(const float* __restrict__ score, int n, int k,
+                                            const int32_t* __restrict__ C, int32_t* __restrict__ positions,
+                                            int32_t* __restrict__ selected, unsigned char* smem) {
+  if (n <= 0 || k <= 0) return;
+  k = min(k, n);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(smem);
+  PartShared<NTH>& sh = *reinterpret_cast<PartShared<NTH>*>(smem + part_keys_bytes<NTH>(n));
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll 4
+  for (int i = threadIdx.x; i < n; i += NTH) {
+    const uint32_t u = value_bits(score[i]);
+    keys[i] = u;
+    mn = min(mn, u);
+    mx = max(mx, u);
+  }
+  // the k most important: the channels at or above the cut of rank n - k
+  split_block<NTH>(keys, n, mn, mx, n - k, n, [=](uint32_t c, int pos, int idx) {
+    if (c == 1u && pos < k) {
+      positions[pos] = idx;
+      if (selected != nullptr) selected[pos] = C[idx];
+    }
+  }, sh);
 }
 
 }  // namespace pop
