@@ -5,7 +5,7 @@ rocprofv3, and summaries of what the counters and the kernel trace recorded.
     # counted on its own), run under one rocprofv3 pass per counter set, with
     # the repository root on PYTHONPATH:
     rocprofv3 --pmc <counters> --output-format csv -d DIR -o pmc -- \\
-        python3 -m online_structured_ffn_amd.profiling run
+        python3 -m online_structured_ffn_amd.profiling run [--workload layer]
     # the summaries:
     python3 -m online_structured_ffn_amd.profiling traffic --reads DIR1 --writes DIR2 --fetch DIR3 --out FILE
     python3 -m online_structured_ffn_amd.profiling mfma --dir DIR4 --out FILE
@@ -39,7 +39,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_HERE)
 KERNEL_SOURCES = ("csrc/decode.hip", "csrc/prefill.hip", "csrc/partition.h", "csrc/pop_device.h",
                   "csrc/pop_internal.h", "csrc/prompt_ffn.hip", "csrc/trace.hip")
+LAYER_SOURCES = KERNEL_SOURCES + ("csrc/layer.hip", "csrc/prompt_gemm.h")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ffn_kernels_llama2_7b_b1_hbm_traffic.md")
+LAYER_WORKLOAD = "llama2_7b_layer_b1"
 _LINE = re.compile(r"^kernel=(?P<k>.+?) fetch_bytes=(?P<f>\d+) write_bytes=(?P<w>\d+) digest=(?P<d>[0-9a-f]+)$")
 
 COPY_MIB = 256
@@ -72,16 +74,9 @@ def traffic_bytes(kernel: str, path: str = TRAFFIC_SUMMARY):
 
 
 # --------------------------------------------------------------------- workload
-def run(layers: int = 4, steps: int = 4) -> None:
-    """The LLaMA-2-7B-shaped batch-1 FFN workload, eager: per layer the prompt
-    FFN, the partition and `steps` pruned and dense decode steps; before it the
-    two known-size kernels (three device copies of COPY_MIB MiB, three
-    stream-read probes of PROBE_BYTES)."""
-    import torch
-
-    from . import configs, pop, synth
-    w = configs.BY_NAME["llama2_7b_ffn_b1"]
-    dev = torch.device("cuda")
+def _known_size_kernels(torch, pop, dev) -> None:
+    """Three device copies of COPY_MIB MiB and three stream-read probes of
+    PROBE_BYTES (alternating between two buffers, each filled first)."""
     n = COPY_MIB << 20
     src = torch.ones(n, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -94,6 +89,22 @@ def run(layers: int = 4, steps: int = 4) -> None:
         pop.pop_hbm_read_probe(bufs[i % 2], sink, 1024)
     torch.cuda.synchronize()
     del bufs
+
+
+def run(layers: int = 4, steps: int = 4, workload: str = "ffn") -> None:
+    """The LLaMA-2-7B-shaped batch-1 FFN workload, eager: per layer the prompt
+    FFN, the partition and `steps` pruned and dense decode steps; before it the
+    known-size kernels.  workload="layer": the decoder-layer stack instead
+    (per layer the prompt's pass, then `steps` decode steps through every
+    layer)."""
+    import torch
+
+    from . import configs, pop, synth
+    dev = torch.device("cuda")
+    _known_size_kernels(torch, pop, dev)
+    if workload == "layer":
+        return _run_layer(torch, configs.BY_NAME[LAYER_WORKLOAD], pop, synth, dev, layers, steps)
+    w = configs.BY_NAME["llama2_7b_ffn_b1"]
     n_tok = w.prompt_batch * w.prompt_len
     ws_dec = pop.workspace(pop.pop_decode_workspace_bytes(1, w.d, w.d_ff), dev)
     for l in range(layers):
@@ -108,6 +119,38 @@ def run(layers: int = 4, steps: int = 4) -> None:
         torch.cuda.synchronize()
         del wt, X
     print(f"profiling workload done: {layers} layers x {steps} decode steps", flush=True)
+
+
+def _run_layer(torch, w, pop, synth, dev, layers: int, steps: int) -> None:
+    a = w.extra["attention"]
+    B, N, d = w.decode_batch, w.prompt_len, w.d
+    cnt = pop.pop_partition_counts(w.d_ff, w.r, w.gamma)
+    lays = []
+    for l in range(layers):
+        wts = dict(synth.torch_layer_weights(w, l, dev))
+        wts.update(synth.torch_attention_weights(w, l, dev))
+        lays.append(pop.Layer(d, a["n_heads"], a["n_kv_heads"], a["head_dim"], w.d_ff, N + steps, wts,
+                              eps=a["eps"], rope_theta=a["rope_theta"]))
+    caches = [lay.cache(B) for lay in lays]
+    x_pre = synth.torch_activations(w, (B * N, d), 0, 0, dev).float().view(B, N, d).contiguous()
+    xdec = synth.torch_activations(w, (steps * B, d), 0, 1, dev).float().view(steps, B, d).contiguous()
+    R = [torch.empty(cnt["n_R"], dtype=torch.int32, device=dev) for _ in range(layers)]
+    C = [torch.empty(cnt["n_C"], dtype=torch.int32, device=dev) for _ in range(layers)]
+    P = [torch.empty(cnt["n_P"], dtype=torch.int32, device=dev) for _ in range(layers)]
+    ws_pre = pop.workspace(pop.pop_layer_prefill_workspace_bytes(B, N, lays[0]), dev)
+    ws_dec = pop.workspace(pop.pop_layer_decode_workspace_bytes(B, lays[0]), dev)
+    for l in range(layers):
+        pop.pop_layer_prefill(x_pre, lays[l], *caches[l], w.r, w.gamma, out=(R[l], C[l], P[l], None), ws=ws_pre)
+    torch.cuda.synchronize()
+    pos = torch.full((1,), N, dtype=torch.int32, device=dev)
+    x = torch.empty((B, d), dtype=torch.float32, device=dev)
+    for t in range(steps):
+        x.copy_(xdec[t])
+        for l in range(layers):
+            pop.pop_layer_decode(x, lays[l], *caches[l], pos, R[l], C[l], w.r, ws=ws_dec)
+        pos.add_(1)
+    torch.cuda.synchronize()
+    print(f"profiling workload done: {w.name}, {layers} layers, a {N}-token prompt, {steps} decode steps", flush=True)
 
 
 # --------------------------------------------------------------------- summaries
@@ -162,9 +205,21 @@ def _calibration(per: dict, fn) -> tuple:
     return _mean(copies), _mean(probes), _mean(fills)
 
 
-def _algorithmic_reads():
+def _algorithmic_reads(workload: str = "ffn", steps: int = 4):
     """Algorithmic read bytes per launch of the kernels of the workload."""
     from . import configs
+    if workload == "layer":
+        w = configs.BY_NAME[LAYER_WORKLOAD]
+        a = w.extra["attention"]
+        H, Hkv, hd, d, e = a["n_heads"], a["n_kv_heads"], a["head_dim"], w.d, 2
+        keys = w.prompt_len + (steps + 1) / 2  # the mean key count over the decode steps
+        return {
+            # the K-major projection weights and the fp32 input row
+            "pop::k_gemv_kmajor<pop::bf16s, 1, 1>": d * (H + 2 * Hkv) * hd * e + 4 * d,
+            "pop::k_gemv_kmajor<pop::bf16s, 1, 2>": H * hd * d * e,
+            # the cached keys and values of every head
+            "pop::k_attn_decode<pop::bf16s, 128>": int(2 * Hkv * keys * hd * e),
+        }
     w = configs.BY_NAME["llama2_7b_ffn_b1"]
     from .pop import pop_partition_counts
     c = pop_partition_counts(w.d_ff, w.r, w.gamma)
@@ -180,7 +235,7 @@ def _algorithmic_reads():
     }
 
 
-def traffic(reads: str, writes: str, fetch: str | None, out: str) -> None:
+def traffic(reads: str, writes: str, fetch: str | None, out: str, workload: str = "ffn", steps: int = 4) -> None:
     pr, pw = _per_dispatch(reads), _per_dispatch(writes)
     pf = _per_dispatch(fetch) if fetch else {}
     copy_r, probe_r, _ = _calibration(pr, _read_bytes)
@@ -193,24 +248,31 @@ def traffic(reads: str, writes: str, fetch: str | None, out: str) -> None:
         fsz = lambda c: c.get("FETCH_SIZE", 0) * 1024
         copy_f, probe_f, _ = _calibration(pf, fsz)
         ff = (copy_f, probe_f)
-    alg = _algorithmic_reads()
-    digest = source_digest()
+    alg = _algorithmic_reads(workload, steps)
+    layer = workload == "layer"
+    digest = source_digest(LAYER_SOURCES if layer else KERNEL_SOURCES)
+    wl = f" --workload layer --layers 2 --steps {steps}" if layer else ""
+    sfx = "_layer" if layer else ""
     lines = [
-        "# HBM traffic per dispatch: LLaMA-2-7B-shaped FFN layers, prompt FFN, partition and batch-1 decode (bf16)",
+        "# HBM traffic per dispatch: " + (
+            f"the LLaMA-2-7B-shaped decoder-layer stack (2 layers, a 512-token prompt, {steps} decode steps at "
+            "batch 1, bf16)" if layer else
+            "LLaMA-2-7B-shaped FFN layers, prompt FFN, partition and batch-1 decode (bf16)"),
         "",
         "Counter passes, one rocprofv3 run each (`$R` = repository root on the GPU box):",
         "",
         "```",
         "cd /tmp && export TMPDIR=/tmp",
         "export PYTHONPATH=$R",
-        "rocprofv3 --pmc " + " ".join(READ_COUNTERS) + " --output-format csv -d $R/gpurun_out/pmc_rd -o pmc -- "
-        "python3 -m online_structured_ffn_amd.profiling run",
-        "rocprofv3 --pmc " + " ".join(WRITE_COUNTERS) + " --output-format csv -d $R/gpurun_out/pmc_wr -o pmc -- "
-        "python3 -m online_structured_ffn_amd.profiling run",
-        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/pmc_fetch -o pmc -- "
-        "python3 -m online_structured_ffn_amd.profiling run",
-        "python3 -m online_structured_ffn_amd.profiling traffic --reads $R/gpurun_out/pmc_rd "
-        "--writes $R/gpurun_out/pmc_wr --fetch $R/gpurun_out/pmc_fetch --out <this file>",
+        "rocprofv3 --pmc " + " ".join(READ_COUNTERS) + f" --output-format csv -d $R/gpurun_out/pmc_rd{sfx} -o pmc -- "
+        "python3 -m online_structured_ffn_amd.profiling run" + wl,
+        "rocprofv3 --pmc " + " ".join(WRITE_COUNTERS) + f" --output-format csv -d $R/gpurun_out/pmc_wr{sfx} -o pmc -- "
+        "python3 -m online_structured_ffn_amd.profiling run" + wl,
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/pmc_fetch{sfx} -o pmc -- "
+        "python3 -m online_structured_ffn_amd.profiling run" + wl,
+        f"python3 -m online_structured_ffn_amd.profiling traffic --reads $R/gpurun_out/pmc_rd{sfx} "
+        f"--writes $R/gpurun_out/pmc_wr{sfx} --fetch $R/gpurun_out/pmc_fetch{sfx}"
+        + (f" --workload layer --steps {steps}" if layer else "") + " --out <this file>",
         "```",
         "",
         "Bytes: reads = 32 x RDREQ_32B + 64 x RDREQ_64B + 128 x RDREQ_128B, writes = 64 x WRREQ_64B + 32 x "
@@ -258,9 +320,13 @@ def traffic(reads: str, writes: str, fetch: str | None, out: str) -> None:
             machine.append(f"kernel={name} fetch_bytes={int(round(rd))} write_bytes={int(round(wr))} digest={digest}")
     lines += [
         "",
-        "Algorithmic reads: k_pop_linked reads the gate and up rows of R u C, the W_downT rows of R u S and x; "
-        "k_pop_step<..., true, 0> (the dense step) every row of the three matrices; k_colsq_slices the prompt; "
-        "k_importance_items W_up and s2.",
+        ("Algorithmic reads: the q|k|v projection (`k_gemv_kmajor<..., 1, 1>`) reads Wqkv_T and the input row; "
+         "the output projection (`<..., 1, 2>`) Wo_T (the attention slices it merges are not counted); decode "
+         f"attention the cached keys and values of every head at the mean key count of the {steps} steps.  The "
+         "FFN's kernels are those of the FFN summary." if layer else
+         "Algorithmic reads: k_pop_linked reads the gate and up rows of R u C, the W_downT rows of R u S and x; "
+         "k_pop_step<..., true, 0> (the dense step) every row of the three matrices; k_colsq_slices the prompt; "
+         "k_importance_items W_up and s2."),
         "",
         "Machine-readable (read by bench.py; valid while the kernel sources hash to the digest):",
         "",
@@ -346,7 +412,10 @@ def main(argv=None) -> None:
     r = sub.add_parser("run")
     r.add_argument("--layers", type=int, default=4)
     r.add_argument("--steps", type=int, default=4)
+    r.add_argument("--workload", choices=("ffn", "layer"), default="ffn")
     t = sub.add_parser("traffic")
+    t.add_argument("--workload", choices=("ffn", "layer"), default="ffn")
+    t.add_argument("--steps", type=int, default=4)
     t.add_argument("--reads", required=True)
     t.add_argument("--writes", required=True)
     t.add_argument("--fetch", default=None)
@@ -360,9 +429,9 @@ def main(argv=None) -> None:
     s.add_argument("--command", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "run":
-        run(a.layers, a.steps)
+        run(a.layers, a.steps, a.workload)
     elif a.cmd == "traffic":
-        traffic(a.reads, a.writes, a.fetch, a.out)
+        traffic(a.reads, a.writes, a.fetch, a.out, a.workload, a.steps)
     elif a.cmd == "mfma":
         mfma(a.dir, a.out)
     else:
