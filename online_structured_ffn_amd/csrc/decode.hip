@@ -176,7 +176,10 @@ constexpr int kFusedThreads = POP_FUSED_THREADS;
 constexpr int kFusedWaves = kFusedThreads / 64;
 constexpr int kFusedTopkMaxN = 4096;
 constexpr int kFusedMaxRows = 512;  // rows per block
-constexpr int kFusedP = 2;          // rows per batch
+#ifndef POP_FUSED_P
+#define POP_FUSED_P 1
+#endif
+constexpr int kFusedP = POP_FUSED_P;  // rows per batch
 
 template <typename T, int NV>
 struct FusedRowBuf {
@@ -190,28 +193,33 @@ __device__ __forceinline__ void fused_issue(FusedRowBuf<T, NV>& b, const int* ro
                                             const T* __restrict__ Wg, const T* __restrict__ Wu,
                                             const T* __restrict__ WdT, int d) {
   constexpr int V = Vec<T>::N;
-  // Lanes past the row's end load its last vector (same cache line, results
-  // unused): the loads carry no per-lane condition, which keeps the compiler's
-  // wait counting exact across the double buffer.
+  // No load carries a condition, so that the compiler's wait counting stays
+  // exact across the double buffer (behind a branch, the count of the path
+  // that skips a row applies to every path, and the consumer of one buffer
+  // then waits for most of the other's loads too).  Lanes past the row's end
+  // load its last vector, and slots past nrows load the list's last row again
+  // (lines already requested by this block; their z is 0).  The scheduling
+  // barriers keep the other buffer's arithmetic from being moved above these
+  // loads, which would make it wait before they are issued.
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int p = 0; p < kFusedP; ++p) {
-    if (i0 + p < nrows) {
-      const int64_t base = (int64_t)rows[i0 + p] * d;
+    const int64_t base = (int64_t)rows[min(i0 + p, nrows - 1)] * d;
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int col = min(j * kFusedThreads * V + (int)threadIdx.x * V, d - V);
-        b.g[p][j] = ld16_stream(Wg + base + col);
-        b.u[p][j] = ld16_stream(Wu + base + col);
-        if (kDown) b.w[p][j] = ld16_stream(WdT + base + col);
-      }
+    for (int j = 0; j < NV; ++j) {
+      const int col = min(j * kFusedThreads * V + (int)threadIdx.x * V, d - V);
+      b.g[p][j] = ld16_stream(Wg + base + col);
+      b.u[p][j] = ld16_stream(Wu + base + col);
+      if (kDown) b.w[p][j] = ld16_stream(WdT + base + col);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Reduces the batch's dot products across the block and applies them.
 // Returns through zs the batch's z values (0 for rows past nrows).  No lane or
 // row condition guards the arithmetic: columns past d hold x = 0, rows past
-// nrows get z = 0, and the buffers start zeroed, so every operand is finite.
+// nrows get z = 0, and every buffer slot holds a loaded (finite) weight.
 template <typename T, int NV, bool kDown, int PB>
 __device__ __forceinline__ void fused_consume(const FusedRowBuf<T, NV>& b, const u32x4 (&xv)[NV], int i0, int nrows,
                                               int d, float (&part)[2][kFusedWaves][2 * kFusedP], float (&acc)[NV][Vec<T>::N],
@@ -271,79 +279,98 @@ __device__ __forceinline__ void fused_consume(const FusedRowBuf<T, NV>& b, const
         for (int v = 0; v < V; ++v) acc[j][v] = fmaf(zs[p], f[v], acc[j][v]);
       }
     }
+    // The products are due here: left to the optimiser they sink past the
+    // next batch's loads, which then cannot reuse this buffer's registers
+    // (the loop then copies a buffer at its back edge, waiting on its loads).
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int v = 0; v < V; ++v) asm volatile("" : "+v"(acc[j][v]));
   }
 }
 
+// Row i's z into zl[i] (LDS; thread 0), for the rows of the pair that exist.
+__device__ __forceinline__ void fused_put_z(float* zl, int i0, int nrows, const float (&zs)[kFusedP]) {
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int p = 0; p < kFusedP; ++p)
+      if (i0 + p < nrows) zl[i0 + p] = zs[p];
+  }
+}
+
+// The rows rows[0 .. nrows) two at a time, double-buffered: the next pair's
+// loads are issued before the current pair is reduced.  Every path issues
+// the same loads (the last pairs are unrolled out of the loop rather than
+// guarded), so each reduction waits only for its own pair.  z of row i goes
+// to zl[i] (LDS, written by thread 0; the caller stores it after a barrier):
+// a global store inside the loop would add to the counter the loads are
+// waited on by.
 template <typename T, int NV, bool kDown>
 __device__ __forceinline__ void fused_rows(const int* rows, int nrows, const T* __restrict__ Wg, const T* __restrict__ Wu,
                                            const T* __restrict__ WdT, int d, const u32x4 (&xv)[NV],
                                            float (&part)[2][kFusedWaves][2 * kFusedP], float (&acc)[NV][Vec<T>::N],
-                                           float* __restrict__ zout, int zbase, float* __restrict__ score,
-                                           uint64_t* __restrict__ pub = nullptr, float* zkeep = nullptr) {
+                                           float* zl) {
   if (nrows <= 0) return;  // block-uniform
   FusedRowBuf<T, NV> A, Bf;
-#pragma unroll
-  for (int p = 0; p < kFusedP; ++p)
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      A.g[p][j] = A.u[p][j] = A.w[p][j] = u32x4{0u, 0u, 0u, 0u};
-      Bf.g[p][j] = Bf.u[p][j] = Bf.w[p][j] = u32x4{0u, 0u, 0u, 0u};
-    }
   float zs[kFusedP];
   fused_issue<T, NV, kDown>(A, rows, 0, nrows, Wg, Wu, WdT, d);
-  for (int i0 = 0; i0 < nrows; i0 += 2 * kFusedP) {
+  int i0 = 0;
+  for (; i0 + 2 * kFusedP < nrows; i0 += 2 * kFusedP) {
     fused_issue<T, NV, kDown>(Bf, rows, i0 + kFusedP, nrows, Wg, Wu, WdT, d);
     fused_consume<T, NV, kDown, 0>(A, xv, i0, nrows, d, part, acc, zs);
-    if (threadIdx.x == 0) {
-#pragma unroll
-      for (int p = 0; p < kFusedP; ++p)
-        if (i0 + p < nrows) {
-          zout[zbase + i0 + p] = zs[p];
-          if (score != nullptr) score[i0 + p] = fabsf(zs[p]);
-          if (pub != nullptr) st_coh(&pub[i0 + p], pack_valid(__float_as_uint(fabsf(zs[p])), __float_as_uint(zs[p])));
-          if (zkeep != nullptr) zkeep[i0 + p] = zs[p];
-        }
-    }
-    if (i0 + kFusedP >= nrows) break;
+    fused_put_z(zl, i0, nrows, zs);
     fused_issue<T, NV, kDown>(A, rows, i0 + 2 * kFusedP, nrows, Wg, Wu, WdT, d);
     fused_consume<T, NV, kDown, 1>(Bf, xv, i0 + kFusedP, nrows, d, part, acc, zs);
-    if (threadIdx.x == 0) {
-#pragma unroll
-      for (int p = 0; p < kFusedP; ++p)
-        if (i0 + kFusedP + p < nrows) {
-          zout[zbase + i0 + kFusedP + p] = zs[p];
-          if (score != nullptr) score[i0 + kFusedP + p] = fabsf(zs[p]);
-          if (pub != nullptr)
-            st_coh(&pub[i0 + kFusedP + p], pack_valid(__float_as_uint(fabsf(zs[p])), __float_as_uint(zs[p])));
-          if (zkeep != nullptr) zkeep[i0 + kFusedP + p] = zs[p];
-        }
-    }
+    fused_put_z(zl, i0 + kFusedP, nrows, zs);
+  }
+  if (i0 + kFusedP < nrows) {  // two pairs left (the second possibly partial)
+    fused_issue<T, NV, kDown>(Bf, rows, i0 + kFusedP, nrows, Wg, Wu, WdT, d);
+    fused_consume<T, NV, kDown, 0>(A, xv, i0, nrows, d, part, acc, zs);
+    fused_put_z(zl, i0, nrows, zs);
+    fused_consume<T, NV, kDown, 1>(Bf, xv, i0 + kFusedP, nrows, d, part, acc, zs);
+    fused_put_z(zl, i0 + kFusedP, nrows, zs);
+  } else {  // one pair left
+    fused_consume<T, NV, kDown, 0>(A, xv, i0, nrows, d, part, acc, zs);
+    fused_put_z(zl, i0, nrows, zs);
   }
 }
 
 // Up to NB candidate rows at once (gate and up rows only): every load issued
 // before any is used, so the batch costs one memory round trip, then one
-// cross-wave reduction for all its rows.  Threads p < nrows write row p's z,
-// |z| and, when pub is set, its hand-over word pack_valid(bits of |z|, bits of z).
+// cross-wave reduction for all its rows.  Split into the issue and the
+// reduction so that a caller can put other loads in flight in between.
 template <typename T, int NV, int NB>
-__device__ __forceinline__ void cand_rows(const int* rows, int nrows, const T* __restrict__ Wg, const T* __restrict__ Wu,
-                                          int d, const u32x4 (&xv)[NV], float (&part)[kFusedWaves][2 * NB],
-                                          float* __restrict__ zout, float* __restrict__ score,
-                                          uint64_t* __restrict__ pub) {
+struct CandBuf {
+  u32x4 g[NB][NV];
+  u32x4 u[NB][NV];
+};
+
+template <typename T, int NV, int NB>
+__device__ __forceinline__ void cand_issue(CandBuf<T, NV, NB>& b, const int* rows, int nrows,
+                                           const T* __restrict__ Wg, const T* __restrict__ Wu, int d) {
   constexpr int V = Vec<T>::N;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  u32x4 g[NB][NV], u[NB][NV];
 #pragma unroll
   for (int p = 0; p < NB; ++p) {
     const int64_t base = (int64_t)rows[min(p, nrows - 1)] * d;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int col = min(j * kFusedThreads * V + (int)threadIdx.x * V, d - V);
-      g[p][j] = ld16_stream(Wg + base + col);
-      u[p][j] = ld16_stream(Wu + base + col);
+      b.g[p][j] = ld16_stream(Wg + base + col);
+      b.u[p][j] = ld16_stream(Wu + base + col);
     }
   }
+}
+
+// Threads p < nrows write row p's z to zout and zl (LDS, when not null), |z|
+// to score and, when pub is set, its hand-over word pack_valid(bits of |z|,
+// bits of z).
+template <typename T, int NV, int NB>
+__device__ __forceinline__ void cand_consume(const CandBuf<T, NV, NB>& b, int nrows, const u32x4 (&xv)[NV],
+                                             float (&part)[kFusedWaves][2 * NB], float* __restrict__ zout,
+                                             float* __restrict__ score, uint64_t* __restrict__ pub, float* zl) {
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   float pg[NB], pu[NB];
 #pragma unroll
   for (int p = 0; p < NB; ++p) {
@@ -351,8 +378,8 @@ __device__ __forceinline__ void cand_rows(const int* rows, int nrows, const T* _
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       float gf[V], uf[V], xx[V];
-      unpack(g[p][j], gf, T{});
-      unpack(u[p][j], uf, T{});
+      unpack(b.g[p][j], gf, T{});
+      unpack(b.u[p][j], uf, T{});
       unpack(xv[j], xx, T{});
 #pragma unroll
       for (int v = 0; v < V; ++v) {
@@ -382,104 +409,20 @@ __device__ __forceinline__ void cand_rows(const int* rows, int nrows, const T* _
     const float zz = silu(gs) * us;
     zout[p] = zz;
     score[p] = fabsf(zz);
+    if (zl != nullptr) zl[p] = zz;
     if (pub != nullptr) st_coh(&pub[p], pack_valid(__float_as_uint(fabsf(zz)), __float_as_uint(zz)));
   }
   __syncthreads();  // part is reused by the next batch
 }
 
-// The end of a worker's stream in one round trip: up to NR retained rows
-// (gate, up and W_downT rows) and up to NS selected candidate rows (W_downT
-// rows, z given) with every load issued before any is used.  The retained
-// rows' z (written by thread 0 to zout) and then the selected rows' z
-// multiply their W_downT rows into acc, in that fixed order.  Unused slots
-// load a clamped channel (the lists' entries there may hold anything) and
-// add nothing.
-template <typename T, int NV, int NR, int NS>
-__device__ __forceinline__ void tail_rows(const int* rrows, int nrr, const int* schan, const float* sz, int nss,
-                                          const T* __restrict__ Wg, const T* __restrict__ Wu,
-                                          const T* __restrict__ WdT, int d, int d_ff, const u32x4 (&xv)[NV],
-                                          float (&part)[kFusedWaves][2 * NR], float (&acc)[NV][Vec<T>::N],
-                                          float* __restrict__ zout) {
-  constexpr int V = Vec<T>::N;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  u32x4 g[NR][NV], u[NR][NV], wr[NR][NV], wsel[NS][NV];
-#pragma unroll
-  for (int p = 0; p < NR; ++p) {
-    const int64_t base = (int64_t)clamp_channel(rrows[min(p, max(nrr - 1, 0))], d_ff) * d;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int col = min(j * kFusedThreads * V + (int)threadIdx.x * V, d - V);
-      g[p][j] = ld16_stream(Wg + base + col);
-      u[p][j] = ld16_stream(Wu + base + col);
-      wr[p][j] = ld16_stream(WdT + base + col);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < NS; ++q) {
-    const int64_t base = (int64_t)clamp_channel(schan[min(q, max(nss - 1, 0))], d_ff) * d;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int col = min(j * kFusedThreads * V + (int)threadIdx.x * V, d - V);
-      wsel[q][j] = ld16_stream(WdT + base + col);
-    }
-  }
-  float zr[NR];
-#pragma unroll
-  for (int p = 0; p < NR; ++p) {
-    float pg = 0.f, pu = 0.f;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      float gf[V], uf[V], xx[V];
-      unpack(g[p][j], gf, T{});
-      unpack(u[p][j], uf, T{});
-      unpack(xv[j], xx, T{});
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        pg = fmaf(gf[v], xx[v], pg);
-        pu = fmaf(uf[v], xx[v], pu);
-      }
-    }
-    pg = wave_sum_last(pg);
-    pu = wave_sum_last(pu);
-    if (lane == 63) {
-      part[wave][2 * p] = pg;
-      part[wave][2 * p + 1] = pu;
-    }
-  }
-  if (NR > 0) __syncthreads();
-#pragma unroll
-  for (int p = 0; p < NR; ++p) {
-    float gs = part[0][2 * p], us = part[0][2 * p + 1];
-#pragma unroll
-    for (int w = 1; w < kFusedWaves; ++w) {
-      gs += part[w][2 * p];
-      us += part[w][2 * p + 1];
-    }
-    zr[p] = p < nrr ? silu(gs) * us : 0.f;
-    if (threadIdx.x == 0 && p < nrr) zout[p] = zr[p];
-  }
-#pragma unroll
-  for (int p = 0; p < NR; ++p)
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      float f[V];
-      unpack(wr[p][j], f, T{});
-#pragma unroll
-      for (int v = 0; v < V; ++v) acc[j][v] = fmaf(zr[p], f[v], acc[j][v]);
-    }
-#pragma unroll
-  for (int q = 0; q < NS; ++q) {
-    const float zz = q < nss ? sz[q] : 0.f;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      float f[V];
-      unpack(wsel[q][j], f, T{});
-#pragma unroll
-      for (int v = 0; v < V; ++v) acc[j][v] = fmaf(zz, f[v], acc[j][v]);
-    }
-  }
-  __syncthreads();  // part and the caller's row lists are reused next
+template <typename T, int NV, int NB>
+__device__ __forceinline__ void cand_rows(const int* rows, int nrows, const T* __restrict__ Wg, const T* __restrict__ Wu,
+                                          int d, const u32x4 (&xv)[NV], float (&part)[kFusedWaves][2 * NB],
+                                          float* __restrict__ zout, float* __restrict__ score,
+                                          uint64_t* __restrict__ pub, float* zl = nullptr) {
+  CandBuf<T, NV, NB> b;
+  cand_issue<T, NV, NB>(b, rows, nrows, Wg, Wu, d);
+  cand_consume<T, NV, NB>(b, nrows, xv, part, zout, score, pub, zl);
 }
 
 // Loads this thread's x vectors and clears its down accumulators.
@@ -521,6 +464,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
   using SelT = typename std::conditional<PHASE == 2, SelShared<kFusedThreads, kFusedTopkMaxN>, NoSel>::type;
   __shared__ SelT sh_sel;
   __shared__ int rows[kFusedMaxRows];
+  __shared__ float zl[kFusedMaxRows];
   __shared__ float part[2][kFusedWaves][2 * kFusedP];
   const int bid = blockIdx.x;
   if (PHASE != 0 && bid < nb0) {
@@ -533,7 +477,12 @@ __global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
       const int nrows = max(0, min(n_C, r0 + rows_per_cblock) - r0);
       for (int i = threadIdx.x; i < nrows; i += kFusedThreads) rows[i] = clamp_channel(C[r0 + i], d_ff);
       __syncthreads();
-      fused_rows<T, NV, false>(rows, nrows, Wg, Wu, (const T*)nullptr, d, xv, part, acc, z, n_R + r0, score + r0);
+      fused_rows<T, NV, false>(rows, nrows, Wg, Wu, (const T*)nullptr, d, xv, part, acc, zl);
+      __syncthreads();
+      for (int i = threadIdx.x; i < nrows; i += kFusedThreads) {
+        z[n_R + r0 + i] = zl[i];
+        score[r0 + i] = fabsf(zl[i]);
+      }
     } else {  // the top-k over the scores phase 1 wrote
       topk_block(score, n_C, k, C, Q, sel, sh_sel);
     }
@@ -547,7 +496,9 @@ __global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
   const int nrows = max(0, min(n_R, r0 + rows_per_rblock) - r0);
   for (int i = threadIdx.x; i < nrows; i += kFusedThreads) rows[i] = kIdentity ? r0 + i : clamp_channel(R[r0 + i], d_ff);
   __syncthreads();
-  fused_rows<T, NV, true>(rows, nrows, Wg, Wu, WdT, d, xv, part, acc, z, r0, nullptr);
+  fused_rows<T, NV, true>(rows, nrows, Wg, Wu, WdT, d, xv, part, acc, zl);
+  __syncthreads();
+  for (int i = threadIdx.x; i < nrows; i += kFusedThreads) z[r0 + i] = zl[i];
   static_assert(kFinCols % V == 0, "a thread's columns lie in one slice");
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
@@ -725,32 +676,39 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
 // retained stream of the first.  Block 0 of k_pop_linked is the candidate
 // top-k; blocks 1 .. nW are workers, and worker w takes an even share
 // (split_at) of each list:
-//   1. its candidate rows: gate and up rows, z and |z|; each row's (|z|, z)
-//      goes to block 0 as one valid-tagged word; once they are all written
-//      (a wait on this wave's own stores, where no load is in flight) the
-//      worker counts itself done;
+//   1. its candidate rows: gate and up rows, z (kept in LDS) and |z|; each
+//      row's (|z|, z) goes to block 0 as one valid-tagged word.  The loads of
+//      its first retained rows are issued before the last candidate batch is
+//      reduced;
 //   2. its retained rows: gate, up and W_downT rows, z, and z * W_downT added
-//      into its partial y (registers);
-//   3. the cut: block 0 publishes (v, tie position) once it has selected; the
-//      worker reads one copy of it and adds z * W_downT[channel, :] for each of
-//      ITS candidate rows that the cut selects (z kept in LDS since step 1);
+//      into its partial y (registers); every second row batch also re-reads
+//      the published cut (one coherent 8-byte load beside the rows' loads);
+//   3. the cut: block 0 publishes (v, tie position) once it has selected.  If
+//      the worker's last completed read of the cut found it out before its
+//      last two row batches, it selects its own candidates against it there
+//      (value above v, or equal at a position up to the tie position) and
+//      their W_downT rows' loads go out with those batches; otherwise it
+//      polls for the cut after its rows and adds the selected rows then.
+//      Both ways add the same rows in the same order;
 //   4. its partial y, slice-major, with plain stores.
 // k_pop_finish then adds the nW partials in a fixed order into y and clears
 // the hand-over words for the next call.  Only block 0 waits on many
-// workgroups (one counter, one poller); a worker waits at most for the cut,
-// which is normally out long before its retained rows end.  Nothing waits on
-// a workgroup that is not running: the host keeps the grid within what the
-// device holds at once, and block 0 needs only the workers' first phase.  Every
-// wait is bounded (kPollLimit polls); one that runs out sets the sticky error
-// word ctl[kCtlErr] and the step goes on (its y is then wrong).
+// workgroups (one poller); a worker waits at most for the cut.  Nothing
+// waits on a workgroup that is not running: the host keeps the grid within
+// what the device holds at once, and block 0 needs only the workers' first
+// phase.  Every wait is bounded (kPollLimit polls); one that runs out sets
+// the sticky error word ctl[kCtlErr] and the step goes on (its y is then
+// wrong).
 #ifndef POP_LINKED_ON
 #define POP_LINKED_ON 1  // 0: batch-1 steps take the three-launch path
 #endif
 constexpr int kLinkedTopkMaxN = 4096;
 constexpr int kLinkedMaxWorkers = POP_FUSED_RBLOCKS - 1;
 constexpr int kPollLimit = 1 << 20;
-constexpr int kSelRowsPerPass = 4;  // selected rows per tail pass
-constexpr int kTailR = 2;           // retained rows kept for the tail pass
+#ifndef POP_LINKED_NS
+#define POP_LINKED_NS 8
+#endif
+constexpr int kLinkedNS = POP_LINKED_NS;  // selected rows carried by the last row batches (and per later pass)
 constexpr int kThrCopies = 32;  // copies of the published cut
 constexpr int kThrStride = 16;  // 64-bit words between copies (128 bytes)
 constexpr int kCandBatch = 8;  // candidate rows whose loads a worker issues together
@@ -765,8 +723,153 @@ static_assert(kHandWords * sizeof(uint64_t) <= kHandBytes, "hand-over region");
 
 __device__ __forceinline__ int split_at(int n, int parts, int i) { return (int)(((int64_t)n * i) / parts); }
 
+// A worker's own candidates (channels crow, z in cz, positions c0 + i) that
+// the cut e selects: value bits of |z| above v, or equal at a position up to
+// the tie position.  Channels and z of the selected ones, in candidate
+// order, into s_chan / s_zv; returns their number.  One thread.
+__device__ __forceinline__ int linked_select(uint64_t e, const int* crow, const float* cz, int c0, int nc,
+                                             int* s_chan, float* s_zv) {
+  const uint32_t cv = (uint32_t)(e >> 32) & 0x7fffffffu;
+  const int tie = (int)(uint32_t)e;
+  int m = 0;
+  for (int i = 0; i < nc; ++i) {
+    const uint32_t xb = __float_as_uint(fabsf(cz[i])) & 0x7fffffffu;
+    if (xb > cv || (xb == cv && c0 + i <= tie)) {
+      s_chan[m] = crow[i];
+      s_zv[m] = cz[i];
+      ++m;
+    }
+  }
+  return m;
+}
+
+// The W_downT rows of up to NS selected candidates, every load issued at
+// once; slots past n load the list's last row again (n >= 1).
+template <typename T, int NV, int NS>
+__device__ __forceinline__ void sel_issue(u32x4 (&ws)[NS][NV], const int* chan, int n, const T* __restrict__ WdT,
+                                          int d, int d_ff) {
+  constexpr int V = Vec<T>::N;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    const int64_t base = (int64_t)clamp_channel(chan[min(q, n - 1)], d_ff) * d;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int col = min(j * kFusedThreads * V + (int)threadIdx.x * V, d - V);
+      ws[q][j] = ld16_stream(WdT + base + col);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Adds z_q * W_downT[chan_q, :] for q < n, in order (slots past n add
+// nothing: they are skipped, not multiplied by zero).
+template <typename T, int NV, int NS>
+__device__ __forceinline__ void sel_consume(const u32x4 (&ws)[NS][NV], const float* zv, int n,
+                                            float (&acc)[NV][Vec<T>::N]) {
+  constexpr int V = Vec<T>::N;
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    if (q < n) {  // block-uniform
+      const float zz = zv[q];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        float f[V];
+        unpack(ws[q][j], f, T{});
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[j][v] = fmaf(zz, f[v], acc[j][v]);
+      }
+    }
+  }
+}
+
+// The last one or two row batches of a worker's stream (X holds batch i0, its
+// loads in flight; PB0 is the partial-sum buffer of the first reduction
+// here), and the selected rows when the cut is known: cw is the last read of
+// the cut, complete by now.  When it is out (and the worker has
+// candidates), its selected candidates go to s_chan / s_zv (count in
+// *sh_nsel) and the first NS of them are added after the rows, their loads
+// issued with the last batches.  Returns how many were added, or -1 when the
+// cut was not known in time.
+template <typename T, int NV, int NS, int PB0>
+__device__ __forceinline__ int linked_last(FusedRowBuf<T, NV>& X, FusedRowBuf<T, NV>& Y, int i0, const int* rows,
+                                           int nrows, const T* __restrict__ Wg, const T* __restrict__ Wu,
+                                           const T* __restrict__ WdT, int d, int d_ff, const u32x4 (&xv)[NV],
+                                           float (&part)[2][kFusedWaves][2 * kFusedP],
+                                           float (&acc)[NV][Vec<T>::N], float* zl, bool sel_here, uint64_t cw,
+                                           const int* crow, const float* cz, int c0, int nc, int* s_chan,
+                                           float* s_zv, int* sh_nsel) {
+  const int nl = max(nrows, 1);
+  float zs[kFusedP];
+  // Each wave read the cut on its own, so the waves may disagree on whether
+  // it is out: thread 0 decides from its read (and selects), and the block
+  // takes its decision from LDS.
+  if (threadIdx.x == 0) *sh_nsel = sel_here && is_valid(cw) ? linked_select(cw, crow, cz, c0, nc, s_chan, s_zv) : -1;
+  lds_barrier();
+  const int got = *sh_nsel;  // block-uniform; -1: the cut was not out
+  const bool early = got >= 0;
+  const int nsl = early ? min(got, NS) : 0;
+  u32x4 ws[NS][NV];
+  const int* srow = nsl > 0 ? s_chan : rows + (nl - 1);
+  if (i0 + kFusedP < nrows) {  // two batches left
+    fused_issue<T, NV, true>(Y, rows, i0 + kFusedP, nl, Wg, Wu, WdT, d);
+    sel_issue<T, NV, NS>(ws, srow, max(nsl, 1), WdT, d, d_ff);
+    fused_consume<T, NV, true, PB0>(X, xv, i0, nrows, d, part, acc, zs);
+    fused_put_z(zl, i0, nrows, zs);
+    fused_consume<T, NV, true, 1 - PB0>(Y, xv, i0 + kFusedP, nrows, d, part, acc, zs);
+    fused_put_z(zl, i0 + kFusedP, nrows, zs);
+  } else {
+    sel_issue<T, NV, NS>(ws, srow, max(nsl, 1), WdT, d, d_ff);
+    fused_consume<T, NV, true, PB0>(X, xv, i0, nrows, d, part, acc, zs);
+    fused_put_z(zl, i0, nrows, zs);
+  }
+  sel_consume<T, NV, NS>(ws, s_zv, nsl, acc);
+  return early ? nsl : -1;
+}
+
+// A worker's retained rows rows[0 .. nrows), double-buffered (the first
+// batch's loads already issued into A by the caller; rows holds at least one
+// entry even when nrows is 0, whose loads then go unused), the cut re-read
+// beside every second batch, and the ending of linked_last.  The first batch
+// is reduced before the loop, so the buffer the loop carries is issued right
+// before it.
+template <typename T, int NV, int NS>
+__device__ __forceinline__ int linked_stream(FusedRowBuf<T, NV>& A, const int* rows, int nrows,
+                                             const T* __restrict__ Wg, const T* __restrict__ Wu,
+                                             const T* __restrict__ WdT, int d, int d_ff, const u32x4 (&xv)[NV],
+                                             float (&part)[2][kFusedWaves][2 * kFusedP],
+                                             float (&acc)[NV][Vec<T>::N], float* zl, bool sel_here,
+                                             const uint64_t* cutw, const int* crow, const float* cz, int c0, int nc,
+                                             int* s_chan, float* s_zv, int* sh_nsel) {
+  const int nl = max(nrows, 1);
+  FusedRowBuf<T, NV> Bf, A2;
+  float zs[kFusedP];
+  if (nrows <= 2 * kFusedP)
+    return linked_last<T, NV, NS, 0>(A, Bf, 0, rows, nrows, Wg, Wu, WdT, d, d_ff, xv, part, acc, zl, sel_here, 0, crow,
+                                     cz, c0, nc, s_chan, s_zv, sh_nsel);
+  uint64_t cw = ld_coh(cutw);
+  fused_issue<T, NV, true>(Bf, rows, kFusedP, nl, Wg, Wu, WdT, d);
+  fused_consume<T, NV, true, 0>(A, xv, 0, nrows, d, part, acc, zs);
+  fused_put_z(zl, 0, nrows, zs);
+  int i0 = kFusedP;  // Bf holds batch i0
+  for (; i0 + 2 * kFusedP < nrows; i0 += 2 * kFusedP) {
+    fused_issue<T, NV, true>(A2, rows, i0 + kFusedP, nl, Wg, Wu, WdT, d);
+    cw = ld_coh(cutw);
+    fused_consume<T, NV, true, 1>(Bf, xv, i0, nrows, d, part, acc, zs);
+    fused_put_z(zl, i0, nrows, zs);
+    fused_issue<T, NV, true>(Bf, rows, i0 + 2 * kFusedP, nl, Wg, Wu, WdT, d);
+    fused_consume<T, NV, true, 0>(A2, xv, i0 + kFusedP, nrows, d, part, acc, zs);
+    fused_put_z(zl, i0 + kFusedP, nrows, zs);
+  }
+  return linked_last<T, NV, NS, 1>(Bf, A2, i0, rows, nrows, Wg, Wu, WdT, d, d_ff, xv, part, acc, zl, sel_here, cw, crow,
+                                   cz, c0, nc, s_chan, s_zv, sh_nsel);
+}
+
+#ifndef POP_LINKED_MINB
+#define POP_LINKED_MINB 2  // workgroups of k_pop_linked resident per CU
+#endif
 template <typename T, int NV, bool kIdentity>
-__global__ __launch_bounds__(kFusedThreads, 2) void k_pop_linked(
+__global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
     const T* __restrict__ x, const T* __restrict__ Wg, const T* __restrict__ Wu, const T* __restrict__ WdT,
     const int32_t* __restrict__ R, const int32_t* __restrict__ C, float* __restrict__ z, float* __restrict__ score,
     uint64_t* __restrict__ hand, int32_t* __restrict__ sel_out, float* __restrict__ partial,
@@ -774,15 +877,14 @@ __global__ __launch_bounds__(kFusedThreads, 2) void k_pop_linked(
   constexpr int V = Vec<T>::N;
   struct Work {
     int rows[kFusedMaxRows];
-    uint64_t cw[kFusedMaxRows];  // hand-over words of this worker's share of C
+    float zr[kFusedMaxRows];  // z of this worker's retained rows
+    float cz[kFusedMaxRows];  // z of this worker's candidates
     float part[2][kFusedWaves][2 * kFusedP];
     float cpart[kFusedWaves][2 * kCandBatch];
     int crow[kFusedMaxRows];  // this worker's share of C (channels)
-    float tpart[kFusedWaves][2 * kTailR];
     int n_sel;
     int s_chan[kFusedMaxRows];  // this worker's selected candidates: channel and z
     float s_zv[kFusedMaxRows];
-    uint64_t cut;
   };
   __shared__ union {
     SelShared<kFusedThreads, kLinkedTopkMaxN> sel;
@@ -807,57 +909,52 @@ __global__ __launch_bounds__(kFusedThreads, 2) void k_pop_linked(
   for (int i = tid; i < nc; i += kFusedThreads) sh.w.crow[i] = clamp_channel(C[c0 + i], d_ff);
   for (int i = tid; i < nr; i += kFusedThreads) sh.w.rows[i] = kIdentity ? r0 + i : clamp_channel(R[r0 + i], d_ff);
   __syncthreads();
-  // 1. candidate rows, kCandBatch at a time (one round trip each)
-  for (int i0 = 0; i0 < nc; i0 += kCandBatch)
-    cand_rows<T, NV, kCandBatch>(sh.w.crow + i0, min(kCandBatch, nc - i0), Wg, Wu, d, xv, sh.w.cpart,
-                                 z + n_R + c0 + i0, score + c0 + i0, chain ? cand + c0 + i0 : nullptr);
-  // 2. retained rows but the last kTailR (when this worker may have selected candidates)
   const bool sel_here = chain && nc > 0;
-  const int nr_head = sel_here ? max(0, nr - kTailR) : nr;
-  fused_rows<T, NV, true>(sh.w.rows, nr_head, Wg, Wu, WdT, d, xv, sh.w.part, acc, z, r0, nullptr);
+  const uint64_t* cutw = thr + (w % kThrCopies) * kThrStride;
+  // with no retained rows, the stream's (unused) loads read the first candidate's rows
+  const int* rlist = nr > 0 ? sh.w.rows : sh.w.crow;
+  FusedRowBuf<T, NV> A;
+  // 1. candidate rows, kCandBatch at a time; the first retained rows' loads
+  //    go out before the last batch is reduced
+  int i0 = 0;
+  for (; i0 + kCandBatch < nc; i0 += kCandBatch)
+    cand_rows<T, NV, kCandBatch>(sh.w.crow + i0, kCandBatch, Wg, Wu, d, xv, sh.w.cpart, z + n_R + c0 + i0,
+                                 score + c0 + i0, chain ? cand + c0 + i0 : nullptr, sh.w.cz + i0);
+  if (nc > 0) {
+    CandBuf<T, NV, kCandBatch> cb;
+    cand_issue<T, NV, kCandBatch>(cb, sh.w.crow + i0, nc - i0, Wg, Wu, d);
+    fused_issue<T, NV, true>(A, rlist, 0, max(nr, 1), Wg, Wu, WdT, d);
+    cand_consume<T, NV, kCandBatch>(cb, nc - i0, xv, sh.w.cpart, z + n_R + c0 + i0, score + c0 + i0,
+                                    chain ? cand + c0 + i0 : nullptr, sh.w.cz + i0);
+  } else {
+    fused_issue<T, NV, true>(A, rlist, 0, max(nr, 1), Wg, Wu, WdT, d);
+  }
+  // 2. retained rows (and, when the cut is out in time, the selected rows)
+  int done = linked_stream<T, NV, kLinkedNS>(A, rlist, nr, Wg, Wu, WdT, d, d_ff, xv, sh.w.part, acc, sh.w.zr, sel_here,
+                                             cutw, sh.w.crow, sh.w.cz, c0, nc, sh.w.s_chan, sh.w.s_zv, &sh.w.n_sel);
   __syncthreads();
-  // 3. the cut, and this worker's candidates that it selects (its static share
-  //    of C: positions c0 .. c0 + nc - 1, z from their hand-over words)
+  for (int i = tid; i < nr; i += kFusedThreads) z[r0 + i] = sh.w.zr[i];
+  // 3. otherwise the cut now, and this worker's selected candidates
   int ns = 0;
   if (sel_here) {
-    // the words are read beside the poll; one read before every word was
-    // written lacks its valid bit and is read again once the cut is out (the
-    // cut is published only after every word was seen valid)
-    for (int i = tid; i < nc; i += kFusedThreads) sh.w.cw[i] = ld_coh(&cand[c0 + i]);
-    if (tid == 0) {
-      bool ok;
-      const uint64_t e = poll_coh(&thr[(w % kThrCopies) * kThrStride], [](uint64_t v) { return is_valid(v); },
-                                  kPollLimit, ok);
-      if (!ok) st_coh(ctl + kCtlErr, 2u);
-      sh.w.cut = ok ? e : 0;
-    }
-    __syncthreads();
-    for (int i = tid; i < nc; i += kFusedThreads)
-      if (!is_valid(sh.w.cw[i])) sh.w.cw[i] = ld_coh(&cand[c0 + i]);
-    __syncthreads();
-    if (tid == 0) {
-      const uint64_t e = sh.w.cut;
-      const uint32_t cv = (uint32_t)(e >> 32) & 0x7fffffffu;
-      const int tie = (int)(uint32_t)e;
-      int m = 0;
-      for (int i = 0; i < nc; ++i) {
-        const uint32_t xb = (uint32_t)(sh.w.cw[i] >> 32) & 0x7fffffffu;  // bits of |z|
-        if (is_valid(e) && (xb > cv || (xb == cv && c0 + i <= tie))) {
-          sh.w.s_chan[m] = sh.w.crow[i];
-          sh.w.s_zv[m] = __uint_as_float((uint32_t)sh.w.cw[i]);
-          ++m;
-        }
+    if (done < 0) {
+      if (tid == 0) {
+        bool ok;
+        const uint64_t e = poll_coh(cutw, [](uint64_t v) { return is_valid(v); }, kPollLimit, ok);
+        if (!ok) st_coh(ctl + kCtlErr, 2u);
+        sh.w.n_sel = ok ? linked_select(e, sh.w.crow, sh.w.cz, c0, nc, sh.w.s_chan, sh.w.s_zv) : 0;
       }
-      sh.w.n_sel = m;
+      __syncthreads();
+      done = 0;
     }
-    __syncthreads();
     ns = sh.w.n_sel;
   }
-  //    then the last retained rows and the selected rows, their loads together
-  for (int t0 = 0, s0 = 0; nr_head + t0 < nr || s0 < ns; t0 += kTailR, s0 += kSelRowsPerPass)
-    tail_rows<T, NV, kTailR, kSelRowsPerPass>(sh.w.rows + nr_head + t0, max(0, min(kTailR, nr - nr_head - t0)),
-                                              sh.w.s_chan + s0, sh.w.s_zv + s0, max(0, min(kSelRowsPerPass, ns - s0)),
-                                              Wg, Wu, WdT, d, d_ff, xv, sh.w.tpart, acc, z + r0 + nr_head + t0);
+  for (int s0 = done; s0 < ns; s0 += kLinkedNS) {
+    u32x4 ws[kLinkedNS][NV];
+    const int m = min(kLinkedNS, ns - s0);
+    sel_issue<T, NV, kLinkedNS>(ws, sh.w.s_chan + s0, m, WdT, d, d_ff);
+    sel_consume<T, NV, kLinkedNS>(ws, sh.w.s_zv + s0, m, acc);
+  }
   // 4. partial y, slice-major: column c of worker w at ((c / kFinCols) * nW + w) * kFinCols + c % kFinCols
   static_assert(kFinCols % V == 0, "a thread's columns lie in one slice");
 #pragma unroll

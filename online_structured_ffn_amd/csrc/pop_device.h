@@ -593,7 +593,7 @@ __device__ __forceinline__ bool is_valid(uint64_t w) { return (w >> 63) != 0; }
 // candidates with plain stores.  A round limit reached sets *err (coherent);
 // the step goes on with score 0 for the missing candidates.
 template <int NTH, int MAXN>
-__device__ void topk_threshold_linked(const uint64_t* __restrict__ cand, int n, int k, const int32_t* __restrict__ C,
+__device__ __forceinline__ void topk_threshold_linked(const uint64_t* __restrict__ cand, int n, int k, const int32_t* __restrict__ C,
                                       int32_t* __restrict__ positions, int32_t* __restrict__ selected,
                                       uint64_t* __restrict__ thr, int n_copies, int stride, SelShared<NTH, MAXN>& sh,
                                       int poll_limit, uint32_t* err) {
@@ -614,16 +614,20 @@ __device__ void topk_threshold_linked(const uint64_t* __restrict__ cand, int n, 
     got[j] = tid + j * NTH >= n;
   }
   for (int round = 0;; ++round) {
+    // every word of the round is requested before any is examined (one
+    // round trip a round; words already seen, and slots past n, read a valid
+    // word again and are ignored)
+    uint64_t wv[EM];
+#pragma unroll
+    for (int j = 0; j < EM; ++j)
+      if (j * NTH < n) wv[j] = ld_coh(&cand[min(tid + j * NTH, n - 1)]);  // block-uniform condition
     bool all = true;
 #pragma unroll
     for (int j = 0; j < EM; ++j) {
-      if (!got[j]) {
-        const uint64_t w = ld_coh(&cand[tid + j * NTH]);
-        if (is_valid(w)) {
-          got[j] = true;
-          vb[j] = (uint32_t)(w >> 32) & 0x7fffffffu;
-          atomicAdd(&sh.hA[sel_slot((int)(vb[j] >> kBinShift))], 1u);
-        }
+      if (j * NTH < n && !got[j] && is_valid(wv[j])) {
+        got[j] = true;
+        vb[j] = (uint32_t)(wv[j] >> 32) & 0x7fffffffu;
+        atomicAdd(&sh.hA[sel_slot((int)(vb[j] >> kBinShift))], 1u);
       }
       all &= got[j];
     }
@@ -676,6 +680,7 @@ __device__ void topk_threshold_linked(const uint64_t* __restrict__ cand, int n, 
   __syncthreads();
   SelTarget t0 = sh.tgt[0];
   int tie_pos;
+  bool published = false;
   if (t0.count <= kSelResolve) {
     // ---- small bin: gather its keys and rank each against the others
     if (tid == 0) sh.rcnt = 0;
@@ -692,41 +697,36 @@ __device__ void topk_threshold_linked(const uint64_t* __restrict__ cand, int n, 
       }
     }
     __syncthreads();
+    // Wave 0 ranks the bin's keys from registers (lane l holds key l): in
+    // ascending order (smaller value first, on equal values the larger index
+    // first) the key with t0.rank bin keys before it is the key of global
+    // rank r, and the cut is that key's own (value, index): the selected
+    // keys are those after it in this order, i.e. of larger value, or of
+    // equal value and an index up to its own.  The wave publishes the cut
+    // at once, with no block barrier in between.
     const int mb = t0.count;
-    // ascending order: smaller value first, on equal values the larger index first
-    if (tid < mb) {
-      const uint32_t vv = sh.rv[tid];
-      const int ii = sh.ri[tid];
-      int below = 0, lt = 0, eqn = 0;
+    if (tid < 64) {
+      const uint32_t vv = tid < mb ? sh.rv[tid] : 0xffffffffu;
+      const int ii = tid < mb ? sh.ri[tid] : -1;
+      int below = 0;
       for (int e = 0; e < mb; ++e) {
-        const uint32_t ve = sh.rv[e];
-        lt += ve < vv ? 1 : 0;
-        eqn += ve == vv ? 1 : 0;
-        below += (ve < vv || (ve == vv && sh.ri[e] > ii)) ? 1 : 0;
+        const uint32_t ve = (uint32_t)__builtin_amdgcn_readlane((int)vv, e);
+        const int ie = __builtin_amdgcn_readlane(ii, e);
+        below += (ve < vv || (ve == vv && ie > ii)) ? 1 : 0;
       }
-      if (below == t0.rank) {
-        SelTarget u;
-        u.prefix = vv;
-        u.shift = 0;
-        u.rank = t0.rank - lt;  // q: keys of value v below the target rank
-        u.count = eqn;          // m: keys of value v
-        u.beyond = 0;
-        sh.tgt[0] = u;
+      const uint64_t hit = __ballot(tid < mb && below == t0.rank);
+      const int src = hit != 0 ? (int)__builtin_ctzll(hit) : 0;
+      const uint32_t cv = (uint32_t)__builtin_amdgcn_readlane((int)vv, src);
+      const int tie = __builtin_amdgcn_readlane(ii, src);
+      for (int c = tid; c < n_copies; c += 64) st_coh(&thr[c * stride], pack_valid(cv, (uint32_t)tie));
+      if (tid == 0) {
+        sh.tgt[1].prefix = cv;
+        sh.scan[0][0] = tie;
       }
     }
+    published = true;
     __syncthreads();
-    t0 = sh.tgt[0];
-    // the selected keys of value v are the (m - q) of lowest index
-    const int m = t0.count, q = t0.rank;
-    if (tid == 0) sh.scan[0][0] = q == 0 ? n : -1;
-    __syncthreads();
-    if (q > 0 && q < m && tid < mb && sh.rv[tid] == t0.prefix) {
-      const int ii = sh.ri[tid];
-      int lower = 0;  // keys of value v with a lower index
-      for (int e = 0; e < mb; ++e) lower += (sh.rv[e] == t0.prefix && sh.ri[e] < ii) ? 1 : 0;
-      if (lower == m - q - 1) sh.scan[0][0] = ii;
-    }
-    __syncthreads();
+    t0.prefix = sh.tgt[1].prefix;
     tie_pos = sh.scan[0][0];
   } else {
     // ---- large bin: the general select over every key (owner layout)
@@ -767,7 +767,7 @@ __device__ void topk_threshold_linked(const uint64_t* __restrict__ cand, int n, 
     t0 = t[0];
   }
   const uint32_t cv = t0.prefix;
-  if (tid < n_copies) st_coh(&thr[tid * stride], pack_valid(cv, (uint32_t)tie_pos));
+  if (!published && tid < n_copies) st_coh(&thr[tid * stride], pack_valid(cv, (uint32_t)tie_pos));
   if (positions == nullptr && selected == nullptr) return;
   // ---- the list, ascending (after the cut is out): flags in LDS, then owner-layout scan
   __syncthreads();  // sh.scan and the LDS buffers are reused below
