@@ -521,7 +521,7 @@ def bench_ffn(args, w, mods, L, T, steps, warmup, detail):
     # the GPU busy while the host enqueues, so the traced kernels run back to back.
     S = min(args.kernel_steps, T)
     vec = 8 if e == 2 else 4
-    fused = B == 1 and d <= 4 * 256 * vec
+    fused = B == 1 and d <= 4 * metrics.LINKED_THREADS * vec
     linked = fused and 0 < n_C <= 4096 and k > 0
     labels_pre = (["k_colsq_slices"] if n_tok <= 8192 else ["k_colsq_partial", "k_sum_chunks(s2)"]) + [
         "k_importance_items", "k_partition"]
@@ -603,10 +603,8 @@ def bench_ffn(args, w, mods, L, T, steps, warmup, detail):
 
     roofline = None
     if linked:
-        nv = -(-d // (256 * vec))
-        tname = "pop::bf16s" if e == 2 else "float"
         dom, dom_bytes = "k_pop_linked", metrics.linked_bytes(d, n_R, n_C, k, e)
-        dom_symbol = f"pop::k_pop_linked<{tname}, {1 if nv <= 1 else 2 if nv <= 2 else 4}, false>"
+        dom_symbol = metrics.linked_symbol(d, e)
         tb = profiling.traffic_bytes(dom_symbol) if w.name == MAIN_WORKLOAD else None
         dom_us = kus[dom]
         dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
@@ -1056,7 +1054,7 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
     dom_gbps = kbytes[dom] / (kus[dom] * 1e-6) / 1e9 if dom else None
     # the same kernel at the same shape as the FFN workload's profiled one: its counters apply
     same_ffn = dom == "k_pop_linked" and (d, d_ff, w.r, w.gamma, B, w.dtype) == (4096, 11008, 0.299, 0.1, 1, "bf16")
-    tb = profiling.traffic_bytes("pop::k_pop_linked<pop::bf16s, 2, false>") if same_ffn else None
+    tb = profiling.traffic_bytes(metrics.linked_symbol(d, e)) if same_ffn else None
     cpu = None if args.no_cpu_baseline else cpu_baseline_layer(w, T, args.cpu_seconds)
     out = {
         "metric": "decoder-layer decode tokens/s per layer (dense attention + POP FFN); HBM GB/s vs peak",

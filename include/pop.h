@@ -203,14 +203,15 @@ size_t pop_decode_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff);
  *              offset POP_DECODE_WS_Z_OFFSET + align_up(4 * batch * d_ff + 16,
  *              256) the candidate scores (fp32 [n_C]).
  * Kernels at batch 1 with a candidate top-k (n_C >= 1, k >= 1, n_C <= 4096,
- * d <= 1024 vectors of 16 bytes): two launches.  In the first, workgroup 0 is
- * the candidate top-k and every other workgroup (a worker) streams an even
- * share of the candidates' gate/up rows (handing each |z| to the top-k through
- * a valid-tagged word), then of the retained channels' gate, up and W_downT
- * rows (z and its down contribution in one pass); the top-k publishes the cut
- * and each worker adds the W_downT rows of its own candidates that the cut
- * selects (their loads issued with its last retained rows), then stores its
- * partial y.  The second adds the partials in a fixed order into y and clears
+ * d <= 2048 vectors of 16 bytes): two launches.  In the first (512-thread
+ * workgroups, at most one per CU), workgroup 0 is the candidate top-k and
+ * every other workgroup (a worker) streams an even share of the candidates'
+ * gate/up rows (handing each |z| to the top-k through a valid-tagged word),
+ * then of the retained channels' gate, up and W_downT rows (z and its down
+ * contribution in one pass); the top-k publishes the cut and each worker adds
+ * the W_downT rows of its own candidates that the cut selects (their loads
+ * issued with its last retained rows when the cut is out by then, else after
+ * its rows), then stores its partial y.  The second adds the partials in a fixed order into y and clears
  * the hand-over words.  The grid never exceeds what the device holds at once
  * and every in-kernel wait is bounded (see POP_DECODE_WS_Z_OFFSET for the
  * error word).  Batch 1 without a top-k (no candidates, k = 0): the retained

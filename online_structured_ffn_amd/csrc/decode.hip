@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 // launch wrote.
 // Launch-shape tunables (overridable with -D for sweeps).
 #ifndef POP_FUSED_RBLOCKS
-#define POP_FUSED_RBLOCKS 512  // most blocks for the retained rows
+#define POP_FUSED_RBLOCKS 256  // most blocks for the retained rows (one per CU)
 #endif
 #ifndef POP_FUSED_CROWS
 #define POP_FUSED_CROWS 4  // candidate rows per block
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 // contiguous run of n_part * kFinCols floats.
 constexpr int kFinCols = POP_FIN_COLS;
 #ifndef POP_FUSED_THREADS
-#define POP_FUSED_THREADS 256  // threads of a k_pop_step block
+#define POP_FUSED_THREADS 512  // threads of a k_pop_step / k_pop_linked block
 #endif
 constexpr int kFusedThreads = POP_FUSED_THREADS;
 constexpr int kFusedWaves = kFusedThreads / 64;
@@ -711,7 +711,10 @@ constexpr int kPollLimit = 1 << 20;
 constexpr int kLinkedNS = POP_LINKED_NS;  // selected rows carried by the last row batches (and per later pass)
 constexpr int kThrCopies = 32;  // copies of the published cut
 constexpr int kThrStride = 16;  // 64-bit words between copies (128 bytes)
-constexpr int kCandBatch = 8;  // candidate rows whose loads a worker issues together
+#ifndef POP_CAND_BATCH
+#define POP_CAND_BATCH 8
+#endif
+constexpr int kCandBatch = POP_CAND_BATCH;  // candidate rows whose loads a worker issues together
 // The control words (1 KB), then the hand-over words: the candidate words (at
 // most kLinkedTopkMaxN) and the copies of the cut.  A fixed region at the
 // start of every decode workspace that no other call writes; k_pop_finish
@@ -866,7 +869,7 @@ __device__ __forceinline__ int linked_stream(FusedRowBuf<T, NV>& A, const int* r
 }
 
 #ifndef POP_LINKED_MINB
-#define POP_LINKED_MINB 2  // workgroups of k_pop_linked resident per CU
+#define POP_LINKED_MINB 1  // workgroups of k_pop_linked resident per CU
 #endif
 template <typename T, int NV, bool kIdentity>
 __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(

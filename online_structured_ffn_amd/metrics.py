@@ -55,13 +55,23 @@ def prefill_ffn_flops(n_tokens: int, d: int, d_ff: int) -> int:
 
 
 # Launch shape of the batch-1 step with candidates (mirrors the library: one
-# workgroup runs the top-k, the others take static shares of C and R, one per
-# 8 rows up to 511 of them; a second launch adds their partial sums).
-LINKED_MAX_WORKERS = 511
+# 512-thread workgroup runs the top-k, the others take static shares of C and
+# R, one per 8 rows up to 255 of them, one workgroup per CU; a second launch
+# adds their partial sums).
+LINKED_THREADS = 512
+LINKED_MAX_WORKERS = 255
 
 
 def linked_workers(n_R: int, n_C: int) -> int:
     return max(1, min((n_R + n_C + 7) // 8, LINKED_MAX_WORKERS))
+
+
+def linked_symbol(d: int, e: int) -> str:
+    """The kernel symbol of the batch-1 step for row width d and element
+    bytes e (its template takes the 16-byte vectors per thread: 1, 2 or 4)."""
+    nv = -(-d // (LINKED_THREADS * (16 // e)))
+    tname = "pop::bf16s" if e == 2 else "float"
+    return f"pop::k_pop_linked<{tname}, {1 if nv <= 1 else 2 if nv <= 2 else 4}, false>"
 
 
 def linked_bytes(d: int, n_R: int, n_C: int, k: int, e: int) -> int:

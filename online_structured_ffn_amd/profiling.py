@@ -221,14 +221,16 @@ def _algorithmic_reads(workload: str = "ffn", steps: int = 4):
             "pop::k_attn_decode<pop::bf16s, 128>": int(2 * Hkv * keys * hd * e),
         }
     w = configs.BY_NAME["llama2_7b_ffn_b1"]
+    from .metrics import linked_symbol
     from .pop import pop_partition_counts
     c = pop_partition_counts(w.d_ff, w.r, w.gamma)
     n_tok, d, d_ff, e = w.prompt_batch * w.prompt_len, w.d, w.d_ff, 2
     n_A = c["n_R"] + c["n_C"]
     return {
         # gate and up rows of R u C, W_downT rows of R u S, x, the index lists
-        "pop::k_pop_linked<pop::bf16s, 2, false>": (2 * n_A + c["n_R"] + c["k"]) * d * e + d * e + 4 * n_A,
-        "pop::k_pop_step<pop::bf16s, 2, true, 0>": 3 * d_ff * d * e + d * e,
+        linked_symbol(d, e): (2 * n_A + c["n_R"] + c["k"]) * d * e + d * e + 4 * n_A,
+        linked_symbol(d, e).replace("k_pop_linked", "k_pop_step").replace(", false>", ", true, 0>"):
+            3 * d_ff * d * e + d * e,
         "pop::k_colsq_slices<pop::bf16s>": n_tok * d * e,
         "pop::k_importance_items<pop::bf16s>": d_ff * d * e + 4 * d,
         "pop::k_read_probe": PROBE_BYTES,

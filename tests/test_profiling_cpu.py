@@ -38,7 +38,7 @@ def test_traffic_summary_calibration_and_digest(tmp_path, monkeypatch, probe_sca
     rd, wr = str(tmp_path / "rd"), str(tmp_path / "wr")
     probe = "pop::k_read_probe(unsigned char const*, int*)"
     fill = "void at::native::vectorized_elementwise_kernel<16, at::native::FillFunctor<unsigned char>>(int)"
-    kern = "void pop::k_pop_linked<pop::bf16s, 2, false>(args)"
+    kern = "void pop::k_pop_linked<pop::bf16s, 1, false>(args)"
     n128 = PROBE * probe_scale / 128
     _write_counters(rd, [
         (1, probe, 262144, {"TCC_EA0_RDREQ_sum": n128, "TCC_EA0_RDREQ_128B_sum": n128}),
@@ -56,13 +56,13 @@ def test_traffic_summary_calibration_and_digest(tmp_path, monkeypatch, probe_sca
     out = str(tmp_path / "traffic.md")
     monkeypatch.setattr(prof, "_algorithmic_reads", lambda *a, **k: {})
     prof.traffic(rd, wr, None, out)
-    rb, wb = prof.traffic_bytes("pop::k_pop_linked<pop::bf16s, 2, false>", out)
+    rb, wb = prof.traffic_bytes("pop::k_pop_linked<pop::bf16s, 1, false>", out)
     assert rb == round((2000 * 128 + 320) / probe_scale)
     assert wb == round((20 * 64 + 30 * 32) / fill_scale)
     # a summary taken on other kernel sources is void
     text = open(out).read().replace(f"digest={prof.source_digest()}", "digest=0000000000000000")
     open(out, "w").write(text)
-    assert prof.traffic_bytes("pop::k_pop_linked<pop::bf16s, 2, false>", out) is None
+    assert prof.traffic_bytes("pop::k_pop_linked<pop::bf16s, 1, false>", out) is None
 
 
 def test_committed_traffic_summary_parses():
