@@ -1000,8 +1000,9 @@ def bench_layer(args, w, np, torch, metrics, pop, synth):
         head = [{"k_gemv_kmajor(qkv)": "k_gemm_decode(qkv)", "k_gemv_kmajor(o)": "k_gemm_decode(o)"
                  }.get(n, n) for n in head]
     if B > 1:   # the library's batch-2..64 FFN kernels (bf16, matrix cores), then the residual add
+        # the selected rows ride in the retained rows' launch (their chunks' shares of C)
         mfma_tail = (["k_gateup_lds"] + (["k_topk"] if n_C > 4096 else [])
-                     + ["k_down_stream.R+topk" if n_C <= 4096 else "k_down_stream.R", "k_down_stream.S", "k_sum_few(y)"])
+                     + ["k_down_stream.R+S+topk" if n_C <= 4096 else "k_down_stream.R+S", "k_sum_few(y)"])
         dense_tail = ["k_gateup_lds(dense)", "k_down_stream(dense)", "k_sum_few(y)"]
     linked = B == 1 and 0 < n_C <= 4096 and k > 0
     # at batch 1 the FFN's last kernel adds its output into the residual stream (no k_add)

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 #define POP_SPLIT_B 100  // percent of the retained blocks beside the top-k
 #endif
 #ifndef POP_FIN_COLS
-#define POP_FIN_COLS 16  // columns of y per k_pop_finish block (16, 32 or 64)
+#define POP_FIN_COLS 32  // columns of y per k_pop_finish block (16, 32 or 64)
 #endif
 // Retained partial sums are stored slice-major: the value of column c of
 // retained block rb sits at ((c / kFinCols) * n_part + rb) * kFinCols +
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
 // The last launch of the batch-1 step.  Block s owns the kFinCols columns
 // c0 = s * kFinCols + [0, kFinCols) of y and adds, in a fixed order, the
 // n_part retained partial sums and (kSel) the k selected rows' z * W_downT,
-// then writes y itself (no partial of its own).  1024 threads = 16 waves:
+// then writes y itself (no partial of its own).  512 threads = 8 waves:
 //   partial rows (slice-major, contiguous): kFinCols / 4 lanes x 4 floats per row;
 //   selected rows: kFinCols / V lanes x 16 bytes per row; row j of S is
 //   (ch, z) = (sel[j], z[zoff + pos[j]]).
@@ -525,7 +525,10 @@ __global__ __launch_bounds__(kFusedThreads) void k_pop_step(POP_STEP_PARAMS) {
 // kFinRowsPerBatch selected rows and kFinPB * PPB partials every load is in
 // flight at once.  The per-lane sums are reduced across lanes (shuffles), then
 // across waves in wave order (LDS).
-constexpr int kFinThreads = 1024;
+#ifndef POP_FIN_THREADS
+#define POP_FIN_THREADS 512
+#endif
+constexpr int kFinThreads = POP_FIN_THREADS;
 // Control word of the single-launch batch-1 step: the sticky error word.
 constexpr int kCtlErr = 0;
 constexpr int kFinRowsPerBatch = 1280;  // selected rows whose loads are in flight together
@@ -1111,6 +1114,9 @@ static DownPlan plan_down(int n_live, int B, int d, int vec) {
 // decreasing in n, so the value at n = d_ff bounds every call).  The retained
 // rows aim at POP_DOWN_BLOCKS blocks; the selected rows, whose launch waits
 // for the top-k, at POP_DOWN_S_BLOCKS.
+#ifndef POP_DOWN_FOLD
+#define POP_DOWN_FOLD 1  // 0: the selected rows in a launch of their own
+#endif
 #ifndef POP_DOWN_BLOCKS
 #define POP_DOWN_BLOCKS 1024
 #endif
@@ -1119,7 +1125,7 @@ static DownPlan plan_down(int n_live, int B, int d, int vec) {
 #endif
 static int down_mfma_chunks(int n, int d, int blocks = POP_DOWN_BLOCKS) {
   const int slices = (d + 63) / 64;
-  int want = (blocks + slices - 1) / slices;
+  int want = blocks / slices;  // the whole grid within the block budget
   const int by_rows = (n + kDsRows - 1) / kDsRows;
   if (want > by_rows) want = by_rows;
   const int least = (n + kDsMaxRows - 1) / kDsMaxRows;
@@ -1265,11 +1271,29 @@ static void launch_select(hipStream_t st, const float* score, int n_C, const int
 // which must then be the positions and channels the down stage reads (Q and
 // sel).  On the matrix cores the top-k (up to 4096 candidates) shares a launch
 // with the retained rows' product, and the selected rows follow.
+// Blocks of `threads` threads of kernel the device holds at once (0 if the
+// runtime cannot tell); cached per device and kernel.
+static int resident_blocks_of(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, kernel);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess)
+    return 0;
+  return cache[key] = cus * per;
+}
+
 template <typename T>
 static void launch_down(hipStream_t st, const float* z, int B, int n_A, const void* WdT, int d, int d_ff,
                         const int32_t* R, int n_R, const int32_t* sel, const int32_t* Q, int k, float* y,
                         float* partial, const float* score = nullptr, const int32_t* C = nullptr, int n_C = 0,
-                        int32_t* topk_Q = nullptr, int32_t* topk_sel = nullptr) {
+                        int32_t* topk_Q = nullptr, int32_t* topk_sel = nullptr, const DecodeWs* lw = nullptr) {
   const bool topk = score != nullptr && n_C > 0 && k > 0;
   if (B == 0) {
     if (topk) launch_select(st, score, n_C, C, k, topk_Q, topk_sel);
@@ -1278,16 +1302,37 @@ static void launch_down(hipStream_t st, const float* z, int B, int n_A, const vo
   const int n_live = n_R + k;
   if (use_mfma<T>(B) && n_live > 0) {
     const bool identity = R == nullptr && k == 0;
+    const bool topk_in = topk && n_C <= 4096;
+    // the retained rows' launch: every block resident at once (the top-k
+    // block included), so that no block starts after others have finished
+    const int MTs = B <= 16 ? 1 : B <= 32 ? 2 : 4;
+    const void* kr = MTs == 1 ? reinterpret_cast<const void*>(&k_down_stream<1, false, 2>)
+                   : MTs == 2 ? reinterpret_cast<const void*>(&k_down_stream<2, false, 2>)
+                              : reinterpret_cast<const void*>(&k_down_stream<4, false, 2>);
+    int budget = resident_blocks_of(kr, 256);
+    if (budget <= 0 || budget > POP_DOWN_BLOCKS) budget = POP_DOWN_BLOCKS;
     int rpcR, nRc, rpcS, nSc;
-    down_mfma_plan(n_R, d, POP_DOWN_BLOCKS, &rpcR, &nRc);
+    down_mfma_plan(n_R, d, budget - (topk_in ? 1 : 0), &rpcR, &nRc);
     down_mfma_plan(k, d, POP_DOWN_S_BLOCKS, &rpcS, &nSc);
     const int ncol = (d + 63) / 64;
-    const bool topk_in = topk && n_C <= 4096;
     if (topk && !topk_in) launch_select(st, score, n_C, C, k, topk_Q, topk_sel);
     const int nb0 = topk_in ? 1 : 0;
+    // The selected rows join the retained rows' launch: each chunk adds the
+    // selected candidates of its share of C.  With the top-k in the launch
+    // (and the decode workspace's hand-over words at hand) the top-k block
+    // hands the cut over inside it (PHASE 2); with the selection given, the
+    // chunks read it from the list (PHASE 3): the same sums either way.
+    const int n_Cs = n_A - n_R;
+    const bool shares_fit = !identity && k > 0 && nRc > 0 && nRc <= 64 && n_Cs > 0 &&
+                            (n_Cs + nRc - 1) / nRc <= kDsMaxRows;
+    const bool fold = POP_DOWN_FOLD && shares_fit && topk_in && lw != nullptr;
+    const bool given = POP_DOWN_FOLD && shares_fit && !topk_in;
+    const CutLink link = fold ? CutLink{lw->hand + kLinkedTopkMaxN, lw->ctl + kCtlErr, kThrCopies, kThrStride,
+                                        kPollLimit}
+                              : CutLink{nullptr, nullptr, 0, 0, 0};
 #define POP_DN_MFMA(MT, ID, PH, grid, rb, re, rpc, cb, nb)                                                        \
   POP_LAUNCH((k_down_stream<MT, ID, PH>), dim3(grid), dim3(256), 0, st, z, n_A, B, (const bf16s*)WdT, d, d_ff, R, \
-             n_R, sel, Q, rb, re, rpc, cb, partial, nb, score, n_C, k, C, topk_Q, topk_sel)
+             n_R, sel, Q, rb, re, rpc, cb, partial, nb, score, n_C, k, C, topk_Q, topk_sel, link)
 #define POP_DN_MFMA_MT(...)      \
   if (B <= 16) {                 \
     POP_DN_MFMA(1, __VA_ARGS__); \
@@ -1298,6 +1343,10 @@ static void launch_down(hipStream_t st, const float* z, int B, int n_A, const vo
   }
     if (identity) {
       POP_DN_MFMA_MT(true, 0, ncol * nRc, 0, n_R, rpcR, 0, 0)
+    } else if (fold) {
+      POP_DN_MFMA_MT(false, 2, 1 + ncol * nRc, 0, n_R, rpcR, 0, 1)
+    } else if (given) {
+      POP_DN_MFMA_MT(false, 3, ncol * nRc, 0, n_R, rpcR, 0, 0)
     } else {
       if (nb0 + nRc > 0) {
         POP_DN_MFMA_MT(false, 1, nb0 + ncol * nRc, 0, n_R, rpcR, 0, nb0)
@@ -1309,14 +1358,17 @@ static void launch_down(hipStream_t st, const float* z, int B, int n_A, const vo
 #undef POP_DN_MFMA_MT
 #undef POP_DN_MFMA
     const int64_t n_out = (int64_t)B * d;
-    const int nch = nRc + nSc;
+    const int nch = fold || given ? nRc : nRc + nSc;
     const dim3 sgrid((unsigned)((n_out + 255) / 256));
+    // the cut's words go back to zero once the launch that read them is done
+    uint64_t* rst = fold ? link.thr : nullptr;
+    const int nrst = fold ? kThrCopies : 0;
     if (nch <= 16) {
-      POP_LAUNCH(k_sum_few<16>, sgrid, dim3(256), 0, st, (const float*)partial, nch, n_out, y);
+      POP_LAUNCH(k_sum_few<16>, sgrid, dim3(256), 0, st, (const float*)partial, nch, n_out, y, rst, nrst, kThrStride);
     } else if (nch <= 32) {
-      POP_LAUNCH(k_sum_few<32>, sgrid, dim3(256), 0, st, (const float*)partial, nch, n_out, y);
+      POP_LAUNCH(k_sum_few<32>, sgrid, dim3(256), 0, st, (const float*)partial, nch, n_out, y, rst, nrst, kThrStride);
     } else if (nch <= 64) {
-      POP_LAUNCH(k_sum_few<64>, sgrid, dim3(256), 0, st, (const float*)partial, nch, n_out, y);
+      POP_LAUNCH(k_sum_few<64>, sgrid, dim3(256), 0, st, (const float*)partial, nch, n_out, y, rst, nrst, kThrStride);
     } else {
       POP_LAUNCH(k_sum_chunks<0>, dim3((unsigned)((n_out + 31) / 32)), dim3(1024), 0, st, (const float*)partial, nch,
                  n_out, y, (unsigned int*)nullptr, 0);
@@ -1427,21 +1479,7 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
 // Workgroups of `kernel` (kFusedThreads threads) the current device holds at
 // once: its compute units times the occupancy per unit (cached per device and
 // kernel; device attributes only, no stream work).
-static int resident_blocks(const void* kernel) {
-  static std::mutex mu;
-  static std::map<std::pair<int, const void*>, int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  const auto key = std::make_pair(dev, kernel);
-  const auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
-  int cus = 0, per = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kFusedThreads, 0) != hipSuccess)
-    return 0;
-  return cache[key] = cus * per;
-}
+static int resident_blocks(const void* kernel) { return resident_blocks_of(kernel, kFusedThreads); }
 
 // The batch-1 step as k_pop_linked + k_pop_finish.  Returns false, having
 // launched nothing, when the step has no candidate top-k (no candidates, or
@@ -1683,7 +1721,7 @@ extern "C" pop_status pop_decode_ffn(const void* x, int32_t batch, int32_t d, co
   POP_DISPATCH(dt, launch_gateup, st, x, batch, d, W_gate, W_up, d_ff, Rk, n_R, Ck, n_C, w.z, w.score);
   int32_t* sel = selected != nullptr ? selected : w.sel;  // the down stage reads the selected channels here
   POP_DISPATCH(dt, launch_down, st, w.z, batch, n_R + n_C, W_downT, d, d_ff, Rk, n_R, sel, w.Q, k, y,
-               (float*)w.down, w.score, Ck, n_C, w.Q, sel);
+               (float*)w.down, w.score, Ck, n_C, w.Q, sel, &w);
   return launched();
 }
 

@@ -53,6 +53,16 @@ struct MoeRows {
   int64_t w_stride;
 };
 
+// Hand-over of the candidate cut inside one launch of k_down_stream (PHASE
+// 2): the top-k workgroup publishes it to n_copies words thr[c * stride]
+// (coherent), each workgroup polls one copy at most poll_limit times and, if
+// that runs out, sets *err to 3 and adds no selected row.
+struct CutLink {
+  uint64_t* thr;
+  uint32_t* err;
+  int n_copies, stride, poll_limit;
+};
+
 // ---------------------------------------------------------------- gate / up, rows streamed through LDS
 // The same product with the weight rows read by LDS-direct loads: one load
 // instruction moves 1 KB of one or a few rows (full 128-byte lines; a
@@ -320,6 +330,14 @@ __global__ __launch_bounds__(256) void k_gateup_lds(const bf16s* __restrict__ x,
 // PHASE 1: blocks [0, nb0) run the candidate top-k instead (one block), so it
 // overlaps the retained rows' product; the selected rows follow in a PHASE 0
 // launch.
+// PHASE 2: as PHASE 1, but the top-k block publishes the cut (CutLink) before
+// it writes the lists;
+// after its retained rows, block (slice, chunk) takes the chunk's even share
+// of the candidate positions (n_A - n_R of them), keeps those the cut selects
+// (in position order) and streams their W_downT rows into the same
+// accumulators: one launch and one partial per block for R and S together.
+// PHASE 3: the same rows from a given selection (sel and pos, positions
+// ascending) instead of a top-k: the same sums, bit for bit.
 #ifndef POP_DS_NS
 #define POP_DS_NS 4
 #endif
@@ -335,6 +353,8 @@ struct DsShared {
   uint16_t zs[2][16 * MT * kDsLd];  // [token][row of the sub-chunk]
   int rch[kDsMaxRows];
   int zcol[kDsMaxRows];
+  uint64_t cut;  // PHASE 2: the cut as read
+  int wsum[4];   // PHASE 2: selected candidates per wave
 };
 
 template <int MT, bool kIdentity, int PHASE, bool kMoe = false>
@@ -346,9 +366,10 @@ __global__ __launch_bounds__(256) void k_down_stream(const float* __restrict__ z
                                                      float* __restrict__ partial, int nb0,
                                                      const float* __restrict__ score, int n_C, int k,
                                                      const int32_t* __restrict__ C, int32_t* __restrict__ Q,
-                                                     int32_t* __restrict__ S, MoeRows moe = {}) {
+                                                     int32_t* __restrict__ S, CutLink link, MoeRows moe = {}) {
   using DS = DsShared<MT>;
-  constexpr size_t kTs = PHASE == 1 ? topk_lds_bytes<256>(4096) : 0;  // the top-k block (up to 4096 candidates)
+  // the top-k block (up to 4096 candidates)
+  constexpr size_t kTs = PHASE == 1 ? topk_lds_bytes<256>(4096) : PHASE == 2 ? sizeof(SelShared<256, 4096>) : 0;
   constexpr size_t kSmem = sizeof(DS) > kTs ? sizeof(DS) : kTs;
   __shared__ __align__(16) unsigned char smem[kSmem];
   int o0 = 0, cnt = B;  // the launch's z rows: all B, or the expert's routed pairs (B = every pair)
@@ -373,15 +394,35 @@ __global__ __launch_bounds__(256) void k_down_stream(const float* __restrict__ z
       return;
     }
   }
+  if constexpr (PHASE == 2) {
+    if ((int)blockIdx.x < nb0) {  // the cut first (published), then the lists
+      topk_threshold_linked<256, 4096>(nullptr, n_C, k, C, Q, S, link.thr, link.n_copies, link.stride,
+                                       *reinterpret_cast<SelShared<256, 4096>*>(smem), link.poll_limit, link.err,
+                                       score);
+      return;
+    }
+  }
   DS& sh = *reinterpret_cast<DS*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int ncol = (d + 63) / 64;
-  const int idx = (int)blockIdx.x - (PHASE == 1 ? nb0 : 0);
+  const int idx = (int)blockIdx.x - (PHASE >= 1 ? nb0 : 0);
   const int c0 = (idx % ncol) * 64;
   const int cl = idx / ncol;
   const int q0 = row_begin + cl * rows_per_chunk;
-  const int nrows = min(row_end, q0 + rows_per_chunk) - q0;  // >= 1: the host launches no empty chunk
+  int nrows = min(row_end, q0 + rows_per_chunk) - q0;  // >= 1: the host launches no empty chunk
+  // PHASE >= 2: this chunk's share [ca, cb) of the candidate positions; PHASE
+  // 2 reads their scores now, long before it needs them
+  const int nchunks = (row_end - row_begin + rows_per_chunk - 1) / rows_per_chunk;
+  const int ca = (int)((int64_t)(n_A - n_R) * cl / nchunks), cb = (int)((int64_t)(n_A - n_R) * (cl + 1) / nchunks);
+  constexpr int kScPer = kDsMaxRows / 256;
+  uint32_t scv[kScPer];
+#pragma unroll
+  for (int u = 0; u < kScPer; ++u) scv[u] = 0u;
+  if constexpr (PHASE == 2) {
+#pragma unroll
+    for (int u = 0; u < kScPer; ++u) scv[u] = value_bits(score[min(ca + kScPer * tid + u, max(cb - 1, 0))]);
+  }
   {  // every index load in flight at once (clamped to the range; stores masked)
     constexpr int kPer = kDsMaxRows / 256;
     int a[kPer], b[kPer];
@@ -463,46 +504,126 @@ __global__ __launch_bounds__(256) void k_down_stream(const float* __restrict__ z
       }
     }
   };
-  // Straight-line ring (the count of sub-chunks padded to a multiple of kDsNS;
-  // padded ones carry z = 0): the compiler then waits for each sub-chunk's
-  // loads and no more.
-  const int nsub = (nrows + kDsRows - 1) / kDsRows;
-  const int T = (nsub + kDsNS - 1) / kDsNS * kDsNS;
+  // Straight-line ring (the count of sub-chunks padded to a multiple of the
+  // ring depth; padded ones carry z = 0): the compiler then waits for each
+  // sub-chunk's loads and no more.
   Ld ring[kDsNS];
-  auto step = [&](int i, auto jc, auto issuec) {
-    constexpr int j = decltype(jc)::value;
-    // the scheduling barriers keep each step's unpacking after the loads it
-    // waits for were given their time (no hoisting of a later step's work)
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (decltype(issuec)::value) issue(i + kDsNS - 1, ring[(j + kDsNS - 1) % kDsNS]);
-    __builtin_amdgcn_sched_barrier(0);
-    put(i, ring[j], j & 1);
-    // LDS only: the later sub-chunks' loads stay in flight across it (a
-    // workgroup-release barrier would wait for all of them at every step).
-    // The buffer put(i + 1) writes was last read by compute(i - 1), which
-    // every wave finished before this barrier of step i.
-    lds_barrier();
-    compute(j & 1);
-  };
+  uint64_t cw = 0;  // PHASE 2: the cut as last read, beside every step's loads
+  const uint64_t* cutp = PHASE == 2 ? link.thr + (int64_t)(idx % max(link.n_copies, 1)) * link.stride : nullptr;
   static_assert(kDsNS % 2 == 0, "the LDS buffer of step i is i & 1 = j & 1");
   using std::integral_constant;
+  // One pass over the rows in sh.rch / sh.zcol [0, nrows) with a ring of NS
+  // sub-chunks (NS even, at most kDsNS).
+  auto ring_pass = [&](auto nsc) {
+    constexpr int NS = decltype(nsc)::value;
+    static_assert(NS % 2 == 0 && NS <= kDsNS, "ring depth");
+    auto step = [&](int i, auto jc, auto issuec) {
+      constexpr int j = decltype(jc)::value;
+      // the scheduling barriers keep each step's unpacking after the loads it
+      // waits for were given their time (no hoisting of a later step's work)
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(issuec)::value) issue(i + NS - 1, ring[(j + NS - 1) % NS]);
+      if constexpr (PHASE == 2) cw = ld_coh(cutp);
+      __builtin_amdgcn_sched_barrier(0);
+      put(i, ring[j], j & 1);
+      // LDS only: the later sub-chunks' loads stay in flight across it (a
+      // workgroup-release barrier would wait for all of them at every step).
+      // The buffer put(i + 1) writes was last read by compute(i - 1), which
+      // every wave finished before this barrier of step i.
+      lds_barrier();
+      compute(j & 1);
+    };
+    const int nsub = (nrows + kDsRows - 1) / kDsRows;
+    const int T = (nsub + NS - 1) / NS * NS;
 #pragma unroll
-  for (int j = 0; j < kDsNS - 1; ++j) issue(j, ring[j]);
-  for (int i0 = 0; i0 < T - kDsNS; i0 += kDsNS) {
-    step(i0, integral_constant<int, 0>(), integral_constant<bool, true>());
-    step(i0 + 1, integral_constant<int, 1>(), integral_constant<bool, true>());
-    if constexpr (kDsNS > 2) {
-      step(i0 + 2, integral_constant<int, 2>(), integral_constant<bool, true>());
-      step(i0 + 3, integral_constant<int, 3>(), integral_constant<bool, true>());
+    for (int j = 0; j < NS - 1; ++j) issue(j, ring[j]);
+    for (int i0 = 0; i0 < T - NS; i0 += NS) {
+      step(i0, integral_constant<int, 0>(), integral_constant<bool, true>());
+      step(i0 + 1, integral_constant<int, 1>(), integral_constant<bool, true>());
+      if constexpr (NS > 2) {
+        step(i0 + 2, integral_constant<int, 2>(), integral_constant<bool, true>());
+        step(i0 + 3, integral_constant<int, 3>(), integral_constant<bool, true>());
+      }
     }
-  }
-  {
-    const int i0 = T - kDsNS;
-    step(i0, integral_constant<int, 0>(), integral_constant<bool, true>());
-    step(i0 + 1, integral_constant<int, 1>(), integral_constant<bool, false>());
-    if constexpr (kDsNS > 2) {
-      step(i0 + 2, integral_constant<int, 2>(), integral_constant<bool, false>());
-      step(i0 + 3, integral_constant<int, 3>(), integral_constant<bool, false>());
+    {
+      const int i0 = T - NS;
+      step(i0, integral_constant<int, 0>(), integral_constant<bool, true>());
+      step(i0 + 1, integral_constant<int, 1>(), integral_constant<bool, false>());
+      if constexpr (NS > 2) {
+        step(i0 + 2, integral_constant<int, 2>(), integral_constant<bool, false>());
+        step(i0 + 3, integral_constant<int, 3>(), integral_constant<bool, false>());
+      }
+    }
+  };
+  ring_pass(integral_constant<int, kDsNS>());
+  if constexpr (PHASE >= 2) {
+    // then the chunk's selected candidates: those at positions in the
+    // chunk's share [ca, cb) of C, in position order, as one more pass (the
+    // host keeps every share within kDsMaxRows candidates)
+    int ns = 0;
+    if constexpr (PHASE == 2) {  // from the scores and the cut, handed over inside this launch
+      // thread 0's last read decides for the workgroup (the waves read the
+      // cut at different times); poll only if it was not out yet
+      if (tid == 0) {
+        bool ok = true;
+        const uint64_t e = is_valid(cw) ? cw : poll_coh(cutp, [](uint64_t v) { return is_valid(v); },
+                                                         link.poll_limit, ok);
+        if (!ok) st_coh(link.err, 3u);
+        sh.cut = ok ? e : 0;
+      }
+      __syncthreads();  // also: every wave is past the first pass's reads of the lists
+      const uint64_t e = sh.cut;
+      const uint32_t cv = (uint32_t)(e >> 32) & 0x7fffffffu;
+      const int tie = (int)(uint32_t)e;
+      int fl = 0, cnt = 0;
+#pragma unroll
+      for (int u = 0; u < kScPer; ++u) {
+        const int i = ca + kScPer * tid + u;
+        if (is_valid(e) && i < cb && (scv[u] > cv || (scv[u] == cv && i <= tie))) {
+          fl |= 1 << u;
+          ++cnt;
+        }
+      }
+      const int incl = wave_incl_scan(cnt);
+      if (lane == 63) sh.wsum[wave] = incl;
+      __syncthreads();
+      int off = incl - cnt;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        off += w < wave ? sh.wsum[w] : 0;
+        ns += sh.wsum[w];
+      }
+#pragma unroll
+      for (int u = 0; u < kScPer; ++u)
+        if ((fl >> u) & 1) {
+          const int i = ca + kScPer * tid + u;
+          sh.rch[off] = clamp_ch(C[i], d_ff);
+          sh.zcol[off] = min(n_R + i, n_A - 1);
+          ++off;
+        }
+    } else {  // from the selected list (positions ascending): the entries [ja, jb) fall in the share
+      if (tid < 2) sh.wsum[tid] = 0;
+      __syncthreads();  // also: every wave is past the first pass's reads of the lists
+      int lo = 0, hi = 0;
+      for (int j = tid; j < k; j += 256) {
+        const int p = pos[j];
+        lo += p < ca ? 1 : 0;
+        hi += p < cb ? 1 : 0;
+      }
+      if (lo) atomicAdd(&sh.wsum[0], lo);
+      if (hi) atomicAdd(&sh.wsum[1], hi);
+      __syncthreads();
+      const int ja = sh.wsum[0];
+      ns = min(sh.wsum[1] - ja, kDsMaxRows);
+      for (int i = tid; i < ns; i += 256) {
+        sh.rch[i] = clamp_ch(sel[ja + i], d_ff);
+        sh.zcol[i] = min(n_R + max(pos[ja + i], 0), n_A - 1);
+      }
+    }
+    __syncthreads();
+    if (ns > 0) {  // block-uniform: a shallow ring for these few sub-chunks
+      nrows = ns;
+      ring_pass(integral_constant<int, 2>());
     }
   }
   const int col = c0 + bcol;

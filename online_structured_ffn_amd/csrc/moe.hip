@@ -366,11 +366,13 @@ static void launch_moe_decode_mfma(hipStream_t st, const void* x, int Tn, int d,
   if (nb0 + usedR > 0)
     POP_LAUNCH((k_down_stream<MT, false, 1, true>), dim3(nb0 + ncol * usedR, E), dim3(256), 0, st,
                (const float*)w.z, n_A, n_pairs, (const bf16s*)WdT, d, d_ff, R, n_R, (const int32_t*)S,
-               (const int32_t*)w.Q, 0, n_R, rpcR, 0, w.partial, nb0, (const float*)w.score, n_C, k, C, w.Q, S, mr);
+               (const int32_t*)w.Q, 0, n_R, rpcR, 0, w.partial, nb0, (const float*)w.score, n_C, k, C, w.Q, S,
+               CutLink{nullptr, nullptr, 0, 0, 0}, mr);
   if (usedS > 0)
     POP_LAUNCH((k_down_stream<MT, false, 0, true>), dim3(ncol * usedS, E), dim3(256), 0, st, (const float*)w.z,
                n_A, n_pairs, (const bf16s*)WdT, d, d_ff, R, n_R, (const int32_t*)S, (const int32_t*)w.Q, n_R, n_live,
-               rpcS, usedR, w.partial, 0, (const float*)nullptr, n_C, k, C, w.Q, S, mr);
+               rpcS, usedR, w.partial, 0, (const float*)nullptr, n_C, k, C, w.Q, S, CutLink{nullptr, nullptr, 0, 0, 0},
+               mr);
   (void)n_live;
 }
 

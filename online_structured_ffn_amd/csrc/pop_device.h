@@ -592,11 +592,13 @@ __device__ __forceinline__ bool is_valid(uint64_t w) { return (w >> 63) != 0; }
 // (ascending, into C) and selected (channels C[p]) of the k selected
 // candidates with plain stores.  A round limit reached sets *err (coherent);
 // the step goes on with score 0 for the missing candidates.
+// With score not NULL the scores are complete in memory already (an earlier
+// launch wrote them): they are read once, cand and poll_limit unused.
 template <int NTH, int MAXN>
 __device__ __forceinline__ void topk_threshold_linked(const uint64_t* __restrict__ cand, int n, int k, const int32_t* __restrict__ C,
                                       int32_t* __restrict__ positions, int32_t* __restrict__ selected,
                                       uint64_t* __restrict__ thr, int n_copies, int stride, SelShared<NTH, MAXN>& sh,
-                                      int poll_limit, uint32_t* err) {
+                                      int poll_limit, uint32_t* err, const float* __restrict__ score = nullptr) {
   constexpr int EM = SelShared<NTH, MAXN>::kPerThread;
   static_assert(sel_slot(MAXN - 1) < kSelSlots, "keys handed over through the histogram buffers");
   constexpr int kBinShift = 31 - 12;  // 12 leading value bits: 4096 bins
@@ -613,7 +615,50 @@ __device__ __forceinline__ void topk_threshold_linked(const uint64_t* __restrict
     vb[j] = 0u;
     got[j] = tid + j * NTH >= n;
   }
-  for (int round = 0;; ++round) {
+  // bin of key u: (u - blo) >> bsh.  Polled words: the 12 leading value bits
+  // (the range is not known in advance).  Scores in memory: 4096 bins over
+  // their own [min, max], so that a bin rarely holds more than kSelResolve keys
+  // even when the scores crowd into a few binades (maxima over a batch).
+  uint32_t blo = 0u;
+  int bsh = kBinShift;
+  if (score != nullptr) {  // block-uniform
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int j = 0; j < EM; ++j)
+      if (!got[j]) {
+        vb[j] = value_bits(score[tid + j * NTH]);
+        mn = min(mn, vb[j]);
+        mx = max(mx, vb[j]);
+      }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    }
+    if ((tid & 63) == 0) {
+      sh.red[tid >> 6][0] = mn;
+      sh.red[tid >> 6][1] = mx;
+    }
+    __syncthreads();
+    mn = 0xffffffffu;
+    mx = 0u;
+#pragma unroll
+    for (int w = 0; w < NTH / 64; ++w) {
+      mn = min(mn, sh.red[w][0]);
+      mx = max(mx, sh.red[w][1]);
+    }
+    const uint32_t span = mx - mn;  // n >= 1: mn <= mx
+    blo = mn;
+    bsh = span < (uint32_t)kSelBins ? 0 : 32 - __builtin_clz(span) - 12;
+#pragma unroll
+    for (int j = 0; j < EM; ++j)
+      if (!got[j]) {
+        got[j] = true;
+        atomicAdd(&sh.hA[sel_slot((int)((vb[j] - blo) >> bsh))], 1u);
+      }
+    __syncthreads();
+  }
+  for (int round = 0; score == nullptr; ++round) {
     // every word of the round is requested before any is examined (one
     // round trip a round; words already seen, and slots past n, read a valid
     // word again and are ignored)
@@ -627,7 +672,7 @@ __device__ __forceinline__ void topk_threshold_linked(const uint64_t* __restrict
       if (j * NTH < n && !got[j] && is_valid(wv[j])) {
         got[j] = true;
         vb[j] = (uint32_t)(wv[j] >> 32) & 0x7fffffffu;
-        atomicAdd(&sh.hA[sel_slot((int)(vb[j] >> kBinShift))], 1u);
+        atomicAdd(&sh.hA[sel_slot((int)((vb[j] - blo) >> bsh))], 1u);
       }
       all &= got[j];
     }
@@ -666,8 +711,8 @@ __device__ __forceinline__ void topk_threshold_linked(const uint64_t* __restrict
         const int c = (int)hb[b];
         if (r >= cum && r < cum + c) {
           SelTarget u;
-          u.prefix = (uint32_t)(tid * BPT + b) << kBinShift;
-          u.shift = kBinShift;
+          u.prefix = (uint32_t)(tid * BPT + b);  // the bin
+          u.shift = bsh;
           u.rank = r - cum;
           u.count = c;
           u.beyond = 0;
@@ -688,7 +733,7 @@ __device__ __forceinline__ void topk_threshold_linked(const uint64_t* __restrict
 #pragma unroll
     for (int j = 0; j < EM; ++j) {
       const int i = tid + j * NTH;
-      if (i < n && (vb[j] >> kBinShift) == (t0.prefix >> kBinShift)) {
+      if (i < n && ((vb[j] - blo) >> bsh) == t0.prefix) {
         const int slot = atomicAdd(&sh.rcnt, 1);
         if (slot < kSelResolve) {
           sh.rv[slot] = vb[j];
@@ -846,9 +891,13 @@ __global__ __launch_bounds__(1024) void k_sum_chunks(const float* __restrict__ p
 // loads re-read the last chunk and add nothing): for the few dozen chunks of
 // the matrix-core down-projection, where the grouped sum above would leave
 // most of its threads idle.
+// reset / n_reset / reset_stride: hand-over words of the launch before
+// (reset[t * reset_stride], t < n_reset) cleared for the next call.
 template <int MAXC>
 __global__ __launch_bounds__(256) void k_sum_few(const float* __restrict__ partial, int n_chunks, int64_t n_out,
-                                                 float* __restrict__ out) {
+                                                 float* __restrict__ out, uint64_t* reset, int n_reset,
+                                                 int reset_stride) {
+  if (blockIdx.x == 0 && (int)threadIdx.x < n_reset) st_coh(&reset[(int64_t)threadIdx.x * reset_stride], (uint64_t)0);
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n_out) return;
   float a[MAXC];
