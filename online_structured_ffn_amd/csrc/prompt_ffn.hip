@@ -11,17 +11,17 @@
 // stored in bf16 (round to nearest even), the operand type of the second GEMM.
 // fp32: the same two products as LDS-tiled fp32 FMA.
 //
-// Both bf16 GEMMs use 256-thread blocks of 128 tokens x 64 output columns and a
-// 64-wide reduction slice per stage: each stage's global loads go to a ring of
-// register slots (2 for gate/up, 4 for the down-projection) and stay in flight
-// under the MFMAs of the stages before it; a stage then moves to one of two
-// LDS buffers.  Whole stages load with no condition (clamped rows and
-// channels), which keeps the compiler from waiting on the loads in flight.
-// Every operand tile is stored K-contiguous in LDS with a 144-byte row pitch,
-// which makes the 16-lane groups of a fragment read hit all 64 banks once.
-// W_downT is [d_ff, d] (K-major for the second GEMM), so its tile is
-// transposed on the way into LDS.
+// Both bf16 GEMMs run one 256-thread workgroup per compute unit, each with a
+// ring of stages in LDS that direct-to-LDS loads (global_load_lds_dwordx4)
+// fill several stages ahead of the matrix cores, so no operand passes through
+// registers on its way in.  Operand tiles sit in LDS K-contiguous (X, W_gate,
+// W_up and Z rows) or N-contiguous (W_downT rows, [d_ff, d], read back with
+// the transposing LDS read ds_read_b64_tr_b16), their 16- or 32-byte units
+// XOR-swizzled so that both the loads' 1 KB writes and the fragment reads
+// stay free of bank conflicts.
 #include <hip/hip_runtime.h>
+
+#include <utility>
 
 #include "pop_device.h"
 #include "pop_internal.h"
@@ -30,24 +30,30 @@
 namespace pop {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGThreads = 256;
-constexpr int kBM = 128;         // tokens per block
-constexpr int kBN = 64;          // output columns per block (per matrix)
-constexpr int kBK = 64;          // reduction slice per stage
-constexpr int kLd = kBK + 8;     // LDS row pitch in bf16 elements (144 bytes)
+constexpr int kWaveThreads = 256;  // one group of four waves
+constexpr int kBM = 128;         // tokens per block (both GEMMs): 32 per wave of a group
+constexpr int kGuKC = 32;        // gate/up: reduction elements per stage
+constexpr int kDnKC = 64;        // down: reduction elements per stage
+constexpr int kDnBN = 64;        // down: output columns per block
 constexpr int kZPad = 64;        // Z row pitch = d_ff rounded up to this
 constexpr int64_t kChunkTokens = 4096;  // tokens per pass (bounds the workspace)
+#ifndef POP_PROMPT_GR
+#define POP_PROMPT_GR 1  // groups of four waves per workgroup (1 or 2), taking alternating stages
+#endif
 #ifndef POP_GATEUP_NS
-#define POP_GATEUP_NS 2  // register stages of the gate/up pass's load pipeline (3 drops to one wave per SIMD)
+#define POP_GATEUP_NS 5  // stages in the gate/up LDS ring (a multiple of the group count)
 #endif
 #ifndef POP_DOWN_NS
-#define POP_DOWN_NS 4  // register stages of the down-projection's load pipeline
+#define POP_DOWN_NS 6  // stages in the down-projection LDS ring (a multiple of the group count)
 #endif
-#ifndef POP_DOWN_BM64_BELOW
-#define POP_DOWN_BM64_BELOW 0  // down-projection tiles of 128 tokens below which 64-token tiles are used
+#ifndef POP_GATEUP_PD
+#define POP_GATEUP_PD 2  // channel fragments read ahead of the MFMAs in the gate/up pass
 #endif
+constexpr int kGuThreads = kWaveThreads * POP_PROMPT_GR;  // threads per workgroup (one per compute unit)
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t b = __float_as_uint(f);
@@ -59,6 +65,55 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) { return *reinterp
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One direct-to-LDS load of a wave: lane i's 16 bytes at g land at LDS byte
+// address lds + 16 i (lds wave-uniform).  Written out rather than taken from
+// the builtin: the compiler makes LDS reads (the transposing read among them)
+// wait for every builtin direct-to-LDS load in flight, which would drain the
+// ring at each stage.  The loads write no register; the ring's own waits
+// (ring_barrier) account for them.  M0 carries the LDS address; nothing else
+// in these kernels uses M0 (LDS reads on gfx950 do not), so the clobber only
+// records that the statement sets it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Waits until at most N vector-memory instructions of this wave are in
+// flight and every LDS access of the wave is done, then a workgroup barrier.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// 16 zero bytes: the source of every operand chunk past the reduction's end.
+__device__ __align__(16) const uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
+
+
+// K-contiguous tiles in LDS: rows of KC elements (KC = 32: 64 bytes, KC = 64:
+// 128 bytes), 16-byte chunk c of row r in slot kslot<KC>(c, r) of the row.
+// With these swizzles the fragment reads (16 rows, one chunk each, per 16-lane
+// group) run without LDS bank conflicts, measured with the bank-conflict
+// counter (4 LDS cycles per 64-lane 16-byte read; the swizzle c ^ ((r >> 2) &
+// 3) of 64-byte rows takes 8), and one wave's direct-to-LDS load fills whole
+// rows.
+template <int KC>
+__device__ __forceinline__ int kslot(int c, int r) {
+  if constexpr (KC == 32)
+    return c ^ ((r >> 1) & 3);
+  else
+    return c ^ ((r >> 1) & 7);
 }
 
 // Tile order: workgroups are handed to the eight XCDs round robin by index, so
@@ -73,327 +128,398 @@ __device__ __forceinline__ void tile_of(int bid, int nb, int mt, int& m_tile, in
 }
 
 // ---------------------------------------------------------------- gate / up
-// Wave w covers tokens (w >> 1) * 64 + [0, 64) and channels (w & 1) * 32 +
-// [0, 32) of the block's tile, for both matrices: 4 x 2 fragments each.
+// Block tile: 128 tokens x 16 NF channels of each matrix.  A stage holds 32
+// reduction columns of the 128 token rows, then the 16 NF gate rows, then the
+// 16 NF up rows (64 bytes each, K-contiguous).  The eight waves form two
+// groups of four; group g computes the stages of parity g, so two waves share
+// each SIMD and one's MFMAs run while the other waits.  Wave w of a group
+// computes tokens 32 w + [0, 32) against every channel of the block (2 x NF
+// fragments per matrix) over its group's stages; at the end group 1 adds its
+// sums into group 0's through LDS (group 0 + group 1, a fixed order).  NF is
+// chosen at launch so that the tiles fill the compute units in as few rounds
+// as possible.
 //
-// IMP > 0: the blocks also compute the importance
+// IMP > 0: the first IMP token tiles' blocks also compute the importance
 // I_i = sqrt(sum_k W_up[i,k]^2 * s2[k]) of the block's channels from the W_up
-// tiles already in LDS (the column norms s2 of the whole prompt are an input),
-// so the prefill needs no second sweep of W_up.  IMP = 16: the blocks of the
-// first four token tiles take 16 of the 64 channels each (m_tile * 16 + [0,
-// 16)), so the extra work is spread evenly; IMP = 64 (fewer than four token
-// tiles): the first token tile takes all 64.  Thread t takes channel
-// t % IMP and the KPT = 64 * IMP / 256 columns (t / IMP) * KPT + [0, KPT) of
-// every 64-column stage, in ascending order; the 256 / IMP column groups of a
-// channel are added in order at the end.
+// rows already in LDS (the column norms s2 of the whole prompt are an input),
+// so the prefill needs no second sweep of W_up.  Block m_tile takes channels
+// m_tile * G + [0, G), G = 16 NF / IMP; wave w of group g sums columns 8 w +
+// [0, 8) of its group's stages (in ascending order) for channel lane + 64 j,
+// with s2 from scalar loads; the eight partial sums of a channel are added in
+// (group, wave) order.
 //
-// Pipeline (as in the down-projection): each stage's loads go to one of NS
-// register slots and stay in flight for NS - 1 stages of MFMA work, then the
-// stage is written to one of two LDS buffers, followed by one barrier.  The
-// stages that lie wholly below d (in groups of NS) load unconditionally: rows
-// past M are clamped to row M - 1 (their outputs are not written) and channels
-// past d_ff to channel d_ff - 1 (their Z columns are written as 0 below).  The
-// last stages (fewer than NS, or a stage that crosses d) load with a column
-// mask so that columns past d are 0, one stage at a time.
-template <int IMP, int NS>
-__global__ __launch_bounds__(kGThreads) void k_prompt_gateup(const bf16s* __restrict__ X, int M, int d,
-                                                             const bf16s* __restrict__ Wg,
-                                                             const bf16s* __restrict__ Wu, int d_ff,
-                                                             uint16_t* __restrict__ Z, int ldz, int mt, int nt,
-                                                             const float* __restrict__ s2, float* __restrict__ I) {
-  __shared__ __align__(16) uint16_t As[2][kBM * kLd];
-  __shared__ __align__(16) uint16_t Bs[2][2 * kBN * kLd];  // gate rows, then up rows
-  constexpr int APER = kBM * (kBK / 8) / kGThreads;
-  constexpr int BPER = 2 * kBN * (kBK / 8) / kGThreads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Ring of NS stages (NS even): stages 0 .. NS - 3 load first; step j waits for
+// the wave's own loads of stages 2 j and 2 j + 1, passes a barrier (every
+// wave's share landed, both groups done with stages 2 j - 2 and 2 j - 1),
+// then group g computes stage 2 j + g while every wave issues its share of
+// stages 2 j + NS - 2 and 2 j + NS - 1 into the freed slots.  Stages past the
+// last one (at most one, when the count is odd, and the refills past the end)
+// load zeros.  Rows past M and channels past d_ff load clamped rows (their
+// outputs are not written, or written as 0); chunks past d load zeros.
+template <int NF, int NS, int IMP, int GR>
+__global__ __launch_bounds__(kWaveThreads * GR, 1) void k_prompt_gateup(const bf16s* __restrict__ X, int M, int d,
+                                                                const bf16s* __restrict__ Wg,
+                                                                const bf16s* __restrict__ Wu, int d_ff,
+                                                                uint16_t* __restrict__ Z, int ldz, int mt, int nt,
+                                                                const float* __restrict__ s2, float* __restrict__ I) {
+  constexpr int KC = kGuKC;
+  constexpr int BR = 16 * NF;            // channels per block and matrix
+  constexpr int ROWS = kBM + 2 * BR;     // tile rows per stage
+  constexpr int NI = ROWS / 16;          // load instructions per stage (16 rows each)
+  constexpr int NW = 4 * GR;             // waves
+  constexpr int LPW = (NI + NW - 1) / NW;  // per wave; the spare ones repeat instruction NI - 1
+  constexpr int STAGE = ROWS * KC;       // bf16 elements per stage
+  constexpr int G = IMP > 0 ? BR / (IMP > 0 ? IMP : 1) : 1;  // importance channels per block
+  constexpr int NPR = (G + 63) / 64;
+  static_assert(NS % GR == 0 && NS >= 2 * GR && (NS - 2 * GR) * LPW < 64, "ring depth");
+  static_assert(GR * LPW <= NF, "the refill loads ride on the first GR LPW channel fragments");
+  __shared__ __align__(16) uint16_t smem[NS * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wv = wave & 3;
   int m_tile, n_tile;
   tile_of(blockIdx.x, mt * nt, mt, m_tile, n_tile);
-  const int m0 = m_tile * kBM, n0 = n_tile * kBN;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = m_tile * kBM, n0 = n_tile * BR;
+  const uint32_t lds0 = lds_addr(smem);
 
-  // importance state (block-uniform)
-  constexpr int IC = IMP > 0 ? IMP : 64;       // channels per importance block
-  constexpr int KPT = 64 * IC / kGThreads;     // columns per thread per stage (4 or 16)
-  constexpr int SPS = IMP > 0 ? KPT : 1;       // s2 values per slot
-  const bool imp = IMP > 0 && m_tile < (IMP == 16 ? 4 : 1);
-  const int c_base = IMP == 16 ? m_tile * 16 : 0;
-  const int ir = tid % IC, ig = tid / IC;
-  float ia = 0.f;
-
-  u32x4 ra[NS][APER], rb[NS][BPER];
-  float rs[NS][SPS];
-  // Whole stages: unconditional loads.  Columns of s2 past d are read at
-  // d - 4 (finite); they only ever meet W_up columns that are 0 in LDS.
-  auto issue = [&](int slot, int k0) {
+  // load instruction m of this wave fills rows 16 j + [0, 16): lane i row 16 j + i / 4, slot i % 4
+  const bf16s* rowp[LPW];
+  uint32_t lofs[LPW];
+  const int co = 8 * kslot<KC>(lane & 3, lane >> 2);  // first element of the chunk this lane loads
 #pragma unroll
-    for (int i = 0; i < APER; ++i) {
-      const int q = tid + i * kGThreads;
-      const int m = min(m0 + (q >> 3), M - 1);
-      ra[slot][i] = ld16(X + (int64_t)m * d + k0 + (q & 7) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < BPER; ++i) {
-      const int q = tid + i * kGThreads;
-      const int row = q >> 3;
-      const int ch = min(n0 + (row & (kBN - 1)), d_ff - 1);
-      const bf16s* W = row < kBN ? Wg : Wu;
-      rb[slot][i] = ld16(W + (int64_t)ch * d + k0 + (q & 7) * 8);
-    }
-    if constexpr (IMP > 0) {
-#pragma unroll
-      for (int q = 0; q < KPT; q += 4) {
-        const float4 f = *reinterpret_cast<const float4*>(s2 + min(k0 + ig * KPT + q, d - 4));
-        rs[slot][q] = f.x;
-        rs[slot][q + 1] = f.y;
-        rs[slot][q + 2] = f.z;
-        rs[slot][q + 3] = f.w;
-      }
-    }
-  };
-  // Tail stages: columns past d load as 0.
-  auto issue_masked = [&](int slot, int k0) {
-#pragma unroll
-    for (int i = 0; i < APER; ++i) {
-      const int q = tid + i * kGThreads;
-      const int m = min(m0 + (q >> 3), M - 1), k = k0 + (q & 7) * 8;
-      ra[slot][i] = k < d ? ld16(X + (int64_t)m * d + k) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < BPER; ++i) {
-      const int q = tid + i * kGThreads;
-      const int row = q >> 3, k = k0 + (q & 7) * 8;
-      const int ch = min(n0 + (row & (kBN - 1)), d_ff - 1);
-      const bf16s* W = row < kBN ? Wg : Wu;
-      rb[slot][i] = k < d ? ld16(W + (int64_t)ch * d + k) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if constexpr (IMP > 0) {
-#pragma unroll
-      for (int q = 0; q < KPT; q += 4) {
-        const float4 f = *reinterpret_cast<const float4*>(s2 + min(k0 + ig * KPT + q, d - 4));
-        rs[slot][q] = f.x;
-        rs[slot][q + 1] = f.y;
-        rs[slot][q + 2] = f.z;
-        rs[slot][q + 3] = f.w;
-      }
-    }
-  };
-  auto put = [&](int slot, int buf) {
-#pragma unroll
-    for (int i = 0; i < APER; ++i) {
-      const int q = tid + i * kGThreads;
-      *reinterpret_cast<u32x4*>(&As[buf][(q >> 3) * kLd + (q & 7) * 8]) = ra[slot][i];
-    }
-#pragma unroll
-    for (int i = 0; i < BPER; ++i) {
-      const int q = tid + i * kGThreads;
-      *reinterpret_cast<u32x4*>(&Bs[buf][(q >> 3) * kLd + (q & 7) * 8]) = rb[slot][i];
-    }
+  for (int m = 0; m < LPW; ++m) {
+    const int j = min(wave + NW * m, NI - 1);
+    const int row = 16 * j + (lane >> 2);
+    const bf16s* p;
+    if (row < kBM)
+      p = X + (int64_t)min(m0 + row, M - 1) * d;
+    else if (row < kBM + BR)
+      p = Wg + (int64_t)min(n0 + row - kBM, d_ff - 1) * d;
+    else
+      p = Wu + (int64_t)min(n0 + row - kBM - BR, d_ff - 1) * d;
+    rowp[m] = p;
+    lofs[m] = 2u * 16u * KC * j;
+  }
+  // load m of stage st into ring slot q
+  auto issue1 = [&](int st, int q, int m) {
+    const int k0 = st * KC;
+    dma16(k0 + co < d ? (const void*)(rowp[m] + k0 + co) : (const void*)kZero16, lds0 + 2u * STAGE * q + lofs[m]);
   };
 
-  f32x4 ag[4][2], au[4][2];
+  const bool imp = IMP > 0 && m_tile < IMP;  // block-uniform
+  float ia[NPR];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < NPR; ++j) ia[j] = 0.f;
+
+  f32x4 ag[2][NF], au[2][NF];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      ag[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      au[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  auto compute = [&](int slot, int buf) {
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) ag[i][f] = au[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15;
+  const int asl = 8 * kslot<KC>(lane >> 4, fr);  // this lane's chunk in every fragment row
+  // Stage st from slot q.  The refill (stages rst and rst + 1 into slots rq
+  // and rq + 1, this wave's share) rides on the first MFMAs, one load per
+  // channel fragment; the scheduling barriers keep that order.
+  auto compute = [&](int st, int q, int rst, int rq) {
+    const uint16_t* base = smem + q * STAGE;
+    float sv[8];
     if constexpr (IMP > 0) {
-      // W_up row n0 + c_base + ir of this stage: columns ig * KPT + [0, KPT)
-      const uint16_t* wr = &Bs[buf][(kBN + c_base + ir) * kLd + ig * KPT];
+      if (imp) {  // this wave's 8 columns of s2 (wave-uniform: scalar loads)
+        const float* sp = s2 + min(st * KC + 8 * wv, d - 8);
 #pragma unroll
-      for (int q = 0; q < KPT; q += 2) {
-        const uint32_t w2 = *reinterpret_cast<const uint32_t*>(wr + q);
-        const float f0 = __uint_as_float(w2 << 16), f1 = __uint_as_float(w2 & 0xffff0000u);
-        ia = fmaf(f0 * f0, rs[slot][q], ia);
-        ia = fmaf(f1 * f1, rs[slot][q + 1], ia);
+        for (int e = 0; e < 8; ++e) sv[e] = sp[e];
       }
     }
+    bf16x8 a[2], bg[NF], bu[NF];
+    auto read_b = [&](int f) {
+      bg[f] = lds_frag(base + (kBM + 16 * f + fr) * KC + asl);
+      bu[f] = lds_frag(base + (kBM + BR + 16 * f + fr) * KC + asl);
+    };
+    // the token fragments and PD channel fragments first; then, per channel
+    // fragment f: the reads of fragment f + PD, a refill load, f's 4 MFMAs
+    constexpr int PD = POP_GATEUP_PD < NF ? POP_GATEUP_PD : NF;
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      bf16x8 fa[4];
+    for (int i = 0; i < 2; ++i) a[i] = lds_frag(base + (32 * wv + 16 * i + fr) * KC + asl);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = lds_frag(&As[buf][(wm * 64 + i * 16 + fr) * kLd + kk + fk]);
+    for (int f = 0; f < PD; ++f) read_b(f);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 fg = lds_frag(&Bs[buf][(wn * 32 + j * 16 + fr) * kLd + kk + fk]);
-        const bf16x8 fu = lds_frag(&Bs[buf][(kBN + wn * 32 + j * 16 + fr) * kLd + kk + fk]);
+    for (int f = 0; f < NF; ++f) {
+      if (f + PD < NF) read_b(f + PD);
+      if (f < GR * LPW) issue1(rst + f / LPW, rq + f / LPW, f % LPW);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ag[i][j] = mfma(fa[i], fg, ag[i][j]);
-          au[i][j] = mfma(fa[i], fu, au[i][j]);
+      for (int i = 0; i < 2; ++i) {
+        ag[i][f] = mfma(a[i], bg[f], ag[i][f]);
+        au[i][f] = mfma(a[i], bu[f], au[i][f]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (IMP > 0) {
+      if (imp && st * KC + 8 * wv < d) {
+#pragma unroll
+        for (int j = 0; j < NPR; ++j) {
+          const int c = lane + 64 * j;
+          if (c < G) {
+            const int row = kBM + BR + m_tile * G + c;
+            const u32x4 w = *reinterpret_cast<const u32x4*>(base + row * KC + 8 * kslot<KC>(wv, row));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float w0 = __uint_as_float(w[e] << 16), w1 = __uint_as_float(w[e] & 0xffff0000u);
+              ia[j] = fmaf(w0 * w0, sv[2 * e], ia[j]);
+              ia[j] = fmaf(w1 * w1, sv[2 * e + 1], ia[j]);
+            }
+          }
         }
       }
     }
   };
 
-  const int nk = (d + kBK - 1) / kBK;
-  const int nmain = d / kBK / NS * NS;  // whole stages, in groups of NS
-  if (nmain > 0) {
+  // (the inner loop unrolls fully: every ring slot index is a constant)
+  const int nst = (d + KC - 1) / KC;
 #pragma unroll
-    for (int u = 0; u < NS - 1; ++u) issue(u, u * kBK);
-  }
-  for (int kt0 = 0; kt0 < nmain; kt0 += NS) {
+  for (int u = 0; u < NS - GR; ++u)
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int kt = kt0 + u;
-      issue((u + NS - 1) % NS, min(kt + NS - 1, nmain - 1) * kBK);  // past the end: reload (unused)
-      put(u, kt & 1);
-      __syncthreads();
-      compute(u, kt & 1);
+    for (int m = 0; m < LPW; ++m) issue1(u, u, m);
+  for (int s0 = 0; s0 < nst; s0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; u += GR) {
+      const int st = s0 + u;
+      if (st >= nst) break;
+      ring_barrier<(NS - 2 * GR) * LPW>();
+      compute(st + grp, u + grp, st + NS - GR, (u + NS - GR) % NS);
     }
   }
-  for (int kt = nmain; kt < nk; ++kt) {  // the last stages, one at a time
-    issue_masked(0, kt * kBK);
-    put(0, kt & 1);
+  ring_barrier<0>();  // the spare loads landed; every wave is done with the ring
+
+  // group 1's sums into group 0's, in two rounds of fragments
+  float* red = reinterpret_cast<float*>(smem);
+  constexpr int NH = (NF + 1) / 2;
+#pragma unroll
+  for (int r = 0; r < (GR > 1 ? 2 : 0); ++r) {
+    const int f0 = r == 0 ? 0 : NH, f1 = r == 0 ? NH : NF;
+    float* rw = red + wv * (2 * NH * 2 * 4) * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int f = f0; f < f1; ++f)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            rw[(((f - f0) * 2 + i) * 8 + e) * 64] = ag[i][f][e];
+            rw[(((f - f0) * 2 + i) * 8 + 4 + e) * 64] = au[i][f][e];
+          }
+    }
     __syncthreads();
-    compute(0, kt & 1);
+    if (grp == 0) {
+#pragma unroll
+      for (int f = f0; f < f1; ++f)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ag[i][f][e] += rw[(((f - f0) * 2 + i) * 8 + e) * 64];
+            au[i][f][e] += rw[(((f - f0) * 2 + i) * 8 + 4 + e) * 64];
+          }
+    }
+    __syncthreads();
   }
-  __syncthreads();  // every wave is done with As before it holds the importance sums
   if (imp) {  // block-uniform
-    float* red = reinterpret_cast<float*>(As[0]);
-    red[ig * IC + ir] = ia;
-    __syncthreads();
-    if (ig == 0 && n0 + c_base + ir < d_ff) {
-      float t = red[ir];
 #pragma unroll
-      for (int g = 1; g < kGThreads / IC; ++g) t += red[g * IC + ir];
-      I[n0 + c_base + ir] = sqrtf(t);
+    for (int j = 0; j < NPR; ++j)
+      if (lane + 64 * j < G) red[wave * G + lane + 64 * j] = ia[j];
+    __syncthreads();
+    for (int c = tid; c < G; c += NW * 64) {
+      const int ch = n0 + m_tile * G + c;
+      float t = red[c];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) t += red[w * G + c];
+      if (ch < d_ff) I[ch] = sqrtf(t);
     }
   }
+  if (grp != 0) return;
   // Output fragment layout: element e of lane l is row (l >> 4) * 4 + e,
   // column l & 15 of the 16 x 16 tile.  Columns in [d_ff, ldz) are written as
   // 0: Z's padding must be zero for the second GEMM.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 32 + j * 16 + fr;
+    for (int f = 0; f < NF; ++f) {
+      const int n = n0 + 16 * f + fr;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+        const int m = m0 + 32 * wv + 16 * i + (lane >> 4) * 4 + e;
         if (m < M && n < ldz)
-          Z[(int64_t)m * ldz + n] = n < d_ff ? bf16_rne(silu(ag[i][j][e]) * au[i][j][e]) : (uint16_t)0;
+          Z[(int64_t)m * ldz + n] = n < d_ff ? bf16_rne(silu(ag[i][f][e]) * au[i][f][e]) : (uint16_t)0;
       }
     }
 }
 
 // ---------------------------------------------------------------- down
-// Y[m, n] = sum_k Z[m, k] W_downT[k, n].  The W_downT tile (kBK rows of kBN
-// columns, row-major in HBM) is written to LDS as [n][k]: thread t loads rows
-// k0 + 2 (t & 31) and the next one at columns (t >> 5) * 8 + [0, 8) and writes
-// eight 4-byte (k, k + 1) pairs; the 32 k-pairs of a half-wave cover all 64
-// banks.  BM = 128: wave w covers tokens (w >> 1) * 64 + [0, 64) and columns
-// (w & 1) * 32 + [0, 32); BM = 64 (twice the blocks, for short prompts): wave w
-// covers all 64 tokens and columns w * 16 + [0, 16).
+// Y[m, n] = sum_k A[m, k] Bk[k, n] (the prompt FFN: A = Z, Bk = W_downT).
+// Block tile: 128 tokens x 64 columns; a stage holds 64 reduction columns of
+// the 128 A rows (K-contiguous, 128 bytes a row) and the 64 Bk rows of those
+// reductions (N-contiguous, 128 bytes a row).  The Bk tile is read with the
+// transposing LDS read: within a 16-lane group, lane i receives element i % 4
+// of the 8 bytes addressed by lanes 4 e + i / 4, e = 0 .. 3; the lanes of
+// group g address rows 8 g + [0, 4) (then 8 g + 4 + [0, 4)), four lanes per
+// row, 4 columns each, which hands every lane the 8 consecutive reductions of
+// one column that the MFMA operand holds.  The 32-byte column units of Bk row
+// r are stored XOR-ed with bsw(r), which keeps the rows that one transposing
+// read touches on distinct banks.  Two groups of four waves take alternating
+// stages as in the gate/up pass; wave w of a group computes tokens 32 w +
+// [0, 32) x all 64 columns (2 x 4 fragments), and group 1's sums join group
+// 0's through LDS at the end.
 //
-// Pipeline: the loads of a stage go to one of NS register slots and stay in
-// flight for NS - 1 stages of MFMA work (a stage's loads take far longer than
-// its arithmetic); each stage is then written to one of two LDS buffers,
-// followed by one barrier.  Every load is unconditional: a Z row past M is
-// clamped to row M - 1 (it only feeds output rows that are not written),
-// W_downT rows past d_ff are clamped to row d_ff - 1 (they meet Z's zero
-// padding) and columns past d to the last vector (their outputs are not
-// written).  No branch or select follows a load.
-template <int BM, int NS>
-__global__ __launch_bounds__(kGThreads) void k_prompt_down(const uint16_t* __restrict__ Z, int M, int ldz,
-                                                           const bf16s* __restrict__ WdT, int d_ff, int d,
-                                                           float* __restrict__ Y, int mt, int nt) {
-  constexpr int WM = BM / 64;            // waves along the tokens
-  constexpr int WN = 4 / WM;             // waves along the columns
-  constexpr int JF = kBN / WN / 16;      // 16-column fragments per wave
-  constexpr int PER = BM * (kBK / 8) / kGThreads;
-  __shared__ __align__(16) uint16_t As[2][BM * kLd];
-  __shared__ __align__(16) uint16_t Bs[2][kBN * kLd];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Ka: A's reduction extent (a multiple of 8; chunks past it load zeros); Kb:
+// Bk's rows (rows past it load clamped rows, which meet those zeros or A's zero
+// padding).  Rows past M and columns past N load clamped data and are not
+// written.  The ring works as in the gate/up pass.
+__device__ __forceinline__ int bsw(int r) { return ((r >> 1) & 1) | ((r >> 2) & 2); }
+
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* p, int second) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + second));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int NS, int GR>
+__global__ __launch_bounds__(kWaveThreads * GR, 1) void k_prompt_down(const uint16_t* __restrict__ A, int M, int lda, int Ka,
+                                                              const bf16s* __restrict__ Bk, int Kb, int N,
+                                                              float* __restrict__ Y, int mt, int nt) {
+  constexpr int KC = kDnKC, BN = kDnBN;
+  constexpr int NIA = kBM * KC / 512;    // A load instructions per stage (8 rows of 128 bytes each)
+  constexpr int NIB = KC * BN / 512;     // Bk load instructions per stage
+  constexpr int NW = 4 * GR;             // waves
+  constexpr int LA = NIA / NW, LB = NIB / NW;
+  constexpr int NV = LA + LB;            // load instructions per stage and wave
+  constexpr int ASZ = kBM * KC;          // bf16 elements of the A part
+  constexpr int STAGE = ASZ + KC * BN;
+  static_assert(KC == 64 && BN == 64, "the transposing reads' offsets assume 64 x 64 Bk tiles");
+  static_assert(NIA % NW == 0 && NIB % NW == 0, "load shares");
+  static_assert(NS % GR == 0 && NS >= 2 * GR && (NS - 2 * GR) * NV < 64, "ring depth");
+  static_assert(GR * NV <= 8, "the refill loads ride on the first GR NV fragment pairs");
+  __shared__ __align__(16) uint16_t smem[NS * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wv = wave & 3;
   int m_tile, n_tile;
   tile_of(blockIdx.x, mt * nt, mt, m_tile, n_tile);
-  const int m0 = m_tile * BM, n0 = n_tile * kBN;
-  const int wm = wave / WN, wn = wave % WN;
-  const int kp = tid & 31, cb = (tid >> 5) * 8;
-  const bf16s* Zb = reinterpret_cast<const bf16s*>(Z);
-  const int nb = min(n0 + cb, d - 8);
+  const int m0 = m_tile * kBM, n0 = n_tile * BN;
+  const bf16s* Ab = reinterpret_cast<const bf16s*>(A);
+  const uint32_t lds0 = lds_addr(smem);
 
-  u32x4 ra[NS][PER], rb0[NS], rb1[NS];
-  auto issue = [&](int slot, int k0) {
+  // A: instruction j fills rows 8 j + [0, 8): lane i row 8 j + i / 8, slot i % 8
+  const bf16s* arow[LA];
+  int aco[LA];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int q = tid + i * kGThreads;
-      const int m = min(m0 + (q >> 3), M - 1);
-      ra[slot][i] = ld16(Zb + (int64_t)m * ldz + k0 + (q & 7) * 8);
-    }
-    const int k = min(k0 + 2 * kp, d_ff - 1), k1 = min(k0 + 2 * kp + 1, d_ff - 1);
-    rb0[slot] = ld16(WdT + (int64_t)k * d + nb);
-    rb1[slot] = ld16(WdT + (int64_t)k1 * d + nb);
+  for (int m = 0; m < LA; ++m) {
+    const int j = wave + NW * m;
+    const int row = 8 * j + (lane >> 3);
+    arow[m] = Ab + (int64_t)min(m0 + row, M - 1) * lda;
+    aco[m] = 8 * ((lane & 7) ^ (((j & 1) << 2) | (lane >> 4)));
+  }
+  // Bk: instruction j fills rows 8 j + [0, 8): lane i row r = 8 j + i / 8,
+  // bytes 16 (i % 8) of it, i.e. half i % 2 of physical unit (i % 8) / 2
+  int bro[LB], bco[LB];
+#pragma unroll
+  for (int m = 0; m < LB; ++m) {
+    const int j = wave + NW * m;
+    const int r = 8 * j + (lane >> 3);
+    const int u = ((lane & 7) >> 1) ^ bsw(r);
+    bro[m] = r;
+    bco[m] = min(n0 + 16 * u + 8 * (lane & 1), N - 8);
+  }
+  // load m of stage st into ring slot q (m < LA: A, else Bk)
+  auto issue1 = [&](int st, int q, int m) {
+    const int k0 = st * KC;
+    const uint32_t base = lds0 + 2u * STAGE * q;
+    if (m < LA)
+      dma16(k0 + aco[m] < Ka ? (const void*)(arow[m] + k0 + aco[m]) : (const void*)kZero16,
+            base + 2u * (8 * (wave + NW * m) * KC));
+    else
+      dma16(Bk + (int64_t)min(k0 + bro[m - LA], Kb - 1) * N + bco[m - LA],
+            base + 2u * (ASZ + 8 * (wave + NW * (m - LA)) * BN));
   };
-  auto put = [&](int slot, int buf) {
+
+  f32x4 acc[2][4];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int q = tid + i * kGThreads;
-      *reinterpret_cast<u32x4*>(&As[buf][(q >> 3) * kLd + (q & 7) * 8]) = ra[slot][i];
-    }
-    uint32_t* s32 = reinterpret_cast<uint32_t*>(Bs[buf]);
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t lo = (rb0[slot][j >> 1] >> ((j & 1) * 16)) & 0xffffu;
-      const uint32_t hi = (rb1[slot][j >> 1] >> ((j & 1) * 16)) & 0xffffu;
-      s32[((cb + j) * kLd) / 2 + kp] = lo | (hi << 16);
-    }
-  };
-  f32x4 acc[4][JF];
+    for (int f = 0; f < 4; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15, g = lane >> 4;
+  // transposing reads: this lane addresses row 8 g + (fr >> 2) (+ 4) of each
+  // 32-reduction half, columns 4 (fr & 3) of the fragment's unit
+  const int trow = 8 * g + (fr >> 2);
+  const int tsw = bsw(trow);
+  // Stage st from slot q: every read first (the second half's land under the
+  // first half's MFMAs), then per (half, fragment) one refill load (stages rst
+  // and rst + 1 into slots rq and rq + 1, this wave's share) and 2 MFMAs.
+  auto compute = [&](int st, int q, int rst, int rq) {
+    const uint16_t* base = smem + q * STAGE;
+    bf16x8 a[2][2], b[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int h = 0; h < 2; ++h) {
+      const int c = 4 * h + g;
 #pragma unroll
-    for (int j = 0; j < JF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      bf16x8 fa[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = lds_frag(&As[buf][(wm * 64 + i * 16 + fr) * kLd + kk + fk]);
-#pragma unroll
-      for (int j = 0; j < JF; ++j) {
-        const bf16x8 fb = lds_frag(&Bs[buf][(wn * JF * 16 + j * 16 + fr) * kLd + kk + fk]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][j] = mfma(fa[i], fb, acc[i][j]);
+      for (int i = 0; i < 2; ++i) {
+        const int row = 32 * wv + 16 * i + fr;
+        a[h][i] = lds_frag(base + row * KC + 8 * kslot<KC>(c, row));
       }
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        b[h][f] = tr_frag(base + ASZ + (32 * h + trow) * BN + 16 * (f ^ tsw) + 4 * (fr & 3), 4 * BN);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int p = 4 * h + f;
+        if (p < GR * NV) issue1(rst + p / NV, rq + p / NV, p % NV);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][f] = mfma(a[h][i], b[h][f], acc[i][f]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
   };
 
-  const int nk = (d_ff + kBK - 1) / kBK;  // Z's pitch ldz >= nk * kBK, its padding is zero
-  const int nmain = nk / NS * NS;
-  if (nmain > 0) {
+  // (the inner loop unrolls fully: every ring slot index is a constant)
+  const int nst = (Ka + KC - 1) / KC;
 #pragma unroll
-    for (int u = 0; u < NS - 1; ++u) issue(u, u * kBK);
-  }
-  for (int kt0 = 0; kt0 < nmain; kt0 += NS) {
+  for (int u = 0; u < NS - GR; ++u)
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int kt = kt0 + u;
-      issue((u + NS - 1) % NS, min(kt + NS - 1, nmain - 1) * kBK);  // past the end: reload (unused)
-      put(u, kt & 1);
-      __syncthreads();
-      compute(kt & 1);
+    for (int m = 0; m < NV; ++m) issue1(u, u, m);
+  for (int s0 = 0; s0 < nst; s0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; u += GR) {
+      const int st = s0 + u;
+      if (st >= nst) break;
+      ring_barrier<(NS - 2 * GR) * NV>();
+      compute(st + grp, u + grp, st + NS - GR, (u + NS - GR) % NS);
     }
   }
-  for (int kt = nmain; kt < nk; ++kt) {  // fewer than NS stages left
-    issue(0, kt * kBK);
-    put(0, kt & 1);
-    __syncthreads();
-    compute(kt & 1);
+  ring_barrier<0>();
+  float* red = reinterpret_cast<float*>(smem) + wv * 32 * 64 + lane;
+  if (GR > 1 && grp == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[((i * 4 + f) * 4 + e) * 64] = acc[i][f][e];
   }
+  __syncthreads();
+  if (grp != 0) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < JF; ++j) {
-      const int n = n0 + wn * JF * 16 + j * 16 + fr;
+    for (int f = 0; f < 4; ++f) {
+      const int n = n0 + 16 * f + fr;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
-        if (m < M && n < d) Y[(int64_t)m * d + n] = acc[i][j][e];
+        const int m = m0 + 32 * wv + 16 * i + 4 * g + e;
+        if (m < M && n < N) Y[(int64_t)m * N + n] = GR > 1 ? acc[i][f][e] + red[((i * 4 + f) * 4 + e) * 64] : acc[i][f][e];
       }
     }
 }
@@ -485,6 +611,111 @@ static pop_status launched() {
   return POP_OK;
 }
 
+// Gate/up block shape.  NF (channel fragments per block and matrix) is picked
+// per launch: the mt x ceil(ldz / 16 NF) tiles run in ceil(tiles / slots)
+// rounds on slots = compute units x resident blocks per unit, and a round
+// costs about (NF + 1) x (resident blocks per unit) units of one unit's time
+// (NF fragments of the weights plus the token operand).  The least total wins;
+// ties go to the larger NF (fewer re-reads of the prompt).
+template <int NF, int IMP>
+static const void* gateup_kernel() {
+  return reinterpret_cast<const void*>(&k_prompt_gateup<NF, POP_GATEUP_NS, IMP, POP_PROMPT_GR>);
+}
+template <int NF>
+static const void* gateup_kernel_imp(int imp) {
+  return imp == 4 ? gateup_kernel<NF, 4>() : imp == 2 ? gateup_kernel<NF, 2>() : imp == 1 ? gateup_kernel<NF, 1>()
+                                                                                          : gateup_kernel<NF, 0>();
+}
+static const void* gateup_kernel_of(int nf, int imp) {
+  switch (nf) {
+    case 4: return gateup_kernel_imp<4>(imp);
+    case 6: return gateup_kernel_imp<6>(imp);
+    case 8: return gateup_kernel_imp<8>(imp);
+    case 10: return gateup_kernel_imp<10>(imp);
+    default: return gateup_kernel_imp<11>(imp);
+  }
+}
+constexpr int kGateupNF[] = {4, 6, 8, 10, 11};
+
+struct GateupShape {
+  int n_cu = 0;
+  int per_cu[5] = {};  // resident blocks per compute unit, by kGateupNF entry
+};
+static const GateupShape& gateup_shape() {
+  static GateupShape sh[64];
+  static bool done[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!done[dev]) {
+    GateupShape s;
+    if (hipDeviceGetAttribute(&s.n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || s.n_cu < 1)
+      s.n_cu = 256;
+    for (int i = 0; i < 5; ++i) {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gateup_kernel_of(kGateupNF[i], 0), kGuThreads, 0) !=
+              hipSuccess ||
+          nb < 1)
+        nb = 1;
+      s.per_cu[i] = nb;
+    }
+    sh[dev] = s;
+    done[dev] = true;
+  }
+  return sh[dev];
+}
+static int gateup_nf(int mt, int ldz) {
+  const GateupShape& s = gateup_shape();
+  int best = 11;
+  int64_t best_cost = -1;
+  for (int i = 0; i < 5; ++i) {
+    const int nf = kGateupNF[i];
+    const int64_t tiles = (int64_t)mt * ((ldz + 16 * nf - 1) / (16 * nf));
+    const int64_t slots = (int64_t)s.n_cu * s.per_cu[i];
+    const int64_t cost = (tiles + slots - 1) / slots * (nf + 1) * s.per_cu[i];
+    if (best_cost < 0 || cost <= best_cost) best = nf, best_cost = cost;
+  }
+  return best;
+}
+
+template <int NF>
+static void launch_gateup_nf(hipStream_t st, int imp, const bf16s* X, int M, int d, const bf16s* Wg,
+                             const bf16s* Wu, int d_ff, uint16_t* Z, int ldz, int mt, const float* s2, float* I) {
+  const int nt = (ldz + 16 * NF - 1) / (16 * NF);
+  const dim3 grid(mt * nt), block(kGuThreads);
+  if (imp == 4)
+    POP_LAUNCH((k_prompt_gateup<NF, POP_GATEUP_NS, 4, POP_PROMPT_GR>), grid, block, 0, st, X, M, d, Wg, Wu, d_ff, Z, ldz, mt, nt, s2, I);
+  else if (imp == 2)
+    POP_LAUNCH((k_prompt_gateup<NF, POP_GATEUP_NS, 2, POP_PROMPT_GR>), grid, block, 0, st, X, M, d, Wg, Wu, d_ff, Z, ldz, mt, nt, s2, I);
+  else if (imp == 1)
+    POP_LAUNCH((k_prompt_gateup<NF, POP_GATEUP_NS, 1, POP_PROMPT_GR>), grid, block, 0, st, X, M, d, Wg, Wu, d_ff, Z, ldz, mt, nt, s2, I);
+  else
+    POP_LAUNCH((k_prompt_gateup<NF, POP_GATEUP_NS, 0, POP_PROMPT_GR>), grid, block, 0, st, X, M, d, Wg, Wu, d_ff, Z, ldz, mt, nt,
+               (const float*)nullptr, (float*)nullptr);
+}
+
+// Z = SiLU(X W_gate^T) * (X W_up^T) for M <= kChunkTokens tokens; with imp > 0
+// (the number of token tiles, 1, 2 or 4, that share the work) the launch also
+// writes I from s2.
+static void launch_gateup(hipStream_t st, int imp, const bf16s* X, int M, int d, const bf16s* Wg, const bf16s* Wu,
+                          int d_ff, uint16_t* Z, int ldz, const float* s2, float* I) {
+  const int mt = (M + kBM - 1) / kBM;
+  switch (gateup_nf(mt, ldz)) {
+    case 4: launch_gateup_nf<4>(st, imp, X, M, d, Wg, Wu, d_ff, Z, ldz, mt, s2, I); break;
+    case 6: launch_gateup_nf<6>(st, imp, X, M, d, Wg, Wu, d_ff, Z, ldz, mt, s2, I); break;
+    case 8: launch_gateup_nf<8>(st, imp, X, M, d, Wg, Wu, d_ff, Z, ldz, mt, s2, I); break;
+    case 10: launch_gateup_nf<10>(st, imp, X, M, d, Wg, Wu, d_ff, Z, ldz, mt, s2, I); break;
+    default: launch_gateup_nf<11>(st, imp, X, M, d, Wg, Wu, d_ff, Z, ldz, mt, s2, I); break;
+  }
+}
+
+// Y [M, N] = A [M, Ka] (pitch lda) x Bk [Kb, N]; see k_prompt_down.
+static void launch_down(hipStream_t st, const uint16_t* A, int M, int lda, int Ka, const bf16s* Bk, int Kb, int N,
+                        float* Y) {
+  const int mt = (M + kBM - 1) / kBM, nt = (N + kDnBN - 1) / kDnBN;
+  POP_LAUNCH((k_prompt_down<POP_DOWN_NS, POP_PROMPT_GR>), dim3(mt * nt), dim3(kGuThreads), 0, st, A, M, lda, Ka, Bk, Kb, N, Y, mt,
+             nt);
+}
+
 // With s2 and I set, the first chunk's gate/up launch also writes I.
 static void launch_prompt_ffn(hipStream_t st, const void* X, int64_t n_tokens, int32_t d, const void* Wg,
                               const void* Wu, const void* WdT, int32_t d_ff, pop_dtype dt, float* Y, void* ws,
@@ -497,25 +728,9 @@ static void launch_prompt_ffn(hipStream_t st, const void* X, int64_t n_tokens, i
     if (dt == POP_BF16) {
       const bf16s* Xc = (const bf16s*)X + t0 * d;
       const int mt = (M + kBM - 1) / kBM;
-      const int nt1 = ldz / kBN;
-      if (imp && mt >= 4)
-        POP_LAUNCH((k_prompt_gateup<16, POP_GATEUP_NS>), dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
-                   (const bf16s*)Wu, (int)d_ff, (uint16_t*)ws, ldz, mt, nt1, s2, I);
-      else if (imp)
-        POP_LAUNCH((k_prompt_gateup<64, POP_GATEUP_NS>), dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
-                   (const bf16s*)Wu, (int)d_ff, (uint16_t*)ws, ldz, mt, nt1, s2, I);
-      else
-        POP_LAUNCH((k_prompt_gateup<0, POP_GATEUP_NS>), dim3(mt * nt1), dim3(kGThreads), 0, st, Xc, M, (int)d, (const bf16s*)Wg,
-                   (const bf16s*)Wu, (int)d_ff, (uint16_t*)ws, ldz, mt, nt1, (const float*)nullptr, (float*)nullptr);
-      const int nt2 = (d + kBN - 1) / kBN;
-      // short prompts: 64-token tiles, for twice the blocks (a block's K loop is latency-bound)
-      const int mt64 = (M + 63) / 64;
-      if (mt * nt2 < POP_DOWN_BM64_BELOW)
-        POP_LAUNCH((k_prompt_down<64, POP_DOWN_NS>), dim3(mt64 * nt2), dim3(kGThreads), 0, st, (const uint16_t*)ws,
-                   M, ldz, (const bf16s*)WdT, (int)d_ff, (int)d, Yc, mt64, nt2);
-      else
-        POP_LAUNCH((k_prompt_down<128, POP_DOWN_NS>), dim3(mt * nt2), dim3(kGThreads), 0, st, (const uint16_t*)ws,
-                   M, ldz, (const bf16s*)WdT, (int)d_ff, (int)d, Yc, mt, nt2);
+      launch_gateup(st, imp ? (mt >= 4 ? 4 : mt >= 2 ? 2 : 1) : 0, Xc, M, (int)d, (const bf16s*)Wg,
+                    (const bf16s*)Wu, (int)d_ff, (uint16_t*)ws, ldz, s2, I);
+      launch_down(st, (const uint16_t*)ws, M, ldz, ldz, (const bf16s*)WdT, (int)d_ff, (int)d, Yc);
     } else {
       const float* Xc = (const float*)X + t0 * d;
       const int mt = (M + kFT - 1) / kFT;
@@ -539,9 +754,7 @@ void launch_gemm_kmajor(void* stream, const void* A, int M, int lda, const void*
     const int Mc = M - m0 < (int)kChunkTokens ? M - m0 : (int)kChunkTokens;
     float* Yc = Y + (int64_t)m0 * N;
     if (dt == POP_BF16) {
-      const int mt = (Mc + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;
-      POP_LAUNCH((k_prompt_down<128, POP_DOWN_NS>), dim3(mt * nt), dim3(kGThreads), 0, st,
-                 (const uint16_t*)A + (int64_t)m0 * lda, Mc, lda, (const bf16s*)Bk, K, N, Yc, mt, nt);
+      launch_down(st, (const uint16_t*)A + (int64_t)m0 * lda, Mc, lda, K, (const bf16s*)Bk, K, N, Yc);
     } else {
       POP_LAUNCH(k_prompt_down_f32, dim3((N + kFT - 1) / kFT, (Mc + kFT - 1) / kFT), dim3(kFT * kFT), 0, st,
                  (const float*)A + (int64_t)m0 * lda, Mc, lda, (const float*)Bk, K, N, Yc);
