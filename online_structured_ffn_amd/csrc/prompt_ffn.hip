@@ -36,7 +36,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaveThreads = 256;  // one group of four waves
 constexpr int kBM = 128;         // tokens per block (both GEMMs): 32 per wave of a group
-constexpr int kGuKC = 32;        // gate/up: reduction elements per stage
 constexpr int kDnKC = 64;        // down: reduction elements per stage
 constexpr int kDnBN = 64;        // down: output columns per block
 constexpr int kZPad = 64;        // Z row pitch = d_ff rounded up to this
@@ -54,6 +53,10 @@ constexpr int64_t kChunkTokens = 4096;  // tokens per pass (bounds the workspace
 #define POP_GATEUP_PD 2  // channel fragments read ahead of the MFMAs in the gate/up pass
 #endif
 constexpr int kGuThreads = kWaveThreads * POP_PROMPT_GR;  // threads per workgroup (one per compute unit)
+#ifndef POP_GATEUP_KC
+#define POP_GATEUP_KC 32  // gate/up: reduction elements per stage (32: 64-byte rows, 64: 128-byte rows)
+#endif
+constexpr int kGuKC = POP_GATEUP_KC;
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t b = __float_as_uint(f);
@@ -163,17 +166,24 @@ __global__ __launch_bounds__(kWaveThreads * GR, 1) void k_prompt_gateup(const bf
                                                                 uint16_t* __restrict__ Z, int ldz, int mt, int nt,
                                                                 const float* __restrict__ s2, float* __restrict__ I) {
   constexpr int KC = kGuKC;
+  constexpr int CPR = KC / 8;            // 16-byte chunks per row and stage
+  constexpr int RPI = 64 / CPR;          // rows per load instruction (1 KB)
+  constexpr int KH = KC / 32;            // 32-reduction halves per stage
   constexpr int BR = 16 * NF;            // channels per block and matrix
   constexpr int ROWS = kBM + 2 * BR;     // tile rows per stage
-  constexpr int NI = ROWS / 16;          // load instructions per stage (16 rows each)
+  constexpr int NI = ROWS / RPI;         // load instructions per stage
   constexpr int NW = 4 * GR;             // waves
   constexpr int LPW = (NI + NW - 1) / NW;  // per wave; the spare ones repeat instruction NI - 1
-  constexpr int STAGE = ROWS * KC;       // bf16 elements per stage
+  constexpr int STILE = ROWS * KC;       // bf16 elements of a stage's tile
+  constexpr int STAGE = STILE + (IMP > 0 ? 512 : 0);   // + 1 KB holding the stage's s^2 (importance only)
+  constexpr int NSF = 163840 / (2 * STAGE) / GR * GR;  // stages that fit in LDS
+  constexpr int NSR = NS < NSF ? NS : NSF;             // ring depth
   constexpr int G = IMP > 0 ? BR / (IMP > 0 ? IMP : 1) : 1;  // importance channels per block
   constexpr int NPR = (G + 63) / 64;
-  static_assert(NS % GR == 0 && NS >= 2 * GR && (NS - 2 * GR) * LPW < 64, "ring depth");
-  static_assert(GR * LPW <= NF, "the refill loads ride on the first GR LPW channel fragments");
-  __shared__ __align__(16) uint16_t smem[NS * STAGE];
+  static_assert(KC == 32 || KC == 64, "stage width");
+  static_assert(NSR % GR == 0 && NSR >= 2 * GR && (NSR - 2 * GR) * LPW < 64, "ring depth");
+  static_assert(GR * LPW <= KH * NF, "the refill loads ride on the first GR LPW fragment steps");
+  __shared__ __align__(16) uint16_t smem[NSR * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2, wv = wave & 3;
@@ -182,14 +192,15 @@ __global__ __launch_bounds__(kWaveThreads * GR, 1) void k_prompt_gateup(const bf
   const int m0 = m_tile * kBM, n0 = n_tile * BR;
   const uint32_t lds0 = lds_addr(smem);
 
-  // load instruction m of this wave fills rows 16 j + [0, 16): lane i row 16 j + i / 4, slot i % 4
+  // load instruction m of this wave fills rows RPI j + [0, RPI): lane i row
+  // RPI j + i / CPR, slot i % CPR, which holds chunk co[m] / 8 of that row
   const bf16s* rowp[LPW];
+  int co[LPW];
   uint32_t lofs[LPW];
-  const int co = 8 * kslot<KC>(lane & 3, lane >> 2);  // first element of the chunk this lane loads
 #pragma unroll
   for (int m = 0; m < LPW; ++m) {
     const int j = min(wave + NW * m, NI - 1);
-    const int row = 16 * j + (lane >> 2);
+    const int row = RPI * j + lane / CPR;
     const bf16s* p;
     if (row < kBM)
       p = X + (int64_t)min(m0 + row, M - 1) * d;
@@ -198,12 +209,19 @@ __global__ __launch_bounds__(kWaveThreads * GR, 1) void k_prompt_gateup(const bf
     else
       p = Wu + (int64_t)min(n0 + row - kBM - BR, d_ff - 1) * d;
     rowp[m] = p;
-    lofs[m] = 2u * 16u * KC * j;
+    co[m] = 8 * kslot<KC>(lane % CPR, row);
+    lofs[m] = 2u * RPI * KC * j;
   }
-  // load m of stage st into ring slot q
+  // load m of stage st into ring slot q; m = LPW (wave 0, importance only):
+  // the stage's KC values of s^2, 16 bytes a lane (lanes past them load zeros)
   auto issue1 = [&](int st, int q, int m) {
     const int k0 = st * KC;
-    dma16(k0 + co < d ? (const void*)(rowp[m] + k0 + co) : (const void*)kZero16, lds0 + 2u * STAGE * q + lofs[m]);
+    if (m < LPW)
+      dma16(k0 + co[m] < d ? (const void*)(rowp[m] + k0 + co[m]) : (const void*)kZero16,
+            lds0 + 2u * STAGE * q + lofs[m]);
+    else if (IMP > 0 && wave == 0)
+      dma16(lane < KC / 4 && k0 + 4 * lane < d ? (const void*)(s2 + k0 + 4 * lane) : (const void*)kZero16,
+            lds0 + 2u * (STAGE * q + STILE));
   };
 
   const bool imp = IMP > 0 && m_tile < IMP;  // block-uniform
@@ -217,77 +235,104 @@ __global__ __launch_bounds__(kWaveThreads * GR, 1) void k_prompt_gateup(const bf
 #pragma unroll
     for (int f = 0; f < NF; ++f) ag[i][f] = au[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15;
-  const int asl = 8 * kslot<KC>(lane >> 4, fr);  // this lane's chunk in every fragment row
-  // Stage st from slot q.  The refill (stages rst and rst + 1 into slots rq
-  // and rq + 1, this wave's share) rides on the first MFMAs, one load per
-  // channel fragment; the scheduling barriers keep that order.
+  // Stage st from slot q, as NX = KH NF fragment steps x = h NF + f (half h,
+  // channel fragment f); the reads run PD steps ahead of the MFMAs, and the
+  // refill (stages rst .. rst + GR - 1 into slots rq .., this wave's share)
+  // rides on the first steps, one load each; the scheduling barriers keep
+  // that order.
   auto compute = [&](int st, int q, int rst, int rq) {
     const uint16_t* base = smem + q * STAGE;
-    float sv[8];
-    if constexpr (IMP > 0) {
-      if (imp) {  // this wave's 8 columns of s2 (wave-uniform: scalar loads)
-        const float* sp = s2 + min(st * KC + 8 * wv, d - 8);
+    constexpr int NX = KH * NF;
+    constexpr int PD = POP_GATEUP_PD < NX ? POP_GATEUP_PD : NX;
+    bf16x8 a[KH][2], bg[NX], bu[NX];
+    auto read_a = [&](int h) {
+      const int sl = 8 * kslot<KC>(4 * h + (lane >> 4), fr);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sv[e] = sp[e];
-      }
-    }
-    bf16x8 a[2], bg[NF], bu[NF];
-    auto read_b = [&](int f) {
-      bg[f] = lds_frag(base + (kBM + 16 * f + fr) * KC + asl);
-      bu[f] = lds_frag(base + (kBM + BR + 16 * f + fr) * KC + asl);
+      for (int i = 0; i < 2; ++i) a[h][i] = lds_frag(base + (32 * wv + 16 * i + fr) * KC + sl);
     };
-    // the token fragments and PD channel fragments first; then, per channel
-    // fragment f: the reads of fragment f + PD, a refill load, f's 4 MFMAs
-    constexpr int PD = POP_GATEUP_PD < NF ? POP_GATEUP_PD : NF;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = lds_frag(base + (32 * wv + 16 * i + fr) * KC + asl);
-#pragma unroll
-    for (int f = 0; f < PD; ++f) read_b(f);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      if (f + PD < NF) read_b(f + PD);
-      if (f < GR * LPW) issue1(rst + f / LPW, rq + f / LPW, f % LPW);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        ag[i][f] = mfma(a[i], bg[f], ag[i][f]);
-        au[i][f] = mfma(a[i], bu[f], au[i][f]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (IMP > 0) {
-      if (imp && st * KC + 8 * wv < d) {
+    auto read_b = [&](int x) {
+      const int h = x / NF, f = x % NF;
+      const int sl = 8 * kslot<KC>(4 * h + (lane >> 4), fr);
+      bg[x] = lds_frag(base + (kBM + 16 * f + fr) * KC + sl);
+      bu[x] = lds_frag(base + (kBM + BR + 16 * f + fr) * KC + sl);
+    };
+    // Importance (IMP > 0): per chunk h (columns 8 (wv + 4 h) + [0, 8)) one
+    // read of the W_up row of channel m_tile G + lane + 64 j and of the
+    // chunk's s^2 (the same 32 bytes for every lane), then four steps of two
+    // products each, spread over the last fragment steps so that they run
+    // between the MFMAs.  Every block does it (the blocks past the first IMP
+    // token tiles and the lanes past G compute sums that are never stored);
+    // chunks past d hold zeros.
+    u32x4 wi[KH][NPR];
+    f32x4 sv[KH][2];
+    constexpr int NK = 5 * KH;  // importance steps
+    auto imp_step = [&](int k) {
+      const int h = k / 5, s = k % 5;
+      if (s == 0) {
+        const f32x4* sp = reinterpret_cast<const f32x4*>(base + STILE) + 2 * (wv + 4 * h);
+        sv[h][0] = sp[0];
+        sv[h][1] = sp[1];
 #pragma unroll
         for (int j = 0; j < NPR; ++j) {
-          const int c = lane + 64 * j;
-          if (c < G) {
-            const int row = kBM + BR + m_tile * G + c;
-            const u32x4 w = *reinterpret_cast<const u32x4*>(base + row * KC + 8 * kslot<KC>(wv, row));
+          const int row = kBM + BR + m_tile * G + min(lane + 64 * j, G - 1);
+          wi[h][j] = *reinterpret_cast<const u32x4*>(base + row * KC + 8 * kslot<KC>(wv + 4 * h, row));
+        }
+      } else {
+        const int e = s - 1;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float w0 = __uint_as_float(w[e] << 16), w1 = __uint_as_float(w[e] & 0xffff0000u);
-              ia[j] = fmaf(w0 * w0, sv[2 * e], ia[j]);
-              ia[j] = fmaf(w1 * w1, sv[2 * e + 1], ia[j]);
-            }
-          }
+        for (int j = 0; j < NPR; ++j) {
+          const float w0 = __uint_as_float(wi[h][j][e] << 16), w1 = __uint_as_float(wi[h][j][e] & 0xffff0000u);
+          ia[j] = fmaf(w0 * w0, sv[h][e >> 1][2 * (e & 1)], ia[j]);
+          ia[j] = fmaf(w1 * w1, sv[h][e >> 1][2 * (e & 1) + 1], ia[j]);
         }
       }
+    };
+    read_a(0);
+#pragma unroll
+    for (int x = 0; x < PD; ++x) {
+      if (x > 0 && x % NF == 0) read_a(x / NF);
+      read_b(x);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      const int y = x + PD;
+      if (y < NX) {
+        if (y % NF == 0) read_a(y / NF);
+        read_b(y);
+      }
+      if (x < GR * LPW) issue1(rst + x / LPW, rq + x / LPW, x % LPW);
+      if (IMP > 0 && x == (GR * LPW < NX ? GR * LPW : NX - 1))
+#pragma unroll
+        for (int r = 0; r < GR; ++r) issue1(rst + r, rq + r, LPW);
+      if constexpr (IMP > 0) {
+#pragma unroll
+        for (int k = 0; k < NK; ++k)
+          if ((NX >= NK ? NX - NK + k : k * NX / NK) == x) imp_step(k);
+      }
+      const int h = x / NF, f = x % NF;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        ag[i][f] = mfma(a[h][i], bg[x], ag[i][f]);
+        au[i][f] = mfma(a[h][i], bu[x], au[i][f]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // (the inner loop unrolls fully: every ring slot index is a constant)
   const int nst = (d + KC - 1) / KC;
 #pragma unroll
-  for (int u = 0; u < NS - GR; ++u)
+  for (int u = 0; u < NSR - GR; ++u)
 #pragma unroll
-    for (int m = 0; m < LPW; ++m) issue1(u, u, m);
-  for (int s0 = 0; s0 < nst; s0 += NS) {
+    for (int m = 0; m < LPW + (IMP > 0 ? 1 : 0); ++m) issue1(u, u, m);
+  for (int s0 = 0; s0 < nst; s0 += NSR) {
 #pragma unroll
-    for (int u = 0; u < NS; u += GR) {
+    for (int u = 0; u < NSR; u += GR) {
       const int st = s0 + u;
       if (st >= nst) break;
-      ring_barrier<(NS - 2 * GR) * LPW>();
-      compute(st + grp, u + grp, st + NS - GR, (u + NS - GR) % NS);
+      ring_barrier<(NSR - 2 * GR) * LPW>();
+      compute(st + grp, u + grp, st + NSR - GR, (u + NSR - GR) % NSR);
     }
   }
   ring_barrier<0>();  // the spare loads landed; every wave is done with the ring
