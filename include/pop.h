@@ -117,6 +117,27 @@ pop_status pop_partition_counts(int32_t d_ff, double r, double gamma, pop_counts
  */
 pop_status pop_decode_topk_count(int32_t d_ff, double r, int32_t n_R, int32_t n_C, int32_t* k);
 
+/*
+ * pop_check_lists — pure host function, no device work: a debug aid.
+ * Checks host copies of a partition's index lists against what every entry
+ * point taking R, C (or P) assumes: counts >= 0 with n_R + n_C + n_P <= d_ff;
+ * each list strictly ascending within [0, d_ff); no channel in two lists.
+ * The device code does not check these (it clamps channel ids into [0, d_ff),
+ * so a bad list gives wrong results, not a fault).  A library built with
+ * POP_DEBUG defined (libpop_debug.so) runs this check on copies of R and C
+ * inside pop_decode_ffn (and so pop_decode_ffn_noalloc), pop_decode_gateup,
+ * pop_decode_ffn_periodic and pop_layer_decode before anything is enqueued:
+ * a device-to-host copy on the call's stream, waited for, and a host
+ * allocation, so such a build can not be captured into a graph.
+ *   R, C, P    host int32 arrays (each may be NULL when its count is 0).
+ * Errors: BAD_SHAPE for d_ff outside [1, POP_MAX_D_FF]; INVALID_ARGUMENT for
+ * negative counts, counts summing past d_ff, a NULL list with a nonzero
+ * count, or the first violation found (pop_last_error() names the list, the
+ * position and the value).
+ */
+pop_status pop_check_lists(const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C, const int32_t* P,
+                           int32_t n_P, int32_t d_ff);
+
 /* Workspace bytes pop_prefill_partition needs for these sizes. */
 size_t pop_prefill_workspace_bytes(int64_t n_tokens, int32_t d, int32_t d_ff);
 

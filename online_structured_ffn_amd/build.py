@@ -1,4 +1,6 @@
-"""Compile libpop.so for gfx950 with hipcc (in-tree, next to this file).
+"""Compile libpop.so for gfx950 with hipcc (in-tree, next to this file), and
+its checking twin libpop_debug.so (POP_DEBUG: every entry point that takes
+a partition's index lists validates them on the host first).
 
     python -m online_structured_ffn_amd.build
 """
@@ -14,6 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libpop.so")
+OUT_DEBUG = os.path.join(PKG, "libpop_debug.so")
+DEBUG_DEFINES = ("POP_DEBUG=1",)
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["pop_host.cpp", "trace.hip", "prefill.hip", "decode.hip", "prompt_ffn.hip", "moe.hip", "periodic.hip", "layer.hip"]
@@ -58,5 +62,10 @@ def build(verbose: bool = True, out: str = OUT, defines=()) -> str:
     return out
 
 
+def build_all(verbose: bool = True) -> None:
+    build(verbose)
+    build(verbose, OUT_DEBUG, DEBUG_DEFINES)
+
+
 if __name__ == "__main__":
-    build()
+    build_all()

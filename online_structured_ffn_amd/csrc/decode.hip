@@ -9,6 +9,8 @@
 //   K6r fixed-order reduction of the partial sums into y
 #include <hip/hip_runtime.h>
 
+#include <vector>
+
 #include <map>
 #include <mutex>
 #include <type_traits>
@@ -1572,14 +1574,30 @@ static pop_status check_shape(int32_t batch, int32_t d, int32_t d_ff, pop_dtype 
 }
 
 static pop_status check_lists(int32_t d_ff, const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C,
-                              bool r_may_be_identity) {
+                              bool r_may_be_identity, void* stream) {
   if (n_R < 0 || n_C < 0 || (int64_t)n_R + n_C > d_ff)
     return fail(POP_ERR_INVALID_ARGUMENT, "n_R=%d, n_C=%d inconsistent with d_ff=%d", n_R, n_C, d_ff);
   if ((n_R > 0 && R == nullptr && !r_may_be_identity) || (n_C > 0 && C == nullptr))
     return fail(POP_ERR_INVALID_ARGUMENT, "R or C is NULL with a nonzero size");
   if (R == nullptr && r_may_be_identity && n_C > 0 && n_R > 0)
     return fail(POP_ERR_INVALID_ARGUMENT, "R == NULL (identity) is only valid with n_C == 0");
+  if (kDebugLists) return debug_check_device_lists(R, n_R, C, n_C, d_ff, stream);
   return POP_OK;
+}
+
+pop_status debug_check_device_lists(const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C, int32_t d_ff,
+                                    void* stream) {
+  if (debug_nesting() > 0) return POP_OK;  // the outer entry point checked its own lists
+  // the copies go on the caller's stream, behind whatever wrote the lists
+  std::vector<int32_t> hr(R != nullptr && n_R > 0 ? n_R : 0), hc(C != nullptr && n_C > 0 ? n_C : 0);
+  const hipStream_t h = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (!hr.empty()) e = hipMemcpyAsync(hr.data(), R, hr.size() * sizeof(int32_t), hipMemcpyDeviceToHost, h);
+  if (e == hipSuccess && !hc.empty()) e = hipMemcpyAsync(hc.data(), C, hc.size() * sizeof(int32_t), hipMemcpyDeviceToHost, h);
+  if (e == hipSuccess) e = hipStreamSynchronize(h);
+  if (e != hipSuccess) return fail(POP_ERR_HIP, "debug copy of the index lists failed: %s", hipGetErrorString(e));
+  return pop_check_lists(hr.empty() ? nullptr : hr.data(), (int32_t)hr.size(), hc.empty() ? nullptr : hc.data(),
+                         (int32_t)hc.size(), nullptr, 0, d_ff);
 }
 
 }  // namespace pop
@@ -1641,7 +1659,7 @@ extern "C" pop_status pop_decode_gateup(const void* x, int32_t batch, int32_t d,
   clear_error();
   pop_status s = check_shape(batch, d, d_ff, dt);
   if (s != POP_OK) return s;
-  if ((s = check_lists(d_ff, R, n_R, C, n_C, true)) != POP_OK) return s;
+  if ((s = check_lists(d_ff, R, n_R, C, n_C, true, stream)) != POP_OK) return s;
   if ((batch > 0 && (x == nullptr || z == nullptr)) || W_gate == nullptr || W_up == nullptr)
     return fail(POP_ERR_INVALID_ARGUMENT, "x, z, W_gate and W_up must be non-NULL");
   if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up))
@@ -1694,7 +1712,7 @@ extern "C" pop_status pop_decode_ffn(const void* x, int32_t batch, int32_t d, co
   pop_status s = check_shape(batch, d, d_ff, dt);
   if (s != POP_OK) return s;
   if (!(r >= 0.0 && r < 1.0)) return fail(POP_ERR_INVALID_ARGUMENT, "r=%g outside [0, 1)", r);
-  if ((s = check_lists(d_ff, R, n_R, C, n_C, false)) != POP_OK) return s;
+  if ((s = check_lists(d_ff, R, n_R, C, n_C, false, stream)) != POP_OK) return s;
   if ((batch > 0 && (x == nullptr || y == nullptr)) || W_gate == nullptr || W_up == nullptr || W_downT == nullptr ||
       ws == nullptr)
     return fail(POP_ERR_INVALID_ARGUMENT, "a required pointer is NULL");

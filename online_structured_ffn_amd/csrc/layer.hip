@@ -1094,7 +1094,12 @@ extern "C" pop_status pop_layer_decode(float* x, int32_t batch, const pop_layer_
       return fail(POP_ERR_INVALID_ARGUMENT, "n_R=%d, n_C=%d inconsistent with d_ff=%d", n_R, n_C, s->d_ff);
     if ((n_R > 0 && R == nullptr) || (n_C > 0 && C == nullptr))
       return fail(POP_ERR_INVALID_ARGUMENT, "R or C is NULL with a nonzero size");
+    if (kDebugLists) {
+      const pop_status sd = debug_check_device_lists(R, n_R, C, n_C, s->d_ff, stream);
+      if (sd != POP_OK) return sd;
+    }
   }
+  const DebugNested nest;  // R and C are checked above
   hipStream_t h = (hipStream_t)stream;
   trace_mark(h);
   if (dt == POP_BF16)

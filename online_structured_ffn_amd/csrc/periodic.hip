@@ -116,6 +116,11 @@ extern "C" pop_status pop_decode_ffn_periodic(const void* x, int32_t batch, int3
       (k > 0 && (memory == nullptr || positions == nullptr || selected == nullptr)) ||
       (n_R + k > 0 && rows == nullptr) || ws == nullptr)
     return fail(POP_ERR_INVALID_ARGUMENT, "R, C, memory, positions, selected, rows and ws must be non-NULL");
+  if (kDebugLists) {
+    const pop_status sd = debug_check_device_lists(R, n_R, C, n_C, d_ff, stream);
+    if (sd != POP_OK) return sd;
+  }
+  const DebugNested nest;  // the calls below pass the retained rows (R, then the selection)
   if (!aligned16(ws)) return fail(POP_ERR_MISALIGNED, "ws must be 16-byte aligned");
   const PeriodicWs w0 = periodic_ws(batch, d, d_ff, nullptr);
   if (ws_bytes < w0.bytes) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, w0.bytes);

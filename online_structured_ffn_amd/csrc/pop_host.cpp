@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "pop_internal.h"
 
 namespace pop {
@@ -21,6 +23,11 @@ pop_status fail(pop_status s, const char* fmt, ...) {
 }
 
 void clear_error() { g_err[0] = '\0'; }
+
+int& debug_nesting() {
+  static thread_local int depth = 0;
+  return depth;
+}
 
 // Round half away from zero (C's round()).
 static int64_t round_half_away(double v) { return (int64_t)round(v); }
@@ -114,6 +121,35 @@ pop_status pop_decode_topk_count(int32_t d_ff, double r, int32_t n_R, int32_t n_
   if (n_R < 0 || n_C < 0 || (int64_t)n_R + n_C > d_ff)
     return pop::fail(POP_ERR_INVALID_ARGUMENT, "n_R=%d, n_C=%d inconsistent with d_ff=%d", n_R, n_C, d_ff);
   *k = pop::topk_count(d_ff, r, n_R, n_C);
+  return POP_OK;
+}
+
+pop_status pop_check_lists(const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C, const int32_t* P,
+                           int32_t n_P, int32_t d_ff) {
+  pop::clear_error();
+  if (d_ff < 1 || d_ff > POP_MAX_D_FF) return pop::fail(POP_ERR_BAD_SHAPE, "d_ff=%d outside [1, %d]", d_ff, POP_MAX_D_FF);
+  if (n_R < 0 || n_C < 0 || n_P < 0 || (int64_t)n_R + n_C + n_P > d_ff)
+    return pop::fail(POP_ERR_INVALID_ARGUMENT, "n_R=%d, n_C=%d, n_P=%d inconsistent with d_ff=%d", n_R, n_C, n_P,
+                     d_ff);
+  const int32_t* lists[3] = {R, C, P};
+  const int32_t ns[3] = {n_R, n_C, n_P};
+  const char* names[3] = {"R", "C", "P"};
+  std::vector<signed char> owner((size_t)d_ff, (signed char)-1);  // the list holding each channel
+  for (int l = 0; l < 3; ++l) {
+    if (ns[l] > 0 && lists[l] == nullptr) return pop::fail(POP_ERR_INVALID_ARGUMENT, "%s is NULL with %d entries", names[l], ns[l]);
+    for (int32_t i = 0; i < ns[l]; ++i) {
+      const int32_t c = lists[l][i];
+      if (c < 0 || c >= d_ff)
+        return pop::fail(POP_ERR_INVALID_ARGUMENT, "%s[%d] = %d outside [0, %d)", names[l], i, c, d_ff);
+      if (i > 0 && c <= lists[l][i - 1])
+        return pop::fail(POP_ERR_INVALID_ARGUMENT, "%s[%d] = %d does not follow %s[%d] = %d in ascending order",
+                         names[l], i, c, names[l], i - 1, lists[l][i - 1]);
+      if (owner[(size_t)c] >= 0)
+        return pop::fail(POP_ERR_INVALID_ARGUMENT, "channel %d is in %s and %s (%s[%d])", c, names[owner[(size_t)c]],
+                         names[l], names[l], i);
+      owner[(size_t)c] = (signed char)l;
+    }
+  }
   return POP_OK;
 }
 

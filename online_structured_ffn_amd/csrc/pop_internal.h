@@ -25,6 +25,29 @@ pop_status check_rate(double r, double gamma);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// pop_check_lists on copies of the device lists R and C (R == NULL: the
+// identity, not checked), copied on `stream` (a hipStream_t) and waited for.
+// Called by the entry points that take R and C only in builds with POP_DEBUG
+// defined (defined in decode.hip).
+pop_status debug_check_device_lists(const int32_t* R, int32_t n_R, const int32_t* C, int32_t n_C, int32_t d_ff,
+                                    void* stream);
+// Entry points calling other entry points on this thread: the debug check
+// runs at the outermost call only, since an inner call may get lists the
+// library built itself (retained rows followed by the selection, say) that
+// need not be ascending.  A DebugNested object marks its scope as inner.
+int& debug_nesting();
+struct DebugNested {
+  DebugNested() { ++debug_nesting(); }
+  ~DebugNested() { --debug_nesting(); }
+  DebugNested(const DebugNested&) = delete;
+  DebugNested& operator=(const DebugNested&) = delete;
+};
+#ifdef POP_DEBUG
+constexpr bool kDebugLists = true;
+#else
+constexpr bool kDebugLists = false;
+#endif
+
 // Prefill pieces shared with the fused prefill FFN (defined in prefill.hip;
 // stream is a hipStream_t).  colsq_ws_bytes sizes the column-norm workspace
 // (partial sums, then s2); launch_colsq writes s2 = sum over the prompt rows of

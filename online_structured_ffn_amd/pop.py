@@ -5,18 +5,27 @@ libpop.so.  Importing this module loads the library and raises ImportError
 when it has not been built (run ``python -m online_structured_ffn_amd.build``);
 there is no fallback.  Tensors are torch tensors on the current HIP device;
 work is enqueued on ``stream`` (default: torch's current stream).
+
+libpop_debug.so, built beside libpop.so, validates the partition's index
+lists on the host inside every entry point that takes them; select it for a
+whole process with POP_LIBRARY, or for a block of calls with
+``using_library(DEBUG_LIB_PATH)``.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
+
+import numpy as np
 
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # POP_LIBRARY selects another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("POP_LIBRARY") or os.path.join(_HERE, "libpop.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libpop_debug.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "pop.h")
 
 POP_F32, POP_BF16 = 0, 1
@@ -46,15 +55,21 @@ class PopError(RuntimeError):
         super().__init__(f"{func}: {status_string(status)}: {detail}")
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m online_structured_ffn_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+_loaded: dict = {}
+
+
+def _load(path: str = LIB_PATH):
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m online_structured_ffn_amd.build`")
+    lib = ctypes.CDLL(path)
     sig = {
         "pop_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pop_last_error": (ctypes.c_char_p, []),
         "pop_partition_counts": (ctypes.c_int, [_c_i32, _c_dbl, _c_dbl, ctypes.POINTER(PopCounts)]),
         "pop_decode_topk_count": (ctypes.c_int, [_c_i32, _c_dbl, _c_i32, _c_i32, ctypes.POINTER(_c_i32)]),
+        "pop_check_lists": (ctypes.c_int, [_c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_i32]),
         "pop_prefill_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32]),
         "pop_prefill_partition": (ctypes.c_int, [_c_vp, _c_i64, _c_i32, _c_vp, _c_i32, ctypes.c_int, _c_dbl, _c_dbl,
                                                  _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
@@ -111,10 +126,24 @@ def _load():
         f = getattr(lib, name)
         f.restype = res
         f.argtypes = args
+    _loaded[path] = lib
     return lib
 
 
 lib = _load()
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route this module's calls through another build of libpop (loaded
+    beside the default one) inside the block; not thread-safe."""
+    global lib
+    prev = lib
+    lib = _load(path)
+    try:
+        yield lib
+    finally:
+        lib = prev
 
 
 def _header_define(name: str) -> int:
@@ -171,6 +200,19 @@ def pop_partition_counts(d_ff: int, r: float, gamma: float) -> dict:
     c = PopCounts()
     _check("pop_partition_counts", lib.pop_partition_counts(int(d_ff), float(r), float(gamma), ctypes.byref(c)))
     return {n: getattr(c, n) for n, _ in PopCounts._fields_}
+
+
+def pop_check_lists(R, C, d_ff: int, P=None) -> None:
+    """Host check of a partition's index lists (array-likes of channel ids):
+    each strictly ascending in [0, d_ff), no channel in two lists.  Raises
+    PopError naming the first violation."""
+    arrs = [np.ascontiguousarray(np.asarray(a if a is not None else [], dtype=np.int64).ravel()) for a in (R, C, P)]
+    if any(a.size and (a.min() < -2**31 or a.max() >= 2**31) for a in arrs):
+        raise ValueError("channel ids must fit in int32")
+    arrs = [a.astype(np.int32) for a in arrs]
+    ptr = lambda a: ctypes.c_void_p(a.ctypes.data) if a.size else None
+    _check("pop_check_lists", lib.pop_check_lists(ptr(arrs[0]), arrs[0].size, ptr(arrs[1]), arrs[1].size,
+                                                  ptr(arrs[2]), arrs[2].size, int(d_ff)))
 
 
 def pop_prefill_workspace_bytes(n_tokens: int, d: int, d_ff: int) -> int:

@@ -21,6 +21,19 @@ def test_exports_every_declared_symbol():
         assert hasattr(pop.lib, n), n
 
 
+def test_debug_library_exports_and_checks():
+    """libpop_debug.so (built beside libpop.so) exports the same functions."""
+    import os
+    if not os.path.exists(pop.DEBUG_LIB_PATH):
+        pytest.skip("libpop_debug.so is not built")
+    with pop.using_library(pop.DEBUG_LIB_PATH) as dbg:
+        for n in pop.declared_functions():
+            assert hasattr(dbg, n), n
+        with pytest.raises(pop.PopError):
+            pop.pop_check_lists([2, 1], [], 4)
+    assert pop.lib is not dbg
+
+
 def test_counts_match_oracle_everywhere():
     g = np.random.default_rng(0)
     for _ in range(3000):
