@@ -202,7 +202,7 @@ size_t pop_decode_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff);
  * the 32-bit word at offset 0 is a sticky error code: nonzero after a batch-1
  * step whose bounded in-kernel wait ran out (that step's y is then not
  * valid).  The library never clears it. */
-#define POP_DECODE_WS_Z_OFFSET 66560
+#define POP_DECODE_WS_Z_OFFSET 70656
 
 /*
  * pop_decode_ffn — POP notes, "Key design 2" and "Overall framework".
@@ -229,10 +229,11 @@ size_t pop_decode_workspace_bytes(int32_t batch, int32_t d, int32_t d_ff);
  * every other workgroup (a worker) streams an even share of the candidates'
  * gate/up rows (handing each |z| to the top-k through a valid-tagged word),
  * then of the retained channels' gate, up and W_downT rows (z and its down
- * contribution in one pass); the top-k publishes the cut and each worker adds
- * the W_downT rows of its own candidates that the cut selects (their loads
- * issued with its last retained rows when the cut is out by then, else after
- * its rows), then stores its partial y.  The second adds the partials in a fixed order into y and clears
+ * contribution in one pass); the top-k publishes the cut, then the selected
+ * candidates as valid-tagged (channel, z) words, and each worker adds the
+ * W_downT rows of an equal share of them by rank (their loads issued with its
+ * last retained rows when its share is in by then, else after its rows), then
+ * stores its partial y.  The second adds the partials in a fixed order into y and clears
  * the hand-over words.  The grid never exceeds what the device holds at once
  * and every in-kernel wait is bounded (see POP_DECODE_WS_Z_OFFSET for the
  * error word).  Batch 1 without a top-k (no candidates, k = 0): the retained

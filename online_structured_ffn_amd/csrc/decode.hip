@@ -688,13 +688,17 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
 //   2. its retained rows: gate, up and W_downT rows, z, and z * W_downT added
 //      into its partial y (registers); every second row batch also re-reads
 //      the published cut (one coherent 8-byte load beside the rows' loads);
-//   3. the cut: block 0 publishes (v, tie position) once it has selected.  If
-//      the worker's last completed read of the cut found it out before its
-//      last two row batches, it selects its own candidates against it there
-//      (value above v, or equal at a position up to the tie position) and
-//      their W_downT rows' loads go out with those batches; otherwise it
-//      polls for the cut after its rows and adds the selected rows then.
-//      Both ways add the same rows in the same order;
+//   3. the selected rows: block 0 publishes the cut (v, tie position), then
+//      writes the selected candidates, in position order, as valid-tagged
+//      (channel, z) pairs.  Worker w adds the selected rows of ranks
+//      split_at(k, nW, w) .. split_at(k, nW, w + 1), an equal share whoever
+//      owned the candidates.  Wave 0 looks at the cut it read two batch pairs
+//      earlier; once it is out, it loads the worker's pairs (coherent), and
+//      two pairs later, if all are valid, puts them in LDS and flags them
+//      ready (else it loads them again).  If they are ready before the last
+//      two row batches, their W_downT rows' loads go out with those batches;
+//      otherwise the worker polls for its pairs after its rows and adds the
+//      rows then.  Both ways add the same rows in the same order;
 //   4. its partial y, slice-major, with plain stores.
 // k_pop_finish then adds the nW partials in a fixed order into y and clears
 // the hand-over words for the next call.  Only block 0 waits on many
@@ -721,35 +725,17 @@ constexpr int kThrStride = 16;  // 64-bit words between copies (128 bytes)
 #endif
 constexpr int kCandBatch = POP_CAND_BATCH;  // candidate rows whose loads a worker issues together
 // The control words (1 KB), then the hand-over words: the candidate words (at
-// most kLinkedTopkMaxN) and the copies of the cut.  A fixed region at the
-// start of every decode workspace that no other call writes; k_pop_finish
-// leaves it zero (the error word aside).
+// most kLinkedTopkMaxN), the copies of the cut, and the selected pairs (at
+// most kLinkedTopkMaxN).  A fixed region at the start of every decode
+// workspace that no other call writes; k_pop_finish leaves it zero (the error
+// word aside).
 constexpr size_t kCtlBytes = 1024;
-constexpr size_t kHandWords = kLinkedTopkMaxN + kThrCopies * kThrStride;
-constexpr size_t kHandBytes = 2 * kLinkedTopkMaxN * sizeof(uint64_t);
-static_assert(kHandWords * sizeof(uint64_t) <= kHandBytes, "hand-over region");
+constexpr size_t kPairsWord = kLinkedTopkMaxN + kThrCopies * kThrStride;  // first pair word
+constexpr size_t kHandWords = kPairsWord + kLinkedTopkMaxN;
+constexpr size_t kHandBytes = kHandWords * sizeof(uint64_t);
+static_assert(kHandBytes % 256 == 0, "z stays 256-byte aligned");
 
 __device__ __forceinline__ int split_at(int n, int parts, int i) { return (int)(((int64_t)n * i) / parts); }
-
-// A worker's own candidates (channels crow, z in cz, positions c0 + i) that
-// the cut e selects: value bits of |z| above v, or equal at a position up to
-// the tie position.  Channels and z of the selected ones, in candidate
-// order, into s_chan / s_zv; returns their number.  One thread.
-__device__ __forceinline__ int linked_select(uint64_t e, const int* crow, const float* cz, int c0, int nc,
-                                             int* s_chan, float* s_zv) {
-  const uint32_t cv = (uint32_t)(e >> 32) & 0x7fffffffu;
-  const int tie = (int)(uint32_t)e;
-  int m = 0;
-  for (int i = 0; i < nc; ++i) {
-    const uint32_t xb = __float_as_uint(fabsf(cz[i])) & 0x7fffffffu;
-    if (xb > cv || (xb == cv && c0 + i <= tie)) {
-      s_chan[m] = crow[i];
-      s_zv[m] = cz[i];
-      ++m;
-    }
-  }
-  return m;
-}
 
 // The W_downT rows of up to NS selected candidates, every load issued at
 // once; slots past n load the list's last row again (n >= 1).
@@ -793,26 +779,22 @@ __device__ __forceinline__ void sel_consume(const u32x4 (&ws)[NS][NV], const flo
 
 // The last one or two row batches of a worker's stream (X holds batch i0, its
 // loads in flight; PB0 is the partial-sum buffer of the first reduction
-// here), and the selected rows when the cut is known: cw is the last read of
-// the cut, complete by now.  When it is out (and the worker has
-// candidates), its selected candidates go to s_chan / s_zv (count in
-// *sh_nsel) and the first NS of them are added after the rows, their loads
-// issued with the last batches.  Returns how many were added, or -1 when the
-// cut was not known in time.
+// here), and the worker's share of the selected rows (m of them) when wave 0
+// has them in s_chan / s_zv already (*sh_ready): the first NS are added after
+// the rows, their loads issued with the last batches.  Returns how many were
+// added, or -1 when the share was not ready in time.
 template <typename T, int NV, int NS, int PB0>
 __device__ __forceinline__ int linked_last(FusedRowBuf<T, NV>& X, FusedRowBuf<T, NV>& Y, int i0, const int* rows,
                                            int nrows, const T* __restrict__ Wg, const T* __restrict__ Wu,
                                            const T* __restrict__ WdT, int d, int d_ff, const u32x4 (&xv)[NV],
                                            float (&part)[2][kFusedWaves][2 * kFusedP],
-                                           float (&acc)[NV][Vec<T>::N], float* zl, bool sel_here, uint64_t cw,
-                                           const int* crow, const float* cz, int c0, int nc, int* s_chan,
-                                           float* s_zv, int* sh_nsel) {
+                                           float (&acc)[NV][Vec<T>::N], float* zl, bool sel_here, int m,
+                                           const int* s_chan, const float* s_zv, const int* sh_ready, int* sh_nsel) {
   const int nl = max(nrows, 1);
   float zs[kFusedP];
-  // Each wave read the cut on its own, so the waves may disagree on whether
-  // it is out: thread 0 decides from its read (and selects), and the block
-  // takes its decision from LDS.
-  if (threadIdx.x == 0) *sh_nsel = sel_here && is_valid(cw) ? linked_select(cw, crow, cz, c0, nc, s_chan, s_zv) : -1;
+  // Wave 0 (thread 0's wave) wrote the share and the ready flag; the block
+  // takes the decision from LDS.
+  if (threadIdx.x == 0) *sh_nsel = sel_here && *sh_ready != 0 ? m : -1;
   lds_barrier();
   const int got = *sh_nsel;  // block-uniform; -1: the cut was not out
   const bool early = got >= 0;
@@ -840,27 +822,55 @@ __device__ __forceinline__ int linked_last(FusedRowBuf<T, NV>& X, FusedRowBuf<T,
 // entry even when nrows is 0, whose loads then go unused), the cut re-read
 // beside every second batch, and the ending of linked_last.  The first batch
 // is reduced before the loop, so the buffer the loop carries is issued right
-// before it.
+// before it.  Wave 0 also fetches the worker's share of the selected pairs
+// (pairs[s0 .. s0 + m), at most 64) once the cut it read two iterations
+// earlier is out; each step uses only values loaded an iteration or more
+// before, so no wait is added to the stream, and a pair not yet valid is
+// loaded again.
 template <typename T, int NV, int NS>
 __device__ __forceinline__ int linked_stream(FusedRowBuf<T, NV>& A, const int* rows, int nrows,
                                              const T* __restrict__ Wg, const T* __restrict__ Wu,
                                              const T* __restrict__ WdT, int d, int d_ff, const u32x4 (&xv)[NV],
                                              float (&part)[2][kFusedWaves][2 * kFusedP],
                                              float (&acc)[NV][Vec<T>::N], float* zl, bool sel_here,
-                                             const uint64_t* cutw, const int* crow, const float* cz, int c0, int nc,
-                                             int* s_chan, float* s_zv, int* sh_nsel) {
+                                             const uint64_t* cutw, const uint64_t* pairs, int s0, int m,
+                                             int* s_chan, float* s_zv, int* sh_ready, int* sh_nsel) {
   const int nl = max(nrows, 1);
   FusedRowBuf<T, NV> Bf, A2;
   float zs[kFusedP];
   if (nrows <= 2 * kFusedP)
-    return linked_last<T, NV, NS, 0>(A, Bf, 0, rows, nrows, Wg, Wu, WdT, d, d_ff, xv, part, acc, zl, sel_here, 0, crow,
-                                     cz, c0, nc, s_chan, s_zv, sh_nsel);
-  uint64_t cw = ld_coh(cutw);
+    return linked_last<T, NV, NS, 0>(A, Bf, 0, rows, nrows, Wg, Wu, WdT, d, d_ff, xv, part, acc, zl, sel_here, m,
+                                     s_chan, s_zv, sh_ready, sh_nsel);
+  const int lane = threadIdx.x & 63;
+  const bool fetcher = sel_here && m <= 64 && __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;  // wave-uniform
+  uint64_t cw = ld_coh(cutw), cw_old = 0, pv = 0;
+  int st = fetcher ? 0 : 3;  // 0: cut not seen; 1, 2: pairs in flight; 3: done (or not this wave's job)
   fused_issue<T, NV, true>(Bf, rows, kFusedP, nl, Wg, Wu, WdT, d);
   fused_consume<T, NV, true, 0>(A, xv, 0, nrows, d, part, acc, zs);
   fused_put_z(zl, 0, nrows, zs);
   int i0 = kFusedP;  // Bf holds batch i0
   for (; i0 + 2 * kFusedP < nrows; i0 += 2 * kFusedP) {
+    if (st < 3) {  // wave-uniform: wave 0 only
+      if (st == 0) {
+        if (is_valid(cw_old)) {  // read two iterations ago: complete
+          pv = ld_coh(&pairs[s0 + min(lane, m - 1)]);
+          st = 1;
+        }
+      } else if (st == 1) {
+        st = 2;
+      } else if (__ballot(lane < m && !is_valid(pv)) != 0) {  // loaded two iterations ago; not all in yet
+        pv = ld_coh(&pairs[s0 + min(lane, m - 1)]);
+        st = 1;
+      } else {
+        if (lane < m) {
+          s_chan[lane] = clamp_channel((int)((uint32_t)(pv >> 32) & 0x7fffffffu), d_ff);
+          s_zv[lane] = __uint_as_float((uint32_t)pv);
+        }
+        if (lane == 0) *sh_ready = 1;  // after the share: one wave's LDS stores stay in order
+        st = 3;
+      }
+    }
+    cw_old = cw;
     fused_issue<T, NV, true>(A2, rows, i0 + kFusedP, nl, Wg, Wu, WdT, d);
     cw = ld_coh(cutw);
     fused_consume<T, NV, true, 1>(Bf, xv, i0, nrows, d, part, acc, zs);
@@ -869,8 +879,8 @@ __device__ __forceinline__ int linked_stream(FusedRowBuf<T, NV>& A, const int* r
     fused_consume<T, NV, true, 0>(A2, xv, i0 + kFusedP, nrows, d, part, acc, zs);
     fused_put_z(zl, i0 + kFusedP, nrows, zs);
   }
-  return linked_last<T, NV, NS, 1>(Bf, A2, i0, rows, nrows, Wg, Wu, WdT, d, d_ff, xv, part, acc, zl, sel_here, cw, crow,
-                                   cz, c0, nc, s_chan, s_zv, sh_nsel);
+  return linked_last<T, NV, NS, 1>(Bf, A2, i0, rows, nrows, Wg, Wu, WdT, d, d_ff, xv, part, acc, zl, sel_here, m,
+                                   s_chan, s_zv, sh_ready, sh_nsel);
 }
 
 #ifndef POP_LINKED_MINB
@@ -881,7 +891,7 @@ __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
     const T* __restrict__ x, const T* __restrict__ Wg, const T* __restrict__ Wu, const T* __restrict__ WdT,
     const int32_t* __restrict__ R, const int32_t* __restrict__ C, float* __restrict__ z, float* __restrict__ score,
     uint64_t* __restrict__ hand, int32_t* __restrict__ sel_out, float* __restrict__ partial,
-    uint32_t* __restrict__ ctl, int d, int d_ff, int n_R, int n_C, int k, int nW) {
+    uint32_t* __restrict__ ctl, uint64_t* __restrict__ pairs, int d, int d_ff, int n_R, int n_C, int k, int nW) {
   constexpr int V = Vec<T>::N;
   struct Work {
     int rows[kFusedMaxRows];
@@ -891,7 +901,8 @@ __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
     float cpart[kFusedWaves][2 * kCandBatch];
     int crow[kFusedMaxRows];  // this worker's share of C (channels)
     int n_sel;
-    int s_chan[kFusedMaxRows];  // this worker's selected candidates: channel and z
+    int ready;                  // s_chan / s_zv hold the share (set by wave 0)
+    int s_chan[kFusedMaxRows];  // this worker's share of the selected candidates: channel and z
     float s_zv[kFusedMaxRows];
   };
   __shared__ union {
@@ -905,19 +916,21 @@ __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
   if (blockIdx.x == 0) {
     if (chain)
       topk_threshold_linked(cand, n_C, k, C, (int32_t*)nullptr, sel_out, thr, kThrCopies, kThrStride, sh.sel,
-                            kPollLimit, ctl + kCtlErr);
+                            kPollLimit, ctl + kCtlErr, nullptr, pairs);
     return;
   }
   const int w = blockIdx.x - 1;
   const int c0 = split_at(n_C, nW, w), nc = split_at(n_C, nW, w + 1) - c0;
   const int r0 = split_at(n_R, nW, w), nr = split_at(n_R, nW, w + 1) - r0;
+  const int s0 = split_at(k, nW, w), m = split_at(k, nW, w + 1) - s0;  // this worker's selected ranks
   u32x4 xv[NV];
   float acc[NV][V];
   fused_setup<T, NV>(x, d, xv, acc);
   for (int i = tid; i < nc; i += kFusedThreads) sh.w.crow[i] = clamp_channel(C[c0 + i], d_ff);
   for (int i = tid; i < nr; i += kFusedThreads) sh.w.rows[i] = kIdentity ? r0 + i : clamp_channel(R[r0 + i], d_ff);
+  if (tid == 0) sh.w.ready = 0;
   __syncthreads();
-  const bool sel_here = chain && nc > 0;
+  const bool sel_here = chain && m > 0;
   const uint64_t* cutw = thr + (w % kThrCopies) * kThrStride;
   // with no retained rows, the stream's (unused) loads read the first candidate's rows
   const int* rlist = nr > 0 ? sh.w.rows : sh.w.crow;
@@ -939,29 +952,32 @@ __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
   }
   // 2. retained rows (and, when the cut is out in time, the selected rows)
   int done = linked_stream<T, NV, kLinkedNS>(A, rlist, nr, Wg, Wu, WdT, d, d_ff, xv, sh.w.part, acc, sh.w.zr, sel_here,
-                                             cutw, sh.w.crow, sh.w.cz, c0, nc, sh.w.s_chan, sh.w.s_zv, &sh.w.n_sel);
+                                             cutw, pairs, s0, m, sh.w.s_chan, sh.w.s_zv, &sh.w.ready, &sh.w.n_sel);
   __syncthreads();
   for (int i = tid; i < nr; i += kFusedThreads) z[r0 + i] = sh.w.zr[i];
-  // 3. otherwise the cut now, and this worker's selected candidates
+  // 3. otherwise this worker's share of the selected pairs now, each polled
+  //    until valid (a wait that runs out leaves z = 0 and sets the error word)
   int ns = 0;
   if (sel_here) {
     if (done < 0) {
-      if (tid == 0) {
+      for (int i = tid; i < m; i += kFusedThreads) {
         bool ok;
-        const uint64_t e = poll_coh(cutw, [](uint64_t v) { return is_valid(v); }, kPollLimit, ok);
+        const uint64_t pv = poll_coh(&pairs[s0 + i], [](uint64_t v) { return is_valid(v); }, kPollLimit, ok);
         if (!ok) st_coh(ctl + kCtlErr, 2u);
-        sh.w.n_sel = ok ? linked_select(e, sh.w.crow, sh.w.cz, c0, nc, sh.w.s_chan, sh.w.s_zv) : 0;
+        sh.w.s_chan[i] = clamp_channel((int)((uint32_t)(pv >> 32) & 0x7fffffffu), d_ff);
+        sh.w.s_zv[i] = ok ? __uint_as_float((uint32_t)pv) : 0.f;
       }
       __syncthreads();
       done = 0;
     }
-    ns = sh.w.n_sel;
+    ns = m;
   }
-  for (int s0 = done; s0 < ns; s0 += kLinkedNS) {
+  // done is -1 for a worker with no share (linked_last's "not early")
+  for (int q0 = max(done, 0); q0 < ns; q0 += kLinkedNS) {
     u32x4 ws[kLinkedNS][NV];
-    const int m = min(kLinkedNS, ns - s0);
-    sel_issue<T, NV, kLinkedNS>(ws, sh.w.s_chan + s0, m, WdT, d, d_ff);
-    sel_consume<T, NV, kLinkedNS>(ws, sh.w.s_zv + s0, m, acc);
+    const int nq = min(kLinkedNS, ns - q0);
+    sel_issue<T, NV, kLinkedNS>(ws, sh.w.s_chan + q0, nq, WdT, d, d_ff);
+    sel_consume<T, NV, kLinkedNS>(ws, sh.w.s_zv + q0, nq, acc);
   }
   // 4. partial y, slice-major: column c of worker w at ((c / kFinCols) * nW + w) * kFinCols + c % kFinCols
   static_assert(kFinCols % V == 0, "a thread's columns lie in one slice");
@@ -1521,8 +1537,8 @@ static bool launch_linked(hipStream_t st, const void* x, int d, const void* Wg, 
   float* partial = (float*)w.down;
 #define POP_LINKED(NVT, ID)                                                                                         \
   POP_LAUNCH((k_pop_linked<T, NVT, ID>), grid, dim3(kFusedThreads), 0, st, (const T*)x, (const T*)Wg,              \
-             (const T*)Wu, (const T*)WdT, R, C, w.z, w.score, w.hand, sel_out, partial, w.ctl, d, d_ff, n_R, n_C, k, \
-             nW)
+             (const T*)Wu, (const T*)WdT, R, C, w.z, w.score, w.hand, sel_out, partial, w.ctl,                     \
+             w.hand + kPairsWord, d, d_ff, n_R, n_C, k, nW)
 #define POP_LINKED_ID(NVT)  \
   if (identity) {           \
     POP_LINKED(NVT, true);  \

@@ -590,15 +590,20 @@ __device__ __forceinline__ bool is_valid(uint64_t w) { return (w >> 63) != 0; }
 // thr[stride], ... (coherent; each reader polls one copy, so no single line is
 // polled by every workgroup).  Then, when not NULL, it writes positions
 // (ascending, into C) and selected (channels C[p]) of the k selected
-// candidates with plain stores.  A round limit reached sets *err (coherent);
-// the step goes on with score 0 for the missing candidates.
+// candidates with plain stores, and with pairs not NULL (polled words only),
+// for the j-th selected candidate in position order, pairs[j] =
+// pack_valid(C[p], bits of z_p) (coherent; a reader polls its pairs until
+// valid, as the words of two addresses are not seen in store order).  A round
+// limit reached sets *err (coherent); the step goes on with score 0 for the
+// missing candidates.
 // With score not NULL the scores are complete in memory already (an earlier
 // launch wrote them): they are read once, cand and poll_limit unused.
 template <int NTH, int MAXN>
 __device__ __forceinline__ void topk_threshold_linked(const uint64_t* __restrict__ cand, int n, int k, const int32_t* __restrict__ C,
                                       int32_t* __restrict__ positions, int32_t* __restrict__ selected,
                                       uint64_t* __restrict__ thr, int n_copies, int stride, SelShared<NTH, MAXN>& sh,
-                                      int poll_limit, uint32_t* err, const float* __restrict__ score = nullptr) {
+                                      int poll_limit, uint32_t* err, const float* __restrict__ score = nullptr,
+                                      uint64_t* __restrict__ pairs = nullptr) {
   constexpr int EM = SelShared<NTH, MAXN>::kPerThread;
   static_assert(sel_slot(MAXN - 1) < kSelSlots, "keys handed over through the histogram buffers");
   constexpr int kBinShift = 31 - 12;  // 12 leading value bits: 4096 bins
@@ -608,11 +613,12 @@ __device__ __forceinline__ void topk_threshold_linked(const uint64_t* __restrict
   for (int i = tid; i < kSelSlots; i += NTH) sh.hA[i] = 0u;
   __syncthreads();
   // ---- the scores as they arrive (element tid + j * NTH)
-  uint32_t vb[EM];
+  uint32_t vb[EM], zb[EM];  // value bits of |z|, bits of z
   bool got[EM];
 #pragma unroll
   for (int j = 0; j < EM; ++j) {
     vb[j] = 0u;
+    zb[j] = 0u;
     got[j] = tid + j * NTH >= n;
   }
   // bin of key u: (u - blo) >> bsh.  Polled words: the 12 leading value bits
@@ -672,6 +678,7 @@ __device__ __forceinline__ void topk_threshold_linked(const uint64_t* __restrict
       if (j * NTH < n && !got[j] && is_valid(wv[j])) {
         got[j] = true;
         vb[j] = (uint32_t)(wv[j] >> 32) & 0x7fffffffu;
+        zb[j] = (uint32_t)wv[j];
         atomicAdd(&sh.hA[sel_slot((int)((vb[j] - blo) >> bsh))], 1u);
       }
       all &= got[j];
@@ -813,13 +820,16 @@ __device__ __forceinline__ void topk_threshold_linked(const uint64_t* __restrict
   }
   const uint32_t cv = t0.prefix;
   if (!published && tid < n_copies) st_coh(&thr[tid * stride], pack_valid(cv, (uint32_t)tie_pos));
-  if (positions == nullptr && selected == nullptr) return;
-  // ---- the list, ascending (after the cut is out): flags in LDS, then owner-layout scan
+  if (positions == nullptr && selected == nullptr && pairs == nullptr) return;
+  // ---- the list, ascending: flags (and with pairs, z) in LDS, then owner-layout scan
   __syncthreads();  // sh.scan and the LDS buffers are reused below
 #pragma unroll
   for (int j = 0; j < EM; ++j) {
     const int i = tid + j * NTH;
-    if (i < n) sh.hB[sel_slot(i)] = (vb[j] > cv || (vb[j] == cv && i <= tie_pos)) ? 1u : 0u;
+    if (i < n) {
+      sh.hB[sel_slot(i)] = (vb[j] > cv || (vb[j] == cv && i <= tie_pos)) ? 1u : 0u;
+      if (pairs != nullptr) sh.hA[sel_slot(i)] = zb[j];
+    }
   }
   __syncthreads();
   const int E = (n + NTH - 1) / NTH;
@@ -840,6 +850,7 @@ __device__ __forceinline__ void topk_threshold_linked(const uint64_t* __restrict
       if (pos[0] < k) {
         if (positions != nullptr) positions[pos[0]] = base + j;
         if (selected != nullptr) selected[pos[0]] = C[base + j];
+        if (pairs != nullptr) st_coh(&pairs[pos[0]], pack_valid((uint32_t)C[base + j], sh.hA[sel_slot(base + j)]));
       }
       ++pos[0];
     }
