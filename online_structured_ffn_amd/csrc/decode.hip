@@ -417,16 +417,6 @@ __device__ __forceinline__ void cand_consume(const CandBuf<T, NV, NB>& b, int nr
   __syncthreads();  // part is reused by the next batch
 }
 
-template <typename T, int NV, int NB>
-__device__ __forceinline__ void cand_rows(const int* rows, int nrows, const T* __restrict__ Wg, const T* __restrict__ Wu,
-                                          int d, const u32x4 (&xv)[NV], float (&part)[kFusedWaves][2 * NB],
-                                          float* __restrict__ zout, float* __restrict__ score,
-                                          uint64_t* __restrict__ pub, float* zl = nullptr) {
-  CandBuf<T, NV, NB> b;
-  cand_issue<T, NV, NB>(b, rows, nrows, Wg, Wu, d);
-  cand_consume<T, NV, NB>(b, nrows, xv, part, zout, score, pub, zl);
-}
-
 // Loads this thread's x vectors and clears its down accumulators.
 template <typename T, int NV>
 __device__ __forceinline__ void fused_setup(const T* __restrict__ x, int d, u32x4 (&xv)[NV],
@@ -721,7 +711,7 @@ constexpr int kLinkedNS = POP_LINKED_NS;  // selected rows carried by the last r
 constexpr int kThrCopies = 32;  // copies of the published cut
 constexpr int kThrStride = 16;  // 64-bit words between copies (128 bytes)
 #ifndef POP_CAND_BATCH
-#define POP_CAND_BATCH 8
+#define POP_CAND_BATCH 3
 #endif
 constexpr int kCandBatch = POP_CAND_BATCH;  // candidate rows whose loads a worker issues together
 // The control words (1 KB), then the hand-over words: the candidate words (at
@@ -896,7 +886,6 @@ __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
   struct Work {
     int rows[kFusedMaxRows];
     float zr[kFusedMaxRows];  // z of this worker's retained rows
-    float cz[kFusedMaxRows];  // z of this worker's candidates
     float part[2][kFusedWaves][2 * kFusedP];
     float cpart[kFusedWaves][2 * kCandBatch];
     int crow[kFusedMaxRows];  // this worker's share of C (channels)
@@ -935,18 +924,42 @@ __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
   // with no retained rows, the stream's (unused) loads read the first candidate's rows
   const int* rlist = nr > 0 ? sh.w.rows : sh.w.crow;
   FusedRowBuf<T, NV> A;
-  // 1. candidate rows, kCandBatch at a time; the first retained rows' loads
-  //    go out before the last batch is reduced
-  int i0 = 0;
-  for (; i0 + kCandBatch < nc; i0 += kCandBatch)
-    cand_rows<T, NV, kCandBatch>(sh.w.crow + i0, kCandBatch, Wg, Wu, d, xv, sh.w.cpart, z + n_R + c0 + i0,
-                                 score + c0 + i0, chain ? cand + c0 + i0 : nullptr, sh.w.cz + i0);
+  // 1. candidate rows, KB at a time, double-buffered: batch b + 1's loads go
+  //    out before batch b is reduced, and the first retained rows' loads
+  //    before the last batch is.  Every pass of the loop issues the same
+  //    loads (no load behind a branch), so the compiler's wait counts stay
+  //    exact; the one or two batches after it are straight-line code.
+  constexpr int KB = kCandBatch / NV > 0 ? kCandBatch / NV : 1;
+  auto cand_at = [&](CandBuf<T, NV, KB>& b, int q) {
+    cand_issue<T, NV, KB>(b, sh.w.crow + q * KB, nc - q * KB, Wg, Wu, d);
+  };
+  auto cand_done = [&](const CandBuf<T, NV, KB>& b, int q) {
+    const int i0 = q * KB;
+    // the first KB pairs of columns of the LDS partials (KB <= kCandBatch)
+    auto& cp = *reinterpret_cast<float(*)[kFusedWaves][2 * KB]>(&sh.w.cpart[0][0]);
+    cand_consume<T, NV, KB>(b, min(KB, nc - i0), xv, cp, z + n_R + c0 + i0, score + c0 + i0,
+                            chain ? cand + c0 + i0 : nullptr, nullptr);
+  };
   if (nc > 0) {
-    CandBuf<T, NV, kCandBatch> cb;
-    cand_issue<T, NV, kCandBatch>(cb, sh.w.crow + i0, nc - i0, Wg, Wu, d);
-    fused_issue<T, NV, true>(A, rlist, 0, max(nr, 1), Wg, Wu, WdT, d);
-    cand_consume<T, NV, kCandBatch>(cb, nc - i0, xv, sh.w.cpart, z + n_R + c0 + i0, score + c0 + i0,
-                                    chain ? cand + c0 + i0 : nullptr, sh.w.cz + i0);
+    const int nb = (nc + KB - 1) / KB;
+    CandBuf<T, NV, KB> ca, cb;
+    cand_at(ca, 0);
+    int b = 0;  // ca holds batch b
+    for (; b + 2 < nb; b += 2) {
+      cand_at(cb, b + 1);
+      cand_done(ca, b);
+      cand_at(ca, b + 2);
+      cand_done(cb, b + 1);
+    }
+    if (b + 2 == nb) {
+      cand_at(cb, b + 1);
+      cand_done(ca, b);
+      fused_issue<T, NV, true>(A, rlist, 0, max(nr, 1), Wg, Wu, WdT, d);
+      cand_done(cb, b + 1);
+    } else {
+      fused_issue<T, NV, true>(A, rlist, 0, max(nr, 1), Wg, Wu, WdT, d);
+      cand_done(ca, b);
+    }
   } else {
     fused_issue<T, NV, true>(A, rlist, 0, max(nr, 1), Wg, Wu, WdT, d);
   }
