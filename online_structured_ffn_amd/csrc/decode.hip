@@ -786,7 +786,7 @@ __device__ __forceinline__ int linked_last(FusedRowBuf<T, NV>& X, FusedRowBuf<T,
   // takes the decision from LDS.
   if (threadIdx.x == 0) *sh_nsel = sel_here && *sh_ready != 0 ? m : -1;
   lds_barrier();
-  const int got = *sh_nsel;  // block-uniform; -1: the cut was not out
+  const int got = *sh_nsel;  // block-uniform; -1: the share was not ready
   const bool early = got >= 0;
   const int nsl = early ? min(got, NS) : 0;
   u32x4 ws[NS][NV];

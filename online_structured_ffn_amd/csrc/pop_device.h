@@ -35,9 +35,9 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 // coherence point, so a value one workgroup stores is the value another
 // workgroup loads, whichever XCD (and L2) each runs on.  No release or acquire
 // fence is used (a device-scope release writes back the whole L2 of the XCD and
-// costs microseconds per workgroup); ordering between locations comes from
-// mem_wait() below, or from a valid bit carried in the same 64-bit word as the
-// data it guards.
+// costs microseconds per workgroup); a reader learns that data is there from a
+// valid bit carried in the same 64-bit word as the data it guards, so no
+// order between stores to different locations is assumed.
 __device__ __forceinline__ void st_coh(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -52,14 +52,6 @@ __device__ __forceinline__ uint64_t ld_coh(const uint64_t* p) {
 }
 __device__ __forceinline__ uint32_t add_coh(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Waits until every memory operation this wave issued has completed (its
-// coherent stores have reached the coherence point).  The signal fences keep
-// the compiler from moving memory operations across the wait.
-__device__ __forceinline__ void mem_wait() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 // Workgroup barrier that orders LDS only: each wave waits for its own LDS
 // accesses (lgkmcnt(0); vmcnt and expcnt left at their maxima in the gfx9
@@ -593,7 +585,8 @@ __device__ __forceinline__ bool is_valid(uint64_t w) { return (w >> 63) != 0; }
 // candidates with plain stores, and with pairs not NULL (polled words only),
 // for the j-th selected candidate in position order, pairs[j] =
 // pack_valid(C[p], bits of z_p) (coherent; a reader polls its pairs until
-// valid, as the words of two addresses are not seen in store order).  A round
+// valid, so nothing depends on the order in which the cut and the pairs
+// become visible).  A round
 // limit reached sets *err (coherent); the step goes on with score 0 for the
 // missing candidates.
 // With score not NULL the scores are complete in memory already (an earlier
