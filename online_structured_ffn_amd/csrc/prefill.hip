@@ -287,7 +287,10 @@ __global__ __launch_bounds__(kPartThreads) void k_partition(const float* __restr
   if (n <= 0) return;
   uint32_t mn = 0xffffffffu, mx = 0u;
   // kPartBatch rows per thread at a time: their loads are in flight together
-  constexpr int kPartBatch = 8;
+#ifndef POP_PART_BATCH
+#define POP_PART_BATCH 12
+#endif
+  constexpr int kPartBatch = POP_PART_BATCH;
   for (int i0 = threadIdx.x; i0 < n; i0 += kPartBatch * kPartThreads) {
     float v[kPartBatch];
     if (n_q == 0) {
