@@ -364,12 +364,14 @@ __device__ __forceinline__ void cand_issue(CandBuf<T, NV, NB>& b, const int* row
 }
 
 // Threads p < nrows write row p's z to zout and zl (LDS, when not null), |z|
-// to score and, when pub is set, its hand-over word pack_valid(bits of |z|,
-// bits of z).
+// to score and, when pub is set, its hand-over word pack_valid(bits of h,
+// bits of z), with h = |z|, or with hm (an activation memory, copied to LDS)
+// h = hm[p] + |z| while mclear[p] (the memory itself) is cleared.
 template <typename T, int NV, int NB>
 __device__ __forceinline__ void cand_consume(const CandBuf<T, NV, NB>& b, int nrows, const u32x4 (&xv)[NV],
                                              float (&part)[kFusedWaves][2 * NB], float* __restrict__ zout,
-                                             float* __restrict__ score, uint64_t* __restrict__ pub, float* zl) {
+                                             float* __restrict__ score, uint64_t* __restrict__ pub, float* zl,
+                                             const float* hm = nullptr, float* __restrict__ mclear = nullptr) {
   constexpr int V = Vec<T>::N;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -412,7 +414,11 @@ __device__ __forceinline__ void cand_consume(const CandBuf<T, NV, NB>& b, int nr
     zout[p] = zz;
     score[p] = fabsf(zz);
     if (zl != nullptr) zl[p] = zz;
-    if (pub != nullptr) st_coh(&pub[p], pack_valid(__float_as_uint(fabsf(zz)), __float_as_uint(zz)));
+    if (pub != nullptr) {
+      const float h = hm != nullptr ? hm[p] + fabsf(zz) : fabsf(zz);
+      st_coh(&pub[p], pack_valid(__float_as_uint(h), __float_as_uint(zz)));
+    }
+    if (mclear != nullptr) mclear[p] = 0.f;
   }
   __syncthreads();  // part is reused by the next batch
 }
@@ -881,11 +887,13 @@ __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
     const T* __restrict__ x, const T* __restrict__ Wg, const T* __restrict__ Wu, const T* __restrict__ WdT,
     const int32_t* __restrict__ R, const int32_t* __restrict__ C, float* __restrict__ z, float* __restrict__ score,
     uint64_t* __restrict__ hand, int32_t* __restrict__ sel_out, float* __restrict__ partial,
-    uint32_t* __restrict__ ctl, uint64_t* __restrict__ pairs, int d, int d_ff, int n_R, int n_C, int k, int nW) {
+    uint32_t* __restrict__ ctl, uint64_t* __restrict__ pairs, int d, int d_ff, int n_R, int n_C, int k, int nW,
+    float* __restrict__ mem, int32_t* __restrict__ pos_out) {
   constexpr int V = Vec<T>::N;
   struct Work {
     int rows[kFusedMaxRows];
     float zr[kFusedMaxRows];  // z of this worker's retained rows
+    float cm[kFusedMaxRows];  // the activation memory of this worker's candidates (periodic refresh)
     float part[2][kFusedWaves][2 * kFusedP];
     float cpart[kFusedWaves][2 * kCandBatch];
     int crow[kFusedMaxRows];  // this worker's share of C (channels)
@@ -904,8 +912,8 @@ __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
   uint64_t* thr = hand + kLinkedTopkMaxN;
   if (blockIdx.x == 0) {
     if (chain)
-      topk_threshold_linked(cand, n_C, k, C, (int32_t*)nullptr, sel_out, thr, kThrCopies, kThrStride, sh.sel,
-                            kPollLimit, ctl + kCtlErr, nullptr, pairs);
+      topk_threshold_linked(cand, n_C, k, C, pos_out, sel_out, thr, kThrCopies, kThrStride, sh.sel, kPollLimit,
+                            ctl + kCtlErr, nullptr, pairs);
     return;
   }
   const int w = blockIdx.x - 1;
@@ -916,6 +924,8 @@ __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
   float acc[NV][V];
   fused_setup<T, NV>(x, d, xv, acc);
   for (int i = tid; i < nc; i += kFusedThreads) sh.w.crow[i] = clamp_channel(C[c0 + i], d_ff);
+  if (mem != nullptr)
+    for (int i = tid; i < nc; i += kFusedThreads) sh.w.cm[i] = mem[c0 + i];
   for (int i = tid; i < nr; i += kFusedThreads) sh.w.rows[i] = kIdentity ? r0 + i : clamp_channel(R[r0 + i], d_ff);
   if (tid == 0) sh.w.ready = 0;
   __syncthreads();
@@ -938,7 +948,8 @@ __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
     // the first KB pairs of columns of the LDS partials (KB <= kCandBatch)
     auto& cp = *reinterpret_cast<float(*)[kFusedWaves][2 * KB]>(&sh.w.cpart[0][0]);
     cand_consume<T, NV, KB>(b, min(KB, nc - i0), xv, cp, z + n_R + c0 + i0, score + c0 + i0,
-                            chain ? cand + c0 + i0 : nullptr, nullptr);
+                            chain ? cand + c0 + i0 : nullptr, nullptr, mem != nullptr ? sh.w.cm + i0 : nullptr,
+                            mem != nullptr ? mem + c0 + i0 : nullptr);
   };
   if (nc > 0) {
     const int nb = (nc + KB - 1) / KB;
@@ -1520,7 +1531,8 @@ static int resident_blocks(const void* kernel) { return resident_blocks_of(kerne
 template <typename T>
 static bool launch_linked(hipStream_t st, const void* x, int d, const void* Wg, const void* Wu, const void* WdT,
                           int d_ff, const int32_t* R, int n_R, const int32_t* C, int n_C, int k, float* y,
-                          const DecodeWs& w, int32_t* sel_out, bool accumulate) {
+                          const DecodeWs& w, int32_t* sel_out, bool accumulate, float* mem = nullptr,
+                          int32_t* pos_out = nullptr) {
   constexpr int V = Vec<T>::N;
   const int nv = (d + kFusedThreads * V - 1) / (kFusedThreads * V);
   // Without candidates there is no chain to overlap: the retained-only
@@ -1551,7 +1563,7 @@ static bool launch_linked(hipStream_t st, const void* x, int d, const void* Wg, 
 #define POP_LINKED(NVT, ID)                                                                                         \
   POP_LAUNCH((k_pop_linked<T, NVT, ID>), grid, dim3(kFusedThreads), 0, st, (const T*)x, (const T*)Wg,              \
              (const T*)Wu, (const T*)WdT, R, C, w.z, w.score, w.hand, sel_out, partial, w.ctl,                     \
-             w.hand + kPairsWord, d, d_ff, n_R, n_C, k, nW)
+             w.hand + kPairsWord, d, d_ff, n_R, n_C, k, nW, mem, pos_out)
 #define POP_LINKED_ID(NVT)  \
   if (identity) {           \
     POP_LINKED(NVT, true);  \
@@ -1662,6 +1674,21 @@ bool decode_ffn_accumulate_b1(const void* x, int32_t d, const void* W_gate, cons
                                     w, selected, true))
     return true;
   return POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, Rk, n_R, Ck, n_C, k, y, wf, true);
+}
+
+bool decode_periodic_refresh_b1(const void* x, int32_t d, const void* W_gate, const void* W_up, const void* W_downT,
+                                int32_t d_ff, pop_dtype dt, const int32_t* R, int32_t n_R, const int32_t* C,
+                                int32_t n_C, int32_t k, float* memory, int32_t* positions, int32_t* selected, float* y,
+                                void* ws, void* stream) {
+  if (R == nullptr || n_C <= 0 || k <= 0 || memory == nullptr || positions == nullptr || selected == nullptr)
+    return false;
+  if (!(dt == POP_BF16 ? fused_fits<bf16s>(d, n_R, n_C) : fused_fits<float>(d, n_R, n_C))) return false;
+  DecodeWs w;
+  decode_ws_layout(1, d, d_ff, (char*)ws, &w);
+  hipStream_t st = (hipStream_t)stream;
+  trace_mark(st);
+  return POP_LINKED_ON && POP_DISPATCH(dt, launch_linked, st, x, d, W_gate, W_up, W_downT, d_ff, R, n_R, C, n_C, k, y,
+                                       w, selected, false, memory, positions);
 }
 
 float* decode_ws_z(void* ws, int32_t batch, int32_t d, int32_t d_ff) {

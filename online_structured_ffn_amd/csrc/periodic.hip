@@ -130,6 +130,14 @@ extern "C" pop_status pop_decode_ffn_periodic(const void* x, int32_t batch, int3
   const int32_t* Rk = R != nullptr ? R : w.rows;
   pop_status s;
   if (step % period == 0) {  // refresh
+    // batch 1: the single-launch step ranks the candidates by memory + |z|
+    // itself (and clears the memory); the retained rows for the kept steps follow
+    if (batch == 1 && n_C > 0 && k > 0 &&
+        decode_periodic_refresh_b1(x, d, W_gate, W_up, W_downT, d_ff, dt, Rk, n_R, C, n_C, k, memory, positions,
+                                   selected, y, w.step, stream)) {
+      POP_LAUNCH(k_concat, blocks_for(n_R + k), dim3(256), 0, st, rows, Rk, n_R, (const int32_t*)selected, k);
+      return launched_ok();
+    }
     if ((s = pop_decode_gateup(x, batch, d, W_gate, W_up, d_ff, dt, Rk, n_R, C, n_C, w.z, w.score, stream)) != POP_OK)
       return s;
     if (n_C > 0 && k > 0) {

@@ -72,6 +72,16 @@ bool decode_ffn_accumulate_b1(const void* x, int32_t d, const void* W_gate, cons
                               int32_t d_ff, pop_dtype dt, bool dense, const int32_t* R, int32_t n_R,
                               const int32_t* C, int32_t n_C, double r, float* y, int32_t* selected, void* ws,
                               void* stream);
+// The refresh step of the periodic mode at batch 1 in the single-launch form:
+// the candidates ranked by memory + |z| (memory [n_C] is read and cleared),
+// the k best written to positions (into C) and selected (channels), y the
+// FFN over R and them; ws a batch-1 decode workspace.  Returns false, having
+// launched nothing, when that form does not apply (the caller then takes the
+// staged calls).
+bool decode_periodic_refresh_b1(const void* x, int32_t d, const void* W_gate, const void* W_up, const void* W_downT,
+                                int32_t d_ff, pop_dtype dt, const int32_t* R, int32_t n_R, const int32_t* C,
+                                int32_t n_C, int32_t k, float* memory, int32_t* positions, int32_t* selected, float* y,
+                                void* ws, void* stream);
 
 // Records the next caller-provided trace event on `stream` (no-op unless
 // pop_set_trace_events armed this thread).
