@@ -543,6 +543,14 @@ __device__ __forceinline__ int fin_slice(int b, int nb) {
   return (q * 8 + x) * SP + h;
 }
 
+// The periodic mode's memory update of a kept step, done by the step's last
+// launch: mem[pos[j]] += |z[zoff + j]| for j < k (batch 1; mem NULL: none).
+struct MemAdd {
+  float* mem;
+  const int32_t* pos;
+  int zoff, k, n_C;
+};
+
 template <typename T, bool kSel>
 __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restrict__ partial, int n_part,
                                                             const float* __restrict__ z, int zoff, int n_A,
@@ -550,7 +558,8 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
                                                             const int32_t* __restrict__ pos, int k,
                                                             const T* __restrict__ WdT, int d, int d_ff,
                                                             float* __restrict__ y, int accumulate,
-                                                            uint64_t* reset_words, int n_reset_words) {
+                                                            uint64_t* reset_words, int n_reset_words,
+                                                            MemAdd ma) {
   constexpr int V = Vec<T>::N;
   constexpr int LR = kFinCols / V;       // lanes per W_downT row
   constexpr int RPW = 64 / LR;           // W_downT rows per wave instruction
@@ -564,6 +573,11 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
   // the single-launch step's hand-over words, cleared for the next call
   for (int i = blockIdx.x * kFinThreads + threadIdx.x; i < n_reset_words; i += gridDim.x * kFinThreads)
     st_coh(&reset_words[i], (uint64_t)0);
+  if (ma.mem != nullptr)  // positions are distinct: one thread per entry
+    for (int j = blockIdx.x * kFinThreads + threadIdx.x; j < ma.k; j += gridDim.x * kFinThreads) {
+      const int p = ma.pos[j];
+      if (p >= 0 && p < ma.n_C) ma.mem[p] += fabsf(z[ma.zoff + j]);
+    }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = fin_slice(blockIdx.x, gridDim.x) * kFinCols;
@@ -1446,7 +1460,7 @@ static void launch_down(hipStream_t st, const float* z, int B, int n_A, const vo
 template <typename T>
 static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, const void* Wu, const void* WdT,
                          int d_ff, const int32_t* R, int n_R, const int32_t* C, int n_C, int k, float* y,
-                         const DecodeWs& w, bool accumulate = false) {
+                         const DecodeWs& w, bool accumulate = false, MemAdd ma = MemAdd{}) {
   constexpr int V = Vec<T>::N;
   const int nv = (d + kFusedThreads * V - 1) / (kFusedThreads * V);
   if (nv > 4) return false;
@@ -1509,11 +1523,11 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
   if (k > 0) {
     POP_LAUNCH((k_pop_finish<T, true>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
                (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, k, (const T*)WdT, d,
-               d_ff, y, (int)accumulate, (uint64_t*)nullptr, 0);
+               d_ff, y, (int)accumulate, (uint64_t*)nullptr, 0, MemAdd{});
   } else {
     POP_LAUNCH((k_pop_finish<T, false>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
                (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, 0, (const T*)WdT, d,
-               d_ff, y, (int)accumulate, (uint64_t*)nullptr, 0);
+               d_ff, y, (int)accumulate, (uint64_t*)nullptr, 0, ma);
   }
   return true;
 }
@@ -1581,7 +1595,7 @@ static bool launch_linked(hipStream_t st, const void* x, int d, const void* Wg, 
 #undef POP_LINKED
   POP_LAUNCH((k_pop_finish<T, false>), dim3((d + kFinCols - 1) / kFinCols), dim3(kFinThreads), 0, st,
              (const float*)partial, nW, (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel,
-             (const int32_t*)w.Q, 0, (const T*)WdT, d, d_ff, y, (int)accumulate, w.hand, (int)kHandWords);
+             (const int32_t*)w.Q, 0, (const T*)WdT, d, d_ff, y, (int)accumulate, w.hand, (int)kHandWords, MemAdd{});
   return true;
 }
 
@@ -1674,6 +1688,21 @@ bool decode_ffn_accumulate_b1(const void* x, int32_t d, const void* W_gate, cons
                                     w, selected, true))
     return true;
   return POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, Rk, n_R, Ck, n_C, k, y, wf, true);
+}
+
+bool decode_periodic_kept_b1(const void* x, int32_t d, const void* W_gate, const void* W_up, const void* W_downT,
+                             int32_t d_ff, pop_dtype dt, const int32_t* rows, int32_t n_R, int32_t k, float* memory,
+                             const int32_t* positions, int32_t n_C, float* y, void* ws, void* stream) {
+  const int32_t n = n_R + k;
+  if (n <= 0 || rows == nullptr || k <= 0 || memory == nullptr || positions == nullptr) return false;
+  if (!(dt == POP_BF16 ? fused_fits<bf16s>(d, n, 0) : fused_fits<float>(d, n, 0))) return false;
+  DecodeWs w;
+  decode_ws_layout(1, d, d_ff, (char*)ws, &w);
+  hipStream_t st = (hipStream_t)stream;
+  trace_mark(st);
+  const MemAdd ma{memory, positions, n_R, k, n_C};
+  return POP_DISPATCH(dt, launch_fused, st, x, d, W_gate, W_up, W_downT, d_ff, rows, n, (const int32_t*)nullptr, 0, 0,
+                      y, w, false, ma);
 }
 
 bool decode_periodic_refresh_b1(const void* x, int32_t d, const void* W_gate, const void* W_up, const void* W_downT,

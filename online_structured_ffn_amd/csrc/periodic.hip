@@ -106,6 +106,11 @@ extern "C" pop_status pop_decode_ffn_periodic(const void* x, int32_t batch, int3
                                               int32_t* selected, int32_t* rows, float* y, void* ws, size_t ws_bytes,
                                               void* stream) {
   clear_error();
+  // the shape checks of the decode entry points: the batch-1 steps below
+  // launch their kernels directly
+  if (const pop_status sc = check_dtype_width(dt, d); sc != POP_OK) return sc;
+  if (d_ff < 1 || d_ff > POP_MAX_D_FF) return fail(POP_ERR_BAD_SHAPE, "d_ff=%d outside [1, %d]", d_ff, POP_MAX_D_FF);
+  if (batch < 0 || batch > POP_MAX_BATCH) return fail(POP_ERR_BAD_SHAPE, "batch=%d outside [0, %d]", batch, POP_MAX_BATCH);
   if (period < 1) return fail(POP_ERR_INVALID_ARGUMENT, "period=%d must be at least 1", period);
   if (step < 0) return fail(POP_ERR_INVALID_ARGUMENT, "step=%d must be non-negative", step);
   if (!(r >= 0.0 && r < 1.0)) return fail(POP_ERR_INVALID_ARGUMENT, "r=%g outside [0, 1)", r);
@@ -121,7 +126,11 @@ extern "C" pop_status pop_decode_ffn_periodic(const void* x, int32_t batch, int3
     if (sd != POP_OK) return sd;
   }
   const DebugNested nest;  // the calls below pass the retained rows (R, then the selection)
+  if ((batch > 0 && (x == nullptr || y == nullptr)) || W_gate == nullptr || W_up == nullptr || W_downT == nullptr)
+    return fail(POP_ERR_INVALID_ARGUMENT, "x, y and the weights must be non-NULL");
   if (!aligned16(ws)) return fail(POP_ERR_MISALIGNED, "ws must be 16-byte aligned");
+  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_downT) || !aligned16(y))
+    return fail(POP_ERR_MISALIGNED, "x, y and the weights must be 16-byte aligned");
   const PeriodicWs w0 = periodic_ws(batch, d, d_ff, nullptr);
   if (ws_bytes < w0.bytes) return fail(POP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, w0.bytes);
   const PeriodicWs w = periodic_ws(batch, d, d_ff, (char*)ws);
@@ -153,6 +162,10 @@ extern "C" pop_status pop_decode_ffn_periodic(const void* x, int32_t batch, int3
   }
   // between refreshes: the step over R plus the kept selection as retained
   // rows (no candidates), whose z of the selected rows joins the memory
+  if (batch == 1 && k > 0 && n_C > 0 &&
+      decode_periodic_kept_b1(x, d, W_gate, W_up, W_downT, d_ff, dt, rows, n_R, k, memory, positions, n_C, y, w.step,
+                              stream))
+    return launched_ok();
   if ((s = pop_decode_ffn(x, batch, d, W_gate, W_up, W_downT, d_ff, dt, n_R + k > 0 ? rows : w.rows, n_R + k,
                           nullptr, 0, r, y, nullptr,
                           w.step, w.step_bytes, stream)) != POP_OK)

@@ -72,6 +72,13 @@ bool decode_ffn_accumulate_b1(const void* x, int32_t d, const void* W_gate, cons
                               int32_t d_ff, pop_dtype dt, bool dense, const int32_t* R, int32_t n_R,
                               const int32_t* C, int32_t n_C, double r, float* y, int32_t* selected, void* ws,
                               void* stream);
+// A kept step of the periodic mode at batch 1: the retained rows rows[0 ..
+// n_R + k) (R, then the selection) in the fused stream, and the memory update
+// memory[positions[j]] += |z of row n_R + j| in the step's last launch.
+// Returns false, having launched nothing, when that form does not apply.
+bool decode_periodic_kept_b1(const void* x, int32_t d, const void* W_gate, const void* W_up, const void* W_downT,
+                             int32_t d_ff, pop_dtype dt, const int32_t* rows, int32_t n_R, int32_t k, float* memory,
+                             const int32_t* positions, int32_t n_C, float* y, void* ws, void* stream);
 // The refresh step of the periodic mode at batch 1 in the single-launch form:
 // the candidates ranked by memory + |z| (memory [n_C] is read and cleared),
 // the k best written to positions (into C) and selected (channels), y the

@@ -152,6 +152,9 @@ def _periodic(x=A, b=1, d=256, Wg=A, Wu=A, Wd=A, d_ff=688, dt=0, R=A, nR=413, C=
     (dict(mem=None), INVALID), (dict(S=None), INVALID), (dict(C=None), INVALID), (dict(rows=None), INVALID),
     (dict(ws=A + 4), MISALIGNED),
     (dict(wsb=100), WS),
+    (dict(dt=3), DTYPE), (dict(d=4, dt=1), SHAPE), (dict(b=-1), SHAPE), (dict(d_ff=0), SHAPE),
+    (dict(x=None), INVALID), (dict(y=None), INVALID), (dict(Wg=None), INVALID),
+    (dict(Wd=A + 2), MISALIGNED), (dict(y=A + 4), MISALIGNED),
 ])
 def test_periodic_validation(kw, status):
     assert _periodic(**kw) == status
