@@ -300,6 +300,11 @@ pop_status pop_decode_ffn_noalloc(const void* x, int32_t batch, int32_t d, const
  * rows are state too.  k, x, weights and lists as pop_decode_ffn;
  * period >= 1, step >= 0.  ws: at least
  * pop_decode_periodic_workspace_bytes(batch, d, d_ff) bytes, 16-byte aligned.
+ * Kernels at batch 1 (when pop_decode_ffn's single launch applies): a
+ * refresh is that launch with each candidate ranked by memory + |z| (the
+ * workers clear the memory they read), then one small launch writing rows; a
+ * kept step is the retained-row stream whose last launch also updates the
+ * memory.  Other batches compose the stage entry points.
  * Errors as pop_decode_ffn and INVALID_ARGUMENT for period < 1 or step < 0.
  * Calls that share memory or ws must be ordered on one stream.
  */
