@@ -551,7 +551,7 @@ struct MemAdd {
   int zoff, k, n_C;
 };
 
-template <typename T, bool kSel>
+template <typename T, bool kSel, bool kMem = false>
 __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restrict__ partial, int n_part,
                                                             const float* __restrict__ z, int zoff, int n_A,
                                                             const int32_t* __restrict__ sel,
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(kFinThreads) void k_pop_finish(const float* __restr
   // the single-launch step's hand-over words, cleared for the next call
   for (int i = blockIdx.x * kFinThreads + threadIdx.x; i < n_reset_words; i += gridDim.x * kFinThreads)
     st_coh(&reset_words[i], (uint64_t)0);
-  if (ma.mem != nullptr)  // positions are distinct: one thread per entry
+  if constexpr (kMem)  // positions are distinct: one thread per entry
     for (int j = blockIdx.x * kFinThreads + threadIdx.x; j < ma.k; j += gridDim.x * kFinThreads) {
       const int p = ma.pos[j];
       if (p >= 0 && p < ma.n_C) ma.mem[p] += fabsf(z[ma.zoff + j]);
@@ -896,7 +896,7 @@ __device__ __forceinline__ int linked_stream(FusedRowBuf<T, NV>& A, const int* r
 #ifndef POP_LINKED_MINB
 #define POP_LINKED_MINB 1  // workgroups of k_pop_linked resident per CU
 #endif
-template <typename T, int NV, bool kIdentity>
+template <typename T, int NV, bool kIdentity, bool kMem>
 __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
     const T* __restrict__ x, const T* __restrict__ Wg, const T* __restrict__ Wu, const T* __restrict__ WdT,
     const int32_t* __restrict__ R, const int32_t* __restrict__ C, float* __restrict__ z, float* __restrict__ score,
@@ -938,7 +938,7 @@ __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
   float acc[NV][V];
   fused_setup<T, NV>(x, d, xv, acc);
   for (int i = tid; i < nc; i += kFusedThreads) sh.w.crow[i] = clamp_channel(C[c0 + i], d_ff);
-  if (mem != nullptr)
+  if constexpr (kMem)
     for (int i = tid; i < nc; i += kFusedThreads) sh.w.cm[i] = mem[c0 + i];
   for (int i = tid; i < nr; i += kFusedThreads) sh.w.rows[i] = kIdentity ? r0 + i : clamp_channel(R[r0 + i], d_ff);
   if (tid == 0) sh.w.ready = 0;
@@ -962,8 +962,8 @@ __global__ __launch_bounds__(kFusedThreads, POP_LINKED_MINB) void k_pop_linked(
     // the first KB pairs of columns of the LDS partials (KB <= kCandBatch)
     auto& cp = *reinterpret_cast<float(*)[kFusedWaves][2 * KB]>(&sh.w.cpart[0][0]);
     cand_consume<T, NV, KB>(b, min(KB, nc - i0), xv, cp, z + n_R + c0 + i0, score + c0 + i0,
-                            chain ? cand + c0 + i0 : nullptr, nullptr, mem != nullptr ? sh.w.cm + i0 : nullptr,
-                            mem != nullptr ? mem + c0 + i0 : nullptr);
+                            chain ? cand + c0 + i0 : nullptr, nullptr, kMem ? sh.w.cm + i0 : nullptr,
+                            kMem ? mem + c0 + i0 : nullptr);
   };
   if (nc > 0) {
     const int nb = (nc + KB - 1) / KB;
@@ -1525,9 +1525,14 @@ static bool launch_fused(hipStream_t st, const void* x, int d, const void* Wg, c
                (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, k, (const T*)WdT, d,
                d_ff, y, (int)accumulate, (uint64_t*)nullptr, 0, MemAdd{});
   } else {
-    POP_LAUNCH((k_pop_finish<T, false>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
-               (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, 0, (const T*)WdT, d,
-               d_ff, y, (int)accumulate, (uint64_t*)nullptr, 0, ma);
+    if (ma.mem != nullptr)
+      POP_LAUNCH((k_pop_finish<T, false, true>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
+                 (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, 0, (const T*)WdT, d,
+                 d_ff, y, (int)accumulate, (uint64_t*)nullptr, 0, ma);
+    else
+      POP_LAUNCH((k_pop_finish<T, false>), fgrid, dim3(kFinThreads), 0, st, (const float*)partial, nbR,
+                 (const float*)w.z, n_R, n_R + n_C, (const int32_t*)w.sel, (const int32_t*)w.Q, 0, (const T*)WdT, d,
+                 d_ff, y, (int)accumulate, (uint64_t*)nullptr, 0, MemAdd{});
   }
   return true;
 }
@@ -1554,9 +1559,10 @@ static bool launch_linked(hipStream_t st, const void* x, int d, const void* Wg, 
   if (nv > 4 || n_C <= 0 || k <= 0 || n_C > kLinkedTopkMaxN || n_R + n_C <= 0) return false;
   const bool identity = R == nullptr;
   const void* kern = nullptr;
-#define POP_LINKED_PICK(NVT)                                                   \
-  kern = identity ? reinterpret_cast<const void*>(&k_pop_linked<T, NVT, true>) \
-                  : reinterpret_cast<const void*>(&k_pop_linked<T, NVT, false>)
+#define POP_LINKED_PICK(NVT)                                                                   \
+  kern = identity ? reinterpret_cast<const void*>(&k_pop_linked<T, NVT, true, false>)          \
+                  : (mem != nullptr ? reinterpret_cast<const void*>(&k_pop_linked<T, NVT, false, true>) \
+                                    : reinterpret_cast<const void*>(&k_pop_linked<T, NVT, false, false>))
   if (nv <= 1) {
     POP_LINKED_PICK(1);
   } else if (nv <= 2) {
@@ -1574,15 +1580,17 @@ static bool launch_linked(hipStream_t st, const void* x, int d, const void* Wg, 
   if ((n_C + nW - 1) / nW + (n_R + nW - 1) / nW > kFusedMaxRows) return false;
   const dim3 grid(1 + nW);
   float* partial = (float*)w.down;
-#define POP_LINKED(NVT, ID)                                                                                         \
-  POP_LAUNCH((k_pop_linked<T, NVT, ID>), grid, dim3(kFusedThreads), 0, st, (const T*)x, (const T*)Wg,              \
+#define POP_LINKED(NVT, ID, MEM)                                                                                         \
+  POP_LAUNCH((k_pop_linked<T, NVT, ID, MEM>), grid, dim3(kFusedThreads), 0, st, (const T*)x, (const T*)Wg,              \
              (const T*)Wu, (const T*)WdT, R, C, w.z, w.score, w.hand, sel_out, partial, w.ctl,                     \
              w.hand + kPairsWord, d, d_ff, n_R, n_C, k, nW, mem, pos_out)
-#define POP_LINKED_ID(NVT)  \
-  if (identity) {           \
-    POP_LINKED(NVT, true);  \
-  } else {                  \
-    POP_LINKED(NVT, false); \
+#define POP_LINKED_ID(NVT)        \
+  if (identity) {                 \
+    POP_LINKED(NVT, true, false);  \
+  } else if (mem != nullptr) {    \
+    POP_LINKED(NVT, false, true);  \
+  } else {                        \
+    POP_LINKED(NVT, false, false); \
   }
   if (nv <= 1) {
     POP_LINKED_ID(1)

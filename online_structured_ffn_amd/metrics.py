@@ -71,7 +71,7 @@ def linked_symbol(d: int, e: int) -> str:
     bytes e (its template takes the 16-byte vectors per thread: 1, 2 or 4)."""
     nv = -(-d // (LINKED_THREADS * (16 // e)))
     tname = "pop::bf16s" if e == 2 else "float"
-    return f"pop::k_pop_linked<{tname}, {1 if nv <= 1 else 2 if nv <= 2 else 4}, false>"
+    return f"pop::k_pop_linked<{tname}, {1 if nv <= 1 else 2 if nv <= 2 else 4}, false, false>"
 
 
 def linked_bytes(d: int, n_R: int, n_C: int, k: int, e: int) -> int:
